@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of the lossless BF16 exponent codec on one MI355X.
+
+One step = the whole hot path over one 64 Mi-value gradient bucket (16 layers of
+4 Mi values, each layer with its own sigma-predicted table): plan the 16 tables on the
+host, compress all layers in one launch, decompress them in one launch.  Inputs are
+resident in HBM before the timed region; three input/output buffer sets rotate so that
+no step finds its data in the 256 MB Infinity Cache.
+
+Printed (one JSON line on stdout):
+  value      BF16 bytes handled per second by the step: (2n compressed + 2n decompressed)
+             / step wall time, in GB/s (the harmonic mean of the two codec directions);
+  roofline   for the compress kernel (the step's dominant kernel): algorithmic HBM bytes
+             per launch (2n read + static part + escapes written) / average launch time
+             from HIP events on the launch stream, against the 8 TB/s HBM peak;
+  cpu_baseline  the plain C oracle, single-threaded, on the same bucket;
+  per_config the other workloads (1 Mi chunk, activations with escapes and specials,
+             MoE dispatch buckets, reduce-scatter share with decode-accumulate and the
+             two-stream pipeline), each with compress / decompress GB/s and HBM fraction.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "codec GB/s (bf16 in) compress/decompress, % of HBM peak, compression ratio"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def median(v):
+    return statistics.median(v) if v else float("nan")
+
+
+class Timer:
+    """HIP events on the launch stream (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def ms(self):
+        self.torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def to_dev(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class BatchCodec:
+    """Device buffers for one workload: R rotating sets of inputs and outputs."""
+
+    def __init__(self, torch, Z, segments, sigmas, sets):
+        self.torch, self.Z = torch, Z
+        self.sizes = [s.size for s in segments]
+        self.n = sum(self.sizes)
+        self.sigmas = sigmas
+        self.static_bytes = sum(Z.static_size(n) for n in self.sizes)
+        self.sets = []
+        for _ in range(sets):
+            ins = [to_dev(torch, s) for s in segments]
+            self.sets.append(dict(
+                ins=ins,
+                static=torch.empty(self.static_bytes, dtype=torch.uint8, device="cuda"),
+                esc=torch.empty(self.n, dtype=torch.uint8, device="cuda"),
+                outs=[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in self.sizes]))
+        self.ws = torch.zeros(Z.workspace_size(self.n, len(self.sizes)), dtype=torch.uint8, device="cuda")
+        self.n_esc = torch.zeros(len(self.sizes) + 1, dtype=torch.int64, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def plans(self):
+        return [self.Z.plan(sigma=s) for s in self.sigmas]
+
+    def compress(self, k, plans):
+        s = self.sets[k % len(self.sets)]
+        self.Z.compress(list(zip(s["ins"], plans)), s["static"], s["esc"], self.ws, self.n_esc, self.status)
+
+    def decompress(self, k):
+        s = self.sets[k % len(self.sets)]
+        self.Z.decompress(s["static"], s["esc"], s["outs"], self.status)
+
+    def verify(self):
+        self.torch.cuda.synchronize()
+        ok = int(self.status.item()) == 0
+        for s in self.sets:
+            for a, b in zip(s["ins"], s["outs"]):
+                ok = ok and bool(self.torch.equal(a.view(self.torch.int16), b.view(self.torch.int16)))
+        return ok
+
+    def n_esc_total(self):
+        return int(self.n_esc[-1].item())
+
+
+def compress_bytes(n, static_bytes, n_esc):
+    return 2 * n + static_bytes + n_esc
+
+
+def time_codec(torch, bc, iters, warmup):
+    plans = bc.plans()
+    for k in range(warmup):
+        bc.compress(k, plans)
+        bc.decompress(k)
+    tc, td = Timer(torch), Timer(torch)
+    for k in range(iters):
+        e = tc.start()
+        bc.compress(k, plans)
+        tc.stop(e)
+        e = td.start()
+        bc.decompress(k)
+        td.stop(e)
+    return tc.ms(), td.ms()
+
+
+def codec_report(bc, c_ms, d_ms):
+    n_esc = bc.n_esc_total()
+    moved = compress_bytes(bc.n, bc.static_bytes, n_esc)
+    c, d = median(c_ms), median(d_ms)
+    return {
+        "elements": bc.n,
+        "segments": len(bc.sizes),
+        "compress_us": round(c * 1e3, 2),
+        "decompress_us": round(d * 1e3, 2),
+        "compress_GBps": round(2 * bc.n / (c * 1e-3) / 1e9, 1),
+        "decompress_GBps": round(2 * bc.n / (d * 1e-3) / 1e9, 1),
+        "compress_hbm_frac": round(moved / (c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "decompress_hbm_frac": round(moved / (d * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "ratio": round(2 * bc.n / (bc.static_bytes + n_esc), 5),
+        "bits_per_value": round(8 * (bc.static_bytes + n_esc) / bc.n, 4),
+        "escape_frac": round(n_esc / bc.n, 5),
+    }
+
+
+def bench_rs(torch, Z, W, iters):
+    """Reduce-scatter receive share: 7 peer shards x 64 Mi, 32 chunks of 2 Mi values."""
+    wl = W.rs_512m()
+    P, chunk, n = wl.extra["peers"], wl.extra["chunk"], wl.extra["shard"]
+    plans = [Z.plan(sigma=s) for s in wl.sigmas]
+    peers = [to_dev(torch, s) for s in wl.segments]
+    local = to_dev(torch, wl.extra["local"])
+    dst = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    nch = n // chunk
+    S = Z.static_size(chunk)
+    # every chunk's compressed output kept (as a receiver would hold what arrived)
+    static = torch.empty(nch * P * S, dtype=torch.uint8, device="cuda")
+    esc = torch.empty(nch * P * chunk, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(Z.workspace_size(P * chunk, P), dtype=torch.uint8, device="cuda")
+    n_esc = torch.zeros(nch, P + 1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def compress_all():
+        for c in range(nch):
+            segs = [(p[c * chunk:(c + 1) * chunk], pl) for p, pl in zip(peers, plans)]
+            Z.compress(segs, static[c * P * S:(c + 1) * P * S], esc[c * P * chunk:(c + 1) * P * chunk], ws,
+                       n_esc[c], status)
+
+    def accumulate_all():
+        for c in range(nch):
+            base = static.data_ptr() + c * P * S
+            eb = esc.data_ptr() + c * P * chunk
+            Z.decompress_accumulate([base + p * S for p in range(P)], [eb] * P, chunk, local[c * chunk:],
+                                    dst[c * chunk:], status, esc_bytes=[P * chunk] * P)
+
+    compress_all()
+    accumulate_all()
+    tc, ta = Timer(torch), Timer(torch)
+    for _ in range(iters):
+        e = tc.start()
+        compress_all()
+        tc.stop(e)
+        e = ta.start()
+        accumulate_all()
+        ta.stop(e)
+    c_ms, a_ms = median(tc.ms()), median(ta.ms())
+    total_esc = int(n_esc[:, -1].sum().item())
+    static_total = nch * P * S
+    comp_moved = 2 * P * n + static_total + total_esc
+    acc_moved = static_total + total_esc + 2 * n + 2 * n
+    # two-stream pipeline, wall time
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    pipe = Z.Pipeline(P, chunk, sa, sb)
+    pipe.reduce(peers, plans, local, dst, status)
+    torch.cuda.synchronize()
+    walls = []
+    for _ in range(iters):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pipe.reduce(peers, plans, local, dst, status)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    pipe.close()
+    ok = int(status.item()) == 0
+    wall = median(walls)
+    return {
+        "elements_per_peer": n, "peers": P, "chunk": chunk, "chunks": nch,
+        "compress_us": round(c_ms * 1e3, 1),
+        "compress_GBps": round(2 * P * n / (c_ms * 1e-3) / 1e9, 1),
+        "compress_hbm_frac": round(comp_moved / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "accumulate_us": round(a_ms * 1e3, 1),
+        "accumulate_GBps_bf16_in": round(2 * P * n / (a_ms * 1e-3) / 1e9, 1),
+        "accumulate_hbm_frac": round(acc_moved / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "pipeline_wall_us": round(wall * 1e6, 1),
+        "pipeline_GBps_bf16_in": round(2 * P * n / wall / 1e9, 1),
+        "ratio": round(2 * P * n / (static_total + total_esc), 5),
+        "escape_frac": round(total_esc / (P * n), 5),
+        "status_ok": ok,
+    }
+
+
+def cpu_baseline(W, O, wl, reps):
+    import numpy as np
+    tables = [O.plan_sigma(s) for s in wl.sigmas]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        st, esc, ne, rc = O.compress_batch(wl.segments, tables)
+        t1 = time.perf_counter()
+        off_st, off_esc = 0, 0
+        for x in wl.segments:
+            sz = O.static_size(x.size)
+            O.decompress(st[off_st:off_st + sz], esc, x.size)
+            off_st += sz
+        t2 = time.perf_counter()
+        times.append((t1 - t0, t2 - t1))
+    c = median([t[0] for t in times])
+    d = median([t[1] for t in times])
+    n = wl.n_total
+    return {"value": round(4 * n / (c + d) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{wl.name} full bucket ({n} values), compress + decompress, median of {reps}, 1 thread",
+            "compress_GBps": round(2 * n / c / 1e9, 4), "decompress_GBps": round(2 * n / d / 1e9, 4),
+            "host_cpus": os.cpu_count()}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and this build has no "
+              f"multi-GPU path; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only (WORLD_SIZE > 1 given)", file=sys.stderr)
+        return 2
+
+    import torch
+    from lossless_bf16_exponent_codec_amd import workloads as W
+    from lossless_bf16_exponent_codec_amd import zipccl as Z
+    torch.cuda.set_device(0)
+
+    log("generating bucket_64m")
+    wl = W.bucket_64m()
+    bc = BatchCodec(torch, Z, wl.segments, wl.sigmas, args.sets)
+    n = bc.n
+
+    def step(k):
+        plans = bc.plans()                  # a1: sigma -> tables, host
+        bc.compress(k, plans)               # a2-a5, a8: one launch over 16 segments
+        bc.decompress(k)                    # a6: one launch
+
+    log(f"warmup {args.warmup}")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    tc, td = Timer(torch), Timer(torch)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        plans = bc.plans()
+        e = tc.start()
+        bc.compress(k, plans)
+        tc.stop(e)
+        e = td.start()
+        bc.decompress(k)
+        td.stop(e)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    c_ms, d_ms = tc.ms(), td.ms()
+    ok = bc.verify()
+    rep = codec_report(bc, c_ms, d_ms)
+    value = 4 * n / (ms_per_step * 1e-3) / 1e9
+    n_esc = bc.n_esc_total()
+    moved = compress_bytes(n, bc.static_bytes, n_esc)
+    c_avg = sum(c_ms) / len(c_ms)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": "bucket_64m: gradient bucket of 16 layers x 4194304 BF16 values, "
+                               "N(0, sigma_l), sigma_l log-uniform in [1e-4, 1e-1], one table per layer",
+                   "elements": n, "segments": len(bc.sizes), "rotating_sets": args.sets},
+        "compress_GBps": rep["compress_GBps"],
+        "decompress_GBps": rep["decompress_GBps"],
+        "compress_hbm_frac": rep["compress_hbm_frac"],
+        "decompress_hbm_frac": rep["decompress_hbm_frac"],
+        "ratio": rep["ratio"],
+        "bits_per_value": rep["bits_per_value"],
+        "escape_frac": rep["escape_frac"],
+        "parity_round_trip": ok,
+        "roofline": {"bound": "hbm", "kernel": "compress_kernel",
+                     "achieved": round(moved / (c_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(moved / (c_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "bytes_per_launch": moved, "avg_launch_us": round(c_avg * 1e3, 2),
+                     "traffic": None},
+    }
+    if not args.no_extra:
+        per = {"bucket_64m": rep}
+        for name in ("chunk_1m", "act_8192x7168", "moe_16384x7168"):
+            log(f"workload {name}")
+            w2 = W.get(name)
+            sets = 8 if name == "chunk_1m" else 3
+            b2 = BatchCodec(torch, Z, w2.segments, w2.sigmas, sets)
+            cm, dm = time_codec(torch, b2, 20, 3)
+            r2 = codec_report(b2, cm, dm)
+            r2["parity_round_trip"] = b2.verify()
+            per[name] = r2
+            del b2
+            torch.cuda.empty_cache()
+        log("workload rs_512m")
+        per["rs_512m"] = bench_rs(torch, Z, W, 5)
+        out["per_config"] = per
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, 1 thread)")
+        from oracle import oracle as O
+        out["cpu_baseline"] = cpu_baseline(W, O, wl, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

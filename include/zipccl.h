@@ -1,0 +1,189 @@
+/*
+ * zipccl.h -- C ABI of the lossless BF16 exponent codec for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The codec follows "ZipCCL: Efficient Lossless Data Compression of Communication
+ * Collectives for Accelerating LLM Training" (gist.science explanation page):
+ *   S2.A  a table of the 7 most frequent exponents predicted from the tensor's
+ *         standard deviation sigma with a Gaussian model, no online histogram;
+ *   S2.B  each BF16 value is split into a sign+mantissa byte and an 8-bit exponent;
+ *         a table exponent becomes a 3-bit code 001..111, any other exponent the
+ *         escape code 000 with the full exponent appended to a separate array;
+ *   S2.C  sections padded to 128 bytes; the 3-bit codes stored as three 1-bit planes;
+ *   S2.D  the reduce-scatter receive side decodes and reduces locally.
+ *
+ * Compressed format, version 1 (all integers little-endian).  One segment of n values,
+ * T = ceil(n/512) tiles, K = ceil(n/4096) blocks, R128 = round up to 128:
+ *   [0,128)   header: u32 magic 0x3143435A, u16 version 1, u16 flags 0, u64 n,
+ *             u8 table[7] (ascending), u8 0, u32 4096, u32 512, u64 n_esc,
+ *             u64 esc_offset, u64 static_bytes, u64 0, 64 zero bytes
+ *   A         512*T bytes: A[i] = sign << 7 | 7-bit mantissa of value i (0 past n)
+ *   B         R128(192*T) bytes: u64 plane word 24*t + 8*p + j holds, in bit l,
+ *             bit p of the code of value 512*t + 8*l + j (0 past n)
+ *   C         R128(4*K) bytes: u32 off[b] = escapes among values [0, 4096*b)
+ *   static_bytes = 128 + 512*T + R128(192*T) + R128(4*K)
+ * Escapes: one exponent byte per code-0 value, in index order, stored in a separate
+ * escape buffer from byte esc_offset on.  code(e) = 1 + rank of e in the ascending
+ * table, 0 if e is not in it; exponents 0 and 255 are never in a table.
+ *
+ * Conventions.
+ *   - All data pointers are device pointers unless stated.  The caller owns every
+ *     buffer; the library allocates no device memory and keeps no global state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues
+ *     work on it and returns; nothing synchronises the host.
+ *   - Argument errors are returned before anything is enqueued.  Data-dependent
+ *     conditions found on the device are OR-ed into the optional device word
+ *     `status` (ZIPCCL_STATUS_*); kernels never trap.
+ *   - BF16 pointers must be 16-byte aligned, static sections 128-byte aligned.
+ *   - One call may hold at most ZIPCCL_MAX_SEGMENTS segments and fewer than 2^32
+ *     values in total.
+ */
+#ifndef ZIPCCL_H
+#define ZIPCCL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZIPCCL_FORMAT_VERSION 1
+#define ZIPCCL_MAGIC 0x3143435Au
+#define ZIPCCL_MAX_SEGMENTS 64
+#define ZIPCCL_MAX_PEERS 16
+
+typedef enum zipccl_status {
+    ZIPCCL_OK = 0,
+    ZIPCCL_ERR_INVALID = 1,   /* bad argument: NULL pointer, bad sigma or table, nseg range */
+    ZIPCCL_ERR_ALIGN = 2,     /* a pointer is not aligned as required */
+    ZIPCCL_ERR_SIZE = 3,      /* a size limit is exceeded or a buffer is too small */
+    ZIPCCL_ERR_HIP = 4,       /* the HIP runtime reported an error */
+    ZIPCCL_ERR_CORRUPT = 5    /* a compressed header failed validation (host-side parse) */
+} zipccl_status;
+
+/* Bits OR-ed into the optional device status word. */
+#define ZIPCCL_STATUS_ESC_OVERFLOW 1u  /* escapes did not fit esc_cap; those past it were dropped */
+#define ZIPCCL_STATUS_CORRUPT 2u       /* decode: header or offset table inconsistent; not decoded */
+#define ZIPCCL_STATUS_SCAN_TIMEOUT 4u  /* compress: cross-workgroup escape scan gave up waiting */
+
+/* A coding plan: 7 distinct exponents in 1..254, ascending; code(table[r]) = r + 1. */
+typedef struct zipccl_plan_t {
+    uint8_t table[7];
+    uint8_t reserved; /* 0 */
+} zipccl_plan_t;
+
+/* One segment to compress: n BF16 values at src (device, 16-byte aligned). */
+typedef struct zipccl_segment_t {
+    const void* src;
+    uint64_t n;
+    zipccl_plan_t plan;
+} zipccl_segment_t;
+
+/* One segment to decompress: n values written to dst (device, 16-byte aligned). */
+typedef struct zipccl_dsegment_t {
+    void* dst;
+    uint64_t n;
+} zipccl_dsegment_t;
+
+/* Plan (S2.A).  With table7 == NULL: the 7 exponents whose binades hold the most
+ * mass of N(0, sigma^2), a contiguous window e0..e0+6 with
+ * e0 = 123 + floor(log2(sigma) - 0.7195805543641254) clamped to 1..248 (the phase
+ * constant is where the lowest and the next binade above the window carry equal
+ * mass).  sigma must be finite and > 0.  With table7 != NULL: those 7 exponents
+ * (distinct, 1..254) sorted ascending; sigma is ignored.  Host only.
+ * Returns ZIPCCL_ERR_INVALID on a bad sigma or table, or a NULL out. */
+zipccl_status zipccl_plan(double sigma, const uint8_t* table7, zipccl_plan_t* out);
+
+/* Bytes of the fixed-size part of one segment of n values (format above). */
+uint64_t zipccl_static_size(uint64_t n);
+
+/* static_size(n) + n_esc: the whole compressed size of one segment (S2.B: 11 bits per
+ * value plus 8 bits per escape plus metadata).  n_esc = n gives the worst case. */
+uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc);
+
+/* Device workspace bytes needed by zipccl_compress for up to nseg segments holding
+ * at most total_n values.  The workspace must be zero-filled before its first use and
+ * then handed to zipccl_compress only (it carries state from call to call).  Calls
+ * that share a workspace must be ordered on one stream.  Re-zero it after any failed
+ * or aborted call. */
+uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
+
+/* Compress nseg segments in one launch (S2.B, S2.C; two-phase layout of S2.D).
+ *   static_out  device, 128-byte aligned, static_cap bytes >= sum of static_size(n_s);
+ *               segment s is written at the sum of the static sizes before it.
+ *   esc_out     device, esc_cap bytes; escapes of segment s follow those of segments
+ *               0..s-1; header field esc_offset records where they start.  Escapes
+ *               beyond esc_cap are dropped and ZIPCCL_STATUS_ESC_OVERFLOW is set; the
+ *               headers still carry the true counts.
+ *   workspace   see zipccl_workspace_size.
+ *   n_esc_out   optional device u64[nseg + 1]: per-segment escape counts, then the total.
+ *   status      optional device u32, bits OR-ed in.
+ * Errors: INVALID (NULL pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS, bad table),
+ * ALIGN, SIZE (segment n >= 2^32, sum >= 2^32, static_cap or workspace too small),
+ * HIP (launch failure). */
+zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
+                              void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
+                              uint64_t* n_esc_out, uint32_t* status, void* stream);
+
+/* Decompress nseg segments whose static parts lie back to back at static_in (as
+ * zipccl_compress writes them; static_bytes = their total size) and whose escapes are
+ * in esc_in (esc_bytes long; each header's esc_offset is relative to it).  Exact
+ * inverse of zipccl_compress.  A segment whose header or offset table is inconsistent
+ * with segs[s].n or the buffer sizes is not decoded and ZIPCCL_STATUS_CORRUPT is set;
+ * no read leaves the given buffers.
+ * Errors: INVALID, ALIGN, SIZE (static_bytes smaller than the segments need), HIP. */
+zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, const void* esc_in,
+                                uint64_t esc_bytes, const zipccl_dsegment_t* segs, int nseg,
+                                uint32_t* status, void* stream);
+
+/* Reduce-scatter receive side (S2.D): for i < n
+ *   dst[i] = bf16_rne( (((f32(local[i]) + f32(peer_0[i])) + f32(peer_1[i])) + ...) )
+ * where peer_p is the one-segment compressed shard at static_in[p] with escapes in
+ * esc_in[p] (esc_bytes[p] long), each of n values; fp32 additions in peer order
+ * 0..npeers-1, round to nearest even, subnormals kept, one rounding to BF16 at the end
+ * (a NaN sum gives 0x7FC0).  static_in, esc_in and esc_bytes are host arrays of
+ * npeers entries (1..ZIPCCL_MAX_PEERS).  dst may equal local.  A corrupt shard sets
+ * ZIPCCL_STATUS_CORRUPT and its blocks are left unwritten.
+ * Errors: INVALID, ALIGN, SIZE (n >= 2^32), HIP. */
+zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const void* const* esc_in,
+                                           const uint64_t* esc_bytes, int npeers, uint64_t n,
+                                           const void* local, void* dst, uint32_t* status, void* stream);
+
+/* Chunked two-stream pipeline over a reduce-scatter receive share.  Chunks of `chunk`
+ * values of every peer shard are compressed on stream_a (one launch per chunk, one
+ * segment per peer) and decoded + accumulated into dst on stream_b (one launch per
+ * chunk); a ring of two compressed-chunk buffers lets chunk c+1 compress while chunk c
+ * is reduced.  The scratch memory is caller-owned device memory of
+ * zipccl_pipeline_scratch_size() bytes, zero-filled before first use.
+ * Overlapping transfers of the compressed chunks would sit between the two streams. */
+typedef struct zipccl_pipeline zipccl_pipeline;
+
+uint64_t zipccl_pipeline_scratch_size(int npeers, uint64_t chunk);
+
+/* Creates the host-side object (HIP events only; no device allocation).
+ * Errors: INVALID (npeers outside 1..ZIPCCL_MAX_PEERS, chunk 0 or not a multiple of
+ * 4096, chunk >= 2^32 / npeers, NULL out), ALIGN (scratch not 256-byte aligned),
+ * SIZE (scratch too small), HIP. */
+zipccl_status zipccl_pipeline_create(int npeers, uint64_t chunk, void* scratch, uint64_t scratch_bytes,
+                                     void* stream_a, void* stream_b, zipccl_pipeline** out);
+
+/* dst = bf16_rne(f32(local) + sum_p f32(peer_src[p])) over n values, through the
+ * codec, chunk by chunk.  peer_src is a host array of npeers device pointers; plans is
+ * a host array of npeers plans.  Inputs must be ready in stream_a's order; dst is
+ * complete in stream_b's order when the enqueued work finishes.  dst may equal local.
+ * Errors: INVALID, ALIGN, SIZE, HIP. */
+zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* peer_src,
+                                     const zipccl_plan_t* plans, uint64_t n, const void* local, void* dst,
+                                     uint32_t* status);
+
+void zipccl_pipeline_destroy(zipccl_pipeline* pipe);
+
+/* Static text for a status code. */
+const char* zipccl_strerror(zipccl_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZIPCCL_H */

@@ -1,0 +1,316 @@
+// Host layer of libzipccl: plans, sizes, argument validation, launches and the
+// two-stream chunk pipeline.  Every device-side step runs in zipccl_kernels.hip.
+//
+// Method: "ZipCCL: Efficient Lossless Data Compression of Communication Collectives
+// for Accelerating LLM Training" (gist.science explanation page), S2.A (sigma-derived
+// exponent table), S2.B (3-bit codes + escapes), S2.D (reduce-scatter local reduction).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "zipccl.h"
+#include "zipccl_internal.h"
+
+using namespace zc;
+
+namespace {
+
+// Where the window of 7 binades moves up by one: for log2(sigma) with fractional part
+// c the lowest binade of the window and the binade just above it hold equal Gaussian
+// mass.  Solved by bisection on 2[Phi(2^(k+1)/s) - Phi(2^k/s)] (continuous model).
+constexpr double kSwitchPhase = 0.7195805543641254;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+zipccl_status hip_status(hipError_t e) { return e == hipSuccess ? ZIPCCL_OK : ZIPCCL_ERR_HIP; }
+
+void pack_table(const zipccl_plan_t& p, uint32_t& lo, uint32_t& hi)
+{
+    lo = uint32_t(p.table[0]) | uint32_t(p.table[1]) << 8 | uint32_t(p.table[2]) << 16 | uint32_t(p.table[3]) << 24;
+    hi = uint32_t(p.table[4]) | uint32_t(p.table[5]) << 8 | uint32_t(p.table[6]) << 16;
+}
+
+bool plan_valid(const zipccl_plan_t& p)
+{
+    for (int r = 0; r < 7; r++) {
+        if (p.table[r] < 1 || p.table[r] > 254) return false;
+        if (r > 0 && p.table[r] <= p.table[r - 1]) return false;   // strictly ascending
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zipccl_strerror(zipccl_status s)
+{
+    switch (s) {
+        case ZIPCCL_OK: return "ok";
+        case ZIPCCL_ERR_INVALID: return "invalid argument";
+        case ZIPCCL_ERR_ALIGN: return "misaligned pointer";
+        case ZIPCCL_ERR_SIZE: return "size limit exceeded or buffer too small";
+        case ZIPCCL_ERR_HIP: return "HIP runtime error";
+        case ZIPCCL_ERR_CORRUPT: return "corrupt compressed data";
+    }
+    return "unknown status";
+}
+
+zipccl_status zipccl_plan(double sigma, const uint8_t* table7, zipccl_plan_t* out)
+{
+    if (!out) return ZIPCCL_ERR_INVALID;
+    zipccl_plan_t p{};
+    if (table7) {
+        uint8_t t[7];
+        std::memcpy(t, table7, 7);
+        std::sort(t, t + 7);
+        std::memcpy(p.table, t, 7);
+        if (!plan_valid(p)) return ZIPCCL_ERR_INVALID;   // also rejects duplicates
+    } else {
+        if (!(sigma > 0.0) || !std::isfinite(sigma)) return ZIPCCL_ERR_INVALID;
+        double e0 = 123.0 + std::floor(std::log2(sigma) - kSwitchPhase);
+        e0 = std::min(248.0, std::max(1.0, e0));
+        for (int r = 0; r < 7; r++) p.table[r] = uint8_t(int(e0) + r);
+    }
+    *out = p;
+    return ZIPCCL_OK;
+}
+
+uint64_t zipccl_static_size(uint64_t n) { return static_bytes_of(n); }
+
+uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc) { return static_bytes_of(n) + n_esc; }
+
+uint64_t zipccl_workspace_size(uint64_t total_n, int nseg)
+{
+    if (nseg < 1) nseg = 1;
+    uint64_t units = total_n / kUnit + uint64_t(nseg);
+    return kWsHeaderBytes + kWsSegBytes + 8 * units;
+}
+
+zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
+                              void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
+                              uint64_t* n_esc_out, uint32_t* status, void* stream)
+{
+    if (!segs || nseg < 1 || nseg > kMaxSegs || !static_out || !workspace) return ZIPCCL_ERR_INVALID;
+    if (!aligned(static_out, 128) || !aligned(workspace, 8) || (n_esc_out && !aligned(n_esc_out, 8)) ||
+        (status && !aligned(status, 4)))
+        return ZIPCCL_ERR_ALIGN;
+    CArgs a;
+    std::memset(&a, 0, sizeof(a));
+    uint64_t total = 0, units = 0, st_off = 0;
+    for (int s = 0; s < nseg; s++) {
+        const zipccl_segment_t& g = segs[s];
+        if (g.n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+        if (g.n > 0 && !g.src) return ZIPCCL_ERR_INVALID;
+        if (!aligned(g.src, 16)) return ZIPCCL_ERR_ALIGN;
+        if (!plan_valid(g.plan)) return ZIPCCL_ERR_INVALID;
+        CSeg& c = a.seg[s];
+        c.src = static_cast<const uint16_t*>(g.src);
+        c.dst = static_cast<uint8_t*>(static_out) + st_off;
+        c.n = uint32_t(g.n);
+        c.unit0 = uint32_t(units);
+        pack_table(g.plan, c.table_lo, c.table_hi);
+        total += g.n;
+        units += units_of(g.n);
+        st_off += static_bytes_of(g.n);
+    }
+    if (total >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+    if (st_off > static_cap) return ZIPCCL_ERR_SIZE;
+    if (kWsHeaderBytes + kWsSegBytes + 8 * units > workspace_bytes) return ZIPCCL_ERR_SIZE;
+    if (esc_cap > 0 && !esc_out) return ZIPCCL_ERR_INVALID;
+    a.esc = static_cast<uint8_t*>(esc_out);
+    a.esc_cap = esc_out ? esc_cap : 0;
+    a.ws = static_cast<uint32_t*>(workspace);
+    a.n_esc_out = n_esc_out;
+    a.status = status;
+    a.nseg = nseg;
+    a.total_units = uint32_t(units);
+    return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)));
+}
+
+zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, const void* esc_in,
+                                uint64_t esc_bytes, const zipccl_dsegment_t* segs, int nseg, uint32_t* status,
+                                void* stream)
+{
+    if (!segs || nseg < 1 || nseg > kMaxSegs || !static_in) return ZIPCCL_ERR_INVALID;
+    if (!aligned(static_in, 128) || (status && !aligned(status, 4))) return ZIPCCL_ERR_ALIGN;
+    DArgs a;
+    std::memset(&a, 0, sizeof(a));
+    uint64_t units = 0, st_off = 0;
+    for (int s = 0; s < nseg; s++) {
+        const zipccl_dsegment_t& g = segs[s];
+        if (g.n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+        if (g.n > 0 && !g.dst) return ZIPCCL_ERR_INVALID;
+        if (!aligned(g.dst, 16)) return ZIPCCL_ERR_ALIGN;
+        DSeg& d = a.seg[s];
+        d.src = static_cast<const uint8_t*>(static_in) + st_off;
+        d.dst = static_cast<uint16_t*>(g.dst);
+        d.n = uint32_t(g.n);
+        d.unit0 = uint32_t(units);
+        units += units_of(g.n);
+        st_off += static_bytes_of(g.n);
+    }
+    if (st_off > static_bytes) return ZIPCCL_ERR_SIZE;
+    if (units >= (1ull << 31)) return ZIPCCL_ERR_SIZE;
+    if (esc_bytes > 0 && !esc_in) return ZIPCCL_ERR_INVALID;
+    // with no escape buffer no escape is ever read; any device address will do
+    a.esc = static_cast<const uint8_t*>(esc_in ? esc_in : static_in);
+    a.esc_bytes = esc_in ? esc_bytes : 0;
+    a.status = status;
+    a.nseg = nseg;
+    a.total_units = uint32_t(units);
+    return hip_status(launch_decompress(a, static_cast<hipStream_t>(stream)));
+}
+
+zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const void* const* esc_in,
+                                           const uint64_t* esc_bytes, int npeers, uint64_t n, const void* local,
+                                           void* dst, uint32_t* status, void* stream)
+{
+    if (npeers < 1 || npeers > kMaxPeers || !static_in || !esc_in || !esc_bytes) return ZIPCCL_ERR_INVALID;
+    if (n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+    if (n > 0 && (!local || !dst)) return ZIPCCL_ERR_INVALID;
+    if (!aligned(local, 16) || !aligned(dst, 16) || (status && !aligned(status, 4))) return ZIPCCL_ERR_ALIGN;
+    AArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int p = 0; p < npeers; p++) {
+        if (!static_in[p]) return ZIPCCL_ERR_INVALID;
+        if (!aligned(static_in[p], 128)) return ZIPCCL_ERR_ALIGN;
+        if (esc_bytes[p] > 0 && !esc_in[p]) return ZIPCCL_ERR_INVALID;
+        a.st[p] = static_cast<const uint8_t*>(static_in[p]);
+        a.esc[p] = static_cast<const uint8_t*>(esc_in[p] ? esc_in[p] : static_in[p]);
+        a.esc_bytes[p] = esc_in[p] ? esc_bytes[p] : 0;
+    }
+    a.local = static_cast<const uint16_t*>(local);
+    a.dst = static_cast<uint16_t*>(dst);
+    a.status = status;
+    a.n = uint32_t(n);
+    a.npeers = npeers;
+    return hip_status(launch_accumulate(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------------
+// two-stream chunk pipeline
+// ---------------------------------------------------------------------------------
+struct zipccl_pipeline {
+    int npeers;
+    uint64_t chunk;
+    uint8_t* scratch;
+    uint64_t slot_static, slot_esc, ws_bytes;   // bytes per ring slot and of the workspace
+    hipStream_t sa, sb;
+    hipEvent_t compressed[2], reduced[2];
+    bool reduced_recorded[2];
+};
+
+namespace {
+
+void pipeline_layout(int npeers, uint64_t chunk, uint64_t& slot_static, uint64_t& slot_esc, uint64_t& ws)
+{
+    slot_static = uint64_t(npeers) * static_bytes_of(chunk);
+    slot_esc = (uint64_t(npeers) * chunk + 255) & ~uint64_t(255);
+    ws = (zipccl_workspace_size(uint64_t(npeers) * chunk, npeers) + 255) & ~uint64_t(255);
+}
+
+}  // namespace
+
+uint64_t zipccl_pipeline_scratch_size(int npeers, uint64_t chunk)
+{
+    if (npeers < 1 || npeers > kMaxPeers || chunk == 0) return 0;
+    uint64_t ss, se, ws;
+    pipeline_layout(npeers, chunk, ss, se, ws);
+    return ws + 2 * (ss + se);
+}
+
+zipccl_status zipccl_pipeline_create(int npeers, uint64_t chunk, void* scratch, uint64_t scratch_bytes,
+                                     void* stream_a, void* stream_b, zipccl_pipeline** out)
+{
+    if (!out || npeers < 1 || npeers > kMaxPeers || chunk == 0 || chunk % kBlock != 0 || !scratch)
+        return ZIPCCL_ERR_INVALID;
+    if (chunk * uint64_t(npeers) >= (1ull << 32)) return ZIPCCL_ERR_INVALID;
+    if (!aligned(scratch, 256)) return ZIPCCL_ERR_ALIGN;
+    if (scratch_bytes < zipccl_pipeline_scratch_size(npeers, chunk)) return ZIPCCL_ERR_SIZE;
+    zipccl_pipeline* p = new (std::nothrow) zipccl_pipeline();
+    if (!p) return ZIPCCL_ERR_INVALID;
+    p->npeers = npeers;
+    p->chunk = chunk;
+    p->scratch = static_cast<uint8_t*>(scratch);
+    pipeline_layout(npeers, chunk, p->slot_static, p->slot_esc, p->ws_bytes);
+    p->sa = static_cast<hipStream_t>(stream_a);
+    p->sb = static_cast<hipStream_t>(stream_b);
+    for (int k = 0; k < 2; k++) {
+        p->reduced_recorded[k] = false;
+        if (hipEventCreateWithFlags(&p->compressed[k], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&p->reduced[k], hipEventDisableTiming) != hipSuccess) {
+            zipccl_pipeline_destroy(p);
+            return ZIPCCL_ERR_HIP;
+        }
+    }
+    *out = p;
+    return ZIPCCL_OK;
+}
+
+zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* peer_src,
+                                     const zipccl_plan_t* plans, uint64_t n, const void* local, void* dst,
+                                     uint32_t* status)
+{
+    if (!pipe || !peer_src || !plans) return ZIPCCL_ERR_INVALID;
+    if (n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+    if (n > 0 && (!local || !dst)) return ZIPCCL_ERR_INVALID;
+    if (!aligned(local, 16) || !aligned(dst, 16)) return ZIPCCL_ERR_ALIGN;
+    const int P = pipe->npeers;
+    for (int p = 0; p < P; p++) {
+        if (n > 0 && !peer_src[p]) return ZIPCCL_ERR_INVALID;
+        if (!aligned(peer_src[p], 16)) return ZIPCCL_ERR_ALIGN;
+        if (!plan_valid(plans[p])) return ZIPCCL_ERR_INVALID;
+    }
+    uint8_t* ws = pipe->scratch;
+    const uint64_t nchunks = (n + pipe->chunk - 1) / pipe->chunk;
+    for (uint64_t c = 0; c < nchunks; c++) {
+        const int slot = int(c & 1);
+        const uint64_t off = c * pipe->chunk;
+        const uint64_t m = std::min(pipe->chunk, n - off);
+        uint8_t* st = pipe->scratch + pipe->ws_bytes + uint64_t(slot) * (pipe->slot_static + pipe->slot_esc);
+        uint8_t* esc = st + pipe->slot_static;
+        if (pipe->reduced_recorded[slot] && hipStreamWaitEvent(pipe->sa, pipe->reduced[slot], 0) != hipSuccess)
+            return ZIPCCL_ERR_HIP;
+        zipccl_segment_t segs[kMaxPeers];
+        for (int p = 0; p < P; p++) {
+            segs[p].src = static_cast<const uint16_t*>(peer_src[p]) + off;
+            segs[p].n = m;
+            segs[p].plan = plans[p];
+        }
+        zipccl_status r = zipccl_compress(segs, P, st, pipe->slot_static, esc, pipe->slot_esc, ws, pipe->ws_bytes,
+                                          nullptr, status, pipe->sa);
+        if (r != ZIPCCL_OK) return r;
+        if (hipEventRecord(pipe->compressed[slot], pipe->sa) != hipSuccess) return ZIPCCL_ERR_HIP;
+        if (hipStreamWaitEvent(pipe->sb, pipe->compressed[slot], 0) != hipSuccess) return ZIPCCL_ERR_HIP;
+        const void* sin[kMaxPeers];
+        const void* ein[kMaxPeers];
+        uint64_t eb[kMaxPeers];
+        for (int p = 0; p < P; p++) {
+            sin[p] = st + uint64_t(p) * static_bytes_of(m);
+            ein[p] = esc;
+            eb[p] = pipe->slot_esc;
+        }
+        r = zipccl_decompress_accumulate(sin, ein, eb, P, m, static_cast<const uint16_t*>(local) + off,
+                                         static_cast<uint16_t*>(dst) + off, status, pipe->sb);
+        if (r != ZIPCCL_OK) return r;
+        if (hipEventRecord(pipe->reduced[slot], pipe->sb) != hipSuccess) return ZIPCCL_ERR_HIP;
+        pipe->reduced_recorded[slot] = true;
+    }
+    return ZIPCCL_OK;
+}
+
+void zipccl_pipeline_destroy(zipccl_pipeline* pipe)
+{
+    if (!pipe) return;
+    for (int k = 0; k < 2; k++) {
+        if (pipe->compressed[k]) (void)hipEventDestroy(pipe->compressed[k]);
+        if (pipe->reduced[k]) (void)hipEventDestroy(pipe->reduced[k]);
+    }
+    delete pipe;
+}
+
+}  // extern "C"

@@ -1,0 +1,259 @@
+"""Python binding of libzipccl (ctypes).  Argument marshalling only: every step of the
+codec runs in the library's HIP kernels; torch supplies device memory and streams.
+
+The names mirror the C ABI in include/zipccl.h.  There is no CPU fallback: if the
+library is not built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libzipccl.so")
+
+OK, ERR_INVALID, ERR_ALIGN, ERR_SIZE, ERR_HIP, ERR_CORRUPT = range(6)
+STATUS_ESC_OVERFLOW, STATUS_CORRUPT, STATUS_SCAN_TIMEOUT = 1, 2, 4
+MAX_SEGMENTS, MAX_PEERS = 64, 16
+FORMAT_VERSION, MAGIC = 1, 0x3143435A
+
+
+class PlanT(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_uint8 * 7), ("reserved", ctypes.c_uint8)]
+
+    @property
+    def exponents(self):
+        return list(self.table)
+
+    def __repr__(self):
+        return f"Plan({list(self.table)})"
+
+
+class SegmentT(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("n", ctypes.c_uint64), ("plan", PlanT)]
+
+
+class DSegmentT(ctypes.Structure):
+    _fields_ = [("dst", ctypes.c_void_p), ("n", ctypes.c_uint64)]
+
+
+class ZipcclError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = _lib.zipccl_strerror(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m lossless_bf16_exponent_codec_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, u64, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int
+    lib.zipccl_strerror.restype = ctypes.c_char_p
+    lib.zipccl_strerror.argtypes = [i32]
+    lib.zipccl_plan.restype = i32
+    lib.zipccl_plan.argtypes = [ctypes.c_double, ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(PlanT)]
+    lib.zipccl_static_size.restype = u64
+    lib.zipccl_static_size.argtypes = [u64]
+    lib.zipccl_compressed_size.restype = u64
+    lib.zipccl_compressed_size.argtypes = [u64, u64]
+    lib.zipccl_workspace_size.restype = u64
+    lib.zipccl_workspace_size.argtypes = [u64, i32]
+    lib.zipccl_compress.restype = i32
+    lib.zipccl_compress.argtypes = [ctypes.POINTER(SegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp, vp]
+    lib.zipccl_decompress.restype = i32
+    lib.zipccl_decompress.argtypes = [vp, u64, vp, u64, ctypes.POINTER(DSegmentT), i32, vp, vp]
+    lib.zipccl_decompress_accumulate.restype = i32
+    lib.zipccl_decompress_accumulate.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64), i32,
+                                                 u64, vp, vp, vp, vp]
+    lib.zipccl_pipeline_scratch_size.restype = u64
+    lib.zipccl_pipeline_scratch_size.argtypes = [i32, u64]
+    lib.zipccl_pipeline_create.restype = i32
+    lib.zipccl_pipeline_create.argtypes = [i32, u64, vp, u64, vp, vp, ctypes.POINTER(vp)]
+    lib.zipccl_pipeline_reduce.restype = i32
+    lib.zipccl_pipeline_reduce.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(PlanT), u64, vp, vp, vp]
+    lib.zipccl_pipeline_destroy.restype = None
+    lib.zipccl_pipeline_destroy.argtypes = [vp]
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise ZipcclError(rc, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+# ------------------------------------------------------------------------------------
+# C ABI mirrors
+# ------------------------------------------------------------------------------------
+def plan(sigma: float | None = None, table=None) -> PlanT:
+    """zipccl_plan: sigma -> 7-exponent window, or a given table (sorted)."""
+    out = PlanT()
+    if table is not None:
+        arr = (ctypes.c_uint8 * 7)(*[int(v) for v in table]) if len(table) == 7 else None
+        if arr is None:
+            raise ZipcclError(ERR_INVALID, "zipccl_plan")
+        _check(_lib.zipccl_plan(0.0, arr, ctypes.byref(out)), "zipccl_plan")
+    else:
+        _check(_lib.zipccl_plan(float(sigma), None, ctypes.byref(out)), "zipccl_plan")
+    return out
+
+
+def static_size(n: int) -> int:
+    return int(_lib.zipccl_static_size(n))
+
+
+def compressed_size(n: int, n_esc: int) -> int:
+    return int(_lib.zipccl_compressed_size(n, n_esc))
+
+
+def workspace_size(total_n: int, nseg: int) -> int:
+    return int(_lib.zipccl_workspace_size(total_n, nseg))
+
+
+def compress(segments, static_out, esc_out, workspace, n_esc_out=None, status=None, stream=None,
+             esc_cap: int | None = None):
+    """zipccl_compress.  segments: list of (bf16 device tensor, PlanT)."""
+    nseg = len(segments)
+    arr = (SegmentT * max(nseg, 1))()
+    for k, (t, p) in enumerate(segments):
+        arr[k].src = _ptr(t) if t.numel() else None
+        arr[k].n = t.numel()
+        arr[k].plan = p
+    cap = _nbytes(esc_out) if esc_cap is None else esc_cap
+    rc = _lib.zipccl_compress(arr, nseg, _ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap,
+                              _ptr(workspace), _nbytes(workspace), _ptr(n_esc_out), _ptr(status), _stream(stream))
+    _check(rc, "zipccl_compress")
+
+
+def decompress(static_in, esc_in, dsts, status=None, stream=None, static_bytes=None, esc_bytes=None):
+    """zipccl_decompress.  dsts: list of bf16 device tensors (their numel is n)."""
+    nseg = len(dsts)
+    arr = (DSegmentT * max(nseg, 1))()
+    for k, t in enumerate(dsts):
+        arr[k].dst = _ptr(t) if t.numel() else None
+        arr[k].n = t.numel()
+    sb = _nbytes(static_in) if static_bytes is None else static_bytes
+    eb = (_nbytes(esc_in) if esc_in is not None else 0) if esc_bytes is None else esc_bytes
+    rc = _lib.zipccl_decompress(_ptr(static_in), sb, _ptr(esc_in), eb, arr, nseg, _ptr(status), _stream(stream))
+    _check(rc, "zipccl_decompress")
+
+
+def decompress_accumulate(static_ins, esc_ins, n: int, local, dst, status=None, stream=None, esc_bytes=None):
+    """zipccl_decompress_accumulate.  static_ins / esc_ins: per-peer device tensors or
+    raw device addresses (int); esc_bytes: per-peer escape buffer sizes."""
+    P = len(static_ins)
+    sp = (ctypes.c_void_p * P)(*[_ptr(t) for t in static_ins])
+    ep = (ctypes.c_void_p * P)(*[_ptr(t) for t in esc_ins])
+    if esc_bytes is None:
+        esc_bytes = [_nbytes(t) for t in esc_ins]
+    eb = (ctypes.c_uint64 * P)(*[int(v) for v in esc_bytes])
+    rc = _lib.zipccl_decompress_accumulate(sp, ep, eb, P, n, _ptr(local), _ptr(dst), _ptr(status), _stream(stream))
+    _check(rc, "zipccl_decompress_accumulate")
+
+
+def pipeline_scratch_size(npeers: int, chunk: int) -> int:
+    return int(_lib.zipccl_pipeline_scratch_size(npeers, chunk))
+
+
+class Pipeline:
+    """zipccl_pipeline_*: chunked compress (stream_a) -> decode-accumulate (stream_b)."""
+
+    def __init__(self, npeers: int, chunk: int, stream_a, stream_b, device=None):
+        self.npeers, self.chunk = npeers, chunk
+        size = pipeline_scratch_size(npeers, chunk)
+        self.scratch = torch.zeros(size, dtype=torch.uint8, device=device or "cuda")
+        h = ctypes.c_void_p()
+        rc = _lib.zipccl_pipeline_create(npeers, chunk, _ptr(self.scratch), size, _stream(stream_a),
+                                         _stream(stream_b), ctypes.byref(h))
+        _check(rc, "zipccl_pipeline_create")
+        self._h = h
+        self.stream_a, self.stream_b = stream_a, stream_b
+
+    def reduce(self, peer_src, plans, local, dst, status=None):
+        P = self.npeers
+        sp = (ctypes.c_void_p * P)(*[_ptr(t) for t in peer_src])
+        pl = (PlanT * P)(*plans)
+        rc = _lib.zipccl_pipeline_reduce(self._h, sp, pl, local.numel(), _ptr(local), _ptr(dst), _ptr(status))
+        _check(rc, "zipccl_pipeline_reduce")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.zipccl_pipeline_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+# ------------------------------------------------------------------------------------
+# convenience: buffers from torch, one call each way
+# ------------------------------------------------------------------------------------
+@dataclass
+class Compressed:
+    static: torch.Tensor        # uint8, segments back to back
+    esc: torch.Tensor           # uint8, escape capacity
+    n_esc: torch.Tensor         # uint64 as int64, nseg + 1 entries (last = total)
+    sizes: list                 # n of each segment
+    status: torch.Tensor        # int32 device status word
+
+    def static_sizes(self):
+        return [static_size(n) for n in self.sizes]
+
+
+def _as_bf16(t):
+    return t if t.dtype == torch.bfloat16 else t.view(torch.bfloat16)
+
+
+def compress_tensors(tensors, plans, esc_cap=None, workspace=None, stream=None) -> Compressed:
+    """Allocates outputs with torch and compresses the tensors in one launch."""
+    dev = tensors[0].device
+    sizes = [t.numel() for t in tensors]
+    total_static = sum(static_size(n) for n in sizes)
+    static = torch.empty(max(total_static, 1), dtype=torch.uint8, device=dev)
+    cap = sum(sizes) if esc_cap is None else esc_cap
+    esc = torch.empty(max(cap, 1), dtype=torch.uint8, device=dev)
+    n_esc = torch.zeros(len(tensors) + 1, dtype=torch.int64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.zeros(workspace_size(sum(sizes), len(tensors)), dtype=torch.uint8, device=dev)
+    compress([(_as_bf16(t), p) for t, p in zip(tensors, plans)], static, esc, workspace, n_esc, status,
+             stream=stream, esc_cap=cap)
+    return Compressed(static, esc, n_esc, sizes, status)
+
+
+def decompress_tensors(c: Compressed, out=None, stream=None):
+    dev = c.static.device
+    if out is None:
+        out = [torch.empty(n, dtype=torch.bfloat16, device=dev) for n in c.sizes]
+    decompress(c.static, c.esc, out, c.status, stream=stream)
+    return out

@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol,
+and its host-only functions (plan, sizes, argument validation) agree with the oracle.
+No compute call touches a GPU here."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zipccl.h")
+
+
+@pytest.fixture(scope="module")
+def Z():
+    from lossless_bf16_exponent_codec_amd import zipccl
+    return zipccl
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zipccl_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for want in ["zipccl_plan", "zipccl_compress", "zipccl_decompress", "zipccl_decompress_accumulate",
+                 "zipccl_compressed_size", "zipccl_static_size", "zipccl_workspace_size",
+                 "zipccl_pipeline_create", "zipccl_pipeline_reduce", "zipccl_pipeline_destroy",
+                 "zipccl_pipeline_scratch_size", "zipccl_strerror"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(Z):
+    out = subprocess.run(["nm", "-D", "--defined-only", Z.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (zipccl_\w+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    for f in declared_functions():
+        assert hasattr(Z.lib(), f)
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "zipccl.h"\nint main(void){zipccl_plan_t p; (void)p; return 0;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-c",
+                    str(src), "-o", str(tmp_path / "t.o")], check=True)
+
+
+def _phase(s):
+    f = math.log2(s)
+    return f - math.floor(f)
+
+
+def test_closed_form_plan_equals_oracle_ranking(Z):
+    # the library's closed form against the oracle's ranking of all 254 binade masses
+    rng = np.random.default_rng(1)
+    sig = 2.0 ** rng.uniform(-140, 140, 20000)
+    sig = np.concatenate([sig, [0.02, 1e-3, 0.5, 1.0, 1e-4, 0.1, 1e-45, 1e38, 3e38]])
+    checked = 0
+    for s in sig:
+        s = float(s)
+        ph = _phase(s)
+        if abs(ph - 0.7195805543641254) < 1e-9:
+            continue
+        assert Z.plan(sigma=s).exponents == list(O.plan_sigma(s)), s
+        checked += 1
+    assert checked > 19000
+
+
+def test_plan_check_values(Z):
+    assert Z.plan(sigma=0.02).exponents == list(range(116, 123))
+    assert Z.plan(sigma=1e-3).exponents == list(range(112, 119))
+    assert Z.plan(sigma=0.5).exponents == list(range(121, 128))
+    assert Z.plan(sigma=1.0).exponents == list(range(122, 129))
+
+
+def test_plan_table_and_errors(Z):
+    assert Z.plan(table=[9, 3, 7, 5, 1, 2, 200]).exponents == [1, 2, 3, 5, 7, 9, 200]
+    for bad in ([0, 1, 2, 3, 4, 5, 6], [1, 2, 3, 4, 5, 6, 255], [1, 1, 2, 3, 4, 5, 6]):
+        with pytest.raises(Z.ZipcclError) as e:
+            Z.plan(table=bad)
+        assert e.value.status == Z.ERR_INVALID
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(Z.ZipcclError):
+            Z.plan(sigma=bad)
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 511, 512, 513, 4095, 4096, 4097, 16384, 2 ** 22, 2 ** 26 + 3,
+                               2 ** 32 - 1])
+def test_sizes_match_oracle(Z, n):
+    assert Z.static_size(n) == O.static_size(n)
+    assert Z.compressed_size(n, 17) == O.static_size(n) + 17
+    assert Z.static_size(n) % 128 == 0
+
+
+def test_workspace_size_is_monotone(Z):
+    a = Z.workspace_size(1 << 20, 1)
+    assert Z.workspace_size(1 << 21, 1) > a and Z.workspace_size(1 << 20, 4) > a
+
+
+def test_argument_errors_before_any_launch(Z):
+    L = Z.lib()
+    p = Z.plan(sigma=1.0)
+    seg = (Z.SegmentT * 1)()
+    seg[0].src, seg[0].n, seg[0].plan = 0x10000, 100, p
+    fake = 0x100000                      # never dereferenced: every case fails validation first
+    ws = Z.workspace_size(100, 1)
+    assert L.zipccl_compress(seg, 0, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_INVALID
+    assert L.zipccl_compress(seg, 65, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_INVALID
+    assert L.zipccl_compress(seg, 1, fake + 64, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_ALIGN
+    seg[0].src = 0x10002
+    assert L.zipccl_compress(seg, 1, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_ALIGN
+    seg[0].src = 0x10000
+    assert L.zipccl_compress(seg, 1, fake, 10, fake, 100, fake, ws, None, None, None) == Z.ERR_SIZE
+    assert L.zipccl_compress(seg, 1, fake, 1 << 20, fake, 100, fake, 8, None, None, None) == Z.ERR_SIZE
+    seg[0].n = 1 << 32
+    assert L.zipccl_compress(seg, 1, fake, 1 << 40, fake, 100, fake, 1 << 30, None, None, None) == Z.ERR_SIZE
+    seg[0].n = 100
+    seg[0].plan.table[3] = seg[0].plan.table[2]
+    assert L.zipccl_compress(seg, 1, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_INVALID
+    d = (Z.DSegmentT * 1)()
+    d[0].dst, d[0].n = 0x10000, 5000
+    assert L.zipccl_decompress(fake, 100, fake, 10, d, 1, None, None) == Z.ERR_SIZE
+    assert L.zipccl_decompress(fake + 8, 1 << 20, fake, 10, d, 1, None, None) == Z.ERR_ALIGN
+    d[0].dst = 0x10001
+    assert L.zipccl_decompress(fake, 1 << 20, fake, 10, d, 1, None, None) == Z.ERR_ALIGN
+    vp = ctypes.c_void_p
+    sp = (vp * 1)(fake)
+    ep = (vp * 1)(fake)
+    eb = (ctypes.c_uint64 * 1)(10)
+    assert L.zipccl_decompress_accumulate(sp, ep, eb, 0, 10, fake, fake, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_accumulate(sp, ep, eb, 17, 10, fake, fake, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_accumulate(sp, ep, eb, 1, 1 << 32, fake, fake, None, None) == Z.ERR_SIZE
+    assert L.zipccl_decompress_accumulate(sp, ep, eb, 1, 10, fake + 2, fake, None, None) == Z.ERR_ALIGN
+    h = vp()
+    assert L.zipccl_pipeline_create(7, 1000, fake, 1 << 30, None, None, ctypes.byref(h)) == Z.ERR_INVALID
+    assert L.zipccl_pipeline_create(7, 4096, fake + 16, 1 << 30, None, None, ctypes.byref(h)) == Z.ERR_ALIGN
+    assert L.zipccl_pipeline_create(7, 4096, fake, 16, None, None, ctypes.byref(h)) == Z.ERR_SIZE
+    assert L.zipccl_strerror(Z.ERR_CORRUPT) == b"corrupt compressed data"

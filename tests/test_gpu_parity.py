@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, byte for byte.
+
+Compressed static bytes, escape bytes, per-segment escape counts and decoded tensors
+must be identical to the oracle's on the same seeded inputs; decode-accumulate is
+bit-exact too.  Outputs are pre-filled with 0xAA so that an unwritten byte shows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from lossless_bf16_exponent_codec_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0xAA
+POISON16 = 0xAAAA - 0x10000      # the 0xAAAA pattern as int16
+
+
+@pytest.fixture(scope="module")
+def Z():
+    from lossless_bf16_exponent_codec_amd import zipccl
+    return zipccl
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_compress(Z, segs, plans, esc_cap=None, workspace=None, poison=True):
+    tens = [dev_bf16(s) for s in segs]
+    sizes = [s.size for s in segs]
+    total_static = sum(Z.static_size(n) for n in sizes)
+    static = torch.full((max(total_static, 1),), POISON, dtype=torch.uint8, device="cuda")
+    cap = sum(sizes) if esc_cap is None else esc_cap
+    esc = torch.full((max(cap, 1),), POISON, dtype=torch.uint8, device="cuda")
+    n_esc = torch.full((len(segs) + 1,), -1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if workspace is None:
+        workspace = torch.zeros(Z.workspace_size(sum(sizes), len(segs)), dtype=torch.uint8, device="cuda")
+    Z.compress(list(zip(tens, plans)), static, esc, workspace, n_esc, status, esc_cap=cap)
+    torch.cuda.synchronize()
+    ne = n_esc.cpu().numpy()
+    return dict(static=static, esc=esc, n_esc=ne, status=int(status.item()), sizes=sizes,
+                static_h=static.cpu().numpy()[:total_static], esc_h=esc.cpu().numpy())
+
+
+def oracle_tables(plans):
+    return [np.array(p.exponents, np.uint8) for p in plans]
+
+
+def check_against_oracle(Z, segs, plans, r):
+    st, esc, ne, rc = O.compress_batch(segs, oracle_tables(plans))
+    assert r["status"] == 0
+    assert list(r["n_esc"][:-1]) == ne
+    assert int(r["n_esc"][-1]) == sum(ne)
+    assert np.array_equal(r["static_h"], st), first_diff(r["static_h"], st)
+    assert np.array_equal(r["esc_h"][:sum(ne)], esc)
+    return st, esc, ne
+
+
+def first_diff(a, b):
+    if a.shape != b.shape:
+        return f"shape {a.shape} vs {b.shape}"
+    d = np.nonzero(a != b)[0]
+    return f"{d.size} bytes differ, first at {d[0]}: {a[d[0]]:#x} vs {b[d[0]]:#x}" if d.size else "equal"
+
+
+def gpu_decompress(Z, r, poison=True):
+    outs = [torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            for n in r["sizes"]]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Z.decompress(r["static"], r["esc"], outs, status)
+    torch.cuda.synchronize()
+    return [host_u16(o) for o in outs], int(status.item())
+
+
+def round_trip(Z, segs, plans):
+    r = gpu_compress(Z, segs, plans)
+    check_against_oracle(Z, segs, plans, r)
+    outs, status = gpu_decompress(Z, r)
+    assert status == 0
+    for x, y in zip(segs, outs):
+        assert np.array_equal(x, y), first_diff(x, y)
+    return r
+
+
+# ------------------------------------------------------------------------------------
+def test_worked_example(Z):
+    x = np.array([0x3F80, 0xBF00, 0x4040, 0x0000, 0x42C8, 0x7FC0, 0x3D00, 0x3C80], np.uint16)
+    r = round_trip(Z, [x], [Z.plan(sigma=1.0)])
+    assert r["static_h"].size == 1024 and list(r["esc_h"][:4]) == [0x00, 0x85, 0xFF, 0x79]
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 63, 64, 511, 512, 513, 4095, 4096, 4097, 16383, 16384, 16385,
+                               65536 + 7, 100003])
+def test_edge_sizes_random_bits(Z, n):
+    rng = np.random.default_rng(1000 + n)
+    x = rng.integers(0, 65536, n, dtype=np.uint32).astype(np.uint16)
+    round_trip(Z, [x], [Z.plan(sigma=0.02)])
+
+
+@pytest.mark.parametrize("n", [1, 513, 4097, 16385, 250001])
+def test_edge_sizes_gaussian(Z, n):
+    round_trip(Z, [W.gaussian_bf16(n, 0.7, n)], [Z.plan(sigma=0.7)])
+
+
+def test_exhaustive_patterns(Z):
+    all16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = np.concatenate([np.roll(all16, s) for s in range(8)] + [all16[:517]])
+    plans = [Z.plan(sigma=1.0), Z.plan(table=[1, 2, 3, 4, 5, 6, 7]), Z.plan(table=[248, 249, 250, 251, 252, 253, 254]),
+             Z.plan(table=[3, 77, 120, 128, 129, 200, 254])]
+    for p in plans:
+        round_trip(Z, [x], [p])
+    # all four in one launch
+    round_trip(Z, [x, x[:70000], x[5:], x[:1]], plans)
+
+
+def test_no_escapes_and_all_escapes(Z):
+    p = Z.plan(sigma=1.0)
+    t = p.exponents
+    x = np.array([(e << 7) | (s << 15) | m for e in t for s in (0, 1) for m in (0, 5, 127)] * 3000, np.uint16)
+    r = round_trip(Z, [x], [p])
+    assert int(r["n_esc"][0]) == 0
+    r = round_trip(Z, [x], [Z.plan(table=[1, 2, 3, 4, 5, 6, 7])])
+    assert int(r["n_esc"][0]) == x.size
+
+
+def test_many_segments_one_launch(Z):
+    rng = np.random.default_rng(5)
+    segs, plans = [], []
+    for k in range(64):
+        n = int(rng.choice([0, 1, 700, 4096, 16384, 20000, 70001]))
+        s = float(10 ** rng.uniform(-4, 1))
+        segs.append(W.gaussian_bf16(n, s, 300 + k))
+        plans.append(Z.plan(sigma=s))
+    round_trip(Z, segs, plans)
+
+
+def test_determinism_and_workspace_reuse(Z):
+    ws = torch.zeros(Z.workspace_size(1 << 22, 64), dtype=torch.uint8, device="cuda")
+    x1 = [W.gaussian_bf16(1 << 20, 0.02, 1)]
+    x2 = [W.gaussian_bf16(n, 1e-3, 7 + n) for n in (1000, 300000, 0, 77777)]
+    p1 = [Z.plan(sigma=0.02)]
+    p2 = [Z.plan(sigma=1e-3)] * 4
+    first = None
+    for rep in range(6):
+        segs, plans = (x1, p1) if rep % 2 == 0 else (x2, p2)
+        r = gpu_compress(Z, segs, plans, workspace=ws)
+        check_against_oracle(Z, segs, plans, r)
+        if rep == 0:
+            first = r["static_h"].copy()
+        elif rep % 2 == 0:
+            assert np.array_equal(first, r["static_h"])
+    # the workspace counters are back at rest: ticket and finished counters are 0
+    w = ws[:16].cpu().numpy().view(np.uint32)
+    assert w[0] == 6 and w[1] == 0 and w[2] == 0
+
+
+def test_escape_overflow_sets_status(Z):
+    x = W.gaussian_bf16(50000, 1.0, 5)
+    p = Z.plan(table=[1, 2, 3, 4, 5, 6, 7])
+    r = gpu_compress(Z, [x], [p], esc_cap=1000)
+    assert r["status"] & Z.STATUS_ESC_OVERFLOW
+    st, esc, ne, rc = O.compress_batch([x], oracle_tables([p]))
+    assert int(r["n_esc"][0]) == 50000 and np.array_equal(r["static_h"], st)
+    assert np.array_equal(r["esc_h"][:1000], esc[:1000])
+
+
+def test_corrupt_header_is_reported_and_not_decoded(Z):
+    x = W.gaussian_bf16(20000, 0.5, 8)
+    r = gpu_compress(Z, [x], [Z.plan(sigma=0.5)])
+    r["static"][0] ^= 1
+    outs, status = gpu_decompress(Z, r)
+    assert status & Z.STATUS_CORRUPT
+    assert (outs[0] == POISON * 257).all()
+    r["static"][0] ^= 1
+    # escape buffer too small for the header's escape range
+    outs = [torch.zeros(20000, dtype=torch.bfloat16, device="cuda")]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Z.decompress(r["static"], r["esc"], outs, status, esc_bytes=int(r["n_esc"][0]) - 1)
+    torch.cuda.synchronize()
+    assert int(status.item()) & Z.STATUS_CORRUPT
+
+
+# ------------------------------------------------------------------------------------
+# decode-accumulate
+# ------------------------------------------------------------------------------------
+def gpu_accumulate(Z, peer_bits, plans, local_bits, inplace=False):
+    n = local_bits.size
+    r = gpu_compress(Z, peer_bits, plans)
+    S = Z.static_size(n)
+    base = r["static"].data_ptr()
+    ins = [base + p * S for p in range(len(peer_bits))]
+    ebase = r["esc"].data_ptr()
+    local = dev_bf16(local_bits)
+    dst = local if inplace else torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Z.decompress_accumulate(ins, [ebase] * len(ins), n, local, dst, status,
+                            esc_bytes=[r["esc"].numel()] * len(ins))
+    torch.cuda.synchronize()
+    return host_u16(dst), int(status.item()), r
+
+
+def oracle_accumulate(Z, peer_bits, plans, local_bits):
+    comp = [O.compress(p, np.array(pl.exponents, np.uint8)) for p, pl in zip(peer_bits, plans)]
+    return O.decompress_accumulate([c[0] for c in comp], [c[1] for c in comp], local_bits.size, local_bits)
+
+
+@pytest.mark.parametrize("n,npeers", [(1, 1), (4097, 7), (16385, 3), (100000, 7), (262144, 16), (70001, 2)])
+def test_accumulate_matches_oracle(Z, n, npeers):
+    peers = [W.gaussian_bf16(n, 1e-3, 500 + p) for p in range(npeers)]
+    local = W.gaussian_bf16(n, 1e-3, 600)
+    plans = [Z.plan(sigma=1e-3)] * npeers
+    got, status, _ = gpu_accumulate(Z, peers, plans, local)
+    assert status == 0
+    want = oracle_accumulate(Z, peers, plans, local)
+    assert np.array_equal(got, want), first_diff(got, want)
+
+
+def test_accumulate_in_place(Z):
+    n = 50000
+    peers = [W.gaussian_bf16(n, 0.3, 20 + p) for p in range(7)]
+    local = W.gaussian_bf16(n, 0.3, 30)
+    plans = [Z.plan(sigma=0.3)] * 7
+    got, status, _ = gpu_accumulate(Z, peers, plans, local, inplace=True)
+    assert status == 0 and np.array_equal(got, oracle_accumulate(Z, peers, plans, local))
+
+
+def test_accumulate_special_values(Z):
+    # subnormals (no flush), signed zeros, infinities, NaNs, overflow and exact ties
+    rng = np.random.default_rng(9)
+    n = 3 * 4096 + 99
+    specials = np.array([0x0001, 0x8001, 0x007F, 0x8000, 0x0000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F7F,
+                         0xFF7F, 0x3F80, 0x3B80, 0x3F81, 0x0080, 0x8080], np.uint16)
+    peers = [specials[rng.integers(0, specials.size, n)] for _ in range(5)]
+    local = specials[rng.integers(0, specials.size, n)]
+    plans = [Z.plan(sigma=1.0), Z.plan(table=[1, 2, 3, 4, 5, 6, 7]), Z.plan(sigma=1e-38),
+             Z.plan(table=[120, 121, 122, 123, 124, 125, 127]), Z.plan(sigma=1e30)]
+    got, status, _ = gpu_accumulate(Z, peers, plans, local)
+    assert status == 0
+    want = oracle_accumulate(Z, peers, plans, local)
+    assert np.array_equal(got, want), first_diff(got, want)
+    two = np.array([0x0001] * 8, np.uint16)
+    got, _, _ = gpu_accumulate(Z, [two], [Z.plan(sigma=1.0)], two)
+    assert (got == 0x0002).all()
+
+
+def test_accumulate_corrupt_peer(Z):
+    n = 9000
+    peers = [W.gaussian_bf16(n, 0.1, 40 + p) for p in range(3)]
+    local = W.gaussian_bf16(n, 0.1, 50)
+    plans = [Z.plan(sigma=0.1)] * 3
+    r = gpu_compress(Z, peers, plans)
+    S = Z.static_size(n)
+    r["static"][S + 8] ^= 4      # peer 1 header: n
+    dst = torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    base = r["static"].data_ptr()
+    Z.decompress_accumulate([base + p * S for p in range(3)], [r["esc"].data_ptr()] * 3, n, dev_bf16(local), dst,
+                            status, esc_bytes=[r["esc"].numel()] * 3)
+    torch.cuda.synchronize()
+    assert int(status.item()) & Z.STATUS_CORRUPT
