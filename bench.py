@@ -228,6 +228,24 @@ def bench_rs(torch, Z, W, iters):
     }
 
 
+def copy_ceiling(torch, iters=10):
+    """A plain 1 GiB device-to-device copy: the practical HBM ceiling (read + write bytes / s)."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    t = Timer(torch)
+    for _ in range(iters):
+        e = t.start()
+        b.copy_(a)
+        t.stop(e)
+    ms = median(t.ms())
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(W, O, wl, reps):
     import numpy as np
     tables = [O.plan_sigma(s) for s in wl.sigmas]
@@ -340,6 +358,9 @@ def main(argv=None) -> int:
                      "bytes_per_launch": moved, "avg_launch_us": round(c_avg * 1e3, 2),
                      "traffic": None},
     }
+    log("copy ceiling")
+    out["hbm_copy_GBps"] = copy_ceiling(torch)
+    out["roofline"]["frac_of_copy"] = round(out["roofline"]["achieved"] / out["hbm_copy_GBps"], 4)
     if not args.no_extra:
         per = {"bucket_64m": rep}
         for name in ("chunk_1m", "act_8192x7168", "moe_16384x7168"):

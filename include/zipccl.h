@@ -65,7 +65,6 @@ typedef enum zipccl_status {
 /* Bits OR-ed into the optional device status word. */
 #define ZIPCCL_STATUS_ESC_OVERFLOW 1u  /* escapes did not fit esc_cap; those past it were dropped */
 #define ZIPCCL_STATUS_CORRUPT 2u       /* decode: header or offset table inconsistent; not decoded */
-#define ZIPCCL_STATUS_SCAN_TIMEOUT 4u  /* compress: cross-workgroup escape scan gave up waiting */
 
 /* A coding plan: 7 distinct exponents in 1..254, ascending; code(table[r]) = r + 1. */
 typedef struct zipccl_plan_t {
@@ -103,10 +102,10 @@ uint64_t zipccl_static_size(uint64_t n);
 uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc);
 
 /* Device workspace bytes needed by zipccl_compress for up to nseg segments holding
- * at most total_n values.  The workspace must be zero-filled before its first use and
- * then handed to zipccl_compress only (it carries state from call to call).  Calls
- * that share a workspace must be ordered on one stream.  Re-zero it after any failed
- * or aborted call. */
+ * at most total_n values (about one byte per value: a 4-byte escape count and a
+ * 4096-byte escape staging slot per 4096-value block).  The workspace carries nothing
+ * from one call to the next and needs no initialisation; it must be 256-byte aligned.
+ * Calls that run concurrently need separate workspaces. */
 uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
 
 /* Compress nseg segments in one launch (S2.B, S2.C; two-phase layout of S2.D).
@@ -116,7 +115,10 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
  *               0..s-1; header field esc_offset records where they start.  Escapes
  *               beyond esc_cap are dropped and ZIPCCL_STATUS_ESC_OVERFLOW is set; the
  *               headers still carry the true counts.
- *   workspace   see zipccl_workspace_size.
+ *   workspace   device scratch, see zipccl_workspace_size.
+ * The work is two kernel launches on `stream`: the encode kernel writes the fixed-size
+ * sections and stages each block's escapes; the finalize kernel computes the escape
+ * positions, writes the offset tables and headers and compacts the escapes.
  *   n_esc_out   optional device u64[nseg + 1]: per-segment escape counts, then the total.
  *   status      optional device u32, bits OR-ed in.
  * Errors: INVALID (NULL pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS, bad table),
@@ -151,11 +153,11 @@ zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const v
                                            const void* local, void* dst, uint32_t* status, void* stream);
 
 /* Chunked two-stream pipeline over a reduce-scatter receive share.  Chunks of `chunk`
- * values of every peer shard are compressed on stream_a (one launch per chunk, one
- * segment per peer) and decoded + accumulated into dst on stream_b (one launch per
+ * values of every peer shard are compressed on stream_a (one compress call per chunk,
+ * one segment per peer) and decoded + accumulated into dst on stream_b (one launch per
  * chunk); a ring of two compressed-chunk buffers lets chunk c+1 compress while chunk c
  * is reduced.  The scratch memory is caller-owned device memory of
- * zipccl_pipeline_scratch_size() bytes, zero-filled before first use.
+ * zipccl_pipeline_scratch_size() bytes.
  * Overlapping transfers of the compressed chunks would sit between the two streams. */
 typedef struct zipccl_pipeline zipccl_pipeline;
 

@@ -86,8 +86,7 @@ uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc) { return static_byte
 uint64_t zipccl_workspace_size(uint64_t total_n, int nseg)
 {
     if (nseg < 1) nseg = 1;
-    uint64_t units = total_n / kUnit + uint64_t(nseg);
-    return kWsHeaderBytes + kWsSegBytes + 8 * units;
+    return ws_bytes(total_n / kBlock + uint64_t(nseg));   // bounds the sum of ceil(n_s / 4096)
 }
 
 zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
@@ -95,12 +94,12 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
                               uint64_t* n_esc_out, uint32_t* status, void* stream)
 {
     if (!segs || nseg < 1 || nseg > kMaxSegs || !static_out || !workspace) return ZIPCCL_ERR_INVALID;
-    if (!aligned(static_out, 128) || !aligned(workspace, 8) || (n_esc_out && !aligned(n_esc_out, 8)) ||
+    if (!aligned(static_out, 128) || !aligned(workspace, 256) || (n_esc_out && !aligned(n_esc_out, 8)) ||
         (status && !aligned(status, 4)))
         return ZIPCCL_ERR_ALIGN;
     CArgs a;
     std::memset(&a, 0, sizeof(a));
-    uint64_t total = 0, units = 0, st_off = 0;
+    uint64_t total = 0, units = 0, blocks = 0, st_off = 0;
     for (int s = 0; s < nseg; s++) {
         const zipccl_segment_t& g = segs[s];
         if (g.n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
@@ -112,22 +111,27 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
         c.dst = static_cast<uint8_t*>(static_out) + st_off;
         c.n = uint32_t(g.n);
         c.unit0 = uint32_t(units);
+        c.block0 = uint32_t(blocks);
         pack_table(g.plan, c.table_lo, c.table_hi);
         total += g.n;
         units += units_of(g.n);
+        blocks += blocks_of(g.n);
         st_off += static_bytes_of(g.n);
     }
     if (total >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
     if (st_off > static_cap) return ZIPCCL_ERR_SIZE;
-    if (kWsHeaderBytes + kWsSegBytes + 8 * units > workspace_bytes) return ZIPCCL_ERR_SIZE;
+    if (ws_bytes(blocks) > workspace_bytes) return ZIPCCL_ERR_SIZE;
     if (esc_cap > 0 && !esc_out) return ZIPCCL_ERR_INVALID;
     a.esc = static_cast<uint8_t*>(esc_out);
     a.esc_cap = esc_out ? esc_cap : 0;
-    a.ws = static_cast<uint32_t*>(workspace);
+    a.counts = static_cast<uint32_t*>(workspace);
+    a.pos = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + ws_counts_bytes(blocks));
+    a.stage = static_cast<uint8_t*>(workspace) + ws_counts_bytes(blocks) + ws_pos_bytes(blocks);
     a.n_esc_out = n_esc_out;
     a.status = status;
     a.nseg = nseg;
     a.total_units = uint32_t(units);
+    a.total_blocks = uint32_t(blocks);
     return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -154,7 +158,6 @@ zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, co
         st_off += static_bytes_of(g.n);
     }
     if (st_off > static_bytes) return ZIPCCL_ERR_SIZE;
-    if (units >= (1ull << 31)) return ZIPCCL_ERR_SIZE;
     if (esc_bytes > 0 && !esc_in) return ZIPCCL_ERR_INVALID;
     // with no escape buffer no escape is ever read; any device address will do
     a.esc = static_cast<const uint8_t*>(esc_in ? esc_in : static_in);
@@ -198,7 +201,7 @@ struct zipccl_pipeline {
     int npeers;
     uint64_t chunk;
     uint8_t* scratch;
-    uint64_t slot_static, slot_esc, ws_bytes;   // bytes per ring slot and of the workspace
+    uint64_t slot_static, slot_esc, ws_size;   // bytes per ring slot and of the workspace
     hipStream_t sa, sb;
     hipEvent_t compressed[2], reduced[2];
     bool reduced_recorded[2];
@@ -236,7 +239,7 @@ zipccl_status zipccl_pipeline_create(int npeers, uint64_t chunk, void* scratch, 
     p->npeers = npeers;
     p->chunk = chunk;
     p->scratch = static_cast<uint8_t*>(scratch);
-    pipeline_layout(npeers, chunk, p->slot_static, p->slot_esc, p->ws_bytes);
+    pipeline_layout(npeers, chunk, p->slot_static, p->slot_esc, p->ws_size);
     p->sa = static_cast<hipStream_t>(stream_a);
     p->sb = static_cast<hipStream_t>(stream_b);
     for (int k = 0; k < 2; k++) {
@@ -271,7 +274,7 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
         const int slot = int(c & 1);
         const uint64_t off = c * pipe->chunk;
         const uint64_t m = std::min(pipe->chunk, n - off);
-        uint8_t* st = pipe->scratch + pipe->ws_bytes + uint64_t(slot) * (pipe->slot_static + pipe->slot_esc);
+        uint8_t* st = pipe->scratch + pipe->ws_size + uint64_t(slot) * (pipe->slot_static + pipe->slot_esc);
         uint8_t* esc = st + pipe->slot_static;
         if (pipe->reduced_recorded[slot] && hipStreamWaitEvent(pipe->sa, pipe->reduced[slot], 0) != hipSuccess)
             return ZIPCCL_ERR_HIP;
@@ -281,7 +284,7 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
             segs[p].n = m;
             segs[p].plan = plans[p];
         }
-        zipccl_status r = zipccl_compress(segs, P, st, pipe->slot_static, esc, pipe->slot_esc, ws, pipe->ws_bytes,
+        zipccl_status r = zipccl_compress(segs, P, st, pipe->slot_static, esc, pipe->slot_esc, ws, pipe->ws_size,
                                           nullptr, status, pipe->sa);
         if (r != ZIPCCL_OK) return r;
         if (hipEventRecord(pipe->compressed[slot], pipe->sa) != hipSuccess) return ZIPCCL_ERR_HIP;

@@ -15,30 +15,41 @@ constexpr uint32_t kUnit = kBlock * kWaves;   // values per workgroup: one block
 constexpr int kMaxSegs = 64;
 constexpr int kMaxPeers = 16;
 
-// Workspace layout (32-bit words): [0] generation, [1] ticket counter, [2] finished
-// counter, [3] 0; then kMaxSegs u64 segment-base slots; then one u64 status word per
-// workgroup unit of the launch.
-constexpr uint64_t kWsHeaderBytes = 16;
-constexpr uint64_t kWsSegBytes = 8ull * kMaxSegs;
+// Compress workspace: a u32 escape count per block of the launch, the launch-wide
+// position of every block's first escape (one more entry for the total), then a
+// staging slot of kBlock bytes per block that holds the block's escape exponents
+// until their positions are known.
+__host__ __device__ inline uint64_t ws_counts_bytes(uint64_t blocks) { return (4 * blocks + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_pos_bytes(uint64_t blocks) { return (4 * (blocks + 1) + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_bytes(uint64_t blocks)
+{
+    return ws_counts_bytes(blocks) + ws_pos_bytes(blocks) + uint64_t(kBlock) * blocks;
+}
 
 struct CSeg {              // compress: one segment
     const uint16_t* src;   // n BF16 values
     uint8_t* dst;          // static part of this segment
     uint32_t n;
-    uint32_t unit0;        // first workgroup unit of the segment in launch order
+    uint32_t unit0;        // first encode workgroup of the segment (units of kUnit values)
+    uint32_t block0;       // first block of the segment in launch-wide block numbering
     uint32_t table_lo;     // table[0..3]
     uint32_t table_hi;     // table[4..6], byte 3 = 0
+    uint32_t pad;
 };
 
 struct CArgs {
     CSeg seg[kMaxSegs];
     uint8_t* esc;
     uint64_t esc_cap;
-    uint32_t* ws;
+    uint32_t* counts;      // workspace: escapes per block
+    uint32_t* pos;         // workspace: launch-wide position of each block's first escape
+    uint8_t* stage;        // workspace: kBlock bytes per block
     uint64_t* n_esc_out;   // nseg + 1 entries or null
     uint32_t* status;      // or null
     int32_t nseg;
     uint32_t total_units;
+    uint32_t total_blocks;
+    uint32_t pad;
 };
 
 struct DSeg {              // decompress: one segment
@@ -71,12 +82,12 @@ struct AArgs {             // decompress + accumulate
 __host__ __device__ inline uint64_t round128(uint64_t v) { return (v + 127) & ~uint64_t(127); }
 __host__ __device__ inline uint64_t tiles_of(uint64_t n) { return (n + kTile - 1) / kTile; }
 __host__ __device__ inline uint64_t blocks_of(uint64_t n) { return (n + kBlock - 1) / kBlock; }
-__host__ __device__ inline uint64_t units_of(uint64_t n) { return n == 0 ? 1 : (n + kUnit - 1) / kUnit; }
+__host__ __device__ inline uint64_t units_of(uint64_t n) { return (n + kUnit - 1) / kUnit; }
 __host__ __device__ inline uint64_t planes_off(uint64_t n) { return 128 + 512 * tiles_of(n); }
 __host__ __device__ inline uint64_t offsets_off(uint64_t n) { return planes_off(n) + round128(192 * tiles_of(n)); }
 __host__ __device__ inline uint64_t static_bytes_of(uint64_t n) { return offsets_off(n) + round128(4 * blocks_of(n)); }
 
-hipError_t launch_compress(const CArgs& a, hipStream_t s);
+hipError_t launch_compress(const CArgs& a, hipStream_t s);   // encode + finalize
 hipError_t launch_decompress(const DArgs& a, hipStream_t s);
 hipError_t launch_accumulate(const AArgs& a, hipStream_t s);
 

@@ -15,23 +15,23 @@
 //     them into one VGPR (lane k gets 32-bit half k) for a 192-byte vector store.
 //   * Escapes: per-column escape ballots, mbcnt gives each lane the number of escapes
 //     in lower lanes, the lane's own escapes follow in column order.  Escape bytes are
-//     staged in LDS per wave and copied out once the unit's global position is known.
-//   * The global escape position of each unit comes from a single-pass decoupled
-//     look-back scan (Merrill & Garland, "Single-pass Parallel Prefix Scan with
-//     Decoupled Look-back", 2016) over per-unit status words in the workspace.  Units
-//     are numbered by a ticket taken at workgroup start, so a unit only ever waits for
-//     units that are already running; every wait is bounded.
+//     staged in LDS per wave, then in a per-block slot of the workspace.
+//   * Compress is two launches.  The encode kernel has no dependency between
+//     workgroups: it writes A, B and a per-block escape count.  The finalize kernel
+//     (one workgroup per 256 blocks) sums the counts before its range, scans its own,
+//     writes the offset table, compacts the staged escapes and writes the headers.
+//     No workgroup ever waits for another, so there is no spin and no state kept in
+//     the workspace from one call to the next.
 #include "zipccl_internal.h"
 #include "zipccl.h"
+
+// llvm.amdgcn.writelane: the compiler knows this instruction, so it also inserts the
+// wait states its operands need (inline assembly would hide them from it).
+__device__ int zc_writelane(int src, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
 namespace zc {
 
 namespace {
-
-constexpr uint32_t kStAggregate = 1;   // status flag: the unit's own count is published
-constexpr uint32_t kStInclusive = 2;   // status flag: count including all earlier units
-constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr uint32_t kTagMask = (1u << 30) - 1;
 
 __device__ inline uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
@@ -49,10 +49,6 @@ __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return
 // mask as its SGPR-pair condition.
 __device__ inline uint32_t lane_select(uint64_t mask, uint32_t k) { return __builtin_amdgcn_inverse_ballot_w64(mask) ? k : 0u; }
 
-// llvm.amdgcn.writelane: the compiler knows this instruction, so it also inserts the
-// wait states its operands need (inline assembly would hide them from it).
-__device__ int zc_writelane(int src, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
-
 // Writes the wave-uniform value v into lane k of w (v_writelane_b32).
 template <int k>
 __device__ inline uint32_t write_lane(uint32_t w, uint32_t v)
@@ -60,19 +56,9 @@ __device__ inline uint32_t write_lane(uint32_t w, uint32_t v)
     return uint32_t(zc_writelane(int(v), k, int(w)));
 }
 
-__device__ inline uint64_t ld_agent(const uint64_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline void st_agent(uint64_t* p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline uint32_t ld_agent32(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline void st_agent32(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline uint32_t add_agent32(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ inline void or_status(uint32_t* s, uint32_t bits)
 {
     if (s) __hip_atomic_fetch_or(s, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline uint64_t pack_status(uint32_t tag, uint32_t flag, uint32_t value)
-{
-    return (uint64_t(tag) << 34) | (uint64_t(flag) << 32) | value;
 }
 
 __device__ inline uint32_t wave_sum(uint32_t v)
@@ -82,15 +68,15 @@ __device__ inline uint32_t wave_sum(uint32_t v)
     return v;
 }
 
-// Segment holding global unit u: the last s with seg[s].unit0 <= u (segments are in
-// unit order, seg[0].unit0 == 0).
-template <class Seg>
+// Segment holding launch-wide index u: the last s with seg[s].*first <= u (segments
+// are in launch order and seg[0].*first == 0).
+template <auto First, class Seg>
 __device__ inline int find_segment(const Seg* seg, int nseg, uint32_t u)
 {
     int lo = 0, hi = nseg - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (seg[mid].unit0 <= u) lo = mid;
+        if (seg[mid].*First <= u) lo = mid;
         else hi = mid - 1;
     }
     return lo;
@@ -110,30 +96,78 @@ __device__ inline uint4 load_lane(const uint16_t* src, uint64_t t, uint32_t lane
 // --------------------------------------------------------------------------------
 // compress
 // --------------------------------------------------------------------------------
-// Lane 2k of w receives the low half of plane word k = 8p + j, lane 2k+1 the high half.
-template <int k>
-__device__ inline void write_planes(uint32_t& w, const uint64_t (&P)[3][8])
+// Per-lane constants of the 32x32 bit transpose within each half-wave (stage s =
+// 16, 8, 4, 2, 1): lanes whose bit s is clear keep the bit columns of mask M_s and
+// take their partner's columns rotated left by s; the others keep ~M_s and take the
+// partner's columns rotated right by s.
+struct Transpose32 {
+    uint32_t keep[5];
+    uint32_t rot[5];   // rotate-right amount for v_alignbit
+};
+
+__device__ inline Transpose32 transpose_consts(uint32_t lane)
 {
-    if constexpr (k < 24) {
-        w = write_lane<2 * k>(w, uint32_t(P[k / 8][k % 8]));
-        w = write_lane<2 * k + 1>(w, uint32_t(P[k / 8][k % 8] >> 32));
-        write_planes<k + 1>(w, P);
+    const uint32_t M[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+    Transpose32 c;
+#pragma unroll
+    for (int k = 0; k < 5; k++) {
+        const uint32_t sft = 16u >> k;
+        const bool upper = (lane & sft) != 0;
+        c.keep[k] = upper ? ~M[k] : M[k];
+        c.rot[k] = upper ? sft : 32u - sft;
     }
+    return c;
 }
-// Encodes one tile held by the wave.  `full`: all 512 values exist.  Writes the 512
-// A bytes and the 192 plane bytes; appends this tile's escape exponents to the wave's
-// LDS staging area at run..; returns the tile's escape count.
+
+// One transpose stage: exchange with lane ^ sft (ds_swizzle bit mode within groups of
+// 32 lanes), rotate the partner's word, keep this lane's own columns.
+template <int k>
+__device__ inline uint32_t transpose_stage(uint32_t x, const Transpose32& c)
+{
+    constexpr int sft = 16 >> k;
+    const uint32_t y = uint32_t(__builtin_amdgcn_ds_swizzle(int(x), 0x1F | (sft << 10)));
+    const uint32_t t = __builtin_amdgcn_alignbit(y, y, c.rot[k]);
+    return (x & c.keep[k]) | (t & ~c.keep[k]);
+}
+
+// Transposes the 32x32 bit matrix held by each half-wave (row = lane, column = bit):
+// afterwards bit i of lane c (within the half) is bit c of lane i.
+__device__ inline uint32_t transpose32(uint32_t x, const Transpose32& c)
+{
+    x = transpose_stage<0>(x, c);
+    x = transpose_stage<1>(x, c);
+    x = transpose_stage<2>(x, c);
+    x = transpose_stage<3>(x, c);
+    return transpose_stage<4>(x, c);
+}
+
+// Code table entry for exponent e: bit p of the code moved to bit 8p, and bit 24 set
+// when the code is 0 (an escape).  Shifting the entry of column j left by j and OR-ing
+// the 8 columns gives a lane word whose byte p holds plane p of the lane's 8 values
+// and whose byte 3 flags its escapes.
+__device__ inline uint32_t spread_code(uint32_t code)
+{
+    return (code & 1u) | ((code & 2u) << 7) | ((code & 4u) << 14) | (code == 0 ? (1u << 24) : 0u);
+}
+
+// Encodes one tile held by the wave.  kFull: all 512 values exist (else `nvalid` of
+// this lane's 8 values do).  Writes the 512 A bytes and the 192 plane bytes, appends
+// the tile's escape exponents to the wave's LDS staging area from `run` on, and
+// returns the tile's escape count.
 template <bool kFull>
-__device__ inline uint32_t encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, const uint8_t* s_lut,
-                                       uint8_t* A_tile, uint32_t* B_tile, uint8_t* s_esc, uint32_t run)
+__device__ inline uint32_t encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, const uint32_t* s_lut,
+                                       const Transpose32& tc, uint8_t* A_tile, uint32_t* B_tile, uint8_t* s_esc,
+                                       uint32_t run)
 {
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-    uint32_t e[8], c[8];
+    uint32_t e[8];
+    uint32_t row = 0;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         e[j] = (d[j >> 1] >> (7 + 16 * (j & 1))) & 0xFFu;
-        c[j] = s_lut[e[j]];
-        if (!kFull && uint32_t(j) >= nvalid) c[j] = 8;   // not a value: no plane bits, no escape
+        uint32_t ent = s_lut[e[j]];
+        if (!kFull && uint32_t(j) >= nvalid) ent = 0;   // not a value: no plane bits, no escape
+        row |= ent << j;
     }
     // sign+mantissa bytes: low byte of a BF16 holds the mantissa (bits 0-6), high byte
     // the sign (bit 7).  Gather low and high bytes of 4 values, then merge.
@@ -144,244 +178,264 @@ __device__ inline uint32_t encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, 
     a.y = (lo1 & 0x7F7F7F7Fu) | (hi1 & 0x80808080u);
     *reinterpret_cast<uint2*>(A_tile + 8 * lane) = a;
 
-    // 24 plane words: ballot of code bit p in column j.
-    uint64_t P[3][8];
-#pragma unroll
-    for (int p = 0; p < 3; p++)
-#pragma unroll
-        for (int j = 0; j < 8; j++) P[p][j] = ballot((c[j] >> p) & 1u);
-    uint32_t w = 0;
-    write_planes<0>(w, P);
-    if (lane < 48) B_tile[lane] = w;
+    // Plane words.  Row bit 8p + j of lane l is bit p of code(8l + j); after the
+    // transpose, lane c of half h holds bit l - 32h of it for l in the half, which is
+    // the 32-bit half h of plane word w = c = 8p + j: dword 2w + h of the tile.
+    const uint32_t col = transpose32(row & 0x00FFFFFFu, tc);
+    const uint32_t c = lane & 31u, h = lane >> 5;
+    if (c < 24) B_tile[2 * c + h] = col;
 
-    // escapes, in value order: lower lanes first, then this lane's columns in order
-    uint64_t Z[8];
-    uint32_t cnt = 0;
+    // escapes in value order: lower lanes first, then this lane's columns in order
+    const uint32_t zm = row >> 24;
+    const uint32_t cnt = __builtin_popcount(zm);
+    uint32_t r = run, total = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {   // prefix over lower lanes of cnt, one bit of cnt at a time
+        const uint64_t bk = ballot((cnt >> k) & 1u);
+        r += mbcnt(bk, 0u) << k;
+        total += uint32_t(__builtin_popcountll(bk)) << k;
+    }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        if (kFull) Z[j] = ~(P[0][j] | P[1][j] | P[2][j]);
-        else Z[j] = ballot(c[j] == 0);
-        cnt += __builtin_popcountll(Z[j]);
+        const uint32_t bit = (zm >> j) & 1u;
+        if (bit) s_esc[r] = uint8_t(e[j]);
+        r += bit;
     }
-    uint32_t r = run;
-#pragma unroll
-    for (int j = 0; j < 8; j++) r = mbcnt(Z[j], r);
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        if (c[j] == 0) {
-            s_esc[r] = uint8_t(e[j]);
-            r++;
-        }
-    }
-    return cnt;
+    return total;
 }
 
-__global__ __launch_bounds__(kThreads) void compress_kernel(const CArgs a)
+// Loads this lane's 8 values of each tile of block b of a segment (zeros past n).
+__device__ inline void load_block(const CSeg& sg, uint32_t b, uint32_t lane, uint4 (&v)[8])
 {
-    __shared__ uint8_t s_lut[256];
-    __shared__ uint8_t s_esc[kWaves][kBlock];
-    __shared__ uint32_t s_cnt[kWaves];
-    __shared__ uint32_t s_misc[4];
-
-    const uint32_t tid = threadIdx.x, lane = lane_id();
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t* wsu = a.ws;
-    uint64_t* seg_base = reinterpret_cast<uint64_t*>(a.ws + 4);
-    uint64_t* ust = seg_base + kMaxSegs;
-
-    if (tid == 0) {
-        s_misc[0] = add_agent32(&wsu[1], 1u);   // ticket = unit number in launch order
-        s_misc[1] = ld_agent32(&wsu[0]);        // generation of this launch's status words
+    const uint32_t n = sg.n, t0 = b * 8;
+    const uint16_t* src = sg.src + uint64_t(t0) * kTile + 8 * lane;
+    if (uint64_t(t0 + 8) * kTile <= n) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = *reinterpret_cast<const uint4*>(src + k * kTile);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = load_lane(sg.src, t0 + k, lane, n);
     }
-    __syncthreads();
-    const uint32_t unit = __builtin_amdgcn_readfirstlane(s_misc[0]);
-    const uint32_t gen = __builtin_amdgcn_readfirstlane(s_misc[1]);
-    const uint32_t tag = (gen + 1) & kTagMask;
-    if (unit >= a.total_units) {
-        // only possible with a workspace that was not zero-filled or a call that was
-        // aborted: touch nothing, report, and still count towards the reset
-        if (tid == 0) {
-            or_status(a.status, ZIPCCL_STATUS_SCAN_TIMEOUT);
-            uint32_t done = add_agent32(&wsu[2], 1u);
-            if (done == a.total_units - 1) {
-                st_agent32(&wsu[1], 0u);
-                st_agent32(&wsu[2], 0u);
-                st_agent32(&wsu[0], gen + 1);
-            }
-        }
-        return;
-    }
+}
 
-    const int s = find_segment(a.seg, a.nseg, unit);
-    const CSeg& sg = a.seg[s];
+// Encodes block b of a segment from the values in v: A bytes, planes, escape count and
+// staged escape exponents; zero padding after the segment's last block.
+__device__ inline void encode_block(const CArgs& a, const CSeg& sg, uint32_t b, uint32_t gb, const uint4 (&v)[8],
+                                    uint32_t lane, const uint32_t* lut, const Transpose32& tc, uint8_t* s_esc)
+{
     const uint32_t n = sg.n;
-    const uint32_t ui = unit - sg.unit0;                 // unit within the segment
-    const uint32_t T = uint32_t(tiles_of(n));
-    const uint32_t K = uint32_t(blocks_of(n));
-    const uint32_t units = uint32_t(units_of(n));
+    const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
     uint8_t* dst = sg.dst;
     uint8_t* A = dst + 128;
     uint32_t* B = reinterpret_cast<uint32_t*>(dst + planes_off(n));
-    uint32_t* C = reinterpret_cast<uint32_t*>(dst + offsets_off(n));
-
-    // this wave's block and tiles
-    const uint32_t b = ui * kWaves + wave;
     const uint32_t t0 = b * 8;
-    const uint32_t ntiles = t0 < T ? min(8u, T - t0) : 0u;
-    const uint32_t nfull = t0 < T ? min(ntiles, n / kTile - min(n / kTile, t0)) : 0u;
+    uint32_t run = 0;
+    if (uint64_t(t0 + 8) * kTile <= n) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const uint32_t t = t0 + k;
+            run += encode_tile<true>(v[k], lane, 8, lut, tc, A + 512ull * t, B + 48ull * t, s_esc, run);
+        }
+    } else {
+        const uint32_t ntiles = min(8u, T - t0);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const uint32_t t = t0 + k;
+            if (uint32_t(k) < ntiles) {
+                const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
+                const uint32_t nvalid = i >= n ? 0u : uint32_t(min<uint64_t>(8, n - i));
+                run += encode_tile<false>(v[k], lane, nvalid, lut, tc, A + 512ull * t, B + 48ull * t, s_esc, run);
+            }
+        }
+    }
+    // hand the block's escapes to the scan and place kernels
+    if (lane == 0) a.counts[gb] = run;
+    uint8_t* stage = a.stage + uint64_t(gb) * kBlock;
+    for (uint32_t k = lane; k < run; k += 64) stage[k] = s_esc[k];
+    if (b == K - 1) {   // zero padding of the plane and offset sections
+        const uint32_t bpad = uint32_t(round128(192ull * T) - 192ull * T);
+        uint8_t* bp = reinterpret_cast<uint8_t*>(B) + 192ull * T;
+        for (uint32_t k = lane; k < bpad; k += 64) bp[k] = 0;
+        const uint32_t cpad = uint32_t(round128(4ull * K) - 4ull * K);
+        uint8_t* cp = dst + offsets_off(n) + 4ull * K;
+        for (uint32_t k = lane; k < cpad; k += 64) cp[k] = 0;
+    }
+}
+
+// Encode: one workgroup per unit of 4 blocks, one block per wave.  No workgroup waits
+// for another: each wave writes its block's A bytes and planes, its escape count and
+// its staged escape exponents.
+__global__ __launch_bounds__(kThreads) void encode_kernel(const CArgs a)
+{
+    __shared__ uint32_t s_lut[256];
+    __shared__ uint8_t s_esc[kWaves][kBlock];
+
+    const uint32_t tid = threadIdx.x, lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t unit = blockIdx.x;
+    const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, unit);
+    const CSeg& sg = a.seg[s];
+    const uint32_t b = (unit - sg.unit0) * kWaves + wave;   // block within the segment
+    const bool active = b < blocks_of(sg.n);
 
     uint4 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++)
-        if (uint32_t(k) < ntiles) v[k] = load_lane(sg.src, t0 + k, lane, n);
-
-    {   // exponent -> code table for this segment
-        uint32_t e = tid, code = 0;
+    if (active) load_block(sg, b, lane, v);   // every load of the block first
+    {   // exponent -> spread code of this segment
+        uint32_t code = 0;
 #pragma unroll
         for (int r = 0; r < 7; r++) {
-            uint32_t te = (r < 4 ? (sg.table_lo >> (8 * r)) : (sg.table_hi >> (8 * (r - 4)))) & 0xFFu;
-            if (te == e) code = r + 1;
+            const uint32_t te = (r < 4 ? (sg.table_lo >> (8 * r)) : (sg.table_hi >> (8 * (r - 4)))) & 0xFFu;
+            if (te == tid) code = r + 1;
         }
-        s_lut[tid] = uint8_t(code);
+        s_lut[tid] = spread_code(code);
     }
+    const Transpose32 tc = transpose_consts(lane);
     __syncthreads();
+    if (!active) return;
+    encode_block(a, sg, b, sg.block0 + b, v, lane, s_lut, tc, s_esc[wave]);
+}
 
-    uint32_t run = 0;
+// Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
+__device__ inline void write_header(const CSeg& sg, uint32_t lane, uint32_t n_esc, uint32_t esc_offset)
+{
+    if (lane >= 32) return;
+    const uint32_t n = sg.n;
+    const uint64_t sbytes = static_bytes_of(n);
+    uint32_t hv = 0;
+    switch (lane) {
+        case 0: hv = ZIPCCL_MAGIC; break;
+        case 1: hv = 1u; break;                  // version 1, flags 0
+        case 2: hv = n; break;
+        case 4: hv = sg.table_lo; break;
+        case 5: hv = sg.table_hi & 0x00FFFFFFu; break;
+        case 6: hv = kBlock; break;
+        case 7: hv = kTile; break;
+        case 8: hv = n_esc; break;
+        case 10: hv = esc_offset; break;
+        case 12: hv = uint32_t(sbytes); break;
+        case 13: hv = uint32_t(sbytes >> 32); break;
+        default: hv = 0; break;
+    }
+    reinterpret_cast<uint32_t*>(sg.dst)[lane] = hv;
+}
+
+constexpr uint32_t kScanThreads = 1024;
+constexpr uint32_t kScanPer = 16;                       // counts per thread per round
+constexpr uint32_t kScanRound = kScanThreads * kScanPer;
+
+// Header of an empty segment (n = 0): esc_offset is where its escapes would start.
+__device__ inline void write_empty_header(const CSeg& sg, uint32_t lane, uint32_t esc_offset)
+{
+    write_header(sg, lane, 0u, esc_offset);
+}
+
+// Scan: one workgroup turns the per-block escape counts into launch-wide positions:
+// pos[b] = escapes of all blocks before b, pos[total_blocks] = all escapes.  Rounds of
+// 16 consecutive counts per thread keep every load and store 16 bytes wide.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
+{
+    __shared__ uint32_t s_wtot[kScanThreads / 64];
+    const uint32_t tid = threadIdx.x, lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t Kt = a.total_blocks;
+    uint32_t carry = 0;
+    for (uint32_t r0 = 0; r0 < Kt; r0 += kScanRound) {
+        const uint32_t lo = r0 + tid * kScanPer;
+        uint32_t c[kScanPer];
+        if (lo + kScanPer <= Kt) {
+            const uint4* q = reinterpret_cast<const uint4*>(a.counts + lo);
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-        uint32_t t = t0 + k;
-        if (uint32_t(k) < nfull) {
-            run += encode_tile<true>(v[k], lane, 8, s_lut, A + 512ull * t, B + 48ull * t, s_esc[wave], run);
-        } else if (uint32_t(k) < ntiles) {
-            uint64_t i = uint64_t(t) * kTile + 8ull * lane;
-            uint32_t nvalid = i >= n ? 0u : uint32_t(min<uint64_t>(8, n - i));
-            run += encode_tile<false>(v[k], lane, nvalid, s_lut, A + 512ull * t, B + 48ull * t, s_esc[wave], run);
-        }
-    }
-    if (lane == 0) s_cnt[wave] = run;
-    __syncthreads();
-    uint32_t before = 0, agg = 0;
+            for (int k = 0; k < 4; k++) {
+                const uint4 v = q[k];
+                c[4 * k] = v.x; c[4 * k + 1] = v.y; c[4 * k + 2] = v.z; c[4 * k + 3] = v.w;
+            }
+        } else {
 #pragma unroll
-    for (uint32_t w = 0; w < kWaves; w++) {
-        uint32_t c = __builtin_amdgcn_readfirstlane(s_cnt[w]);
-        if (w < wave) before += c;
-        agg += c;
+            for (uint32_t k = 0; k < kScanPer; k++) c[k] = lo + k < Kt ? a.counts[lo + k] : 0u;
+        }
+        uint32_t mine = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kScanPer; k++) mine += c[k];
+        uint32_t incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            uint32_t y = __shfl_up(incl, o, 64);
+            if (lane >= uint32_t(o)) incl += y;
+        }
+        __syncthreads();                       // previous round's readers of s_wtot are done
+        if (lane == 63) s_wtot[wave] = incl;
+        __syncthreads();
+        uint32_t base = carry, total = 0;
+        for (uint32_t w = 0; w < kScanThreads / 64; w++) {
+            const uint32_t t = s_wtot[w];
+            if (w < wave) base += t;
+            total += t;
+        }
+        uint32_t run = base + incl - mine;
+        uint32_t p[kScanPer];
+#pragma unroll
+        for (uint32_t k = 0; k < kScanPer; k++) {
+            p[k] = run;
+            run += c[k];
+        }
+        if (lo + kScanPer <= Kt) {
+            uint4* q = reinterpret_cast<uint4*>(a.pos + lo);
+#pragma unroll
+            for (int k = 0; k < 4; k++) q[k] = make_uint4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
+        } else {
+#pragma unroll
+            for (uint32_t k = 0; k < kScanPer; k++)
+                if (lo + k < Kt) a.pos[lo + k] = p[k];
+        }
+        carry += total;
     }
-
-    // ---- decoupled look-back: exclusive escape count of all earlier units ----
-    if (wave == 0) {
-        uint32_t excl = 0;
-        if (unit == 0) {
-            if (lane == 0) st_agent(&ust[0], pack_status(tag, kStInclusive, agg));
-        } else {
-            if (lane == 0) st_agent(&ust[unit], pack_status(tag, kStAggregate, agg));
-            int64_t hi = int64_t(unit) - 1;
-            uint32_t spins = 0;
-            while (true) {
-                int64_t idx = hi - int64_t(lane);
-                uint64_t wv = idx >= 0 ? ld_agent(&ust[idx]) : pack_status(tag, kStInclusive, 0);
-                uint32_t flag = uint32_t(wv >> 32) & 3u;
-                bool ready = (uint32_t(wv >> 34) == tag) && flag != 0;
-                uint64_t notready = ~ballot(ready);
-                uint64_t incl = ballot(ready && flag == kStInclusive);
-                if (incl) {
-                    uint32_t L = __builtin_ctzll(incl);
-                    uint64_t need = L == 63 ? ~0ull : ((2ull << L) - 1);
-                    if ((notready & need) == 0) {
-                        excl += wave_sum(lane <= L ? uint32_t(wv) : 0u);
-                        break;
-                    }
-                } else if (notready == 0) {
-                    excl += wave_sum(uint32_t(wv));
-                    hi -= 64;
-                    continue;
-                }
-                if (++spins > kSpinLimit) {
-                    if (lane == 0) or_status(a.status, ZIPCCL_STATUS_SCAN_TIMEOUT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if (lane == 0) st_agent(&ust[unit], pack_status(tag, kStInclusive, excl + agg));
-        }
-        // escape count before the segment's first unit
-        uint32_t segbase = excl;
-        if (ui == 0) {
-            if (lane == 0) st_agent(&seg_base[s], pack_status(tag, kStInclusive, excl));
-        } else {
-            uint32_t spins = 0;
-            while (true) {
-                uint64_t wv = ld_agent(&seg_base[s]);
-                if (uint32_t(wv >> 34) == tag && ((uint32_t(wv >> 32) & 3u) == kStInclusive)) {
-                    segbase = uint32_t(wv);
-                    break;
-                }
-                if (++spins > kSpinLimit) {
-                    if (lane == 0) or_status(a.status, ZIPCCL_STATUS_SCAN_TIMEOUT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        if (lane == 0) {
-            s_misc[2] = excl;
-            s_misc[3] = segbase;
+    if (tid == 0) a.pos[Kt] = carry;
+    if (tid == 0 && a.n_esc_out) a.n_esc_out[a.nseg] = carry;
+    if (Kt == 0 && wave == 0) {   // only empty segments: every header says offset 0
+        for (int s = 0; s < a.nseg; s++) {
+            write_empty_header(a.seg[s], lane, 0u);
+            if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = 0;
         }
     }
-    __syncthreads();
-    const uint32_t excl = __builtin_amdgcn_readfirstlane(s_misc[2]);
-    const uint32_t segbase = __builtin_amdgcn_readfirstlane(s_misc[3]);
+}
 
-    // ---- outputs that need the position: offsets, escapes, header ----
-    const uint32_t mine = s_cnt[wave];
-    const uint64_t gpos = uint64_t(excl) + before;   // first escape of this wave, launch-wide
-    if (b < K && lane == 0) C[b] = uint32_t(gpos - segbase);
-    for (uint32_t k = lane; k < mine; k += 64) {
-        uint64_t pos = gpos + k;
-        if (pos < a.esc_cap) a.esc[pos] = s_esc[wave][k];
+// Place: one wave per block.  Writes the block's offset-table entry, moves its staged
+// escape bytes to their compacted position, and writes the segment header from the
+// wave of the segment's last block.
+__global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t gb = blockIdx.x * kWaves + wave;
+    if (gb >= a.total_blocks) return;
+    const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
+    const CSeg& sg = a.seg[s];
+    const uint32_t K = uint32_t(blocks_of(sg.n));
+    const uint32_t p0 = a.pos[gb], p1 = a.pos[gb + 1], base = a.pos[sg.block0];
+    if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
+    const uint8_t* stage = a.stage + uint64_t(gb) * kBlock;
+    for (uint32_t k = lane; k < p1 - p0; k += 64) {
+        const uint64_t at = uint64_t(p0) + k;
+        if (at < a.esc_cap) a.esc[at] = stage[k];
         else or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     }
-
-    if (ui == units - 1) {
-        const uint32_t n_esc = excl + agg - segbase;
-        if (wave == 0 && lane < 32) {
-            const uint64_t sb = static_bytes_of(n);
-            uint32_t hv = 0;
-            switch (lane) {
-                case 0: hv = ZIPCCL_MAGIC; break;
-                case 1: hv = 1u; break;                  // version 1, flags 0
-                case 2: hv = n; break;
-                case 4: hv = sg.table_lo; break;
-                case 5: hv = sg.table_hi & 0x00FFFFFFu; break;
-                case 6: hv = kBlock; break;
-                case 7: hv = kTile; break;
-                case 8: hv = n_esc; break;
-                case 10: hv = segbase; break;
-                case 12: hv = uint32_t(sb); break;
-                case 13: hv = uint32_t(sb >> 32); break;
-                default: hv = 0; break;
-            }
-            reinterpret_cast<uint32_t*>(dst)[lane] = hv;
-            if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = n_esc;
-            if (lane == 0 && a.n_esc_out && unit == a.total_units - 1) a.n_esc_out[a.nseg] = excl + agg;
-        }
-        if (wave == 1) {   // zero padding of the plane and offset sections
-            const uint32_t bpad = uint32_t(round128(192ull * T) - 192ull * T);
-            uint8_t* bp = reinterpret_cast<uint8_t*>(B) + 192ull * T;
-            for (uint32_t k = lane; k < bpad; k += 64) bp[k] = 0;
-            const uint32_t cpad = uint32_t(round128(4ull * K) - 4ull * K);
-            uint8_t* cp = reinterpret_cast<uint8_t*>(C) + 4ull * K;
-            for (uint32_t k = lane; k < cpad; k += 64) cp[k] = 0;
+    if (gb == sg.block0 + K - 1) {
+        const uint32_t end = a.pos[sg.block0 + K];
+        write_header(sg, lane, end - base, base);
+        if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = end - base;
+    }
+    // empty segments just before this one start where it starts; those after the
+    // launch's last block start at the end
+    if (gb == sg.block0) {
+        for (int e = s - 1; e >= 0 && a.seg[e].n == 0; e--) {
+            write_empty_header(a.seg[e], lane, p0);
+            if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
         }
     }
-
-    // ---- last workgroup to finish resets the counters and advances the generation ----
-    if (tid == 0) {
-        uint32_t done = add_agent32(&wsu[2], 1u);
-        if (done == a.total_units - 1) {
-            st_agent32(&wsu[1], 0u);
-            st_agent32(&wsu[2], 0u);
-            st_agent32(&wsu[0], gen + 1);
+    if (gb + 1 == a.total_blocks) {
+        for (int e = s + 1; e < a.nseg; e++) {
+            write_empty_header(a.seg[e], lane, p1);
+            if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
         }
     }
 }
@@ -560,7 +614,7 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(const DArgs a)
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t unit = blockIdx.x;
-    const int s = find_segment(a.seg, a.nseg, unit);
+    const int s = find_segment<&DSeg::unit0>(a.seg, a.nseg, unit);
     const uint32_t n = a.seg[s].n;
     const uint32_t b = (unit - a.seg[s].unit0) * kWaves + wave;
     if (b >= blocks_of(n)) return;
@@ -577,98 +631,171 @@ __device__ inline uint32_t round_bf16_bits(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__global__ __launch_bounds__(kThreads) void accumulate_kernel(const AArgs a)
-{
-    __shared__ uint8_t s_esc[kWaves][kBlock];
-    const uint32_t tid = threadIdx.x, lane = lane_id();
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t n = a.n;
-    const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
-    const uint32_t b = blockIdx.x * kWaves + wave;
-    if (b >= K) return;
-    const uint32_t t0 = b * 8;
-    const uint32_t ntiles = min(8u, T - t0);
-    const uint32_t nvals = min(kBlock, n - b * kBlock);
+// Spreads bits 0..3 of x to bit 0 of bytes 0..3 (x < 16; the four partial products
+// of the multiply land on distinct bits, so nothing carries).
+__device__ inline uint32_t spread4(uint32_t x) { return __umul24(x, 0x00204081u) & 0x01010101u; }
 
-    // acc = f32(local)
-    float acc[8][8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-        if (uint32_t(k) < ntiles) {
-            uint4 v = load_lane(a.local, t0 + k, lane, n);
-            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 8; j++) acc[k][j] = __uint_as_float((j & 1) ? (d[j >> 1] & 0xFFFF0000u) : (d[j >> 1] << 16));
-        }
-    }
+// Codes of 4 columns as bytes, from a lane row whose byte p holds plane p of the lane's
+// 8 columns (column j at bit j): columns 0..3 for half 0, 4..7 for half 1.
+__device__ inline uint32_t codes_of_row(uint32_t row, int half)
+{
+    const uint32_t x0 = (row >> (4 * half)) & 0xFu, x1 = (row >> (8 + 4 * half)) & 0xFu,
+                   x2 = (row >> (16 + 4 * half)) & 0xFu;
+    return spread4(x0) | (spread4(x1) << 1) | (spread4(x2) << 2);
+}
+
+constexpr uint32_t kAccWaves = 8;                  // one wave per tile of a block
+constexpr uint32_t kAccThreads = 64 * kAccWaves;
+
+// Decode-accumulate: one workgroup per block, one wave per tile.  Every peer's bytes
+// for the tile are requested up front; each wave counts its tile's escapes per peer
+// from the plane rows, one barrier shares the counts so that every wave knows where
+// its tile's escapes start, then the peers are decoded and added in order.
+template <int kPeers>
+__global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
+{
+    __shared__ uint32_t s_cnt[kPeers][kAccWaves];
+    __shared__ uint8_t s_esc[kAccWaves][kTile];
+    const uint32_t lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n = a.n, P = uint32_t(a.npeers);
+    const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
+    const uint32_t b = blockIdx.x;
+    const uint32_t t = b * 8 + wave;
+    const bool has_tile = t < T;
+    const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
+    const uint32_t nvalid = (!has_tile || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
+    const uint32_t c = lane & 31u, h = lane >> 5;
+
+    // ---- requests: local values, and per peer the A bytes and one plane dword ----
+    uint4 lv = make_uint4(0, 0, 0, 0);
+    if (nvalid == 8) lv = *reinterpret_cast<const uint4*>(a.local + i0);
+    else if (nvalid > 0) lv = load_lane(a.local, t, lane, n);
+    uint2 Ap[kPeers];
+    uint32_t pw[kPeers];
     bool bad = false;
-    for (int p = 0; p < a.npeers; p++) {
-        const uint8_t* st = a.st[p];
-        const SegHeader h = read_header(st, n, a.esc_bytes[p]);
-        const uint8_t* A = st + 128;
-        const uint8_t* B = st + planes_off(n);
-        const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
-        uint32_t first = 0, last = 0;
-        if (!h.ok || !block_escapes(C, b, K, h.n_esc, nvals, first, last)) {
-            bad = true;
-            break;
-        }
-        const uint8_t* esc = a.esc[p] + h.esc_offset + first;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        for (uint32_t k = lane; k < last - first; k += 64) s_esc[wave][k] = esc[k];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint32_t run = 0;
+    uint32_t off0[kPeers], blk[kPeers], tlo[kPeers], thi[kPeers];
+    uint64_t eoff[kPeers];
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            if (uint32_t(k) < ntiles) {
-                const uint32_t t = t0 + k;
-                uint64_t P[24];
-                load_planes(B + 192ull * t, P);
-                uint2 Ap = *reinterpret_cast<const uint2*>(A + 512ull * t + 8 * lane);
-                uint32_t cnt;
-                uint4 o;
-                if ((uint64_t(t) + 1) * kTile <= n) {
-                    o = decode_tile<true>(Ap, P, h.tlo, h.thi, s_esc[wave], run, lane, 8, &cnt);
-                } else {
-                    const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
-                    uint32_t nvalid = i >= n ? 0u : uint32_t(min<uint64_t>(8, n - i));
-                    o = decode_tile<false>(Ap, P, h.tlo, h.thi, s_esc[wave], run, lane, nvalid, &cnt);
-                }
-                run += cnt;
-                const uint32_t d[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-                for (int j = 0; j < 8; j++)
-                    acc[k][j] = acc[k][j] + __uint_as_float((j & 1) ? (d[j >> 1] & 0xFFFF0000u) : (d[j >> 1] << 16));
+    for (int p = 0; p < kPeers; p++) {
+        Ap[p] = make_uint2(0, 0);
+        pw[p] = 0;
+        off0[p] = 0;
+        blk[p] = 0;
+        tlo[p] = thi[p] = 0;
+        eoff[p] = 0;
+        if (uint32_t(p) < P) {
+            const uint8_t* st = a.st[p];
+            const SegHeader hd = read_header(st, n, a.esc_bytes[p]);
+            const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
+            uint32_t first = 0, last = 0;
+            bad = bad || !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
+            off0[p] = first;
+            blk[p] = last - first;
+            tlo[p] = hd.tlo;
+            thi[p] = hd.thi;
+            eoff[p] = hd.esc_offset;
+            if (has_tile && !bad) {
+                Ap[p] = *reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane);
+                if (c < 24) pw[p] = reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t)[2 * c + h];
             }
         }
-        if (run != last - first) {
-            bad = true;
-            break;
+    }
+
+    // ---- per peer: plane rows, escape flags, escape ranks within the tile ----
+    const Transpose32 tc = transpose_consts(lane);
+    const uint32_t vmask = nvalid >= 8 ? 0xFFu : ((1u << nvalid) - 1u);
+    uint32_t rows[kPeers], zm[kPeers], rank[kPeers];
+#pragma unroll
+    for (int p = 0; p < kPeers; p++) {
+        rows[p] = 0;
+        zm[p] = 0;
+        rank[p] = 0;
+        if (uint32_t(p) < P) {
+            const uint32_t r = transpose32(pw[p], tc);
+            rows[p] = r;
+            zm[p] = ~(r | (r >> 8) | (r >> 16)) & vmask;
+            const uint32_t cnt = __builtin_popcount(zm[p]);
+            uint32_t pre = 0, total = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint64_t bk = ballot((cnt >> k) & 1u);
+                pre += mbcnt(bk, 0u) << k;
+                total += uint32_t(__builtin_popcountll(bk)) << k;
+            }
+            rank[p] = pre;
+            if (lane == 0) s_cnt[p][wave] = total;
+        }
+    }
+    __syncthreads();
+
+    // ---- decode and add, peers in order ----
+    float acc[8];
+    {
+        const uint32_t d[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[j] = __uint_as_float((j & 1) ? (d[j >> 1] & 0xFFFF0000u) : (d[j >> 1] << 16));
+    }
+    uint8_t* esc_lds = s_esc[wave];
+#pragma unroll
+    for (int p = 0; p < kPeers; p++) {
+        if (uint32_t(p) < P) {
+            uint32_t before = 0, block_total = 0;
+#pragma unroll
+            for (uint32_t w = 0; w < kAccWaves; w++) {
+                const uint32_t v = s_cnt[p][w];
+                if (w < wave) before += v;
+                block_total += v;
+            }
+            const uint32_t mine = s_cnt[p][wave];
+            bad = bad || block_total != blk[p];   // the offset table must agree with the planes
+            if (!bad && has_tile) {
+                const uint8_t* esc = a.esc[p] + eoff[p] + off0[p] + before;
+                for (uint32_t k = lane; k < mine; k += 64) esc_lds[k] = esc[k];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                uint32_t E0 = perm(thi[p], tlo[p], codes_of_row(rows[p], 0));
+                uint32_t E1 = perm(thi[p], tlo[p], codes_of_row(rows[p], 1));
+                uint32_t z = zm[p], r = rank[p];
+                while (z) {   // this lane's escapes, in column order
+                    const uint32_t j = __builtin_ctz(z);
+                    const uint32_t x = esc_lds[r++];
+                    const uint32_t sh = 8 * (j & 3);
+                    if (j < 4) E0 = (E0 & ~(0xFFu << sh)) | (x << sh);
+                    else E1 = (E1 & ~(0xFFu << sh)) | (x << sh);
+                    z &= z - 1;
+                }
+                // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
+                const uint32_t lo0 = (Ap[p].x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
+                const uint32_t hi0 = (Ap[p].x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
+                const uint32_t lo1 = (Ap[p].y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
+                const uint32_t hi1 = (Ap[p].y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
+                    const uint32_t sel = 0x0C0Cu | ((j & 3u) << 16) | ((4u + (j & 3u)) << 24);
+                    const uint32_t f = j < 4 ? perm(hi0, lo0, sel) : perm(hi1, lo1, sel);
+                    acc[j] = acc[j] + __uint_as_float(f);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            }
         }
     }
     if (bad) {
-        if (lane == 0) or_status(a.status, ZIPCCL_STATUS_CORRUPT);
+        if (lane == 0 && wave == 0) or_status(a.status, ZIPCCL_STATUS_CORRUPT);
         return;
     }
+    if (nvalid == 0) return;
+    uint32_t r[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-        if (uint32_t(k) < ntiles) {
-            const uint32_t t = t0 + k;
-            const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
-            uint32_t r[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) r[j] = round_bf16_bits(acc[k][j]);
-            if (i + 8 <= n) {
-                uint4 o = make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
-                *reinterpret_cast<uint4*>(a.dst + i) = o;
-            } else {
-                for (uint32_t j = 0; j < 8; j++)
-                    if (i + j < n) a.dst[i + j] = uint16_t(r[j]);
-            }
-        }
+    for (int j = 0; j < 8; j++) r[j] = round_bf16_bits(acc[j]);
+    if (nvalid == 8) {
+        *reinterpret_cast<uint4*>(a.dst + i0) =
+            make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
+    } else {
+        for (uint32_t j = 0; j < nvalid; j++) a.dst[i0 + j] = uint16_t(r[j]);
     }
 }
 
@@ -676,21 +803,26 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(const AArgs a)
 
 hipError_t launch_compress(const CArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL(compress_kernel, dim3(a.total_units), dim3(kThreads), 0, s, a);
+    if (a.total_units > 0) hipLaunchKernelGGL(encode_kernel, dim3(a.total_units), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+    if (a.total_blocks > 0)
+        hipLaunchKernelGGL(place_kernel, dim3((a.total_blocks + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_decompress(const DArgs& a, hipStream_t s)
 {
+    if (a.total_units == 0) return hipSuccess;
     hipLaunchKernelGGL(decompress_kernel, dim3(a.total_units), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_accumulate(const AArgs& a, hipStream_t s)
 {
-    uint32_t grid = uint32_t((blocks_of(a.n) + kWaves - 1) / kWaves);
+    const uint32_t grid = uint32_t(blocks_of(a.n));
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(accumulate_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+    if (a.npeers <= 8) hipLaunchKernelGGL(accumulate_kernel<8>, dim3(grid), dim3(kAccThreads), 0, s, a);
+    else hipLaunchKernelGGL(accumulate_kernel<kMaxPeers>, dim3(grid), dim3(kAccThreads), 0, s, a);
     return hipGetLastError();
 }
 

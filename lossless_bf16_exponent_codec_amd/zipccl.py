@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libzipccl.so")
 
 OK, ERR_INVALID, ERR_ALIGN, ERR_SIZE, ERR_HIP, ERR_CORRUPT = range(6)
-STATUS_ESC_OVERFLOW, STATUS_CORRUPT, STATUS_SCAN_TIMEOUT = 1, 2, 4
+STATUS_ESC_OVERFLOW, STATUS_CORRUPT = 1, 2
 MAX_SEGMENTS, MAX_PEERS = 64, 16
 FORMAT_VERSION, MAGIC = 1, 0x3143435A
 
@@ -245,7 +245,7 @@ def compress_tensors(tensors, plans, esc_cap=None, workspace=None, stream=None) 
     n_esc = torch.zeros(len(tensors) + 1, dtype=torch.int64, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = torch.zeros(workspace_size(sum(sizes), len(tensors)), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(workspace_size(sum(sizes), len(tensors)), dtype=torch.uint8, device=dev)
     compress([(_as_bf16(t), p) for t, p in zip(tensors, plans)], static, esc, workspace, n_esc, status,
              stream=stream, esc_cap=cap)
     return Compressed(static, esc, n_esc, sizes, status)
