@@ -15,12 +15,17 @@ constexpr uint32_t kUnit = kBlock * kWaves;   // values per workgroup: one block
 constexpr int kMaxSegs = 64;
 constexpr int kMaxPeers = 16;
 
-// Compress workspace: a u32 escape count per block of the launch, the launch-wide
-// position of every block's first escape (one more entry for the total), then a
-// staging slot of kBlock bytes per block that holds the block's escape exponents
-// until their positions are known.
-__host__ __device__ inline uint64_t ws_counts_bytes(uint64_t blocks) { return (4 * blocks + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_pos_bytes(uint64_t blocks) { return (4 * (blocks + 1) + 255) & ~uint64_t(255); }
+// Encode granule: half a block (4 tiles, 2048 values) per wave, 8 waves per workgroup.
+constexpr uint32_t kHalf = kBlock / 2;
+constexpr uint32_t kEncWaves = 8;
+constexpr uint32_t kEncThreads = 64 * kEncWaves;
+
+// Compress workspace: a u32 escape count per half block of the launch, the
+// launch-wide position of every half block's first escape (one more entry for the
+// total), then a staging slot of kHalf bytes per half block that holds its escape
+// exponents until their positions are known.
+__host__ __device__ inline uint64_t ws_counts_bytes(uint64_t blocks) { return (8 * blocks + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_pos_bytes(uint64_t blocks) { return (4 * (2 * blocks + 1) + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_bytes(uint64_t blocks)
 {
     return ws_counts_bytes(blocks) + ws_pos_bytes(blocks) + uint64_t(kBlock) * blocks;
@@ -41,9 +46,9 @@ struct CArgs {
     CSeg seg[kMaxSegs];
     uint8_t* esc;
     uint64_t esc_cap;
-    uint32_t* counts;      // workspace: escapes per block
-    uint32_t* pos;         // workspace: launch-wide position of each block's first escape
-    uint8_t* stage;        // workspace: kBlock bytes per block
+    uint32_t* counts;      // workspace: escapes per half block
+    uint32_t* pos;         // workspace: launch-wide position of each half block's first escape
+    uint8_t* stage;        // workspace: kHalf bytes per half block
     uint64_t* n_esc_out;   // nseg + 1 entries or null
     uint32_t* status;      // or null
     int32_t nseg;
@@ -56,7 +61,7 @@ struct DSeg {              // decompress: one segment
     const uint8_t* src;    // static part
     uint16_t* dst;
     uint32_t n;
-    uint32_t unit0;
+    uint32_t unit0;        // first workgroup unit of the segment (units of kUnit values)
 };
 
 struct DArgs {

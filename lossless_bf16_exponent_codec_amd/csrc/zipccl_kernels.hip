@@ -7,27 +7,24 @@
 // three 1-bit planes), S2.D (local reduction on the reduce-scatter receive side).
 // The byte layout (format version 1) is documented in include/zipccl.h.
 //
-// Work decomposition.  A tile is 512 values: lane l of a wave holds values
-// 8l..8l+7, one 16-byte load.  A block is 8 tiles (4096 values, one escape-offset
-// entry) and belongs to one wave.  A workgroup of 4 waves handles a unit of 4 blocks.
-//   * Plane word (p, j) of a tile is the wave ballot of "bit p of code(8l + j)", so
-//     the 24 words of a tile come from 24 ballots and land in SGPRs; v_writelane moves
-//     them into one VGPR (lane k gets 32-bit half k) for a 192-byte vector store.
-//   * Escapes: per-column escape ballots, mbcnt gives each lane the number of escapes
-//     in lower lanes, the lane's own escapes follow in column order.  Escape bytes are
-//     staged in LDS per wave, then in a per-block slot of the workspace.
-//   * Compress is two launches.  The encode kernel has no dependency between
-//     workgroups: it writes A, B and a per-block escape count.  The finalize kernel
-//     (one workgroup per 256 blocks) sums the counts before its range, scans its own,
-//     writes the offset table, compacts the staged escapes and writes the headers.
-//     No workgroup ever waits for another, so there is no spin and no state kept in
-//     the workspace from one call to the next.
+// Work decomposition.  A tile is 512 values: lane l of a wave holds values 8l..8l+7,
+// one 16-byte load.  A block is 8 tiles (4096 values, one escape-offset entry).
+//   * Planes.  A lane looks up, per value, its code with bit p moved to bit 8p (plus
+//     an escape flag in bit 24) and ORs the 8 entries, shifted by their column, into
+//     one 32-bit row.  A 32x32 bit transpose inside each half-wave (5 stages of
+//     ds_swizzle + v_alignbit + v_bfi) turns the rows of 32 lanes into 24 plane dwords:
+//     lane c of half h then holds bits 32h..32h+31 of plane word c.  The decoders run
+//     the same transpose on the loaded plane dwords to get each lane's row back.
+//   * Escapes.  Per-lane escape counts; ballots of their bits and mbcnt give each lane
+//     the escapes of the lower lanes; the lane's own escapes follow in column order.
+//   * Compress is three launches, none of which waits on another workgroup: encode
+//     (one half block per wave: A bytes, planes, escape count, escapes staged in the
+//     workspace), scan (one workgroup: escape positions), place (one wave per block:
+//     offset table, compacted escapes, headers).  The workspace keeps no state.
+//   * Decompress and decode-accumulate: one workgroup per block, one wave per tile;
+//     one barrier shares the tiles' escape counts.
 #include "zipccl_internal.h"
 #include "zipccl.h"
-
-// llvm.amdgcn.writelane: the compiler knows this instruction, so it also inserts the
-// wait states its operands need (inline assembly would hide them from it).
-__device__ int zc_writelane(int src, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
 namespace zc {
 
@@ -43,29 +40,21 @@ __device__ inline uint32_t mbcnt(uint64_t m, uint32_t acc)
     return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), acc));
 }
 
-__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
-
-// k if this lane's bit of the wave-uniform mask is set, else 0: one v_cndmask with the
-// mask as its SGPR-pair condition.
-__device__ inline uint32_t lane_select(uint64_t mask, uint32_t k) { return __builtin_amdgcn_inverse_ballot_w64(mask) ? k : 0u; }
-
-// Writes the wave-uniform value v into lane k of w (v_writelane_b32).
-template <int k>
-__device__ inline uint32_t write_lane(uint32_t w, uint32_t v)
+// Streaming stores of the encoder's output (written once, read by another kernel
+// later): non-temporal.
+typedef unsigned int zc_u32x2 __attribute__((ext_vector_type(2)));
+__device__ inline void store_nt(uint2* p, uint2 v)
 {
-    return uint32_t(zc_writelane(int(v), k, int(w)));
+    zc_u32x2 x = {v.x, v.y};
+    __builtin_nontemporal_store(x, reinterpret_cast<zc_u32x2*>(p));
 }
+__device__ inline void store_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
+__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
 
 __device__ inline void or_status(uint32_t* s, uint32_t bits)
 {
     if (s) __hip_atomic_fetch_or(s, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline uint32_t wave_sum(uint32_t v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
 }
 
 // Segment holding launch-wide index u: the last s with seg[s].*first <= u (segments
@@ -176,14 +165,14 @@ __device__ inline uint32_t encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, 
     uint2 a;
     a.x = (lo0 & 0x7F7F7F7Fu) | (hi0 & 0x80808080u);
     a.y = (lo1 & 0x7F7F7F7Fu) | (hi1 & 0x80808080u);
-    *reinterpret_cast<uint2*>(A_tile + 8 * lane) = a;
+    store_nt(reinterpret_cast<uint2*>(A_tile + 8 * lane), a);
 
     // Plane words.  Row bit 8p + j of lane l is bit p of code(8l + j); after the
     // transpose, lane c of half h holds bit l - 32h of it for l in the half, which is
     // the 32-bit half h of plane word w = c = 8p + j: dword 2w + h of the tile.
     const uint32_t col = transpose32(row & 0x00FFFFFFu, tc);
     const uint32_t c = lane & 31u, h = lane >> 5;
-    if (c < 24) B_tile[2 * c + h] = col;
+    if (c < 24) store_nt(B_tile + 2 * c + h, col);
 
     // escapes in value order: lower lanes first, then this lane's columns in order
     const uint32_t zm = row >> 24;
@@ -204,42 +193,29 @@ __device__ inline uint32_t encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, 
     return total;
 }
 
-// Loads this lane's 8 values of each tile of block b of a segment (zeros past n).
-__device__ inline void load_block(const CSeg& sg, uint32_t b, uint32_t lane, uint4 (&v)[8])
-{
-    const uint32_t n = sg.n, t0 = b * 8;
-    const uint16_t* src = sg.src + uint64_t(t0) * kTile + 8 * lane;
-    if (uint64_t(t0 + 8) * kTile <= n) {
-#pragma unroll
-        for (int k = 0; k < 8; k++) v[k] = *reinterpret_cast<const uint4*>(src + k * kTile);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; k++) v[k] = load_lane(sg.src, t0 + k, lane, n);
-    }
-}
-
-// Encodes block b of a segment from the values in v: A bytes, planes, escape count and
-// staged escape exponents; zero padding after the segment's last block.
-__device__ inline void encode_block(const CArgs& a, const CSeg& sg, uint32_t b, uint32_t gb, const uint4 (&v)[8],
-                                    uint32_t lane, const uint32_t* lut, const Transpose32& tc, uint8_t* s_esc)
+// Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
+// planes, the escape count and the staged escape exponents; zero padding after the
+// segment's last half block.  gh: the half block's launch-wide index.
+__device__ inline void encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
+                                   uint32_t lane, const uint32_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
     const uint32_t n = sg.n;
     const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
     uint8_t* dst = sg.dst;
     uint8_t* A = dst + 128;
     uint32_t* B = reinterpret_cast<uint32_t*>(dst + planes_off(n));
-    const uint32_t t0 = b * 8;
+    const uint32_t t0 = hb * 4;
     uint32_t run = 0;
-    if (uint64_t(t0 + 8) * kTile <= n) {
+    if (uint64_t(t0 + 4) * kTile <= n) {
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < 4; k++) {
             const uint32_t t = t0 + k;
             run += encode_tile<true>(v[k], lane, 8, lut, tc, A + 512ull * t, B + 48ull * t, s_esc, run);
         }
     } else {
-        const uint32_t ntiles = min(8u, T - t0);
+        const uint32_t ntiles = t0 < T ? min(4u, T - t0) : 0u;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < 4; k++) {
             const uint32_t t = t0 + k;
             if (uint32_t(k) < ntiles) {
                 const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
@@ -248,11 +224,11 @@ __device__ inline void encode_block(const CArgs& a, const CSeg& sg, uint32_t b, 
             }
         }
     }
-    // hand the block's escapes to the scan and place kernels
-    if (lane == 0) a.counts[gb] = run;
-    uint8_t* stage = a.stage + uint64_t(gb) * kBlock;
+    // hand the escapes to the scan and place kernels
+    if (lane == 0) a.counts[gh] = run;
+    uint8_t* stage = a.stage + uint64_t(gh) * kHalf;
     for (uint32_t k = lane; k < run; k += 64) stage[k] = s_esc[k];
-    if (b == K - 1) {   // zero padding of the plane and offset sections
+    if (hb == 2 * K - 1) {   // zero padding of the plane and offset sections
         const uint32_t bpad = uint32_t(round128(192ull * T) - 192ull * T);
         uint8_t* bp = reinterpret_cast<uint8_t*>(B) + 192ull * T;
         for (uint32_t k = lane; k < bpad; k += 64) bp[k] = 0;
@@ -262,25 +238,36 @@ __device__ inline void encode_block(const CArgs& a, const CSeg& sg, uint32_t b, 
     }
 }
 
-// Encode: one workgroup per unit of 4 blocks, one block per wave.  No workgroup waits
-// for another: each wave writes its block's A bytes and planes, its escape count and
-// its staged escape exponents.
-__global__ __launch_bounds__(kThreads) void encode_kernel(const CArgs a)
+// Encode: one workgroup per unit of 4 blocks, one half block per wave.  No workgroup
+// waits for another: each wave writes its tiles' A bytes and planes, its escape count
+// and its staged escape exponents.
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
 {
     __shared__ uint32_t s_lut[256];
-    __shared__ uint8_t s_esc[kWaves][kBlock];
+    __shared__ uint8_t s_esc[kEncWaves][kHalf];
 
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t unit = blockIdx.x;
     const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, unit);
     const CSeg& sg = a.seg[s];
-    const uint32_t b = (unit - sg.unit0) * kWaves + wave;   // block within the segment
-    const bool active = b < blocks_of(sg.n);
+    const uint32_t n = sg.n;
+    const uint32_t hb = (unit - sg.unit0) * kEncWaves + wave;   // half block within the segment
+    const bool active = hb < 2 * blocks_of(n);
 
-    uint4 v[8];
-    if (active) load_block(sg, b, lane, v);   // every load of the block first
-    {   // exponent -> spread code of this segment
+    uint4 v[4];   // every load of the half block first (values past n read as 0)
+    if (active) {
+        const uint32_t t0 = hb * 4;
+        const uint16_t* src = sg.src + uint64_t(t0) * kTile + 8 * lane;
+        if (uint64_t(t0 + 4) * kTile <= n) {
+#pragma unroll
+            for (int k = 0; k < 4; k++) v[k] = *reinterpret_cast<const uint4*>(src + k * kTile);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, t0 + k, lane, n);
+        }
+    }
+    if (tid < 256) {   // exponent -> spread code of this segment
         uint32_t code = 0;
 #pragma unroll
         for (int r = 0; r < 7; r++) {
@@ -292,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const CArgs a)
     const Transpose32 tc = transpose_consts(lane);
     __syncthreads();
     if (!active) return;
-    encode_block(a, sg, b, sg.block0 + b, v, lane, s_lut, tc, s_esc[wave]);
+    encode_half(a, sg, hb, 2 * sg.block0 + hb, v, lane, s_lut, tc, s_esc[wave]);
 }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
@@ -329,15 +316,16 @@ __device__ inline void write_empty_header(const CSeg& sg, uint32_t lane, uint32_
     write_header(sg, lane, 0u, esc_offset);
 }
 
-// Scan: one workgroup turns the per-block escape counts into launch-wide positions:
-// pos[b] = escapes of all blocks before b, pos[total_blocks] = all escapes.  Rounds of
-// 16 consecutive counts per thread keep every load and store 16 bytes wide.
+// Scan: one workgroup turns the per-half-block escape counts into launch-wide
+// positions: pos[h] = escapes of all half blocks before h, pos[2 * total_blocks] = all
+// escapes.  Rounds of 16 consecutive counts per thread keep loads and stores 16 bytes
+// wide.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
 {
     __shared__ uint32_t s_wtot[kScanThreads / 64];
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t Kt = a.total_blocks;
+    const uint32_t Kt = 2 * a.total_blocks;   // half blocks
     uint32_t carry = 0;
     for (uint32_t r0 = 0; r0 < Kt; r0 += kScanRound) {
         const uint32_t lo = r0 + tid * kScanPer;
@@ -399,9 +387,29 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
     }
 }
 
-// Place: one wave per block.  Writes the block's offset-table entry, moves its staged
-// escape bytes to their compacted position, and writes the segment header from the
-// wave of the segment's last block.
+// Copies one half block's staged escapes to esc[p ...]; `head` holds staged bytes
+// 4*hl .. 4*hl+3 (hl = lane within the half of the wave that loaded them).
+__device__ inline bool place_half(const CArgs& a, const uint8_t* stage, uint32_t head, uint32_t hl, uint32_t p,
+                                  uint32_t cnt)
+{
+    bool over = false;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; q++) {
+        const uint32_t k = 4 * hl + q;
+        if (k < cnt) {
+            const uint64_t at = uint64_t(p) + k;
+            if (at < a.esc_cap) a.esc[at] = uint8_t(head >> (8 * q));
+            else over = true;
+        }
+    }
+    return over;
+}
+
+// Place: one wave per block.  Writes the block's offset-table entry, moves the staged
+// escape bytes of its two half blocks to their compacted position, and writes the
+// segment header from the wave of the segment's last block.  The first 128 staged
+// bytes of each half are requested together with the positions, so a typical block
+// costs one round trip.
 __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
 {
     const uint32_t lane = lane_id();
@@ -411,16 +419,26 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
     const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
     const CSeg& sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
-    const uint32_t p0 = a.pos[gb], p1 = a.pos[gb + 1], base = a.pos[sg.block0];
+    const uint32_t hl = lane & 31u, hsel = lane >> 5;
+    const uint8_t* stage = a.stage + uint64_t(2 * gb + hsel) * kHalf;   // lanes 0-31: half 0, 32-63: half 1
+    const uint32_t head = reinterpret_cast<const uint32_t*>(stage)[hl];
+    const uint32_t p0 = a.pos[2 * gb], p1 = a.pos[2 * gb + 1], p2 = a.pos[2 * gb + 2];
+    const uint32_t base = a.pos[2 * sg.block0];
     if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
-    const uint8_t* stage = a.stage + uint64_t(gb) * kBlock;
-    for (uint32_t k = lane; k < p1 - p0; k += 64) {
-        const uint64_t at = uint64_t(p0) + k;
-        if (at < a.esc_cap) a.esc[at] = stage[k];
-        else or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
+    const uint32_t hp = hsel ? p1 : p0, hc = hsel ? p2 - p1 : p1 - p0;
+    bool over = place_half(a, stage, head, hl, hp, hc);
+    for (uint32_t hh = 0; hh < 2; hh++) {   // rare: more than 128 escapes in a half block
+        const uint32_t c = hh ? p2 - p1 : p1 - p0, q = hh ? p1 : p0;
+        const uint8_t* st = a.stage + uint64_t(2 * gb + hh) * kHalf;
+        for (uint32_t k = 128 + lane; k < c; k += 64) {
+            const uint64_t at = uint64_t(q) + k;
+            if (at < a.esc_cap) a.esc[at] = st[k];
+            else over = true;
+        }
     }
+    if (over) or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     if (gb == sg.block0 + K - 1) {
-        const uint32_t end = a.pos[sg.block0 + K];
+        const uint32_t end = a.pos[2 * (sg.block0 + K)];
         write_header(sg, lane, end - base, base);
         if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = end - base;
     }
@@ -434,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
     }
     if (gb + 1 == a.total_blocks) {
         for (int e = s + 1; e < a.nseg; e++) {
-            write_empty_header(a.seg[e], lane, p1);
+            write_empty_header(a.seg[e], lane, p2);
             if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
         }
     }
@@ -488,137 +506,6 @@ __device__ inline bool block_escapes(const uint32_t* C, uint32_t b, uint32_t K, 
     first = C[b];
     last = (b + 1 < K) ? C[b + 1] : n_esc;
     return first <= last && last <= n_esc && last - first <= nvals;
-}
-
-__device__ inline uint32_t load_sgpr32(const uint32_t* p) { return __builtin_amdgcn_readfirstlane(*p); }
-
-// Decodes one tile: returns the 8 BF16 values of this lane as 4 dwords.
-//   Ap: this lane's 8 A bytes; P: the tile's 24 plane words; esc: the wave's staged
-//   escape bytes starting at this tile's first escape; valid: values of this lane that
-//   exist (8 for a full tile).  Returns the tile's escape count via *cnt.
-template <bool kFull>
-__device__ inline uint4 decode_tile(uint2 Ap, const uint64_t* P, uint32_t tlo, uint32_t thi, const uint8_t* s_esc,
-                                    uint32_t run, uint32_t lane, uint32_t nvalid, uint32_t* cnt)
-{
-    // codes as bytes: C0 = columns 0..3, C1 = columns 4..7
-    uint32_t C0 = 0, C1 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        C0 |= lane_select(P[j], 1u << (8 * j)) | lane_select(P[8 + j], 2u << (8 * j)) |
-              lane_select(P[16 + j], 4u << (8 * j));
-        C1 |= lane_select(P[4 + j], 1u << (8 * j)) | lane_select(P[12 + j], 2u << (8 * j)) |
-              lane_select(P[20 + j], 4u << (8 * j));
-    }
-    uint32_t E0 = perm(thi, tlo, C0), E1 = perm(thi, tlo, C1);
-
-    // escapes of the tile: code 0 and inside the segment
-    uint64_t Z[8];
-    uint32_t total = 0;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        Z[j] = ~(P[j] | P[8 + j] | P[16 + j]);
-        if (!kFull) Z[j] &= ballot(uint32_t(j) < nvalid);
-        total += __builtin_popcountll(Z[j]);
-    }
-    *cnt = total;
-    if (total) {
-        uint32_t r = run;
-#pragma unroll
-        for (int j = 0; j < 8; j++) r = mbcnt(Z[j], r);
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            if ((Z[j] >> lane) & 1ull) {
-                uint32_t x = s_esc[r++];
-                if (j < 4) E0 = (E0 & ~(0xFFu << (8 * j))) | (x << (8 * j));
-                else E1 = (E1 & ~(0xFFu << (8 * (j - 4)))) | (x << (8 * (j - 4)));
-            }
-        }
-    }
-    // reassemble: low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
-    uint32_t lo0 = (Ap.x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
-    uint32_t hi0 = (Ap.x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
-    uint32_t lo1 = (Ap.y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
-    uint32_t hi1 = (Ap.y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
-    uint4 o;
-    o.x = perm(hi0, lo0, 0x05010400u);
-    o.y = perm(hi0, lo0, 0x07030602u);
-    o.z = perm(hi1, lo1, 0x05010400u);
-    o.w = perm(hi1, lo1, 0x07030602u);
-    return o;
-}
-
-__device__ inline void load_planes(const uint8_t* Bt, uint64_t P[24])
-{
-    const uint64_t* q = reinterpret_cast<const uint64_t*>(Bt);
-#pragma unroll
-    for (int w = 0; w < 24; w++) P[w] = q[w];
-}
-
-// --------------------------------------------------------------------------------
-// decompress
-// --------------------------------------------------------------------------------
-// Decodes block b of one segment.  `st` is only read in the kernel, so it is marked
-// restrict: the plane words and the header then load through the scalar cache.
-__device__ __forceinline__ void decode_block(const uint8_t* __restrict__ st, const uint8_t* __restrict__ esc_base,
-                                          uint64_t esc_bytes, uint16_t* dst, uint32_t n, uint32_t b, uint32_t lane,
-                                          uint8_t* s_esc, uint32_t* status)
-{
-    const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
-    const SegHeader h = read_header(st, n, esc_bytes);
-    if (!h.ok) {
-        if (lane == 0) or_status(status, ZIPCCL_STATUS_CORRUPT);
-        return;
-    }
-    const uint8_t* A = st + 128;
-    const uint8_t* B = st + planes_off(n);
-    const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
-    const uint32_t nvals = min(kBlock, n - b * kBlock);
-    uint32_t first, last;
-    if (!block_escapes(C, b, K, h.n_esc, nvals, first, last)) {
-        if (lane == 0) or_status(status, ZIPCCL_STATUS_CORRUPT);
-        return;
-    }
-    const uint8_t* esc = esc_base + h.esc_offset + first;
-    for (uint32_t k = lane; k < last - first; k += 64) s_esc[k] = esc[k];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    const uint32_t t0 = b * 8;
-    const uint32_t ntiles = min(8u, T - t0);
-    uint32_t run = 0;
-    for (uint32_t k = 0; k < ntiles; k++) {
-        const uint32_t t = t0 + k;
-        uint64_t P[24];
-        load_planes(B + 192ull * t, P);
-        uint2 Ap = *reinterpret_cast<const uint2*>(A + 512ull * t + 8 * lane);
-        const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
-        uint32_t cnt;
-        if ((uint64_t(t) + 1) * kTile <= n) {
-            uint4 o = decode_tile<true>(Ap, P, h.tlo, h.thi, s_esc, run, lane, 8, &cnt);
-            *reinterpret_cast<uint4*>(dst + i) = o;
-        } else {
-            uint32_t nvalid = i >= n ? 0u : uint32_t(min<uint64_t>(8, n - i));
-            uint4 o = decode_tile<false>(Ap, P, h.tlo, h.thi, s_esc, run, lane, nvalid, &cnt);
-            const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
-            for (uint32_t j = 0; j < nvalid; j++) dst[i + j] = uint16_t(ov[j >> 1] >> (16 * (j & 1)));
-        }
-        run += cnt;
-    }
-    if (run != last - first && lane == 0) or_status(status, ZIPCCL_STATUS_CORRUPT);
-}
-
-__global__ __launch_bounds__(kThreads) void decompress_kernel(const DArgs a)
-{
-    __shared__ uint8_t s_esc[kWaves][kBlock];
-    const uint32_t lane = lane_id();
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t unit = blockIdx.x;
-    const int s = find_segment<&DSeg::unit0>(a.seg, a.nseg, unit);
-    const uint32_t n = a.seg[s].n;
-    const uint32_t b = (unit - a.seg[s].unit0) * kWaves + wave;
-    if (b >= blocks_of(n)) return;
-    decode_block(a.seg[s].src, a.esc, a.esc_bytes, a.seg[s].dst, n, b, lane, s_esc[wave], a.status);
 }
 
 // --------------------------------------------------------------------------------
@@ -729,6 +616,26 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     }
     __syncthreads();
 
+    // ---- every peer's first 64 escape bytes of this tile, requested together ----
+    uint32_t before[kPeers], mine[kPeers], ev[kPeers];
+#pragma unroll
+    for (int p = 0; p < kPeers; p++) {
+        before[p] = mine[p] = ev[p] = 0;
+        if (uint32_t(p) < P) {
+            uint32_t bsum = 0, total = 0;
+#pragma unroll
+            for (uint32_t w = 0; w < kAccWaves; w++) {
+                const uint32_t v = s_cnt[p][w];
+                if (w < wave) bsum += v;
+                total += v;
+            }
+            before[p] = bsum;
+            mine[p] = s_cnt[p][wave];
+            bad = bad || total != blk[p];   // the offset table must agree with the planes
+            if (!bad && lane < mine[p]) ev[p] = a.esc[p][eoff[p] + off0[p] + bsum + lane];
+        }
+    }
+
     // ---- decode and add, peers in order ----
     float acc[8];
     {
@@ -739,48 +646,41 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     uint8_t* esc_lds = s_esc[wave];
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        if (uint32_t(p) < P) {
-            uint32_t before = 0, block_total = 0;
-#pragma unroll
-            for (uint32_t w = 0; w < kAccWaves; w++) {
-                const uint32_t v = s_cnt[p][w];
-                if (w < wave) before += v;
-                block_total += v;
+        if (uint32_t(p) < P && !bad && has_tile) {
+            // stage this peer's tile escapes in the wave's LDS slot
+            if (lane < mine[p]) esc_lds[lane] = uint8_t(ev[p]);
+            if (mine[p] > 64) {   // more than 64 escapes in one tile (escape-heavy tables)
+                const uint8_t* esc = a.esc[p] + eoff[p] + off0[p] + before[p];
+                for (uint32_t k = 64 + lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
             }
-            const uint32_t mine = s_cnt[p][wave];
-            bad = bad || block_total != blk[p];   // the offset table must agree with the planes
-            if (!bad && has_tile) {
-                const uint8_t* esc = a.esc[p] + eoff[p] + off0[p] + before;
-                for (uint32_t k = lane; k < mine; k += 64) esc_lds[k] = esc[k];
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                uint32_t E0 = perm(thi[p], tlo[p], codes_of_row(rows[p], 0));
-                uint32_t E1 = perm(thi[p], tlo[p], codes_of_row(rows[p], 1));
-                uint32_t z = zm[p], r = rank[p];
-                while (z) {   // this lane's escapes, in column order
-                    const uint32_t j = __builtin_ctz(z);
-                    const uint32_t x = esc_lds[r++];
-                    const uint32_t sh = 8 * (j & 3);
-                    if (j < 4) E0 = (E0 & ~(0xFFu << sh)) | (x << sh);
-                    else E1 = (E1 & ~(0xFFu << sh)) | (x << sh);
-                    z &= z - 1;
-                }
-                // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
-                const uint32_t lo0 = (Ap[p].x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
-                const uint32_t hi0 = (Ap[p].x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
-                const uint32_t lo1 = (Ap[p].y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
-                const uint32_t hi1 = (Ap[p].y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
-                    const uint32_t sel = 0x0C0Cu | ((j & 3u) << 16) | ((4u + (j & 3u)) << 24);
-                    const uint32_t f = j < 4 ? perm(hi0, lo0, sel) : perm(hi1, lo1, sel);
-                    acc[j] = acc[j] + __uint_as_float(f);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint32_t E0 = perm(thi[p], tlo[p], codes_of_row(rows[p], 0));
+            uint32_t E1 = perm(thi[p], tlo[p], codes_of_row(rows[p], 1));
+            uint32_t z = zm[p], r = rank[p];
+            while (z) {   // this lane's escapes, in column order
+                const uint32_t j = __builtin_ctz(z);
+                const uint32_t x = esc_lds[r++];
+                const uint32_t sh = 8 * (j & 3);
+                if (j < 4) E0 = (E0 & ~(0xFFu << sh)) | (x << sh);
+                else E1 = (E1 & ~(0xFFu << sh)) | (x << sh);
+                z &= z - 1;
             }
+            // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
+            const uint32_t lo0 = (Ap[p].x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
+            const uint32_t hi0 = (Ap[p].x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
+            const uint32_t lo1 = (Ap[p].y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
+            const uint32_t hi1 = (Ap[p].y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
+                const uint32_t sel = 0x0C0Cu | ((j & 3u) << 16) | ((4u + (j & 3u)) << 24);
+                const uint32_t f = j < 4 ? perm(hi0, lo0, sel) : perm(hi1, lo1, sel);
+                acc[j] = acc[j] + __uint_as_float(f);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
         }
     }
     if (bad) {
@@ -799,11 +699,138 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     }
 }
 
+// Decompress: one workgroup per unit of 4 blocks, one half block (4 tiles) per wave,
+// as in the encoder.  Each wave requests the A bytes and one plane dword per lane of
+// its 4 tiles at once, turns the planes back into per-lane rows with the half-wave bit
+// transpose (its own inverse), counts its escapes, learns through one barrier how
+// many escapes the first half of its block holds, then fetches its half block's
+// escapes and writes its 2048 values.
+constexpr uint32_t kDecHalfTiles = 4;
+
+__global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
+{
+    __shared__ uint32_t s_cnt[kEncWaves];
+    __shared__ uint8_t s_esc[kEncWaves][kHalf];
+    const uint32_t lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t unit = blockIdx.x;
+    const int s = find_segment<&DSeg::unit0>(a.seg, a.nseg, unit);
+    const DSeg& sg = a.seg[s];
+    const uint32_t n = sg.n;
+    const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
+    const uint32_t hb = (unit - sg.unit0) * kEncWaves + wave;   // half block within the segment
+    const uint32_t b = hb >> 1, half = hb & 1;
+    const bool active = b < K;
+    const uint32_t c = lane & 31u, h = lane >> 5;
+    const uint8_t* st = sg.src;
+
+    bool bad = false;
+    uint32_t first = 0, last = 0;
+    SegHeader hd = {};
+    uint2 Ap[kDecHalfTiles];
+    uint32_t pw[kDecHalfTiles];
+#pragma unroll
+    for (int k = 0; k < int(kDecHalfTiles); k++) {
+        Ap[k] = make_uint2(0, 0);
+        pw[k] = 0;
+    }
+    if (active) {
+        hd = read_header(st, n, a.esc_bytes);
+        const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
+        bad = !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
+        if (!bad) {
+#pragma unroll
+            for (int k = 0; k < int(kDecHalfTiles); k++) {
+                const uint32_t t = hb * kDecHalfTiles + k;
+                if (t < T) {
+                    Ap[k] = *reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane);
+                    if (c < 24) pw[k] = reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t)[2 * c + h];
+                }
+            }
+        }
+    }
+    // rows, escape flags, per-tile escape totals and this lane's rank within its tile
+    const Transpose32 tc = transpose_consts(lane);
+    uint32_t rows[kDecHalfTiles], zm[kDecHalfTiles], rank[kDecHalfTiles], tstart[kDecHalfTiles];
+    uint32_t half_total = 0;
+#pragma unroll
+    for (int k = 0; k < int(kDecHalfTiles); k++) {
+        const uint32_t t = hb * kDecHalfTiles + k;
+        const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
+        const uint32_t nvalid = (!active || t >= T || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
+        const uint32_t vmask = nvalid >= 8 ? 0xFFu : ((1u << nvalid) - 1u);
+        rows[k] = transpose32(pw[k], tc);
+        zm[k] = ~(rows[k] | (rows[k] >> 8) | (rows[k] >> 16)) & vmask;
+        const uint32_t cnt = __builtin_popcount(zm[k]);
+        uint32_t pre = 0, total = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const uint64_t bq = ballot((cnt >> q) & 1u);
+            pre += mbcnt(bq, 0u) << q;
+            total += uint32_t(__builtin_popcountll(bq)) << q;
+        }
+        rank[k] = pre;
+        tstart[k] = half_total;
+        half_total += total;
+    }
+    if (lane == 0) s_cnt[wave] = half_total;
+    __syncthreads();
+    if (!active) return;
+    const uint32_t other = s_cnt[wave ^ 1u];
+    const uint32_t half_start = half ? other : 0u;
+    bad = bad || half_total + other != last - first;   // the offset table must agree with the planes
+    if (bad) {
+        if (lane == 0) or_status(a.status, ZIPCCL_STATUS_CORRUPT);
+        return;
+    }
+    // every lane of the wave helps stage the half block's escapes
+    const uint8_t* esc = a.esc + hd.esc_offset + first + half_start;
+    uint8_t* esc_lds = s_esc[wave];
+    for (uint32_t k = lane; k < half_total; k += 64) esc_lds[k] = esc[k];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < int(kDecHalfTiles); k++) {
+        const uint32_t t = hb * kDecHalfTiles + k;
+        const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
+        const uint32_t nvalid = (t >= T || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
+        if (nvalid == 0) continue;
+        uint32_t E0 = perm(hd.thi, hd.tlo, codes_of_row(rows[k], 0));
+        uint32_t E1 = perm(hd.thi, hd.tlo, codes_of_row(rows[k], 1));
+        uint32_t z = zm[k], r = tstart[k] + rank[k];
+        while (z) {   // this lane's escapes, in column order
+            const uint32_t j = __builtin_ctz(z);
+            const uint32_t x = esc_lds[r++];
+            const uint32_t sh = 8 * (j & 3);
+            if (j < 4) E0 = (E0 & ~(0xFFu << sh)) | (x << sh);
+            else E1 = (E1 & ~(0xFFu << sh)) | (x << sh);
+            z &= z - 1;
+        }
+        // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
+        const uint32_t lo0 = (Ap[k].x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
+        const uint32_t hi0 = (Ap[k].x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
+        const uint32_t lo1 = (Ap[k].y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
+        const uint32_t hi1 = (Ap[k].y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
+        uint4 o;
+        o.x = perm(hi0, lo0, 0x05010400u);
+        o.y = perm(hi0, lo0, 0x07030602u);
+        o.z = perm(hi1, lo1, 0x05010400u);
+        o.w = perm(hi1, lo1, 0x07030602u);
+        if (nvalid == 8) {
+            *reinterpret_cast<uint4*>(sg.dst + i0) = o;
+        } else {
+            const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t j = 0; j < nvalid; j++) sg.dst[i0 + j] = uint16_t(ov[j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_compress(const CArgs& a, hipStream_t s)
 {
-    if (a.total_units > 0) hipLaunchKernelGGL(encode_kernel, dim3(a.total_units), dim3(kThreads), 0, s, a);
+    if (a.total_units > 0) hipLaunchKernelGGL(encode_kernel, dim3(a.total_units), dim3(kEncThreads), 0, s, a);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
     if (a.total_blocks > 0)
         hipLaunchKernelGGL(place_kernel, dim3((a.total_blocks + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
@@ -813,7 +840,7 @@ hipError_t launch_compress(const CArgs& a, hipStream_t s)
 hipError_t launch_decompress(const DArgs& a, hipStream_t s)
 {
     if (a.total_units == 0) return hipSuccess;
-    hipLaunchKernelGGL(decompress_kernel, dim3(a.total_units), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(decompress_kernel, dim3(a.total_units), dim3(kEncThreads), 0, s, a);
     return hipGetLastError();
 }
 
