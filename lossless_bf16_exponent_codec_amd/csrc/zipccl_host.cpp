@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -26,6 +27,16 @@ constexpr double kSwitchPhase = 0.7195805543641254;
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 zipccl_status hip_status(hipError_t e) { return e == hipSuccess ? ZIPCCL_OK : ZIPCCL_ERR_HIP; }
+
+// Largest launch (in workgroup units) whose escape positions the place kernel computes
+// itself.  ZIPCCL_DIRECT_PREFIX_MAX_UNITS lowers it, which tests use to exercise the
+// scan-kernel path on small inputs.
+uint64_t direct_prefix_max_units()
+{
+    const char* e = std::getenv("ZIPCCL_DIRECT_PREFIX_MAX_UNITS");
+    if (!e || !*e) return kDirectPrefixMaxUnits;
+    return std::min<uint64_t>(std::strtoull(e, nullptr, 10), kDirectPrefixMaxUnits);
+}
 
 void pack_table(const zipccl_plan_t& p, uint32_t& lo, uint32_t& hi)
 {
@@ -124,14 +135,17 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
     if (esc_cap > 0 && !esc_out) return ZIPCCL_ERR_INVALID;
     a.esc = static_cast<uint8_t*>(esc_out);
     a.esc_cap = esc_out ? esc_cap : 0;
-    a.counts = static_cast<uint32_t*>(workspace);
-    a.pos = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + ws_counts_bytes(blocks));
-    a.stage = static_cast<uint8_t*>(workspace) + ws_counts_bytes(blocks) + ws_pos_bytes(blocks);
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.counts = reinterpret_cast<uint32_t*>(w);
+    a.pos = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(blocks));
+    a.unit_counts = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(blocks) + ws_pos_bytes(blocks));
+    a.stage = w + ws_counts_bytes(blocks) + ws_pos_bytes(blocks) + ws_units_bytes(blocks);
     a.n_esc_out = n_esc_out;
     a.status = status;
     a.nseg = nseg;
     a.total_units = uint32_t(units);
     a.total_blocks = uint32_t(blocks);
+    a.direct = (units > 0 && units <= direct_prefix_max_units()) ? 1u : 0u;
     return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -22,14 +22,20 @@ constexpr uint32_t kEncThreads = 64 * kEncWaves;
 
 // Compress workspace: a u32 escape count per half block of the launch, the
 // launch-wide position of every half block's first escape (one more entry for the
-// total), then a staging slot of kHalf bytes per half block that holds its escape
-// exponents until their positions are known.
+// total; used only when the positions come from the scan kernel), a u32 escape count
+// per workgroup unit, then a staging slot of kHalf bytes per half block that holds its
+// escape exponents until their positions are known.
 __host__ __device__ inline uint64_t ws_counts_bytes(uint64_t blocks) { return (8 * blocks + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_pos_bytes(uint64_t blocks) { return (4 * (2 * blocks + 1) + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_units_bytes(uint64_t blocks) { return (4 * (blocks + 1) + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_bytes(uint64_t blocks)
 {
-    return ws_counts_bytes(blocks) + ws_pos_bytes(blocks) + uint64_t(kBlock) * blocks;
+    return ws_counts_bytes(blocks) + ws_pos_bytes(blocks) + ws_units_bytes(blocks) + uint64_t(kBlock) * blocks;
 }
+
+// Up to this many workgroup units (2^28 values) the place kernel sums the unit counts
+// before its unit itself; above, a one-workgroup scan kernel computes the positions.
+constexpr uint32_t kDirectPrefixMaxUnits = 16384;
 
 struct CSeg {              // compress: one segment
     const uint16_t* src;   // n BF16 values
@@ -48,13 +54,14 @@ struct CArgs {
     uint64_t esc_cap;
     uint32_t* counts;      // workspace: escapes per half block
     uint32_t* pos;         // workspace: launch-wide position of each half block's first escape
+    uint32_t* unit_counts; // workspace: escapes per workgroup unit
     uint8_t* stage;        // workspace: kHalf bytes per half block
     uint64_t* n_esc_out;   // nseg + 1 entries or null
     uint32_t* status;      // or null
     int32_t nseg;
     uint32_t total_units;
     uint32_t total_blocks;
-    uint32_t pad;
+    uint32_t direct;       // 1: the place kernel computes positions from unit_counts
 };
 
 struct DSeg {              // decompress: one segment

@@ -196,8 +196,8 @@ __device__ inline uint32_t encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, 
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
 // planes, the escape count and the staged escape exponents; zero padding after the
 // segment's last half block.  gh: the half block's launch-wide index.
-__device__ inline void encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
-                                   uint32_t lane, const uint32_t* lut, const Transpose32& tc, uint8_t* s_esc)
+__device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
+                                       uint32_t lane, const uint32_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
     const uint32_t n = sg.n;
     const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
@@ -236,6 +236,7 @@ __device__ inline void encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, 
         uint8_t* cp = dst + offsets_off(n) + 4ull * K;
         for (uint32_t k = lane; k < cpad; k += 64) cp[k] = 0;
     }
+    return run;
 }
 
 // Encode: one workgroup per unit of 4 blocks, one half block per wave.  No workgroup
@@ -267,6 +268,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
             for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, t0 + k, lane, n);
         }
     }
+    __shared__ uint32_t s_hcnt[kEncWaves];
     if (tid < 256) {   // exponent -> spread code of this segment
         uint32_t code = 0;
 #pragma unroll
@@ -278,8 +280,18 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     }
     const Transpose32 tc = transpose_consts(lane);
     __syncthreads();
-    if (!active) return;
-    encode_half(a, sg, hb, 2 * sg.block0 + hb, v, lane, s_lut, tc, s_esc[wave]);
+    uint32_t run = 0;
+    if (active) run = encode_half(a, sg, hb, 2 * sg.block0 + hb, v, lane, s_lut, tc, s_esc[wave]);
+    if (a.direct) {   // the unit's escape count, for the place kernel's prefix sums
+        if (lane == 0) s_hcnt[wave] = run;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t t = 0;
+#pragma unroll
+            for (uint32_t w = 0; w < kEncWaves; w++) t += s_hcnt[w];
+            a.unit_counts[unit] = t;
+        }
+    }
 }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
@@ -378,7 +390,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
         carry += total;
     }
     if (tid == 0) a.pos[Kt] = carry;
-    if (tid == 0 && a.n_esc_out) a.n_esc_out[a.nseg] = carry;
+    if (tid == 0 && a.n_esc_out && Kt == 0) a.n_esc_out[a.nseg] = 0;
     if (Kt == 0 && wave == 0) {   // only empty segments: every header says offset 0
         for (int s = 0; s < a.nseg; s++) {
             write_empty_header(a.seg[s], lane, 0u);
@@ -389,8 +401,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
 
 // Copies one half block's staged escapes to esc[p ...]; `head` holds staged bytes
 // 4*hl .. 4*hl+3 (hl = lane within the half of the wave that loaded them).
-__device__ inline bool place_half(const CArgs& a, const uint8_t* stage, uint32_t head, uint32_t hl, uint32_t p,
-                                  uint32_t cnt)
+__device__ inline bool place_half(const CArgs& a, uint32_t head, uint32_t hl, uint32_t p, uint32_t cnt)
 {
     bool over = false;
 #pragma unroll
@@ -405,28 +416,20 @@ __device__ inline bool place_half(const CArgs& a, const uint8_t* stage, uint32_t
     return over;
 }
 
-// Place: one wave per block.  Writes the block's offset-table entry, moves the staged
-// escape bytes of its two half blocks to their compacted position, and writes the
-// segment header from the wave of the segment's last block.  The first 128 staged
-// bytes of each half are requested together with the positions, so a typical block
-// costs one round trip.
-__global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
+// Places block gb (launch-wide) of segment s: its offset-table entry, the staged escape
+// bytes of its two half blocks (positions p0, p1, p2 = start of half 0, half 1, end;
+// base = the segment's first escape), the segment header from the segment's last
+// block, and the headers of empty segments next to it.  The first 128 staged bytes of
+// each half are requested before the positions are needed.
+__device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint32_t head, uint32_t p0, uint32_t p1,
+                                   uint32_t p2, uint32_t base, uint32_t lane)
 {
-    const uint32_t lane = lane_id();
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t gb = blockIdx.x * kWaves + wave;
-    if (gb >= a.total_blocks) return;
-    const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
     const CSeg& sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
     const uint32_t hl = lane & 31u, hsel = lane >> 5;
-    const uint8_t* stage = a.stage + uint64_t(2 * gb + hsel) * kHalf;   // lanes 0-31: half 0, 32-63: half 1
-    const uint32_t head = reinterpret_cast<const uint32_t*>(stage)[hl];
-    const uint32_t p0 = a.pos[2 * gb], p1 = a.pos[2 * gb + 1], p2 = a.pos[2 * gb + 2];
-    const uint32_t base = a.pos[2 * sg.block0];
     if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
     const uint32_t hp = hsel ? p1 : p0, hc = hsel ? p2 - p1 : p1 - p0;
-    bool over = place_half(a, stage, head, hl, hp, hc);
+    bool over = place_half(a, head, hl, hp, hc);
     for (uint32_t hh = 0; hh < 2; hh++) {   // rare: more than 128 escapes in a half block
         const uint32_t c = hh ? p2 - p1 : p1 - p0, q = hh ? p1 : p0;
         const uint8_t* st = a.stage + uint64_t(2 * gb + hh) * kHalf;
@@ -438,9 +441,8 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
     }
     if (over) or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     if (gb == sg.block0 + K - 1) {
-        const uint32_t end = a.pos[2 * (sg.block0 + K)];
-        write_header(sg, lane, end - base, base);
-        if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = end - base;
+        write_header(sg, lane, p2 - base, base);
+        if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = p2 - base;
     }
     // empty segments just before this one start where it starts; those after the
     // launch's last block start at the end
@@ -455,6 +457,111 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
             write_empty_header(a.seg[e], lane, p2);
             if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
         }
+        if (lane == 0 && a.n_esc_out) a.n_esc_out[a.nseg] = p2;
+    }
+}
+
+// Staged bytes 4*hl .. 4*hl+3 of this lane's half of block gb (lanes 0-31: half 0).
+__device__ inline uint32_t stage_head(const CArgs& a, uint32_t gb, uint32_t lane)
+{
+    const uint8_t* stage = a.stage + uint64_t(2 * gb + (lane >> 5)) * kHalf;
+    return reinterpret_cast<const uint32_t*>(stage)[lane & 31u];
+}
+
+// Place, after the scan kernel: one wave per block, positions from pos[].
+__global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t gb = blockIdx.x * kWaves + wave;
+    if (gb >= a.total_blocks) return;
+    const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
+    const uint32_t head = stage_head(a, gb, lane);
+    const uint32_t p0 = a.pos[2 * gb], p1 = a.pos[2 * gb + 1], p2 = a.pos[2 * gb + 2];
+    place_block(a, s, gb, head, p0, p1, p2, a.pos[2 * a.seg[s].block0], lane);
+}
+
+// Place without the scan kernel: one workgroup per 8 encode units, one unit (4 blocks)
+// per wave.  The workgroup sums the escape counts of all units before its first one
+// (and before the first unit of that unit's segment) from unit_counts[], a few
+// kilobytes read from L2; each wave then derives its blocks' positions from its unit's
+// 8 half-block counts.  The staged heads of all 4 blocks are requested first.
+constexpr uint32_t kPlaceUnits = 8;
+constexpr uint32_t kPlaceThreads = 64 * kPlaceUnits;
+
+__global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a)
+{
+    __shared__ uint32_t s_red[2][kPlaceUnits];
+    __shared__ uint32_t s_ucnt[kPlaceUnits];
+    const uint32_t tid = threadIdx.x, lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t u_first = blockIdx.x * kPlaceUnits;
+    const uint32_t unit = u_first + wave;
+    const bool active = unit < a.total_units;
+    const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
+    const CSeg& sg = a.seg[s];
+    const uint32_t K = uint32_t(blocks_of(sg.n));
+    const uint32_t b0 = (unit - sg.unit0) * kWaves;   // first block of the unit within the segment
+    uint32_t head[kWaves];
+#pragma unroll
+    for (uint32_t k = 0; k < kWaves; k++) head[k] = (active && b0 + k < K) ? stage_head(a, sg.block0 + b0 + k, lane) : 0u;
+    if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
+
+    // escapes before the group's first unit and before the first unit of its segment
+    const int s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
+    const uint32_t u0 = a.seg[s_first].unit0;
+    uint32_t acc = 0, accs = 0;
+    for (uint32_t i = 4 * tid; i < u_first; i += 4 * kPlaceThreads) {
+        uint32_t v[4];
+        if (i + 4 <= u_first) {
+            const uint4 q = *reinterpret_cast<const uint4*>(a.unit_counts + i);
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; k++) v[k] = i + k < u_first ? a.unit_counts[i + k] : 0u;
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < 4; k++) {
+            acc += v[k];
+            if (i + k < u0) accs += v[k];
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        acc += __shfl_xor(acc, o, 64);
+        accs += __shfl_xor(accs, o, 64);
+    }
+    if (lane == 0) {
+        s_red[0][wave] = acc;
+        s_red[1][wave] = accs;
+    }
+    __syncthreads();
+    if (!active) return;
+    uint32_t pre = 0, first_base = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kPlaceUnits; w++) {
+        pre += s_red[0][w];
+        first_base += s_red[1][w];
+    }
+    // this unit's position, and its segment's first escape: a segment that starts inside
+    // the group starts at `pre` plus the units of the group before it; otherwise it is
+    // the segment of the group's first unit, whose start was summed above
+    uint32_t upos = pre;
+    for (uint32_t w = 0; w < wave; w++) upos += s_ucnt[w];
+    uint32_t base = first_base;
+    if (sg.unit0 >= u_first) {
+        base = pre;
+        for (uint32_t w = 0; w < sg.unit0 - u_first; w++) base += s_ucnt[w];
+    }
+    // positions of the unit's blocks from its 8 half-block counts
+    const uint32_t* hc = a.counts + 2 * (sg.block0 + b0);
+    uint32_t p = upos;
+#pragma unroll
+    for (uint32_t k = 0; k < kWaves; k++) {
+        if (b0 + k >= K) break;
+        const uint32_t p0 = p, p1 = p0 + hc[2 * k], p2 = p1 + hc[2 * k + 1];
+        place_block(a, s, sg.block0 + b0 + k, head[k], p0, p1, p2, base, lane);
+        p = p2;
     }
 }
 
@@ -831,9 +938,14 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
 hipError_t launch_compress(const CArgs& a, hipStream_t s)
 {
     if (a.total_units > 0) hipLaunchKernelGGL(encode_kernel, dim3(a.total_units), dim3(kEncThreads), 0, s, a);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
-    if (a.total_blocks > 0)
-        hipLaunchKernelGGL(place_kernel, dim3((a.total_blocks + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
+    if (a.direct) {
+        hipLaunchKernelGGL(place_direct_kernel, dim3((a.total_units + kPlaceUnits - 1) / kPlaceUnits),
+                           dim3(kPlaceThreads), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+        if (a.total_blocks > 0)
+            hipLaunchKernelGGL(place_kernel, dim3((a.total_blocks + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

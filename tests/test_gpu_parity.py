@@ -274,3 +274,37 @@ def test_accumulate_corrupt_peer(Z):
                             status, esc_bytes=[r["esc"].numel()] * 3)
     torch.cuda.synchronize()
     assert int(status.item()) & Z.STATUS_CORRUPT
+
+
+# ------------------------------------------------------------------------------------
+# the scan-kernel path for escape positions (used above 2^28 values per call), forced
+# on small inputs
+# ------------------------------------------------------------------------------------
+@pytest.fixture
+def scan_path(monkeypatch):
+    monkeypatch.setenv("ZIPCCL_DIRECT_PREFIX_MAX_UNITS", "0")
+    yield
+
+
+def test_scan_path_many_segments(Z, scan_path):
+    rng = np.random.default_rng(6)
+    segs, plans = [], []
+    for k in range(40):
+        n = int(rng.choice([0, 1, 700, 4096, 16384, 20000, 70001, 300000]))
+        s = float(10 ** rng.uniform(-4, 1))
+        segs.append(W.gaussian_bf16(n, s, 900 + k))
+        plans.append(Z.plan(sigma=s))
+    round_trip(Z, segs, plans)
+
+
+def test_scan_path_empty_and_overflow(Z, scan_path):
+    sizes = [0, 0, 256 * 4096, 0, 5, 0, 4096 * 300 + 17, 0, 0]
+    segs = [W.gaussian_bf16(n, 0.05, 70 + k) for k, n in enumerate(sizes)]
+    round_trip(Z, segs, [Z.plan(sigma=0.05)] * len(segs))
+    round_trip(Z, [np.zeros(0, np.uint16)] * 3, [Z.plan(sigma=1.0)] * 3)
+    x = W.gaussian_bf16(50000, 1.0, 5)
+    p = Z.plan(table=[1, 2, 3, 4, 5, 6, 7])
+    r = gpu_compress(Z, [x], [p], esc_cap=1000)
+    assert r["status"] & Z.STATUS_ESC_OVERFLOW
+    st, esc, ne, rc = O.compress_batch([x], oracle_tables([p]))
+    assert np.array_equal(r["static_h"], st) and np.array_equal(r["esc_h"][:1000], esc[:1000])
