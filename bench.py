@@ -339,10 +339,14 @@ def main(argv=None) -> int:
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                 "bytes_per_launch": moved, "avg_launch_us": round(avg_ms * 1e3, 2), "traffic": None}
 
-    # the step's dominant kernel: decompress is one launch; compress is three
-    # (encode_kernel, scan_kernel, place_kernel), timed together by the events
+    # the step's dominant kernel: decompress is one launch; compress is two (encode_kernel,
+    # place_direct_kernel; three with scan_kernel above 2^28 values), timed together by
+    # the events
+    units = sum((m + 16383) // 16384 for m in bc.sizes)
+    c_launches = (["encode_kernel", "place_direct_kernel"] if units <= 16384
+                  else ["encode_kernel", "scan_kernel", "place_kernel"])
     roof_d = roof("decompress_kernel", d_avg, ["decompress_kernel"])
-    roof_c = roof("compress", c_avg, ["encode_kernel", "scan_kernel", "place_kernel"])
+    roof_c = roof("compress", c_avg, c_launches)
     primary, secondary = (roof_d, roof_c) if d_avg >= c_avg else (roof_c, roof_d)
     out = {
         "metric": METRIC,

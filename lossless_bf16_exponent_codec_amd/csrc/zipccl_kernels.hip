@@ -130,104 +130,175 @@ __device__ inline uint32_t transpose32(uint32_t x, const Transpose32& c)
     return transpose_stage<4>(x, c);
 }
 
-// Code table entry for exponent e: bit p of the code moved to bit 8p, and bit 24 set
-// when the code is 0 (an escape).  Shifting the entry of column j left by j and OR-ing
-// the 8 columns gives a lane word whose byte p holds plane p of the lane's 8 values
-// and whose byte 3 flags its escapes.
-__device__ inline uint32_t spread_code(uint32_t code)
+// Inclusive prefix sum over the 64 lanes of the wave (every lane active): running sums
+// inside each row of 16 lanes by DPP row shifts, then the totals of rows 0 and 2, and
+// of rows 0-1, added to the rows after them (DPP row broadcasts).
+__device__ inline uint32_t wave_scan_incl(uint32_t x)
 {
-    return (code & 1u) | ((code & 2u) << 7) | ((code & 4u) << 14) | (code == 0 ? (1u << 24) : 0u);
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xF, 0xF, true));    // row_shr:1
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xF, 0xF, true));    // row_shr:2
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xF, 0xF, true));    // row_shr:4
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xF, 0xF, true));    // row_shr:8
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xA, 0xF, false));   // row_bcast:15
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return x;
 }
 
+// Escape ranks for kN counts per lane (kN even; each count at most 512, so two share a
+// dword as 16-bit fields and one scan serves both).  excl[i]: escapes of count i in
+// the lanes below this one; total[i]: of the whole wave.  Counts from `live` on are 0
+// and skipped (live is the same in every lane).
+template <int kN>
+__device__ inline void wave_ranks(const uint32_t (&cnt)[kN], uint32_t (&excl)[kN], uint32_t (&total)[kN],
+                                  uint32_t live = kN)
+{
+#pragma unroll
+    for (int i = 0; i < kN; i += 2) {
+        excl[i] = excl[i + 1] = total[i] = total[i + 1] = 0;
+        if (uint32_t(i) >= live) continue;
+        const uint32_t x = cnt[i] | (cnt[i + 1] << 16);
+        const uint32_t incl = wave_scan_incl(x);
+        const uint32_t t = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+        const uint32_t e = incl - x;   // no borrow between the fields: incl >= x in each
+        excl[i] = e & 0xFFFFu;
+        excl[i + 1] = e >> 16;
+        total[i] = t & 0xFFFFu;
+        total[i + 1] = t >> 16;
+    }
+}
+
+// Ranks of a wave's escapes over its 4 tiles in value order (tile by tile, lanes in
+// order inside a tile): start[k] = position of this lane's first escape of tile k.
+// Returns the escapes of all 4 tiles.
+__device__ inline uint32_t half_ranks(const uint32_t (&cnt)[4], uint32_t (&start)[4])
+{
+    uint32_t excl[4], total[4];
+    wave_ranks<4>(cnt, excl, total);
+    uint32_t base = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        start[k] = base + excl[k];
+        base += total[k];
+    }
+    return base;
+}
+
+// Orders LDS writes of the wave's lanes before the reads of other lanes of the wave.
+__device__ inline void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Code table entry of an exponent (one byte): the 3-bit code in bits 0-2, bit 3 set
+// when the code is 0 (an escape).  Encoder row of a lane: the entry of column j shifted
+// left by 4j, so bit 4j + p is plane p of column j and bit 4j + 3 flags an escape.
+__device__ inline uint32_t code_entry(uint32_t code) { return code | (code == 0 ? 8u : 0u); }
+
+// Plane dword stored by a lane after the encoder's transpose: lane c of half h holds
+// row bit c = 4j + p, i.e. bit p of column j for the 32 lanes of the half, which is
+// dword h of plane word 8p + j; lanes with p = 3 hold escape flags and store nothing.
+__device__ inline uint32_t encoder_plane_dword(uint32_t lane)
+{
+    const uint32_t c = lane & 31u, p = c & 3u;
+    return p < 3 ? 2 * (8 * p + (c >> 2)) + (lane >> 5) : ~0u;
+}
+
+// What one tile leaves for the escape pass: the lane's escape flags (bit 4j + 3 for
+// column j) and the 8 exponents of the lane (columns 0-3 in e0, 4-7 in e1, one byte
+// each).
+struct TileEsc {
+    uint32_t m, e0, e1;
+};
+
 // Encodes one tile held by the wave.  kFull: all 512 values exist (else `nvalid` of
-// this lane's 8 values do).  Writes the 512 A bytes and the 192 plane bytes, appends
-// the tile's escape exponents to the wave's LDS staging area from `run` on, and
-// returns the tile's escape count.
+// this lane's 8 values do).  Writes the 512 A bytes and the 192 plane bytes.
 template <bool kFull>
-__device__ inline uint32_t encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, const uint32_t* s_lut,
-                                       const Transpose32& tc, uint8_t* A_tile, uint32_t* B_tile, uint8_t* s_esc,
-                                       uint32_t run)
+__device__ inline TileEsc encode_tile(uint4 v, uint32_t lane, uint32_t nvalid, const uint8_t* s_lut,
+                                      const Transpose32& tc, uint32_t bdw, uint8_t* A_tile, uint32_t* B_tile)
 {
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-    uint32_t e[8];
     uint32_t row = 0;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        e[j] = (d[j >> 1] >> (7 + 16 * (j & 1))) & 0xFFu;
-        uint32_t ent = s_lut[e[j]];
+        uint32_t ent = s_lut[(d[j >> 1] >> (7 + 16 * (j & 1))) & 0xFFu];
         if (!kFull && uint32_t(j) >= nvalid) ent = 0;   // not a value: no plane bits, no escape
-        row |= ent << j;
+        row |= ent << (4 * j);
     }
     // sign+mantissa bytes: low byte of a BF16 holds the mantissa (bits 0-6), high byte
     // the sign (bit 7).  Gather low and high bytes of 4 values, then merge.
-    uint32_t lo0 = perm(d[1], d[0], 0x06040200u), hi0 = perm(d[1], d[0], 0x07050301u);
-    uint32_t lo1 = perm(d[3], d[2], 0x06040200u), hi1 = perm(d[3], d[2], 0x07050301u);
+    const uint32_t lo0 = perm(d[1], d[0], 0x06040200u), hi0 = perm(d[1], d[0], 0x07050301u);
+    const uint32_t lo1 = perm(d[3], d[2], 0x06040200u), hi1 = perm(d[3], d[2], 0x07050301u);
     uint2 a;
     a.x = (lo0 & 0x7F7F7F7Fu) | (hi0 & 0x80808080u);
     a.y = (lo1 & 0x7F7F7F7Fu) | (hi1 & 0x80808080u);
     store_nt(reinterpret_cast<uint2*>(A_tile + 8 * lane), a);
 
-    // Plane words.  Row bit 8p + j of lane l is bit p of code(8l + j); after the
-    // transpose, lane c of half h holds bit l - 32h of it for l in the half, which is
-    // the 32-bit half h of plane word w = c = 8p + j: dword 2w + h of the tile.
-    const uint32_t col = transpose32(row & 0x00FFFFFFu, tc);
-    const uint32_t c = lane & 31u, h = lane >> 5;
-    if (c < 24) store_nt(B_tile + 2 * c + h, col);
+    const uint32_t col = transpose32(row, tc);
+    if (bdw != ~0u) store_nt(B_tile + bdw, col);
 
-    // escapes in value order: lower lanes first, then this lane's columns in order
-    const uint32_t zm = row >> 24;
-    const uint32_t cnt = __builtin_popcount(zm);
-    uint32_t r = run, total = 0;
-#pragma unroll
-    for (int k = 0; k < 4; k++) {   // prefix over lower lanes of cnt, one bit of cnt at a time
-        const uint64_t bk = ballot((cnt >> k) & 1u);
-        r += mbcnt(bk, 0u) << k;
-        total += uint32_t(__builtin_popcountll(bk)) << k;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint32_t bit = (zm >> j) & 1u;
-        if (bit) s_esc[r] = uint8_t(e[j]);
-        r += bit;
-    }
-    return total;
+    TileEsc r;
+    r.m = row & 0x88888888u;
+    // exponent = low 7 bits of the high byte, then bit 7 of the low byte
+    r.e0 = ((hi0 << 1) & 0xFEFEFEFEu) | ((lo0 >> 7) & 0x01010101u);
+    r.e1 = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
+    return r;
+}
+
+// Writes the lane's escape exponents of one tile to s_esc from position r on, in
+// column order.  Most lanes have none or one, so the loop is short.
+__device__ inline void stage_tile_escapes(const TileEsc& te, uint32_t r, uint8_t* s_esc)
+{
+    for (uint32_t m = te.m; m; m &= m - 1) s_esc[r++] = uint8_t(perm(te.e1, te.e0, __builtin_ctz(m) >> 2));
 }
 
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
 // planes, the escape count and the staged escape exponents; zero padding after the
 // segment's last half block.  gh: the half block's launch-wide index.
 __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
-                                       uint32_t lane, const uint32_t* lut, const Transpose32& tc, uint8_t* s_esc)
+                                       uint32_t lane, const uint8_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
     const uint32_t n = sg.n;
     const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
     uint8_t* dst = sg.dst;
     uint8_t* A = dst + 128;
     uint32_t* B = reinterpret_cast<uint32_t*>(dst + planes_off(n));
+    const uint32_t bdw = encoder_plane_dword(lane);
     const uint32_t t0 = hb * 4;
-    uint32_t run = 0;
+    TileEsc te[4];
     if (uint64_t(t0 + 4) * kTile <= n) {
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const uint32_t t = t0 + k;
-            run += encode_tile<true>(v[k], lane, 8, lut, tc, A + 512ull * t, B + 48ull * t, s_esc, run);
+            te[k] = encode_tile<true>(v[k], lane, 8, lut, tc, bdw, A + 512ull * t, B + 48ull * t);
         }
     } else {
         const uint32_t ntiles = t0 < T ? min(4u, T - t0) : 0u;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const uint32_t t = t0 + k;
+            te[k] = TileEsc{0, 0, 0};
             if (uint32_t(k) < ntiles) {
                 const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
                 const uint32_t nvalid = i >= n ? 0u : uint32_t(min<uint64_t>(8, n - i));
-                run += encode_tile<false>(v[k], lane, nvalid, lut, tc, A + 512ull * t, B + 48ull * t, s_esc, run);
+                te[k] = encode_tile<false>(v[k], lane, nvalid, lut, tc, bdw, A + 512ull * t, B + 48ull * t);
             }
         }
     }
-    // hand the escapes to the scan and place kernels
+    // escapes in value order: tile by tile, lower lanes first, a lane's columns in order
+    uint32_t cnt[4], start[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) cnt[k] = __builtin_popcount(te[k].m);
+    const uint32_t run = min(half_ranks(cnt, start), kHalf);
+#pragma unroll
+    for (int k = 0; k < 4; k++) stage_tile_escapes(te[k], start[k], s_esc);
+    wave_lds_sync();
+    // hand the escapes to the place kernel (whole dwords; bytes past `run` are unused)
     if (lane == 0) a.counts[gh] = run;
     uint8_t* stage = a.stage + uint64_t(gh) * kHalf;
-    for (uint32_t k = lane; k < run; k += 64) stage[k] = s_esc[k];
+    for (uint32_t k = 4 * lane; k < run; k += 256)
+        *reinterpret_cast<uint32_t*>(stage + k) = *reinterpret_cast<const uint32_t*>(s_esc + k);
     if (hb == 2 * K - 1) {   // zero padding of the plane and offset sections
         const uint32_t bpad = uint32_t(round128(192ull * T) - 192ull * T);
         uint8_t* bp = reinterpret_cast<uint8_t*>(B) + 192ull * T;
@@ -244,8 +315,8 @@ __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t 
 // and its staged escape exponents.
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
 {
-    __shared__ uint32_t s_lut[256];
-    __shared__ uint8_t s_esc[kEncWaves][kHalf];
+    __shared__ uint8_t s_lut[256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_esc[kEncWaves][kHalf];
 
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -269,14 +340,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
         }
     }
     __shared__ uint32_t s_hcnt[kEncWaves];
-    if (tid < 256) {   // exponent -> spread code of this segment
+    if (tid < 256) {   // exponent -> code entry of this segment
         uint32_t code = 0;
 #pragma unroll
         for (int r = 0; r < 7; r++) {
             const uint32_t te = (r < 4 ? (sg.table_lo >> (8 * r)) : (sg.table_hi >> (8 * (r - 4)))) & 0xFFu;
             if (te == tid) code = r + 1;
         }
-        s_lut[tid] = spread_code(code);
+        s_lut[tid] = uint8_t(code_entry(code));
     }
     const Transpose32 tc = transpose_consts(lane);
     __syncthreads();
@@ -399,17 +470,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
     }
 }
 
-// Copies one half block's staged escapes to esc[p ...]; `head` holds staged bytes
-// 4*hl .. 4*hl+3 (hl = lane within the half of the wave that loaded them).
-__device__ inline bool place_half(const CArgs& a, uint32_t head, uint32_t hl, uint32_t p, uint32_t cnt)
+// Copies the first 256 staged escapes of one half block to esc[p ...]; `head` holds
+// staged bytes 8*hl .. 8*hl+7 (hl = lane within the half of the wave that loaded them).
+__device__ inline bool place_half(const CArgs& a, uint2 head, uint32_t hl, uint32_t p, uint32_t cnt)
 {
     bool over = false;
 #pragma unroll
-    for (uint32_t q = 0; q < 4; q++) {
-        const uint32_t k = 4 * hl + q;
+    for (uint32_t q = 0; q < 8; q++) {
+        const uint32_t k = 8 * hl + q;
         if (k < cnt) {
             const uint64_t at = uint64_t(p) + k;
-            if (at < a.esc_cap) a.esc[at] = uint8_t(head >> (8 * q));
+            if (at < a.esc_cap) a.esc[at] = uint8_t((q < 4 ? head.x : head.y) >> (8 * (q & 3)));
             else over = true;
         }
     }
@@ -419,9 +490,9 @@ __device__ inline bool place_half(const CArgs& a, uint32_t head, uint32_t hl, ui
 // Places block gb (launch-wide) of segment s: its offset-table entry, the staged escape
 // bytes of its two half blocks (positions p0, p1, p2 = start of half 0, half 1, end;
 // base = the segment's first escape), the segment header from the segment's last
-// block, and the headers of empty segments next to it.  The first 128 staged bytes of
+// block, and the headers of empty segments next to it.  The first 256 staged bytes of
 // each half are requested before the positions are needed.
-__device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint32_t head, uint32_t p0, uint32_t p1,
+__device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint2 head, uint32_t p0, uint32_t p1,
                                    uint32_t p2, uint32_t base, uint32_t lane)
 {
     const CSeg& sg = a.seg[s];
@@ -430,10 +501,10 @@ __device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint32_t 
     if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
     const uint32_t hp = hsel ? p1 : p0, hc = hsel ? p2 - p1 : p1 - p0;
     bool over = place_half(a, head, hl, hp, hc);
-    for (uint32_t hh = 0; hh < 2; hh++) {   // rare: more than 128 escapes in a half block
+    for (uint32_t hh = 0; hh < 2; hh++) {   // rare: more than 256 escapes in a half block
         const uint32_t c = hh ? p2 - p1 : p1 - p0, q = hh ? p1 : p0;
         const uint8_t* st = a.stage + uint64_t(2 * gb + hh) * kHalf;
-        for (uint32_t k = 128 + lane; k < c; k += 64) {
+        for (uint32_t k = 256 + lane; k < c; k += 64) {
             const uint64_t at = uint64_t(q) + k;
             if (at < a.esc_cap) a.esc[at] = st[k];
             else over = true;
@@ -461,11 +532,11 @@ __device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint32_t 
     }
 }
 
-// Staged bytes 4*hl .. 4*hl+3 of this lane's half of block gb (lanes 0-31: half 0).
-__device__ inline uint32_t stage_head(const CArgs& a, uint32_t gb, uint32_t lane)
+// Staged bytes 8*hl .. 8*hl+7 of this lane's half of block gb (lanes 0-31: half 0).
+__device__ inline uint2 stage_head(const CArgs& a, uint32_t gb, uint32_t lane)
 {
     const uint8_t* stage = a.stage + uint64_t(2 * gb + (lane >> 5)) * kHalf;
-    return reinterpret_cast<const uint32_t*>(stage)[lane & 31u];
+    return reinterpret_cast<const uint2*>(stage)[lane & 31u];
 }
 
 // Place, after the scan kernel: one wave per block, positions from pos[].
@@ -476,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
     const uint32_t gb = blockIdx.x * kWaves + wave;
     if (gb >= a.total_blocks) return;
     const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
-    const uint32_t head = stage_head(a, gb, lane);
+    const uint2 head = stage_head(a, gb, lane);
     const uint32_t p0 = a.pos[2 * gb], p1 = a.pos[2 * gb + 1], p2 = a.pos[2 * gb + 2];
     place_block(a, s, gb, head, p0, p1, p2, a.pos[2 * a.seg[s].block0], lane);
 }
@@ -502,10 +573,15 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
     const CSeg& sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
     const uint32_t b0 = (unit - sg.unit0) * kWaves;   // first block of the unit within the segment
-    uint32_t head[kWaves];
+    uint2 head[kWaves];
 #pragma unroll
-    for (uint32_t k = 0; k < kWaves; k++) head[k] = (active && b0 + k < K) ? stage_head(a, sg.block0 + b0 + k, lane) : 0u;
+    for (uint32_t k = 0; k < kWaves; k++)
+        head[k] = (active && b0 + k < K) ? stage_head(a, sg.block0 + b0 + k, lane) : make_uint2(0, 0);
     if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
+    uint32_t hc[2 * kWaves];   // the unit's half-block escape counts
+#pragma unroll
+    for (uint32_t k = 0; k < 2 * kWaves; k++)
+        hc[k] = (active && b0 + k / 2 < K) ? a.counts[2 * (sg.block0 + b0) + k] : 0u;
 
     // escapes before the group's first unit and before the first unit of its segment
     const int s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
@@ -554,7 +630,6 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
         for (uint32_t w = 0; w < sg.unit0 - u_first; w++) base += s_ucnt[w];
     }
     // positions of the unit's blocks from its 8 half-block counts
-    const uint32_t* hc = a.counts + 2 * (sg.block0 + b0);
     uint32_t p = upos;
 #pragma unroll
     for (uint32_t k = 0; k < kWaves; k++) {
@@ -625,21 +700,72 @@ __device__ inline uint32_t round_bf16_bits(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Spreads bits 0..3 of x to bit 0 of bytes 0..3 (x < 16; the four partial products
-// of the multiply land on distinct bits, so nothing carries).
-__device__ inline uint32_t spread4(uint32_t x) { return __umul24(x, 0x00204081u) & 0x01010101u; }
-
-// Codes of 4 columns as bytes, from a lane row whose byte p holds plane p of the lane's
-// 8 columns (column j at bit j): columns 0..3 for half 0, 4..7 for half 1.
-__device__ inline uint32_t codes_of_row(uint32_t row, int half)
+// Plane dword a lane loads in the decoders, chosen so that after the half-wave transpose
+// byte b of the lane's row holds the code of column b in bits 0-2 and the code of
+// column b + 4 in bits 4-6: lane c = 8b + 4g + p of half h takes dword h of plane word
+// 8p + b + 4g; lanes with p = 3 take nothing (their row bits stay 0).
+__device__ inline uint32_t decoder_plane_dword(uint32_t lane)
 {
-    const uint32_t x0 = (row >> (4 * half)) & 0xFu, x1 = (row >> (8 + 4 * half)) & 0xFu,
-                   x2 = (row >> (16 + 4 * half)) & 0xFu;
-    return spread4(x0) | (spread4(x1) << 1) | (spread4(x2) << 2);
+    const uint32_t c = lane & 31u, p = c & 3u;
+    return p < 3 ? 2 * (8 * p + (c >> 3) + 4 * ((c >> 2) & 1u)) + (lane >> 5) : ~0u;
+}
+
+// Escape flags of the valid columns of a decoder row: column b at bit 8b, column b + 4
+// at bit 8b + 4 (0x11111111 when all 8 exist).
+__device__ inline uint32_t valid_flags(uint32_t nvalid)
+{
+    if (nvalid >= 8) return 0x11111111u;
+    const uint32_t lo = nvalid >= 4 ? 0x01010101u : 0x01010101u & ((1u << (8 * nvalid)) - 1u);
+    const uint32_t hi = nvalid > 4 ? (0x01010101u & ((1u << (8 * (nvalid - 4))) - 1u)) << 4 : 0u;
+    return lo | hi;
+}
+
+__device__ inline uint32_t escape_flags(uint32_t row, uint32_t vflags)
+{
+    return ~(row | (row >> 1) | (row >> 2)) & vflags;
+}
+
+// A lane's 8 decoded values as the low and high bytes of their BF16 bits (values 0-3 in
+// lo0/hi0, 4-7 in lo1/hi1).  row: the lane's decoder row; z: its escape flags; r: the
+// position of its first escape in esc_lds; tlo/thi: the 8-byte decode table (byte 0 is
+// the code-0 placeholder, 0).
+struct LaneBytes {
+    uint32_t lo0, hi0, lo1, hi1;
+};
+
+__device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint32_t tlo, uint32_t thi, uint32_t r,
+                                        const uint8_t* esc_lds)
+{
+    const uint32_t z0 = z & 0x01010101u, z1 = (z >> 4) & 0x01010101u;
+    const uint32_t n0 = __builtin_popcount(z0), n1 = __builtin_popcount(z1);
+    // a code 0 selects table byte 0: the first escape of each group of 4 columns goes
+    // there, so a group with at most one escape decodes with one v_perm
+    const uint32_t x0 = esc_lds[r], x1 = esc_lds[r + n0];
+    uint32_t E0 = perm(thi, tlo | x0, row & 0x07070707u);
+    uint32_t E1 = perm(thi, tlo | x1, (row >> 4) & 0x07070707u);
+    if (n0 > 1 || n1 > 1) {   // rare: several escapes among 4 columns of the lane
+        uint32_t rr = r;
+        for (uint32_t m = z0; m; m &= m - 1) {
+            const uint32_t sh = __builtin_ctz(m);   // 8 * column
+            E0 = (E0 & ~(0xFFu << sh)) | (uint32_t(esc_lds[rr++]) << sh);
+        }
+        for (uint32_t m = z1; m; m &= m - 1) {
+            const uint32_t sh = __builtin_ctz(m);
+            E1 = (E1 & ~(0xFFu << sh)) | (uint32_t(esc_lds[rr++]) << sh);
+        }
+    }
+    // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
+    LaneBytes o;
+    o.lo0 = (A.x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
+    o.hi0 = (A.x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
+    o.lo1 = (A.y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
+    o.hi1 = (A.y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
+    return o;
 }
 
 constexpr uint32_t kAccWaves = 8;                  // one wave per tile of a block
 constexpr uint32_t kAccThreads = 64 * kAccWaves;
+constexpr uint32_t kEscPad = 16;                   // decode_lane may read esc_lds[total]
 
 // Decode-accumulate: one workgroup per block, one wave per tile.  Every peer's bytes
 // for the tile are requested up front; each wave counts its tile's escapes per peer
@@ -649,7 +775,7 @@ template <int kPeers>
 __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 {
     __shared__ uint32_t s_cnt[kPeers][kAccWaves];
-    __shared__ uint8_t s_esc[kAccWaves][kTile];
+    __shared__ uint8_t s_esc[kAccWaves][kTile + kEscPad];
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t n = a.n, P = uint32_t(a.npeers);
@@ -659,7 +785,7 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     const bool has_tile = t < T;
     const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
     const uint32_t nvalid = (!has_tile || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
-    const uint32_t c = lane & 31u, h = lane >> 5;
+    const uint32_t pdw = decoder_plane_dword(lane);
 
     // ---- requests: local values, and per peer the A bytes and one plane dword ----
     uint4 lv = make_uint4(0, 0, 0, 0);
@@ -680,6 +806,11 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
         eoff[p] = 0;
         if (uint32_t(p) < P) {
             const uint8_t* st = a.st[p];
+            // A and plane addresses follow from n alone: issue these loads first
+            if (has_tile) {
+                Ap[p] = *reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane);
+                if (pdw != ~0u) pw[p] = reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t)[pdw];
+            }
             const SegHeader hd = read_header(st, n, a.esc_bytes[p]);
             const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
             uint32_t first = 0, last = 0;
@@ -689,37 +820,23 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
             tlo[p] = hd.tlo;
             thi[p] = hd.thi;
             eoff[p] = hd.esc_offset;
-            if (has_tile && !bad) {
-                Ap[p] = *reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane);
-                if (c < 24) pw[p] = reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t)[2 * c + h];
-            }
         }
     }
 
     // ---- per peer: plane rows, escape flags, escape ranks within the tile ----
     const Transpose32 tc = transpose_consts(lane);
-    const uint32_t vmask = nvalid >= 8 ? 0xFFu : ((1u << nvalid) - 1u);
-    uint32_t rows[kPeers], zm[kPeers], rank[kPeers];
+    const uint32_t vf = valid_flags(nvalid);
+    uint32_t rows[kPeers], zf[kPeers], cnt[kPeers], rank[kPeers], total[kPeers];
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        rows[p] = 0;
-        zm[p] = 0;
-        rank[p] = 0;
-        if (uint32_t(p) < P) {
-            const uint32_t r = transpose32(pw[p], tc);
-            rows[p] = r;
-            zm[p] = ~(r | (r >> 8) | (r >> 16)) & vmask;
-            const uint32_t cnt = __builtin_popcount(zm[p]);
-            uint32_t pre = 0, total = 0;
+        rows[p] = uint32_t(p) < P ? transpose32(pw[p], tc) : 0u;
+        zf[p] = uint32_t(p) < P ? escape_flags(rows[p], vf) : 0u;
+        cnt[p] = __builtin_popcount(zf[p]);
+    }
+    wave_ranks<kPeers>(cnt, rank, total, P);
+    if (lane == 0) {
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint64_t bk = ballot((cnt >> k) & 1u);
-                pre += mbcnt(bk, 0u) << k;
-                total += uint32_t(__builtin_popcountll(bk)) << k;
-            }
-            rank[p] = pre;
-            if (lane == 0) s_cnt[p][wave] = total;
-        }
+        for (int p = 0; p < kPeers; p++) s_cnt[p][wave] = total[p];
     }
     __syncthreads();
 
@@ -729,16 +846,16 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     for (int p = 0; p < kPeers; p++) {
         before[p] = mine[p] = ev[p] = 0;
         if (uint32_t(p) < P) {
-            uint32_t bsum = 0, total = 0;
+            uint32_t bsum = 0, tot = 0;
 #pragma unroll
             for (uint32_t w = 0; w < kAccWaves; w++) {
                 const uint32_t v = s_cnt[p][w];
                 if (w < wave) bsum += v;
-                total += v;
+                tot += v;
             }
             before[p] = bsum;
-            mine[p] = s_cnt[p][wave];
-            bad = bad || total != blk[p];   // the offset table must agree with the planes
+            mine[p] = total[p];
+            bad = bad || tot != blk[p];   // the offset table must agree with the planes
             if (!bad && lane < mine[p]) ev[p] = a.esc[p][eoff[p] + off0[p] + bsum + lane];
         }
     }
@@ -760,30 +877,13 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
                 const uint8_t* esc = a.esc[p] + eoff[p] + off0[p] + before[p];
                 for (uint32_t k = 64 + lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            uint32_t E0 = perm(thi[p], tlo[p], codes_of_row(rows[p], 0));
-            uint32_t E1 = perm(thi[p], tlo[p], codes_of_row(rows[p], 1));
-            uint32_t z = zm[p], r = rank[p];
-            while (z) {   // this lane's escapes, in column order
-                const uint32_t j = __builtin_ctz(z);
-                const uint32_t x = esc_lds[r++];
-                const uint32_t sh = 8 * (j & 3);
-                if (j < 4) E0 = (E0 & ~(0xFFu << sh)) | (x << sh);
-                else E1 = (E1 & ~(0xFFu << sh)) | (x << sh);
-                z &= z - 1;
-            }
-            // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
-            const uint32_t lo0 = (Ap[p].x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
-            const uint32_t hi0 = (Ap[p].x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
-            const uint32_t lo1 = (Ap[p].y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
-            const uint32_t hi1 = (Ap[p].y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
+            wave_lds_sync();
+            const LaneBytes o = decode_lane(rows[p], zf[p], Ap[p], tlo[p], thi[p], rank[p], esc_lds);
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
                 const uint32_t sel = 0x0C0Cu | ((j & 3u) << 16) | ((4u + (j & 3u)) << 24);
-                const uint32_t f = j < 4 ? perm(hi0, lo0, sel) : perm(hi1, lo1, sel);
+                const uint32_t f = j < 4 ? perm(o.hi0, o.lo0, sel) : perm(o.hi1, o.lo1, sel);
                 acc[j] = acc[j] + __uint_as_float(f);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -809,15 +909,15 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 // Decompress: one workgroup per unit of 4 blocks, one half block (4 tiles) per wave,
 // as in the encoder.  Each wave requests the A bytes and one plane dword per lane of
 // its 4 tiles at once, turns the planes back into per-lane rows with the half-wave bit
-// transpose (its own inverse), counts its escapes, learns through one barrier how
-// many escapes the first half of its block holds, then fetches its half block's
-// escapes and writes its 2048 values.
+// transpose (its own inverse), ranks its escapes, learns through one barrier how many
+// escapes the first half of its block holds, then fetches its half block's escapes and
+// writes its 2048 values.
 constexpr uint32_t kDecHalfTiles = 4;
 
 __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
 {
     __shared__ uint32_t s_cnt[kEncWaves];
-    __shared__ uint8_t s_esc[kEncWaves][kHalf];
+    __shared__ uint8_t s_esc[kEncWaves][kHalf + kEscPad];
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t unit = blockIdx.x;
@@ -828,7 +928,8 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
     const uint32_t hb = (unit - sg.unit0) * kEncWaves + wave;   // half block within the segment
     const uint32_t b = hb >> 1, half = hb & 1;
     const bool active = b < K;
-    const uint32_t c = lane & 31u, h = lane >> 5;
+    const bool full = uint64_t(hb + 1) * kHalf <= n;          // all 2048 values exist
+    const uint32_t pdw = decoder_plane_dword(lane);
     const uint8_t* st = sg.src;
 
     bool bad = false;
@@ -842,44 +943,37 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
         pw[k] = 0;
     }
     if (active) {
+        // A and plane addresses follow from n alone, so these loads are issued before
+        // (and independently of) the header checks; escapes are read only once the
+        // header and offset table have been validated
+#pragma unroll
+        for (int k = 0; k < int(kDecHalfTiles); k++) {
+            const uint32_t t = hb * kDecHalfTiles + k;
+            if (t < T) {
+                Ap[k] = *reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane);
+                if (pdw != ~0u) pw[k] = reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t)[pdw];
+            }
+        }
         hd = read_header(st, n, a.esc_bytes);
         const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
         bad = !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
-        if (!bad) {
-#pragma unroll
-            for (int k = 0; k < int(kDecHalfTiles); k++) {
-                const uint32_t t = hb * kDecHalfTiles + k;
-                if (t < T) {
-                    Ap[k] = *reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane);
-                    if (c < 24) pw[k] = reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t)[2 * c + h];
-                }
-            }
-        }
     }
-    // rows, escape flags, per-tile escape totals and this lane's rank within its tile
+    // rows, escape flags and the ranks of this lane's escapes within the half block
     const Transpose32 tc = transpose_consts(lane);
-    uint32_t rows[kDecHalfTiles], zm[kDecHalfTiles], rank[kDecHalfTiles], tstart[kDecHalfTiles];
-    uint32_t half_total = 0;
+    uint32_t rows[kDecHalfTiles], zf[kDecHalfTiles], cnt[kDecHalfTiles], start[kDecHalfTiles];
 #pragma unroll
     for (int k = 0; k < int(kDecHalfTiles); k++) {
-        const uint32_t t = hb * kDecHalfTiles + k;
-        const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
-        const uint32_t nvalid = (!active || t >= T || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
-        const uint32_t vmask = nvalid >= 8 ? 0xFFu : ((1u << nvalid) - 1u);
-        rows[k] = transpose32(pw[k], tc);
-        zm[k] = ~(rows[k] | (rows[k] >> 8) | (rows[k] >> 16)) & vmask;
-        const uint32_t cnt = __builtin_popcount(zm[k]);
-        uint32_t pre = 0, total = 0;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const uint64_t bq = ballot((cnt >> q) & 1u);
-            pre += mbcnt(bq, 0u) << q;
-            total += uint32_t(__builtin_popcountll(bq)) << q;
+        uint32_t vf = 0x11111111u;
+        if (!full) {
+            const uint32_t t = hb * kDecHalfTiles + k;
+            const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
+            vf = valid_flags((!active || t >= T || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0)));
         }
-        rank[k] = pre;
-        tstart[k] = half_total;
-        half_total += total;
+        rows[k] = transpose32(pw[k], tc);
+        zf[k] = escape_flags(rows[k], vf);
+        cnt[k] = __builtin_popcount(zf[k]);
     }
+    const uint32_t half_total = half_ranks(cnt, start);
     if (lane == 0) s_cnt[wave] = half_total;
     __syncthreads();
     if (!active) return;
@@ -894,36 +988,19 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
     const uint8_t* esc = a.esc + hd.esc_offset + first + half_start;
     uint8_t* esc_lds = s_esc[wave];
     for (uint32_t k = lane; k < half_total; k += 64) esc_lds[k] = esc[k];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();
 #pragma unroll
     for (int k = 0; k < int(kDecHalfTiles); k++) {
         const uint32_t t = hb * kDecHalfTiles + k;
         const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
         const uint32_t nvalid = (t >= T || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
         if (nvalid == 0) continue;
-        uint32_t E0 = perm(hd.thi, hd.tlo, codes_of_row(rows[k], 0));
-        uint32_t E1 = perm(hd.thi, hd.tlo, codes_of_row(rows[k], 1));
-        uint32_t z = zm[k], r = tstart[k] + rank[k];
-        while (z) {   // this lane's escapes, in column order
-            const uint32_t j = __builtin_ctz(z);
-            const uint32_t x = esc_lds[r++];
-            const uint32_t sh = 8 * (j & 3);
-            if (j < 4) E0 = (E0 & ~(0xFFu << sh)) | (x << sh);
-            else E1 = (E1 & ~(0xFFu << sh)) | (x << sh);
-            z &= z - 1;
-        }
-        // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
-        const uint32_t lo0 = (Ap[k].x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
-        const uint32_t hi0 = (Ap[k].x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
-        const uint32_t lo1 = (Ap[k].y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
-        const uint32_t hi1 = (Ap[k].y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
+        const LaneBytes y = decode_lane(rows[k], zf[k], Ap[k], hd.tlo, hd.thi, start[k], esc_lds);
         uint4 o;
-        o.x = perm(hi0, lo0, 0x05010400u);
-        o.y = perm(hi0, lo0, 0x07030602u);
-        o.z = perm(hi1, lo1, 0x05010400u);
-        o.w = perm(hi1, lo1, 0x07030602u);
+        o.x = perm(y.hi0, y.lo0, 0x05010400u);
+        o.y = perm(y.hi0, y.lo0, 0x07030602u);
+        o.z = perm(y.hi1, y.lo1, 0x05010400u);
+        o.w = perm(y.hi1, y.lo1, 0x07030602u);
         if (nvalid == 8) {
             *reinterpret_cast<uint4*>(sg.dst + i0) = o;
         } else {
