@@ -11,10 +11,14 @@ its input in the 256 MB Infinity Cache (steady state of a pipelined round trip).
 Printed (one JSON line on stdout):
   value      BF16 bytes handled per second by the step: (2n compressed + 2n decompressed)
              / step wall time, in GB/s (the harmonic mean of the two codec directions);
-  roofline   for the step's dominant operation (decompress, one kernel, when it takes
-             longer than compress): algorithmic HBM bytes per launch (2n BF16 bytes +
-             static part + escapes) / average launch time from HIP events on the launch
-             stream, against the 8 TB/s HBM peak; roofline_other_op for the other one;
+  roofline   for the step's dominant operation (compress: encode_kernel + place_direct_kernel,
+             or decompress: decompress_kernel, whichever takes longer): algorithmic HBM
+             bytes per launch (2n BF16 bytes + static part + escapes) / average launch
+             time, from HIP events on the launch stream around back-to-back launches over
+             the rotating sets, against the 8 TB/s HBM peak; traffic: the HBM bytes per
+             launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
+             (profiles/pmc_traffic_bucket_64m.txt; null when that was taken on other
+             kernel sources); roofline_other_op for the other operation;
   cpu_baseline  the plain C oracle, single-threaded, on the same bucket;
   per_config the other workloads (1 Mi chunk, activations with escapes and specials,
              MoE dispatch buckets, reduce-scatter share with decode-accumulate and the
@@ -146,16 +150,31 @@ def run_codec(torch, bc, iters, warmup, per_step_plans=False):
     t0 = time.perf_counter()
     for i in range(warmup, warmup + iters):
         if per_step_plans:
-            plans = bc.plans()                  # a1: sigma -> tables on the host
+            plans = bc.plans()                  # sigma -> tables, on the host
         e = tc.start()
-        bc.compress(i % R, plans)               # a2-a5, a8
+        bc.compress(i % R, plans)
         tc.stop(e)
         e = td.start()
-        bc.decompress((i - LAG) % R)            # a6
+        bc.decompress((i - LAG) % R)
         td.stop(e)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / iters * 1e3
     return tc.ms(), td.ms(), wall
+
+
+def batched_ms(torch, fn, sets, rounds):
+    """Average time of one launch of fn(k) over rounds x sets back-to-back launches on
+    the rotating sets, from two HIP events on the launch stream around the whole batch
+    (the events' own latency is then not counted per launch)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        for k in range(sets):
+            fn(k)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (rounds * sets)
 
 
 def codec_report(bc, c_ms, d_ms):
@@ -295,6 +314,112 @@ def cpu_baseline(W, O, wl, reps):
             "host_cpus": os.cpu_count()}
 
 
+# ------------------------------------------------------------------------------------
+# rocprofv3 summaries kept under profiles/ (text), and the measured HBM traffic
+# ------------------------------------------------------------------------------------
+KERNEL_SRC = os.path.join(ROOT, "lossless_bf16_exponent_codec_amd", "csrc", "zipccl_kernels.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "pmc_traffic_bucket_64m.txt")
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/stats -o bench -- "
+             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra")
+PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{counter} -o run -- "
+           "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-extra")
+OUR_KERNELS = ("encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel", "decompress_kernel",
+               "accumulate_kernel")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+GIB = 1 << 30
+
+
+def kernel_source_sha256():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def short_kernel_name(name):
+    for k in OUR_KERNELS:
+        if k in name:
+            return k
+    return COPY_KERNEL if COPY_KERNEL in name else None
+
+
+def summarize_stats(csv_path, out_path):
+    """profiles/ text from rocprofv3 --stats (kernel_stats.csv) of TRACE_CMD."""
+    import csv
+    rows = [r for r in csv.DictReader(open(csv_path)) if short_kernel_name(r["Name"]) in OUR_KERNELS]
+    lines = ["# Kernel durations, bucket_64m (16 x 4 Mi BF16 values, one table per layer)", "",
+             "Command (from the repository root on the GPU host; rocprofv3's own averages):", "",
+             "    " + TRACE_CMD, "",
+             f"Kernel source sha256: `{kernel_source_sha256()}`", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "Calls include the warmup and verification round trips; all launches are of the",
+              "bucket workload (compress: encode_kernel + place_direct_kernel, decompress: decompress_kernel)."]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
+def summarize_pmc(fetch_csv, write_csv, out_path, n_units=4096):
+    """profiles/ text from two rocprofv3 --pmc runs of PMC_CMD (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads for the
+    bench's 1 GiB device-to-device copy (the copy reads and writes 1 GiB).  Bucket
+    launches are told apart from others by grid size."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = short_kernel_name(r["Kernel_Name"])
+            if k is None:
+                continue
+            grid = int(r["Grid_Size"])
+            acc.setdefault((k, grid), []).append(float(r["Counter_Value"]))
+        return {key: sum(v) / len(v) for key, v in acc.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_f = max(v for (k, g), v in f.items() if k == COPY_KERNEL)
+    copy_w = max(v for (k, g), v in w.items() if k == COPY_KERNEL)
+    sf, sw = (GIB / 1024) / copy_f, (GIB / 1024) / copy_w      # true KiB per counted KiB
+    enc = ("encode_kernel", n_units * 512)
+    plc = ("place_direct_kernel", ((n_units + 7) // 8) * 512)
+    dec = ("decompress_kernel", n_units * 512)
+    kib = {k: (f[k] * sf, w[k] * sw) for k in (enc, plc, dec)}
+    comp = sum(kib[enc]) + sum(kib[plc])
+    decomp = sum(kib[dec])
+    lines = ["# Measured HBM traffic, bucket_64m (16 x 4 Mi BF16 values)", "",
+             "Commands (from the repository root on the GPU host), one run per counter:", "",
+             "    " + PMC_CMD.format(counter="FETCH_SIZE"), "    " + PMC_CMD.format(counter="WRITE_SIZE"), "",
+             f"Scale factors from the 1 GiB copy in the same runs: FETCH_SIZE x{sf:.4f}, WRITE_SIZE x{sw:.4f}",
+             f"(the copy counted {copy_f:.0f} KiB fetched and {copy_w:.0f} KiB written per dispatch).", "",
+             "| kernel | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
+             "|---|---|---|---|---|---|"]
+    for k in (enc, plc, dec):
+        lines.append(f"| {k[0]} | {k[1]} | {f[k]:.1f} | {w[k]:.1f} | {kib[k][0] * 1024 / 1e6:.2f} | "
+                     f"{kib[k][1] * 1024 / 1e6:.2f} |")
+    lines += ["", "Machine-readable (bench.py reports these as roofline.traffic while the kernel",
+              "source hash matches; bytes per launch):", "", "```",
+              f"source_sha256={kernel_source_sha256()}",
+              f"compress_traffic_bytes={int(comp * 1024)}",
+              f"decompress_traffic_bytes={int(decomp * 1024)}", "```"]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
+def measured_traffic():
+    """Bytes per launch from the committed PMC summary, or {} if it is missing or was
+    taken on another version of the kernels."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return {}
+    kv = dict(line.split("=", 1) for line in text.splitlines() if "=" in line and " " not in line.strip())
+    if kv.get("source_sha256") != kernel_source_sha256():
+        return {}
+    return {"compress": int(kv["compress_traffic_bytes"]), "decompress": int(kv["decompress_traffic_bytes"])}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,7 +429,17 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of a rocprofv3 --stats run and exit")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and this build has no "
               f"multi-GPU path; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -330,14 +465,19 @@ def main(argv=None) -> int:
     value = 4 * n / (ms_per_step * 1e-3) / 1e9
     n_esc = bc.n_esc_total()
     moved = compress_bytes(n, bc.static_bytes, n_esc)
-    c_avg = sum(c_ms) / len(c_ms)
-    d_avg = sum(d_ms) / len(d_ms)
+    # per-launch averages for the roofline: back-to-back launches over the rotating sets
+    plans = bc.plans()
+    rounds = max(2, args.steps // len(bc.sets))
+    c_avg = batched_ms(torch, lambda k: bc.compress(k, plans), len(bc.sets), rounds)
+    d_avg = batched_ms(torch, bc.decompress, len(bc.sets), rounds)
 
-    def roof(name, avg_ms, launches):
+    traffic = measured_traffic()
+
+    def roof(name, op, avg_ms, launches):
         ach = moved / (avg_ms * 1e-3) / 1e9
         return {"bound": "hbm", "kernel": name, "launches": launches, "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                "bytes_per_launch": moved, "avg_launch_us": round(avg_ms * 1e3, 2), "traffic": None}
+                "bytes_per_launch": moved, "avg_launch_us": round(avg_ms * 1e3, 2), "traffic": traffic.get(op)}
 
     # the step's dominant kernel: decompress is one launch; compress is two (encode_kernel,
     # place_direct_kernel; three with scan_kernel above 2^28 values), timed together by
@@ -345,8 +485,8 @@ def main(argv=None) -> int:
     units = sum((m + 16383) // 16384 for m in bc.sizes)
     c_launches = (["encode_kernel", "place_direct_kernel"] if units <= 16384
                   else ["encode_kernel", "scan_kernel", "place_kernel"])
-    roof_d = roof("decompress_kernel", d_avg, ["decompress_kernel"])
-    roof_c = roof("compress", c_avg, c_launches)
+    roof_d = roof("decompress_kernel", "decompress", d_avg, ["decompress_kernel"])
+    roof_c = roof("compress", "compress", c_avg, c_launches)
     primary, secondary = (roof_d, roof_c) if d_avg >= c_avg else (roof_c, roof_d)
     out = {
         "metric": METRIC,

@@ -103,7 +103,7 @@ uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc);
 
 /* Device workspace bytes needed by zipccl_compress for up to nseg segments holding
  * at most total_n values (about one byte per value: a 4-byte escape count and a
- * 4096-byte escape staging slot per 4096-value block).  The workspace carries nothing
+ * 2048-byte escape staging slot per 2048-value half block, eight per 16384 values).  The workspace carries nothing
  * from one call to the next and needs no initialisation; it must be 256-byte aligned.
  * Calls that run concurrently need separate workspaces. */
 uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);

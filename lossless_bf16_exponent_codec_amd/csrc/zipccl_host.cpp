@@ -97,7 +97,7 @@ uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc) { return static_byte
 uint64_t zipccl_workspace_size(uint64_t total_n, int nseg)
 {
     if (nseg < 1) nseg = 1;
-    return ws_bytes(total_n / kBlock + uint64_t(nseg));   // bounds the sum of ceil(n_s / 4096)
+    return ws_bytes(total_n / kUnit + uint64_t(nseg));   // bounds the sum of ceil(n_s / 16384)
 }
 
 zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
@@ -131,15 +131,15 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
     }
     if (total >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
     if (st_off > static_cap) return ZIPCCL_ERR_SIZE;
-    if (ws_bytes(blocks) > workspace_bytes) return ZIPCCL_ERR_SIZE;
+    if (ws_bytes(units) > workspace_bytes) return ZIPCCL_ERR_SIZE;
     if (esc_cap > 0 && !esc_out) return ZIPCCL_ERR_INVALID;
     a.esc = static_cast<uint8_t*>(esc_out);
     a.esc_cap = esc_out ? esc_cap : 0;
     uint8_t* w = static_cast<uint8_t*>(workspace);
     a.counts = reinterpret_cast<uint32_t*>(w);
-    a.pos = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(blocks));
-    a.unit_counts = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(blocks) + ws_pos_bytes(blocks));
-    a.stage = w + ws_counts_bytes(blocks) + ws_pos_bytes(blocks) + ws_units_bytes(blocks);
+    a.pos = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(units));
+    a.unit_counts = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(units) + ws_pos_bytes(units));
+    a.stage = w + ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units);
     a.n_esc_out = n_esc_out;
     a.status = status;
     a.nseg = nseg;

@@ -20,17 +20,18 @@ constexpr uint32_t kHalf = kBlock / 2;
 constexpr uint32_t kEncWaves = 8;
 constexpr uint32_t kEncThreads = 64 * kEncWaves;
 
-// Compress workspace: a u32 escape count per half block of the launch, the
-// launch-wide position of every half block's first escape (one more entry for the
-// total; used only when the positions come from the scan kernel), a u32 escape count
-// per workgroup unit, then a staging slot of kHalf bytes per half block that holds its
-// escape exponents until their positions are known.
-__host__ __device__ inline uint64_t ws_counts_bytes(uint64_t blocks) { return (8 * blocks + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_pos_bytes(uint64_t blocks) { return (4 * (2 * blocks + 1) + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_units_bytes(uint64_t blocks) { return (4 * (blocks + 1) + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_bytes(uint64_t blocks)
+// Compress workspace, by half-block slot: slot 8u + w belongs to wave w of workgroup
+// unit u (slots past a segment's end hold 0 escapes).  A u32 escape count per slot,
+// the launch-wide position of each slot's first escape (one more entry for the total;
+// used only when the positions come from the scan kernel), a u32 escape count per
+// unit, then kHalf staging bytes per slot that hold its escape exponents until their
+// positions are known.
+__host__ __device__ inline uint64_t ws_counts_bytes(uint64_t units) { return (32 * units + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_pos_bytes(uint64_t units) { return (4 * (8 * units + 1) + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_units_bytes(uint64_t units) { return (4 * (units + 1) + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_bytes(uint64_t units)
 {
-    return ws_counts_bytes(blocks) + ws_pos_bytes(blocks) + ws_units_bytes(blocks) + uint64_t(kBlock) * blocks;
+    return ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units) + uint64_t(kHalf) * 8 * units;
 }
 
 // Up to this many workgroup units (2^28 values) the place kernel sums the unit counts
@@ -52,10 +53,10 @@ struct CArgs {
     CSeg seg[kMaxSegs];
     uint8_t* esc;
     uint64_t esc_cap;
-    uint32_t* counts;      // workspace: escapes per half block
-    uint32_t* pos;         // workspace: launch-wide position of each half block's first escape
+    uint32_t* counts;      // workspace: escapes per half-block slot
+    uint32_t* pos;         // workspace: launch-wide position of each slot's first escape
     uint32_t* unit_counts; // workspace: escapes per workgroup unit
-    uint8_t* stage;        // workspace: kHalf bytes per half block
+    uint8_t* stage;        // workspace: kHalf bytes per slot
     uint64_t* n_esc_out;   // nseg + 1 entries or null
     uint32_t* status;      // or null
     int32_t nseg;

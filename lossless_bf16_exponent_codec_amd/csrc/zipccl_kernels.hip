@@ -52,9 +52,13 @@ __device__ inline void store_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal
 
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
 
+// ORs bits into the status word; skips the atomic when they are set already (on bad
+// input every workgroup may report, and atomics on one address are serialised).
 __device__ inline void or_status(uint32_t* s, uint32_t bits)
 {
-    if (s) __hip_atomic_fetch_or(s, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!s) return;
+    if ((__hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & bits) == bits) return;
+    __hip_atomic_fetch_or(s, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Segment holding launch-wide index u: the last s with seg[s].*first <= u (segments
@@ -255,7 +259,7 @@ __device__ inline void stage_tile_escapes(const TileEsc& te, uint32_t r, uint8_t
 
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
 // planes, the escape count and the staged escape exponents; zero padding after the
-// segment's last half block.  gh: the half block's launch-wide index.
+// segment's last half block.  gh: the half block's workspace slot.
 __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
                                        uint32_t lane, const uint8_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
@@ -352,7 +356,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     const Transpose32 tc = transpose_consts(lane);
     __syncthreads();
     uint32_t run = 0;
-    if (active) run = encode_half(a, sg, hb, 2 * sg.block0 + hb, v, lane, s_lut, tc, s_esc[wave]);
+    const uint32_t slot = unit * kEncWaves + wave;
+    if (active) run = encode_half(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
+    else if (lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
     if (a.direct) {   // the unit's escape count, for the place kernel's prefix sums
         if (lane == 0) s_hcnt[wave] = run;
         __syncthreads();
@@ -399,16 +405,15 @@ __device__ inline void write_empty_header(const CSeg& sg, uint32_t lane, uint32_
     write_header(sg, lane, 0u, esc_offset);
 }
 
-// Scan: one workgroup turns the per-half-block escape counts into launch-wide
-// positions: pos[h] = escapes of all half blocks before h, pos[2 * total_blocks] = all
-// escapes.  Rounds of 16 consecutive counts per thread keep loads and stores 16 bytes
+// Scan: one workgroup turns the per-slot escape counts into launch-wide positions:
+// pos[h] = escapes of all slots before h, pos[8 * total_units] = all escapes.  Rounds of 16 consecutive counts per thread keep loads and stores 16 bytes
 // wide.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
 {
     __shared__ uint32_t s_wtot[kScanThreads / 64];
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t Kt = 2 * a.total_blocks;   // half blocks
+    const uint32_t Kt = kEncWaves * a.total_units;   // half-block slots
     uint32_t carry = 0;
     for (uint32_t r0 = 0; r0 < Kt; r0 += kScanRound) {
         const uint32_t lo = r0 + tid * kScanPer;
@@ -487,13 +492,14 @@ __device__ inline bool place_half(const CArgs& a, uint2 head, uint32_t hl, uint3
     return over;
 }
 
-// Places block gb (launch-wide) of segment s: its offset-table entry, the staged escape
-// bytes of its two half blocks (positions p0, p1, p2 = start of half 0, half 1, end;
+// Places block gb (launch-wide) of segment s, whose halves are in workspace slots slot
+// and slot + 1: its offset-table entry, the staged escape bytes of the two halves
+// (positions p0, p1, p2 = start of half 0, half 1, end;
 // base = the segment's first escape), the segment header from the segment's last
 // block, and the headers of empty segments next to it.  The first 256 staged bytes of
 // each half are requested before the positions are needed.
-__device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint2 head, uint32_t p0, uint32_t p1,
-                                   uint32_t p2, uint32_t base, uint32_t lane)
+__device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint32_t slot, uint2 head, uint32_t p0,
+                                   uint32_t p1, uint32_t p2, uint32_t base, uint32_t lane)
 {
     const CSeg& sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
@@ -503,7 +509,7 @@ __device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint2 hea
     bool over = place_half(a, head, hl, hp, hc);
     for (uint32_t hh = 0; hh < 2; hh++) {   // rare: more than 256 escapes in a half block
         const uint32_t c = hh ? p2 - p1 : p1 - p0, q = hh ? p1 : p0;
-        const uint8_t* st = a.stage + uint64_t(2 * gb + hh) * kHalf;
+        const uint8_t* st = a.stage + uint64_t(slot + hh) * kHalf;
         for (uint32_t k = 256 + lane; k < c; k += 64) {
             const uint64_t at = uint64_t(q) + k;
             if (at < a.esc_cap) a.esc[at] = st[k];
@@ -532,11 +538,19 @@ __device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint2 hea
     }
 }
 
-// Staged bytes 8*hl .. 8*hl+7 of this lane's half of block gb (lanes 0-31: half 0).
-__device__ inline uint2 stage_head(const CArgs& a, uint32_t gb, uint32_t lane)
+// Staged bytes 8*hl .. 8*hl+7 of slot + (lane >> 5), hl = lane & 31 (lanes 0-31: the
+// block's first half).
+__device__ inline uint2 stage_head(const CArgs& a, uint32_t slot, uint32_t lane)
 {
-    const uint8_t* stage = a.stage + uint64_t(2 * gb + (lane >> 5)) * kHalf;
+    const uint8_t* stage = a.stage + uint64_t(slot + (lane >> 5)) * kHalf;
     return reinterpret_cast<const uint2*>(stage)[lane & 31u];
+}
+
+// Workspace slot of the first half of block gb (launch-wide) of segment s.
+__device__ inline uint32_t block_slot(const CSeg& sg, uint32_t gb)
+{
+    const uint32_t lb = gb - sg.block0;
+    return (sg.unit0 + lb / kWaves) * kEncWaves + (lb % kWaves) * 2;
 }
 
 // Place, after the scan kernel: one wave per block, positions from pos[].
@@ -547,18 +561,21 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
     const uint32_t gb = blockIdx.x * kWaves + wave;
     if (gb >= a.total_blocks) return;
     const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
-    const uint2 head = stage_head(a, gb, lane);
-    const uint32_t p0 = a.pos[2 * gb], p1 = a.pos[2 * gb + 1], p2 = a.pos[2 * gb + 2];
-    place_block(a, s, gb, head, p0, p1, p2, a.pos[2 * a.seg[s].block0], lane);
+    const uint32_t slot = block_slot(a.seg[s], gb);
+    const uint2 head = stage_head(a, slot, lane);
+    const uint32_t p0 = a.pos[slot], p1 = a.pos[slot + 1], p2 = a.pos[slot + 2];
+    place_block(a, s, gb, slot, head, p0, p1, p2, a.pos[a.seg[s].unit0 * kEncWaves], lane);
 }
 
 // Place without the scan kernel: one workgroup per 8 encode units, one unit (4 blocks)
 // per wave.  The workgroup sums the escape counts of all units before its first one
 // (and before the first unit of that unit's segment) from unit_counts[], a few
 // kilobytes read from L2; each wave then derives its blocks' positions from its unit's
-// 8 half-block counts.  The staged heads of all 4 blocks are requested first.
+// 8 half-block counts.  Every load that needs no segment information (workspace slots
+// are indexed by unit) is issued before the segment lookups in the kernel arguments.
 constexpr uint32_t kPlaceUnits = 8;
 constexpr uint32_t kPlaceThreads = 64 * kPlaceUnits;
+constexpr uint32_t kPrefixLoads = kDirectPrefixMaxUnits / (4 * kPlaceThreads);   // uint4 loads per thread
 
 __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a)
 {
@@ -569,33 +586,35 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
     const uint32_t u_first = blockIdx.x * kPlaceUnits;
     const uint32_t unit = u_first + wave;
     const bool active = unit < a.total_units;
+    const uint32_t slot0 = unit * kEncWaves;
+    uint2 head[kWaves];        // staged heads of the unit's 4 blocks
+    uint32_t hc[2 * kWaves];   // the unit's half-block escape counts
+#pragma unroll
+    for (uint32_t k = 0; k < kWaves; k++) head[k] = active ? stage_head(a, slot0 + 2 * k, lane) : make_uint2(0, 0);
+#pragma unroll
+    for (uint32_t k = 0; k < 2 * kWaves; k++) hc[k] = active ? a.counts[slot0 + k] : 0u;
+    if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
+    uint4 q[kPrefixLoads];     // unit_counts[0 .. u_first), 4 per load (u_first is a multiple of 8)
+#pragma unroll
+    for (uint32_t r = 0; r < kPrefixLoads; r++) {
+        const uint32_t i = 4 * (tid + r * kPlaceThreads);
+        q[r] = i < u_first ? *reinterpret_cast<const uint4*>(a.unit_counts + i) : make_uint4(0, 0, 0, 0);
+    }
+
+    // segment lookups meanwhile
     const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
     const CSeg& sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
     const uint32_t b0 = (unit - sg.unit0) * kWaves;   // first block of the unit within the segment
-    uint2 head[kWaves];
-#pragma unroll
-    for (uint32_t k = 0; k < kWaves; k++)
-        head[k] = (active && b0 + k < K) ? stage_head(a, sg.block0 + b0 + k, lane) : make_uint2(0, 0);
-    if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
-    uint32_t hc[2 * kWaves];   // the unit's half-block escape counts
-#pragma unroll
-    for (uint32_t k = 0; k < 2 * kWaves; k++)
-        hc[k] = (active && b0 + k / 2 < K) ? a.counts[2 * (sg.block0 + b0) + k] : 0u;
-
-    // escapes before the group's first unit and before the first unit of its segment
     const int s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
     const uint32_t u0 = a.seg[s_first].unit0;
+
+    // escapes before the group's first unit and before the first unit of its segment
     uint32_t acc = 0, accs = 0;
-    for (uint32_t i = 4 * tid; i < u_first; i += 4 * kPlaceThreads) {
-        uint32_t v[4];
-        if (i + 4 <= u_first) {
-            const uint4 q = *reinterpret_cast<const uint4*>(a.unit_counts + i);
-            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-        } else {
 #pragma unroll
-            for (uint32_t k = 0; k < 4; k++) v[k] = i + k < u_first ? a.unit_counts[i + k] : 0u;
-        }
+    for (uint32_t r = 0; r < kPrefixLoads; r++) {
+        const uint32_t i = 4 * (tid + r * kPlaceThreads);
+        const uint32_t v[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
 #pragma unroll
         for (uint32_t k = 0; k < 4; k++) {
             acc += v[k];
@@ -635,7 +654,7 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
     for (uint32_t k = 0; k < kWaves; k++) {
         if (b0 + k >= K) break;
         const uint32_t p0 = p, p1 = p0 + hc[2 * k], p2 = p1 + hc[2 * k + 1];
-        place_block(a, s, sg.block0 + b0 + k, head[k], p0, p1, p2, base, lane);
+        place_block(a, s, sg.block0 + b0 + k, slot0 + 2 * k, head[k], p0, p1, p2, base, lane);
         p = p2;
     }
 }
