@@ -475,38 +475,39 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
     }
 }
 
-// Copies the first 256 staged escapes of one half block to esc[p ...]; `head` holds
-// staged bytes 8*hl .. 8*hl+7 (hl = lane within the half of the wave that loaded them).
-__device__ inline bool place_half(const CArgs& a, uint2 head, uint32_t hl, uint32_t p, uint32_t cnt)
+// Copies the first min(cnt, 256) staged escapes of one half block from LDS (src) to
+// esc[p ...]: lane l writes bytes l, l + 64, ..., so each store instruction covers 64
+// consecutive bytes.  Returns true if a byte fell at or past esc_cap.
+__device__ inline bool place_half(const CArgs& a, const uint8_t* src, uint32_t p, uint32_t cnt, uint32_t lane)
 {
+    const uint32_t m = min(cnt, 256u);
+    uint8_t* dst = a.esc + p;
+    if (uint64_t(p) + m <= a.esc_cap) {   // the common case: no per-byte check
+        for (uint32_t k = lane; k < m; k += 64) dst[k] = src[k];
+        return false;
+    }
     bool over = false;
-#pragma unroll
-    for (uint32_t q = 0; q < 8; q++) {
-        const uint32_t k = 8 * hl + q;
-        if (k < cnt) {
-            const uint64_t at = uint64_t(p) + k;
-            if (at < a.esc_cap) a.esc[at] = uint8_t((q < 4 ? head.x : head.y) >> (8 * (q & 3)));
-            else over = true;
-        }
+    for (uint32_t k = lane; k < m; k += 64) {
+        if (uint64_t(p) + k < a.esc_cap) dst[k] = src[k];
+        else over = true;
     }
     return over;
 }
 
-// Places block gb (launch-wide) of segment s, whose halves are in workspace slots slot
-// and slot + 1: its offset-table entry, the staged escape bytes of the two halves
-// (positions p0, p1, p2 = start of half 0, half 1, end;
-// base = the segment's first escape), the segment header from the segment's last
-// block, and the headers of empty segments next to it.  The first 256 staged bytes of
-// each half are requested before the positions are needed.
-__device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint32_t slot, uint2 head, uint32_t p0,
-                                   uint32_t p1, uint32_t p2, uint32_t base, uint32_t lane)
+// Places block gb (launch-wide) of segment sg (index s), whose halves are in workspace
+// slots slot and slot + 1: its offset-table entry, the staged escape bytes of the two
+// halves (positions p0, p1, p2 = start of half 0, half 1, end; base = the segment's
+// first escape), the segment header from the segment's last block, and the headers of
+// empty segments next to it.  heads: the first 256 staged bytes of each half in LDS
+// (half 1 at heads + 256), requested before the positions were known.
+__device__ inline void place_block(const CArgs& a, const CSeg& sg, int s, uint32_t gb, uint32_t slot,
+                                   const uint8_t* heads, uint32_t p0, uint32_t p1, uint32_t p2, uint32_t base,
+                                   uint32_t lane)
 {
-    const CSeg& sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
-    const uint32_t hl = lane & 31u, hsel = lane >> 5;
     if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
-    const uint32_t hp = hsel ? p1 : p0, hc = hsel ? p2 - p1 : p1 - p0;
-    bool over = place_half(a, head, hl, hp, hc);
+    bool over = place_half(a, heads, p0, p1 - p0, lane);
+    over = place_half(a, heads + 256, p1, p2 - p1, lane) || over;
     for (uint32_t hh = 0; hh < 2; hh++) {   // rare: more than 256 escapes in a half block
         const uint32_t c = hh ? p2 - p1 : p1 - p0, q = hh ? p1 : p0;
         const uint8_t* st = a.stage + uint64_t(slot + hh) * kHalf;
@@ -516,7 +517,7 @@ __device__ inline void place_block(const CArgs& a, int s, uint32_t gb, uint32_t 
             else over = true;
         }
     }
-    if (over) or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
+    if (ballot(over) && lane == 0) or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     if (gb == sg.block0 + K - 1) {
         write_header(sg, lane, p2 - base, base);
         if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = p2 - base;
@@ -559,12 +560,15 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t gb = blockIdx.x * kWaves + wave;
+    __shared__ __attribute__((aligned(16))) uint8_t s_head[kWaves][512];
     if (gb >= a.total_blocks) return;
     const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
-    const uint32_t slot = block_slot(a.seg[s], gb);
-    const uint2 head = stage_head(a, slot, lane);
+    const CSeg sg = a.seg[s];
+    const uint32_t slot = block_slot(sg, gb);
+    reinterpret_cast<uint2*>(s_head[wave])[lane] = stage_head(a, slot, lane);
     const uint32_t p0 = a.pos[slot], p1 = a.pos[slot + 1], p2 = a.pos[slot + 2];
-    place_block(a, s, gb, slot, head, p0, p1, p2, a.pos[a.seg[s].unit0 * kEncWaves], lane);
+    wave_lds_sync();
+    place_block(a, sg, s, gb, slot, s_head[wave], p0, p1, p2, a.pos[sg.unit0 * kEncWaves], lane);
 }
 
 // Place without the scan kernel: one workgroup per 8 encode units, one unit (4 blocks)
@@ -581,6 +585,7 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
 {
     __shared__ uint32_t s_red[2][kPlaceUnits];
     __shared__ uint32_t s_ucnt[kPlaceUnits];
+    __shared__ __attribute__((aligned(16))) uint8_t s_head[kPlaceUnits][kWaves][512];   // 16 KB
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t u_first = blockIdx.x * kPlaceUnits;
@@ -603,7 +608,7 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
 
     // segment lookups meanwhile
     const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
-    const CSeg& sg = a.seg[s];
+    const CSeg sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
     const uint32_t b0 = (unit - sg.unit0) * kWaves;   // first block of the unit within the segment
     const int s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
@@ -630,6 +635,8 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
         s_red[0][wave] = acc;
         s_red[1][wave] = accs;
     }
+#pragma unroll
+    for (uint32_t k = 0; k < kWaves; k++) reinterpret_cast<uint2*>(s_head[wave][k])[lane] = head[k];
     __syncthreads();
     if (!active) return;
     uint32_t pre = 0, first_base = 0;
@@ -654,7 +661,7 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
     for (uint32_t k = 0; k < kWaves; k++) {
         if (b0 + k >= K) break;
         const uint32_t p0 = p, p1 = p0 + hc[2 * k], p2 = p1 + hc[2 * k + 1];
-        place_block(a, s, sg.block0 + b0 + k, slot0 + 2 * k, head[k], p0, p1, p2, base, lane);
+        place_block(a, sg, s, sg.block0 + b0 + k, slot0 + 2 * k, s_head[wave][k], p0, p1, p2, base, lane);
         p = p2;
     }
 }
