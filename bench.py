@@ -76,7 +76,8 @@ def to_dev(torch, bits):
 
 
 class BatchCodec:
-    """Device buffers for one workload: R rotating sets of inputs and outputs."""
+    """Device buffers for one workload: R rotating sets of inputs and outputs, each with
+    its compress and decompress calls marshalled once."""
 
     def __init__(self, torch, Z, segments, sigmas, sets):
         self.torch, self.Z = torch, Z
@@ -84,28 +85,29 @@ class BatchCodec:
         self.n = sum(self.sizes)
         self.sigmas = sigmas
         self.static_bytes = sum(Z.static_size(n) for n in self.sizes)
-        self.sets = []
-        for _ in range(sets):
-            ins = [to_dev(torch, s) for s in segments]
-            self.sets.append(dict(
-                ins=ins,
-                static=torch.empty(self.static_bytes, dtype=torch.uint8, device="cuda"),
-                esc=torch.empty(self.n, dtype=torch.uint8, device="cuda"),
-                outs=[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in self.sizes]))
         self.ws = torch.zeros(Z.workspace_size(self.n, len(self.sizes)), dtype=torch.uint8, device="cuda")
         self.n_esc = torch.zeros(len(self.sizes) + 1, dtype=torch.int64, device="cuda")
         self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.sets = []
+        for _ in range(sets):
+            ins = [to_dev(torch, s) for s in segments]
+            st = dict(
+                ins=ins,
+                static=torch.empty(self.static_bytes, dtype=torch.uint8, device="cuda"),
+                esc=torch.empty(self.n, dtype=torch.uint8, device="cuda"),
+                outs=[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in self.sizes])
+            st["c"] = Z.PreparedCompress(ins, st["static"], st["esc"], self.ws, self.n_esc, self.status)
+            st["d"] = Z.PreparedDecompress(st["static"], st["esc"], st["outs"], self.status)
+            self.sets.append(st)
 
     def plans(self):
-        return [self.Z.plan(sigma=s) for s in self.sigmas]
+        return self.Z.plan_many(self.sigmas)
 
     def compress(self, k, plans):
-        s = self.sets[k % len(self.sets)]
-        self.Z.compress(list(zip(s["ins"], plans)), s["static"], s["esc"], self.ws, self.n_esc, self.status)
+        self.sets[k % len(self.sets)]["c"].run(plans)
 
     def decompress(self, k):
-        s = self.sets[k % len(self.sets)]
-        self.Z.decompress(s["static"], s["esc"], s["outs"], self.status)
+        self.sets[k % len(self.sets)]["d"].run()
 
     def verify(self):
         """One clean round trip per set, compared on the device with the inputs."""
@@ -132,11 +134,12 @@ def compress_bytes(n, static_bytes, n_esc):
 LAG = 2   # a set is decompressed two iterations after it was compressed
 
 
-def run_codec(torch, bc, iters, warmup, per_step_plans=False):
-    """Steady-state loop.  Iteration i compresses set i % R and decompresses set
+def run_codec(torch, bc, iters, warmup):
+    """Steady-state loop, timed by the host clock between two device synchronisations.
+    Iteration i plans the tables on the host, compresses set i % R and decompresses set
     (i - LAG) % R, compressed LAG iterations earlier; in between, other sets' traffic
     (> 2 x 256 MB) has gone through, so neither kernel finds its input in the Infinity
-    Cache.  Returns (compress ms list, decompress ms list, wall ms per step)."""
+    Cache.  Returns the wall ms per step."""
     R = len(bc.sets)
     assert R > LAG
     plans = bc.plans()
@@ -146,20 +149,22 @@ def run_codec(torch, bc, iters, warmup, per_step_plans=False):
         bc.compress(i % R, plans)
         bc.decompress((i - LAG) % R)
     torch.cuda.synchronize()
-    tc, td = Timer(torch), Timer(torch)
     t0 = time.perf_counter()
     for i in range(warmup, warmup + iters):
-        if per_step_plans:
-            plans = bc.plans()                  # sigma -> tables, on the host
-        e = tc.start()
+        plans = bc.plans()                  # sigma -> tables, on the host
         bc.compress(i % R, plans)
-        tc.stop(e)
-        e = td.start()
         bc.decompress((i - LAG) % R)
-        td.stop(e)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / iters * 1e3
-    return tc.ms(), td.ms(), wall
+    return (time.perf_counter() - t0) / iters * 1e3
+
+
+def op_times(torch, bc, rounds):
+    """Average launch times (ms) of compress and decompress over back-to-back launches on
+    the rotating sets."""
+    plans = bc.plans()
+    c = batched_ms(torch, lambda k: bc.compress(k, plans), len(bc.sets), rounds)
+    d = batched_ms(torch, bc.decompress, len(bc.sets), rounds)
+    return c, d
 
 
 def batched_ms(torch, fn, sets, rounds):
@@ -177,10 +182,10 @@ def batched_ms(torch, fn, sets, rounds):
     return e0.elapsed_time(e1) / (rounds * sets)
 
 
-def codec_report(bc, c_ms, d_ms):
+def codec_report(bc, c, d):
+    """Per-operation figures from average launch times c, d (ms)."""
     n_esc = bc.n_esc_total()
     moved = compress_bytes(bc.n, bc.static_bytes, n_esc)
-    c, d = median(c_ms), median(d_ms)
     return {
         "elements": bc.n,
         "segments": len(bc.sizes),
@@ -213,18 +218,19 @@ def bench_rs(torch, Z, W, iters):
     n_esc = torch.zeros(nch, P + 1, dtype=torch.int64, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
 
+    comp = [Z.PreparedCompress([p[c * chunk:(c + 1) * chunk] for p in peers], static[c * P * S:(c + 1) * P * S],
+                               esc[c * P * chunk:(c + 1) * P * chunk], ws, n_esc[c], status) for c in range(nch)]
+    acc = [Z.PreparedAccumulate([static.data_ptr() + (c * P + p) * S for p in range(P)],
+                                [esc.data_ptr() + c * P * chunk] * P, chunk, local[c * chunk:], dst[c * chunk:],
+                                status, esc_bytes=[P * chunk] * P) for c in range(nch)]
+
     def compress_all():
         for c in range(nch):
-            segs = [(p[c * chunk:(c + 1) * chunk], pl) for p, pl in zip(peers, plans)]
-            Z.compress(segs, static[c * P * S:(c + 1) * P * S], esc[c * P * chunk:(c + 1) * P * chunk], ws,
-                       n_esc[c], status)
+            comp[c].run(plans)
 
     def accumulate_all():
         for c in range(nch):
-            base = static.data_ptr() + c * P * S
-            eb = esc.data_ptr() + c * P * chunk
-            Z.decompress_accumulate([base + p * S for p in range(P)], [eb] * P, chunk, local[c * chunk:],
-                                    dst[c * chunk:], status, esc_bytes=[P * chunk] * P)
+            acc[c].run()
 
     compress_all()
     accumulate_all()
@@ -459,17 +465,15 @@ def main(argv=None) -> int:
     n = bc.n
 
     log(f"warmup {args.warmup}, timing {args.steps} steps")
-    c_ms, d_ms, ms_per_step = run_codec(torch, bc, args.steps, args.warmup, per_step_plans=True)
-    ok = bc.verify()
-    rep = codec_report(bc, c_ms, d_ms)
+    ms_per_step = run_codec(torch, bc, args.steps, args.warmup)
     value = 4 * n / (ms_per_step * 1e-3) / 1e9
+    # per-launch averages (roofline, per-operation figures): back-to-back launches over
+    # the rotating sets
+    c_avg, d_avg = op_times(torch, bc, max(2, args.steps // len(bc.sets)))
+    ok = bc.verify()
+    rep = codec_report(bc, c_avg, d_avg)
     n_esc = bc.n_esc_total()
     moved = compress_bytes(n, bc.static_bytes, n_esc)
-    # per-launch averages for the roofline: back-to-back launches over the rotating sets
-    plans = bc.plans()
-    rounds = max(2, args.steps // len(bc.sets))
-    c_avg = batched_ms(torch, lambda k: bc.compress(k, plans), len(bc.sets), rounds)
-    d_avg = batched_ms(torch, bc.decompress, len(bc.sets), rounds)
 
     traffic = measured_traffic()
 
@@ -479,9 +483,8 @@ def main(argv=None) -> int:
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                 "bytes_per_launch": moved, "avg_launch_us": round(avg_ms * 1e3, 2), "traffic": traffic.get(op)}
 
-    # the step's dominant kernel: decompress is one launch; compress is two (encode_kernel,
-    # place_direct_kernel; three with scan_kernel above 2^28 values), timed together by
-    # the events
+    # the step's dominant operation: decompress is one launch; compress is two
+    # (encode_kernel, place_direct_kernel; three with scan_kernel above 2^28 values)
     units = sum((m + 16383) // 16384 for m in bc.sizes)
     c_launches = (["encode_kernel", "place_direct_kernel"] if units <= 16384
                   else ["encode_kernel", "scan_kernel", "place_kernel"])
@@ -525,7 +528,8 @@ def main(argv=None) -> int:
             w2 = W.get(name)
             sets = 8 if name == "chunk_1m" else 4
             b2 = BatchCodec(torch, Z, w2.segments, w2.sigmas, sets)
-            cm, dm, _ = run_codec(torch, b2, 20, 3)
+            run_codec(torch, b2, 3, 3)
+            cm, dm = op_times(torch, b2, 5)
             r2 = codec_report(b2, cm, dm)
             r2["parity_round_trip"] = b2.verify()
             per[name] = r2

@@ -94,6 +94,11 @@ typedef struct zipccl_dsegment_t {
  * Returns ZIPCCL_ERR_INVALID on a bad sigma or table, or a NULL out. */
 zipccl_status zipccl_plan(double sigma, const uint8_t* table7, zipccl_plan_t* out);
 
+/* Plans for n tensors at once (S2.A): out[i] = zipccl_plan(sigma[i], NULL, ...).  sigma
+ * and out are host arrays of n entries (n >= 0).  On a bad sigma returns
+ * ZIPCCL_ERR_INVALID; out[i] is then written for the sigmas before it only.  Host only. */
+zipccl_status zipccl_plan_many(const double* sigma, int n, zipccl_plan_t* out);
+
 /* Bytes of the fixed-size part of one segment of n values (format above). */
 uint64_t zipccl_static_size(uint64_t n);
 

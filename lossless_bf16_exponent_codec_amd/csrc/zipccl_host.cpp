@@ -90,6 +90,16 @@ zipccl_status zipccl_plan(double sigma, const uint8_t* table7, zipccl_plan_t* ou
     return ZIPCCL_OK;
 }
 
+zipccl_status zipccl_plan_many(const double* sigma, int n, zipccl_plan_t* out)
+{
+    if (n < 0 || (n > 0 && (!sigma || !out))) return ZIPCCL_ERR_INVALID;
+    for (int i = 0; i < n; i++) {
+        const zipccl_status r = zipccl_plan(sigma[i], nullptr, out + i);
+        if (r != ZIPCCL_OK) return r;
+    }
+    return ZIPCCL_OK;
+}
+
 uint64_t zipccl_static_size(uint64_t n) { return static_bytes_of(n); }
 
 uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc) { return static_bytes_of(n) + n_esc; }

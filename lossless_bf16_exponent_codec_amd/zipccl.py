@@ -56,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_strerror.argtypes = [i32]
     lib.zipccl_plan.restype = i32
     lib.zipccl_plan.argtypes = [ctypes.c_double, ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(PlanT)]
+    lib.zipccl_plan_many.restype = i32
+    lib.zipccl_plan_many.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(PlanT)]
     lib.zipccl_static_size.restype = u64
     lib.zipccl_static_size.argtypes = [u64]
     lib.zipccl_compressed_size.restype = u64
@@ -128,6 +130,15 @@ def plan(sigma: float | None = None, table=None) -> PlanT:
     return out
 
 
+def plan_many(sigmas):
+    """zipccl_plan_many: one plan per sigma, as a ctypes array of PlanT."""
+    n = len(sigmas)
+    sig = (ctypes.c_double * max(n, 1))(*[float(x) for x in sigmas])
+    out = (PlanT * max(n, 1))()
+    _check(_lib.zipccl_plan_many(sig, n, out), "zipccl_plan_many")
+    return out
+
+
 def static_size(n: int) -> int:
     return int(_lib.zipccl_static_size(n))
 
@@ -179,6 +190,65 @@ def decompress_accumulate(static_ins, esc_ins, n: int, local, dst, status=None, 
     eb = (ctypes.c_uint64 * P)(*[int(v) for v in esc_bytes])
     rc = _lib.zipccl_decompress_accumulate(sp, ep, eb, P, n, _ptr(local), _ptr(dst), _ptr(status), _stream(stream))
     _check(rc, "zipccl_decompress_accumulate")
+
+
+class PreparedCompress:
+    """A zipccl_compress call over fixed buffers: the segment table and every other
+    argument are marshalled once; run(plans) writes this call's plans into the table and
+    makes the call (for loops that compress the same buffers with new plans)."""
+
+    def __init__(self, tensors, static_out, esc_out, workspace, n_esc_out=None, status=None, stream=None,
+                 esc_cap=None):
+        self.n = len(tensors)
+        self._arr = (SegmentT * max(self.n, 1))()
+        for k, t in enumerate(tensors):
+            self._arr[k].src = _ptr(t) if t.numel() else None
+            self._arr[k].n = t.numel()
+        cap = _nbytes(esc_out) if esc_cap is None else esc_cap
+        self._args = (_ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap, _ptr(workspace),
+                      _nbytes(workspace), _ptr(n_esc_out), _ptr(status), _stream(stream))
+        self._keep = (tensors, static_out, esc_out, workspace, n_esc_out, status)
+
+    def run(self, plans):
+        arr = self._arr
+        for k in range(self.n):
+            arr[k].plan = plans[k]
+        _check(_lib.zipccl_compress(arr, self.n, *self._args), "zipccl_compress")
+
+
+class PreparedDecompress:
+    """A zipccl_decompress call over fixed buffers, marshalled once; run() makes it."""
+
+    def __init__(self, static_in, esc_in, dsts, status=None, stream=None, static_bytes=None, esc_bytes=None):
+        self.n = len(dsts)
+        self._arr = (DSegmentT * max(self.n, 1))()
+        for k, t in enumerate(dsts):
+            self._arr[k].dst = _ptr(t) if t.numel() else None
+            self._arr[k].n = t.numel()
+        sb = _nbytes(static_in) if static_bytes is None else static_bytes
+        eb = (_nbytes(esc_in) if esc_in is not None else 0) if esc_bytes is None else esc_bytes
+        self._args = (_ptr(static_in), sb, _ptr(esc_in), eb, self._arr, self.n, _ptr(status), _stream(stream))
+        self._keep = (static_in, esc_in, dsts, status)
+
+    def run(self):
+        _check(_lib.zipccl_decompress(*self._args), "zipccl_decompress")
+
+
+class PreparedAccumulate:
+    """A zipccl_decompress_accumulate call over fixed buffers, marshalled once."""
+
+    def __init__(self, static_ins, esc_ins, n: int, local, dst, status=None, stream=None, esc_bytes=None):
+        P = len(static_ins)
+        self._sp = (ctypes.c_void_p * P)(*[_ptr(t) for t in static_ins])
+        self._ep = (ctypes.c_void_p * P)(*[_ptr(t) for t in esc_ins])
+        if esc_bytes is None:
+            esc_bytes = [_nbytes(t) for t in esc_ins]
+        self._eb = (ctypes.c_uint64 * P)(*[int(v) for v in esc_bytes])
+        self._args = (self._sp, self._ep, self._eb, P, n, _ptr(local), _ptr(dst), _ptr(status), _stream(stream))
+        self._keep = (static_ins, esc_ins, local, dst, status)
+
+    def run(self):
+        _check(_lib.zipccl_decompress_accumulate(*self._args), "zipccl_decompress_accumulate")
 
 
 def pipeline_scratch_size(npeers: int, chunk: int) -> int:

@@ -33,7 +33,7 @@ def test_header_declares_the_abi():
     for want in ["zipccl_plan", "zipccl_compress", "zipccl_decompress", "zipccl_decompress_accumulate",
                  "zipccl_compressed_size", "zipccl_static_size", "zipccl_workspace_size",
                  "zipccl_pipeline_create", "zipccl_pipeline_reduce", "zipccl_pipeline_destroy",
-                 "zipccl_pipeline_scratch_size", "zipccl_strerror"]:
+                 "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many"]:
         assert want in names
 
 
@@ -91,6 +91,19 @@ def test_plan_table_and_errors(Z):
     for bad in (0.0, -1.0, float("nan"), float("inf")):
         with pytest.raises(Z.ZipcclError):
             Z.plan(sigma=bad)
+
+
+def test_plan_many_matches_plan(Z):
+    rng = np.random.default_rng(12)
+    sig = [float(10 ** x) for x in rng.uniform(-30, 30, 500)] + [1e-300, 1e300, 1.0, 2.0 ** -126]
+    many = Z.plan_many(sig)
+    for i, s in enumerate(sig):
+        assert list(many[i].table) == list(Z.plan(sigma=s).table)
+    assert Z.lib().zipccl_plan_many(None, 0, None) == Z.OK
+    bad = (ctypes.c_double * 3)(1.0, -1.0, 2.0)
+    out = (Z.PlanT * 3)()
+    assert Z.lib().zipccl_plan_many(bad, 3, out) == Z.ERR_INVALID
+    assert list(out[0].table) == list(Z.plan(sigma=1.0).table)
 
 
 @pytest.mark.parametrize("n", [0, 1, 7, 8, 511, 512, 513, 4095, 4096, 4097, 16384, 2 ** 22, 2 ** 26 + 3,

@@ -160,6 +160,45 @@ def test_determinism_and_workspace_reuse(Z):
             assert np.array_equal(first, r["static_h"])
 
 
+def test_prepared_calls_match_plain_calls(Z):
+    # the marshalled-once call objects give the same bytes as the plain calls
+    segs = [W.gaussian_bf16(n, s, 300 + k) for k, (n, s) in enumerate([(70001, 0.02), (0, 1.0), (4096, 3e-3)])]
+    sig = [0.02, 1.0, 3e-3]
+    r = gpu_compress(Z, segs, list(Z.plan_many(sig)))
+    check_against_oracle(Z, segs, list(Z.plan_many(sig)), r)
+    tens = [dev_bf16(x) for x in segs]
+    static = torch.full_like(r["static"], POISON)
+    esc = torch.full_like(r["esc"], POISON)
+    n_esc = torch.full((len(segs) + 1,), -1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(Z.workspace_size(sum(x.size for x in segs), len(segs)), dtype=torch.uint8, device="cuda")
+    pc = Z.PreparedCompress(tens, static, esc, ws, n_esc, status)
+    for _ in range(2):
+        pc.run(Z.plan_many(sig))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and list(n_esc.cpu().numpy()) == list(r["n_esc"])
+    assert torch.equal(static, r["static"]) and torch.equal(esc[:int(r["n_esc"][-1])], r["esc"][:int(r["n_esc"][-1])])
+    outs = [torch.full((x.size,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16) for x in segs]
+    Z.PreparedDecompress(static, esc, outs, status).run()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for x, o in zip(segs, outs):
+        assert np.array_equal(x, host_u16(o))
+    # accumulate: three 9000-value peers against the plain call
+    n = 9000
+    peers = [W.gaussian_bf16(n, 0.1, 40 + p) for p in range(3)]
+    local = W.gaussian_bf16(n, 0.1, 50)
+    plans = [Z.plan(sigma=0.1)] * 3
+    want, st_plain, rr = gpu_accumulate(Z, peers, plans, local)
+    S = Z.static_size(n)
+    dst = torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    base = rr["static"].data_ptr()
+    Z.PreparedAccumulate([base + p * S for p in range(3)], [rr["esc"].data_ptr()] * 3, n, dev_bf16(local), dst,
+                         status, esc_bytes=[rr["esc"].numel()] * 3).run()
+    torch.cuda.synchronize()
+    assert st_plain == 0 and int(status.item()) == 0 and np.array_equal(host_u16(dst), want)
+
+
 def test_all_empty_and_boundary_segments(Z):
     # empty segments first, between blocks and at the end; a segment of exactly 256
     # blocks puts the following ones on a finalize-workgroup boundary
