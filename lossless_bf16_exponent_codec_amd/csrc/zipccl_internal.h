@@ -24,8 +24,8 @@ constexpr uint32_t kEncThreads = 64 * kEncWaves;
 // unit u (slots past a segment's end hold 0 escapes).  A u32 escape count per slot,
 // the launch-wide position of each slot's first escape (one more entry for the total;
 // used only when the positions come from the scan kernel), a u32 escape count per
-// unit, then kHalf staging bytes per slot that hold its escape exponents until their
-// positions are known.
+// unit, then kUnit staging bytes per unit that hold its escape exponents, contiguous
+// in value order, until their positions are known.
 __host__ __device__ inline uint64_t ws_counts_bytes(uint64_t units) { return (32 * units + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_pos_bytes(uint64_t units) { return (4 * (8 * units + 1) + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_units_bytes(uint64_t units) { return (4 * (units + 1) + 255) & ~uint64_t(255); }
@@ -56,7 +56,7 @@ struct CArgs {
     uint32_t* counts;      // workspace: escapes per half-block slot
     uint32_t* pos;         // workspace: launch-wide position of each slot's first escape
     uint32_t* unit_counts; // workspace: escapes per workgroup unit
-    uint8_t* stage;        // workspace: kHalf bytes per slot
+    uint8_t* stage;        // workspace: kUnit bytes per unit
     uint64_t* n_esc_out;   // nseg + 1 entries or null
     uint32_t* status;      // or null
     int32_t nseg;

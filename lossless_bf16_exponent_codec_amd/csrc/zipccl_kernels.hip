@@ -276,8 +276,8 @@ __device__ inline void stage_tile_escapes(const TileEsc& te, uint32_t r, uint8_t
 }
 
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
-// planes, the escape count and the staged escape exponents; zero padding after the
-// segment's last half block.  gh: the half block's workspace slot.
+// planes, the escape count (to workspace slot gh) and the escape exponents in value
+// order in s_esc; zero padding after the segment's last half block.
 __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
                                        uint32_t lane, const uint8_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
@@ -315,12 +315,7 @@ __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t 
     const uint32_t run = min(half_ranks(cnt, start), kHalf);
 #pragma unroll
     for (int k = 0; k < 4; k++) stage_tile_escapes(te[k], start[k], s_esc);
-    wave_lds_sync();
-    // hand the escapes to the place kernel (whole dwords; bytes past `run` are unused)
     if (lane == 0) a.counts[gh] = run;
-    uint8_t* stage = a.stage + uint64_t(gh) * kHalf;
-    for (uint32_t k = 4 * lane; k < run; k += 256)
-        *reinterpret_cast<uint32_t*>(stage + k) = *reinterpret_cast<const uint32_t*>(s_esc + k);
     if (hb == 2 * K - 1) {   // zero padding of the plane and offset sections
         const uint32_t bpad = uint32_t(round128(192ull * T) - 192ull * T);
         uint8_t* bp = reinterpret_cast<uint8_t*>(B) + 192ull * T;
@@ -333,8 +328,8 @@ __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t 
 }
 
 // Encode: one workgroup per unit of 4 blocks, one half block per wave.  No workgroup
-// waits for another: each wave writes its tiles' A bytes and planes, its escape count
-// and its staged escape exponents.
+// waits for another: each wave writes its tiles' A bytes and planes and its escape
+// count; the unit's escape exponents go, in value order, to the unit's staging area.
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
 {
     __shared__ uint8_t s_lut[256];
@@ -377,16 +372,21 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     const uint32_t slot = unit * kEncWaves + wave;
     if (active) run = encode_half(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
     else if (lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
-    if (a.direct) {   // the unit's escape count, for the place kernel's prefix sums
-        if (lane == 0) s_hcnt[wave] = run;
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t t = 0;
+    if (lane == 0) s_hcnt[wave] = run;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
 #pragma unroll
-            for (uint32_t w = 0; w < kEncWaves; w++) t += s_hcnt[w];
-            a.unit_counts[unit] = t;
-        }
+    for (uint32_t w = 0; w < kEncWaves; w++) {
+        const uint32_t c = s_hcnt[w];
+        if (w < wave) before += c;
+        total += c;
     }
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (tid == 0) a.unit_counts[unit] = total;   // for the place kernel's prefix sums
+    // the unit's escapes, contiguous in value order: one run per unit for the place kernel
+    uint8_t* stage = a.stage + uint64_t(unit) * kUnit + before;
+    const uint8_t* esc_lds = s_esc[wave];
+    for (uint32_t k = lane; k < run; k += 64) stage[k] = esc_lds[k];
 }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
@@ -493,49 +493,52 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
     }
 }
 
-// Copies the first min(cnt, 256) staged escapes of one half block from LDS (src) to
-// esc[p ...]: lane l writes bytes l, l + 64, ..., so each store instruction covers 64
-// consecutive bytes.  Returns true if a byte fell at or past esc_cap.
-__device__ inline bool place_half(const CArgs& a, const uint8_t* src, uint32_t p, uint32_t cnt, uint32_t lane)
+// Copies len bytes from LDS (src) to esc[p + off ...], lane l writing bytes l, l + 64, ...
+// so that each store instruction covers 64 consecutive bytes.  Bytes at or past esc_cap
+// are dropped (returns true if there were any).
+__device__ inline bool copy_run(const CArgs& a, const uint8_t* src, uint32_t p, uint32_t off, uint32_t len,
+                                uint32_t lane)
 {
-    const uint32_t m = min(cnt, 256u);
-    uint8_t* dst = a.esc + p;
-    if (uint64_t(p) + m <= a.esc_cap) {   // the common case: no per-byte check
-        for (uint32_t k = lane; k < m; k += 64) dst[k] = src[k];
+    uint8_t* dst = a.esc + p + off;
+    if (uint64_t(p) + off + len <= a.esc_cap) {   // the common case: no per-byte check
+        for (uint32_t k = lane; k < len; k += 64) dst[k] = src[k];
         return false;
     }
     bool over = false;
-    for (uint32_t k = lane; k < m; k += 64) {
-        if (uint64_t(p) + k < a.esc_cap) dst[k] = src[k];
+    for (uint32_t k = lane; k < len; k += 64) {
+        if (uint64_t(p) + off + k < a.esc_cap) dst[k] = src[k];
         else over = true;
     }
     return over;
 }
 
-// Places block gb (launch-wide) of segment sg (index s), whose halves are in workspace
-// slots slot and slot + 1: its offset-table entry, the staged escape bytes of the two
-// halves (positions p0, p1, p2 = start of half 0, half 1, end; base = the segment's
-// first escape), the segment header from the segment's last block, and the headers of
-// empty segments next to it.  heads: the first 256 staged bytes of each half in LDS
-// (half 1 at heads + 256), requested before the positions were known.
-__device__ inline void place_block(const CArgs& a, const CSeg& sg, int s, uint32_t gb, uint32_t slot,
-                                   const uint8_t* heads, uint32_t p0, uint32_t p1, uint32_t p2, uint32_t base,
-                                   uint32_t lane)
+// Copies the m staged escapes of one unit to esc[p ...] (every lane of one wave).  lds:
+// the wave's 1 KB LDS buffer, holding the first 512 staged bytes; more (rare) are
+// brought from the unit's staging area (stage) 1 KB at a time, 16 bytes per lane.
+// Returns true if a byte fell at or past esc_cap.
+__device__ inline bool place_unit_escapes(const CArgs& a, uint8_t* lds, const uint8_t* stage, uint32_t p,
+                                          uint32_t m, uint32_t lane)
+{
+    bool over = copy_run(a, lds, p, 0, min(m, 512u), lane);
+    for (uint32_t c0 = 512; c0 < m; c0 += 1024) {   // rare: more than 512 escapes in the unit
+        const uint32_t o = c0 + 16 * lane;
+        const uint4 x = o + 16 <= kUnit ? reinterpret_cast<const uint4*>(stage + o)[0] : make_uint4(0, 0, 0, 0);
+        wave_lds_sync();   // earlier reads of the buffer are done
+        reinterpret_cast<uint4*>(lds)[lane] = x;
+        wave_lds_sync();
+        over = copy_run(a, lds, p, c0, min(m - c0, 1024u), lane) || over;
+    }
+    return over;
+}
+
+// Offset-table entry of block gb (launch-wide) of segment sg (index s), whose escapes
+// occupy [p0, p2) (base = the segment's first escape); the segment header from the
+// segment's last block, and the headers of empty segments next to it.
+__device__ inline void place_block_tables(const CArgs& a, const CSeg& sg, int s, uint32_t gb, uint32_t p0,
+                                          uint32_t p2, uint32_t base, uint32_t lane)
 {
     const uint32_t K = uint32_t(blocks_of(sg.n));
     if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
-    bool over = place_half(a, heads, p0, p1 - p0, lane);
-    over = place_half(a, heads + 256, p1, p2 - p1, lane) || over;
-    for (uint32_t hh = 0; hh < 2; hh++) {   // rare: more than 256 escapes in a half block
-        const uint32_t c = hh ? p2 - p1 : p1 - p0, q = hh ? p1 : p0;
-        const uint8_t* st = a.stage + uint64_t(slot + hh) * kHalf;
-        for (uint32_t k = 256 + lane; k < c; k += 64) {
-            const uint64_t at = uint64_t(q) + k;
-            if (at < a.esc_cap) a.esc[at] = st[k];
-            else over = true;
-        }
-    }
-    if (ballot(over) && lane == 0) or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     if (gb == sg.block0 + K - 1) {
         write_header(sg, lane, p2 - base, base);
         if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = p2 - base;
@@ -557,14 +560,6 @@ __device__ inline void place_block(const CArgs& a, const CSeg& sg, int s, uint32
     }
 }
 
-// Staged bytes 8*hl .. 8*hl+7 of slot + (lane >> 5), hl = lane & 31 (lanes 0-31: the
-// block's first half).
-__device__ inline uint2 stage_head(const CArgs& a, uint32_t slot, uint32_t lane)
-{
-    const uint8_t* stage = a.stage + uint64_t(slot + (lane >> 5)) * kHalf;
-    return reinterpret_cast<const uint2*>(stage)[lane & 31u];
-}
-
 // Workspace slot of the first half of block gb (launch-wide) of segment s.
 __device__ inline uint32_t block_slot(const CSeg& sg, uint32_t gb)
 {
@@ -572,29 +567,37 @@ __device__ inline uint32_t block_slot(const CSeg& sg, uint32_t gb)
     return (sg.unit0 + lb / kWaves) * kEncWaves + (lb % kWaves) * 2;
 }
 
-// Place, after the scan kernel: one wave per block, positions from pos[].
+// Place, after the scan kernel: one wave per block, positions from pos[]; the block's
+// escapes are copied from its unit's staging area byte by byte.
 __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
 {
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t gb = blockIdx.x * kWaves + wave;
-    __shared__ __attribute__((aligned(16))) uint8_t s_head[kWaves][512];
     if (gb >= a.total_blocks) return;
     const int s = find_segment<&CSeg::block0>(a.seg, a.nseg, gb);
     const CSeg sg = a.seg[s];
     const uint32_t slot = block_slot(sg, gb);
-    reinterpret_cast<uint2*>(s_head[wave])[lane] = stage_head(a, slot, lane);
-    const uint32_t p0 = a.pos[slot], p1 = a.pos[slot + 1], p2 = a.pos[slot + 2];
-    wave_lds_sync();
-    place_block(a, sg, s, gb, slot, s_head[wave], p0, p1, p2, a.pos[sg.unit0 * kEncWaves], lane);
+    const uint32_t unit = slot / kEncWaves;
+    const uint32_t p0 = a.pos[slot], p2 = a.pos[slot + 2], pu = a.pos[unit * kEncWaves];
+    const uint8_t* stage = a.stage + uint64_t(unit) * kUnit + (p0 - pu);
+    bool over = false;
+    for (uint32_t k = lane; k < p2 - p0; k += 64) {
+        const uint64_t at = uint64_t(p0) + k;
+        if (at < a.esc_cap) a.esc[at] = stage[k];
+        else over = true;
+    }
+    if (ballot(over) && lane == 0) or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
+    place_block_tables(a, sg, s, gb, p0, p2, a.pos[sg.unit0 * kEncWaves], lane);
 }
 
 // Place without the scan kernel: one workgroup per 8 encode units, one unit (4 blocks)
 // per wave.  The workgroup sums the escape counts of all units before its first one
 // (and before the first unit of that unit's segment) from unit_counts[], a few
-// kilobytes read from L2; each wave then derives its blocks' positions from its unit's
-// 8 half-block counts.  Every load that needs no segment information (workspace slots
-// are indexed by unit) is issued before the segment lookups in the kernel arguments.
+// kilobytes read from L2; each wave then copies its unit's escapes (staged contiguous,
+// the first 512 bytes requested up front) in one run and derives its blocks' offsets
+// from the unit's 8 half-block counts.  Every load that needs no segment information
+// is issued before the segment lookups in the kernel arguments.
 constexpr uint32_t kPlaceUnits = 8;
 constexpr uint32_t kPlaceThreads = 64 * kPlaceUnits;
 constexpr uint32_t kPrefixLoads = kDirectPrefixMaxUnits / (4 * kPlaceThreads);   // uint4 loads per thread
@@ -603,17 +606,16 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
 {
     __shared__ uint32_t s_red[2][kPlaceUnits];
     __shared__ uint32_t s_ucnt[kPlaceUnits];
-    __shared__ __attribute__((aligned(16))) uint8_t s_head[kPlaceUnits][kWaves][512];   // 16 KB
+    __shared__ __attribute__((aligned(16))) uint8_t s_head[kPlaceUnits][1024];   // staged escapes, per wave
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t u_first = blockIdx.x * kPlaceUnits;
     const uint32_t unit = u_first + wave;
     const bool active = unit < a.total_units;
     const uint32_t slot0 = unit * kEncWaves;
-    uint2 head[kWaves];        // staged heads of the unit's 4 blocks
+    const uint8_t* stage = a.stage + uint64_t(unit) * kUnit;   // the unit's escapes, contiguous
+    const uint2 head = active ? reinterpret_cast<const uint2*>(stage)[lane] : make_uint2(0, 0);
     uint32_t hc[2 * kWaves];   // the unit's half-block escape counts
-#pragma unroll
-    for (uint32_t k = 0; k < kWaves; k++) head[k] = active ? stage_head(a, slot0 + 2 * k, lane) : make_uint2(0, 0);
 #pragma unroll
     for (uint32_t k = 0; k < 2 * kWaves; k++) hc[k] = active ? a.counts[slot0 + k] : 0u;
     if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
@@ -653,8 +655,7 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
         s_red[0][wave] = acc;
         s_red[1][wave] = accs;
     }
-#pragma unroll
-    for (uint32_t k = 0; k < kWaves; k++) reinterpret_cast<uint2*>(s_head[wave][k])[lane] = head[k];
+    reinterpret_cast<uint2*>(s_head[wave])[lane] = head;
     __syncthreads();
     if (!active) return;
     uint32_t pre = 0, first_base = 0;
@@ -673,13 +674,15 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
         base = pre;
         for (uint32_t w = 0; w < sg.unit0 - u_first; w++) base += s_ucnt[w];
     }
-    // positions of the unit's blocks from its 8 half-block counts
+    // the unit's escapes in one run; its blocks' positions from its 8 half-block counts
+    if (ballot(place_unit_escapes(a, s_head[wave], stage, upos, s_ucnt[wave], lane)) && lane == 0)
+        or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     uint32_t p = upos;
 #pragma unroll
     for (uint32_t k = 0; k < kWaves; k++) {
         if (b0 + k >= K) break;
-        const uint32_t p0 = p, p1 = p0 + hc[2 * k], p2 = p1 + hc[2 * k + 1];
-        place_block(a, sg, s, sg.block0 + b0 + k, slot0 + 2 * k, s_head[wave][k], p0, p1, p2, base, lane);
+        const uint32_t p0 = p, p2 = p0 + hc[2 * k] + hc[2 * k + 1];
+        place_block_tables(a, sg, s, sg.block0 + b0 + k, p0, p2, base, lane);
         p = p2;
     }
 }
