@@ -814,14 +814,28 @@ constexpr uint32_t kAccWaves = 8;                  // one wave per tile of a blo
 constexpr uint32_t kAccThreads = 64 * kAccWaves;
 constexpr uint32_t kEscPad = 16;                   // decode_lane may read esc_lds[total]
 
+// What decode-accumulate needs of a peer's header for the workgroup's block, checked by
+// one wave and shared through LDS: the v_perm decode table, where the block's escapes
+// start in the peer's escape buffer and how many there are.
+struct PeerBlock {
+    uint32_t tlo, thi;
+    uint32_t esc_lo, esc_hi;   // escape-buffer offset of the block's first escape
+    uint32_t count;
+    uint32_t ok;
+};
+
 // Decode-accumulate: one workgroup per block, one wave per tile.  Every peer's bytes
-// for the tile are requested up front; each wave counts its tile's escapes per peer
-// from the plane rows, one barrier shares the counts so that every wave knows where
-// its tile's escapes start, then the peers are decoded and added in order.
+// for the tile are requested up front; wave p checks peer p's header and offset-table
+// entries (one chain of scalar loads per wave instead of one per peer in every wave)
+// and leaves what the others need in LDS; each wave counts its tile's escapes per peer
+// from the plane rows, one barrier shares the counts and the peer records so that every
+// wave knows where its tile's escapes start, then the peers are decoded and added in
+// order.
 template <int kPeers>
 __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 {
     __shared__ uint32_t s_cnt[kPeers][kAccWaves];
+    __shared__ PeerBlock s_peer[kPeers];
     __shared__ uint8_t s_esc[kAccWaves][kTile + kEscPad];
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -840,33 +854,30 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     else if (nvalid > 0) lv = load_lane(a.local, t, lane, n);
     uint2 Ap[kPeers];
     uint32_t pw[kPeers];
-    bool bad = false;
-    uint32_t off0[kPeers], blk[kPeers], tlo[kPeers], thi[kPeers];
-    uint64_t eoff[kPeers];
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
         Ap[p] = make_uint2(0, 0);
         pw[p] = 0;
-        off0[p] = 0;
-        blk[p] = 0;
-        tlo[p] = thi[p] = 0;
-        eoff[p] = 0;
-        if (uint32_t(p) < P) {
+        // A and plane addresses follow from n alone
+        if (uint32_t(p) < P && has_tile) {
             const uint8_t* st = a.st[p];
-            // A and plane addresses follow from n alone: issue these loads first
-            if (has_tile) {
-                Ap[p] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane));
-                if (pdw != ~0u) pw[p] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t) + pdw);
-            }
+            Ap[p] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane));
+            if (pdw != ~0u) pw[p] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t) + pdw);
+        }
+    }
+    // ---- this wave's share of the header checks: peers wave, wave + 8 ----
+#pragma unroll
+    for (uint32_t p = wave; p < uint32_t(kPeers); p += kAccWaves) {
+        if (p < P) {
+            const uint8_t* st = a.st[p];
             const SegHeader hd = read_header(st, n, a.esc_bytes[p]);
             const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
             uint32_t first = 0, last = 0;
-            bad = bad || !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
-            off0[p] = first;
-            blk[p] = last - first;
-            tlo[p] = hd.tlo;
-            thi[p] = hd.thi;
-            eoff[p] = hd.esc_offset;
+            const bool ok = hd.ok && block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
+            if (lane == 0) {
+                const uint64_t e = hd.esc_offset + first;
+                s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, ok ? 1u : 0u};
+            }
         }
     }
 
@@ -889,6 +900,12 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 
     // ---- every peer's first 64 escape bytes of this tile, requested together ----
     uint32_t before[kPeers], mine[kPeers], ev[kPeers];
+    bool bad = false;
+#pragma unroll
+    for (int p = 0; p < kPeers; p++) {
+        if (uint32_t(p) < P) bad = bad || !s_peer[p].ok;
+    }
+    bad = __builtin_amdgcn_readfirstlane(bad);
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
         before[p] = mine[p] = ev[p] = 0;
@@ -902,8 +919,9 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
             }
             before[p] = bsum;
             mine[p] = total[p];
-            bad = bad || tot != blk[p];   // the offset table must agree with the planes
-            if (!bad && lane < mine[p]) ev[p] = a.esc[p][eoff[p] + off0[p] + bsum + lane];
+            bad = bad || tot != s_peer[p].count;   // the offset table must agree with the planes
+            const uint64_t e = uint64_t(s_peer[p].esc_hi) << 32 | s_peer[p].esc_lo;
+            if (!bad && lane < mine[p]) ev[p] = a.esc[p][e + bsum + lane];
         }
     }
 
@@ -921,11 +939,12 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
             // stage this peer's tile escapes in the wave's LDS slot
             if (lane < mine[p]) esc_lds[lane] = uint8_t(ev[p]);
             if (mine[p] > 64) {   // more than 64 escapes in one tile (escape-heavy tables)
-                const uint8_t* esc = a.esc[p] + eoff[p] + off0[p] + before[p];
+                const uint64_t e = uint64_t(s_peer[p].esc_hi) << 32 | s_peer[p].esc_lo;
+                const uint8_t* esc = a.esc[p] + e + before[p];
                 for (uint32_t k = 64 + lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
             }
             wave_lds_sync();
-            const LaneBytes o = decode_lane(rows[p], zf[p], Ap[p], tlo[p], thi[p], rank[p], esc_lds);
+            const LaneBytes o = decode_lane(rows[p], zf[p], Ap[p], s_peer[p].tlo, s_peer[p].thi, rank[p], esc_lds);
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
