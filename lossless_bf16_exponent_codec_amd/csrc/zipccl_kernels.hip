@@ -812,6 +812,7 @@ __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint3
 
 constexpr uint32_t kAccWaves = 8;                  // one wave per tile of a block
 constexpr uint32_t kAccThreads = 64 * kAccWaves;
+constexpr uint32_t kAccBlkHead = 512;              // escape bytes per peer fetched for a block before the barrier
 constexpr uint32_t kEscPad = 16;                   // decode_lane may read esc_lds[total]
 
 // What decode-accumulate needs of a peer's header for the workgroup's block, checked by
@@ -836,7 +837,8 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 {
     __shared__ uint32_t s_cnt[kPeers][kAccWaves];
     __shared__ PeerBlock s_peer[kPeers];
-    __shared__ uint8_t s_esc[kAccWaves][kTile + kEscPad];
+    __shared__ uint8_t s_blk[kPeers][kAccBlkHead + kEscPad];   // each peer's first escapes of the block
+    __shared__ uint8_t s_esc[kAccWaves][kTile + kEscPad];      // a tile's escapes when they lie further on
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t n = a.n, P = uint32_t(a.npeers);
@@ -866,18 +868,29 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
         }
     }
     // ---- this wave's share of the header checks: peers wave, wave + 8 ----
+    constexpr int kMine = (kPeers + kAccWaves - 1) / kAccWaves;   // peers checked per wave
+    uint32_t head[kMine][kAccBlkHead / 64];                       // their blocks' first escapes
+    uint32_t head_m[kMine];
 #pragma unroll
-    for (uint32_t p = wave; p < uint32_t(kPeers); p += kAccWaves) {
+    for (int i = 0; i < kMine; i++) {
+        const uint32_t p = wave + i * kAccWaves;
+        head_m[i] = 0;
         if (p < P) {
             const uint8_t* st = a.st[p];
             const SegHeader hd = read_header(st, n, a.esc_bytes[p]);
             const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
             uint32_t first = 0, last = 0;
             const bool ok = hd.ok && block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
-            if (lane == 0) {
-                const uint64_t e = hd.esc_offset + first;
-                s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, ok ? 1u : 0u};
-            }
+            const uint64_t e = hd.esc_offset + first;
+            if (lane == 0) s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, ok ? 1u : 0u};
+            // the block's first escapes, requested now so that they arrive while the
+            // tiles are transposed (written to LDS just before the barrier): lane l
+            // fetches bytes l, l + 64, ...
+            const uint32_t m = ok ? min(last - first, kAccBlkHead) : 0u;
+            head_m[i] = m;
+            const uint8_t* src = a.esc[p] + e;
+#pragma unroll
+            for (uint32_t k = 0; k < kAccBlkHead / 64; k++) head[i][k] = 64 * k + lane < m ? src[64 * k + lane] : 0u;
         }
     }
 
@@ -896,10 +909,17 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 #pragma unroll
         for (int p = 0; p < kPeers; p++) s_cnt[p][wave] = total[p];
     }
+#pragma unroll
+    for (int i = 0; i < kMine; i++) {
+        const uint32_t p = wave + i * kAccWaves;
+#pragma unroll
+        for (uint32_t k = 0; k < kAccBlkHead / 64; k++)
+            if (p < P && 64 * k + lane < head_m[i]) s_blk[p][64 * k + lane] = uint8_t(head[i][k]);
+    }
     __syncthreads();
 
-    // ---- every peer's first 64 escape bytes of this tile, requested together ----
-    uint32_t before[kPeers], mine[kPeers], ev[kPeers];
+    // ---- where each peer's escapes of this tile start within the block ----
+    uint32_t before[kPeers], mine[kPeers];
     bool bad = false;
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
@@ -908,7 +928,7 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     bad = __builtin_amdgcn_readfirstlane(bad);
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        before[p] = mine[p] = ev[p] = 0;
+        before[p] = mine[p] = 0;
         if (uint32_t(p) < P) {
             uint32_t bsum = 0, tot = 0;
 #pragma unroll
@@ -920,8 +940,6 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
             before[p] = bsum;
             mine[p] = total[p];
             bad = bad || tot != s_peer[p].count;   // the offset table must agree with the planes
-            const uint64_t e = uint64_t(s_peer[p].esc_hi) << 32 | s_peer[p].esc_lo;
-            if (!bad && lane < mine[p]) ev[p] = a.esc[p][e + bsum + lane];
         }
     }
 
@@ -936,15 +954,17 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
         if (uint32_t(p) < P && !bad && has_tile) {
-            // stage this peer's tile escapes in the wave's LDS slot
-            if (lane < mine[p]) esc_lds[lane] = uint8_t(ev[p]);
-            if (mine[p] > 64) {   // more than 64 escapes in one tile (escape-heavy tables)
+            const uint8_t* tile_esc = s_blk[p] + before[p];
+            if (before[p] + mine[p] > kAccBlkHead) {
+                // rare (escape-heavy tables): the tile's escapes go past the block's
+                // first 512; stage them in the wave's own LDS slot
                 const uint64_t e = uint64_t(s_peer[p].esc_hi) << 32 | s_peer[p].esc_lo;
                 const uint8_t* esc = a.esc[p] + e + before[p];
-                for (uint32_t k = 64 + lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
+                for (uint32_t k = lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
+                wave_lds_sync();
+                tile_esc = esc_lds;
             }
-            wave_lds_sync();
-            const LaneBytes o = decode_lane(rows[p], zf[p], Ap[p], s_peer[p].tlo, s_peer[p].thi, rank[p], esc_lds);
+            const LaneBytes o = decode_lane(rows[p], zf[p], Ap[p], s_peer[p].tlo, s_peer[p].thi, rank[p], tile_esc);
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
