@@ -107,9 +107,9 @@ uint64_t zipccl_static_size(uint64_t n);
 uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc);
 
 /* Device workspace bytes needed by zipccl_compress for up to nseg segments holding
- * at most total_n values (about one byte per value: a 4-byte escape count and a
- * 2048-byte escape staging slot per 2048-value half block, eight per 16384 values).  The workspace carries nothing
- * from one call to the next and needs no initialisation; it must be 256-byte aligned.
+ * at most total_n values (about one byte per value: a 4-byte escape count per 2048-value
+ * half block and a 16384-byte escape staging area per 16384 values).  The workspace
+ * carries nothing from one call to the next and needs no initialisation; it must be 256-byte aligned.
  * Calls that run concurrently need separate workspaces. */
 uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
 
@@ -122,8 +122,9 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
  *               headers still carry the true counts.
  *   workspace   device scratch, see zipccl_workspace_size.
  * The work is two kernel launches on `stream`: the encode kernel writes the fixed-size
- * sections and stages each block's escapes; the finalize kernel computes the escape
- * positions, writes the offset tables and headers and compacts the escapes.
+ * sections and stages each unit's escapes; the place kernel computes the escape
+ * positions, writes the offset tables and headers and compacts the escapes (above 2^28
+ * values in one call a one-workgroup scan launch computes the positions first).
  *   n_esc_out   optional device u64[nseg + 1]: per-segment escape counts, then the total.
  *   status      optional device u32, bits OR-ed in.
  * Errors: INVALID (NULL pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS, bad table),

@@ -8,21 +8,28 @@
 // The byte layout (format version 1) is documented in include/zipccl.h.
 //
 // Work decomposition.  A tile is 512 values: lane l of a wave holds values 8l..8l+7,
-// one 16-byte load.  A block is 8 tiles (4096 values, one escape-offset entry).
-//   * Planes.  A lane looks up, per value, its code with bit p moved to bit 8p (plus
-//     an escape flag in bit 24) and ORs the 8 entries, shifted by their column, into
-//     one 32-bit row.  A 32x32 bit transpose inside each half-wave (5 stages of
-//     ds_swizzle + v_alignbit + v_bfi) turns the rows of 32 lanes into 24 plane dwords:
-//     lane c of half h then holds bits 32h..32h+31 of plane word c.  The decoders run
-//     the same transpose on the loaded plane dwords to get each lane's row back.
-//   * Escapes.  Per-lane escape counts; ballots of their bits and mbcnt give each lane
-//     the escapes of the lower lanes; the lane's own escapes follow in column order.
-//   * Compress is three launches, none of which waits on another workgroup: encode
-//     (one half block per wave: A bytes, planes, escape count, escapes staged in the
-//     workspace), scan (one workgroup: escape positions), place (one wave per block:
-//     offset table, compacted escapes, headers).  The workspace keeps no state.
-//   * Decompress and decode-accumulate: one workgroup per block, one wave per tile;
-//     one barrier shares the tiles' escape counts.
+// one 16-byte load.  A block is 8 tiles (4096 values, one escape-offset entry); a unit
+// is 4 blocks (one compress or decompress workgroup, one half block per wave).
+//   * Planes.  A lane looks up, per value, a one-byte code entry (3-bit code plus an
+//     escape flag) and ORs the 8 entries, the one of column j shifted by 4j, into one
+//     32-bit row.  A 32x32 bit transpose inside each half-wave (5 stages: a lane
+//     exchange by DPP or ds_swizzle, v_alignbit, v_bfi) turns the rows of 32 lanes into
+//     plane dwords, each lane holding one bit position of the rows.  The decoders load
+//     the plane dwords in an order chosen so that the same transpose (its own inverse)
+//     gives each lane a row with the codes of its columns b and b+4 in byte b.
+//   * Escapes.  A DPP prefix scan over the wave's per-lane escape counts gives each
+//     lane the position of its first escape; a lane's escapes follow in column order.
+//     Decoding replaces the code-0 byte of the v_perm table with the lane's first
+//     escape of each group of 4 columns, so only lanes with two escapes in one group
+//     patch bytes one by one.
+//   * Compress is two launches, neither of which waits on another workgroup: encode
+//     (A bytes, planes, escape counts; each unit's escapes staged contiguously in the
+//     workspace) and place (escape positions from the units' counts, compacted escapes,
+//     offset tables, headers); above 2^28 values a one-workgroup scan kernel computes
+//     the positions and a per-block place kernel follows.  The workspace keeps no state.
+//   * Decompress: one half block per wave, one barrier to share the escape count of
+//     the first half of each block.  Decode-accumulate: one workgroup per block, one
+//     wave per tile, all peers of a tile in one wave.
 #include "zipccl_internal.h"
 #include "zipccl.h"
 
@@ -130,13 +137,25 @@ __device__ inline Transpose32 transpose_consts(uint32_t lane)
     return c;
 }
 
-// One transpose stage: exchange with lane ^ sft (ds_swizzle bit mode within groups of
-// 32 lanes), rotate the partner's word, keep this lane's own columns.
+// The word of lane ^ sft.  xor 8, 2 and 1 stay inside a row of 16 lanes and are DPP
+// moves (row_ror:8, quad_perm [2,3,0,1], quad_perm [1,0,3,2]): a few cycles on the
+// VALU.  xor 16 and 4 go through ds_swizzle's bit mode (groups of 32 lanes).
+template <int sft>
+__device__ inline uint32_t partner(uint32_t x)
+{
+    if constexpr (sft == 8) return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x128, 0xF, 0xF, false));
+    else if constexpr (sft == 2) return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x4E, 0xF, 0xF, false));
+    else if constexpr (sft == 1) return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0xB1, 0xF, 0xF, false));
+    else return uint32_t(__builtin_amdgcn_ds_swizzle(int(x), 0x1F | (sft << 10)));
+}
+
+// One transpose stage: exchange with lane ^ sft, rotate the partner's word, keep this
+// lane's own columns.
 template <int k>
 __device__ inline uint32_t transpose_stage(uint32_t x, const Transpose32& c)
 {
     constexpr int sft = 16 >> k;
-    const uint32_t y = uint32_t(__builtin_amdgcn_ds_swizzle(int(x), 0x1F | (sft << 10)));
+    const uint32_t y = partner<sft>(x);
     const uint32_t t = __builtin_amdgcn_alignbit(y, y, c.rot[k]);
     return (x & c.keep[k]) | (t & ~c.keep[k]);
 }
