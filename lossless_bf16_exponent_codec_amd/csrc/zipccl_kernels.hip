@@ -869,31 +869,38 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     const uint32_t nvalid = (!has_tile || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
     const uint32_t pdw = decoder_plane_dword(lane);
 
-    // ---- requests: local values, and per peer the A bytes and one plane dword ----
-    uint4 lv = make_uint4(0, 0, 0, 0);
-    if (nvalid == 8) lv = load_nt(reinterpret_cast<const uint4*>(a.local + i0));
-    else if (nvalid > 0) lv = load_lane(a.local, t, lane, n);
-    uint2 Ap[kPeers];
+    // ---- requests ----
+    // Every lane issues the same vector loads, unconditionally (addresses of what does
+    // not exist are clamped into peer 0's static part, which is at least 896 bytes), so
+    // that the compiler can wait for exactly the loads each step needs: the transposes
+    // start once the plane dwords are in while the A bytes, the local values and the
+    // escape heads are still on their way.  Plane dwords first, then A bytes, then local.
+    const uint8_t* const safe = a.st[0];
+    const uint32_t tl = has_tile ? t : T - 1;   // T >= 1: a launch has at least one block
+    const uint32_t pdl = pdw == ~0u ? 0u : pdw;   // lanes with p = 3: any dword (bits unused)
     uint32_t pw[kPeers];
+    uint2 Ap[kPeers];
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        Ap[p] = make_uint2(0, 0);
-        pw[p] = 0;
-        // A and plane addresses follow from n alone
-        if (uint32_t(p) < P && has_tile) {
-            const uint8_t* st = a.st[p];
-            Ap[p] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane));
-            if (pdw != ~0u) pw[p] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t) + pdw);
-        }
+        const uint8_t* st = a.st[uint32_t(p) < P ? p : 0];
+        pw[p] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * tl) + pdl);
     }
+#pragma unroll
+    for (int p = 0; p < kPeers; p++) {
+        const uint8_t* st = a.st[uint32_t(p) < P ? p : 0];
+        Ap[p] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * tl + 8 * lane));
+    }
+    uint4 lv = load_nt(reinterpret_cast<const uint4*>(nvalid == 8 ? reinterpret_cast<const uint8_t*>(a.local + i0)
+                                                                    : safe));
+
     // ---- this wave's share of the header checks: peers wave, wave + 8 ----
     constexpr int kMine = (kPeers + kAccWaves - 1) / kAccWaves;   // peers checked per wave
     uint32_t head[kMine][kAccBlkHead / 64];                       // their blocks' first escapes
-    uint32_t head_m[kMine];
 #pragma unroll
     for (int i = 0; i < kMine; i++) {
         const uint32_t p = wave + i * kAccWaves;
-        head_m[i] = 0;
+        const uint8_t* src = safe;   // with m = 0 every lane reads byte 0 of it
+        uint32_t m = 0;
         if (p < P) {
             const uint8_t* st = a.st[p];
             const SegHeader hd = read_header(st, n, a.esc_bytes[p]);
@@ -902,25 +909,28 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
             const bool ok = hd.ok && block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
             const uint64_t e = hd.esc_offset + first;
             if (lane == 0) s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, ok ? 1u : 0u};
-            // the block's first escapes, requested now so that they arrive while the
-            // tiles are transposed (written to LDS just before the barrier): lane l
-            // fetches bytes l, l + 64, ...
-            const uint32_t m = ok ? min(last - first, kAccBlkHead) : 0u;
-            head_m[i] = m;
-            const uint8_t* src = a.esc[p] + e;
-#pragma unroll
-            for (uint32_t k = 0; k < kAccBlkHead / 64; k++) head[i][k] = 64 * k + lane < m ? src[64 * k + lane] : 0u;
+            m = ok ? min(last - first, kAccBlkHead) : 0u;
+            if (m > 0) src = a.esc[p] + e;
         }
+        // the block's first escapes, requested now so that they arrive while the tiles
+        // are transposed (written to LDS just before the barrier): lane l fetches bytes
+        // l, l + 64, ... (indexes past m re-read byte m - 1)
+        const uint32_t last_i = m > 0 ? m - 1 : 0u;
+#pragma unroll
+        for (uint32_t k = 0; k < kAccBlkHead / 64; k++) head[i][k] = src[min(64 * k + lane, last_i)];
     }
 
     // ---- per peer: plane rows, escape flags, escape ranks within the tile ----
     const Transpose32 tc = transpose_consts(lane);
-    const uint32_t vf = valid_flags(nvalid);
+    const uint32_t vf = valid_flags(nvalid);   // 0 in a wave without a tile
     uint32_t rows[kPeers], zf[kPeers], cnt[kPeers], rank[kPeers], total[kPeers];
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        rows[p] = uint32_t(p) < P ? transpose32(pw[p], tc) : 0u;
-        zf[p] = uint32_t(p) < P ? escape_flags(rows[p], vf) : 0u;
+        rows[p] = zf[p] = 0;
+        if (uint32_t(p) < P) {
+            rows[p] = transpose32(pw[p], tc);
+            zf[p] = escape_flags(rows[p], vf);
+        }
         cnt[p] = __builtin_popcount(zf[p]);
     }
     wave_ranks<kPeers>(cnt, rank, total, P);
@@ -931,36 +941,42 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 #pragma unroll
     for (int i = 0; i < kMine; i++) {
         const uint32_t p = wave + i * kAccWaves;
+        if (p < P) {
 #pragma unroll
-        for (uint32_t k = 0; k < kAccBlkHead / 64; k++)
-            if (p < P && 64 * k + lane < head_m[i]) s_blk[p][64 * k + lane] = uint8_t(head[i][k]);
+            for (uint32_t k = 0; k < kAccBlkHead / 64; k++) s_blk[p][64 * k + lane] = uint8_t(head[i][k]);
+        }
     }
     __syncthreads();
 
     // ---- where each peer's escapes of this tile start within the block ----
+    // Lane 8p + w reads tile w's count of peer p; one prefix sum over the wave then
+    // gives every peer's count before this wave's tile and its block total by readlane.
+    static_assert(kAccWaves == 8, "one lane per (peer, tile) pair in groups of 8");
     uint32_t before[kPeers], mine[kPeers];
     bool bad = false;
 #pragma unroll
-    for (int p = 0; p < kPeers; p++) {
-        if (uint32_t(p) < P) bad = bad || !s_peer[p].ok;
-    }
-    bad = __builtin_amdgcn_readfirstlane(bad);
+    for (int h = 0; h < (kPeers * kAccWaves + 63) / 64; h++) {
+        const uint32_t idx = 64 * h + lane;
+        const uint32_t v = idx < uint32_t(kPeers * kAccWaves) ? (&s_cnt[0][0])[idx] : 0u;
+        const uint32_t incl = wave_scan_incl(v), excl = incl - v;
 #pragma unroll
-    for (int p = 0; p < kPeers; p++) {
-        before[p] = mine[p] = 0;
-        if (uint32_t(p) < P) {
-            uint32_t bsum = 0, tot = 0;
-#pragma unroll
-            for (uint32_t w = 0; w < kAccWaves; w++) {
-                const uint32_t v = s_cnt[p][w];
-                if (w < wave) bsum += v;
-                tot += v;
+        for (int q = 0; q < 8 && 8 * h + q < kPeers; q++) {
+            const int p = 8 * h + q;
+            before[p] = mine[p] = 0;
+            if (uint32_t(p) < P) {
+                const uint32_t base = uint32_t(__builtin_amdgcn_readlane(int(excl), 8 * q));
+                const uint32_t next = q < 7 ? uint32_t(__builtin_amdgcn_readlane(int(excl), 8 * q + 8))
+                                            : uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+                before[p] = uint32_t(__builtin_amdgcn_readlane(int(excl), int(8 * q + wave))) - base;
+                mine[p] = total[p];
+                // the offset table must agree with the planes
+                bad = bad || !s_peer[p].ok || next - base != s_peer[p].count;
             }
-            before[p] = bsum;
-            mine[p] = total[p];
-            bad = bad || tot != s_peer[p].count;   // the offset table must agree with the planes
         }
     }
+    bad = __builtin_amdgcn_readfirstlane(bad);
+    // a lane holding the last values of the segment (fewer than 8) reads them now
+    if (nvalid > 0 && nvalid < 8) lv = load_lane(a.local, t, lane, n);
 
     // ---- decode and add, peers in order ----
     float acc[8];
@@ -1142,7 +1158,11 @@ hipError_t launch_accumulate(const AArgs& a, hipStream_t s)
 {
     const uint32_t grid = uint32_t(blocks_of(a.n));
     if (grid == 0) return hipSuccess;
-    if (a.npeers <= 8) hipLaunchKernelGGL(accumulate_kernel<8>, dim3(grid), dim3(kAccThreads), 0, s, a);
+    // every peer slot of the instance issues its loads, so the instance is the smallest
+    // that holds npeers
+    if (a.npeers <= 2) hipLaunchKernelGGL(accumulate_kernel<2>, dim3(grid), dim3(kAccThreads), 0, s, a);
+    else if (a.npeers <= 4) hipLaunchKernelGGL(accumulate_kernel<4>, dim3(grid), dim3(kAccThreads), 0, s, a);
+    else if (a.npeers <= 8) hipLaunchKernelGGL(accumulate_kernel<8>, dim3(grid), dim3(kAccThreads), 0, s, a);
     else hipLaunchKernelGGL(accumulate_kernel<kMaxPeers>, dim3(grid), dim3(kAccThreads), 0, s, a);
     return hipGetLastError();
 }

@@ -277,9 +277,10 @@ class Pipeline:
         _check(rc, "zipccl_pipeline_reduce")
 
     def close(self):
-        if getattr(self, "_h", None):
+        # at interpreter exit the module globals may already be gone
+        if getattr(self, "_h", None) and _lib is not None:
             _lib.zipccl_pipeline_destroy(self._h)
-            self._h = None
+        self._h = None
 
     def __del__(self):
         self.close()
