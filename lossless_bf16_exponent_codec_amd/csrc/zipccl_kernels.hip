@@ -297,6 +297,7 @@ __device__ inline void stage_tile_escapes(const TileEsc& te, uint32_t r, uint8_t
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
 // planes, the escape count (to workspace slot gh) and the escape exponents in value
 // order in s_esc; zero padding after the segment's last half block.
+template <bool kFull>
 __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
                                        uint32_t lane, const uint8_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
@@ -308,7 +309,7 @@ __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t 
     const uint32_t bdw = encoder_plane_dword(lane);
     const uint32_t t0 = hb * 4;
     TileEsc te[4];
-    if (uint64_t(t0 + 4) * kTile <= n) {
+    if constexpr (kFull) {   // all 2048 values exist
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const uint32_t t = t0 + k;
@@ -363,17 +364,15 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     const uint32_t hb = (unit - sg.unit0) * kEncWaves + wave;   // half block within the segment
     const bool active = hb < 2 * blocks_of(n);
 
-    uint4 v[4];   // every load of the half block first (values past n read as 0)
-    if (active) {
-        const uint32_t t0 = hb * 4;
-        const uint16_t* src = sg.src + uint64_t(t0) * kTile + 8 * lane;
-        if (uint64_t(t0 + 4) * kTile <= n) {
+    // Every load of the half block first.  A half block with all 2048 values loads in
+    // straight-line code, so each tile waits only for its own load; the segment's last,
+    // partial half block loads after the barrier (values past n read as 0).
+    const bool full = active && uint64_t(hb + 1) * kHalf <= n;
+    const uint16_t* src = sg.src + uint64_t(hb) * kHalf + 8 * lane;
+    uint4 v[4];
+    if (full) {
 #pragma unroll
-            for (int k = 0; k < 4; k++) v[k] = load_nt(reinterpret_cast<const uint4*>(src + k * kTile));
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, t0 + k, lane, n);
-        }
+        for (int k = 0; k < 4; k++) v[k] = load_nt(reinterpret_cast<const uint4*>(src + k * kTile));
     }
     __shared__ uint32_t s_hcnt[kEncWaves];
     if (tid < 256) {   // exponent -> code entry of this segment
@@ -389,8 +388,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     __syncthreads();
     uint32_t run = 0;
     const uint32_t slot = unit * kEncWaves + wave;
-    if (active) run = encode_half(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
-    else if (lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
+    if (full) {
+        run = encode_half<true>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
+    } else if (active) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, hb * 4 + k, lane, n);
+        run = encode_half<false>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
+    }
     if (lane == 0) s_hcnt[wave] = run;
     __syncthreads();
     uint32_t before = 0, total = 0;
@@ -406,6 +410,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     uint8_t* stage = a.stage + uint64_t(unit) * kUnit + before;
     const uint8_t* esc_lds = s_esc[wave];
     for (uint32_t k = lane; k < run; k += 64) stage[k] = esc_lds[k];
+    if (!active && lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
 }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
@@ -1053,28 +1058,29 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
     const uint32_t pdw = decoder_plane_dword(lane);
     const uint8_t* st = sg.src;
 
-    bool bad = false;
-    uint32_t first = 0, last = 0;
-    SegHeader hd = {};
+    // A and plane addresses follow from n alone, so these loads are issued before (and
+    // independently of) the header checks; escapes are read only once the header and
+    // offset table have been validated.  Every wave issues the same loads, plane dwords
+    // first, in straight-line code (tiles past the segment's last re-read it, lanes with
+    // no plane dword read dword 0), so each transpose waits only for its own dword.
+    const uint32_t T1 = T - 1;   // n >= 1: a segment with no values has no units
+    const uint32_t pdl = pdw == ~0u ? 0u : pdw;
     uint2 Ap[kDecHalfTiles];
     uint32_t pw[kDecHalfTiles];
 #pragma unroll
     for (int k = 0; k < int(kDecHalfTiles); k++) {
-        Ap[k] = make_uint2(0, 0);
-        pw[k] = 0;
+        const uint32_t t = min(hb * kDecHalfTiles + k, T1);
+        pw[k] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t) + pdl);
     }
-    if (active) {
-        // A and plane addresses follow from n alone, so these loads are issued before
-        // (and independently of) the header checks; escapes are read only once the
-        // header and offset table have been validated
 #pragma unroll
-        for (int k = 0; k < int(kDecHalfTiles); k++) {
-            const uint32_t t = hb * kDecHalfTiles + k;
-            if (t < T) {
-                Ap[k] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane));
-                if (pdw != ~0u) pw[k] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t) + pdw);
-            }
-        }
+    for (int k = 0; k < int(kDecHalfTiles); k++) {
+        const uint32_t t = min(hb * kDecHalfTiles + k, T1);
+        Ap[k] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * t + 8 * lane));
+    }
+    bool bad = false;
+    uint32_t first = 0, last = 0;
+    SegHeader hd = {};
+    if (active) {
         hd = read_header(st, n, a.esc_bytes);
         const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
         bad = !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
