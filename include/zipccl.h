@@ -158,12 +158,16 @@ zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const v
                                            const uint64_t* esc_bytes, int npeers, uint64_t n,
                                            const void* local, void* dst, uint32_t* status, void* stream);
 
-/* Chunked two-stream pipeline over a reduce-scatter receive share.  Chunks of `chunk`
- * values of every peer shard are compressed on stream_a (one compress call per chunk,
- * one segment per peer) and decoded + accumulated into dst on stream_b (one launch per
- * chunk); a ring of two compressed-chunk buffers lets chunk c+1 compress while chunk c
- * is reduced.  The scratch memory is caller-owned device memory of
- * zipccl_pipeline_scratch_size() bytes.
+/* Chunked two-stream pipeline over a reduce-scatter receive share (S2.D; the chunked
+ * multi-stream overlap of the CCCL page's pipeline section).  Chunks of `chunk` values
+ * of every peer shard are compressed on stream_a (one compress call per chunk, one
+ * segment per peer) and decoded + accumulated into dst on stream_b (one launch per
+ * chunk).  The streams hand chunks over in groups of G (a power of two, at most 16, the
+ * smallest with G * npeers * chunk >= 2^25 values, since each event record or wait costs
+ * the host microseconds); a ring of two groups of chunk buffers lets group g + 1
+ * compress while group g is reduced.  The scratch memory is caller-owned device memory
+ * of zipccl_pipeline_scratch_size() bytes: the compress workspace plus 2 * G chunk
+ * buffers of npeers * (static_size(chunk) + chunk) bytes.
  * Overlapping transfers of the compressed chunks would sit between the two streams. */
 typedef struct zipccl_pipeline zipccl_pipeline;
 

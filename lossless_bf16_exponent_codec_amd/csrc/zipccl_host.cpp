@@ -224,15 +224,29 @@ zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const v
 struct zipccl_pipeline {
     int npeers;
     uint64_t chunk;
+    uint32_t group;            // chunks per hand-off between the streams
     uint8_t* scratch;
-    uint64_t slot_static, slot_esc, ws_size;   // bytes per ring slot and of the workspace
+    uint64_t slot_static, slot_esc, ws_size;   // bytes per chunk slot and of the workspace
     hipStream_t sa, sb;
-    hipEvent_t compressed[2], reduced[2];
+    hipEvent_t compressed[2], reduced[2];      // one per half of the ring
     bool reduced_recorded[2];
 };
 
 namespace {
 
+// Chunks per hand-off: an event record or wait costs the host a few microseconds, about
+// what the codec needs for one chunk of a few million values, so the streams hand over
+// groups of chunks holding at least 2^25 values (still one compress call and one
+// decode-accumulate launch per chunk).
+uint32_t pipeline_group(int npeers, uint64_t chunk)
+{
+    uint32_t g = 1;
+    while (g < 16 && uint64_t(g) * uint64_t(npeers) * chunk < (1ull << 25)) g *= 2;
+    return g;
+}
+
+// Scratch layout: the compress workspace, then 2 * group chunk slots (a ring of two
+// groups), each holding the chunk's npeers static parts and room for all its escapes.
 void pipeline_layout(int npeers, uint64_t chunk, uint64_t& slot_static, uint64_t& slot_esc, uint64_t& ws)
 {
     slot_static = uint64_t(npeers) * static_bytes_of(chunk);
@@ -247,7 +261,7 @@ uint64_t zipccl_pipeline_scratch_size(int npeers, uint64_t chunk)
     if (npeers < 1 || npeers > kMaxPeers || chunk == 0) return 0;
     uint64_t ss, se, ws;
     pipeline_layout(npeers, chunk, ss, se, ws);
-    return ws + 2 * (ss + se);
+    return ws + 2ull * pipeline_group(npeers, chunk) * (ss + se);
 }
 
 zipccl_status zipccl_pipeline_create(int npeers, uint64_t chunk, void* scratch, uint64_t scratch_bytes,
@@ -264,6 +278,7 @@ zipccl_status zipccl_pipeline_create(int npeers, uint64_t chunk, void* scratch, 
     p->chunk = chunk;
     p->scratch = static_cast<uint8_t*>(scratch);
     pipeline_layout(npeers, chunk, p->slot_static, p->slot_esc, p->ws_size);
+    p->group = pipeline_group(npeers, chunk);
     p->sa = static_cast<hipStream_t>(stream_a);
     p->sb = static_cast<hipStream_t>(stream_b);
     for (int k = 0; k < 2; k++) {
@@ -294,38 +309,52 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
     }
     uint8_t* ws = pipe->scratch;
     const uint64_t nchunks = (n + pipe->chunk - 1) / pipe->chunk;
-    for (uint64_t c = 0; c < nchunks; c++) {
-        const int slot = int(c & 1);
-        const uint64_t off = c * pipe->chunk;
-        const uint64_t m = std::min(pipe->chunk, n - off);
-        uint8_t* st = pipe->scratch + pipe->ws_size + uint64_t(slot) * (pipe->slot_static + pipe->slot_esc);
-        uint8_t* esc = st + pipe->slot_static;
-        if (pipe->reduced_recorded[slot] && hipStreamWaitEvent(pipe->sa, pipe->reduced[slot], 0) != hipSuccess)
+    const uint64_t G = pipe->group;
+    for (uint64_t c0 = 0; c0 < nchunks; c0 += G) {
+        const int half = int((c0 / G) & 1);   // which half of the ring this group uses
+        const uint64_t c1 = std::min(nchunks, c0 + G);
+        // the group two hand-offs back used these slots: its reduction must be done
+        if (pipe->reduced_recorded[half] && hipStreamWaitEvent(pipe->sa, pipe->reduced[half], 0) != hipSuccess)
             return ZIPCCL_ERR_HIP;
-        zipccl_segment_t segs[kMaxPeers];
-        for (int p = 0; p < P; p++) {
-            segs[p].src = static_cast<const uint16_t*>(peer_src[p]) + off;
-            segs[p].n = m;
-            segs[p].plan = plans[p];
+        for (int pass = 0; pass < 2; pass++) {   // 0: compress the group on a, 1: reduce it on b
+            for (uint64_t c = c0; c < c1; c++) {
+                const uint64_t off = c * pipe->chunk;
+                const uint64_t m = std::min(pipe->chunk, n - off);
+                uint8_t* st = pipe->scratch + pipe->ws_size +
+                              (uint64_t(half) * G + (c - c0)) * (pipe->slot_static + pipe->slot_esc);
+                uint8_t* esc = st + pipe->slot_static;
+                zipccl_status r;
+                if (pass == 0) {
+                    zipccl_segment_t segs[kMaxPeers];
+                    for (int p = 0; p < P; p++) {
+                        segs[p].src = static_cast<const uint16_t*>(peer_src[p]) + off;
+                        segs[p].n = m;
+                        segs[p].plan = plans[p];
+                    }
+                    r = zipccl_compress(segs, P, st, pipe->slot_static, esc, pipe->slot_esc, ws, pipe->ws_size,
+                                        nullptr, status, pipe->sa);
+                } else {
+                    const void* sin[kMaxPeers];
+                    const void* ein[kMaxPeers];
+                    uint64_t eb[kMaxPeers];
+                    for (int p = 0; p < P; p++) {
+                        sin[p] = st + uint64_t(p) * static_bytes_of(m);
+                        ein[p] = esc;
+                        eb[p] = pipe->slot_esc;
+                    }
+                    r = zipccl_decompress_accumulate(sin, ein, eb, P, m, static_cast<const uint16_t*>(local) + off,
+                                                     static_cast<uint16_t*>(dst) + off, status, pipe->sb);
+                }
+                if (r != ZIPCCL_OK) return r;
+            }
+            if (pass == 0) {
+                if (hipEventRecord(pipe->compressed[half], pipe->sa) != hipSuccess ||
+                    hipStreamWaitEvent(pipe->sb, pipe->compressed[half], 0) != hipSuccess)
+                    return ZIPCCL_ERR_HIP;
+            }
         }
-        zipccl_status r = zipccl_compress(segs, P, st, pipe->slot_static, esc, pipe->slot_esc, ws, pipe->ws_size,
-                                          nullptr, status, pipe->sa);
-        if (r != ZIPCCL_OK) return r;
-        if (hipEventRecord(pipe->compressed[slot], pipe->sa) != hipSuccess) return ZIPCCL_ERR_HIP;
-        if (hipStreamWaitEvent(pipe->sb, pipe->compressed[slot], 0) != hipSuccess) return ZIPCCL_ERR_HIP;
-        const void* sin[kMaxPeers];
-        const void* ein[kMaxPeers];
-        uint64_t eb[kMaxPeers];
-        for (int p = 0; p < P; p++) {
-            sin[p] = st + uint64_t(p) * static_bytes_of(m);
-            ein[p] = esc;
-            eb[p] = pipe->slot_esc;
-        }
-        r = zipccl_decompress_accumulate(sin, ein, eb, P, m, static_cast<const uint16_t*>(local) + off,
-                                         static_cast<uint16_t*>(dst) + off, status, pipe->sb);
-        if (r != ZIPCCL_OK) return r;
-        if (hipEventRecord(pipe->reduced[slot], pipe->sb) != hipSuccess) return ZIPCCL_ERR_HIP;
-        pipe->reduced_recorded[slot] = true;
+        if (hipEventRecord(pipe->reduced[half], pipe->sb) != hipSuccess) return ZIPCCL_ERR_HIP;
+        pipe->reduced_recorded[half] = true;
     }
     return ZIPCCL_OK;
 }

@@ -315,6 +315,32 @@ def test_accumulate_corrupt_peer(Z):
     assert int(status.item()) & Z.STATUS_CORRUPT
 
 
+@pytest.mark.parametrize("npeers,chunk,n", [(2, 4096, 40 * 4096 + 100),   # 3 hand-offs of 16 chunks: the ring wraps
+                                             (3, 8192, 5 * 8192),          # fewer chunks than one hand-off
+                                             (16, 1 << 20, (2 << 20) + 4097)])   # hand-offs of 2, ragged last chunk
+def test_pipeline_matches_oracle(Z, npeers, chunk, n):
+    print(f"pipeline P={npeers} chunk={chunk} n={n}", flush=True)
+    peers = [W.gaussian_bf16(n, 1e-3, 700 + p) for p in range(npeers)]
+    local = W.gaussian_bf16(n, 1e-3, 800)
+    plans = [Z.plan(sigma=1e-3)] * npeers
+    want = oracle_accumulate(Z, peers, plans, local)
+    peer_t = [dev_bf16(p) for p in peers]
+    local_t = dev_bf16(local)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    pipe = Z.Pipeline(npeers, chunk, sa, sb)
+    for _ in range(2):   # the second call reuses the first call's events and slots
+        dst = torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        sb.wait_stream(torch.cuda.current_stream())
+        pipe.reduce(peer_t, plans, local_t, dst, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        got = host_u16(dst)
+        assert np.array_equal(got, want), first_diff(got, want)
+    pipe.close()
+
+
 # ------------------------------------------------------------------------------------
 # the scan-kernel path for escape positions (used above 2^28 values per call), forced
 # on small inputs
