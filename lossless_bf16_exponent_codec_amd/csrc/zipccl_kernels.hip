@@ -143,9 +143,9 @@ __device__ inline Transpose32 transpose_consts(uint32_t lane)
 template <int sft>
 __device__ inline uint32_t partner(uint32_t x)
 {
-    if constexpr (sft == 8) return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x128, 0xF, 0xF, false));
-    else if constexpr (sft == 2) return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x4E, 0xF, 0xF, false));
-    else if constexpr (sft == 1) return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0xB1, 0xF, 0xF, false));
+    if constexpr (sft == 8) return uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x128, 0xF, 0xF, true));
+    else if constexpr (sft == 2) return uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x4E, 0xF, 0xF, true));
+    else if constexpr (sft == 1) return uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0xB1, 0xF, 0xF, true));
     else return uint32_t(__builtin_amdgcn_ds_swizzle(int(x), 0x1F | (sft << 10)));
 }
 
