@@ -21,8 +21,9 @@ Printed (one JSON line on stdout):
              kernel sources); roofline_other_op for the other operation;
   cpu_baseline  the plain C oracle, single-threaded, on the same bucket;
   per_config the other workloads (1 Mi chunk, activations with escapes and specials,
-             MoE dispatch buckets, reduce-scatter share with decode-accumulate and the
-             two-stream pipeline), each with compress / decompress GB/s and HBM fraction.
+             MoE dispatch buckets, the all-gather receive side decoding 16 separately
+             compressed shards in one launch, reduce-scatter share with decode-accumulate
+             and the two-stream pipeline), each with GB/s and HBM fraction.
 """
 from __future__ import annotations
 
@@ -275,6 +276,41 @@ def bench_rs(torch, Z, W, iters):
         "ratio": round(2 * P * n / (static_total + total_esc), 5),
         "escape_frac": round(total_esc / (P * n), 5),
         "status_ok": ok,
+    }
+
+
+def bench_allgather(torch, Z, W, rounds):
+    """All-gather receive side: the bucket's 16 layers as 16 ranks' shards, each
+    compressed by its own call into its own buffers, all decoded by one
+    zipccl_decompress_shards launch into the gathered 64 Mi tensor.  Two rotating sets
+    (> 2 x 256 MB together) keep the inputs out of the Infinity Cache."""
+    wl = W.bucket_64m()
+    plans = [Z.plan(sigma=s) for s in wl.sigmas]
+    sizes = [s.size for s in wl.segments]
+    n = sum(sizes)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sets = []
+    n_esc = 0
+    for k in range(2):
+        comp = [Z.compress_tensors([to_dev(torch, seg)], [pl]) for seg, pl in zip(wl.segments, plans)]
+        torch.cuda.synchronize()
+        if k == 0:
+            n_esc = sum(int(c.n_esc[-1].item()) for c in comp)
+        out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        call = Z.PreparedDecompressShards([c.static for c in comp], [c.esc for c in comp],
+                                          list(torch.split(out, sizes)), status)
+        sets.append(dict(out=out, call=call))
+    d = batched_ms(torch, lambda k: sets[k % 2]["call"].run(), 2, rounds)
+    want = torch.cat([to_dev(torch, seg) for seg in wl.segments])
+    ok = int(status.item()) == 0
+    ok = ok and all(bool(torch.equal(s["out"].view(torch.int16), want.view(torch.int16))) for s in sets)
+    moved = sum(Z.static_size(m) for m in sizes) + n_esc + 2 * n
+    return {
+        "elements": n, "shards": len(sizes),
+        "decompress_us": round(d * 1e3, 2),
+        "decompress_GBps": round(2 * n / (d * 1e-3) / 1e9, 1),
+        "decompress_hbm_frac": round(moved / (d * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "parity_round_trip": ok,
     }
 
 
@@ -535,6 +571,9 @@ def main(argv=None) -> int:
             per[name] = r2
             del b2
             torch.cuda.empty_cache()
+        log("workload allgather_16x4m")
+        per["allgather_16x4m"] = bench_allgather(torch, Z, W, 5)
+        torch.cuda.empty_cache()
         log("workload rs_512m")
         per["rs_512m"] = bench_rs(torch, Z, W, 5)
         out["per_config"] = per

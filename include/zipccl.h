@@ -10,7 +10,8 @@
  *         a table exponent becomes a 3-bit code 001..111, any other exponent the
  *         escape code 000 with the full exponent appended to a separate array;
  *   S2.C  sections padded to 128 bytes; the 3-bit codes stored as three 1-bit planes;
- *   S2.D  the reduce-scatter receive side decodes and reduces locally.
+ *   S2.D  the reduce-scatter receive side decodes and reduces locally;
+ *   S4    the all-gather measured there: one compressed shard per rank, decoded by all.
  *
  * Compressed format, version 1 (all integers little-endian).  One segment of n values,
  * T = ceil(n/512) tiles, K = ceil(n/4096) blocks, R128 = round up to 128:
@@ -144,6 +145,21 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
 zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, const void* esc_in,
                                 uint64_t esc_bytes, const zipccl_dsegment_t* segs, int nseg,
                                 uint32_t* status, void* stream);
+
+/* All-gather receive side (the all-gather measurement of S4; each rank's shard is
+ * compressed once and every receiver decodes all of them): decodes nseg one-segment
+ * compressed shards that lie in separate buffers, in one launch, to segs[s].dst (the
+ * slices of the gathered tensor).  static_in, esc_in and esc_bytes are host arrays of
+ * nseg entries: static_in[s] is the shard's static part (device, 128-byte aligned,
+ * static_size(segs[s].n) bytes as zipccl_compress wrote it) and esc_in[s] (esc_bytes[s]
+ * long, NULL when 0) the escape buffer its header's esc_offset refers to.  A shard whose
+ * header or offset table is inconsistent with segs[s].n or esc_bytes[s] is not decoded
+ * and ZIPCCL_STATUS_CORRUPT is set; no read leaves the given buffers.
+ * Errors: INVALID (NULL arrays or pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS), ALIGN,
+ * SIZE (a segment n >= 2^32), HIP. */
+zipccl_status zipccl_decompress_shards(const void* const* static_in, const void* const* esc_in,
+                                       const uint64_t* esc_bytes, const zipccl_dsegment_t* segs, int nseg,
+                                       uint32_t* status, void* stream);
 
 /* Reduce-scatter receive side (S2.D): for i < n
  *   dst[i] = bf16_rne( (((f32(local[i]) + f32(peer_0[i])) + f32(peer_1[i])) + ...) )

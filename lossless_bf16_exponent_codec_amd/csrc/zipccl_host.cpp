@@ -165,6 +165,7 @@ zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, co
 {
     if (!segs || nseg < 1 || nseg > kMaxSegs || !static_in) return ZIPCCL_ERR_INVALID;
     if (!aligned(static_in, 128) || (status && !aligned(status, 4))) return ZIPCCL_ERR_ALIGN;
+    if (esc_bytes > 0 && !esc_in) return ZIPCCL_ERR_INVALID;
     DArgs a;
     std::memset(&a, 0, sizeof(a));
     uint64_t units = 0, st_off = 0;
@@ -175,6 +176,9 @@ zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, co
         if (!aligned(g.dst, 16)) return ZIPCCL_ERR_ALIGN;
         DSeg& d = a.seg[s];
         d.src = static_cast<const uint8_t*>(static_in) + st_off;
+        // with no escape buffer no escape is ever read; any device address will do
+        d.esc = static_cast<const uint8_t*>(esc_in ? esc_in : static_in);
+        d.esc_bytes = esc_in ? esc_bytes : 0;
         d.dst = static_cast<uint16_t*>(g.dst);
         d.n = uint32_t(g.n);
         d.unit0 = uint32_t(units);
@@ -182,10 +186,35 @@ zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, co
         st_off += static_bytes_of(g.n);
     }
     if (st_off > static_bytes) return ZIPCCL_ERR_SIZE;
-    if (esc_bytes > 0 && !esc_in) return ZIPCCL_ERR_INVALID;
-    // with no escape buffer no escape is ever read; any device address will do
-    a.esc = static_cast<const uint8_t*>(esc_in ? esc_in : static_in);
-    a.esc_bytes = esc_in ? esc_bytes : 0;
+    a.status = status;
+    a.nseg = nseg;
+    a.total_units = uint32_t(units);
+    return hip_status(launch_decompress(a, static_cast<hipStream_t>(stream)));
+}
+
+zipccl_status zipccl_decompress_shards(const void* const* static_in, const void* const* esc_in,
+                                       const uint64_t* esc_bytes, const zipccl_dsegment_t* segs, int nseg,
+                                       uint32_t* status, void* stream)
+{
+    if (!segs || !static_in || !esc_in || !esc_bytes || nseg < 1 || nseg > kMaxSegs) return ZIPCCL_ERR_INVALID;
+    if (status && !aligned(status, 4)) return ZIPCCL_ERR_ALIGN;
+    DArgs a;
+    std::memset(&a, 0, sizeof(a));
+    uint64_t units = 0;
+    for (int s = 0; s < nseg; s++) {
+        const zipccl_dsegment_t& g = segs[s];
+        if (g.n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+        if (!static_in[s] || (g.n > 0 && !g.dst) || (esc_bytes[s] > 0 && !esc_in[s])) return ZIPCCL_ERR_INVALID;
+        if (!aligned(static_in[s], 128) || !aligned(g.dst, 16)) return ZIPCCL_ERR_ALIGN;
+        DSeg& d = a.seg[s];
+        d.src = static_cast<const uint8_t*>(static_in[s]);
+        d.esc = static_cast<const uint8_t*>(esc_in[s] ? esc_in[s] : static_in[s]);
+        d.esc_bytes = esc_in[s] ? esc_bytes[s] : 0;
+        d.dst = static_cast<uint16_t*>(g.dst);
+        d.n = uint32_t(g.n);
+        d.unit0 = uint32_t(units);
+        units += units_of(g.n);
+    }
     a.status = status;
     a.nseg = nseg;
     a.total_units = uint32_t(units);

@@ -67,6 +67,8 @@ struct CArgs {
 
 struct DSeg {              // decompress: one segment
     const uint8_t* src;    // static part
+    const uint8_t* esc;    // escape buffer the header's esc_offset refers to
+    uint64_t esc_bytes;
     uint16_t* dst;
     uint32_t n;
     uint32_t unit0;        // first workgroup unit of the segment (units of kUnit values)
@@ -74,8 +76,6 @@ struct DSeg {              // decompress: one segment
 
 struct DArgs {
     DSeg seg[kMaxSegs];
-    const uint8_t* esc;
-    uint64_t esc_bytes;
     uint32_t* status;
     int32_t nseg;
     uint32_t total_units;

@@ -1081,7 +1081,7 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
     uint32_t first = 0, last = 0;
     SegHeader hd = {};
     if (active) {
-        hd = read_header(st, n, a.esc_bytes);
+        hd = read_header(st, n, sg.esc_bytes);
         const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
         bad = !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
     }
@@ -1112,7 +1112,7 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
         return;
     }
     // every lane of the wave helps stage the half block's escapes
-    const uint8_t* esc = a.esc + hd.esc_offset + first + half_start;
+    const uint8_t* esc = sg.esc + hd.esc_offset + first + half_start;
     uint8_t* esc_lds = s_esc[wave];
     for (uint32_t k = lane; k < half_total; k += 64) esc_lds[k] = esc[k];
     wave_lds_sync();

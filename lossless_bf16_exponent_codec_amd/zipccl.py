@@ -68,6 +68,9 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_compress.argtypes = [ctypes.POINTER(SegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp, vp]
     lib.zipccl_decompress.restype = i32
     lib.zipccl_decompress.argtypes = [vp, u64, vp, u64, ctypes.POINTER(DSegmentT), i32, vp, vp]
+    lib.zipccl_decompress_shards.restype = i32
+    lib.zipccl_decompress_shards.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64),
+                                             ctypes.POINTER(DSegmentT), i32, vp, vp]
     lib.zipccl_decompress_accumulate.restype = i32
     lib.zipccl_decompress_accumulate.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64), i32,
                                                  u64, vp, vp, vp, vp]
@@ -177,6 +180,34 @@ def decompress(static_in, esc_in, dsts, status=None, stream=None, static_bytes=N
     eb = (_nbytes(esc_in) if esc_in is not None else 0) if esc_bytes is None else esc_bytes
     rc = _lib.zipccl_decompress(_ptr(static_in), sb, _ptr(esc_in), eb, arr, nseg, _ptr(status), _stream(stream))
     _check(rc, "zipccl_decompress")
+
+
+def decompress_shards(static_ins, esc_ins, dsts, status=None, stream=None, esc_bytes=None):
+    """zipccl_decompress_shards.  static_ins / esc_ins: per-shard device tensors or raw
+    device addresses (int; an escape entry may be None); dsts: bf16 device tensors, one
+    per shard (their numel is n); esc_bytes: per-shard escape buffer sizes."""
+    PreparedDecompressShards(static_ins, esc_ins, dsts, status, stream, esc_bytes).run()
+
+
+class PreparedDecompressShards:
+    """A zipccl_decompress_shards call over fixed buffers, marshalled once; run() makes it."""
+
+    def __init__(self, static_ins, esc_ins, dsts, status=None, stream=None, esc_bytes=None):
+        nseg = len(dsts)
+        sp = (ctypes.c_void_p * nseg)(*[_ptr(t) for t in static_ins])
+        ep = (ctypes.c_void_p * nseg)(*[_ptr(t) for t in esc_ins])
+        if esc_bytes is None:
+            esc_bytes = [_nbytes(t) if t is not None else 0 for t in esc_ins]
+        eb = (ctypes.c_uint64 * nseg)(*[int(v) for v in esc_bytes])
+        arr = (DSegmentT * max(nseg, 1))()
+        for k, t in enumerate(dsts):
+            arr[k].dst = _ptr(t) if t.numel() else None
+            arr[k].n = t.numel()
+        self._args = (sp, ep, eb, arr, nseg, _ptr(status), _stream(stream))
+        self._keep = (static_ins, esc_ins, dsts, status)
+
+    def run(self):
+        _check(_lib.zipccl_decompress_shards(*self._args), "zipccl_decompress_shards")
 
 
 def decompress_accumulate(static_ins, esc_ins, n: int, local, dst, status=None, stream=None, esc_bytes=None):

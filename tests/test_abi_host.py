@@ -33,7 +33,8 @@ def test_header_declares_the_abi():
     for want in ["zipccl_plan", "zipccl_compress", "zipccl_decompress", "zipccl_decompress_accumulate",
                  "zipccl_compressed_size", "zipccl_static_size", "zipccl_workspace_size",
                  "zipccl_pipeline_create", "zipccl_pipeline_reduce", "zipccl_pipeline_destroy",
-                 "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many"]:
+                 "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many",
+                 "zipccl_decompress_shards"]:
         assert want in names
 
 
@@ -149,6 +150,16 @@ def test_argument_errors_before_any_launch(Z):
     sp = (vp * 1)(fake)
     ep = (vp * 1)(fake)
     eb = (ctypes.c_uint64 * 1)(10)
+    d[0].dst = 0x10000
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 0, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 65, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_shards(None, ep, eb, d, 1, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_shards(sp, (vp * 1)(None), eb, d, 1, None, None) == Z.ERR_INVALID   # 10 escape bytes at NULL
+    assert L.zipccl_decompress_shards((vp * 1)(fake + 64), ep, eb, d, 1, None, None) == Z.ERR_ALIGN
+    d[0].dst = 0x10001
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 1, None, None) == Z.ERR_ALIGN
+    d[0].dst, d[0].n = 0x10000, 1 << 32
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 1, None, None) == Z.ERR_SIZE
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 0, 10, fake, fake, None, None) == Z.ERR_INVALID
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 17, 10, fake, fake, None, None) == Z.ERR_INVALID
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 1, 1 << 32, fake, fake, None, None) == Z.ERR_SIZE

@@ -341,6 +341,48 @@ def test_pipeline_matches_oracle(Z, npeers, chunk, n):
     pipe.close()
 
 
+def test_decompress_shards_gathers_separate_buffers(Z):
+    # shards compressed one call each (as every rank of an all-gather would), plus one
+    # that is the second segment of a two-segment call, so that its escapes start past
+    # the first segment's in its escape buffer; all decoded in one launch into slices of
+    # one gathered tensor
+    sizes = [4096 * 5 + 17, 0, 1, 70000, 16384 * 3]
+    sigmas = [0.02, 1.0, 0.5, 1e-3, 3.0]
+    shards = [W.gaussian_bf16(n, s, 900 + k) for k, (n, s) in enumerate(zip(sizes, sigmas))]
+    comp = [gpu_compress(Z, [b], [Z.plan(sigma=s)]) for b, s in zip(shards, sigmas)]
+    pre, extra = W.gaussian_bf16(5000, 0.1, 951), W.gaussian_bf16(9000, 0.1, 950)
+    pl = Z.plan(sigma=0.1)
+    r2 = gpu_compress(Z, [pre, extra], [pl, pl])
+    assert r2["n_esc"][0] > 0
+    static_ins = [c["static"] for c in comp] + [r2["static"].data_ptr() + Z.static_size(pre.size)]
+    esc_ins = [c["esc"] for c in comp] + [r2["esc"]]
+    ns = sizes + [extra.size]
+    offs = [0]   # slices start 16-byte aligned; the gaps between them must stay untouched
+    for m in ns[:-1]:
+        offs.append((offs[-1] + m + 7) // 8 * 8)
+    out = torch.full((offs[-1] + ns[-1],), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dsts = [out[o:o + m] for o, m in zip(offs, ns)]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Z.decompress_shards(static_ins, esc_ins, dsts, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    want = np.full(out.numel(), 0xAAAA, np.uint16)
+    for o, b in zip(offs, shards + [extra]):
+        want[o:o + b.size] = b
+    got = host_u16(out)
+    assert np.array_equal(got, want), first_diff(got, want)
+    # a shard with a bad header is reported and left unwritten; the others decode
+    comp[3]["static"][8] ^= 4    # n
+    out.view(torch.int16).fill_(POISON16)
+    status.zero_()
+    Z.decompress_shards(static_ins, esc_ins, dsts, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & Z.STATUS_CORRUPT
+    got = host_u16(out)
+    want[offs[3]:offs[3] + ns[3]] = 0xAAAA
+    assert np.array_equal(got, want), first_diff(got, want)
+
+
 # ------------------------------------------------------------------------------------
 # the scan-kernel path for escape positions (used above 2^28 values per call), forced
 # on small inputs
