@@ -66,6 +66,7 @@ typedef enum zipccl_status {
 /* Bits OR-ed into the optional device status word. */
 #define ZIPCCL_STATUS_ESC_OVERFLOW 1u  /* escapes did not fit esc_cap; those past it were dropped */
 #define ZIPCCL_STATUS_CORRUPT 2u       /* decode: header or offset table inconsistent; not decoded */
+#define ZIPCCL_STATUS_BAD_INDEX 4u     /* gathered compress: a row index outside the matrix (row 0 was read) */
 
 /* A coding plan: 7 distinct exponents in 1..254, ascending; code(table[r]) = r + 1. */
 typedef struct zipccl_plan_t {
@@ -134,6 +135,34 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
 zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
                               void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
                               uint64_t* n_esc_out, uint32_t* status, void* stream);
+
+/* One segment whose values are rows of a row-major BF16 matrix picked by index: the
+ * MoE all-to-all dispatch payload of one destination (S2.D), compressed where the
+ * tokens lie instead of after a permute copy.  The segment's values are rows
+ * rows[0], rows[1], ..., rows[nrows - 1] of src, each row_len values, in that order
+ * (n = nrows * row_len); its compressed form is the one zipccl_compress gives for those
+ * values laid out contiguously.
+ *   src       device, 16-byte aligned: the matrix, src_rows rows of row_len values
+ *   rows      device, 4-byte aligned: nrows row indices; an index outside [0, src_rows)
+ *             sets ZIPCCL_STATUS_BAD_INDEX and row 0 is read in its place
+ *   row_len   a multiple of 8, at least 512 */
+typedef struct zipccl_gather_segment_t {
+    const void* src;
+    uint64_t src_rows;
+    uint64_t row_len;
+    const int32_t* rows;
+    uint64_t nrows;
+    zipccl_plan_t plan;
+} zipccl_gather_segment_t;
+
+/* zipccl_compress over gathered segments: the same outputs, layout, workspace and
+ * launches (the encode kernel reads each tile's row indices with scalar loads).
+ * Errors: as zipccl_compress; INVALID also for row_len not a multiple of 8 or below 512,
+ * or NULL src / rows with nrows > 0; ALIGN for rows not 4-byte aligned; SIZE for
+ * nrows * row_len >= 2^32 or src_rows >= 2^32. */
+zipccl_status zipccl_compress_gather(const zipccl_gather_segment_t* segs, int nseg, void* static_out,
+                                     uint64_t static_cap, void* esc_out, uint64_t esc_cap, void* workspace,
+                                     uint64_t workspace_bytes, uint64_t* n_esc_out, uint32_t* status, void* stream);
 
 /* Decompress nseg segments whose static parts lie back to back at static_in (as
  * zipccl_compress writes them; static_bytes = their total size) and whose escapes are

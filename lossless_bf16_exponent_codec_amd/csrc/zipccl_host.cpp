@@ -110,34 +110,24 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg)
     return ws_bytes(total_n / kUnit + uint64_t(nseg));   // bounds the sum of ceil(n_s / 16384)
 }
 
-zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
-                              void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
-                              uint64_t* n_esc_out, uint32_t* status, void* stream)
+namespace {
+
+// Completes the compress arguments once a.seg[0..nseg) holds src, rows, row_len,
+// src_rows, n and the table of each segment, and launches.
+zipccl_status compress_segments(CArgs& a, int nseg, void* static_out, uint64_t static_cap, void* esc_out,
+                                uint64_t esc_cap, void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
+                                uint32_t* status, void* stream)
 {
-    if (!segs || nseg < 1 || nseg > kMaxSegs || !static_out || !workspace) return ZIPCCL_ERR_INVALID;
-    if (!aligned(static_out, 128) || !aligned(workspace, 256) || (n_esc_out && !aligned(n_esc_out, 8)) ||
-        (status && !aligned(status, 4)))
-        return ZIPCCL_ERR_ALIGN;
-    CArgs a;
-    std::memset(&a, 0, sizeof(a));
     uint64_t total = 0, units = 0, blocks = 0, st_off = 0;
     for (int s = 0; s < nseg; s++) {
-        const zipccl_segment_t& g = segs[s];
-        if (g.n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
-        if (g.n > 0 && !g.src) return ZIPCCL_ERR_INVALID;
-        if (!aligned(g.src, 16)) return ZIPCCL_ERR_ALIGN;
-        if (!plan_valid(g.plan)) return ZIPCCL_ERR_INVALID;
         CSeg& c = a.seg[s];
-        c.src = static_cast<const uint16_t*>(g.src);
         c.dst = static_cast<uint8_t*>(static_out) + st_off;
-        c.n = uint32_t(g.n);
         c.unit0 = uint32_t(units);
         c.block0 = uint32_t(blocks);
-        pack_table(g.plan, c.table_lo, c.table_hi);
-        total += g.n;
-        units += units_of(g.n);
-        blocks += blocks_of(g.n);
-        st_off += static_bytes_of(g.n);
+        total += c.n;
+        units += units_of(c.n);
+        blocks += blocks_of(c.n);
+        st_off += static_bytes_of(c.n);
     }
     if (total >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
     if (st_off > static_cap) return ZIPCCL_ERR_SIZE;
@@ -157,6 +147,70 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
     a.total_blocks = uint32_t(blocks);
     a.direct = (units > 0 && units <= direct_prefix_max_units()) ? 1u : 0u;
     return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)));
+}
+
+zipccl_status check_compress_buffers(int nseg, void* static_out, void* workspace, uint64_t* n_esc_out,
+                                     uint32_t* status)
+{
+    if (nseg < 1 || nseg > kMaxSegs || !static_out || !workspace) return ZIPCCL_ERR_INVALID;
+    if (!aligned(static_out, 128) || !aligned(workspace, 256) || (n_esc_out && !aligned(n_esc_out, 8)) ||
+        (status && !aligned(status, 4)))
+        return ZIPCCL_ERR_ALIGN;
+    return ZIPCCL_OK;
+}
+
+}  // namespace
+
+zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
+                              void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
+                              uint64_t* n_esc_out, uint32_t* status, void* stream)
+{
+    if (!segs) return ZIPCCL_ERR_INVALID;
+    if (zipccl_status r = check_compress_buffers(nseg, static_out, workspace, n_esc_out, status)) return r;
+    CArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int s = 0; s < nseg; s++) {
+        const zipccl_segment_t& g = segs[s];
+        if (g.n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+        if (g.n > 0 && !g.src) return ZIPCCL_ERR_INVALID;
+        if (!aligned(g.src, 16)) return ZIPCCL_ERR_ALIGN;
+        if (!plan_valid(g.plan)) return ZIPCCL_ERR_INVALID;
+        CSeg& c = a.seg[s];
+        c.src = static_cast<const uint16_t*>(g.src);
+        c.n = uint32_t(g.n);
+        pack_table(g.plan, c.table_lo, c.table_hi);
+    }
+    return compress_segments(a, nseg, static_out, static_cap, esc_out, esc_cap, workspace, workspace_bytes,
+                             n_esc_out, status, stream);
+}
+
+zipccl_status zipccl_compress_gather(const zipccl_gather_segment_t* segs, int nseg, void* static_out,
+                                     uint64_t static_cap, void* esc_out, uint64_t esc_cap, void* workspace,
+                                     uint64_t workspace_bytes, uint64_t* n_esc_out, uint32_t* status, void* stream)
+{
+    if (!segs) return ZIPCCL_ERR_INVALID;
+    if (zipccl_status r = check_compress_buffers(nseg, static_out, workspace, n_esc_out, status)) return r;
+    CArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int s = 0; s < nseg; s++) {
+        const zipccl_gather_segment_t& g = segs[s];
+        if (g.row_len % 8 != 0 || g.row_len < 512 || g.row_len >= (1ull << 32)) return ZIPCCL_ERR_INVALID;
+        if (g.src_rows >= (1ull << 32) || g.nrows >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+        const uint64_t n = g.nrows * g.row_len;
+        if (n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+        if (n > 0 && (!g.src || !g.rows || g.src_rows == 0)) return ZIPCCL_ERR_INVALID;
+        if (!aligned(g.src, 16) || !aligned(g.rows, 4)) return ZIPCCL_ERR_ALIGN;
+        if (!plan_valid(g.plan)) return ZIPCCL_ERR_INVALID;
+        CSeg& c = a.seg[s];
+        c.src = static_cast<const uint16_t*>(g.src);
+        c.rows = n > 0 ? g.rows : nullptr;
+        c.row_len = uint32_t(g.row_len);
+        c.src_rows = uint32_t(g.src_rows);
+        c.n = uint32_t(n);
+        pack_table(g.plan, c.table_lo, c.table_hi);
+    }
+    return compress_segments(a, nseg, static_out, static_cap, esc_out, esc_cap, workspace, workspace_bytes,
+                             n_esc_out, status, stream);
 }
 
 zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, const void* esc_in,

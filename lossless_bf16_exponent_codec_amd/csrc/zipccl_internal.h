@@ -39,13 +39,16 @@ __host__ __device__ inline uint64_t ws_bytes(uint64_t units)
 constexpr uint32_t kDirectPrefixMaxUnits = 16384;
 
 struct CSeg {              // compress: one segment
-    const uint16_t* src;   // n BF16 values
+    const uint16_t* src;   // n BF16 values, or the matrix the rows are gathered from
     uint8_t* dst;          // static part of this segment
+    const int32_t* rows;   // gathered segment: n / row_len row indices; null: src is contiguous
     uint32_t n;
     uint32_t unit0;        // first encode workgroup of the segment (units of kUnit values)
     uint32_t block0;       // first block of the segment in launch-wide block numbering
     uint32_t table_lo;     // table[0..3]
     uint32_t table_hi;     // table[4..6], byte 3 = 0
+    uint32_t row_len;      // gathered segment: values per row (a multiple of 8, >= 512)
+    uint32_t src_rows;     // gathered segment: rows of the matrix (indices must be below)
     uint32_t pad;
 };
 
@@ -64,6 +67,8 @@ struct CArgs {
     uint32_t total_blocks;
     uint32_t direct;       // 1: the place kernel computes positions from unit_counts
 };
+
+static_assert(sizeof(CArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 struct DSeg {              // decompress: one segment
     const uint8_t* src;    // static part

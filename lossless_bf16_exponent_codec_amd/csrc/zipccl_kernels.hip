@@ -111,6 +111,45 @@ __device__ inline uint4 load_lane(const uint16_t* src, uint64_t t, uint32_t lane
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Gathered segments (CSeg::rows set): value i of the segment is column i % row_len of
+// matrix row rows[i / row_len].  row_len is a multiple of 8 and at least 512, so a
+// lane's 8 values lie in one row and a tile spans at most two.  A row index outside the
+// matrix is replaced by 0 and reported through `bad`.
+//
+// Address of this lane's 8 values in the tile that starts at value i0 (all 512 exist):
+// the tile's rows are read with scalar loads, the lane picks one by its column.
+__device__ inline const uint16_t* gathered_lane_ptr(const CSeg& sg, uint32_t i0, uint32_t lane, bool& bad)
+{
+    const uint32_t L = sg.row_len;
+    const uint32_t r0 = __builtin_amdgcn_readfirstlane(i0 / L);
+    const uint32_t c0 = i0 - r0 * L;
+    const uint32_t split = L - c0;   // values of the tile still in row r0
+    const uint32_t r1 = __builtin_amdgcn_readfirstlane(min(r0 + 1, sg.n / L - 1));
+    // both indices are the same for the whole wave: scalar loads
+    const uint32_t x0 = __builtin_amdgcn_readfirstlane(sg.rows[r0]);
+    const uint32_t x1 = __builtin_amdgcn_readfirstlane(sg.rows[r1]);
+    const uint32_t j = 8 * lane;
+    const bool second = j >= split;
+    uint32_t x = second ? x1 : x0;
+    const uint32_t col = second ? j - split : c0 + j;
+    const bool b = x >= sg.src_rows;   // negative indices compare as large
+    bad = bad || b;
+    return sg.src + uint64_t(b ? 0u : x) * L + col;
+}
+
+// This lane's 8 values of tile t of a gathered segment (0 past n; n is a multiple of 8).
+__device__ inline uint4 load_lane_rows(const CSeg& sg, uint32_t t, uint32_t lane, bool& bad)
+{
+    const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
+    if (i >= sg.n) return make_uint4(0, 0, 0, 0);
+    const uint32_t L = sg.row_len;
+    const uint32_t r = uint32_t(i) / L;
+    const uint32_t x = uint32_t(sg.rows[r]);
+    const bool b = x >= sg.src_rows;
+    bad = bad || b;
+    return load_nt(reinterpret_cast<const uint4*>(sg.src + uint64_t(b ? 0u : x) * L + (uint32_t(i) - r * L)));
+}
+
 // --------------------------------------------------------------------------------
 // compress
 // --------------------------------------------------------------------------------
@@ -368,11 +407,21 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     // straight-line code, so each tile waits only for its own load; the segment's last,
     // partial half block loads after the barrier (values past n read as 0).
     const bool full = active && uint64_t(hb + 1) * kHalf <= n;
-    const uint16_t* src = sg.src + uint64_t(hb) * kHalf + 8 * lane;
+    bool bad_row = false;   // a gathered row index outside the matrix
     uint4 v[4];
     if (full) {
+        // addresses first (a gathered segment reads its row indices with scalar loads),
+        // then the 4 loads in straight-line code
+        const uint16_t* src[4];
+        if (sg.rows == nullptr) {
 #pragma unroll
-        for (int k = 0; k < 4; k++) v[k] = load_nt(reinterpret_cast<const uint4*>(src + k * kTile));
+            for (int k = 0; k < 4; k++) src[k] = sg.src + uint64_t(hb) * kHalf + k * kTile + 8 * lane;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; k++) src[k] = gathered_lane_ptr(sg, hb * kHalf + k * kTile, lane, bad_row);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) v[k] = load_nt(reinterpret_cast<const uint4*>(src[k]));
     }
     __shared__ uint32_t s_hcnt[kEncWaves];
     if (tid < 256) {   // exponent -> code entry of this segment
@@ -391,8 +440,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     if (full) {
         run = encode_half<true>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
     } else if (active) {
+        if (sg.rows == nullptr) {
 #pragma unroll
-        for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, hb * 4 + k, lane, n);
+            for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, hb * 4 + k, lane, n);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; k++) v[k] = load_lane_rows(sg, hb * 4 + k, lane, bad_row);
+        }
         run = encode_half<false>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
     }
     if (lane == 0) s_hcnt[wave] = run;
@@ -411,6 +465,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     const uint8_t* esc_lds = s_esc[wave];
     for (uint32_t k = lane; k < run; k += 64) stage[k] = esc_lds[k];
     if (!active && lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
+    if (ballot(bad_row) && lane == 0) or_status(a.status, ZIPCCL_STATUS_BAD_INDEX);
 }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libzipccl.so")
 
 OK, ERR_INVALID, ERR_ALIGN, ERR_SIZE, ERR_HIP, ERR_CORRUPT = range(6)
-STATUS_ESC_OVERFLOW, STATUS_CORRUPT = 1, 2
+STATUS_ESC_OVERFLOW, STATUS_CORRUPT, STATUS_BAD_INDEX = 1, 2, 4
 MAX_SEGMENTS, MAX_PEERS = 64, 16
 FORMAT_VERSION, MAGIC = 1, 0x3143435A
 
@@ -34,6 +34,11 @@ class PlanT(ctypes.Structure):
 
 class SegmentT(ctypes.Structure):
     _fields_ = [("src", ctypes.c_void_p), ("n", ctypes.c_uint64), ("plan", PlanT)]
+
+
+class GatherSegmentT(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("src_rows", ctypes.c_uint64), ("row_len", ctypes.c_uint64),
+                ("rows", ctypes.c_void_p), ("nrows", ctypes.c_uint64), ("plan", PlanT)]
 
 
 class DSegmentT(ctypes.Structure):
@@ -66,6 +71,9 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_workspace_size.argtypes = [u64, i32]
     lib.zipccl_compress.restype = i32
     lib.zipccl_compress.argtypes = [ctypes.POINTER(SegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp, vp]
+    lib.zipccl_compress_gather.restype = i32
+    lib.zipccl_compress_gather.argtypes = [ctypes.POINTER(GatherSegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp,
+                                           vp]
     lib.zipccl_decompress.restype = i32
     lib.zipccl_decompress.argtypes = [vp, u64, vp, u64, ctypes.POINTER(DSegmentT), i32, vp, vp]
     lib.zipccl_decompress_shards.restype = i32
@@ -167,6 +175,38 @@ def compress(segments, static_out, esc_out, workspace, n_esc_out=None, status=No
     rc = _lib.zipccl_compress(arr, nseg, _ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap,
                               _ptr(workspace), _nbytes(workspace), _ptr(n_esc_out), _ptr(status), _stream(stream))
     _check(rc, "zipccl_compress")
+
+
+def compress_gather(segments, static_out, esc_out, workspace, n_esc_out=None, status=None, stream=None,
+                    esc_cap: int | None = None):
+    """zipccl_compress_gather.  segments: list of (matrix, rows, plan): matrix a 2-D bf16
+    device tensor (row-major, contiguous), rows a 1-D int32 device tensor of row indices."""
+    PreparedCompressGather(segments, static_out, esc_out, workspace, n_esc_out, status, stream, esc_cap).run()
+
+
+class PreparedCompressGather:
+    """A zipccl_compress_gather call over fixed buffers, marshalled once; run() makes it."""
+
+    def __init__(self, segments, static_out, esc_out, workspace, n_esc_out=None, status=None, stream=None,
+                 esc_cap: int | None = None):
+        nseg = len(segments)
+        self._arr = (GatherSegmentT * max(nseg, 1))()
+        for k, (m, rows, p) in enumerate(segments):
+            if m.dim() != 2 or not m.is_contiguous() or rows.dtype != torch.int32:
+                raise ValueError("compress_gather takes a contiguous 2-D matrix and int32 row indices")
+            self._arr[k].src = _ptr(m) if m.numel() else None
+            self._arr[k].src_rows = m.shape[0]
+            self._arr[k].row_len = m.shape[1]
+            self._arr[k].rows = _ptr(rows) if rows.numel() else None
+            self._arr[k].nrows = rows.numel()
+            self._arr[k].plan = p
+        cap = _nbytes(esc_out) if esc_cap is None else esc_cap
+        self._args = (self._arr, nseg, _ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap, _ptr(workspace),
+                      _nbytes(workspace), _ptr(n_esc_out), _ptr(status), _stream(stream))
+        self._keep = (segments, static_out, esc_out, workspace, n_esc_out, status)
+
+    def run(self):
+        _check(_lib.zipccl_compress_gather(*self._args), "zipccl_compress_gather")
 
 
 def decompress(static_in, esc_in, dsts, status=None, stream=None, static_bytes=None, esc_bytes=None):

@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
                  "zipccl_compressed_size", "zipccl_static_size", "zipccl_workspace_size",
                  "zipccl_pipeline_create", "zipccl_pipeline_reduce", "zipccl_pipeline_destroy",
                  "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many",
-                 "zipccl_decompress_shards"]:
+                 "zipccl_decompress_shards", "zipccl_compress_gather"]:
         assert want in names
 
 
@@ -140,6 +140,22 @@ def test_argument_errors_before_any_launch(Z):
     seg[0].n = 100
     seg[0].plan.table[3] = seg[0].plan.table[2]
     assert L.zipccl_compress(seg, 1, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_INVALID
+    g = (Z.GatherSegmentT * 1)()
+    g[0].src, g[0].src_rows, g[0].row_len, g[0].rows, g[0].nrows, g[0].plan = 0x10000, 100, 7168, 0x20000, 10, p
+    gws = Z.workspace_size(71680, 1)
+    assert L.zipccl_compress_gather(g, 0, fake, 1 << 20, fake, 100, fake, gws, None, None, None) == Z.ERR_INVALID
+    g[0].row_len = 7170                  # not a multiple of 8
+    assert L.zipccl_compress_gather(g, 1, fake, 1 << 20, fake, 100, fake, gws, None, None, None) == Z.ERR_INVALID
+    g[0].row_len = 256                   # below 512
+    assert L.zipccl_compress_gather(g, 1, fake, 1 << 20, fake, 100, fake, gws, None, None, None) == Z.ERR_INVALID
+    g[0].row_len, g[0].rows = 7168, 0x20002
+    assert L.zipccl_compress_gather(g, 1, fake, 1 << 20, fake, 100, fake, gws, None, None, None) == Z.ERR_ALIGN
+    g[0].rows = None
+    assert L.zipccl_compress_gather(g, 1, fake, 1 << 20, fake, 100, fake, gws, None, None, None) == Z.ERR_INVALID
+    g[0].rows, g[0].nrows = 0x20000, 1 << 20      # 7168 << 20 values
+    assert L.zipccl_compress_gather(g, 1, fake, 1 << 40, fake, 100, fake, 1 << 40, None, None, None) == Z.ERR_SIZE
+    g[0].nrows = 10
+    assert L.zipccl_compress_gather(g, 1, fake, 10, fake, 100, fake, gws, None, None, None) == Z.ERR_SIZE
     d = (Z.DSegmentT * 1)()
     d[0].dst, d[0].n = 0x10000, 5000
     assert L.zipccl_decompress(fake, 100, fake, 10, d, 1, None, None) == Z.ERR_SIZE

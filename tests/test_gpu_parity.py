@@ -384,6 +384,64 @@ def test_decompress_shards_gathers_separate_buffers(Z):
 
 
 # ------------------------------------------------------------------------------------
+# compress of rows gathered by index (MoE dispatch without a permute copy)
+# ------------------------------------------------------------------------------------
+def gpu_compress_gather(Z, matrix_bits, rows_list, plans):
+    """Compresses matrix rows picked by each int32 index array; returns what
+    gpu_compress returns (sizes = values per segment)."""
+    H = matrix_bits.shape[1]
+    mat = dev_bf16(matrix_bits.reshape(-1)).view(matrix_bits.shape[0], H)
+    rows_t = [torch.from_numpy(np.ascontiguousarray(r, np.int32)).cuda() for r in rows_list]
+    sizes = [len(r) * H for r in rows_list]
+    total_static = sum(Z.static_size(n) for n in sizes)
+    static = torch.full((max(total_static, 1),), POISON, dtype=torch.uint8, device="cuda")
+    esc = torch.full((max(sum(sizes), 1),), POISON, dtype=torch.uint8, device="cuda")
+    n_esc = torch.full((len(sizes) + 1,), -1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(Z.workspace_size(sum(sizes), len(sizes)), dtype=torch.uint8, device="cuda")
+    Z.compress_gather(list(zip([mat] * len(rows_t), rows_t, plans)), static, esc, ws, n_esc, status)
+    torch.cuda.synchronize()
+    return dict(static=static, esc=esc, n_esc=n_esc.cpu().numpy(), status=int(status.item()), sizes=sizes,
+                static_h=static.cpu().numpy()[:total_static], esc_h=esc.cpu().numpy())
+
+
+@pytest.mark.parametrize("tokens,H", [(1200, 7168), (700, 1000), (900, 512)])
+def test_compress_gather_matches_oracle(Z, tokens, H):
+    # a routed dispatch: tokens go to 8 destinations with Zipf(1.2) counts; bucket 0 keeps
+    # the router's (random) order, the others ascending; one bucket also repeats a row
+    print(f"gather tokens={tokens} H={H}", flush=True)
+    mat = W.gaussian_bf16(tokens * H, 0.5, 70 + H).reshape(tokens, H)
+    rng = np.random.default_rng(H)
+    perm = rng.permutation(tokens)
+    counts = W.zipf_counts(tokens, 8, 1.2)
+    rows_list, r = [], 0
+    for b, c in enumerate(counts):
+        idx = perm[r:r + c]
+        rows_list.append(idx if b == 0 else np.sort(idx))
+        r += c
+    rows_list[3] = np.concatenate([rows_list[3], rows_list[3][:5]])
+    rows_list.append(np.zeros(0, np.int64))          # a destination that gets no tokens
+    plans = [Z.plan(sigma=0.5)] * 8 + [Z.plan(sigma=1.0)]
+    res = gpu_compress_gather(Z, mat, rows_list, plans)
+    segs = [mat[idx].reshape(-1) for idx in rows_list]
+    check_against_oracle(Z, segs, plans, res)
+    outs, status = gpu_decompress(Z, res)
+    assert status == 0
+    for x, y in zip(segs, outs):
+        assert np.array_equal(x, y), first_diff(x, y)
+
+
+def test_compress_gather_bad_index(Z):
+    tokens, H = 64, 1024
+    mat = W.gaussian_bf16(tokens * H, 0.5, 77).reshape(tokens, H)
+    rows = np.array([5, 63, 64, -1, 7, 2**31 - 1, 0, 9], np.int64)
+    res = gpu_compress_gather(Z, mat, [rows], [Z.plan(sigma=0.5)])
+    assert res["status"] & Z.STATUS_BAD_INDEX
+    used = np.where((rows >= 0) & (rows < tokens), rows, 0)   # row 0 is read in their place
+    check_against_oracle(Z, [mat[used].reshape(-1)], [Z.plan(sigma=0.5)], dict(res, status=0))
+
+
+# ------------------------------------------------------------------------------------
 # the scan-kernel path for escape positions (used above 2^28 values per call), forced
 # on small inputs
 # ------------------------------------------------------------------------------------
