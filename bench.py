@@ -21,7 +21,9 @@ Printed (one JSON line on stdout):
              kernel sources); roofline_other_op for the other operation;
   cpu_baseline  the plain C oracle, single-threaded, on the same bucket;
   per_config the other workloads (1 Mi chunk, activations with escapes and specials,
-             MoE dispatch buckets, the all-gather receive side decoding 16 separately
+             MoE dispatch buckets, the same dispatch compressed from the unpermuted
+             token matrix by row index (against a permute copy + compress), the
+             all-gather receive side decoding 16 separately
              compressed shards in one launch, reduce-scatter share with decode-accumulate
              and the two-stream pipeline), each with GB/s and HBM fraction.
 """
@@ -314,6 +316,66 @@ def bench_allgather(torch, Z, W, rounds):
     }
 
 
+def bench_moe_gather(torch, Z, W, rounds):
+    """MoE dispatch from the unpermuted token matrix: the 8 destinations' rows compressed
+    in one zipccl_compress_gather launch, against a permute copy (torch index_select)
+    followed by zipccl_compress of the permuted buckets.  Two rotating sets."""
+    import numpy as np
+    wl = W.moe_routed_16384x7168()
+    H, rows = wl.extra["hidden"], wl.extra["rows"]
+    T = wl.segments[0].size // H
+    plans = [Z.plan(sigma=s) for s in wl.sigmas]
+    sizes = [len(r) * H for r in rows]
+    n = sum(sizes)
+    static_bytes = sum(Z.static_size(m) for m in sizes)
+    ws = torch.zeros(Z.workspace_size(n, len(sizes)), dtype=torch.uint8, device="cuda")
+    n_esc = torch.zeros(len(sizes) + 1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    order = torch.from_numpy(np.concatenate(rows).astype(np.int64)).cuda()
+    sets = []
+    for _ in range(2):
+        mat = to_dev(torch, wl.segments[0]).view(T, H)
+        rows_t = [torch.from_numpy(r).cuda() for r in rows]
+        st = torch.empty(static_bytes, dtype=torch.uint8, device="cuda")
+        esc = torch.empty(n, dtype=torch.uint8, device="cuda")
+        perm = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        bufs = list(torch.split(perm, sizes))
+        sets.append(dict(
+            mat=mat, perm=perm, st=st, esc=esc,
+            gather=Z.PreparedCompressGather(list(zip([mat] * len(rows_t), rows_t, plans)), st, esc, ws, n_esc, status),
+            compress=Z.PreparedCompress(bufs, st, esc, ws, n_esc, status)))
+
+    def permute(k):
+        s = sets[k % 2]
+        torch.index_select(s["mat"], 0, order, out=s["perm"].view(-1, H))
+
+    g = batched_ms(torch, lambda k: sets[k % 2]["gather"].run(plans), 2, rounds)
+    # parity: the gathered compress equals the compress of the permuted copy, byte for byte
+    s0 = sets[0]
+    s0["gather"].run(plans)
+    torch.cuda.synchronize()
+    st_g, esc_g = s0["st"].clone(), s0["esc"][:int(n_esc[-1].item())].clone()
+    pm = batched_ms(torch, permute, 2, rounds)
+    cp = batched_ms(torch, lambda k: sets[k % 2]["compress"].run(plans), 2, rounds)
+    permute(0)
+    s0["compress"].run(plans)
+    torch.cuda.synchronize()
+    total_esc = int(n_esc[-1].item())
+    ok = (int(status.item()) == 0 and bool(torch.equal(st_g, s0["st"]))
+          and bool(torch.equal(esc_g, s0["esc"][:total_esc])))
+    moved = compress_bytes(n, static_bytes, total_esc)
+    return {
+        "elements": n, "segments": len(sizes),
+        "gather_compress_us": round(g * 1e3, 2),
+        "gather_compress_GBps": round(2 * n / (g * 1e-3) / 1e9, 1),
+        "gather_compress_hbm_frac": round(moved / (g * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "permute_us": round(pm * 1e3, 2),
+        "compress_permuted_us": round(cp * 1e3, 2),
+        "permute_plus_compress_us": round((pm + cp) * 1e3, 2),
+        "parity_vs_permuted": ok,
+    }
+
+
 def copy_ceiling(torch, iters=10):
     """A plain 1 GiB device-to-device copy: the practical HBM ceiling (read + write bytes / s)."""
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -571,6 +633,9 @@ def main(argv=None) -> int:
             per[name] = r2
             del b2
             torch.cuda.empty_cache()
+        log("workload moe_routed_16384x7168")
+        per["moe_routed_16384x7168"] = bench_moe_gather(torch, Z, W, 5)
+        torch.cuda.empty_cache()
         log("workload allgather_16x4m")
         per["allgather_16x4m"] = bench_allgather(torch, Z, W, 5)
         torch.cuda.empty_cache()

@@ -25,6 +25,11 @@ Workloads:
                contiguous destination buckets whose token counts follow Zipf(s=1.2)
                (largest-remainder rounding of 16384 * k**-1.2 / sum); one segment per
                bucket.
+  moe_routed_16384x7168  the same token matrix before the permute: each of the 16384
+               tokens is routed to one of 8 destinations with the same Zipf(1.2) counts
+               by a seeded permutation (numpy default_rng(41)); destination b gets the
+               tokens perm[c_0 + ... + c_(b-1) :][:c_b] in ascending order.  For the
+               compress of rows gathered by index.
   rs_512m      reduce-scatter receive share: 7 peer shards of 64 Mi values from
                N(0, 1e-3) with seeds 500..506 and the local shard with seed 507;
                processed in chunks of 2 Mi values (4 MiB of BF16) per peer.
@@ -37,7 +42,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "gaussian_bf16", "chunk_1m", "bucket_64m", "act_8192x7168",
-           "moe_16384x7168", "rs_512m", "zipf_counts", "WORKLOADS", "get"]
+           "moe_16384x7168", "moe_routed_16384x7168", "rs_512m", "zipf_counts", "WORKLOADS", "get"]
 
 
 @dataclass
@@ -134,6 +139,20 @@ def moe_16384x7168(tokens: int = 16384, hidden: int = 7168, buckets: int = 8, s:
                     {"counts": counts, "hidden": hidden})
 
 
+def moe_routed_16384x7168(tokens: int = 16384, hidden: int = 7168, buckets: int = 8, s: float = 1.2,
+                          sigma: float = 0.5, seed: int = 4, route_seed: int = 41) -> Workload:
+    flat = gaussian_bf16(tokens * hidden, sigma, seed)
+    counts = zipf_counts(tokens, buckets, s)
+    perm = np.random.default_rng(route_seed).permutation(tokens)
+    rows, r = [], 0
+    for c in counts:
+        rows.append(np.sort(perm[r:r + c]).astype(np.int32))
+        r += c
+    return Workload("moe_routed_16384x7168", [flat], [sigma] * buckets,
+                    f"{tokens}x{hidden} N(0,{sigma}) tokens routed to {buckets} destinations, Zipf({s}) counts {counts}",
+                    {"counts": counts, "hidden": hidden, "rows": rows})
+
+
 def rs_512m(peers: int = 7, shard: int = 1 << 26, chunk: int = 1 << 21, sigma: float = 1e-3) -> Workload:
     segs = [gaussian_bf16(shard, sigma, 500 + p) for p in range(peers)]
     local = gaussian_bf16(shard, sigma, 500 + peers)
@@ -147,6 +166,7 @@ WORKLOADS = {
     "bucket_64m": bucket_64m,
     "act_8192x7168": act_8192x7168,
     "moe_16384x7168": moe_16384x7168,
+    "moe_routed_16384x7168": moe_routed_16384x7168,
     "rs_512m": rs_512m,
 }
 

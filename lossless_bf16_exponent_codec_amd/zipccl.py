@@ -185,7 +185,8 @@ def compress_gather(segments, static_out, esc_out, workspace, n_esc_out=None, st
 
 
 class PreparedCompressGather:
-    """A zipccl_compress_gather call over fixed buffers, marshalled once; run() makes it."""
+    """A zipccl_compress_gather call over fixed buffers, marshalled once; run([plans])
+    makes it."""
 
     def __init__(self, segments, static_out, esc_out, workspace, n_esc_out=None, status=None, stream=None,
                  esc_cap: int | None = None):
@@ -205,7 +206,11 @@ class PreparedCompressGather:
                       _nbytes(workspace), _ptr(n_esc_out), _ptr(status), _stream(stream))
         self._keep = (segments, static_out, esc_out, workspace, n_esc_out, status)
 
-    def run(self):
+    def run(self, plans=None):
+        """Makes the call; `plans`, if given, replaces the segments' plans first."""
+        if plans is not None:
+            for k, p in enumerate(plans):
+                self._arr[k].plan = p
         _check(_lib.zipccl_compress_gather(*self._args), "zipccl_compress_gather")
 
 
