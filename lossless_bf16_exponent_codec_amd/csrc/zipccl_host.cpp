@@ -113,10 +113,10 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg)
 namespace {
 
 // Completes the compress arguments once a.seg[0..nseg) holds src, rows, row_len,
-// src_rows, n and the table of each segment, and launches.
-zipccl_status compress_segments(CArgs& a, int nseg, void* static_out, uint64_t static_cap, void* esc_out,
-                                uint64_t esc_cap, void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
-                                uint32_t* status, void* stream)
+// src_rows, n and the table of each segment.
+zipccl_status prepare_compress(CArgs& a, int nseg, void* static_out, uint64_t static_cap, void* esc_out,
+                               uint64_t esc_cap, void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
+                               uint32_t* status)
 {
     uint64_t total = 0, units = 0, blocks = 0, st_off = 0;
     for (int s = 0; s < nseg; s++) {
@@ -146,7 +146,38 @@ zipccl_status compress_segments(CArgs& a, int nseg, void* static_out, uint64_t s
     a.total_units = uint32_t(units);
     a.total_blocks = uint32_t(blocks);
     a.direct = (units > 0 && units <= direct_prefix_max_units()) ? 1u : 0u;
+    return ZIPCCL_OK;
+}
+
+zipccl_status compress_segments(CArgs& a, int nseg, void* static_out, uint64_t static_cap, void* esc_out,
+                                uint64_t esc_cap, void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
+                                uint32_t* status, void* stream)
+{
+    if (zipccl_status r = prepare_compress(a, nseg, static_out, static_cap, esc_out, esc_cap, workspace,
+                                           workspace_bytes, n_esc_out, status))
+        return r;
     return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)));
+}
+
+// The arguments of a call with at most kMaxPeers segments in the pipeline's smaller form.
+CArgsP chunk_args(const CArgs& a)
+{
+    CArgsP c;
+    std::memset(&c, 0, sizeof(c));
+    for (int s = 0; s < a.nseg && s < kMaxPeers; s++) c.seg[s] = a.seg[s];
+    c.esc = a.esc;
+    c.esc_cap = a.esc_cap;
+    c.counts = a.counts;
+    c.pos = a.pos;
+    c.unit_counts = a.unit_counts;
+    c.stage = a.stage;
+    c.n_esc_out = a.n_esc_out;
+    c.status = a.status;
+    c.nseg = a.nseg;
+    c.total_units = a.total_units;
+    c.total_blocks = a.total_blocks;
+    c.direct = a.direct;
+    return c;
 }
 
 zipccl_status check_compress_buffers(int nseg, void* static_out, void* workspace, uint64_t* n_esc_out,
@@ -309,7 +340,7 @@ struct zipccl_pipeline {
     uint64_t chunk;
     uint32_t group;            // chunks per hand-off between the streams
     uint8_t* scratch;
-    uint64_t slot_static, slot_esc, ws_size;   // bytes per chunk slot and of the workspace
+    uint64_t slot_static, slot_esc, ws_size;   // bytes per chunk slot and of one workspace
     hipStream_t sa, sb;
     hipEvent_t compressed[2], reduced[2];      // one per half of the ring
     bool reduced_recorded[2];
@@ -328,8 +359,10 @@ uint32_t pipeline_group(int npeers, uint64_t chunk)
     return g;
 }
 
-// Scratch layout: the compress workspace, then 2 * group chunk slots (a ring of two
-// groups), each holding the chunk's npeers static parts and room for all its escapes.
+// Scratch layout: two compress workspaces (consecutive chunks alternate, so that one
+// launch can place a chunk while it encodes the next), then 2 * group chunk slots (a
+// ring of two groups), each holding the chunk's npeers static parts and room for all
+// its escapes.
 void pipeline_layout(int npeers, uint64_t chunk, uint64_t& slot_static, uint64_t& slot_esc, uint64_t& ws)
 {
     slot_static = uint64_t(npeers) * static_bytes_of(chunk);
@@ -344,7 +377,7 @@ uint64_t zipccl_pipeline_scratch_size(int npeers, uint64_t chunk)
     if (npeers < 1 || npeers > kMaxPeers || chunk == 0) return 0;
     uint64_t ss, se, ws;
     pipeline_layout(npeers, chunk, ss, se, ws);
-    return ws + 2ull * pipeline_group(npeers, chunk) * (ss + se);
+    return 2 * ws + 2ull * pipeline_group(npeers, chunk) * (ss + se);
 }
 
 zipccl_status zipccl_pipeline_create(int npeers, uint64_t chunk, void* scratch, uint64_t scratch_bytes,
@@ -390,53 +423,75 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
         if (!aligned(peer_src[p], 16)) return ZIPCCL_ERR_ALIGN;
         if (!plan_valid(plans[p])) return ZIPCCL_ERR_INVALID;
     }
-    uint8_t* ws = pipe->scratch;
     const uint64_t nchunks = (n + pipe->chunk - 1) / pipe->chunk;
     const uint64_t G = pipe->group;
+    hipStream_t sa = pipe->sa, sb = pipe->sb;
+    uint8_t* slots = pipe->scratch + 2 * pipe->ws_size;
+    const uint64_t slot_bytes = pipe->slot_static + pipe->slot_esc;
     for (uint64_t c0 = 0; c0 < nchunks; c0 += G) {
         const int half = int((c0 / G) & 1);   // which half of the ring this group uses
         const uint64_t c1 = std::min(nchunks, c0 + G);
         // the group two hand-offs back used these slots: its reduction must be done
-        if (pipe->reduced_recorded[half] && hipStreamWaitEvent(pipe->sa, pipe->reduced[half], 0) != hipSuccess)
+        if (pipe->reduced_recorded[half] && hipStreamWaitEvent(sa, pipe->reduced[half], 0) != hipSuccess)
             return ZIPCCL_ERR_HIP;
-        for (int pass = 0; pass < 2; pass++) {   // 0: compress the group on a, 1: reduce it on b
-            for (uint64_t c = c0; c < c1; c++) {
-                const uint64_t off = c * pipe->chunk;
-                const uint64_t m = std::min(pipe->chunk, n - off);
-                uint8_t* st = pipe->scratch + pipe->ws_size +
-                              (uint64_t(half) * G + (c - c0)) * (pipe->slot_static + pipe->slot_esc);
-                uint8_t* esc = st + pipe->slot_static;
-                zipccl_status r;
-                if (pass == 0) {
-                    zipccl_segment_t segs[kMaxPeers];
-                    for (int p = 0; p < P; p++) {
-                        segs[p].src = static_cast<const uint16_t*>(peer_src[p]) + off;
-                        segs[p].n = m;
-                        segs[p].plan = plans[p];
-                    }
-                    r = zipccl_compress(segs, P, st, pipe->slot_static, esc, pipe->slot_esc, ws, pipe->ws_size,
-                                        nullptr, status, pipe->sa);
-                } else {
-                    const void* sin[kMaxPeers];
-                    const void* ein[kMaxPeers];
-                    uint64_t eb[kMaxPeers];
-                    for (int p = 0; p < P; p++) {
-                        sin[p] = st + uint64_t(p) * static_bytes_of(m);
-                        ein[p] = esc;
-                        eb[p] = pipe->slot_esc;
-                    }
-                    r = zipccl_decompress_accumulate(sin, ein, eb, P, m, static_cast<const uint16_t*>(local) + off,
-                                                     static_cast<uint16_t*>(dst) + off, status, pipe->sb);
-                }
-                if (r != ZIPCCL_OK) return r;
+        // compress the group on stream a: chunk c is encoded by the launch that places
+        // chunk c - 1 (each launch is one kernel of both roles), the group's last chunk
+        // placed by a launch of its own
+        CArgsP prev;
+        bool have_prev = false;
+        for (uint64_t c = c0; c < c1; c++) {
+            const uint64_t off = c * pipe->chunk;
+            const uint64_t m = std::min(pipe->chunk, n - off);
+            uint8_t* st = slots + (uint64_t(half) * G + (c - c0)) * slot_bytes;
+            CArgs a;
+            std::memset(&a, 0, sizeof(a));
+            for (int p = 0; p < P; p++) {
+                CSeg& g = a.seg[p];
+                g.src = static_cast<const uint16_t*>(peer_src[p]) + off;
+                g.n = uint32_t(m);
+                pack_table(plans[p], g.table_lo, g.table_hi);
             }
-            if (pass == 0) {
-                if (hipEventRecord(pipe->compressed[half], pipe->sa) != hipSuccess ||
-                    hipStreamWaitEvent(pipe->sb, pipe->compressed[half], 0) != hipSuccess)
-                    return ZIPCCL_ERR_HIP;
+            zipccl_status r = prepare_compress(a, P, st, pipe->slot_static, st + pipe->slot_static, pipe->slot_esc,
+                                               pipe->scratch + (c & 1) * pipe->ws_size, pipe->ws_size, nullptr,
+                                               status);
+            if (r != ZIPCCL_OK) return r;
+            if (!a.direct) {   // positions need the scan kernel: plain launches
+                if (hipError_t e = launch_compress(a, sa)) return hip_status(e);
+                continue;
             }
+            const CArgsP cur = chunk_args(a);
+            CArgsP none;
+            std::memset(&none, 0, sizeof(none));
+            if (hipError_t e = launch_encode_place(cur, have_prev ? prev : none, sa)) return hip_status(e);
+            prev = cur;
+            have_prev = true;
         }
-        if (hipEventRecord(pipe->reduced[half], pipe->sb) != hipSuccess) return ZIPCCL_ERR_HIP;
+        if (have_prev) {
+            CArgsP none;
+            std::memset(&none, 0, sizeof(none));
+            if (hipError_t e = launch_encode_place(none, prev, sa)) return hip_status(e);
+        }
+        if (hipEventRecord(pipe->compressed[half], sa) != hipSuccess ||
+            hipStreamWaitEvent(sb, pipe->compressed[half], 0) != hipSuccess)
+            return ZIPCCL_ERR_HIP;
+        // reduce the group on stream b
+        for (uint64_t c = c0; c < c1; c++) {
+            const uint64_t off = c * pipe->chunk;
+            const uint64_t m = std::min(pipe->chunk, n - off);
+            uint8_t* st = slots + (uint64_t(half) * G + (c - c0)) * slot_bytes;
+            const void* sin[kMaxPeers];
+            const void* ein[kMaxPeers];
+            uint64_t eb[kMaxPeers];
+            for (int p = 0; p < P; p++) {
+                sin[p] = st + uint64_t(p) * static_bytes_of(m);
+                ein[p] = st + pipe->slot_static;
+                eb[p] = pipe->slot_esc;
+            }
+            zipccl_status r = zipccl_decompress_accumulate(sin, ein, eb, P, m, static_cast<const uint16_t*>(local) + off,
+                                                           static_cast<uint16_t*>(dst) + off, status, sb);
+            if (r != ZIPCCL_OK) return r;
+        }
+        if (hipEventRecord(pipe->reduced[half], sb) != hipSuccess) return ZIPCCL_ERR_HIP;
         pipe->reduced_recorded[half] = true;
     }
     return ZIPCCL_OK;

@@ -52,8 +52,9 @@ struct CSeg {              // compress: one segment
     uint32_t pad;
 };
 
-struct CArgs {
-    CSeg seg[kMaxSegs];
+template <int kSegs>
+struct CArgsN {
+    CSeg seg[kSegs];
     uint8_t* esc;
     uint64_t esc_cap;
     uint32_t* counts;      // workspace: escapes per half-block slot
@@ -68,7 +69,11 @@ struct CArgs {
     uint32_t direct;       // 1: the place kernel computes positions from unit_counts
 };
 
+using CArgs = CArgsN<kMaxSegs>;    // one compress call
+using CArgsP = CArgsN<kMaxPeers>;  // one chunk of the pipeline: a segment per peer
+
 static_assert(sizeof(CArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+static_assert(2 * sizeof(CArgsP) + 16 <= 4096, "the fused encode + place launch takes two chunks' arguments");
 
 struct DSeg {              // decompress: one segment
     const uint8_t* src;    // static part
@@ -105,7 +110,10 @@ __host__ __device__ inline uint64_t planes_off(uint64_t n) { return 128 + 512 * 
 __host__ __device__ inline uint64_t offsets_off(uint64_t n) { return planes_off(n) + round128(192 * tiles_of(n)); }
 __host__ __device__ inline uint64_t static_bytes_of(uint64_t n) { return offsets_off(n) + round128(4 * blocks_of(n)); }
 
-hipError_t launch_compress(const CArgs& a, hipStream_t s);   // encode + finalize
+hipError_t launch_compress(const CArgs& a, hipStream_t s);   // encode + place
+// One launch that places chunk `place` (encoded by an earlier launch on the stream) and
+// encodes chunk `enc`; either may have no units.  Both need direct == 1.
+hipError_t launch_encode_place(const CArgsP& enc, const CArgsP& place, hipStream_t s);
 hipError_t launch_decompress(const DArgs& a, hipStream_t s);
 hipError_t launch_accumulate(const AArgs& a, hipStream_t s);
 

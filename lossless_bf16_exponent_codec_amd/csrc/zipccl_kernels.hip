@@ -336,8 +336,8 @@ __device__ inline void stage_tile_escapes(const TileEsc& te, uint32_t r, uint8_t
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
 // planes, the escape count (to workspace slot gh) and the escape exponents in value
 // order in s_esc; zero padding after the segment's last half block.
-template <bool kFull>
-__device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
+template <bool kFull, class Args>
+__device__ inline uint32_t encode_half(const Args& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
                                        uint32_t lane, const uint8_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
     const uint32_t n = sg.n;
@@ -389,14 +389,14 @@ __device__ inline uint32_t encode_half(const CArgs& a, const CSeg& sg, uint32_t 
 // Encode: one workgroup per unit of 4 blocks, one half block per wave.  No workgroup
 // waits for another: each wave writes its tiles' A bytes and planes and its escape
 // count; the unit's escape exponents go, in value order, to the unit's staging area.
-__global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
+template <class Args>
+__device__ inline void encode_unit(const Args& a, uint32_t unit)
 {
     __shared__ uint8_t s_lut[256];
     __shared__ __attribute__((aligned(16))) uint8_t s_esc[kEncWaves][kHalf];
 
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t unit = blockIdx.x;
     const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, unit);
     const CSeg& sg = a.seg[s];
     const uint32_t n = sg.n;
@@ -467,6 +467,8 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a)
     if (!active && lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
     if (ballot(bad_row) && lane == 0) or_status(a.status, ZIPCCL_STATUS_BAD_INDEX);
 }
+
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a) { encode_unit(a, blockIdx.x); }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
 __device__ inline void write_header(const CSeg& sg, uint32_t lane, uint32_t n_esc, uint32_t esc_offset)
@@ -575,7 +577,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
 // Copies len bytes from LDS (src) to esc[p + off ...], lane l writing bytes l, l + 64, ...
 // so that each store instruction covers 64 consecutive bytes.  Bytes at or past esc_cap
 // are dropped (returns true if there were any).
-__device__ inline bool copy_run(const CArgs& a, const uint8_t* src, uint32_t p, uint32_t off, uint32_t len,
+template <class Args>
+__device__ inline bool copy_run(const Args& a, const uint8_t* src, uint32_t p, uint32_t off, uint32_t len,
                                 uint32_t lane)
 {
     uint8_t* dst = a.esc + p + off;
@@ -595,7 +598,8 @@ __device__ inline bool copy_run(const CArgs& a, const uint8_t* src, uint32_t p, 
 // the wave's 1 KB LDS buffer, holding the first 512 staged bytes; more (rare) are
 // brought from the unit's staging area (stage) 1 KB at a time, 16 bytes per lane.
 // Returns true if a byte fell at or past esc_cap.
-__device__ inline bool place_unit_escapes(const CArgs& a, uint8_t* lds, const uint8_t* stage, uint32_t p,
+template <class Args>
+__device__ inline bool place_unit_escapes(const Args& a, uint8_t* lds, const uint8_t* stage, uint32_t p,
                                           uint32_t m, uint32_t lane)
 {
     bool over = copy_run(a, lds, p, 0, min(m, 512u), lane);
@@ -613,7 +617,8 @@ __device__ inline bool place_unit_escapes(const CArgs& a, uint8_t* lds, const ui
 // Offset-table entry of block gb (launch-wide) of segment sg (index s), whose escapes
 // occupy [p0, p2) (base = the segment's first escape); the segment header from the
 // segment's last block, and the headers of empty segments next to it.
-__device__ inline void place_block_tables(const CArgs& a, const CSeg& sg, int s, uint32_t gb, uint32_t p0,
+template <class Args>
+__device__ inline void place_block_tables(const Args& a, const CSeg& sg, int s, uint32_t gb, uint32_t p0,
                                           uint32_t p2, uint32_t base, uint32_t lane)
 {
     const uint32_t K = uint32_t(blocks_of(sg.n));
@@ -681,14 +686,15 @@ constexpr uint32_t kPlaceUnits = 8;
 constexpr uint32_t kPlaceThreads = 64 * kPlaceUnits;
 constexpr uint32_t kPrefixLoads = kDirectPrefixMaxUnits / (4 * kPlaceThreads);   // uint4 loads per thread
 
-__global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a)
+template <class Args>
+__device__ inline void place_group(const Args& a, uint32_t group)
 {
     __shared__ uint32_t s_red[2][kPlaceUnits];
     __shared__ uint32_t s_ucnt[kPlaceUnits];
     __shared__ __attribute__((aligned(16))) uint8_t s_head[kPlaceUnits][1024];   // staged escapes, per wave
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t u_first = blockIdx.x * kPlaceUnits;
+    const uint32_t u_first = group * kPlaceUnits;
     const uint32_t unit = u_first + wave;
     const bool active = unit < a.total_units;
     const uint32_t slot0 = unit * kEncWaves;
@@ -764,6 +770,21 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
         place_block_tables(a, sg, s, sg.block0 + b0 + k, p0, p2, base, lane);
         p = p2;
     }
+}
+
+__global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a) { place_group(a, blockIdx.x); }
+
+// Two consecutive chunks of the pipeline in one launch: the first place_groups
+// workgroups place chunk p (its encode ran in an earlier launch on the same stream, and
+// it uses the other workspace), the rest encode chunk e.  The place work, a few
+// microseconds of mostly latency, then runs beside the next chunk's encode instead of
+// in a launch of its own.
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void encode_place_kernel(const CArgsP e, const CArgsP p, uint32_t place_groups)
+{
+    static_assert(kEncThreads == kPlaceThreads, "both roles use the same workgroup size");
+    if (blockIdx.x < place_groups) place_group(p, blockIdx.x);
+    else encode_unit(e, blockIdx.x - place_groups);
 }
 
 // --------------------------------------------------------------------------------
@@ -1205,6 +1226,15 @@ hipError_t launch_compress(const CArgs& a, hipStream_t s)
         if (a.total_blocks > 0)
             hipLaunchKernelGGL(place_kernel, dim3((a.total_blocks + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_place(const CArgsP& enc, const CArgsP& place, hipStream_t s)
+{
+    const uint32_t groups = (place.total_units + kPlaceUnits - 1) / kPlaceUnits;
+    const uint32_t grid = groups + enc.total_units;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(encode_place_kernel, dim3(grid), dim3(kEncThreads), 0, s, enc, place, groups);
     return hipGetLastError();
 }
 
