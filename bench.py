@@ -355,7 +355,18 @@ def bench_moe_gather(torch, Z, W, rounds):
     s0["gather"].run(plans)
     torch.cuda.synchronize()
     st_g, esc_g = s0["st"].clone(), s0["esc"][:int(n_esc[-1].item())].clone()
-    pm = batched_ms(torch, permute, 2, rounds)
+    # torch's row gather, timed launch by launch (median); at the copy ceiling a permute
+    # of these bytes could not take less than 2 x 235 MB / (5 TB/s), ~94 us
+    pm_all = []
+    for k in range(2 * rounds):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        permute(k)
+        e1.record()
+        torch.cuda.synchronize()
+        pm_all.append(e0.elapsed_time(e1))
+    pm = median(pm_all)
     cp = batched_ms(torch, lambda k: sets[k % 2]["compress"].run(plans), 2, rounds)
     permute(0)
     s0["compress"].run(plans)
