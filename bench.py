@@ -223,11 +223,21 @@ def bench_rs(torch, Z, W, iters):
 
     comp = [Z.PreparedCompress([p[c * chunk:(c + 1) * chunk] for p in peers], static[c * P * S:(c + 1) * P * S],
                                esc[c * P * chunk:(c + 1) * P * chunk], ws, n_esc[c], status) for c in range(nch)]
+    # the same 32 calls through zipccl_compress_chunks: one launch per chunk, each placing
+    # the chunk before it
+    ws2 = torch.zeros(2 * Z.workspace_size(P * chunk, P), dtype=torch.uint8, device="cuda")
+    comp_seq = Z.PreparedCompressChunks([[p[c * chunk:(c + 1) * chunk] for p in peers] for c in range(nch)],
+                                        [static[c * P * S:(c + 1) * P * S] for c in range(nch)],
+                                        [esc[c * P * chunk:(c + 1) * P * chunk] for c in range(nch)], ws2,
+                                        n_esc.view(-1), status)
     acc = [Z.PreparedAccumulate([static.data_ptr() + (c * P + p) * S for p in range(P)],
                                 [esc.data_ptr() + c * P * chunk] * P, chunk, local[c * chunk:], dst[c * chunk:],
                                 status, esc_bytes=[P * chunk] * P) for c in range(nch)]
 
     def compress_all():
+        comp_seq.run(plans)
+
+    def compress_calls():
         for c in range(nch):
             comp[c].run(plans)
 
@@ -246,6 +256,12 @@ def bench_rs(torch, Z, W, iters):
         accumulate_all()
         ta.stop(e)
     c_ms, a_ms = median(tc.ms()), median(ta.ms())
+    tp = Timer(torch)
+    for _ in range(iters):
+        e = tp.start()
+        compress_calls()
+        tp.stop(e)
+    cp_ms = median(tp.ms())
     total_esc = int(n_esc[:, -1].sum().item())
     static_total = nch * P * S
     comp_moved = 2 * P * n + static_total + total_esc
@@ -270,6 +286,7 @@ def bench_rs(torch, Z, W, iters):
         "compress_us": round(c_ms * 1e3, 1),
         "compress_GBps": round(2 * P * n / (c_ms * 1e-3) / 1e9, 1),
         "compress_hbm_frac": round(comp_moved / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "compress_separate_calls_us": round(cp_ms * 1e3, 1),
         "accumulate_us": round(a_ms * 1e3, 1),
         "accumulate_GBps_bf16_in": round(2 * P * n / (a_ms * 1e-3) / 1e9, 1),
         "accumulate_hbm_frac": round(acc_moved / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

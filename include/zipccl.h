@@ -136,6 +136,28 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
                               void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
                               uint64_t* n_esc_out, uint32_t* status, void* stream);
 
+/* A sequence of nchunks independent compress calls on one stream, as the chunked
+ * pipeline of the CCCL page's pipeline section issues them: chunk k is what
+ *   zipccl_compress(segs + k * nseg, nseg, static_out[k], static_cap[k], esc_out[k],
+ *                   esc_cap[k], ..., n_esc_out + k * (nseg + 1), status, stream)
+ * writes, byte for byte (each chunk's escapes and esc_offsets are its own), but one
+ * kernel launch places chunk k - 1 while it encodes chunk k, so the place work of one
+ * chunk overlaps the encode of the next: nchunks + 1 launches instead of 2 * nchunks.
+ *   segs        host array of nchunks * nseg segments, chunk after chunk; 1 <= nseg <=
+ *               ZIPCCL_MAX_PEERS
+ *   static_out, static_cap, esc_out, esc_cap   host arrays of nchunks entries
+ *   workspace   device, 256-byte aligned, at least 2 * zipccl_workspace_size(v, nseg)
+ *               bytes where v is the most values in one chunk (consecutive chunks use
+ *               its two halves in turn)
+ *   n_esc_out   optional device u64[nchunks * (nseg + 1)]
+ * Every chunk is checked before anything is enqueued.  nchunks == 0 does nothing.
+ * Errors: as zipccl_compress, per chunk; INVALID also for nseg outside 1..ZIPCCL_MAX_PEERS
+ * or nchunks < 0. */
+zipccl_status zipccl_compress_chunks(const zipccl_segment_t* segs, int nseg, int nchunks, void* const* static_out,
+                                     const uint64_t* static_cap, void* const* esc_out, const uint64_t* esc_cap,
+                                     void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
+                                     uint32_t* status, void* stream);
+
 /* One segment whose values are rows of a row-major BF16 matrix picked by index: the
  * MoE all-to-all dispatch payload of one destination (S2.D), compressed where the
  * tokens lie instead of after a permute copy.  The segment's values are rows

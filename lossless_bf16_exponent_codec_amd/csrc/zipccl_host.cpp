@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 #include <new>
 
 #include "zipccl.h"
@@ -192,13 +193,11 @@ zipccl_status check_compress_buffers(int nseg, void* static_out, void* workspace
 
 }  // namespace
 
-zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
-                              void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
-                              uint64_t* n_esc_out, uint32_t* status, void* stream)
+namespace {
+
+// Segments of a plain (contiguous) compress call into a.seg.
+zipccl_status fill_segments(CArgs& a, const zipccl_segment_t* segs, int nseg)
 {
-    if (!segs) return ZIPCCL_ERR_INVALID;
-    if (zipccl_status r = check_compress_buffers(nseg, static_out, workspace, n_esc_out, status)) return r;
-    CArgs a;
     std::memset(&a, 0, sizeof(a));
     for (int s = 0; s < nseg; s++) {
         const zipccl_segment_t& g = segs[s];
@@ -211,8 +210,74 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
         c.n = uint32_t(g.n);
         pack_table(g.plan, c.table_lo, c.table_hi);
     }
+    return ZIPCCL_OK;
+}
+
+// Launches prepared chunk calls in order on one stream.  A chunk whose positions the
+// place kernel computes itself (direct) is placed by the launch that encodes the next
+// such chunk; the last one by a launch of its own.
+zipccl_status launch_chunks(const std::vector<CArgs>& calls, hipStream_t stream)
+{
+    CArgsP prev, none;
+    std::memset(&none, 0, sizeof(none));
+    bool have_prev = false;
+    for (const CArgs& a : calls) {
+        if (!a.direct || a.nseg > kMaxPeers) {   // scan-kernel positions or many segments: its own launches
+            if (hipError_t e = launch_compress(a, stream)) return hip_status(e);
+            continue;
+        }
+        const CArgsP cur = chunk_args(a);
+        if (hipError_t e = launch_encode_place(cur, have_prev ? prev : none, stream)) return hip_status(e);
+        prev = cur;
+        have_prev = true;
+    }
+    if (have_prev)
+        if (hipError_t e = launch_encode_place(none, prev, stream)) return hip_status(e);
+    return ZIPCCL_OK;
+}
+
+}  // namespace
+
+zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
+                              void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
+                              uint64_t* n_esc_out, uint32_t* status, void* stream)
+{
+    if (!segs) return ZIPCCL_ERR_INVALID;
+    if (zipccl_status r = check_compress_buffers(nseg, static_out, workspace, n_esc_out, status)) return r;
+    CArgs a;
+    if (zipccl_status r = fill_segments(a, segs, nseg)) return r;
     return compress_segments(a, nseg, static_out, static_cap, esc_out, esc_cap, workspace, workspace_bytes,
                              n_esc_out, status, stream);
+}
+
+zipccl_status zipccl_compress_chunks(const zipccl_segment_t* segs, int nseg, int nchunks, void* const* static_out,
+                                     const uint64_t* static_cap, void* const* esc_out, const uint64_t* esc_cap,
+                                     void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
+                                     uint32_t* status, void* stream)
+{
+    if (nchunks < 0 || nseg < 1 || nseg > kMaxPeers) return ZIPCCL_ERR_INVALID;
+    if (nchunks == 0) return ZIPCCL_OK;
+    if (!segs || !static_out || !static_cap || !esc_out || !esc_cap || !workspace) return ZIPCCL_ERR_INVALID;
+    if (!aligned(workspace, 256)) return ZIPCCL_ERR_ALIGN;
+    // two workspaces: consecutive chunks alternate
+    const uint64_t half = (workspace_bytes / 2) & ~uint64_t(255);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    std::vector<CArgs> calls;   // every chunk is checked before anything is enqueued
+    try {
+        calls.resize(size_t(nchunks));
+    } catch (...) {
+        return ZIPCCL_ERR_SIZE;
+    }
+    for (int k = 0; k < nchunks; k++) {
+        uint64_t* ne = n_esc_out ? n_esc_out + uint64_t(k) * (nseg + 1) : nullptr;
+        if (zipccl_status r = check_compress_buffers(nseg, static_out[k], ws, ne, status)) return r;
+        CArgs& a = calls[size_t(k)];
+        if (zipccl_status r = fill_segments(a, segs + uint64_t(k) * nseg, nseg)) return r;
+        if (zipccl_status r = prepare_compress(a, nseg, static_out[k], static_cap[k], esc_out[k], esc_cap[k],
+                                               ws + (k & 1) * half, half, ne, status))
+            return r;
+    }
+    return launch_chunks(calls, static_cast<hipStream_t>(stream));
 }
 
 zipccl_status zipccl_compress_gather(const zipccl_gather_segment_t* segs, int nseg, void* static_out,
@@ -434,43 +499,30 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
         // the group two hand-offs back used these slots: its reduction must be done
         if (pipe->reduced_recorded[half] && hipStreamWaitEvent(sa, pipe->reduced[half], 0) != hipSuccess)
             return ZIPCCL_ERR_HIP;
-        // compress the group on stream a: chunk c is encoded by the launch that places
-        // chunk c - 1 (each launch is one kernel of both roles), the group's last chunk
-        // placed by a launch of its own
-        CArgsP prev;
-        bool have_prev = false;
+        // compress the group on stream a (one launch per chunk: each places the chunk
+        // before it while it encodes its own)
+        zipccl_segment_t segs[16 * kMaxPeers];
+        void* st_out[16];
+        void* esc_out[16];
+        uint64_t st_cap[16], esc_cap[16];
         for (uint64_t c = c0; c < c1; c++) {
-            const uint64_t off = c * pipe->chunk;
+            const uint64_t k = c - c0, off = c * pipe->chunk;
             const uint64_t m = std::min(pipe->chunk, n - off);
-            uint8_t* st = slots + (uint64_t(half) * G + (c - c0)) * slot_bytes;
-            CArgs a;
-            std::memset(&a, 0, sizeof(a));
+            uint8_t* st = slots + (uint64_t(half) * G + k) * slot_bytes;
             for (int p = 0; p < P; p++) {
-                CSeg& g = a.seg[p];
+                zipccl_segment_t& g = segs[k * P + p];
                 g.src = static_cast<const uint16_t*>(peer_src[p]) + off;
-                g.n = uint32_t(m);
-                pack_table(plans[p], g.table_lo, g.table_hi);
+                g.n = m;
+                g.plan = plans[p];
             }
-            zipccl_status r = prepare_compress(a, P, st, pipe->slot_static, st + pipe->slot_static, pipe->slot_esc,
-                                               pipe->scratch + (c & 1) * pipe->ws_size, pipe->ws_size, nullptr,
-                                               status);
-            if (r != ZIPCCL_OK) return r;
-            if (!a.direct) {   // positions need the scan kernel: plain launches
-                if (hipError_t e = launch_compress(a, sa)) return hip_status(e);
-                continue;
-            }
-            const CArgsP cur = chunk_args(a);
-            CArgsP none;
-            std::memset(&none, 0, sizeof(none));
-            if (hipError_t e = launch_encode_place(cur, have_prev ? prev : none, sa)) return hip_status(e);
-            prev = cur;
-            have_prev = true;
+            st_out[k] = st;
+            st_cap[k] = pipe->slot_static;
+            esc_out[k] = st + pipe->slot_static;
+            esc_cap[k] = pipe->slot_esc;
         }
-        if (have_prev) {
-            CArgsP none;
-            std::memset(&none, 0, sizeof(none));
-            if (hipError_t e = launch_encode_place(none, prev, sa)) return hip_status(e);
-        }
+        if (zipccl_status r = zipccl_compress_chunks(segs, P, int(c1 - c0), st_out, st_cap, esc_out, esc_cap,
+                                                     pipe->scratch, 2 * pipe->ws_size, nullptr, status, sa))
+            return r;
         if (hipEventRecord(pipe->compressed[half], sa) != hipSuccess ||
             hipStreamWaitEvent(sb, pipe->compressed[half], 0) != hipSuccess)
             return ZIPCCL_ERR_HIP;

@@ -71,6 +71,10 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_workspace_size.argtypes = [u64, i32]
     lib.zipccl_compress.restype = i32
     lib.zipccl_compress.argtypes = [ctypes.POINTER(SegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp, vp]
+    lib.zipccl_compress_chunks.restype = i32
+    lib.zipccl_compress_chunks.argtypes = [ctypes.POINTER(SegmentT), i32, i32, ctypes.POINTER(vp),
+                                           ctypes.POINTER(u64), ctypes.POINTER(vp), ctypes.POINTER(u64), vp, u64,
+                                           vp, vp, vp]
     lib.zipccl_compress_gather.restype = i32
     lib.zipccl_compress_gather.argtypes = [ctypes.POINTER(GatherSegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp,
                                            vp]
@@ -175,6 +179,38 @@ def compress(segments, static_out, esc_out, workspace, n_esc_out=None, status=No
     rc = _lib.zipccl_compress(arr, nseg, _ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap,
                               _ptr(workspace), _nbytes(workspace), _ptr(n_esc_out), _ptr(status), _stream(stream))
     _check(rc, "zipccl_compress")
+
+
+class PreparedCompressChunks:
+    """A zipccl_compress_chunks call over fixed buffers, marshalled once.  chunks: a list
+    of per-chunk lists of bf16 device tensors (the same number in each); static_outs /
+    esc_outs: per-chunk uint8 device tensors.  run(plans) uses plans[i] for segment i of
+    every chunk."""
+
+    def __init__(self, chunks, static_outs, esc_outs, workspace, n_esc_out=None, status=None, stream=None):
+        self.nchunks, self.nseg = len(chunks), len(chunks[0])
+        self._arr = (SegmentT * (self.nchunks * self.nseg))()
+        for k, tensors in enumerate(chunks):
+            if len(tensors) != self.nseg:
+                raise ValueError("every chunk needs the same number of segments")
+            for i, t in enumerate(tensors):
+                e = self._arr[k * self.nseg + i]
+                e.src = _ptr(t) if t.numel() else None
+                e.n = t.numel()
+        C = self.nchunks
+        sp = (ctypes.c_void_p * C)(*[_ptr(t) for t in static_outs])
+        sc = (ctypes.c_uint64 * C)(*[_nbytes(t) for t in static_outs])
+        ep = (ctypes.c_void_p * C)(*[_ptr(t) for t in esc_outs])
+        ec = (ctypes.c_uint64 * C)(*[_nbytes(t) for t in esc_outs])
+        self._args = (sp, sc, ep, ec, _ptr(workspace), _nbytes(workspace), _ptr(n_esc_out), _ptr(status),
+                      _stream(stream))
+        self._keep = (chunks, static_outs, esc_outs, workspace, n_esc_out, status)
+
+    def run(self, plans):
+        for k in range(self.nchunks):
+            for i in range(self.nseg):
+                self._arr[k * self.nseg + i].plan = plans[i]
+        _check(_lib.zipccl_compress_chunks(self._arr, self.nseg, self.nchunks, *self._args), "zipccl_compress_chunks")
 
 
 def compress_gather(segments, static_out, esc_out, workspace, n_esc_out=None, status=None, stream=None,

@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
                  "zipccl_compressed_size", "zipccl_static_size", "zipccl_workspace_size",
                  "zipccl_pipeline_create", "zipccl_pipeline_reduce", "zipccl_pipeline_destroy",
                  "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many",
-                 "zipccl_decompress_shards", "zipccl_compress_gather"]:
+                 "zipccl_decompress_shards", "zipccl_compress_gather", "zipccl_compress_chunks"]:
         assert want in names
 
 
@@ -140,6 +140,21 @@ def test_argument_errors_before_any_launch(Z):
     seg[0].n = 100
     seg[0].plan.table[3] = seg[0].plan.table[2]
     assert L.zipccl_compress(seg, 1, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_INVALID
+    segs2 = (Z.SegmentT * 2)()
+    for e in segs2:
+        e.src, e.n, e.plan = 0x10000, 100, Z.plan(sigma=1.0)
+    vp_ = ctypes.c_void_p
+    so, eo = (vp_ * 2)(fake, fake), (vp_ * 2)(fake, fake)
+    sc, ec = (ctypes.c_uint64 * 2)(1 << 20, 1 << 20), (ctypes.c_uint64 * 2)(100, 100)
+    cws = 2 * Z.workspace_size(100, 1)
+    assert L.zipccl_compress_chunks(segs2, 1, 0, None, None, None, None, None, 0, None, None, None) == Z.OK
+    assert L.zipccl_compress_chunks(segs2, 0, 2, so, sc, eo, ec, fake, cws, None, None, None) == Z.ERR_INVALID
+    assert L.zipccl_compress_chunks(segs2, 17, 2, so, sc, eo, ec, fake, cws, None, None, None) == Z.ERR_INVALID
+    assert L.zipccl_compress_chunks(segs2, 1, -1, so, sc, eo, ec, fake, cws, None, None, None) == Z.ERR_INVALID
+    assert L.zipccl_compress_chunks(segs2, 1, 2, so, sc, eo, ec, fake + 16, cws, None, None, None) == Z.ERR_ALIGN
+    assert L.zipccl_compress_chunks(segs2, 1, 2, so, sc, eo, ec, fake, 8, None, None, None) == Z.ERR_SIZE
+    so[1] = fake + 64                    # the second chunk's static part misaligned: nothing enqueued
+    assert L.zipccl_compress_chunks(segs2, 1, 2, so, sc, eo, ec, fake, cws, None, None, None) == Z.ERR_ALIGN
     g = (Z.GatherSegmentT * 1)()
     g[0].src, g[0].src_rows, g[0].row_len, g[0].rows, g[0].nrows, g[0].plan = 0x10000, 100, 7168, 0x20000, 10, p
     gws = Z.workspace_size(71680, 1)

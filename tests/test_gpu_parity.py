@@ -451,6 +451,42 @@ def scan_path(monkeypatch):
     yield
 
 
+def compress_chunks_vs_oracle(Z, chunks_bits, plans):
+    C, S = len(chunks_bits), len(chunks_bits[0])
+    tens = [[dev_bf16(b) for b in ch] for ch in chunks_bits]
+    sizes = [[b.size for b in ch] for ch in chunks_bits]
+    st_sizes = [sum(Z.static_size(n) for n in sz) for sz in sizes]
+    statics = [torch.full((max(t, 1),), POISON, dtype=torch.uint8, device="cuda") for t in st_sizes]
+    escs = [torch.full((max(sum(sz), 1),), POISON, dtype=torch.uint8, device="cuda") for sz in sizes]
+    ws = torch.full((2 * Z.workspace_size(max(sum(sz) for sz in sizes), S),), POISON, dtype=torch.uint8,
+                    device="cuda")
+    n_esc = torch.full((C * (S + 1),), -1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Z.PreparedCompressChunks(tens, statics, escs, ws, n_esc, status).run(plans)
+    torch.cuda.synchronize()
+    ne = n_esc.cpu().numpy()
+    for k in range(C):
+        r = dict(status=int(status.item()), n_esc=ne[k * (S + 1):(k + 1) * (S + 1)],
+                 static_h=statics[k].cpu().numpy()[:st_sizes[k]], esc_h=escs[k].cpu().numpy())
+        check_against_oracle(Z, chunks_bits[k], plans, r)
+
+
+def chunk_sequence():
+    # 6 chunks of 3 segments: full, ragged, empty and tiny segments; the last chunk short
+    shapes = [[1 << 20, 1 << 20, 1 << 20], [70001, 4096, 1], [0, 5000, 16384 * 3], [1 << 20, 1 << 20, 1 << 20],
+              [513, 0, 0], [12345, 8, 100000]]
+    sig = [0.02, 1.0, 1e-3]
+    return [[W.gaussian_bf16(n, sig[i], 1000 + 10 * k + i) for i, n in enumerate(ch)] for k, ch in enumerate(shapes)]
+
+
+def test_compress_chunks_matches_per_call_oracle(Z):
+    compress_chunks_vs_oracle(Z, chunk_sequence(), [Z.plan(sigma=s) for s in (0.02, 1.0, 1e-3)])
+
+
+def test_compress_chunks_scan_path(Z, scan_path):
+    compress_chunks_vs_oracle(Z, chunk_sequence()[:3], [Z.plan(sigma=s) for s in (0.02, 1.0, 1e-3)])
+
+
 def test_scan_path_many_segments(Z, scan_path):
     rng = np.random.default_rng(6)
     segs, plans = [], []
