@@ -234,6 +234,12 @@ def bench_rs(torch, Z, W, iters):
                                 [esc.data_ptr() + c * P * chunk] * P, chunk, local[c * chunk:], dst[c * chunk:],
                                 status, esc_bytes=[P * chunk] * P) for c in range(nch)]
 
+    # the 32 decode-accumulates through zipccl_decompress_accumulate_chunks (18 chunks of
+    # 7 peers per launch)
+    acc_seq = Z.PreparedAccumulateChunks([static.data_ptr() + (c * P + p) * S for c in range(nch) for p in range(P)],
+                                         [esc.data_ptr() + c * P * chunk for c in range(nch) for _ in range(P)],
+                                         P, chunk, n, local, dst, status, esc_bytes=[P * chunk] * (P * nch))
+
     def compress_all():
         comp_seq.run(plans)
 
@@ -242,6 +248,9 @@ def bench_rs(torch, Z, W, iters):
             comp[c].run(plans)
 
     def accumulate_all():
+        acc_seq.run()
+
+    def accumulate_calls():
         for c in range(nch):
             acc[c].run()
 
@@ -256,12 +265,15 @@ def bench_rs(torch, Z, W, iters):
         accumulate_all()
         ta.stop(e)
     c_ms, a_ms = median(tc.ms()), median(ta.ms())
-    tp = Timer(torch)
+    tp, tq = Timer(torch), Timer(torch)
     for _ in range(iters):
         e = tp.start()
         compress_calls()
         tp.stop(e)
-    cp_ms = median(tp.ms())
+        e = tq.start()
+        accumulate_calls()
+        tq.stop(e)
+    cp_ms, ap_ms = median(tp.ms()), median(tq.ms())
     total_esc = int(n_esc[:, -1].sum().item())
     static_total = nch * P * S
     comp_moved = 2 * P * n + static_total + total_esc
@@ -290,6 +302,7 @@ def bench_rs(torch, Z, W, iters):
         "accumulate_us": round(a_ms * 1e3, 1),
         "accumulate_GBps_bf16_in": round(2 * P * n / (a_ms * 1e-3) / 1e9, 1),
         "accumulate_hbm_frac": round(acc_moved / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "accumulate_separate_calls_us": round(ap_ms * 1e3, 1),
         "pipeline_wall_us": round(wall * 1e6, 1),
         "pipeline_GBps_bf16_in": round(2 * P * n / wall / 1e9, 1),
         "ratio": round(2 * P * n / (static_total + total_esc), 5),

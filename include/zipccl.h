@@ -225,6 +225,19 @@ zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const v
                                            const uint64_t* esc_bytes, int npeers, uint64_t n,
                                            const void* local, void* dst, uint32_t* status, void* stream);
 
+/* zipccl_decompress_accumulate over consecutive chunks, in as few launches as the kernel
+ * arguments allow (128 / npeers chunks each): chunk c covers values [c * chunk,
+ * min(n, (c + 1) * chunk)) of local and dst, and peer p's compressed segment of it is at
+ * static_in[c * npeers + p] with escapes in esc_in[c * npeers + p] (esc_bytes[...] long).
+ * The result is that of one zipccl_decompress_accumulate call per chunk.  static_in,
+ * esc_in and esc_bytes are host arrays of ceil(n / chunk) * npeers entries; chunk is a
+ * multiple of 4096.  Every entry is checked before anything is enqueued; n == 0 does
+ * nothing.  Errors: INVALID (npeers outside 1..ZIPCCL_MAX_PEERS, chunk 0 or not a
+ * multiple of 4096, NULL pointers), ALIGN, SIZE (n >= 2^32), HIP. */
+zipccl_status zipccl_decompress_accumulate_chunks(const void* const* static_in, const void* const* esc_in,
+                                                  const uint64_t* esc_bytes, int npeers, uint64_t chunk, uint64_t n,
+                                                  const void* local, void* dst, uint32_t* status, void* stream);
+
 /* Chunked two-stream pipeline over a reduce-scatter receive share (S2.D; the chunked
  * multi-stream overlap of the CCCL page's pipeline section).  Chunks of `chunk` values
  * of every peer shard are compressed on stream_a (one compress call per chunk, one
@@ -232,7 +245,8 @@ zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const v
  * chunk).  The streams hand chunks over in groups of G (a power of two, at most 16, the
  * smallest with G * npeers * chunk >= 2^25 values, since each event record or wait costs
  * the host microseconds); a ring of two groups of chunk buffers lets group g + 1
- * compress while group g is reduced.  The scratch memory is caller-owned device memory
+ * compress while group g is reduced.  Each group is compressed by one
+ * zipccl_compress_chunks call and reduced by one zipccl_decompress_accumulate_chunks call.  The scratch memory is caller-owned device memory
  * of zipccl_pipeline_scratch_size() bytes: the compress workspace plus 2 * G chunk
  * buffers of npeers * (static_size(chunk) + chunk) bytes.
  * Overlapping transfers of the compressed chunks would sit between the two streams. */

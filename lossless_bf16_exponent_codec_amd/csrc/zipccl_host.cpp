@@ -393,8 +393,51 @@ zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const v
     a.dst = static_cast<uint16_t*>(dst);
     a.status = status;
     a.n = uint32_t(n);
+    a.chunk = uint32_t(n);
     a.npeers = npeers;
+    a.nchunks = 1;
     return hip_status(launch_accumulate(a, static_cast<hipStream_t>(stream)));
+}
+
+zipccl_status zipccl_decompress_accumulate_chunks(const void* const* static_in, const void* const* esc_in,
+                                                  const uint64_t* esc_bytes, int npeers, uint64_t chunk, uint64_t n,
+                                                  const void* local, void* dst, uint32_t* status, void* stream)
+{
+    if (npeers < 1 || npeers > kMaxPeers || chunk == 0 || chunk % kBlock != 0) return ZIPCCL_ERR_INVALID;
+    if (n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+    if (n == 0) return ZIPCCL_OK;
+    if (!static_in || !esc_in || !esc_bytes || !local || !dst) return ZIPCCL_ERR_INVALID;
+    if (!aligned(local, 16) || !aligned(dst, 16) || (status && !aligned(status, 4))) return ZIPCCL_ERR_ALIGN;
+    const uint64_t nchunks = (n + chunk - 1) / chunk;
+    for (uint64_t i = 0; i < nchunks * uint64_t(npeers); i++) {   // everything checked before any launch
+        if (!static_in[i] || (esc_bytes[i] > 0 && !esc_in[i])) return ZIPCCL_ERR_INVALID;
+        if (!aligned(static_in[i], 128)) return ZIPCCL_ERR_ALIGN;
+    }
+    // as many chunks per launch as the kernel arguments hold
+    const uint64_t per_launch = uint64_t(kMaxAccSlots / npeers);
+    for (uint64_t c0 = 0; c0 < nchunks; c0 += per_launch) {
+        const uint64_t c1 = std::min(nchunks, c0 + per_launch);
+        AArgs a;
+        std::memset(&a, 0, sizeof(a));
+        for (uint64_t c = c0; c < c1; c++) {
+            for (int p = 0; p < npeers; p++) {
+                const uint64_t i = c * npeers + p, j = (c - c0) * npeers + p;
+                a.st[j] = static_cast<const uint8_t*>(static_in[i]);
+                a.esc[j] = static_cast<const uint8_t*>(esc_in[i] ? esc_in[i] : static_in[i]);
+                a.esc_bytes[j] = esc_in[i] ? esc_bytes[i] : 0;
+            }
+        }
+        const uint64_t first = c0 * chunk;
+        a.local = static_cast<const uint16_t*>(local) + first;
+        a.dst = static_cast<uint16_t*>(dst) + first;
+        a.status = status;
+        a.n = uint32_t(std::min(n, c1 * chunk) - first);
+        a.chunk = uint32_t(chunk);
+        a.npeers = npeers;
+        a.nchunks = int32_t(c1 - c0);
+        if (hipError_t e = launch_accumulate(a, static_cast<hipStream_t>(stream))) return hip_status(e);
+    }
+    return ZIPCCL_OK;
 }
 
 // ---------------------------------------------------------------------------------
@@ -526,23 +569,25 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
         if (hipEventRecord(pipe->compressed[half], sa) != hipSuccess ||
             hipStreamWaitEvent(sb, pipe->compressed[half], 0) != hipSuccess)
             return ZIPCCL_ERR_HIP;
-        // reduce the group on stream b
+        // reduce the group on stream b: one decode-accumulate launch for its chunks
+        const void* sin[16 * kMaxPeers];
+        const void* ein[16 * kMaxPeers];
+        uint64_t eb[16 * kMaxPeers];
         for (uint64_t c = c0; c < c1; c++) {
-            const uint64_t off = c * pipe->chunk;
-            const uint64_t m = std::min(pipe->chunk, n - off);
-            uint8_t* st = slots + (uint64_t(half) * G + (c - c0)) * slot_bytes;
-            const void* sin[kMaxPeers];
-            const void* ein[kMaxPeers];
-            uint64_t eb[kMaxPeers];
+            const uint64_t k = c - c0;
+            const uint64_t m = std::min(pipe->chunk, n - c * pipe->chunk);
+            uint8_t* st = slots + (uint64_t(half) * G + k) * slot_bytes;
             for (int p = 0; p < P; p++) {
-                sin[p] = st + uint64_t(p) * static_bytes_of(m);
-                ein[p] = st + pipe->slot_static;
-                eb[p] = pipe->slot_esc;
+                sin[k * P + p] = st + uint64_t(p) * static_bytes_of(m);
+                ein[k * P + p] = st + pipe->slot_static;
+                eb[k * P + p] = pipe->slot_esc;
             }
-            zipccl_status r = zipccl_decompress_accumulate(sin, ein, eb, P, m, static_cast<const uint16_t*>(local) + off,
-                                                           static_cast<uint16_t*>(dst) + off, status, sb);
-            if (r != ZIPCCL_OK) return r;
         }
+        const uint64_t first = c0 * pipe->chunk, m_all = std::min(n, c1 * pipe->chunk) - first;
+        if (zipccl_status r = zipccl_decompress_accumulate_chunks(
+                sin, ein, eb, P, pipe->chunk, m_all, static_cast<const uint16_t*>(local) + first,
+                static_cast<uint16_t*>(dst) + first, status, sb))
+            return r;
         if (hipEventRecord(pipe->reduced[half], sb) != hipSuccess) return ZIPCCL_ERR_HIP;
         pipe->reduced_recorded[half] = true;
     }

@@ -91,16 +91,25 @@ struct DArgs {
     uint32_t total_units;
 };
 
-struct AArgs {             // decompress + accumulate
-    const uint8_t* st[kMaxPeers];
-    const uint8_t* esc[kMaxPeers];
-    uint64_t esc_bytes[kMaxPeers];
+// Decompress + accumulate over nchunks consecutive chunks of `chunk` values (the last
+// may be shorter; chunk is a multiple of kBlock unless nchunks == 1): chunk c covers
+// values [c * chunk, min(n, (c + 1) * chunk)) of local / dst and has one compressed
+// segment per peer, at st[c * npeers + p] with escapes in esc[c * npeers + p].
+constexpr int kMaxAccSlots = 128;
+
+struct AArgs {
+    const uint8_t* st[kMaxAccSlots];
+    const uint8_t* esc[kMaxAccSlots];
+    uint64_t esc_bytes[kMaxAccSlots];
     const uint16_t* local;
     uint16_t* dst;
     uint32_t* status;
-    uint32_t n;
+    uint32_t n;             // values of all chunks together
+    uint32_t chunk;
     int32_t npeers;
+    int32_t nchunks;
 };
+static_assert(sizeof(AArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 __host__ __device__ inline uint64_t round128(uint64_t v) { return (v + 127) & ~uint64_t(127); }
 __host__ __device__ inline uint64_t tiles_of(uint64_t n) { return (n + kTile - 1) / kTile; }

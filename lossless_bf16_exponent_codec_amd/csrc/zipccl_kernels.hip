@@ -941,9 +941,19 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     __shared__ uint8_t s_esc[kAccWaves][kTile + kEscPad];      // a tile's escapes when they lie further on
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t n = a.n, P = uint32_t(a.npeers);
+    // the workgroup's chunk, and its block within the chunk
+    const uint32_t P = uint32_t(a.npeers);
+    const uint32_t bpc = uint32_t(blocks_of(a.chunk));
+    const uint32_t c = blockIdx.x / bpc;
+    const uint32_t b = blockIdx.x - c * bpc;
+    const uint64_t first = uint64_t(c) * a.chunk;
+    const uint32_t n = uint32_t(min<uint64_t>(a.chunk, a.n - first));
+    const uint8_t* const* peer_st = a.st + c * P;
+    const uint8_t* const* peer_esc = a.esc + c * P;
+    const uint64_t* peer_eb = a.esc_bytes + c * P;
+    const uint16_t* local = a.local + first;
+    uint16_t* dst = a.dst + first;
     const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
-    const uint32_t b = blockIdx.x;
     const uint32_t t = b * 8 + wave;
     const bool has_tile = t < T;
     const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
@@ -952,26 +962,26 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 
     // ---- requests ----
     // Every lane issues the same vector loads, unconditionally (addresses of what does
-    // not exist are clamped into peer 0's static part, which is at least 896 bytes), so
+    // not exist are clamped into peer 0's static part of the chunk, which is at least 896 bytes), so
     // that the compiler can wait for exactly the loads each step needs: the transposes
     // start once the plane dwords are in while the A bytes, the local values and the
     // escape heads are still on their way.  Plane dwords first, then A bytes, then local.
-    const uint8_t* const safe = a.st[0];
+    const uint8_t* const safe = peer_st[0];
     const uint32_t tl = has_tile ? t : T - 1;   // T >= 1: a launch has at least one block
     const uint32_t pdl = pdw == ~0u ? 0u : pdw;   // lanes with p = 3: any dword (bits unused)
     uint32_t pw[kPeers];
     uint2 Ap[kPeers];
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        const uint8_t* st = a.st[uint32_t(p) < P ? p : 0];
+        const uint8_t* st = peer_st[uint32_t(p) < P ? p : 0];
         pw[p] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * tl) + pdl);
     }
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        const uint8_t* st = a.st[uint32_t(p) < P ? p : 0];
+        const uint8_t* st = peer_st[uint32_t(p) < P ? p : 0];
         Ap[p] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * tl + 8 * lane));
     }
-    uint4 lv = load_nt(reinterpret_cast<const uint4*>(nvalid == 8 ? reinterpret_cast<const uint8_t*>(a.local + i0)
+    uint4 lv = load_nt(reinterpret_cast<const uint4*>(nvalid == 8 ? reinterpret_cast<const uint8_t*>(local + i0)
                                                                     : safe));
 
     // ---- this wave's share of the header checks: peers wave, wave + 8 ----
@@ -983,15 +993,15 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
         const uint8_t* src = safe;   // with m = 0 every lane reads byte 0 of it
         uint32_t m = 0;
         if (p < P) {
-            const uint8_t* st = a.st[p];
-            const SegHeader hd = read_header(st, n, a.esc_bytes[p]);
+            const uint8_t* st = peer_st[p];
+            const SegHeader hd = read_header(st, n, peer_eb[p]);
             const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
             uint32_t first = 0, last = 0;
             const bool ok = hd.ok && block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
             const uint64_t e = hd.esc_offset + first;
             if (lane == 0) s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, ok ? 1u : 0u};
             m = ok ? min(last - first, kAccBlkHead) : 0u;
-            if (m > 0) src = a.esc[p] + e;
+            if (m > 0) src = peer_esc[p] + e;
         }
         // the block's first escapes, requested now so that they arrive while the tiles
         // are transposed (written to LDS just before the barrier): lane l fetches bytes
@@ -1057,7 +1067,7 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
     }
     bad = __builtin_amdgcn_readfirstlane(bad);
     // a lane holding the last values of the segment (fewer than 8) reads them now
-    if (nvalid > 0 && nvalid < 8) lv = load_lane(a.local, t, lane, n);
+    if (nvalid > 0 && nvalid < 8) lv = load_lane(local, t, lane, n);
 
     // ---- decode and add, peers in order ----
     float acc[8];
@@ -1075,7 +1085,7 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
                 // rare (escape-heavy tables): the tile's escapes go past the block's
                 // first 512; stage them in the wave's own LDS slot
                 const uint64_t e = uint64_t(s_peer[p].esc_hi) << 32 | s_peer[p].esc_lo;
-                const uint8_t* esc = a.esc[p] + e + before[p];
+                const uint8_t* esc = peer_esc[p] + e + before[p];
                 for (uint32_t k = lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
                 wave_lds_sync();
                 tile_esc = esc_lds;
@@ -1101,10 +1111,10 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
 #pragma unroll
     for (int j = 0; j < 8; j++) r[j] = round_bf16_bits(acc[j]);
     if (nvalid == 8) {
-        store_nt(reinterpret_cast<uint4*>(a.dst + i0),
+        store_nt(reinterpret_cast<uint4*>(dst + i0),
                  make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16)));
     } else {
-        for (uint32_t j = 0; j < nvalid; j++) a.dst[i0 + j] = uint16_t(r[j]);
+        for (uint32_t j = 0; j < nvalid; j++) dst[i0 + j] = uint16_t(r[j]);
     }
 }
 
@@ -1247,7 +1257,9 @@ hipError_t launch_decompress(const DArgs& a, hipStream_t s)
 
 hipError_t launch_accumulate(const AArgs& a, hipStream_t s)
 {
-    const uint32_t grid = uint32_t(blocks_of(a.n));
+    if (a.n == 0 || a.nchunks < 1) return hipSuccess;
+    const uint64_t last = a.n - uint64_t(a.nchunks - 1) * a.chunk;   // values of the last chunk
+    const uint32_t grid = uint32_t(uint64_t(a.nchunks - 1) * blocks_of(a.chunk) + blocks_of(last));
     if (grid == 0) return hipSuccess;
     // every peer slot of the instance issues its loads, so the instance is the smallest
     // that holds npeers

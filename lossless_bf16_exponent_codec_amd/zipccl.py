@@ -86,6 +86,9 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_decompress_accumulate.restype = i32
     lib.zipccl_decompress_accumulate.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64), i32,
                                                  u64, vp, vp, vp, vp]
+    lib.zipccl_decompress_accumulate_chunks.restype = i32
+    lib.zipccl_decompress_accumulate_chunks.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64),
+                                                        i32, u64, u64, vp, vp, vp, vp]
     lib.zipccl_pipeline_scratch_size.restype = u64
     lib.zipccl_pipeline_scratch_size.argtypes = [i32, u64]
     lib.zipccl_pipeline_create.restype = i32
@@ -365,6 +368,26 @@ class PreparedAccumulate:
 
 def pipeline_scratch_size(npeers: int, chunk: int) -> int:
     return int(_lib.zipccl_pipeline_scratch_size(npeers, chunk))
+
+
+class PreparedAccumulateChunks:
+    """A zipccl_decompress_accumulate_chunks call over fixed buffers, marshalled once.
+    static_ins / esc_ins / esc_bytes: per-(chunk, peer) entries, chunk-major (device
+    tensors or raw addresses); n values of local and dst in chunks of `chunk`."""
+
+    def __init__(self, static_ins, esc_ins, npeers: int, chunk: int, n: int, local, dst, status=None,
+                 stream=None, esc_bytes=None):
+        m = len(static_ins)
+        sp = (ctypes.c_void_p * m)(*[_ptr(t) for t in static_ins])
+        ep = (ctypes.c_void_p * m)(*[_ptr(t) for t in esc_ins])
+        if esc_bytes is None:
+            esc_bytes = [_nbytes(t) for t in esc_ins]
+        eb = (ctypes.c_uint64 * m)(*[int(v) for v in esc_bytes])
+        self._args = (sp, ep, eb, npeers, chunk, n, _ptr(local), _ptr(dst), _ptr(status), _stream(stream))
+        self._keep = (static_ins, esc_ins, local, dst, status)
+
+    def run(self):
+        _check(_lib.zipccl_decompress_accumulate_chunks(*self._args), "zipccl_decompress_accumulate_chunks")
 
 
 class Pipeline:

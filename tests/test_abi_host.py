@@ -34,7 +34,8 @@ def test_header_declares_the_abi():
                  "zipccl_compressed_size", "zipccl_static_size", "zipccl_workspace_size",
                  "zipccl_pipeline_create", "zipccl_pipeline_reduce", "zipccl_pipeline_destroy",
                  "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many",
-                 "zipccl_decompress_shards", "zipccl_compress_gather", "zipccl_compress_chunks"]:
+                 "zipccl_decompress_shards", "zipccl_compress_gather", "zipccl_compress_chunks",
+                 "zipccl_decompress_accumulate_chunks"]:
         assert want in names
 
 
@@ -195,6 +196,19 @@ def test_argument_errors_before_any_launch(Z):
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 17, 10, fake, fake, None, None) == Z.ERR_INVALID
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 1, 1 << 32, fake, fake, None, None) == Z.ERR_SIZE
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 1, 10, fake + 2, fake, None, None) == Z.ERR_ALIGN
+    sp2, ep2 = (vp * 2)(fake, fake), (vp * 2)(fake, fake)
+    eb2 = (ctypes.c_uint64 * 2)(10, 10)
+    acc_chunks = L.zipccl_decompress_accumulate_chunks
+    assert acc_chunks(sp2, ep2, eb2, 1, 4096, 0, None, None, None, None) == Z.OK
+    assert acc_chunks(sp2, ep2, eb2, 0, 4096, 8192, fake, fake, None, None) == Z.ERR_INVALID
+    assert acc_chunks(sp2, ep2, eb2, 1, 4000, 8192, fake, fake, None, None) == Z.ERR_INVALID
+    assert acc_chunks(sp2, ep2, eb2, 1, 4096, 1 << 32, fake, fake, None, None) == Z.ERR_SIZE
+    assert acc_chunks(sp2, ep2, eb2, 1, 4096, 8192, fake + 2, fake, None, None) == Z.ERR_ALIGN
+    sp2[1] = fake + 64                   # the second chunk's static part: nothing is enqueued
+    assert acc_chunks(sp2, ep2, eb2, 1, 4096, 8192, fake, fake, None, None) == Z.ERR_ALIGN
+    ep2[1] = None
+    sp2[1] = fake
+    assert acc_chunks(sp2, ep2, eb2, 1, 4096, 8192, fake, fake, None, None) == Z.ERR_INVALID
     h = vp()
     assert L.zipccl_pipeline_create(7, 1000, fake, 1 << 30, None, None, ctypes.byref(h)) == Z.ERR_INVALID
     assert L.zipccl_pipeline_create(7, 4096, fake + 16, 1 << 30, None, None, ctypes.byref(h)) == Z.ERR_ALIGN

@@ -315,6 +315,54 @@ def test_accumulate_corrupt_peer(Z):
     assert int(status.item()) & Z.STATUS_CORRUPT
 
 
+def accumulate_chunks_setup(Z, npeers, chunk, n, seed):
+    peers = [W.gaussian_bf16(n, 1e-3, seed + p) for p in range(npeers)]
+    local = W.gaussian_bf16(n, 1e-3, seed + 99)
+    plans = [Z.plan(sigma=1e-3)] * npeers
+    comps, sin, ein, eb = [], [], [], []
+    for c0 in range(0, n, chunk):
+        segs = [p[c0:c0 + chunk] for p in peers]
+        r = gpu_compress(Z, segs, plans)
+        comps.append(r)
+        S = Z.static_size(segs[0].size)
+        for p in range(npeers):
+            sin.append(r["static"].data_ptr() + p * S)
+            ein.append(r["esc"].data_ptr())
+            eb.append(r["esc"].numel())
+    return peers, local, plans, comps, sin, ein, eb
+
+
+@pytest.mark.parametrize("npeers,chunk,n", [(3, 8192, 5 * 8192 + 1000),   # ragged last chunk
+                                             (16, 4096, 9 * 4096),          # 8 chunks per launch: two launches
+                                             (7, 1 << 20, (1 << 20) + 4096)])
+def test_accumulate_chunks_matches_oracle(Z, npeers, chunk, n):
+    print(f"accumulate chunks P={npeers} chunk={chunk} n={n}", flush=True)
+    peers, local, plans, comps, sin, ein, eb = accumulate_chunks_setup(Z, npeers, chunk, n, 1300)
+    dst = torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Z.PreparedAccumulateChunks(sin, ein, npeers, chunk, n, dev_bf16(local), dst, status, esc_bytes=eb).run()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    got = host_u16(dst)
+    want = oracle_accumulate(Z, peers, plans, local)
+    assert np.array_equal(got, want), first_diff(got, want)
+
+
+def test_accumulate_chunks_corrupt_chunk(Z):
+    npeers, chunk, n = 2, 8192, 4 * 8192
+    peers, local, plans, comps, sin, ein, eb = accumulate_chunks_setup(Z, npeers, chunk, n, 1400)
+    comps[2]["static"][Z.static_size(chunk) + 8] ^= 4   # chunk 2, peer 1: header n
+    dst = torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Z.PreparedAccumulateChunks(sin, ein, npeers, chunk, n, dev_bf16(local), dst, status, esc_bytes=eb).run()
+    torch.cuda.synchronize()
+    assert int(status.item()) & Z.STATUS_CORRUPT
+    got = host_u16(dst)
+    want = oracle_accumulate(Z, peers, plans, local)
+    want[2 * chunk:3 * chunk] = 0xAAAA
+    assert np.array_equal(got, want), first_diff(got, want)
+
+
 @pytest.mark.parametrize("npeers,chunk,n", [(2, 4096, 40 * 4096 + 100),   # 3 hand-offs of 16 chunks: the ring wraps
                                              (3, 8192, 5 * 8192),          # fewer chunks than one hand-off
                                              (16, 1 << 20, (2 << 20) + 4097)])   # hand-offs of 2, ragged last chunk
