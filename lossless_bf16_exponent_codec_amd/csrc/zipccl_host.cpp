@@ -1,9 +1,12 @@
-// Host layer of libzipccl: plans, sizes, argument validation, launches and the
-// two-stream chunk pipeline.  Every device-side step runs in zipccl_kernels.hip.
+// Host layer of libzipccl: plans, sizes, argument validation, launches, chunk
+// sequences and the two-stream chunk pipeline.  Every device-side step runs in
+// zipccl_kernels.hip.
 //
 // Method: "ZipCCL: Efficient Lossless Data Compression of Communication Collectives
 // for Accelerating LLM Training" (gist.science explanation page), S2.A (sigma-derived
-// exponent table), S2.B (3-bit codes + escapes), S2.D (reduce-scatter local reduction).
+// exponent table), S2.B (3-bit codes + escapes), S2.D (two-phase MoE all-to-all and the
+// reduce-scatter's local reduction), S4 (the all-gather); the chunked multi-stream
+// pipeline follows the CCCL page's pipeline section.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -4,7 +4,8 @@
 // for Accelerating LLM Training" (gist.science explanation page), S2.B (split into
 // sign+mantissa and exponent; top-7 exponents -> 3-bit codes, others -> escape code 0
 // with the exponent in a separate array), S2.C (128-byte aligned sections, codes as
-// three 1-bit planes), S2.D (local reduction on the reduce-scatter receive side).
+// three 1-bit planes), S2.D (local reduction on the reduce-scatter receive side; the
+// MoE dispatch, whose token rows the encoder can read by index).
 // The byte layout (format version 1) is documented in include/zipccl.h.
 //
 // Work decomposition.  A tile is 512 values: lane l of a wave holds values 8l..8l+7,
@@ -27,9 +28,12 @@
 //     workspace) and place (escape positions from the units' counts, compacted escapes,
 //     offset tables, headers); above 2^28 values a one-workgroup scan kernel computes
 //     the positions and a per-block place kernel follows.  The workspace keeps no state.
+//     A sequence of chunk calls uses one launch per chunk that places the chunk before
+//     it while it encodes its own (encode_place_kernel: two roles by workgroup index).
 //   * Decompress: one half block per wave, one barrier to share the escape count of
-//     the first half of each block.  Decode-accumulate: one workgroup per block, one
-//     wave per tile, all peers of a tile in one wave.
+//     the first half of each block; each segment has its own escape buffer.
+//     Decode-accumulate: one workgroup per block, one wave per tile, all peers of a
+//     tile in one wave; one launch may cover several chunks, each with its own peers.
 #include "zipccl_internal.h"
 #include "zipccl.h"
 
