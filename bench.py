@@ -468,8 +468,10 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out
              "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra")
 PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{counter} -o run -- "
            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-extra")
-OUR_KERNELS = ("encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel", "decompress_kernel",
-               "accumulate_kernel")
+RS_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/stats_rs -o rs -- "
+                "python3 bench.py --only rs_512m")
+OUR_KERNELS = ("encode_place_kernel", "encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel",
+               "decompress_kernel", "accumulate_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 GIB = 1 << 30
 
@@ -487,20 +489,29 @@ def short_kernel_name(name):
     return COPY_KERNEL if COPY_KERNEL in name else None
 
 
-def summarize_stats(csv_path, out_path):
-    """profiles/ text from rocprofv3 --stats (kernel_stats.csv) of TRACE_CMD."""
+def summarize_stats(csv_path, out_path, rs=False):
+    """profiles/ text from rocprofv3 --stats (kernel_stats.csv) of TRACE_CMD (or, with rs,
+    of RS_TRACE_CMD)."""
     import csv
     rows = [r for r in csv.DictReader(open(csv_path)) if short_kernel_name(r["Name"]) in OUR_KERNELS]
-    lines = ["# Kernel durations, bucket_64m (16 x 4 Mi BF16 values, one table per layer)", "",
+    title = ("# Kernel durations, rs_512m (7 peers x 64 Mi BF16 values in 32 chunks of 2 Mi)" if rs else
+             "# Kernel durations, bucket_64m (16 x 4 Mi BF16 values, one table per layer)")
+    lines = [title, "",
              "Command (from the repository root on the GPU host; rocprofv3's own averages):", "",
-             "    " + TRACE_CMD, "",
+             "    " + (RS_TRACE_CMD if rs else TRACE_CMD), "",
              f"Kernel source sha256: `{kernel_source_sha256()}`", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    lines += ["", "Calls include the warmup and verification round trips; all launches are of the",
-              "bucket workload (compress: encode_kernel + place_direct_kernel, decompress: decompress_kernel)."]
+    if rs:
+        lines += ["", "The chunk compresses run as separate calls (encode_kernel + place_direct_kernel, 7",
+                  "segments of 2 Mi values each) and through zipccl_compress_chunks and the pipeline",
+                  "(encode_place_kernel: one chunk placed while the next is encoded); decode-accumulate",
+                  "runs one chunk per launch and 18 chunks per launch (accumulate_kernel)."]
+    else:
+        lines += ["", "Calls include the warmup and verification round trips; all launches are of the",
+                  "bucket workload (compress: encode_kernel + place_direct_kernel, decompress: decompress_kernel)."]
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
@@ -578,12 +589,19 @@ def main(argv=None) -> int:
                     help="write a profiles/ summary of a rocprofv3 --stats run and exit")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="write a profiles/ summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-rs-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of a rocprofv3 --stats run of --only rs_512m and exit")
+    ap.add_argument("--only", default=None,
+                    help="run one of the other workloads alone (for profiling) and print its figures")
     args = ap.parse_args(argv)
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
         return 0
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return 0
+    if args.summarize_rs_stats:
+        summarize_stats(*args.summarize_rs_stats, rs=True)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and this build has no "
@@ -597,6 +615,16 @@ def main(argv=None) -> int:
     from lossless_bf16_exponent_codec_amd import workloads as W
     from lossless_bf16_exponent_codec_amd import zipccl as Z
     torch.cuda.set_device(0)
+
+    if args.only:
+        runners = {"rs_512m": lambda: bench_rs(torch, Z, W, 5),
+                   "allgather_16x4m": lambda: bench_allgather(torch, Z, W, 5),
+                   "moe_routed_16384x7168": lambda: bench_moe_gather(torch, Z, W, 5)}
+        if args.only not in runners:
+            print(f"--only takes one of {sorted(runners)}", file=sys.stderr)
+            return 2
+        print(json.dumps({"workload": args.only, **runners[args.only]()}), flush=True)
+        return 0
 
     log("generating bucket_64m")
     wl = W.bucket_64m()

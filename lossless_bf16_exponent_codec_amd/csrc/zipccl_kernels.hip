@@ -937,7 +937,8 @@ struct PeerBlock {
 // wave knows where its tile's escapes start, then the peers are decoded and added in
 // order.
 template <int kPeers>
-__global__ __launch_bounds__(kAccThreads) void accumulate_kernel(const AArgs a)
+__global__ __launch_bounds__(kAccThreads) __attribute__((amdgpu_waves_per_eu(kPeers <= 8 ? 6 : 4)))
+void accumulate_kernel(const AArgs a)
 {
     __shared__ uint32_t s_cnt[kPeers][kAccWaves];
     __shared__ PeerBlock s_peer[kPeers];
