@@ -141,6 +141,21 @@ def test_many_segments_one_launch(Z):
     round_trip(Z, segs, plans)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_segments_random_tables(Z, seed):
+    # random bit patterns (mostly escapes) and random explicit tables, up to 64 segments
+    # of random sizes in one launch
+    rng = np.random.default_rng(1000 + seed)
+    nseg = int(rng.integers(1, 65))
+    segs, plans = [], []
+    for _ in range(nseg):
+        n = int(rng.choice([0, 1, 8, 511, 4097, int(rng.integers(0, 40000))]))
+        segs.append(rng.integers(0, 65536, n, dtype=np.uint32).astype(np.uint16))
+        plans.append(Z.plan(table=sorted(int(v) for v in rng.choice(np.arange(1, 255), 7, replace=False))))
+    print(f"random segments seed={seed} nseg={nseg} n={sum(x.size for x in segs)}", flush=True)
+    round_trip(Z, segs, plans)
+
+
 def test_determinism_and_workspace_reuse(Z):
     # the workspace needs no initialisation and carries nothing between calls: start
     # from garbage and alternate two different batches through one workspace

@@ -109,6 +109,27 @@ def test_sizes_and_edges(n):
     assert np.array_equal(O.decompress(st, esc, n), x)
 
 
+from hypothesis import given, settings, strategies as st_
+
+
+@settings(max_examples=60, deadline=None)
+@given(n=st_.integers(0, 20000), seed=st_.integers(0, 2**32 - 1),
+       table=st_.sets(st_.integers(1, 254), min_size=7, max_size=7))
+def test_round_trip_random_bits_and_tables(n, seed, table):
+    # any bit patterns and any 7-exponent table: decode(encode(x)) == x, the escape count
+    # is the brute-force count of exponents outside the table, and the size is the
+    # static part plus one byte per escape
+    x = np.random.default_rng(seed).integers(0, 65536, n, dtype=np.uint32).astype(np.uint16)
+    t = O.plan_table(sorted(table))
+    st, esc, k = O.compress(x, t)
+    e = (x.astype(np.int64) >> 7) & 0xFF
+    outside = ~np.isin(e, np.array(sorted(table), np.int64))
+    assert k == int(outside.sum()) and esc.size == k
+    assert np.array_equal(esc, e[outside].astype(np.uint8))
+    assert st.size == O.static_size(n)
+    assert np.array_equal(O.decompress(st, esc, n), x)
+
+
 def test_size_is_eleven_bits_per_value_plus_escapes_and_metadata():
     # section 2.B: 3-bit code + 8-bit sign+mantissa = 11 bits per value; escapes add a
     # full 8-bit exponent each.  For n a multiple of 128 blocks the only other bytes are
