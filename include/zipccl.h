@@ -203,14 +203,19 @@ zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, co
  * slices of the gathered tensor).  static_in, esc_in and esc_bytes are host arrays of
  * nseg entries: static_in[s] is the shard's static part (device, 128-byte aligned,
  * static_size(segs[s].n) bytes as zipccl_compress wrote it) and esc_in[s] (esc_bytes[s]
- * long, NULL when 0) the escape buffer its header's esc_offset refers to.  A shard whose
- * header or offset table is inconsistent with segs[s].n or esc_bytes[s] is not decoded
- * and ZIPCCL_STATUS_CORRUPT is set; no read leaves the given buffers.
- * Errors: INVALID (NULL arrays or pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS), ALIGN,
- * SIZE (a segment n >= 2^32), HIP. */
+ * long, NULL when 0) the escape buffer its header's esc_offset refers to, or, with
+ * ZIPCCL_SHARDS_ESC_AT_FIRST in flags, a buffer that starts at the shard's first escape
+ * (the two-phase all-to-all of S2.D: a receiver gets each sender's static part and that
+ * segment's escape bytes, esc_offset .. esc_offset + n_esc of the sender's escape buffer,
+ * and keeps them on their own).  A shard whose header or offset table is inconsistent
+ * with segs[s].n or esc_bytes[s] is not decoded and ZIPCCL_STATUS_CORRUPT is set; no read
+ * leaves the given buffers.
+ * Errors: INVALID (NULL arrays or pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS, unknown
+ * flags), ALIGN, SIZE (a segment n >= 2^32), HIP. */
+#define ZIPCCL_SHARDS_ESC_AT_FIRST 1u
 zipccl_status zipccl_decompress_shards(const void* const* static_in, const void* const* esc_in,
                                        const uint64_t* esc_bytes, const zipccl_dsegment_t* segs, int nseg,
-                                       uint32_t* status, void* stream);
+                                       uint32_t flags, uint32_t* status, void* stream);
 
 /* Reduce-scatter receive side (S2.D): for i < n
  *   dst[i] = bf16_rne( (((f32(local[i]) + f32(peer_0[i])) + f32(peer_1[i])) + ...) )

@@ -347,9 +347,10 @@ zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, co
 
 zipccl_status zipccl_decompress_shards(const void* const* static_in, const void* const* esc_in,
                                        const uint64_t* esc_bytes, const zipccl_dsegment_t* segs, int nseg,
-                                       uint32_t* status, void* stream)
+                                       uint32_t flags, uint32_t* status, void* stream)
 {
     if (!segs || !static_in || !esc_in || !esc_bytes || nseg < 1 || nseg > kMaxSegs) return ZIPCCL_ERR_INVALID;
+    if (flags & ~ZIPCCL_SHARDS_ESC_AT_FIRST) return ZIPCCL_ERR_INVALID;
     if (status && !aligned(status, 4)) return ZIPCCL_ERR_ALIGN;
     DArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -366,6 +367,7 @@ zipccl_status zipccl_decompress_shards(const void* const* static_in, const void*
         d.dst = static_cast<uint16_t*>(g.dst);
         d.n = uint32_t(g.n);
         d.unit0 = uint32_t(units);
+        d.esc_at_first = (flags & ZIPCCL_SHARDS_ESC_AT_FIRST) ? 1u : 0u;
         units += units_of(g.n);
     }
     a.status = status;

@@ -82,6 +82,8 @@ struct DSeg {              // decompress: one segment
     uint16_t* dst;
     uint32_t n;
     uint32_t unit0;        // first workgroup unit of the segment (units of kUnit values)
+    uint32_t esc_at_first; // 1: esc points at the segment's first escape (header esc_offset ignored)
+    uint32_t pad;
 };
 
 struct DArgs {
@@ -90,6 +92,7 @@ struct DArgs {
     int32_t nseg;
     uint32_t total_units;
 };
+static_assert(sizeof(DArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Decompress + accumulate over nchunks consecutive chunks of `chunk` values (the last
 // may be shorter; chunk is a multiple of kBlock unless nchunks == 1): chunk c covers

@@ -801,8 +801,10 @@ struct SegHeader {
     uint64_t esc_offset;
 };
 
-// Reads and validates a segment header against the expected n and buffer sizes.
-__device__ inline SegHeader read_header(const uint8_t* st, uint32_t n, uint64_t esc_bytes)
+// Reads and validates a segment header against the expected n and buffer sizes.  With
+// at_first the escape buffer starts at the segment's first escape, whatever esc_offset
+// the header records (a shard received on its own).
+__device__ inline SegHeader read_header(const uint8_t* st, uint32_t n, uint64_t esc_bytes, bool at_first = false)
 {
     const uint32_t* h = reinterpret_cast<const uint32_t*>(st);
     SegHeader r;
@@ -810,7 +812,7 @@ __device__ inline SegHeader read_header(const uint8_t* st, uint32_t n, uint64_t 
     uint32_t t0 = h[4], t1 = h[5];
     uint32_t blk = h[6], tile = h[7];
     uint64_t n_esc = uint64_t(h[8]) | (uint64_t(h[9]) << 32);
-    uint64_t eoff = uint64_t(h[10]) | (uint64_t(h[11]) << 32);
+    uint64_t eoff = at_first ? 0ull : (uint64_t(h[10]) | (uint64_t(h[11]) << 32));
     uint64_t sb = uint64_t(h[12]) | (uint64_t(h[13]) << 32);
     bool ok = magic == ZIPCCL_MAGIC && ver == 1u && nlo == n && nhi == 0 && blk == kBlock && tile == kTile &&
               sb == static_bytes_of(n) && n_esc <= n && eoff <= esc_bytes && n_esc <= esc_bytes - eoff;
@@ -1172,7 +1174,7 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
     uint32_t first = 0, last = 0;
     SegHeader hd = {};
     if (active) {
-        hd = read_header(st, n, sg.esc_bytes);
+        hd = read_header(st, n, sg.esc_bytes, sg.esc_at_first != 0);
         const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
         bad = !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
     }

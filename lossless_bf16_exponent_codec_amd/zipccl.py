@@ -82,7 +82,7 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_decompress.argtypes = [vp, u64, vp, u64, ctypes.POINTER(DSegmentT), i32, vp, vp]
     lib.zipccl_decompress_shards.restype = i32
     lib.zipccl_decompress_shards.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64),
-                                             ctypes.POINTER(DSegmentT), i32, vp, vp]
+                                             ctypes.POINTER(DSegmentT), i32, ctypes.c_uint32, vp, vp]
     lib.zipccl_decompress_accumulate.restype = i32
     lib.zipccl_decompress_accumulate.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64), i32,
                                                  u64, vp, vp, vp, vp]
@@ -266,17 +266,21 @@ def decompress(static_in, esc_in, dsts, status=None, stream=None, static_bytes=N
     _check(rc, "zipccl_decompress")
 
 
-def decompress_shards(static_ins, esc_ins, dsts, status=None, stream=None, esc_bytes=None):
+SHARDS_ESC_AT_FIRST = 1
+
+
+def decompress_shards(static_ins, esc_ins, dsts, status=None, stream=None, esc_bytes=None, flags=0):
     """zipccl_decompress_shards.  static_ins / esc_ins: per-shard device tensors or raw
     device addresses (int; an escape entry may be None); dsts: bf16 device tensors, one
-    per shard (their numel is n); esc_bytes: per-shard escape buffer sizes."""
-    PreparedDecompressShards(static_ins, esc_ins, dsts, status, stream, esc_bytes).run()
+    per shard (their numel is n); esc_bytes: per-shard escape buffer sizes; flags:
+    SHARDS_ESC_AT_FIRST when each escape buffer starts at its shard's first escape."""
+    PreparedDecompressShards(static_ins, esc_ins, dsts, status, stream, esc_bytes, flags).run()
 
 
 class PreparedDecompressShards:
     """A zipccl_decompress_shards call over fixed buffers, marshalled once; run() makes it."""
 
-    def __init__(self, static_ins, esc_ins, dsts, status=None, stream=None, esc_bytes=None):
+    def __init__(self, static_ins, esc_ins, dsts, status=None, stream=None, esc_bytes=None, flags=0):
         nseg = len(dsts)
         sp = (ctypes.c_void_p * nseg)(*[_ptr(t) for t in static_ins])
         ep = (ctypes.c_void_p * nseg)(*[_ptr(t) for t in esc_ins])
@@ -287,7 +291,7 @@ class PreparedDecompressShards:
         for k, t in enumerate(dsts):
             arr[k].dst = _ptr(t) if t.numel() else None
             arr[k].n = t.numel()
-        self._args = (sp, ep, eb, arr, nseg, _ptr(status), _stream(stream))
+        self._args = (sp, ep, eb, arr, nseg, flags, _ptr(status), _stream(stream))
         self._keep = (static_ins, esc_ins, dsts, status)
 
     def run(self):

@@ -183,15 +183,16 @@ def test_argument_errors_before_any_launch(Z):
     ep = (vp * 1)(fake)
     eb = (ctypes.c_uint64 * 1)(10)
     d[0].dst = 0x10000
-    assert L.zipccl_decompress_shards(sp, ep, eb, d, 0, None, None) == Z.ERR_INVALID
-    assert L.zipccl_decompress_shards(sp, ep, eb, d, 65, None, None) == Z.ERR_INVALID
-    assert L.zipccl_decompress_shards(None, ep, eb, d, 1, None, None) == Z.ERR_INVALID
-    assert L.zipccl_decompress_shards(sp, (vp * 1)(None), eb, d, 1, None, None) == Z.ERR_INVALID   # 10 escape bytes at NULL
-    assert L.zipccl_decompress_shards((vp * 1)(fake + 64), ep, eb, d, 1, None, None) == Z.ERR_ALIGN
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 0, 0, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 65, 0, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_shards(None, ep, eb, d, 1, 0, None, None) == Z.ERR_INVALID
+    assert L.zipccl_decompress_shards(sp, (vp * 1)(None), eb, d, 1, 0, None, None) == Z.ERR_INVALID   # 10 escape bytes at NULL
+    assert L.zipccl_decompress_shards((vp * 1)(fake + 64), ep, eb, d, 1, 0, None, None) == Z.ERR_ALIGN
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 1, 2, None, None) == Z.ERR_INVALID   # unknown flag
     d[0].dst = 0x10001
-    assert L.zipccl_decompress_shards(sp, ep, eb, d, 1, None, None) == Z.ERR_ALIGN
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 1, 0, None, None) == Z.ERR_ALIGN
     d[0].dst, d[0].n = 0x10000, 1 << 32
-    assert L.zipccl_decompress_shards(sp, ep, eb, d, 1, None, None) == Z.ERR_SIZE
+    assert L.zipccl_decompress_shards(sp, ep, eb, d, 1, 1, None, None) == Z.ERR_SIZE
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 0, 10, fake, fake, None, None) == Z.ERR_INVALID
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 17, 10, fake, fake, None, None) == Z.ERR_INVALID
     assert L.zipccl_decompress_accumulate(sp, ep, eb, 1, 1 << 32, fake, fake, None, None) == Z.ERR_SIZE

@@ -446,6 +446,52 @@ def test_decompress_shards_gathers_separate_buffers(Z):
     assert np.array_equal(got, want), first_diff(got, want)
 
 
+def test_two_phase_all_to_all_on_one_gpu(Z):
+    # S senders each compress their tokens for D destinations in one gathered launch.
+    # Destination r receives, from every sender, that segment's static part (phase 1:
+    # fixed size, known from n alone) and its escape bytes (phase 2: esc_offset ..
+    # esc_offset + n_esc of the sender's escape buffer), each into a buffer of its own;
+    # device-to-device copies stand in for the transfers.  It decodes the S shards in one
+    # launch with the escape buffers starting at each shard's first escape.
+    S, D, H = 3, 4, 1024
+    rng = np.random.default_rng(77)
+    mats, routes, comps = [], [], []
+    for s in range(S):
+        tokens = int(rng.integers(200, 400))
+        mat = W.gaussian_bf16(tokens * H, 0.5, 2000 + s).reshape(tokens, H)
+        dest = rng.integers(0, D, tokens)
+        rows = [np.flatnonzero(dest == d) for d in range(D)]
+        mats.append(mat)
+        routes.append(rows)
+        comps.append(gpu_compress_gather(Z, mat, rows, [Z.plan(sigma=0.5)] * D))
+    for r in range(D):
+        recv_st, recv_esc, n_escs, dsts, want = [], [], [], [], []
+        for s in range(S):
+            c = comps[s]
+            n = len(routes[s][r]) * H
+            off_st = sum(Z.static_size(m) for m in c["sizes"][:r])
+            off_esc = int(sum(c["n_esc"][:r]))
+            k = int(c["n_esc"][r])
+            recv_st.append(c["static"][off_st:off_st + Z.static_size(n)].clone())
+            recv_esc.append(c["esc"][off_esc:off_esc + max(k, 1)].clone())
+            n_escs.append(k)
+            dsts.append(torch.full((n,), POISON16, dtype=torch.int16, device="cuda").view(torch.bfloat16))
+            want.append(mats[s][routes[s][r]].reshape(-1))
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        Z.decompress_shards(recv_st, recv_esc, dsts, status, esc_bytes=n_escs, flags=Z.SHARDS_ESC_AT_FIRST)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        for got_t, w in zip(dsts, want):
+            got = host_u16(got_t)
+            assert np.array_equal(got, w), first_diff(got, w)
+        # the same shards without the flag: their headers point past the received bytes
+        if r > 0:
+            status.zero_()
+            Z.decompress_shards(recv_st, recv_esc, dsts, status, esc_bytes=n_escs)
+            torch.cuda.synchronize()
+            assert int(status.item()) & Z.STATUS_CORRUPT
+
+
 # ------------------------------------------------------------------------------------
 # compress of rows gathered by index (MoE dispatch without a permute copy)
 # ------------------------------------------------------------------------------------
