@@ -417,6 +417,23 @@ def bench_moe_gather(torch, Z, W, rounds):
     }
 
 
+def bench_switcher(torch, Z, W):
+    """The reduce-scatter switcher on this GPU: the codec profile on one 2 Mi-value chunk of
+    the reduce-scatter share with 7 peers, and the choice for the share's full size
+    (1 GiB of BF16 per rank over 8 ranks) on three kinds of link."""
+    wl = W.rs_512m()
+    x = to_dev(torch, wl.segments[0][:wl.extra["chunk"]])
+    prof = Z.profile_codec(x, Z.plan(sigma=wl.sigmas[0]), wl.extra["peers"])
+    links = {"xgmi_7x153GBps": Z.LinkT(153.0, 2.0, 7), "pcie5_x16_64GBps": Z.LinkT(64.0, 5.0, 1),
+             "ib_ndr_50GBps": Z.LinkT(50.0, 5.0, 1)}
+    out = {"compress_GBps": round(prof.compress_GBps, 1), "accumulate_GBps": round(prof.accumulate_GBps, 1),
+           "ratio": round(prof.ratio, 5), "ranks": 8, "bytes_per_rank": 8 * wl.extra["shard"] * 2}
+    for name, link in links.items():
+        use, tn, tz = Z.rs_choose(prof, link, 8, out["bytes_per_rank"])
+        out[name] = {"use_codec": use, "native_us": round(tn, 1), "zipped_us": round(tz, 1)}
+    return out
+
+
 def copy_ceiling(torch, iters=10):
     """A plain 1 GiB device-to-device copy: the practical HBM ceiling (read + write bytes / s)."""
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -635,6 +652,7 @@ def main(argv=None) -> int:
 
     if args.only:
         runners = {"rs_512m": lambda: bench_rs(torch, Z, W, 5),
+                   "rs_switcher": lambda: bench_switcher(torch, Z, W),
                    "allgather_16x4m": lambda: bench_allgather(torch, Z, W, 5),
                    "moe_routed_16384x7168": lambda: bench_moe_gather(torch, Z, W, 5)}
         if args.only not in runners:
@@ -727,6 +745,8 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         log("workload rs_512m")
         per["rs_512m"] = bench_rs(torch, Z, W, 5)
+        log("reduce-scatter switcher")
+        per["rs_switcher"] = bench_switcher(torch, Z, W)
         out["per_config"] = per
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, 1 thread)")

@@ -277,6 +277,47 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
 
 void zipccl_pipeline_destroy(zipccl_pipeline* pipe);
 
+/* ---- Reduce-scatter switcher (S2.D): profile once, then choose per call ----
+ * The pages' switcher measures the cluster at start-up (bandwidth, latency, compression
+ * ratio) and then picks, per reduce-scatter, the native collective or the zipped
+ * all-to-all followed by the local decode-accumulate.  The pages give no formula; the
+ * cost model below is this library's reading of that choice. */
+typedef struct zipccl_codec_profile_t {
+    double compress_GBps;     /* BF16 bytes compressed per second on this GPU */
+    double accumulate_GBps;   /* BF16 bytes of peer shards decoded and accumulated per second */
+    double ratio;             /* compressed bytes / BF16 bytes of the sample */
+} zipccl_codec_profile_t;
+
+typedef struct zipccl_link_t {
+    double bw_GBps;           /* bandwidth of one link from this rank */
+    double latency_us;        /* per message */
+    int links;                /* peers a rank sends to at once (xGMI in one node: 7; a ring: 1) */
+} zipccl_link_t;
+
+/* Device scratch bytes zipccl_profile_codec needs for a sample of n values and npeers. */
+uint64_t zipccl_profile_scratch_size(uint64_t n, int npeers);
+
+/* Measures this GPU's codec on a caller's sample (device BF16, n values, 16-byte aligned,
+ * compressed with `plan`): a compress of npeers segments (all the sample) and a
+ * decode-accumulate of npeers peer shards, each timed with HIP events over 3 launches
+ * after one warm-up, and the compressed size.  Synchronises `stream` (an initialisation
+ * call).  scratch: device, 256-byte aligned, zipccl_profile_scratch_size() bytes.
+ * Errors: INVALID (NULL pointers, n == 0, npeers outside 1..ZIPCCL_MAX_PEERS, bad plan),
+ * ALIGN, SIZE (n * npeers >= 2^32, scratch too small), HIP. */
+zipccl_status zipccl_profile_codec(const void* sample, uint64_t n, zipccl_plan_t plan, int npeers, void* scratch,
+                                   uint64_t scratch_bytes, void* stream, zipccl_codec_profile_t* out);
+
+/* Chooses for a reduce-scatter of `bytes` BF16 bytes per rank over `ranks` ranks (each
+ * rank keeps bytes / ranks).  With shard = bytes / ranks and m = ranks - 1 peers:
+ *   native  = ceil(m / links) * (latency + shard / bw)        (the reduction rides along)
+ *   zipped  = m * shard / compress + ceil(m / links) * (latency + ratio * shard / bw)
+ *             + m * shard / accumulate
+ * use_codec = zipped < native, except that tensors under 1 MiB and ratios of 1 or more
+ * always take the native path.  Host only; any output pointer may be NULL.
+ * Errors: INVALID (NULL prof or link, ranks < 2, links < 1, non-positive rates). */
+zipccl_status zipccl_rs_choose(const zipccl_codec_profile_t* prof, const zipccl_link_t* link, int ranks,
+                               uint64_t bytes, int* use_codec, double* native_us, double* zipped_us);
+
 /* Static text for a status code. */
 const char* zipccl_strerror(zipccl_status s);
 

@@ -446,6 +446,116 @@ zipccl_status zipccl_decompress_accumulate_chunks(const void* const* static_in, 
 }
 
 // ---------------------------------------------------------------------------------
+// reduce-scatter switcher: device profile and host cost model
+// ---------------------------------------------------------------------------------
+namespace {
+
+struct ProfileLayout {
+    uint64_t ws, st, esc, ne, dst, total;
+};
+
+ProfileLayout profile_layout(uint64_t n, int npeers)
+{
+    auto r256 = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+    ProfileLayout l;
+    l.ws = 0;
+    l.st = l.ws + r256(zipccl_workspace_size(n * uint64_t(npeers), npeers));
+    l.esc = l.st + r256(uint64_t(npeers) * static_bytes_of(n));
+    l.ne = l.esc + r256(uint64_t(npeers) * n);
+    l.dst = l.ne + r256(8 * uint64_t(npeers + 1));
+    l.total = l.dst + r256(2 * n);
+    return l;
+}
+
+}  // namespace
+
+uint64_t zipccl_profile_scratch_size(uint64_t n, int npeers)
+{
+    if (npeers < 1 || npeers > kMaxPeers) return 0;
+    return profile_layout(n, npeers).total;
+}
+
+zipccl_status zipccl_profile_codec(const void* sample, uint64_t n, zipccl_plan_t plan, int npeers, void* scratch,
+                                   uint64_t scratch_bytes, void* stream, zipccl_codec_profile_t* out)
+{
+    if (!sample || !scratch || !out || n == 0 || npeers < 1 || npeers > kMaxPeers || !plan_valid(plan))
+        return ZIPCCL_ERR_INVALID;
+    if (n * uint64_t(npeers) >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+    if (!aligned(sample, 16) || !aligned(scratch, 256)) return ZIPCCL_ERR_ALIGN;
+    const ProfileLayout l = profile_layout(n, npeers);
+    if (scratch_bytes < l.total) return ZIPCCL_ERR_SIZE;
+    uint8_t* base = static_cast<uint8_t*>(scratch);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    zipccl_segment_t segs[kMaxPeers];
+    const void* sin[kMaxPeers];
+    const void* ein[kMaxPeers];
+    uint64_t eb[kMaxPeers];
+    for (int p = 0; p < npeers; p++) {
+        segs[p].src = sample;
+        segs[p].n = n;
+        segs[p].plan = plan;
+        sin[p] = base + l.st + uint64_t(p) * static_bytes_of(n);
+        ein[p] = base + l.esc;
+        eb[p] = uint64_t(npeers) * n;
+    }
+    uint64_t* ne_dev = reinterpret_cast<uint64_t*>(base + l.ne);
+    auto compress = [&]() {
+        return zipccl_compress(segs, npeers, base + l.st, uint64_t(npeers) * static_bytes_of(n), base + l.esc,
+                               uint64_t(npeers) * n, base + l.ws, l.st - l.ws, ne_dev, nullptr, stream);
+    };
+    auto accumulate = [&]() {
+        return zipccl_decompress_accumulate(sin, ein, eb, npeers, n, sample, base + l.dst, nullptr, stream);
+    };
+    hipEvent_t e[4] = {};
+    for (auto& ev : e)
+        if (hipEventCreate(&ev) != hipSuccess) {
+            for (auto& x : e)
+                if (x) (void)hipEventDestroy(x);
+            return ZIPCCL_ERR_HIP;
+        }
+    zipccl_status r = compress();   // warm-up, and the compressed size
+    if (r == ZIPCCL_OK) r = accumulate();
+    constexpr int kReps = 3;
+    bool ok = r == ZIPCCL_OK && hipEventRecord(e[0], s) == hipSuccess;
+    for (int k = 0; ok && k < kReps; k++) ok = compress() == ZIPCCL_OK;
+    ok = ok && hipEventRecord(e[1], s) == hipSuccess && hipEventRecord(e[2], s) == hipSuccess;
+    for (int k = 0; ok && k < kReps; k++) ok = accumulate() == ZIPCCL_OK;
+    ok = ok && hipEventRecord(e[3], s) == hipSuccess && hipEventSynchronize(e[3]) == hipSuccess;
+    float tc = 0, ta = 0;
+    uint64_t total_esc = 0;
+    ok = ok && hipEventElapsedTime(&tc, e[0], e[1]) == hipSuccess && hipEventElapsedTime(&ta, e[2], e[3]) == hipSuccess;
+    ok = ok && hipMemcpy(&total_esc, ne_dev + npeers, sizeof(total_esc), hipMemcpyDeviceToHost) == hipSuccess;
+    for (auto& ev : e) (void)hipEventDestroy(ev);
+    if (r != ZIPCCL_OK) return r;
+    if (!ok || tc <= 0 || ta <= 0) return ZIPCCL_ERR_HIP;
+    const double bf16 = 2.0 * double(n) * npeers;   // bytes of one launch
+    out->compress_GBps = bf16 / (tc * 1e-3 / kReps) / 1e9;
+    out->accumulate_GBps = bf16 / (ta * 1e-3 / kReps) / 1e9;
+    out->ratio = (double(npeers) * double(static_bytes_of(n)) + double(total_esc)) / bf16;
+    return ZIPCCL_OK;
+}
+
+zipccl_status zipccl_rs_choose(const zipccl_codec_profile_t* prof, const zipccl_link_t* link, int ranks,
+                               uint64_t bytes, int* use_codec, double* native_us, double* zipped_us)
+{
+    if (!prof || !link || ranks < 2 || link->links < 1 || !(link->bw_GBps > 0) || !(link->latency_us >= 0) ||
+        !(prof->compress_GBps > 0) || !(prof->accumulate_GBps > 0) || !(prof->ratio > 0))
+        return ZIPCCL_ERR_INVALID;
+    const double m = ranks - 1;
+    const double shard = double(bytes) / ranks;
+    const double rounds = std::ceil(m / link->links);
+    const double native = rounds * (link->latency_us + shard / (link->bw_GBps * 1e3));
+    const double zipped = m * shard / (prof->compress_GBps * 1e3) +
+                          rounds * (link->latency_us + prof->ratio * shard / (link->bw_GBps * 1e3)) +
+                          m * shard / (prof->accumulate_GBps * 1e3);
+    const bool raw = bytes < (1ull << 20) || prof->ratio >= 1.0;
+    if (use_codec) *use_codec = (!raw && zipped < native) ? 1 : 0;
+    if (native_us) *native_us = native;
+    if (zipped_us) *zipped_us = zipped;
+    return ZIPCCL_OK;
+}
+
+// ---------------------------------------------------------------------------------
 // two-stream chunk pipeline
 // ---------------------------------------------------------------------------------
 struct zipccl_pipeline {

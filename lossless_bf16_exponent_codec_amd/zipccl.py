@@ -41,6 +41,15 @@ class GatherSegmentT(ctypes.Structure):
                 ("rows", ctypes.c_void_p), ("nrows", ctypes.c_uint64), ("plan", PlanT)]
 
 
+class CodecProfileT(ctypes.Structure):
+    _fields_ = [("compress_GBps", ctypes.c_double), ("accumulate_GBps", ctypes.c_double),
+                ("ratio", ctypes.c_double)]
+
+
+class LinkT(ctypes.Structure):
+    _fields_ = [("bw_GBps", ctypes.c_double), ("latency_us", ctypes.c_double), ("links", ctypes.c_int)]
+
+
 class DSegmentT(ctypes.Structure):
     _fields_ = [("dst", ctypes.c_void_p), ("n", ctypes.c_uint64)]
 
@@ -89,6 +98,14 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_decompress_accumulate_chunks.restype = i32
     lib.zipccl_decompress_accumulate_chunks.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(u64),
                                                         i32, u64, u64, vp, vp, vp, vp]
+    lib.zipccl_profile_scratch_size.restype = u64
+    lib.zipccl_profile_scratch_size.argtypes = [u64, i32]
+    lib.zipccl_profile_codec.restype = i32
+    lib.zipccl_profile_codec.argtypes = [vp, u64, PlanT, i32, vp, u64, vp, ctypes.POINTER(CodecProfileT)]
+    lib.zipccl_rs_choose.restype = i32
+    lib.zipccl_rs_choose.argtypes = [ctypes.POINTER(CodecProfileT), ctypes.POINTER(LinkT), i32, u64,
+                                     ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double)]
     lib.zipccl_pipeline_scratch_size.restype = u64
     lib.zipccl_pipeline_scratch_size.argtypes = [i32, u64]
     lib.zipccl_pipeline_create.restype = i32
@@ -392,6 +409,26 @@ class PreparedAccumulateChunks:
 
     def run(self):
         _check(_lib.zipccl_decompress_accumulate_chunks(*self._args), "zipccl_decompress_accumulate_chunks")
+
+
+def profile_codec(sample, plan, npeers: int, stream=None) -> CodecProfileT:
+    """zipccl_profile_codec on a bf16 device tensor (scratch allocated with torch)."""
+    n = sample.numel()
+    size = _lib.zipccl_profile_scratch_size(n, npeers)
+    scratch = torch.empty(max(size, 1), dtype=torch.uint8, device=sample.device)
+    out = CodecProfileT()
+    _check(_lib.zipccl_profile_codec(_ptr(sample), n, plan, npeers, _ptr(scratch), size, _stream(stream),
+                                     ctypes.byref(out)), "zipccl_profile_codec")
+    return out
+
+
+def rs_choose(profile: CodecProfileT, link: LinkT, ranks: int, nbytes: int):
+    """zipccl_rs_choose: (use_codec, native_us, zipped_us)."""
+    use = ctypes.c_int32()
+    t_n, t_z = ctypes.c_double(), ctypes.c_double()
+    _check(_lib.zipccl_rs_choose(ctypes.byref(profile), ctypes.byref(link), ranks, nbytes, ctypes.byref(use),
+                                 ctypes.byref(t_n), ctypes.byref(t_z)), "zipccl_rs_choose")
+    return bool(use.value), t_n.value, t_z.value
 
 
 class Pipeline:

@@ -35,7 +35,8 @@ def test_header_declares_the_abi():
                  "zipccl_pipeline_create", "zipccl_pipeline_reduce", "zipccl_pipeline_destroy",
                  "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many",
                  "zipccl_decompress_shards", "zipccl_compress_gather", "zipccl_compress_chunks",
-                 "zipccl_decompress_accumulate_chunks"]:
+                 "zipccl_decompress_accumulate_chunks", "zipccl_profile_codec", "zipccl_profile_scratch_size",
+                 "zipccl_rs_choose"]:
         assert want in names
 
 
@@ -215,3 +216,34 @@ def test_argument_errors_before_any_launch(Z):
     assert L.zipccl_pipeline_create(7, 4096, fake + 16, 1 << 30, None, None, ctypes.byref(h)) == Z.ERR_ALIGN
     assert L.zipccl_pipeline_create(7, 4096, fake, 16, None, None, ctypes.byref(h)) == Z.ERR_SIZE
     assert L.zipccl_strerror(Z.ERR_CORRUPT) == b"corrupt compressed data"
+
+
+def test_rs_switcher_cost_model(Z):
+    # a codec of ~2.5 TB/s compressing to 70 %: inside a node (7 xGMI links of ~150 GB/s
+    # each) the saved wire time does not pay for the codec; across nodes (one 25 GB/s
+    # link) it does.  Small tensors and incompressible data always go native.
+    prof = Z.CodecProfileT(2500.0, 3200.0, 0.70)
+    xgmi, ib = Z.LinkT(150.0, 5.0, 7), Z.LinkT(25.0, 5.0, 1)
+    use, tn, tz = Z.rs_choose(prof, xgmi, 8, 512 << 20)
+    assert not use and tz > tn > 0
+    use, tn, tz = Z.rs_choose(prof, ib, 8, 512 << 20)
+    assert use and tn > tz > 0
+    # the times follow the stated model
+    shard, m = (512 << 20) / 8, 7
+    assert abs(tn - m * (5.0 + shard / 25e3)) < 1e-6 * tn
+    assert abs(tz - (m * shard / 2500e3 + m * (5.0 + 0.7 * shard / 25e3) + m * shard / 3200e3)) < 1e-6 * tz
+    assert not Z.rs_choose(prof, ib, 8, (1 << 20) - 1)[0]                       # under 1 MiB
+    assert not Z.rs_choose(Z.CodecProfileT(2500.0, 3200.0, 1.0), ib, 8, 512 << 20)[0]   # incompressible
+    # a slower link never makes the codec less attractive
+    prev = None
+    for bw in (400.0, 200.0, 100.0, 50.0, 25.0, 12.5):
+        use = Z.rs_choose(prof, Z.LinkT(bw, 5.0, 1), 8, 512 << 20)[0]
+        assert prev is None or use >= prev
+        prev = use
+    L = Z.lib()
+    assert L.zipccl_rs_choose(None, ctypes.byref(ib), 8, 1 << 30, None, None, None) == Z.ERR_INVALID
+    assert L.zipccl_rs_choose(ctypes.byref(prof), None, 8, 1 << 30, None, None, None) == Z.ERR_INVALID
+    assert Z.lib().zipccl_rs_choose(ctypes.byref(prof), ctypes.byref(ib), 1, 1 << 30, None, None, None) == Z.ERR_INVALID
+    assert Z.lib().zipccl_rs_choose(ctypes.byref(prof), ctypes.byref(Z.LinkT(0.0, 5.0, 1)), 8, 1 << 30, None, None,
+                                    None) == Z.ERR_INVALID
+    assert Z.lib().zipccl_profile_codec(None, 10, Z.plan(sigma=1.0), 1, None, 0, None, None) == Z.ERR_INVALID

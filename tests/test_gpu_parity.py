@@ -550,6 +550,20 @@ def test_compress_gather_bad_index(Z):
     check_against_oracle(Z, [mat[used].reshape(-1)], [Z.plan(sigma=0.5)], dict(res, status=0))
 
 
+def test_profile_codec(Z):
+    # the switcher's start-up profile: positive rates, and the compressed fraction is the
+    # oracle's compressed size over the BF16 bytes, exactly
+    n, P = 1 << 21, 7
+    x = W.gaussian_bf16(n, 1e-3, 42)
+    pl = Z.plan(sigma=1e-3)
+    prof = Z.profile_codec(dev_bf16(x), pl, P)
+    assert prof.compress_GBps > 50 and prof.accumulate_GBps > 50
+    st, esc, k = O.compress(x, np.array(pl.exponents, np.uint8))
+    assert abs(prof.ratio - (st.size + k) / (2 * n)) < 1e-12
+    use, tn, tz = Z.rs_choose(prof, Z.LinkT(25.0, 5.0, 1), 8, 1 << 30)
+    assert tn > 0 and tz > 0
+
+
 # ------------------------------------------------------------------------------------
 # the scan-kernel path for escape positions (used above 2^28 values per call), forced
 # on small inputs
