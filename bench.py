@@ -434,6 +434,48 @@ def bench_switcher(torch, Z, W):
     return out
 
 
+def bench_estimated_plans(torch, Z, W, rounds):
+    """The bucket coded with plans estimated on the device (every 16th tile of 512 values)
+    instead of the layers' known sigmas: the estimate's launch time, the compress with
+    device plans, and the compressed size against the known-sigma plans."""
+    wl = W.bucket_64m()
+    tens = [to_dev(torch, x) for x in wl.segments]
+    n = wl.n_total
+    k = len(tens)
+    plans_dev = torch.empty(8 * k, dtype=torch.uint8, device="cuda")
+    static_bytes = sum(Z.static_size(x.size) for x in wl.segments)
+    st = torch.empty(static_bytes, dtype=torch.uint8, device="cuda")
+    esc = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(Z.workspace_size(n, k), dtype=torch.uint8, device="cuda")
+    n_esc = torch.zeros(k + 1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # both calls marshalled once, so that the launch times are the GPU's
+    import ctypes
+    segs = Z._segment_array(tens)
+    L = Z.lib()
+    est_args = (segs, k, 16, ctypes.c_void_p(plans_dev.data_ptr()), None)
+    comp_args = (segs, k, ctypes.c_void_p(plans_dev.data_ptr()), ctypes.c_void_p(st.data_ptr()), st.numel(),
+                 ctypes.c_void_p(esc.data_ptr()), esc.numel(), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                 ctypes.c_void_p(n_esc.data_ptr()), ctypes.c_void_p(status.data_ptr()), None)
+    L.zipccl_estimate_plans(*est_args)          # first launches load the kernels
+    L.zipccl_compress_device_plans(*comp_args)
+    est = batched_ms(torch, lambda _: L.zipccl_estimate_plans(*est_args), 1, rounds)
+    comp = batched_ms(torch, lambda _: L.zipccl_compress_device_plans(*comp_args), 1, rounds)
+    torch.cuda.synchronize()
+    esc_est = int(n_esc[-1].item())
+    raw = plans_dev.cpu().numpy().tobytes()
+    same = sum(list(Z.PlanT.from_buffer_copy(raw[8 * i:8 * i + 8]).exponents) == Z.plan(sigma=s).exponents
+               for i, s in enumerate(wl.sigmas))
+    Z.compress(list(zip(tens, Z.plan_many(wl.sigmas))), st, esc, ws, n_esc, status)
+    torch.cuda.synchronize()
+    esc_known = int(n_esc[-1].item())
+    return {"elements": n, "segments": k, "estimate_us": round(est * 1e3, 2),
+            "compress_device_plans_us": round(comp * 1e3, 2),
+            "ratio_estimated": round(2 * n / (static_bytes + esc_est), 5),
+            "ratio_known_sigma": round(2 * n / (static_bytes + esc_known), 5),
+            "tables_equal_to_known_sigma": f"{same}/{k}", "status_ok": int(status.item()) == 0}
+
+
 def copy_ceiling(torch, iters=10):
     """A plain 1 GiB device-to-device copy: the practical HBM ceiling (read + write bytes / s)."""
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -653,6 +695,7 @@ def main(argv=None) -> int:
     if args.only:
         runners = {"rs_512m": lambda: bench_rs(torch, Z, W, 5),
                    "rs_switcher": lambda: bench_switcher(torch, Z, W),
+                   "bucket_64m_estimated_plans": lambda: bench_estimated_plans(torch, Z, W, 5),
                    "allgather_16x4m": lambda: bench_allgather(torch, Z, W, 5),
                    "moe_routed_16384x7168": lambda: bench_moe_gather(torch, Z, W, 5)}
         if args.only not in runners:
@@ -739,6 +782,9 @@ def main(argv=None) -> int:
             torch.cuda.empty_cache()
         log("workload moe_routed_16384x7168")
         per["moe_routed_16384x7168"] = bench_moe_gather(torch, Z, W, 5)
+        torch.cuda.empty_cache()
+        log("bucket with plans estimated on the device")
+        per["bucket_64m_estimated_plans"] = bench_estimated_plans(torch, Z, W, 5)
         torch.cuda.empty_cache()
         log("workload allgather_16x4m")
         per["allgather_16x4m"] = bench_allgather(torch, Z, W, 5)

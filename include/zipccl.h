@@ -136,6 +136,29 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
                               void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
                               uint64_t* n_esc_out, uint32_t* status, void* stream);
 
+/* Plans estimated on the device, for tensors whose sigma the caller does not know
+ * (S2.A's Gaussian model; the pages derive sigma from the layer's weights instead): for
+ * each segment, sigma = sqrt(mean of x^2) over the finite values of every stride-th tile
+ * of 512 values (tiles k * stride, k = 0, 1, ...; one workgroup per segment reads them),
+ * summed in fp64 in a fixed order, then
+ * the table of zipccl_plan(sigma, NULL) (no finite value, or sigma 0: sigma = 1) written
+ * to plans_dev[s].  segs[s].plan is ignored.  One launch, nothing returns to the host.
+ *   plans_dev   device, 8-byte aligned, nseg entries
+ * Errors: INVALID (NULL pointers with n > 0, nseg outside 1..ZIPCCL_MAX_SEGMENTS,
+ * stride 0), ALIGN, SIZE (n >= 2^32), HIP. */
+zipccl_status zipccl_estimate_plans(const zipccl_segment_t* segs, int nseg, uint32_t stride, zipccl_plan_t* plans_dev,
+                                    void* stream);
+
+/* zipccl_compress with segment s coded by the plan in device memory at plans_dev[s]
+ * (written by zipccl_estimate_plans, or by the caller: 7 distinct ascending exponents in
+ * 1..254, then a zero byte) instead of segs[s].plan.  Same outputs and errors as
+ * zipccl_compress; ALIGN also for plans_dev not 8-byte aligned.  A device plan that is not
+ * a valid table gives a segment whose header the decoders reject. */
+zipccl_status zipccl_compress_device_plans(const zipccl_segment_t* segs, int nseg, const zipccl_plan_t* plans_dev,
+                                           void* static_out, uint64_t static_cap, void* esc_out, uint64_t esc_cap,
+                                           void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
+                                           uint32_t* status, void* stream);
+
 /* A sequence of nchunks independent compress calls on one stream, as the chunked
  * pipeline of the CCCL page's pipeline section issues them: chunk k is what
  *   zipccl_compress(segs + k * nseg, nseg, static_out[k], static_cap[k], esc_out[k],

@@ -181,6 +181,7 @@ CArgsP chunk_args(const CArgs& a)
     c.total_units = a.total_units;
     c.total_blocks = a.total_blocks;
     c.direct = a.direct;
+    c.dplans = a.dplans;
     return c;
 }
 
@@ -198,8 +199,9 @@ zipccl_status check_compress_buffers(int nseg, void* static_out, void* workspace
 
 namespace {
 
-// Segments of a plain (contiguous) compress call into a.seg.
-zipccl_status fill_segments(CArgs& a, const zipccl_segment_t* segs, int nseg)
+// Segments of a plain (contiguous) compress call into a.seg (their plans are checked
+// unless the tables come from device memory).
+zipccl_status fill_segments(CArgs& a, const zipccl_segment_t* segs, int nseg, bool check_plans = true)
 {
     std::memset(&a, 0, sizeof(a));
     for (int s = 0; s < nseg; s++) {
@@ -207,7 +209,7 @@ zipccl_status fill_segments(CArgs& a, const zipccl_segment_t* segs, int nseg)
         if (g.n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
         if (g.n > 0 && !g.src) return ZIPCCL_ERR_INVALID;
         if (!aligned(g.src, 16)) return ZIPCCL_ERR_ALIGN;
-        if (!plan_valid(g.plan)) return ZIPCCL_ERR_INVALID;
+        if (check_plans && !plan_valid(g.plan)) return ZIPCCL_ERR_INVALID;
         CSeg& c = a.seg[s];
         c.src = static_cast<const uint16_t*>(g.src);
         c.n = uint32_t(g.n);
@@ -249,6 +251,41 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
     if (zipccl_status r = check_compress_buffers(nseg, static_out, workspace, n_esc_out, status)) return r;
     CArgs a;
     if (zipccl_status r = fill_segments(a, segs, nseg)) return r;
+    return compress_segments(a, nseg, static_out, static_cap, esc_out, esc_cap, workspace, workspace_bytes,
+                             n_esc_out, status, stream);
+}
+
+zipccl_status zipccl_estimate_plans(const zipccl_segment_t* segs, int nseg, uint32_t stride, zipccl_plan_t* plans_dev,
+                                    void* stream)
+{
+    if (!segs || nseg < 1 || nseg > kMaxSegs || stride < 1 || !plans_dev) return ZIPCCL_ERR_INVALID;
+    if (!aligned(plans_dev, 8)) return ZIPCCL_ERR_ALIGN;
+    EArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int s = 0; s < nseg; s++) {
+        if (segs[s].n >= (1ull << 32)) return ZIPCCL_ERR_SIZE;
+        if (segs[s].n > 0 && !segs[s].src) return ZIPCCL_ERR_INVALID;
+        if (!aligned(segs[s].src, 16)) return ZIPCCL_ERR_ALIGN;
+        a.src[s] = static_cast<const uint16_t*>(segs[s].src);
+        a.n[s] = uint32_t(segs[s].n);
+    }
+    a.plans = reinterpret_cast<uint8_t*>(plans_dev);
+    a.stride = stride;
+    a.nseg = nseg;
+    return hip_status(launch_estimate_plans(a, static_cast<hipStream_t>(stream)));
+}
+
+zipccl_status zipccl_compress_device_plans(const zipccl_segment_t* segs, int nseg, const zipccl_plan_t* plans_dev,
+                                           void* static_out, uint64_t static_cap, void* esc_out, uint64_t esc_cap,
+                                           void* workspace, uint64_t workspace_bytes, uint64_t* n_esc_out,
+                                           uint32_t* status, void* stream)
+{
+    if (!segs || !plans_dev) return ZIPCCL_ERR_INVALID;
+    if (!aligned(plans_dev, 8)) return ZIPCCL_ERR_ALIGN;
+    if (zipccl_status r = check_compress_buffers(nseg, static_out, workspace, n_esc_out, status)) return r;
+    CArgs a;
+    if (zipccl_status r = fill_segments(a, segs, nseg, false)) return r;
+    a.dplans = reinterpret_cast<const uint8_t*>(plans_dev);
     return compress_segments(a, nseg, static_out, static_cap, esc_out, esc_cap, workspace, workspace_bytes,
                              n_esc_out, status, stream);
 }

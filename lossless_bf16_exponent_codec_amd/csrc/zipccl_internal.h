@@ -63,6 +63,7 @@ struct CArgsN {
     uint8_t* stage;        // workspace: kUnit bytes per unit
     uint64_t* n_esc_out;   // nseg + 1 entries or null
     uint32_t* status;      // or null
+    const uint8_t* dplans; // device plans (8 bytes per segment) replacing the segments' tables, or null
     int32_t nseg;
     uint32_t total_units;
     uint32_t total_blocks;
@@ -127,6 +128,16 @@ hipError_t launch_compress(const CArgs& a, hipStream_t s);   // encode + place
 // encodes chunk `enc`; either may have no units.  Both need direct == 1.
 hipError_t launch_encode_place(const CArgsP& enc, const CArgsP& place, hipStream_t s);
 hipError_t launch_decompress(const DArgs& a, hipStream_t s);
+// Plans from a strided sample of each segment (one workgroup per segment).
+struct EArgs {
+    const uint16_t* src[kMaxSegs];
+    uint32_t n[kMaxSegs];
+    uint8_t* plans;        // device, 8 bytes per segment
+    uint32_t stride;       // every stride-th group of 8 values is sampled
+    int32_t nseg;
+};
+static_assert(sizeof(EArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+hipError_t launch_estimate_plans(const EArgs& a, hipStream_t s);
 hipError_t launch_accumulate(const AArgs& a, hipStream_t s);
 
 }  // namespace zc

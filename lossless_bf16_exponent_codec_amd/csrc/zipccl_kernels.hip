@@ -340,6 +340,21 @@ __device__ inline void stage_tile_escapes(const TileEsc& te, uint32_t r, uint8_t
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
 // planes, the escape count (to workspace slot gh) and the escape exponents in value
 // order in s_esc; zero padding after the segment's last half block.
+// The code table of segment s: the segment descriptor's, or the plan the caller left in
+// device memory (8 bytes per segment: 7 ascending exponents and a zero byte).
+template <class Args>
+__device__ inline void seg_table(const Args& a, int s, uint32_t& lo, uint32_t& hi)
+{
+    if (a.dplans) {
+        const uint32_t* t = reinterpret_cast<const uint32_t*>(a.dplans + 8 * s);
+        lo = __builtin_amdgcn_readfirstlane(t[0]);
+        hi = __builtin_amdgcn_readfirstlane(t[1]) & 0x00FFFFFFu;
+    } else {
+        lo = a.seg[s].table_lo;
+        hi = a.seg[s].table_hi;
+    }
+}
+
 template <bool kFull, class Args>
 __device__ inline uint32_t encode_half(const Args& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
                                        uint32_t lane, const uint8_t* lut, const Transpose32& tc, uint8_t* s_esc)
@@ -428,11 +443,13 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
         for (int k = 0; k < 4; k++) v[k] = load_nt(reinterpret_cast<const uint4*>(src[k]));
     }
     __shared__ uint32_t s_hcnt[kEncWaves];
+    uint32_t table_lo, table_hi;
+    seg_table(a, s, table_lo, table_hi);
     if (tid < 256) {   // exponent -> code entry of this segment
         uint32_t code = 0;
 #pragma unroll
         for (int r = 0; r < 7; r++) {
-            const uint32_t te = (r < 4 ? (sg.table_lo >> (8 * r)) : (sg.table_hi >> (8 * (r - 4)))) & 0xFFu;
+            const uint32_t te = (r < 4 ? (table_lo >> (8 * r)) : (table_hi >> (8 * (r - 4)))) & 0xFFu;
             if (te == tid) code = r + 1;
         }
         s_lut[tid] = uint8_t(code_entry(code));
@@ -475,7 +492,8 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a) { encode_unit(a, blockIdx.x); }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
-__device__ inline void write_header(const CSeg& sg, uint32_t lane, uint32_t n_esc, uint32_t esc_offset)
+__device__ inline void write_header(const CSeg& sg, uint32_t table_lo, uint32_t table_hi, uint32_t lane,
+                                    uint32_t n_esc, uint32_t esc_offset)
 {
     if (lane >= 32) return;
     const uint32_t n = sg.n;
@@ -485,8 +503,8 @@ __device__ inline void write_header(const CSeg& sg, uint32_t lane, uint32_t n_es
         case 0: hv = ZIPCCL_MAGIC; break;
         case 1: hv = 1u; break;                  // version 1, flags 0
         case 2: hv = n; break;
-        case 4: hv = sg.table_lo; break;
-        case 5: hv = sg.table_hi & 0x00FFFFFFu; break;
+        case 4: hv = table_lo; break;
+        case 5: hv = table_hi & 0x00FFFFFFu; break;
         case 6: hv = kBlock; break;
         case 7: hv = kTile; break;
         case 8: hv = n_esc; break;
@@ -502,10 +520,14 @@ constexpr uint32_t kScanThreads = 1024;
 constexpr uint32_t kScanPer = 16;                       // counts per thread per round
 constexpr uint32_t kScanRound = kScanThreads * kScanPer;
 
-// Header of an empty segment (n = 0): esc_offset is where its escapes would start.
-__device__ inline void write_empty_header(const CSeg& sg, uint32_t lane, uint32_t esc_offset)
+// Header of segment s: its escape count and where its escapes start (for an empty
+// segment, where they would start).
+template <class Args>
+__device__ inline void write_seg_header(const Args& a, int s, uint32_t lane, uint32_t n_esc, uint32_t esc_offset)
 {
-    write_header(sg, lane, 0u, esc_offset);
+    uint32_t lo, hi;
+    seg_table(a, s, lo, hi);
+    write_header(a.seg[s], lo, hi, lane, n_esc, esc_offset);
 }
 
 // Scan: one workgroup turns the per-slot escape counts into launch-wide positions:
@@ -572,7 +594,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
     if (tid == 0 && a.n_esc_out && Kt == 0) a.n_esc_out[a.nseg] = 0;
     if (Kt == 0 && wave == 0) {   // only empty segments: every header says offset 0
         for (int s = 0; s < a.nseg; s++) {
-            write_empty_header(a.seg[s], lane, 0u);
+            write_seg_header(a, s, lane, 0u, 0u);
             if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = 0;
         }
     }
@@ -628,20 +650,20 @@ __device__ inline void place_block_tables(const Args& a, const CSeg& sg, int s, 
     const uint32_t K = uint32_t(blocks_of(sg.n));
     if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
     if (gb == sg.block0 + K - 1) {
-        write_header(sg, lane, p2 - base, base);
+        write_seg_header(a, s, lane, p2 - base, base);
         if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = p2 - base;
     }
     // empty segments just before this one start where it starts; those after the
     // launch's last block start at the end
     if (gb == sg.block0) {
         for (int e = s - 1; e >= 0 && a.seg[e].n == 0; e--) {
-            write_empty_header(a.seg[e], lane, p0);
+            write_seg_header(a, e, lane, 0u, p0);
             if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
         }
     }
     if (gb + 1 == a.total_blocks) {
         for (int e = s + 1; e < a.nseg; e++) {
-            write_empty_header(a.seg[e], lane, p2);
+            write_seg_header(a, e, lane, 0u, p2);
             if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
         }
         if (lane == 0 && a.n_esc_out) a.n_esc_out[a.nseg] = p2;
@@ -1252,6 +1274,96 @@ hipError_t launch_encode_place(const CArgsP& enc, const CArgsP& place, hipStream
     const uint32_t grid = groups + enc.total_units;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(encode_place_kernel, dim3(grid), dim3(kEncThreads), 0, s, enc, place, groups);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------------
+// plans from the data: sigma estimated on the device
+// --------------------------------------------------------------------------------
+// One workgroup per segment (16 waves).  The sample is every stride-th tile of 512
+// values: wave w reads sampled tiles w, w + 16, ..., 16 at a time, lane l the 16 bytes of
+// values 8l .. 8l + 7 (coalesced 1 KB per wave load).  Each thread sums, in fp64, the
+// squares of its finite values and counts them; the workgroup adds the 1024 partial sums
+// in a fixed order, so the estimate is the same on every run.  sigma = sqrt(sum / count)
+// (the model's mean is 0; no finite sample, or sigma 0, counts as sigma 1), then the
+// plan's closed form: e0 = 123 + floor(log2(sigma) - c), clamped to 1..248, table
+// e0 .. e0 + 6.
+constexpr uint32_t kEstThreads = 1024;
+constexpr uint32_t kEstWaves = kEstThreads / 64;
+constexpr double kSwitchPhaseDev = 0.7195805543641254;   // where the 7-binade window moves up
+
+namespace {
+
+__global__ __launch_bounds__(kEstThreads) void estimate_plans_kernel(const EArgs a)
+{
+    __shared__ double s_sum[kEstThreads];
+    __shared__ uint32_t s_cnt[kEstThreads];
+    const uint32_t tid = threadIdx.x, lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = blockIdx.x;
+    const uint16_t* src = a.src[s];
+    const uint32_t n = a.n[s];
+    const uint64_t T = tiles_of(n);
+    double sum = 0.0;
+    uint32_t cnt = 0;
+    constexpr uint32_t kBatch = 16;   // sampled tiles in flight per wave
+    for (uint64_t k0 = wave; k0 * a.stride < T; k0 += uint64_t(kBatch) * kEstWaves) {
+        uint4 v[kBatch];
+#pragma unroll
+        for (uint32_t b = 0; b < kBatch; b++) {
+            const uint64_t i = (k0 + uint64_t(b) * kEstWaves) * a.stride * kTile + 8ull * lane;
+            if (i + 8 <= n) {
+                v[b] = load_nt(reinterpret_cast<const uint4*>(src + i));
+            } else {   // the segment's ragged end, or past it: missing values read as NaN
+                uint32_t w[4];
+                for (uint32_t j = 0; j < 4; j++) {
+                    const uint64_t q = i + 2 * j;
+                    w[j] = (q < n ? uint32_t(src[q]) : 0x7FC0u) | (q + 1 < n ? uint32_t(src[q + 1]) << 16 : 0x7FC00000u);
+                }
+                v[b] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+#pragma unroll
+        for (uint32_t b = 0; b < kBatch; b++) {
+            const uint32_t w[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float f = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+                if (__builtin_isfinite(f)) {
+                    const double d = double(f);
+                    sum += d * d;
+                    cnt++;
+                }
+            }
+        }
+    }
+    s_sum[tid] = sum;
+    s_cnt[tid] = cnt;
+    __syncthreads();
+    for (uint32_t h = kEstThreads / 2; h > 0; h >>= 1) {
+        if (tid < h) {
+            s_sum[tid] += s_sum[tid + h];
+            s_cnt[tid] += s_cnt[tid + h];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        double sigma = s_cnt[0] ? sqrt(s_sum[0] / double(s_cnt[0])) : 1.0;
+        if (!(sigma > 0.0) || !__builtin_isfinite(sigma)) sigma = 1.0;
+        const double e = 123.0 + floor(log2(sigma) - kSwitchPhaseDev);
+        const uint32_t e0 = uint32_t(fmin(248.0, fmax(1.0, e)));
+        const uint32_t lo = e0 | (e0 + 1) << 8 | (e0 + 2) << 16 | (e0 + 3) << 24;
+        const uint32_t hi = (e0 + 4) | (e0 + 5) << 8 | (e0 + 6) << 16;
+        reinterpret_cast<uint2*>(a.plans)[s] = make_uint2(lo, hi);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_estimate_plans(const EArgs& a, hipStream_t s)
+{
+    if (a.nseg < 1) return hipSuccess;
+    hipLaunchKernelGGL(estimate_plans_kernel, dim3(a.nseg), dim3(kEstThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -84,6 +84,11 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_compress_chunks.argtypes = [ctypes.POINTER(SegmentT), i32, i32, ctypes.POINTER(vp),
                                            ctypes.POINTER(u64), ctypes.POINTER(vp), ctypes.POINTER(u64), vp, u64,
                                            vp, vp, vp]
+    lib.zipccl_estimate_plans.restype = i32
+    lib.zipccl_estimate_plans.argtypes = [ctypes.POINTER(SegmentT), i32, ctypes.c_uint32, vp, vp]
+    lib.zipccl_compress_device_plans.restype = i32
+    lib.zipccl_compress_device_plans.argtypes = [ctypes.POINTER(SegmentT), i32, vp, vp, u64, vp, u64, vp, u64, vp,
+                                                 vp, vp]
     lib.zipccl_compress_gather.restype = i32
     lib.zipccl_compress_gather.argtypes = [ctypes.POINTER(GatherSegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp,
                                            vp]
@@ -231,6 +236,31 @@ class PreparedCompressChunks:
             for i in range(self.nseg):
                 self._arr[k * self.nseg + i].plan = plans[i]
         _check(_lib.zipccl_compress_chunks(self._arr, self.nseg, self.nchunks, *self._args), "zipccl_compress_chunks")
+
+
+def _segment_array(tensors):
+    arr = (SegmentT * max(len(tensors), 1))()
+    for k, t in enumerate(tensors):
+        arr[k].src = _ptr(t) if t.numel() else None
+        arr[k].n = t.numel()
+    return arr
+
+
+def estimate_plans(tensors, plans_dev, stride: int = 16, stream=None):
+    """zipccl_estimate_plans: plans_dev, a uint8 device tensor of 8 * len(tensors) bytes,
+    receives one plan per bf16 tensor.  PlanT.from_buffer_copy on its bytes reads them."""
+    _check(_lib.zipccl_estimate_plans(_segment_array(tensors), len(tensors), stride, _ptr(plans_dev),
+                                      _stream(stream)), "zipccl_estimate_plans")
+
+
+def compress_device_plans(tensors, plans_dev, static_out, esc_out, workspace, n_esc_out=None, status=None,
+                          stream=None, esc_cap: int | None = None):
+    """zipccl_compress_device_plans: tensors coded by the plans in plans_dev (device)."""
+    cap = _nbytes(esc_out) if esc_cap is None else esc_cap
+    _check(_lib.zipccl_compress_device_plans(_segment_array(tensors), len(tensors), _ptr(plans_dev),
+                                             _ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap,
+                                             _ptr(workspace), _nbytes(workspace), _ptr(n_esc_out), _ptr(status),
+                                             _stream(stream)), "zipccl_compress_device_plans")
 
 
 def compress_gather(segments, static_out, esc_out, workspace, n_esc_out=None, status=None, stream=None,

@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
                  "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many",
                  "zipccl_decompress_shards", "zipccl_compress_gather", "zipccl_compress_chunks",
                  "zipccl_decompress_accumulate_chunks", "zipccl_profile_codec", "zipccl_profile_scratch_size",
-                 "zipccl_rs_choose"]:
+                 "zipccl_rs_choose", "zipccl_estimate_plans", "zipccl_compress_device_plans"]:
         assert want in names
 
 
@@ -157,6 +157,15 @@ def test_argument_errors_before_any_launch(Z):
     assert L.zipccl_compress_chunks(segs2, 1, 2, so, sc, eo, ec, fake, 8, None, None, None) == Z.ERR_SIZE
     so[1] = fake + 64                    # the second chunk's static part misaligned: nothing enqueued
     assert L.zipccl_compress_chunks(segs2, 1, 2, so, sc, eo, ec, fake, cws, None, None, None) == Z.ERR_ALIGN
+    est = L.zipccl_estimate_plans
+    assert est(seg, 1, 16, None, None) == Z.ERR_INVALID
+    assert est(seg, 0, 16, fake, None) == Z.ERR_INVALID
+    assert est(seg, 1, 0, fake, None) == Z.ERR_INVALID
+    assert est(seg, 1, 16, fake + 4, None) == Z.ERR_ALIGN
+    cdp = L.zipccl_compress_device_plans
+    assert cdp(seg, 1, None, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_INVALID
+    assert cdp(seg, 1, fake + 4, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_ALIGN
+    assert cdp(seg, 1, fake, fake, 10, fake, 100, fake, ws, None, None, None) == Z.ERR_SIZE
     g = (Z.GatherSegmentT * 1)()
     g[0].src, g[0].src_rows, g[0].row_len, g[0].rows, g[0].nrows, g[0].plan = 0x10000, 100, 7168, 0x20000, 10, p
     gws = Z.workspace_size(71680, 1)

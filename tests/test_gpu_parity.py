@@ -564,6 +564,58 @@ def test_profile_codec(Z):
     assert tn > 0 and tz > 0
 
 
+def sample_sigma(x, stride):
+    """sigma of the finite values among every stride-th tile of 512 (fp64, numpy)."""
+    n = x.size
+    starts = np.arange(0, n, 512 * stride, dtype=np.int64)
+    idx = (starts[:, None] + np.arange(512)).ravel()
+    idx = idx[idx < n]
+    f = (x[idx].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    f = f[np.isfinite(f)]
+    s = float(np.sqrt((f * f).sum() / f.size)) if f.size else 1.0
+    return s if s > 0 and np.isfinite(s) else 1.0
+
+
+@pytest.mark.parametrize("stride", [1, 16])
+def test_estimate_plans_and_compress_with_them(Z, stride):
+    import math
+    nan = np.full(4096, 0x7FC1, np.uint16)
+    mixed = W.gaussian_bf16(50000, 0.3, 91)
+    mixed[::97] = 0x7F80                                  # +Inf every 97th value
+    segs = [W.gaussian_bf16(1 << 22, 0.02, 90), W.gaussian_bf16(70001, 1e-3, 92), np.zeros(0, np.uint16),
+            W.gaussian_bf16(5, 1.0, 93), nan, W.gaussian_bf16(100000, 3.0, 94), mixed,
+            W.gaussian_bf16(30000, 1e-30, 95)]
+    tens = [dev_bf16(x) for x in segs]
+    plans_dev = torch.full((8 * len(segs),), 0xAA, dtype=torch.uint8, device="cuda")
+    Z.estimate_plans(tens, plans_dev, stride=stride)
+    torch.cuda.synchronize()
+    raw = plans_dev.cpu().numpy().tobytes()
+    got = [Z.PlanT.from_buffer_copy(raw[8 * k:8 * k + 8]) for k in range(len(segs))]
+    for k, x in enumerate(segs):
+        s = sample_sigma(x, stride)
+        phase = math.log2(s) - math.floor(math.log2(s))
+        if abs(phase - 0.7195805543641254) < 1e-9:
+            continue                                      # at the switch: either window
+        assert list(got[k].exponents) == [int(v) for v in O.plan_sigma(s)], (k, s)
+        assert got[k].reserved == 0
+    # compress with the device plans == compress with the same plans passed by value
+    r_ref = gpu_compress(Z, segs, got)
+    check_against_oracle(Z, segs, got, r_ref)
+    total_static = sum(Z.static_size(x.size) for x in segs)
+    static = torch.full((total_static,), POISON, dtype=torch.uint8, device="cuda")
+    esc = torch.full((sum(x.size for x in segs),), POISON, dtype=torch.uint8, device="cuda")
+    n_esc = torch.full((len(segs) + 1,), -1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(Z.workspace_size(sum(x.size for x in segs), len(segs)), dtype=torch.uint8, device="cuda")
+    Z.compress_device_plans(tens, plans_dev, static, esc, ws, n_esc, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(static.cpu().numpy(), r_ref["static_h"])
+    ne = n_esc.cpu().numpy()
+    assert np.array_equal(ne, r_ref["n_esc"])
+    assert np.array_equal(esc.cpu().numpy()[:ne[-1]], r_ref["esc_h"][:ne[-1]])
+
+
 # ------------------------------------------------------------------------------------
 # the scan-kernel path for escape positions (used above 2^28 values per call), forced
 # on small inputs
