@@ -642,6 +642,41 @@ def summarize_pmc(fetch_csv, write_csv, out_path, n_units=4096):
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
+SQ_COUNTERS = "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_BUSY_CYCLES"
+SQ_CMD = ("rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv -d gpurun_out/pmc_sq_rs -o run -- "
+          "python3 bench.py --only rs_512m")
+
+
+def summarize_sq(csv_path, out_path):
+    """profiles/ text from one rocprofv3 --pmc run of SQ_CMD: instruction counts per
+    launch of the reduce-scatter kernels, and the VALU issue time they imply (a wave64
+    VALU instruction occupies a SIMD for 4 cycles; 1024 SIMDs at 2.4 GHz)."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = short_kernel_name(r["Kernel_Name"])
+        if k is None or k == COPY_KERNEL:
+            continue
+        grid = int(r.get("Grid_Size", 0) or 0)
+        acc.setdefault((k, grid), {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# Instruction counts, rs_512m kernels (rocprofv3 SQ counters, mean per launch)", "",
+             "Command (from the repository root on the GPU host):", "", "    " + SQ_CMD, "",
+             f"Kernel source sha256: `{kernel_source_sha256()}`", "",
+             "| kernel | grid | launches | waves | VALU | SALU | LDS | VMEM rd | VMEM wr | VALU issue us |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for (k, grid), d in sorted(acc.items()):
+        m = {c: sum(v) / len(v) for c, v in d.items()}
+        n = len(next(iter(d.values())))
+        valu_us = m.get("SQ_INSTS_VALU", 0) * 4 / 1024 / 2.4e3
+        lines.append(f"| {k} | {grid} | {n} | {m.get('SQ_WAVES', 0):.0f} | {m.get('SQ_INSTS_VALU', 0):.0f} | "
+                     f"{m.get('SQ_INSTS_SALU', 0):.0f} | {m.get('SQ_INSTS_LDS', 0):.0f} | "
+                     f"{m.get('SQ_INSTS_VMEM_RD', 0):.0f} | {m.get('SQ_INSTS_VMEM_WR', 0):.0f} | {valu_us:.2f} |")
+    lines += ["", "Counters are per launch (the profiler serialises launches).  VALU issue us = VALU",
+              "instructions x 4 cycles / 1024 SIMDs / 2.4 GHz: the time the launch's VALU work",
+              "needs if every SIMD issued one wave64 VALU instruction every 4 cycles."]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
 def measured_traffic():
     """Bytes per launch from the committed PMC summary, or {} if it is missing or was
     taken on another version of the kernels."""
@@ -670,6 +705,8 @@ def main(argv=None) -> int:
                     help="write a profiles/ summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-rs-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
                     help="write a profiles/ summary of a rocprofv3 --stats run of --only rs_512m and exit")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of a rocprofv3 SQ-counter run of --only rs_512m and exit")
     ap.add_argument("--only", default=None,
                     help="run one of the other workloads alone (for profiling) and print its figures")
     args = ap.parse_args(argv)
@@ -681,6 +718,9 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_rs_stats:
         summarize_stats(*args.summarize_rs_stats, rs=True)
+        return 0
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and this build has no "
