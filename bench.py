@@ -543,11 +543,11 @@ def cpu_baseline(W, O, wl, reps):
 # ------------------------------------------------------------------------------------
 KERNEL_SRC = os.path.join(ROOT, "lossless_bf16_exponent_codec_amd", "csrc", "zipccl_kernels.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "pmc_traffic_bucket_64m.txt")
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/stats -o bench -- "
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats -o bench -- "
              "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra")
-PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{counter} -o run -- "
+PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d rocprof_out/pmc_{counter} -o run -- "
            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-extra")
-RS_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/stats_rs -o rs -- "
+RS_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats_rs -o rs -- "
                 "python3 bench.py --only rs_512m")
 OUR_KERNELS = ("encode_place_kernel", "encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel",
                "decompress_kernel", "accumulate_kernel")
@@ -643,7 +643,7 @@ def summarize_pmc(fetch_csv, write_csv, out_path, n_units=4096):
 
 
 SQ_COUNTERS = "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_BUSY_CYCLES"
-SQ_CMD = ("rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv -d gpurun_out/pmc_sq_rs -o run -- "
+SQ_CMD = ("rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv -d rocprof_out/pmc_sq_rs -o run -- "
           "python3 bench.py --only rs_512m")
 
 
@@ -723,7 +723,7 @@ def main(argv=None) -> int:
         summarize_sq(*args.summarize_sq)
         return 0
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and this build has no "
+        print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and there is no "
               f"multi-GPU path; --gpus {args.gpus} is not supported", file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -309,7 +309,7 @@ static float bf16_to_f32(uint16_t b)
 static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 
 /* Round a binary32 value to the nearest BF16, ties to the even significand, by the
- * definition: of the two BF16 neighbours choose the nearer one.  Overflow is judged
+ * definition: of the two BF16 neighbours choose the nearer one.  Overflow is decided
  * against 2^128, the value the next binade would start at.  NaN -> 0x7FC0. */
 uint16_t zo_round_bf16(float f)
 {
