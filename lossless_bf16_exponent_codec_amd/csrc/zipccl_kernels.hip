@@ -1043,17 +1043,21 @@ void accumulate_kernel(const AArgs a)
     // ---- per peer: plane rows, escape flags, escape ranks within the tile ----
     const Transpose32 tc = transpose_consts(lane);
     const uint32_t vf = valid_flags(nvalid);   // 0 in a wave without a tile
-    uint32_t rows[kPeers], zf[kPeers], cnt[kPeers], rank[kPeers], total[kPeers];
+    constexpr int kPairs = (kPeers + 1) & ~1;   // the rank scans take counts in pairs
+    uint32_t rows[kPeers], zf[kPeers], cnt[kPairs], rank[kPairs], total[kPairs];
 #pragma unroll
-    for (int p = 0; p < kPeers; p++) {
-        rows[p] = zf[p] = 0;
-        if (uint32_t(p) < P) {
-            rows[p] = transpose32(pw[p], tc);
-            zf[p] = escape_flags(rows[p], vf);
+    for (int p = 0; p < kPairs; p++) {
+        cnt[p] = 0;
+        if (p < kPeers) {
+            rows[p] = zf[p] = 0;
+            if (uint32_t(p) < P) {
+                rows[p] = transpose32(pw[p], tc);
+                zf[p] = escape_flags(rows[p], vf);
+            }
+            cnt[p] = __builtin_popcount(zf[p]);
         }
-        cnt[p] = __builtin_popcount(zf[p]);
     }
-    wave_ranks<kPeers>(cnt, rank, total, P);
+    wave_ranks<kPairs>(cnt, rank, total, P);
     if (lane == 0) {
 #pragma unroll
         for (int p = 0; p < kPeers; p++) s_cnt[p][wave] = total[p];
@@ -1380,12 +1384,19 @@ hipError_t launch_accumulate(const AArgs& a, hipStream_t s)
     const uint64_t last = a.n - uint64_t(a.nchunks - 1) * a.chunk;   // values of the last chunk
     const uint32_t grid = uint32_t(uint64_t(a.nchunks - 1) * blocks_of(a.chunk) + blocks_of(last));
     if (grid == 0) return hipSuccess;
-    // every peer slot of the instance issues its loads, so the instance is the smallest
-    // that holds npeers
-    if (a.npeers <= 2) hipLaunchKernelGGL(accumulate_kernel<2>, dim3(grid), dim3(kAccThreads), 0, s, a);
-    else if (a.npeers <= 4) hipLaunchKernelGGL(accumulate_kernel<4>, dim3(grid), dim3(kAccThreads), 0, s, a);
-    else if (a.npeers <= 8) hipLaunchKernelGGL(accumulate_kernel<8>, dim3(grid), dim3(kAccThreads), 0, s, a);
-    else hipLaunchKernelGGL(accumulate_kernel<kMaxPeers>, dim3(grid), dim3(kAccThreads), 0, s, a);
+    // every peer slot of the instance issues its loads, so up to 8 peers the instance
+    // holds exactly npeers
+    switch (a.npeers) {
+        case 1: hipLaunchKernelGGL(accumulate_kernel<1>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(accumulate_kernel<2>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 3: hipLaunchKernelGGL(accumulate_kernel<3>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(accumulate_kernel<4>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 5: hipLaunchKernelGGL(accumulate_kernel<5>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 6: hipLaunchKernelGGL(accumulate_kernel<6>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 7: hipLaunchKernelGGL(accumulate_kernel<7>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 8: hipLaunchKernelGGL(accumulate_kernel<8>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL(accumulate_kernel<kMaxPeers>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

@@ -274,7 +274,8 @@ def oracle_accumulate(Z, peer_bits, plans, local_bits):
     return O.decompress_accumulate([c[0] for c in comp], [c[1] for c in comp], local_bits.size, local_bits)
 
 
-@pytest.mark.parametrize("n,npeers", [(1, 1), (4097, 7), (16385, 3), (100000, 7), (262144, 16), (70001, 2)])
+@pytest.mark.parametrize("n,npeers", [(1, 1), (4097, 7), (16385, 3), (100000, 7), (262144, 16), (70001, 2),
+                                     (50000, 4), (33333, 5), (20000, 6), (8192, 8), (9000, 9)])
 def test_accumulate_matches_oracle(Z, n, npeers):
     peers = [W.gaussian_bf16(n, 1e-3, 500 + p) for p in range(npeers)]
     local = W.gaussian_bf16(n, 1e-3, 600)
