@@ -11,7 +11,7 @@ its input in the 256 MB Infinity Cache (steady state of a pipelined round trip).
 Printed (one JSON line on stdout):
   value      BF16 bytes handled per second by the step: (2n compressed + 2n decompressed)
              / step wall time, in GB/s (the harmonic mean of the two codec directions);
-  roofline   for the step's dominant operation (compress: encode_kernel + place_direct_kernel,
+  roofline   for the step's dominant operation (compress: compress_single_kernel,
              or decompress: decompress_kernel, whichever takes longer): algorithmic HBM
              bytes per launch (2n BF16 bytes + static part + escapes) / average launch
              time, from HIP events on the launch stream around back-to-back launches over
@@ -549,7 +549,7 @@ PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d rocprof_out/pmc_{co
            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-extra")
 RS_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats_rs -o rs -- "
                 "python3 bench.py --only rs_512m")
-OUR_KERNELS = ("encode_place_kernel", "encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel",
+OUR_KERNELS = ("compress_single_kernel", "encode_place_kernel", "encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel",
                "decompress_kernel", "accumulate_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 GIB = 1 << 30
@@ -771,10 +771,10 @@ def main(argv=None) -> int:
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                 "bytes_per_launch": moved, "avg_launch_us": round(avg_ms * 1e3, 2), "traffic": traffic.get(op)}
 
-    # the step's dominant operation: decompress is one launch; compress is two
-    # (encode_kernel, place_direct_kernel; three with scan_kernel above 2^28 values)
+    # the step's dominant operation: decompress is one launch; so is compress
+    # (compress_single_kernel; encode_kernel, scan_kernel, place_kernel above 2^28 values)
     units = sum((m + 16383) // 16384 for m in bc.sizes)
-    c_launches = (["encode_kernel", "place_direct_kernel"] if units <= 16384
+    c_launches = (["compress_single_kernel"] if units <= 16384
                   else ["encode_kernel", "scan_kernel", "place_kernel"])
     roof_d = roof("decompress_kernel", "decompress", d_avg, ["decompress_kernel"])
     roof_c = roof("compress", "compress", c_avg, c_launches)

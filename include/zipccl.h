@@ -67,6 +67,9 @@ typedef enum zipccl_status {
 #define ZIPCCL_STATUS_ESC_OVERFLOW 1u  /* escapes did not fit esc_cap; those past it were dropped */
 #define ZIPCCL_STATUS_CORRUPT 2u       /* decode: header or offset table inconsistent; not decoded */
 #define ZIPCCL_STATUS_BAD_INDEX 4u     /* gathered compress: a row index outside the matrix (row 0 was read) */
+#define ZIPCCL_STATUS_WAIT_LIMIT 8u    /* compress: a placing workgroup gave up waiting for an encoder's
+                                          count (bounded wait); that unit's escapes, offsets and headers
+                                          were not written */
 
 /* A coding plan: 7 distinct exponents in 1..254, ascending; code(table[r]) = r + 1. */
 typedef struct zipccl_plan_t {
@@ -111,7 +114,9 @@ uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc);
 /* Device workspace bytes needed by zipccl_compress for up to nseg segments holding
  * at most total_n values (about one byte per value: a 4-byte escape count per 2048-value
  * half block and a 16384-byte escape staging area per 16384 values).  The workspace
- * carries nothing from one call to the next and needs no initialisation; it must be 256-byte aligned.
+ * carries nothing from one call to the next and needs no initialisation (each call tags
+ * what it publishes there with a value no earlier call in the process used); it must be
+ * 256-byte aligned.
  * Calls that run concurrently need separate workspaces. */
 uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
 
@@ -123,10 +128,13 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
  *               beyond esc_cap are dropped and ZIPCCL_STATUS_ESC_OVERFLOW is set; the
  *               headers still carry the true counts.
  *   workspace   device scratch, see zipccl_workspace_size.
- * The work is two kernel launches on `stream`: the encode kernel writes the fixed-size
- * sections and stages each unit's escapes; the place kernel computes the escape
- * positions, writes the offset tables and headers and compacts the escapes (above 2^28
- * values in one call a one-workgroup scan launch computes the positions first).
+ * The work is one kernel launch on `stream`: its encoding workgroups write the
+ * fixed-size sections, stage each unit's escapes and publish the unit's escape count in
+ * the workspace; its last workgroups compute the escape positions from those counts
+ * (bounded wait), write the offset tables and headers and compact the escapes.  While
+ * `stream` is being captured into a graph, or with ZIPCCL_SINGLE_LAUNCH=0 in the
+ * environment, the same work is two launches (encode, then place); above 2^28 values in
+ * one call it is encode, a one-workgroup scan launch, then place.
  *   n_esc_out   optional device u64[nseg + 1]: per-segment escape counts, then the total.
  *   status      optional device u32, bits OR-ed in.
  * Errors: INVALID (NULL pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS, bad table),

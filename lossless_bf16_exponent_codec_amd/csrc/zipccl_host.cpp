@@ -10,11 +10,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
 #include <new>
+#include <random>
 
 #include "zipccl.h"
 #include "zipccl_internal.h"
@@ -40,6 +43,43 @@ uint64_t direct_prefix_max_units()
     const char* e = std::getenv("ZIPCCL_DIRECT_PREFIX_MAX_UNITS");
     if (!e || !*e) return kDirectPrefixMaxUnits;
     return std::min<uint64_t>(std::strtoull(e, nullptr, 10), kDirectPrefixMaxUnits);
+}
+
+// Tags of the single-launch compress: one per call, process-wide, 48 bits, never 0.  The
+// ready words a call's encoders write carry its tag, so the placing workgroups tell them
+// from words an earlier call left in the same workspace (no call repeats a tag in this
+// process; the random start makes a match with memory another process left unlikely).
+uint64_t next_tag()
+{
+    static std::atomic<uint64_t> counter{[] {
+        std::random_device rd;
+        const uint64_t t = uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+        return (uint64_t(rd()) << 32) ^ uint64_t(rd()) ^ (t * 0x9E3779B97F4A7C15ull);
+    }()};
+    for (;;) {
+        const uint64_t t = counter.fetch_add(1, std::memory_order_relaxed) & ((1ull << (64 - kReadyCountBits)) - 1);
+        if (t != 0) return t;
+    }
+}
+
+// Whether a compress call runs as one launch: yes unless the positions need the scan
+// kernel, the stream is being captured into a graph (a replay would repeat the tag baked
+// into the captured arguments), or ZIPCCL_SINGLE_LAUNCH=0 asks for the two-launch path.
+bool single_launch(const CArgs& a, hipStream_t stream)
+{
+    if (!a.direct) return false;
+    const char* e = std::getenv("ZIPCCL_SINGLE_LAUNCH");
+    if (e && e[0] == '0' && e[1] == 0) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return false;
+    return cs == hipStreamCaptureStatusNone;
+}
+
+hipError_t compress_launch(CArgs& a, hipStream_t stream)
+{
+    const bool single = single_launch(a, stream);
+    a.tag = single ? next_tag() : 0;
+    return launch_compress(a, stream, single);
 }
 
 void pack_table(const zipccl_plan_t& p, uint32_t& lo, uint32_t& hi)
@@ -143,7 +183,8 @@ zipccl_status prepare_compress(CArgs& a, int nseg, void* static_out, uint64_t st
     a.counts = reinterpret_cast<uint32_t*>(w);
     a.pos = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(units));
     a.unit_counts = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(units) + ws_pos_bytes(units));
-    a.stage = w + ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units);
+    a.ready = reinterpret_cast<uint64_t*>(w + ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units));
+    a.stage = w + ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units) + ws_ready_bytes(units);
     a.n_esc_out = n_esc_out;
     a.status = status;
     a.nseg = nseg;
@@ -160,7 +201,7 @@ zipccl_status compress_segments(CArgs& a, int nseg, void* static_out, uint64_t s
     if (zipccl_status r = prepare_compress(a, nseg, static_out, static_cap, esc_out, esc_cap, workspace,
                                            workspace_bytes, n_esc_out, status))
         return r;
-    return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)));
+    return hip_status(compress_launch(a, static_cast<hipStream_t>(stream)));
 }
 
 // The arguments of a call with at most kMaxPeers segments in the pipeline's smaller form.
@@ -228,7 +269,8 @@ zipccl_status launch_chunks(const std::vector<CArgs>& calls, hipStream_t stream)
     bool have_prev = false;
     for (const CArgs& a : calls) {
         if (!a.direct || a.nseg > kMaxPeers) {   // scan-kernel positions or many segments: its own launches
-            if (hipError_t e = launch_compress(a, stream)) return hip_status(e);
+            CArgs c = a;
+            if (hipError_t e = compress_launch(c, stream)) return hip_status(e);
             continue;
         }
         const CArgsP cur = chunk_args(a);

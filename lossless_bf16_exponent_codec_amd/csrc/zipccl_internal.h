@@ -24,15 +24,22 @@ constexpr uint32_t kEncThreads = 64 * kEncWaves;
 // unit u (slots past a segment's end hold 0 escapes).  A u32 escape count per slot,
 // the launch-wide position of each slot's first escape (one more entry for the total;
 // used only when the positions come from the scan kernel), a u32 escape count per
-// unit, then kUnit staging bytes per unit that hold its escape exponents, contiguous
-// in value order, until their positions are known.
+// unit, a u64 ready word per unit (the single-launch compress: the call's tag above
+// the unit's escape count), then kUnit staging bytes per unit that hold its escape
+// exponents, contiguous in value order, until their positions are known.
 __host__ __device__ inline uint64_t ws_counts_bytes(uint64_t units) { return (32 * units + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_pos_bytes(uint64_t units) { return (4 * (8 * units + 1) + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_units_bytes(uint64_t units) { return (4 * (units + 1) + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t ws_ready_bytes(uint64_t units) { return (8 * units + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t ws_bytes(uint64_t units)
 {
-    return ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units) + uint64_t(kHalf) * 8 * units;
+    return ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units) + ws_ready_bytes(units) +
+           uint64_t(kHalf) * 8 * units;
 }
+
+// Ready word of a unit in the single-launch compress: the call's tag (48 bits, drawn
+// per call by the host, never 0) above the unit's escape count (at most kUnit).
+constexpr uint32_t kReadyCountBits = 16;
 
 // Up to this many workgroup units (2^28 values) the place kernel sums the unit counts
 // before its unit itself; above, a one-workgroup scan kernel computes the positions.
@@ -61,6 +68,8 @@ struct CArgsN {
     uint32_t* pos;         // workspace: launch-wide position of each slot's first escape
     uint32_t* unit_counts; // workspace: escapes per workgroup unit
     uint8_t* stage;        // workspace: kUnit bytes per unit
+    uint64_t* ready;       // workspace: a ready word per unit (single-launch compress)
+    uint64_t tag;          // this call's tag in the ready words (single-launch compress)
     uint64_t* n_esc_out;   // nseg + 1 entries or null
     uint32_t* status;      // or null
     const uint8_t* dplans; // device plans (8 bytes per segment) replacing the segments' tables, or null
@@ -123,7 +132,10 @@ __host__ __device__ inline uint64_t planes_off(uint64_t n) { return 128 + 512 * 
 __host__ __device__ inline uint64_t offsets_off(uint64_t n) { return planes_off(n) + round128(192 * tiles_of(n)); }
 __host__ __device__ inline uint64_t static_bytes_of(uint64_t n) { return offsets_off(n) + round128(4 * blocks_of(n)); }
 
-hipError_t launch_compress(const CArgs& a, hipStream_t s);   // encode + place
+// Encode + place.  single: one launch whose last workgroups place the units once their
+// encoders have published their ready words (a.ready, a.tag); else encode, then place
+// (or scan + place) in launches of their own.  single needs direct == 1.
+hipError_t launch_compress(const CArgs& a, hipStream_t s, bool single);
 // One launch that places chunk `place` (encoded by an earlier launch on the stream) and
 // encodes chunk `enc`; either may have no units.  Both need direct == 1.
 hipError_t launch_encode_place(const CArgsP& enc, const CArgsP& place, hipStream_t s);

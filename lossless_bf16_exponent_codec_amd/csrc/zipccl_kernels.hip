@@ -23,11 +23,17 @@
 //     Decoding replaces the code-0 byte of the v_perm table with the lane's first
 //     escape of each group of 4 columns, so only lanes with two escapes in one group
 //     patch bytes one by one.
-//   * Compress is two launches, neither of which waits on another workgroup: encode
-//     (A bytes, planes, escape counts; each unit's escapes staged contiguously in the
-//     workspace) and place (escape positions from the units' counts, compacted escapes,
-//     offset tables, headers); above 2^28 values a one-workgroup scan kernel computes
-//     the positions and a per-block place kernel follows.  The workspace keeps no state.
+//   * Compress is one launch (compress_single_kernel): encoding workgroups write the A
+//     bytes and planes, stage each unit's escapes contiguously in the workspace and then
+//     publish the unit's escape count in a ready word tagged with the call's tag; the
+//     grid's last workgroups (dispatched after every encoder) wait, bounded, for the
+//     ready words before their units, then compute escape positions, compact the
+//     escapes and write offset tables and headers.  What one workgroup hands to another
+//     goes through agent-scope (write-through) stores and loads, so no cache-wide
+//     write-back or invalidate is needed.  Under graph capture the same work is two
+//     launches that wait for nothing (encode_kernel, place_direct_kernel); above 2^28
+//     values a one-workgroup scan kernel computes the positions and a per-block place
+//     kernel follows.
 //     A sequence of chunk calls uses one launch per chunk that places the chunk before
 //     it while it encodes its own (encode_place_kernel: two roles by workgroup index).
 //   * Decompress: one half block per wave, one barrier to share the escape count of
@@ -78,6 +84,17 @@ __device__ inline uint2 load_nt(const uint2* p)
     return make_uint2(x.x, x.y);
 }
 __device__ inline uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
+// Agent-scope accesses for what one workgroup hands to another inside a launch (the
+// single-launch compress): stores written through to memory, loads that bypass the
+// non-coherent caches, so no cache-wide write-back or invalidate is needed.
+template <class T>
+__device__ inline void store_agent(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <class T>
+__device__ inline T load_agent(const T* p) { return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Waits until this wave's memory accesses have completed (agent-scope stores included).
+__device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0); expcnt, lgkmcnt untouched
 
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) { return __builtin_amdgcn_perm(hi, lo, sel); }
 
@@ -355,7 +372,7 @@ __device__ inline void seg_table(const Args& a, int s, uint32_t& lo, uint32_t& h
     }
 }
 
-template <bool kFull, class Args>
+template <bool kFull, bool kPublish, class Args>
 __device__ inline uint32_t encode_half(const Args& a, const CSeg& sg, uint32_t hb, uint32_t gh, const uint4 (&v)[4],
                                        uint32_t lane, const uint8_t* lut, const Transpose32& tc, uint8_t* s_esc)
 {
@@ -393,7 +410,10 @@ __device__ inline uint32_t encode_half(const Args& a, const CSeg& sg, uint32_t h
     const uint32_t run = min(half_ranks(cnt, start), kHalf);
 #pragma unroll
     for (int k = 0; k < 4; k++) stage_tile_escapes(te[k], start[k], s_esc);
-    if (lane == 0) a.counts[gh] = run;
+    if (lane == 0) {
+        if constexpr (kPublish) store_agent(a.counts + gh, run);
+        else a.counts[gh] = run;
+    }
     if (hb == 2 * K - 1) {   // zero padding of the plane and offset sections
         const uint32_t bpad = uint32_t(round128(192ull * T) - 192ull * T);
         uint8_t* bp = reinterpret_cast<uint8_t*>(B) + 192ull * T;
@@ -408,7 +428,9 @@ __device__ inline uint32_t encode_half(const Args& a, const CSeg& sg, uint32_t h
 // Encode: one workgroup per unit of 4 blocks, one half block per wave.  No workgroup
 // waits for another: each wave writes its tiles' A bytes and planes and its escape
 // count; the unit's escape exponents go, in value order, to the unit's staging area.
-template <class Args>
+// kPublish (single-launch compress): the unit's ready word is written last, after every
+// wave's counts and staged escapes have reached memory.
+template <bool kPublish, class Args>
 __device__ inline void encode_unit(const Args& a, uint32_t unit)
 {
     __shared__ uint8_t s_lut[256];
@@ -459,7 +481,7 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
     uint32_t run = 0;
     const uint32_t slot = unit * kEncWaves + wave;
     if (full) {
-        run = encode_half<true>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
+        run = encode_half<true, kPublish>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
     } else if (active) {
         if (sg.rows == nullptr) {
 #pragma unroll
@@ -468,7 +490,7 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
 #pragma unroll
             for (int k = 0; k < 4; k++) v[k] = load_lane_rows(sg, hb * 4 + k, lane, bad_row);
         }
-        run = encode_half<false>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
+        run = encode_half<false, kPublish>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
     }
     if (lane == 0) s_hcnt[wave] = run;
     __syncthreads();
@@ -480,16 +502,33 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
         total += c;
     }
     before = __builtin_amdgcn_readfirstlane(before);
-    if (tid == 0) a.unit_counts[unit] = total;   // for the place kernel's prefix sums
+    total = __builtin_amdgcn_readfirstlane(total);
+    if (!kPublish && tid == 0) a.unit_counts[unit] = total;   // for the place kernel's prefix sums
     // the unit's escapes, contiguous in value order: one run per unit for the place kernel
     uint8_t* stage = a.stage + uint64_t(unit) * kUnit + before;
     const uint8_t* esc_lds = s_esc[wave];
-    for (uint32_t k = lane; k < run; k += 64) stage[k] = esc_lds[k];
-    if (!active && lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
+    if constexpr (kPublish) {
+        for (uint32_t k = lane; k < run; k += 64) store_agent(stage + k, esc_lds[k]);
+        if (!active && lane == 0) store_agent(a.counts + slot, 0u);
+    } else {
+        for (uint32_t k = lane; k < run; k += 64) stage[k] = esc_lds[k];
+        if (!active && lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
+    }
     if (ballot(bad_row) && lane == 0) or_status(a.status, ZIPCCL_STATUS_BAD_INDEX);
+    if constexpr (kPublish) {
+        // What the placing workgroup reads (the half-block counts and the staged escapes)
+        // was stored at agent scope, i.e. written through to memory; each wave waits for
+        // its stores to complete, and after the barrier the ready word is written.  (A
+        // release fence would write back the XCD's whole L2 per wave: ~20x slower.)
+        wait_vm();
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(a.ready + unit, (a.tag << kReadyCountBits) | total, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-__global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a) { encode_unit(a, blockIdx.x); }
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(const CArgs a) { encode_unit<false>(a, blockIdx.x); }
 
 // Writes the 128-byte header block of a segment (lanes 0..31 of one wave).
 __device__ inline void write_header(const CSeg& sg, uint32_t table_lo, uint32_t table_hi, uint32_t lane,
@@ -624,14 +663,24 @@ __device__ inline bool copy_run(const Args& a, const uint8_t* src, uint32_t p, u
 // the wave's 1 KB LDS buffer, holding the first 512 staged bytes; more (rare) are
 // brought from the unit's staging area (stage) 1 KB at a time, 16 bytes per lane.
 // Returns true if a byte fell at or past esc_cap.
-template <class Args>
+template <bool kAgent, class Args>
 __device__ inline bool place_unit_escapes(const Args& a, uint8_t* lds, const uint8_t* stage, uint32_t p,
                                           uint32_t m, uint32_t lane)
 {
     bool over = copy_run(a, lds, p, 0, min(m, 512u), lane);
     for (uint32_t c0 = 512; c0 < m; c0 += 1024) {   // rare: more than 512 escapes in the unit
         const uint32_t o = c0 + 16 * lane;
-        const uint4 x = o + 16 <= kUnit ? reinterpret_cast<const uint4*>(stage + o)[0] : make_uint4(0, 0, 0, 0);
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (o + 16 <= kUnit) {
+            const uint4* q = reinterpret_cast<const uint4*>(stage + o);
+            if constexpr (kAgent) {
+                const uint64_t* q2 = reinterpret_cast<const uint64_t*>(q);
+                const uint64_t x0 = load_agent(q2), x1 = load_agent(q2 + 1);
+                x = make_uint4(uint32_t(x0), uint32_t(x0 >> 32), uint32_t(x1), uint32_t(x1 >> 32));
+            } else {
+                x = q[0];
+            }
+        }
         wave_lds_sync();   // earlier reads of the buffer are done
         reinterpret_cast<uint4*>(lds)[lane] = x;
         wave_lds_sync();
@@ -712,11 +761,65 @@ constexpr uint32_t kPlaceUnits = 8;
 constexpr uint32_t kPlaceThreads = 64 * kPlaceUnits;
 constexpr uint32_t kPrefixLoads = kDirectPrefixMaxUnits / (4 * kPlaceThreads);   // uint4 loads per thread
 
+// Bounded wait of the single-launch compress: polls for the ready word of unit u of this
+// call (tag) and returns its escape count; after kWaitPolls polls (about 0.1 s) sets
+// `late` and returns 0.  A placing workgroup is dispatched only after every encoder
+// workgroup of the launch (they come first in the grid), and encoders wait for nothing,
+// so the wait ends long before the limit.
+constexpr uint32_t kWaitPolls = 1u << 16;
+
+__device__ inline uint32_t wait_ready(const uint64_t* ready, uint32_t u, uint64_t tag, uint64_t w, bool& late)
+{
+    for (uint32_t k = 0; (w >> kReadyCountBits) != tag; k++) {
+        if (late || k >= kWaitPolls) {   // once one wait has run out, the thread waits no more
+            late = true;
+            return 0;
+        }
+        __builtin_amdgcn_s_sleep(8);
+        w = __hip_atomic_load(ready + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return uint32_t(w & ((1u << kReadyCountBits) - 1u));
+}
+
+// Unit counts of the single-launch compress, from the ready words of units [0, u_end)
+// (each thread takes every kPlaceThreads-th, 4 loads in flight): the escapes before
+// u_first (acc) and before u0 (accs); the counts of the group's own units go to s_ucnt.
 template <class Args>
+__device__ inline bool wait_unit_counts(const Args& a, uint32_t u_first, uint32_t u_end, uint32_t u0, uint32_t tid,
+                                        uint32_t* s_ucnt, uint32_t& acc, uint32_t& accs)
+{
+    constexpr uint32_t kPer = 4;
+    bool late = false;
+    acc = accs = 0;
+    for (uint32_t base = 0; base < u_end; base += kPer * kPlaceThreads) {
+        uint64_t w[kPer];
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; k++) {
+            const uint32_t u = base + tid + k * kPlaceThreads;
+            w[k] = u < u_end ? __hip_atomic_load(a.ready + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; k++) {
+            const uint32_t u = base + tid + k * kPlaceThreads;
+            if (u >= u_end) break;
+            const uint32_t c = wait_ready(a.ready, u, a.tag, w[k], late);
+            if (u < u_first) acc += c;
+            else s_ucnt[u - u_first] = c;
+            if (u < u0) accs += c;
+        }
+    }
+    return late;
+}
+
+// kWait (single-launch compress): the counts come from the encoders' ready words, waited
+// for; the encoder output read after that (half-block counts, staged escapes) is read
+// with agent-scope loads.
+template <bool kWait, class Args>
 __device__ inline void place_group(const Args& a, uint32_t group)
 {
     __shared__ uint32_t s_red[2][kPlaceUnits];
     __shared__ uint32_t s_ucnt[kPlaceUnits];
+    __shared__ uint32_t s_late;
     __shared__ __attribute__((aligned(16))) uint8_t s_head[kPlaceUnits][1024];   // staged escapes, per wave
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -725,38 +828,52 @@ __device__ inline void place_group(const Args& a, uint32_t group)
     const bool active = unit < a.total_units;
     const uint32_t slot0 = unit * kEncWaves;
     const uint8_t* stage = a.stage + uint64_t(unit) * kUnit;   // the unit's escapes, contiguous
-    const uint2 head = active ? reinterpret_cast<const uint2*>(stage)[lane] : make_uint2(0, 0);
+    uint2 head = make_uint2(0, 0);
     uint32_t hc[2 * kWaves];   // the unit's half-block escape counts
+    uint32_t acc = 0, accs = 0;
+    int s, s_first;
+    uint32_t u0;
+    if constexpr (!kWait) {
+        head = active ? reinterpret_cast<const uint2*>(stage)[lane] : make_uint2(0, 0);
 #pragma unroll
-    for (uint32_t k = 0; k < 2 * kWaves; k++) hc[k] = active ? a.counts[slot0 + k] : 0u;
-    if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
-    uint4 q[kPrefixLoads];     // unit_counts[0 .. u_first), 4 per load (u_first is a multiple of 8)
+        for (uint32_t k = 0; k < 2 * kWaves; k++) hc[k] = active ? a.counts[slot0 + k] : 0u;
+        if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
+        uint4 q[kPrefixLoads];     // unit_counts[0 .. u_first), 4 per load (u_first is a multiple of 8)
 #pragma unroll
-    for (uint32_t r = 0; r < kPrefixLoads; r++) {
-        const uint32_t i = 4 * (tid + r * kPlaceThreads);
-        q[r] = i < u_first ? *reinterpret_cast<const uint4*>(a.unit_counts + i) : make_uint4(0, 0, 0, 0);
+        for (uint32_t r = 0; r < kPrefixLoads; r++) {
+            const uint32_t i = 4 * (tid + r * kPlaceThreads);
+            q[r] = i < u_first ? *reinterpret_cast<const uint4*>(a.unit_counts + i) : make_uint4(0, 0, 0, 0);
+        }
+        // segment lookups meanwhile
+        s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
+        s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
+        u0 = a.seg[s_first].unit0;
+        // escapes before the group's first unit and before the first unit of its segment
+#pragma unroll
+        for (uint32_t r = 0; r < kPrefixLoads; r++) {
+            const uint32_t i = 4 * (tid + r * kPlaceThreads);
+            const uint32_t v[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
+#pragma unroll
+            for (uint32_t k = 0; k < 4; k++) {
+                acc += v[k];
+                if (i + k < u0) accs += v[k];
+            }
+        }
+    } else {
+        s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
+        s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
+        u0 = a.seg[s_first].unit0;
+        const uint32_t u_end = min(u_first + kPlaceUnits, a.total_units);
+        if (tid == 0) s_late = 0;
+        if (tid < kPlaceUnits && u_first + tid >= u_end) s_ucnt[tid] = 0;
+        __syncthreads();
+        const bool late = wait_unit_counts(a, u_first, u_end, u0, tid, s_ucnt, acc, accs);
+        if (late) s_late = 1;   // any thread; read after the barrier below
     }
-
-    // segment lookups meanwhile
-    const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
     const CSeg sg = a.seg[s];
     const uint32_t K = uint32_t(blocks_of(sg.n));
     const uint32_t b0 = (unit - sg.unit0) * kWaves;   // first block of the unit within the segment
-    const int s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
-    const uint32_t u0 = a.seg[s_first].unit0;
 
-    // escapes before the group's first unit and before the first unit of its segment
-    uint32_t acc = 0, accs = 0;
-#pragma unroll
-    for (uint32_t r = 0; r < kPrefixLoads; r++) {
-        const uint32_t i = 4 * (tid + r * kPlaceThreads);
-        const uint32_t v[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
-#pragma unroll
-        for (uint32_t k = 0; k < 4; k++) {
-            acc += v[k];
-            if (i + k < u0) accs += v[k];
-        }
-    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         acc += __shfl_xor(acc, o, 64);
@@ -766,8 +883,23 @@ __device__ inline void place_group(const Args& a, uint32_t group)
         s_red[0][wave] = acc;
         s_red[1][wave] = accs;
     }
-    reinterpret_cast<uint2*>(s_head[wave])[lane] = head;
+    if constexpr (!kWait) reinterpret_cast<uint2*>(s_head[wave])[lane] = head;
     __syncthreads();
+    if constexpr (kWait) {
+        if (s_late) {   // an encoder's count never arrived: place nothing, report it
+            if (tid == 0) or_status(a.status, ZIPCCL_STATUS_WAIT_LIMIT);
+            return;
+        }
+        if (!active) return;
+        // the encoder's agent-scope stores completed before its ready word was written:
+        // agent-scope loads see them (an acquire fence would invalidate the L2 per wave)
+        const uint64_t h = load_agent(reinterpret_cast<const uint64_t*>(stage) + lane);
+        head = make_uint2(uint32_t(h), uint32_t(h >> 32));
+#pragma unroll
+        for (uint32_t k = 0; k < 2 * kWaves; k++) hc[k] = load_agent(a.counts + slot0 + k);
+        reinterpret_cast<uint2*>(s_head[wave])[lane] = head;
+        wave_lds_sync();
+    }
     if (!active) return;
     uint32_t pre = 0, first_base = 0;
 #pragma unroll
@@ -786,7 +918,7 @@ __device__ inline void place_group(const Args& a, uint32_t group)
         for (uint32_t w = 0; w < sg.unit0 - u_first; w++) base += s_ucnt[w];
     }
     // the unit's escapes in one run; its blocks' positions from its 8 half-block counts
-    if (ballot(place_unit_escapes(a, s_head[wave], stage, upos, s_ucnt[wave], lane)) && lane == 0)
+    if (ballot(place_unit_escapes<kWait>(a, s_head[wave], stage, upos, s_ucnt[wave], lane)) && lane == 0)
         or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     uint32_t p = upos;
 #pragma unroll
@@ -798,7 +930,18 @@ __device__ inline void place_group(const Args& a, uint32_t group)
     }
 }
 
-__global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a) { place_group(a, blockIdx.x); }
+__global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a) { place_group<false>(a, blockIdx.x); }
+
+// Compress in one launch: workgroups 0 .. total_units - 1 encode (as encode_kernel) and
+// publish each unit's escape count in its ready word; the last ceil(total_units / 8)
+// place (as place_direct_kernel) once the ready words they need carry this call's tag.
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void compress_single_kernel(const CArgs a)
+{
+    static_assert(kEncThreads == kPlaceThreads, "both roles use the same workgroup size");
+    if (blockIdx.x < a.total_units) encode_unit<true>(a, blockIdx.x);
+    else place_group<true>(a, blockIdx.x - a.total_units);
+}
 
 // Two consecutive chunks of the pipeline in one launch: the first place_groups
 // workgroups place chunk p (its encode ran in an earlier launch on the same stream, and
@@ -809,8 +952,8 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(8))
 void encode_place_kernel(const CArgsP e, const CArgsP p, uint32_t place_groups)
 {
     static_assert(kEncThreads == kPlaceThreads, "both roles use the same workgroup size");
-    if (blockIdx.x < place_groups) place_group(p, blockIdx.x);
-    else encode_unit(e, blockIdx.x - place_groups);
+    if (blockIdx.x < place_groups) place_group<false>(p, blockIdx.x);
+    else encode_unit<false>(e, blockIdx.x - place_groups);
 }
 
 // --------------------------------------------------------------------------------
@@ -1258,8 +1401,13 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
 
 }  // namespace
 
-hipError_t launch_compress(const CArgs& a, hipStream_t s)
+hipError_t launch_compress(const CArgs& a, hipStream_t s, bool single)
 {
+    if (single && a.direct) {
+        const uint32_t groups = (a.total_units + kPlaceUnits - 1) / kPlaceUnits;
+        hipLaunchKernelGGL(compress_single_kernel, dim3(a.total_units + groups), dim3(kEncThreads), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.total_units > 0) hipLaunchKernelGGL(encode_kernel, dim3(a.total_units), dim3(kEncThreads), 0, s, a);
     if (a.direct) {
         hipLaunchKernelGGL(place_direct_kernel, dim3((a.total_units + kPlaceUnits - 1) / kPlaceUnits),

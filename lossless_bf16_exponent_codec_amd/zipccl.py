@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libzipccl.so")
 
 OK, ERR_INVALID, ERR_ALIGN, ERR_SIZE, ERR_HIP, ERR_CORRUPT = range(6)
-STATUS_ESC_OVERFLOW, STATUS_CORRUPT, STATUS_BAD_INDEX = 1, 2, 4
+STATUS_ESC_OVERFLOW, STATUS_CORRUPT, STATUS_BAD_INDEX, STATUS_WAIT_LIMIT = 1, 2, 4, 8
 MAX_SEGMENTS, MAX_PEERS = 64, 16
 FORMAT_VERSION, MAGIC = 1, 0x3143435A
 

@@ -685,3 +685,122 @@ def test_scan_path_empty_and_overflow(Z, scan_path):
     assert r["status"] & Z.STATUS_ESC_OVERFLOW
     st, esc, ne, rc = O.compress_batch([x], oracle_tables([p]))
     assert np.array_equal(r["static_h"], st) and np.array_equal(r["esc_h"][:1000], esc[:1000])
+
+
+# ------------------------------------------------------------------------------------
+# one launch (encoders, then placing workgroups that wait for the encoders' ready words)
+# against the two-launch path; reused workspaces; graph capture
+# ------------------------------------------------------------------------------------
+@pytest.fixture
+def two_launches(monkeypatch):
+    monkeypatch.setenv("ZIPCCL_SINGLE_LAUNCH", "0")
+    yield
+
+
+def mixed_batch(seed, nseg=40):
+    rng = np.random.default_rng(seed)
+    segs, plans = [], []
+    for k in range(nseg):
+        n = int(rng.choice([0, 1, 700, 4096, 16384, 20000, 70001, 300000, 1 << 20]))
+        s = float(10 ** rng.uniform(-4, 1))
+        segs.append(W.gaussian_bf16(n, s, 5000 + 100 * seed + k))
+        plans.append(Z_plan(s))
+    return segs, plans
+
+
+def Z_plan(s):
+    from lossless_bf16_exponent_codec_amd import zipccl
+    return zipccl.plan(sigma=s)
+
+
+def test_two_launch_path_many_segments(Z, two_launches):
+    segs, plans = mixed_batch(1)
+    round_trip(Z, segs, plans)
+
+
+def test_two_launch_path_edges_and_overflow(Z, two_launches):
+    for n in (1, 4097, 16385, 250001):
+        round_trip(Z, [W.gaussian_bf16(n, 0.02, n)], [Z.plan(sigma=0.02)])
+    x = W.gaussian_bf16(50000, 1.0, 5)
+    p = Z.plan(table=[1, 2, 3, 4, 5, 6, 7])
+    r = gpu_compress(Z, [x], [p], esc_cap=1000)
+    assert r["status"] == Z.STATUS_ESC_OVERFLOW
+    st, esc, ne, rc = O.compress_batch([x], oracle_tables([p]))
+    assert np.array_equal(r["static_h"], st) and np.array_equal(r["esc_h"][:1000], esc[:1000])
+
+
+def test_single_launch_overflow_status_only(Z):
+    # the escape overflow is the only status bit: the placing workgroups never ran out of
+    # their bounded wait
+    x = W.gaussian_bf16(300000, 1.0, 6)
+    p = Z.plan(table=[1, 2, 3, 4, 5, 6, 7])
+    r = gpu_compress(Z, [x], [p], esc_cap=5000)
+    assert r["status"] == Z.STATUS_ESC_OVERFLOW
+    st, esc, ne, rc = O.compress_batch([x], oracle_tables([p]))
+    assert np.array_equal(r["static_h"], st) and np.array_equal(r["esc_h"][:5000], esc[:5000])
+
+
+def test_single_launch_stale_ready_words(Z):
+    # one workspace, calls of different sizes in a row: a call with fewer units leaves the
+    # later ready words of the call before it, and a call that follows a larger one finds
+    # that call's words for every unit.  Each call must wait for its own.  The workspace
+    # starts as garbage (0xFF: every ready word claims the largest tag).
+    big = 4 << 20
+    ws = torch.full((Z.workspace_size(big, 8),), 0xFF, dtype=torch.uint8, device="cuda")
+    batches = [([W.gaussian_bf16(big, 0.02, 21)], [Z.plan(sigma=0.02)]),
+               ([W.gaussian_bf16(n, 1e-3, 22 + n) for n in (100000, 1 << 20, 0, 7)], [Z.plan(sigma=1e-3)] * 4),
+               ([W.gaussian_bf16(big, 0.5, 23)], [Z.plan(sigma=0.5)]),
+               ([W.gaussian_bf16(3 << 20, 1.0, 24)], [Z.plan(table=[1, 2, 3, 4, 5, 6, 7])])]   # all escapes
+    for rep in range(2):
+        for segs, plans in batches:
+            print(f"stale ready words rep={rep} sizes={[s.size for s in segs]}", flush=True)
+            r = gpu_compress(Z, segs, plans, workspace=ws)
+            check_against_oracle(Z, segs, plans, r)
+
+
+def test_single_and_two_launch_paths_agree(Z, monkeypatch):
+    segs, plans = mixed_batch(2, nseg=24)
+    r1 = gpu_compress(Z, segs, plans)
+    monkeypatch.setenv("ZIPCCL_SINGLE_LAUNCH", "0")
+    r2 = gpu_compress(Z, segs, plans)
+    assert r1["status"] == r2["status"] == 0
+    assert np.array_equal(r1["static_h"], r2["static_h"])
+    assert np.array_equal(r1["n_esc"], r2["n_esc"])
+    t = int(r1["n_esc"][-1])
+    assert np.array_equal(r1["esc_h"][:t], r2["esc_h"][:t])
+    check_against_oracle(Z, segs, plans, r1)
+
+
+def test_compress_in_captured_graph(Z):
+    # under graph capture the call takes the two-launch path (no per-call tag is baked
+    # into the graph); every replay, with new input between replays, matches the oracle
+    n = [300000, 4096, 70001]
+    sig = [0.02, 1e-3, 0.5]
+    plans = [Z.plan(sigma=s) for s in sig]
+    inputs = [dev_bf16(W.gaussian_bf16(k, s, 40 + i)) for i, (k, s) in enumerate(zip(n, sig))]
+    total_static = sum(Z.static_size(k) for k in n)
+    static = torch.full((total_static,), POISON, dtype=torch.uint8, device="cuda")
+    esc = torch.full((sum(n),), POISON, dtype=torch.uint8, device="cuda")
+    n_esc = torch.full((len(n) + 1,), -1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(Z.workspace_size(sum(n), len(n)), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        Z.PreparedCompress(inputs, static, esc, ws, n_esc, status).run(plans)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Z.PreparedCompress(inputs, static, esc, ws, n_esc, status).run(plans)
+    for rep in range(4):
+        segs = [W.gaussian_bf16(k, s, 700 + 10 * rep + i) for i, (k, s) in enumerate(zip(n, sig))]
+        for t, x in zip(inputs, segs):
+            t.copy_(dev_bf16(x))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"graph replay {rep}", flush=True)
+        r = dict(status=int(status.item()), n_esc=n_esc.cpu().numpy(), static_h=static.cpu().numpy(),
+                 esc_h=esc.cpu().numpy())
+        check_against_oracle(Z, segs, plans, r)
