@@ -226,9 +226,9 @@ def bench_rs(torch, Z, W, iters):
 
     comp = [Z.PreparedCompress([p[c * chunk:(c + 1) * chunk] for p in peers], static[c * P * S:(c + 1) * P * S],
                                esc[c * P * chunk:(c + 1) * P * chunk], ws, n_esc[c], status) for c in range(nch)]
-    # the same 32 calls through zipccl_compress_chunks: one launch per chunk, each placing
-    # the chunk before it
-    ws2 = torch.zeros(2 * Z.workspace_size(P * chunk, P), dtype=torch.uint8, device="cuda")
+    # the same 32 calls through zipccl_compress_chunks: 8 chunks (56 segments) share a
+    # launch, with a workspace that holds them (as the pipeline's does)
+    ws2 = torch.zeros(Z.workspace_size(8 * P * chunk, 8 * P), dtype=torch.uint8, device="cuda")
     comp_seq = Z.PreparedCompressChunks([[p[c * chunk:(c + 1) * chunk] for p in peers] for c in range(nch)],
                                         [static[c * P * S:(c + 1) * P * S] for c in range(nch)],
                                         [esc[c * P * chunk:(c + 1) * P * chunk] for c in range(nch)], ws2,

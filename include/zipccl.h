@@ -171,15 +171,15 @@ zipccl_status zipccl_compress_device_plans(const zipccl_segment_t* segs, int nse
  * pipeline of the CCCL page's pipeline section issues them: chunk k is what
  *   zipccl_compress(segs + k * nseg, nseg, static_out[k], static_cap[k], esc_out[k],
  *                   esc_cap[k], ..., n_esc_out + k * (nseg + 1), status, stream)
- * writes, byte for byte (each chunk's escapes and esc_offsets are its own), but one
- * kernel launch places chunk k - 1 while it encodes chunk k, so the place work of one
- * chunk overlaps the encode of the next: nchunks + 1 launches instead of 2 * nchunks.
+ * writes, byte for byte (each chunk's escapes and esc_offsets are its own), but
+ * consecutive chunks share a kernel launch (up to 8 chunks and 64 segments per launch)
+ * while the workspace holds them all, so that a launch has enough work to fill the GPU.
  *   segs        host array of nchunks * nseg segments, chunk after chunk; 1 <= nseg <=
  *               ZIPCCL_MAX_PEERS
  *   static_out, static_cap, esc_out, esc_cap   host arrays of nchunks entries
- *   workspace   device, 256-byte aligned, at least 2 * zipccl_workspace_size(v, nseg)
- *               bytes where v is the most values in one chunk (consecutive chunks use
- *               its two halves in turn)
+ *   workspace   device, 256-byte aligned, at least zipccl_workspace_size(v, nseg) bytes
+ *               where v is the most values in one chunk; chunks k .. j share a launch
+ *               when it holds zipccl_workspace_size(their values, their segments)
  *   n_esc_out   optional device u64[nchunks * (nseg + 1)]
  * Every chunk is checked before anything is enqueued.  nchunks == 0 does nothing.
  * Errors: as zipccl_compress, per chunk; INVALID also for nseg outside 1..ZIPCCL_MAX_PEERS

@@ -156,6 +156,21 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg)
 
 namespace {
 
+// Workspace sections of a launch of `units` units (the sizes depend on the count).
+void set_workspace(CArgs& a, void* workspace, uint64_t units)
+{
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.counts = reinterpret_cast<uint32_t*>(w);
+    w += ws_counts_bytes(units);
+    a.pos = reinterpret_cast<uint32_t*>(w);
+    w += ws_pos_bytes(units);
+    a.unit_counts = reinterpret_cast<uint32_t*>(w);
+    w += ws_units_bytes(units);
+    a.ready = reinterpret_cast<uint64_t*>(w);
+    w += ws_ready_bytes(units);
+    a.stage = w;
+}
+
 // Completes the compress arguments once a.seg[0..nseg) holds src, rows, row_len,
 // src_rows, n and the table of each segment.
 zipccl_status prepare_compress(CArgs& a, int nseg, void* static_out, uint64_t static_cap, void* esc_out,
@@ -177,15 +192,17 @@ zipccl_status prepare_compress(CArgs& a, int nseg, void* static_out, uint64_t st
     if (st_off > static_cap) return ZIPCCL_ERR_SIZE;
     if (ws_bytes(units) > workspace_bytes) return ZIPCCL_ERR_SIZE;
     if (esc_cap > 0 && !esc_out) return ZIPCCL_ERR_INVALID;
-    a.esc = static_cast<uint8_t*>(esc_out);
-    a.esc_cap = esc_out ? esc_cap : 0;
-    uint8_t* w = static_cast<uint8_t*>(workspace);
-    a.counts = reinterpret_cast<uint32_t*>(w);
-    a.pos = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(units));
-    a.unit_counts = reinterpret_cast<uint32_t*>(w + ws_counts_bytes(units) + ws_pos_bytes(units));
-    a.ready = reinterpret_cast<uint64_t*>(w + ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units));
-    a.stage = w + ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units) + ws_ready_bytes(units);
-    a.n_esc_out = n_esc_out;
+    CCall& c = a.call[0];
+    c.esc = static_cast<uint8_t*>(esc_out);
+    c.esc_cap = esc_out ? esc_cap : 0;
+    c.n_esc_out = n_esc_out;
+    c.seg0 = 0;
+    c.nseg = uint32_t(nseg);
+    c.unit0 = 0;
+    c.block_end = uint32_t(blocks);
+    for (int s = 0; s < nseg; s++) a.seg[s].call = 0;
+    a.ncalls = 1;
+    set_workspace(a, workspace, units);
     a.status = status;
     a.nseg = nseg;
     a.total_units = uint32_t(units);
@@ -202,28 +219,6 @@ zipccl_status compress_segments(CArgs& a, int nseg, void* static_out, uint64_t s
                                            workspace_bytes, n_esc_out, status))
         return r;
     return hip_status(compress_launch(a, static_cast<hipStream_t>(stream)));
-}
-
-// The arguments of a call with at most kMaxPeers segments in the pipeline's smaller form.
-CArgsP chunk_args(const CArgs& a)
-{
-    CArgsP c;
-    std::memset(&c, 0, sizeof(c));
-    for (int s = 0; s < a.nseg && s < kMaxPeers; s++) c.seg[s] = a.seg[s];
-    c.esc = a.esc;
-    c.esc_cap = a.esc_cap;
-    c.counts = a.counts;
-    c.pos = a.pos;
-    c.unit_counts = a.unit_counts;
-    c.stage = a.stage;
-    c.n_esc_out = a.n_esc_out;
-    c.status = a.status;
-    c.nseg = a.nseg;
-    c.total_units = a.total_units;
-    c.total_blocks = a.total_blocks;
-    c.direct = a.direct;
-    c.dplans = a.dplans;
-    return c;
 }
 
 zipccl_status check_compress_buffers(int nseg, void* static_out, void* workspace, uint64_t* n_esc_out,
@@ -259,27 +254,46 @@ zipccl_status fill_segments(CArgs& a, const zipccl_segment_t* segs, int nseg, bo
     return ZIPCCL_OK;
 }
 
-// Launches prepared chunk calls in order on one stream.  A chunk whose positions the
-// place kernel computes itself (direct) is placed by the launch that encodes the next
-// such chunk; the last one by a launch of its own.
-zipccl_status launch_chunks(const std::vector<CArgs>& calls, hipStream_t stream)
+// Launches prepared chunk calls in order on one stream.  Consecutive calls whose
+// positions the place workgroups compute themselves (direct) share a launch while the
+// launch has room (kMaxCalls calls, kMaxSegs segments, kDirectPrefixMaxUnits units) and
+// the workspace holds all their units; each keeps its own outputs and escape numbering.
+zipccl_status launch_chunks(const std::vector<CArgs>& calls, void* workspace, uint64_t workspace_bytes,
+                            hipStream_t stream)
 {
-    CArgsP prev, none;
-    std::memset(&none, 0, sizeof(none));
-    bool have_prev = false;
-    for (const CArgs& a : calls) {
-        if (!a.direct || a.nseg > kMaxPeers) {   // scan-kernel positions or many segments: its own launches
-            CArgs c = a;
-            if (hipError_t e = compress_launch(c, stream)) return hip_status(e);
-            continue;
+    const uint64_t max_units = direct_prefix_max_units();
+    size_t k = 0;
+    while (k < calls.size()) {
+        CArgs b = calls[k];
+        size_t j = k + 1;
+        if (b.direct && !b.dplans) {
+            for (; j < calls.size() && b.ncalls < kMaxCalls; j++) {
+                const CArgs& c = calls[j];
+                const uint64_t units = uint64_t(b.total_units) + c.total_units;
+                if (!c.direct || c.dplans || b.nseg + c.nseg > kMaxSegs || units > max_units ||
+                    ws_bytes(units) > workspace_bytes)
+                    break;
+                for (int s = 0; s < c.nseg; s++) {
+                    CSeg g = c.seg[s];
+                    g.unit0 += b.total_units;
+                    g.block0 += b.total_blocks;
+                    g.call = uint32_t(b.ncalls);
+                    b.seg[b.nseg + s] = g;
+                }
+                CCall cc = c.call[0];
+                cc.seg0 = uint32_t(b.nseg);
+                cc.unit0 = b.total_units;
+                cc.block_end = b.total_blocks + c.total_blocks;
+                b.call[b.ncalls++] = cc;
+                b.nseg += c.nseg;
+                b.total_units = uint32_t(units);
+                b.total_blocks += c.total_blocks;
+            }
+            set_workspace(b, workspace, b.total_units);
         }
-        const CArgsP cur = chunk_args(a);
-        if (hipError_t e = launch_encode_place(cur, have_prev ? prev : none, stream)) return hip_status(e);
-        prev = cur;
-        have_prev = true;
+        if (hipError_t e = compress_launch(b, stream)) return hip_status(e);
+        k = j;
     }
-    if (have_prev)
-        if (hipError_t e = launch_encode_place(none, prev, stream)) return hip_status(e);
     return ZIPCCL_OK;
 }
 
@@ -341,8 +355,6 @@ zipccl_status zipccl_compress_chunks(const zipccl_segment_t* segs, int nseg, int
     if (nchunks == 0) return ZIPCCL_OK;
     if (!segs || !static_out || !static_cap || !esc_out || !esc_cap || !workspace) return ZIPCCL_ERR_INVALID;
     if (!aligned(workspace, 256)) return ZIPCCL_ERR_ALIGN;
-    // two workspaces: consecutive chunks alternate
-    const uint64_t half = (workspace_bytes / 2) & ~uint64_t(255);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     std::vector<CArgs> calls;   // every chunk is checked before anything is enqueued
     try {
@@ -356,10 +368,10 @@ zipccl_status zipccl_compress_chunks(const zipccl_segment_t* segs, int nseg, int
         CArgs& a = calls[size_t(k)];
         if (zipccl_status r = fill_segments(a, segs + uint64_t(k) * nseg, nseg)) return r;
         if (zipccl_status r = prepare_compress(a, nseg, static_out[k], static_cap[k], esc_out[k], esc_cap[k],
-                                               ws + (k & 1) * half, half, ne, status))
+                                               ws, workspace_bytes, ne, status))
             return r;
     }
-    return launch_chunks(calls, static_cast<hipStream_t>(stream));
+    return launch_chunks(calls, ws, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 zipccl_status zipccl_compress_gather(const zipccl_gather_segment_t* segs, int nseg, void* static_out,
@@ -663,15 +675,18 @@ uint32_t pipeline_group(int npeers, uint64_t chunk)
     return g;
 }
 
-// Scratch layout: two compress workspaces (consecutive chunks alternate, so that one
-// launch can place a chunk while it encodes the next), then 2 * group chunk slots (a
-// ring of two groups), each holding the chunk's npeers static parts and room for all
-// its escapes.
+// Scratch layout: one compress workspace that holds as many chunks as share a compress
+// launch (at most kMaxCalls, kMaxSegs segments, kDirectPrefixMaxUnits units), then
+// 2 * group chunk slots (a ring of two groups), each holding the chunk's npeers static
+// parts and room for all its escapes.
 void pipeline_layout(int npeers, uint64_t chunk, uint64_t& slot_static, uint64_t& slot_esc, uint64_t& ws)
 {
     slot_static = uint64_t(npeers) * static_bytes_of(chunk);
     slot_esc = (uint64_t(npeers) * chunk + 255) & ~uint64_t(255);
-    ws = (zipccl_workspace_size(uint64_t(npeers) * chunk, npeers) + 255) & ~uint64_t(255);
+    uint64_t b = std::min<uint64_t>({uint64_t(pipeline_group(npeers, chunk)), uint64_t(kMaxCalls),
+                                     uint64_t(kMaxSegs / npeers)});
+    while (b > 1 && b * units_of(chunk) * uint64_t(npeers) > kDirectPrefixMaxUnits) b--;
+    ws = (zipccl_workspace_size(b * uint64_t(npeers) * chunk, int(b) * npeers) + 255) & ~uint64_t(255);
 }
 
 }  // namespace
@@ -681,7 +696,7 @@ uint64_t zipccl_pipeline_scratch_size(int npeers, uint64_t chunk)
     if (npeers < 1 || npeers > kMaxPeers || chunk == 0) return 0;
     uint64_t ss, se, ws;
     pipeline_layout(npeers, chunk, ss, se, ws);
-    return 2 * ws + 2ull * pipeline_group(npeers, chunk) * (ss + se);
+    return ws + 2ull * pipeline_group(npeers, chunk) * (ss + se);
 }
 
 zipccl_status zipccl_pipeline_create(int npeers, uint64_t chunk, void* scratch, uint64_t scratch_bytes,
@@ -730,7 +745,7 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
     const uint64_t nchunks = (n + pipe->chunk - 1) / pipe->chunk;
     const uint64_t G = pipe->group;
     hipStream_t sa = pipe->sa, sb = pipe->sb;
-    uint8_t* slots = pipe->scratch + 2 * pipe->ws_size;
+    uint8_t* slots = pipe->scratch + pipe->ws_size;
     const uint64_t slot_bytes = pipe->slot_static + pipe->slot_esc;
     for (uint64_t c0 = 0; c0 < nchunks; c0 += G) {
         const int half = int((c0 / G) & 1);   // which half of the ring this group uses
@@ -738,8 +753,7 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
         // the group two hand-offs back used these slots: its reduction must be done
         if (pipe->reduced_recorded[half] && hipStreamWaitEvent(sa, pipe->reduced[half], 0) != hipSuccess)
             return ZIPCCL_ERR_HIP;
-        // compress the group on stream a (one launch per chunk: each places the chunk
-        // before it while it encodes its own)
+        // compress the group on stream a (its chunks share launches: up to kMaxCalls each)
         zipccl_segment_t segs[16 * kMaxPeers];
         void* st_out[16];
         void* esc_out[16];
@@ -760,7 +774,7 @@ zipccl_status zipccl_pipeline_reduce(zipccl_pipeline* pipe, const void* const* p
             esc_cap[k] = pipe->slot_esc;
         }
         if (zipccl_status r = zipccl_compress_chunks(segs, P, int(c1 - c0), st_out, st_cap, esc_out, esc_cap,
-                                                     pipe->scratch, 2 * pipe->ws_size, nullptr, status, sa))
+                                                     pipe->scratch, pipe->ws_size, nullptr, status, sa))
             return r;
         if (hipEventRecord(pipe->compressed[half], sa) != hipSuccess ||
             hipStreamWaitEvent(sb, pipe->compressed[half], 0) != hipSuccess)

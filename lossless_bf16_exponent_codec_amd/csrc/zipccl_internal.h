@@ -56,34 +56,43 @@ struct CSeg {              // compress: one segment
     uint32_t table_hi;     // table[4..6], byte 3 = 0
     uint32_t row_len;      // gathered segment: values per row (a multiple of 8, >= 512)
     uint32_t src_rows;     // gathered segment: rows of the matrix (indices must be below)
-    uint32_t pad;
+    uint32_t call;         // the compress call (CCall) the segment belongs to
 };
 
-template <int kSegs>
-struct CArgsN {
-    CSeg seg[kSegs];
+// One compress call of a launch: a launch may compress several independent calls (the
+// chunks of a sequence), each with its own escape buffer, escape positions counted from
+// its own first escape, and its own escape-count output.  Its segments, units and
+// blocks are consecutive in the launch.
+struct CCall {
     uint8_t* esc;
     uint64_t esc_cap;
+    uint64_t* n_esc_out;   // nseg + 1 entries or null
+    uint32_t seg0;         // first segment of the call
+    uint32_t nseg;
+    uint32_t unit0;        // first unit of the call
+    uint32_t block_end;    // one past the call's last block (launch-wide numbering)
+};
+constexpr int kMaxCalls = 8;
+
+struct CArgs {
+    CSeg seg[kMaxSegs];
+    CCall call[kMaxCalls];
     uint32_t* counts;      // workspace: escapes per half-block slot
     uint32_t* pos;         // workspace: launch-wide position of each slot's first escape
     uint32_t* unit_counts; // workspace: escapes per workgroup unit
     uint8_t* stage;        // workspace: kUnit bytes per unit
     uint64_t* ready;       // workspace: a ready word per unit (single-launch compress)
-    uint64_t tag;          // this call's tag in the ready words (single-launch compress)
-    uint64_t* n_esc_out;   // nseg + 1 entries or null
+    uint64_t tag;          // this launch's tag in the ready words (single-launch compress)
     uint32_t* status;      // or null
     const uint8_t* dplans; // device plans (8 bytes per segment) replacing the segments' tables, or null
     int32_t nseg;
+    int32_t ncalls;        // 1 unless direct
     uint32_t total_units;
     uint32_t total_blocks;
     uint32_t direct;       // 1: the place kernel computes positions from unit_counts
 };
 
-using CArgs = CArgsN<kMaxSegs>;    // one compress call
-using CArgsP = CArgsN<kMaxPeers>;  // one chunk of the pipeline: a segment per peer
-
 static_assert(sizeof(CArgs) <= 4096, "kernel arguments are limited to 4 KiB");
-static_assert(2 * sizeof(CArgsP) + 16 <= 4096, "the fused encode + place launch takes two chunks' arguments");
 
 struct DSeg {              // decompress: one segment
     const uint8_t* src;    // static part
@@ -136,9 +145,6 @@ __host__ __device__ inline uint64_t static_bytes_of(uint64_t n) { return offsets
 // encoders have published their ready words (a.ready, a.tag); else encode, then place
 // (or scan + place) in launches of their own.  single needs direct == 1.
 hipError_t launch_compress(const CArgs& a, hipStream_t s, bool single);
-// One launch that places chunk `place` (encoded by an earlier launch on the stream) and
-// encodes chunk `enc`; either may have no units.  Both need direct == 1.
-hipError_t launch_encode_place(const CArgsP& enc, const CArgsP& place, hipStream_t s);
 hipError_t launch_decompress(const DArgs& a, hipStream_t s);
 // Plans from a strided sample of each segment (one workgroup per segment).
 struct EArgs {

@@ -34,8 +34,9 @@
 //     launches that wait for nothing (encode_kernel, place_direct_kernel); above 2^28
 //     values a one-workgroup scan kernel computes the positions and a per-block place
 //     kernel follows.
-//     A sequence of chunk calls uses one launch per chunk that places the chunk before
-//     it while it encodes its own (encode_place_kernel: two roles by workgroup index).
+//     One launch may compress several independent calls (the chunks of a sequence):
+//     each segment names its call, and positions, offsets and headers count from the
+//     first escape of the call.
 //   * Decompress: one half block per wave, one barrier to share the escape count of
 //     the first half of each block; each segment has its own escape buffer.
 //     Decode-accumulate: one workgroup per block, one wave per tile, all peers of a
@@ -630,11 +631,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
         carry += total;
     }
     if (tid == 0) a.pos[Kt] = carry;
-    if (tid == 0 && a.n_esc_out && Kt == 0) a.n_esc_out[a.nseg] = 0;
+    uint64_t* const ne = a.call[0].n_esc_out;   // the scan path has one call
+    if (tid == 0 && ne && Kt == 0) ne[a.nseg] = 0;
     if (Kt == 0 && wave == 0) {   // only empty segments: every header says offset 0
         for (int s = 0; s < a.nseg; s++) {
             write_seg_header(a, s, lane, 0u, 0u);
-            if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = 0;
+            if (lane == 0 && ne) ne[s] = 0;
         }
     }
 }
@@ -642,32 +644,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
 // Copies len bytes from LDS (src) to esc[p + off ...], lane l writing bytes l, l + 64, ...
 // so that each store instruction covers 64 consecutive bytes.  Bytes at or past esc_cap
 // are dropped (returns true if there were any).
-template <class Args>
-__device__ inline bool copy_run(const Args& a, const uint8_t* src, uint32_t p, uint32_t off, uint32_t len,
+__device__ inline bool copy_run(const CCall& c, const uint8_t* src, uint32_t p, uint32_t off, uint32_t len,
                                 uint32_t lane)
 {
-    uint8_t* dst = a.esc + p + off;
-    if (uint64_t(p) + off + len <= a.esc_cap) {   // the common case: no per-byte check
+    uint8_t* dst = c.esc + p + off;
+    if (uint64_t(p) + off + len <= c.esc_cap) {   // the common case: no per-byte check
         for (uint32_t k = lane; k < len; k += 64) dst[k] = src[k];
         return false;
     }
     bool over = false;
     for (uint32_t k = lane; k < len; k += 64) {
-        if (uint64_t(p) + off + k < a.esc_cap) dst[k] = src[k];
+        if (uint64_t(p) + off + k < c.esc_cap) dst[k] = src[k];
         else over = true;
     }
     return over;
 }
 
-// Copies the m staged escapes of one unit to esc[p ...] (every lane of one wave).  lds:
+// Copies the m staged escapes of one unit to its call's esc[p ...] (every lane of one wave).  lds:
 // the wave's 1 KB LDS buffer, holding the first 512 staged bytes; more (rare) are
 // brought from the unit's staging area (stage) 1 KB at a time, 16 bytes per lane.
 // Returns true if a byte fell at or past esc_cap.
-template <bool kAgent, class Args>
-__device__ inline bool place_unit_escapes(const Args& a, uint8_t* lds, const uint8_t* stage, uint32_t p,
+template <bool kAgent>
+__device__ inline bool place_unit_escapes(const CCall& c, uint8_t* lds, const uint8_t* stage, uint32_t p,
                                           uint32_t m, uint32_t lane)
 {
-    bool over = copy_run(a, lds, p, 0, min(m, 512u), lane);
+    bool over = copy_run(c, lds, p, 0, min(m, 512u), lane);
     for (uint32_t c0 = 512; c0 < m; c0 += 1024) {   // rare: more than 512 escapes in the unit
         const uint32_t o = c0 + 16 * lane;
         uint4 x = make_uint4(0, 0, 0, 0);
@@ -684,38 +685,40 @@ __device__ inline bool place_unit_escapes(const Args& a, uint8_t* lds, const uin
         wave_lds_sync();   // earlier reads of the buffer are done
         reinterpret_cast<uint4*>(lds)[lane] = x;
         wave_lds_sync();
-        over = copy_run(a, lds, p, c0, min(m - c0, 1024u), lane) || over;
+        over = copy_run(c, lds, p, c0, min(m - c0, 1024u), lane) || over;
     }
     return over;
 }
 
-// Offset-table entry of block gb (launch-wide) of segment sg (index s), whose escapes
-// occupy [p0, p2) (base = the segment's first escape); the segment header from the
-// segment's last block, and the headers of empty segments next to it.
+// Offset-table entry of block gb (launch-wide) of segment sg (index s, of call c), whose
+// escapes occupy [p0, p2) of the call's escapes (base = the segment's first escape); the
+// segment header from the segment's last block, and the headers of the call's empty
+// segments next to it.
 template <class Args>
-__device__ inline void place_block_tables(const Args& a, const CSeg& sg, int s, uint32_t gb, uint32_t p0,
-                                          uint32_t p2, uint32_t base, uint32_t lane)
+__device__ inline void place_block_tables(const Args& a, const CCall& c, const CSeg& sg, int s, uint32_t gb,
+                                          uint32_t p0, uint32_t p2, uint32_t base, uint32_t lane)
 {
     const uint32_t K = uint32_t(blocks_of(sg.n));
+    const int e0 = int(c.seg0), e1 = int(c.seg0 + c.nseg);   // the call's segments
     if (lane == 0) reinterpret_cast<uint32_t*>(sg.dst + offsets_off(sg.n))[gb - sg.block0] = p0 - base;
     if (gb == sg.block0 + K - 1) {
         write_seg_header(a, s, lane, p2 - base, base);
-        if (lane == 0 && a.n_esc_out) a.n_esc_out[s] = p2 - base;
+        if (lane == 0 && c.n_esc_out) c.n_esc_out[s - e0] = p2 - base;
     }
     // empty segments just before this one start where it starts; those after the
-    // launch's last block start at the end
+    // call's last block start at the end
     if (gb == sg.block0) {
-        for (int e = s - 1; e >= 0 && a.seg[e].n == 0; e--) {
+        for (int e = s - 1; e >= e0 && a.seg[e].n == 0; e--) {
             write_seg_header(a, e, lane, 0u, p0);
-            if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
+            if (lane == 0 && c.n_esc_out) c.n_esc_out[e - e0] = 0;
         }
     }
-    if (gb + 1 == a.total_blocks) {
-        for (int e = s + 1; e < a.nseg; e++) {
+    if (gb + 1 == c.block_end) {
+        for (int e = s + 1; e < e1; e++) {
             write_seg_header(a, e, lane, 0u, p2);
-            if (lane == 0 && a.n_esc_out) a.n_esc_out[e] = 0;
+            if (lane == 0 && c.n_esc_out) c.n_esc_out[e - e0] = 0;
         }
-        if (lane == 0 && a.n_esc_out) a.n_esc_out[a.nseg] = p2;
+        if (lane == 0 && c.n_esc_out) c.n_esc_out[c.nseg] = p2;
     }
 }
 
@@ -741,13 +744,14 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
     const uint32_t p0 = a.pos[slot], p2 = a.pos[slot + 2], pu = a.pos[unit * kEncWaves];
     const uint8_t* stage = a.stage + uint64_t(unit) * kUnit + (p0 - pu);
     bool over = false;
+    const CCall& c = a.call[0];   // the scan path has one call, starting at unit 0
     for (uint32_t k = lane; k < p2 - p0; k += 64) {
         const uint64_t at = uint64_t(p0) + k;
-        if (at < a.esc_cap) a.esc[at] = stage[k];
+        if (at < c.esc_cap) c.esc[at] = stage[k];
         else over = true;
     }
     if (ballot(over) && lane == 0) or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
-    place_block_tables(a, sg, s, gb, p0, p2, a.pos[sg.unit0 * kEncWaves], lane);
+    place_block_tables(a, c, sg, s, gb, p0, p2, a.pos[sg.unit0 * kEncWaves], lane);
 }
 
 // Place without the scan kernel: one workgroup per 8 encode units, one unit (4 blocks)
@@ -783,14 +787,16 @@ __device__ inline uint32_t wait_ready(const uint64_t* ready, uint32_t u, uint64_
 
 // Unit counts of the single-launch compress, from the ready words of units [0, u_end)
 // (each thread takes every kPlaceThreads-th, 4 loads in flight): the escapes before
-// u_first (acc) and before u0 (accs); the counts of the group's own units go to s_ucnt.
+// u_first (acc), before u0 (accs) and before c0 (accc); the counts of the group's own
+// units go to s_ucnt.
 template <class Args>
-__device__ inline bool wait_unit_counts(const Args& a, uint32_t u_first, uint32_t u_end, uint32_t u0, uint32_t tid,
-                                        uint32_t* s_ucnt, uint32_t& acc, uint32_t& accs)
+__device__ inline bool wait_unit_counts(const Args& a, uint32_t u_first, uint32_t u_end, uint32_t u0, uint32_t c0,
+                                        uint32_t tid, uint32_t* s_ucnt, uint32_t& acc, uint32_t& accs,
+                                        uint32_t& accc)
 {
     constexpr uint32_t kPer = 4;
     bool late = false;
-    acc = accs = 0;
+    acc = accs = accc = 0;
     for (uint32_t base = 0; base < u_end; base += kPer * kPlaceThreads) {
         uint64_t w[kPer];
 #pragma unroll
@@ -806,18 +812,22 @@ __device__ inline bool wait_unit_counts(const Args& a, uint32_t u_first, uint32_
             if (u < u_first) acc += c;
             else s_ucnt[u - u_first] = c;
             if (u < u0) accs += c;
+            if (u < c0) accc += c;
         }
     }
     return late;
 }
 
+// Positions count from the first escape of the unit's call: each workgroup sums the
+// unit counts before its first unit, before the first unit of that unit's segment and
+// before the first unit of that unit's call.
 // kWait (single-launch compress): the counts come from the encoders' ready words, waited
 // for; the encoder output read after that (half-block counts, staged escapes) is read
 // with agent-scope loads.
 template <bool kWait, class Args>
 __device__ inline void place_group(const Args& a, uint32_t group)
 {
-    __shared__ uint32_t s_red[2][kPlaceUnits];
+    __shared__ uint32_t s_red[3][kPlaceUnits];
     __shared__ uint32_t s_ucnt[kPlaceUnits];
     __shared__ uint32_t s_late;
     __shared__ __attribute__((aligned(16))) uint8_t s_head[kPlaceUnits][1024];   // staged escapes, per wave
@@ -830,9 +840,9 @@ __device__ inline void place_group(const Args& a, uint32_t group)
     const uint8_t* stage = a.stage + uint64_t(unit) * kUnit;   // the unit's escapes, contiguous
     uint2 head = make_uint2(0, 0);
     uint32_t hc[2 * kWaves];   // the unit's half-block escape counts
-    uint32_t acc = 0, accs = 0;
+    uint32_t acc = 0, accs = 0, accc = 0;
     int s, s_first;
-    uint32_t u0;
+    uint32_t u0, c0;
     if constexpr (!kWait) {
         head = active ? reinterpret_cast<const uint2*>(stage)[lane] : make_uint2(0, 0);
 #pragma unroll
@@ -848,7 +858,8 @@ __device__ inline void place_group(const Args& a, uint32_t group)
         s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
         s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
         u0 = a.seg[s_first].unit0;
-        // escapes before the group's first unit and before the first unit of its segment
+        c0 = a.call[a.seg[s_first].call].unit0;
+        // escapes before the group's first unit, the first unit of its segment and of its call
 #pragma unroll
         for (uint32_t r = 0; r < kPrefixLoads; r++) {
             const uint32_t i = 4 * (tid + r * kPlaceThreads);
@@ -857,17 +868,19 @@ __device__ inline void place_group(const Args& a, uint32_t group)
             for (uint32_t k = 0; k < 4; k++) {
                 acc += v[k];
                 if (i + k < u0) accs += v[k];
+                if (i + k < c0) accc += v[k];
             }
         }
     } else {
         s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
         s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
         u0 = a.seg[s_first].unit0;
+        c0 = a.call[a.seg[s_first].call].unit0;
         const uint32_t u_end = min(u_first + kPlaceUnits, a.total_units);
         if (tid == 0) s_late = 0;
         if (tid < kPlaceUnits && u_first + tid >= u_end) s_ucnt[tid] = 0;
         __syncthreads();
-        const bool late = wait_unit_counts(a, u_first, u_end, u0, tid, s_ucnt, acc, accs);
+        const bool late = wait_unit_counts(a, u_first, u_end, u0, c0, tid, s_ucnt, acc, accs, accc);
         if (late) s_late = 1;   // any thread; read after the barrier below
     }
     const CSeg sg = a.seg[s];
@@ -878,10 +891,12 @@ __device__ inline void place_group(const Args& a, uint32_t group)
     for (int o = 32; o > 0; o >>= 1) {
         acc += __shfl_xor(acc, o, 64);
         accs += __shfl_xor(accs, o, 64);
+        accc += __shfl_xor(accc, o, 64);
     }
     if (lane == 0) {
         s_red[0][wave] = acc;
         s_red[1][wave] = accs;
+        s_red[2][wave] = accc;
     }
     if constexpr (!kWait) reinterpret_cast<uint2*>(s_head[wave])[lane] = head;
     __syncthreads();
@@ -901,15 +916,18 @@ __device__ inline void place_group(const Args& a, uint32_t group)
         wave_lds_sync();
     }
     if (!active) return;
-    uint32_t pre = 0, first_base = 0;
+    uint32_t pre = 0, first_base = 0, call_base = 0;
 #pragma unroll
     for (uint32_t w = 0; w < kPlaceUnits; w++) {
         pre += s_red[0][w];
         first_base += s_red[1][w];
+        call_base += s_red[2][w];
     }
-    // this unit's position, and its segment's first escape: a segment that starts inside
-    // the group starts at `pre` plus the units of the group before it; otherwise it is
-    // the segment of the group's first unit, whose start was summed above
+    // escapes before this unit, before its segment's first unit and before its call's
+    // first unit (launch-wide): a segment or call that starts inside the group starts at
+    // `pre` plus the units of the group before it; otherwise it holds the group's first
+    // unit, and its start was summed above
+    const CCall& c = a.call[sg.call];
     uint32_t upos = pre;
     for (uint32_t w = 0; w < wave; w++) upos += s_ucnt[w];
     uint32_t base = first_base;
@@ -917,15 +935,22 @@ __device__ inline void place_group(const Args& a, uint32_t group)
         base = pre;
         for (uint32_t w = 0; w < sg.unit0 - u_first; w++) base += s_ucnt[w];
     }
+    uint32_t cbase = call_base;
+    if (c.unit0 >= u_first) {
+        cbase = pre;
+        for (uint32_t w = 0; w < c.unit0 - u_first; w++) cbase += s_ucnt[w];
+    }
+    upos -= cbase;   // positions within the call's escapes
+    base -= cbase;
     // the unit's escapes in one run; its blocks' positions from its 8 half-block counts
-    if (ballot(place_unit_escapes<kWait>(a, s_head[wave], stage, upos, s_ucnt[wave], lane)) && lane == 0)
+    if (ballot(place_unit_escapes<kWait>(c, s_head[wave], stage, upos, s_ucnt[wave], lane)) && lane == 0)
         or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     uint32_t p = upos;
 #pragma unroll
     for (uint32_t k = 0; k < kWaves; k++) {
         if (b0 + k >= K) break;
         const uint32_t p0 = p, p2 = p0 + hc[2 * k] + hc[2 * k + 1];
-        place_block_tables(a, sg, s, sg.block0 + b0 + k, p0, p2, base, lane);
+        place_block_tables(a, c, sg, s, sg.block0 + b0 + k, p0, p2, base, lane);
         p = p2;
     }
 }
@@ -943,18 +968,6 @@ void compress_single_kernel(const CArgs a)
     else place_group<true>(a, blockIdx.x - a.total_units);
 }
 
-// Two consecutive chunks of the pipeline in one launch: the first place_groups
-// workgroups place chunk p (its encode ran in an earlier launch on the same stream, and
-// it uses the other workspace), the rest encode chunk e.  The place work, a few
-// microseconds of mostly latency, then runs beside the next chunk's encode instead of
-// in a launch of its own.
-__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void encode_place_kernel(const CArgsP e, const CArgsP p, uint32_t place_groups)
-{
-    static_assert(kEncThreads == kPlaceThreads, "both roles use the same workgroup size");
-    if (blockIdx.x < place_groups) place_group<false>(p, blockIdx.x);
-    else encode_unit<false>(e, blockIdx.x - place_groups);
-}
 
 // --------------------------------------------------------------------------------
 // decode helpers
@@ -1417,15 +1430,6 @@ hipError_t launch_compress(const CArgs& a, hipStream_t s, bool single)
         if (a.total_blocks > 0)
             hipLaunchKernelGGL(place_kernel, dim3((a.total_blocks + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_encode_place(const CArgsP& enc, const CArgsP& place, hipStream_t s)
-{
-    const uint32_t groups = (place.total_units + kPlaceUnits - 1) / kPlaceUnits;
-    const uint32_t grid = groups + enc.total_units;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(encode_place_kernel, dim3(grid), dim3(kEncThreads), 0, s, enc, place, groups);
     return hipGetLastError();
 }
 

@@ -210,9 +210,10 @@ class PreparedCompressChunks:
     """A zipccl_compress_chunks call over fixed buffers, marshalled once.  chunks: a list
     of per-chunk lists of bf16 device tensors (the same number in each); static_outs /
     esc_outs: per-chunk uint8 device tensors.  run(plans) uses plans[i] for segment i of
-    every chunk."""
+    every chunk.  esc_caps: per-chunk escape capacities (default: each buffer's size)."""
 
-    def __init__(self, chunks, static_outs, esc_outs, workspace, n_esc_out=None, status=None, stream=None):
+    def __init__(self, chunks, static_outs, esc_outs, workspace, n_esc_out=None, status=None, stream=None,
+                 esc_caps=None):
         self.nchunks, self.nseg = len(chunks), len(chunks[0])
         self._arr = (SegmentT * (self.nchunks * self.nseg))()
         for k, tensors in enumerate(chunks):
@@ -226,7 +227,7 @@ class PreparedCompressChunks:
         sp = (ctypes.c_void_p * C)(*[_ptr(t) for t in static_outs])
         sc = (ctypes.c_uint64 * C)(*[_nbytes(t) for t in static_outs])
         ep = (ctypes.c_void_p * C)(*[_ptr(t) for t in esc_outs])
-        ec = (ctypes.c_uint64 * C)(*[_nbytes(t) for t in esc_outs])
+        ec = (ctypes.c_uint64 * C)(*([_nbytes(t) for t in esc_outs] if esc_caps is None else esc_caps))
         self._args = (sp, sc, ep, ec, _ptr(workspace), _nbytes(workspace), _ptr(n_esc_out), _ptr(status),
                       _stream(stream))
         self._keep = (chunks, static_outs, esc_outs, workspace, n_esc_out, status)

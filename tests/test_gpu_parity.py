@@ -627,24 +627,35 @@ def scan_path(monkeypatch):
     yield
 
 
-def compress_chunks_vs_oracle(Z, chunks_bits, plans):
+def compress_chunks_vs_oracle(Z, chunks_bits, plans, ws_bytes=None, esc_caps=None):
+    # ws_bytes: workspace size (default: twice what the largest chunk needs, so that
+    # about two chunks share a launch); esc_caps: per-chunk escape capacities (default:
+    # room for every value)
     C, S = len(chunks_bits), len(chunks_bits[0])
     tens = [[dev_bf16(b) for b in ch] for ch in chunks_bits]
     sizes = [[b.size for b in ch] for ch in chunks_bits]
     st_sizes = [sum(Z.static_size(n) for n in sz) for sz in sizes]
     statics = [torch.full((max(t, 1),), POISON, dtype=torch.uint8, device="cuda") for t in st_sizes]
-    escs = [torch.full((max(sum(sz), 1),), POISON, dtype=torch.uint8, device="cuda") for sz in sizes]
-    ws = torch.full((2 * Z.workspace_size(max(sum(sz) for sz in sizes), S),), POISON, dtype=torch.uint8,
-                    device="cuda")
+    caps = [sum(sz) for sz in sizes] if esc_caps is None else esc_caps
+    escs = [torch.full((max(c, 1),), POISON, dtype=torch.uint8, device="cuda") for c in caps]
+    if ws_bytes is None:
+        ws_bytes = 2 * Z.workspace_size(max(sum(sz) for sz in sizes), S)
+    ws = torch.full((ws_bytes,), POISON, dtype=torch.uint8, device="cuda")
     n_esc = torch.full((C * (S + 1),), -1, dtype=torch.int64, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    Z.PreparedCompressChunks(tens, statics, escs, ws, n_esc, status).run(plans)
+    Z.PreparedCompressChunks(tens, statics, escs, ws, n_esc, status, esc_caps=esc_caps).run(plans)
     torch.cuda.synchronize()
     ne = n_esc.cpu().numpy()
+    st_all = int(status.item())
     for k in range(C):
-        r = dict(status=int(status.item()), n_esc=ne[k * (S + 1):(k + 1) * (S + 1)],
-                 static_h=statics[k].cpu().numpy()[:st_sizes[k]], esc_h=escs[k].cpu().numpy())
-        check_against_oracle(Z, chunks_bits[k], plans, r)
+        st, esc, ne_o, rc = O.compress_batch(chunks_bits[k], oracle_tables(plans))
+        assert list(ne[k * (S + 1):(k + 1) * (S + 1) - 1]) == ne_o, f"chunk {k}"
+        assert int(ne[(k + 1) * (S + 1) - 1]) == sum(ne_o), f"chunk {k}"
+        sh = statics[k].cpu().numpy()[:st_sizes[k]]
+        assert np.array_equal(sh, st), f"chunk {k}: " + first_diff(sh, st)
+        m = min(sum(ne_o), caps[k])
+        assert np.array_equal(escs[k].cpu().numpy()[:m], esc[:m]), f"chunk {k}"
+    return st_all
 
 
 def chunk_sequence():
@@ -804,3 +815,59 @@ def test_compress_in_captured_graph(Z):
         r = dict(status=int(status.item()), n_esc=n_esc.cpu().numpy(), static_h=static.cpu().numpy(),
                  esc_h=esc.cpu().numpy())
         check_against_oracle(Z, segs, plans, r)
+
+
+# ------------------------------------------------------------------------------------
+# chunk sequences whose calls share launches (up to 8 calls per launch)
+# ------------------------------------------------------------------------------------
+def long_chunk_sequence(nchunks=11, S=3, seed=0):
+    # ragged, tiny and empty segments; chunk 4 is all empty (a launch of its own) and
+    # chunk 7 has a single tiny segment
+    rng = np.random.default_rng(seed)
+    sig = [0.02, 1.0, 1e-3][:S]
+    out = []
+    for k in range(nchunks):
+        if k == 4:
+            ns = [0] * S
+        elif k == 7:
+            ns = [0] * (S - 1) + [5]
+        else:
+            ns = [int(rng.choice([0, 1, 513, 4096, 16385, 70001, 1 << 20])) for _ in range(S)]
+        out.append([W.gaussian_bf16(n, sig[i], 3000 + 17 * k + i + 1000 * seed) for i, n in enumerate(ns)])
+    return out, [Z_plan(x) for x in sig]
+
+
+def batch_workspace(Z, chunks):
+    return Z.workspace_size(sum(b.size for ch in chunks for b in ch), sum(len(ch) for ch in chunks))
+
+
+def test_compress_chunks_shared_launches(Z):
+    chunks, plans = long_chunk_sequence()
+    print("chunks sharing launches", [[b.size for b in ch] for ch in chunks], flush=True)
+    assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
+
+
+def test_compress_chunks_shared_launches_many_peers(Z):
+    # 7 segments per chunk: at most 9 chunks fit the 64-segment launch, 8 calls at most
+    chunks, _ = long_chunk_sequence(nchunks=10, S=3, seed=1)
+    rng = np.random.default_rng(5)
+    chunks = [[W.gaussian_bf16(int(rng.choice([4096, 20000, 65536])), 1e-3, 4000 + 7 * k + i) for i in range(7)]
+              for k in range(10)]
+    plans = [Z.plan(sigma=1e-3)] * 7
+    assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
+
+
+def test_compress_chunks_shared_launches_two_launch_path(Z, two_launches):
+    chunks, plans = long_chunk_sequence(seed=2)
+    assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
+
+
+def test_compress_chunks_overflow_in_one_call(Z):
+    # chunk 2 of 5 gets a small escape buffer: the status reports the overflow, its
+    # escapes before the cap and every other chunk's bytes are still exact
+    chunks = [[W.gaussian_bf16(200000, 1.0, 6100 + 3 * k + i) for i in range(3)] for k in range(5)]
+    plans = [Z.plan(table=[120, 121, 122, 123, 124, 125, 126])] * 3   # many escapes
+    caps = [600000] * 5
+    caps[2] = 5000
+    st = compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks), esc_caps=caps)
+    assert st == Z.STATUS_ESC_OVERFLOW
