@@ -549,7 +549,7 @@ PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d rocprof_out/pmc_{co
            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-extra")
 RS_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats_rs -o rs -- "
                 "python3 bench.py --only rs_512m")
-OUR_KERNELS = ("compress_single_kernel", "encode_place_kernel", "encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel",
+OUR_KERNELS = ("compress_single_kernel", "encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel",
                "decompress_kernel", "accumulate_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 GIB = 1 << 30
@@ -584,13 +584,13 @@ def summarize_stats(csv_path, out_path, rs=False):
         lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     if rs:
-        lines += ["", "The chunk compresses run as separate calls (encode_kernel + place_direct_kernel, 7",
-                  "segments of 2 Mi values each) and through zipccl_compress_chunks and the pipeline",
-                  "(encode_place_kernel: one chunk placed while the next is encoded); decode-accumulate",
+        lines += ["", "The chunk compresses run as separate calls (compress_single_kernel, 7 segments of",
+                  "2 Mi values each) and through zipccl_compress_chunks and the pipeline",
+                  "(compress_single_kernel over 8 chunks, 56 segments, per launch); decode-accumulate",
                   "runs one chunk per launch and 18 chunks per launch (accumulate_kernel)."]
     else:
         lines += ["", "Calls include the warmup and verification round trips; all launches are of the",
-                  "bucket workload (compress: encode_kernel + place_direct_kernel, decompress: decompress_kernel)."]
+                  "bucket workload (compress: compress_single_kernel, decompress: decompress_kernel)."]
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
@@ -618,11 +618,10 @@ def summarize_pmc(fetch_csv, write_csv, out_path, n_units=4096):
     copy_f = max(v for (k, g), v in f.items() if k == COPY_KERNEL)
     copy_w = max(v for (k, g), v in w.items() if k == COPY_KERNEL)
     sf, sw = (GIB / 1024) / copy_f, (GIB / 1024) / copy_w      # true KiB per counted KiB
-    enc = ("encode_kernel", n_units * 512)
-    plc = ("place_direct_kernel", ((n_units + 7) // 8) * 512)
+    cmp_ = ("compress_single_kernel", (n_units + (n_units + 7) // 8) * 512)
     dec = ("decompress_kernel", n_units * 512)
-    kib = {k: (f[k] * sf, w[k] * sw) for k in (enc, plc, dec)}
-    comp = sum(kib[enc]) + sum(kib[plc])
+    kib = {k: (f[k] * sf, w[k] * sw) for k in (cmp_, dec)}
+    comp = sum(kib[cmp_])
     decomp = sum(kib[dec])
     lines = ["# Measured HBM traffic, bucket_64m (16 x 4 Mi BF16 values)", "",
              "Commands (from the repository root on the GPU host), one run per counter:", "",
@@ -631,7 +630,7 @@ def summarize_pmc(fetch_csv, write_csv, out_path, n_units=4096):
              f"(the copy counted {copy_f:.0f} KiB fetched and {copy_w:.0f} KiB written per dispatch).", "",
              "| kernel | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
              "|---|---|---|---|---|---|"]
-    for k in (enc, plc, dec):
+    for k in (cmp_, dec):
         lines.append(f"| {k[0]} | {k[1]} | {f[k]:.1f} | {w[k]:.1f} | {kib[k][0] * 1024 / 1e6:.2f} | "
                      f"{kib[k][1] * 1024 / 1e6:.2f} |")
     lines += ["", "Machine-readable (bench.py reports these as roofline.traffic while the kernel",
