@@ -1024,11 +1024,30 @@ __device__ inline bool block_escapes(const uint32_t* C, uint32_t b, uint32_t K, 
 // --------------------------------------------------------------------------------
 // decompress + fp32 accumulate + one rounding
 // --------------------------------------------------------------------------------
-__device__ inline uint32_t round_bf16_bits(float f)
+// Two fp32 sums rounded once to BF16 (round to nearest, ties to even), packed low/high:
+// one v_cvt_pk_bf16_f32.  On every non-NaN fp32 pattern tried (2^24 random patterns plus
+// ties, near-ties and specials in every binade, denormals included) it gives the bits of
+// the integer rule (u + 0x7FFF + ((u >> 16) & 1)) >> 16; a NaN comes out as a NaN that
+// keeps sign and payload bits, which fix_nan_bf16x2 replaces.
+typedef __bf16 zc_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float zc_f32x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2_rne(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const zc_f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, zc_bf16x2));
+}
+
+// Bit 15 / 31 set where the low / high BF16 half is a NaN: (h & 0x7FFF) > 0x7F80, i.e.
+// (h & 0x7FFF) + 0x7F reaches 0x8000 (no carry crosses into the other half).
+__device__ inline uint32_t nan_halves(uint32_t x) { return ((x & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u; }
+
+// Every NaN half becomes the canonical 0x7FC0.
+__device__ inline uint32_t fix_nan_bf16x2(uint32_t x)
+{
+    const uint32_t m = nan_halves(x);
+    if (m & 0x8000u) x = (x & 0xFFFF0000u) | 0x7FC0u;
+    if (m & 0x80000000u) x = (x & 0x0000FFFFu) | 0x7FC00000u;
+    return x;
 }
 
 // Plane dword a lane loads in the decoders, chosen so that after the half-wave transpose
@@ -1296,14 +1315,19 @@ void accumulate_kernel(const AArgs a)
         return;
     }
     if (nvalid == 0) return;
-    uint32_t r[8];
+    // one rounding per value (RNE), NaN -> 0x7FC0; the fix-up only runs in a lane that
+    // holds a NaN
+    uint32_t r[4];
 #pragma unroll
-    for (int j = 0; j < 8; j++) r[j] = round_bf16_bits(acc[j]);
+    for (int q = 0; q < 4; q++) r[q] = pack_bf16x2_rne(acc[2 * q], acc[2 * q + 1]);
+    if (nan_halves(r[0]) | nan_halves(r[1]) | nan_halves(r[2]) | nan_halves(r[3])) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) r[q] = fix_nan_bf16x2(r[q]);
+    }
     if (nvalid == 8) {
-        store_nt(reinterpret_cast<uint4*>(dst + i0),
-                 make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16)));
+        store_nt(reinterpret_cast<uint4*>(dst + i0), make_uint4(r[0], r[1], r[2], r[3]));
     } else {
-        for (uint32_t j = 0; j < nvalid; j++) dst[i0 + j] = uint16_t(r[j]);
+        for (uint32_t j = 0; j < nvalid; j++) dst[i0 + j] = uint16_t(r[j >> 1] >> (16 * (j & 1)));
     }
 }
 

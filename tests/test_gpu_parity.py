@@ -314,6 +314,29 @@ def test_accumulate_special_values(Z):
     assert (got == 0x0002).all()
 
 
+@pytest.mark.parametrize("npeers,band", [(3, False), (7, False), (2, True), (7, True)])
+def test_accumulate_random_bits_and_ties(Z, npeers, band):
+    # the one rounding of the fp32 sum, bit for bit: uniformly random BF16 patterns (NaN
+    # payloads of both signs, subnormals, infinities: NaN -> 0x7FC0 by the rule), or values
+    # from a narrow exponent band, where sums of few terms often fall exactly on a tie
+    rng = np.random.default_rng(40 + npeers + 10 * band)
+    n = 200000 + 77
+
+    def draw():
+        if not band:
+            return rng.integers(0, 1 << 16, n, dtype=np.int64).astype(np.uint16)
+        e = rng.integers(124, 128, n)
+        return ((rng.integers(0, 2, n) << 15) | (e << 7) | rng.integers(0, 128, n)).astype(np.uint16)
+
+    peers = [draw() for _ in range(npeers)]
+    local = draw()
+    plans = [Z.plan(sigma=1.0)] * npeers
+    got, status, _ = gpu_accumulate(Z, peers, plans, local)
+    assert status == 0
+    want = oracle_accumulate(Z, peers, plans, local)
+    assert np.array_equal(got, want), first_diff(got, want)
+
+
 def test_accumulate_corrupt_peer(Z):
     n = 9000
     peers = [W.gaussian_bf16(n, 0.1, 40 + p) for p in range(3)]
