@@ -1410,10 +1410,19 @@ __global__ __launch_bounds__(kEncThreads) void decompress_kernel(const DArgs a)
         if (lane == 0) or_status(a.status, ZIPCCL_STATUS_CORRUPT);
         return;
     }
-    // every lane of the wave helps stage the half block's escapes
+    // every lane of the wave helps stage the half block's escapes: 4 bytes per lane in
+    // flight per round of 256 (indexes past the last escape re-read it), so that a half
+    // block with up to 256 escapes waits for one memory round trip rather than one per 64
     const uint8_t* esc = sg.esc + hd.esc_offset + first + half_start;
     uint8_t* esc_lds = s_esc[wave];
-    for (uint32_t k = lane; k < half_total; k += 64) esc_lds[k] = esc[k];
+    for (uint32_t k0 = 0; k0 < half_total; k0 += 256) {
+        uint32_t x[4];
+#pragma unroll
+        for (uint32_t j = 0; j < 4; j++) x[j] = esc[min(k0 + 64 * j + lane, half_total - 1)];
+#pragma unroll
+        for (uint32_t j = 0; j < 4; j++)
+            if (k0 + 64 * j + lane < half_total) esc_lds[k0 + 64 * j + lane] = uint8_t(x[j]);
+    }
     wave_lds_sync();
 #pragma unroll
     for (int k = 0; k < int(kDecHalfTiles); k++) {
