@@ -1136,13 +1136,17 @@ struct PeerBlock {
 // wave knows where its tile's escapes start, then the peers are decoded and added in
 // order.
 template <int kPeers>
-__global__ __launch_bounds__(kAccThreads) __attribute__((amdgpu_waves_per_eu(kPeers <= 8 ? 6 : 4)))
+// Up to 7 peers the kernel fits 64 VGPRs without spills (the A bytes wait in LDS, not in
+// registers), so 4 workgroups run per CU; the kernel is latency-bound (at 2 workgroups
+// per CU it took 1.77x as long as at 3), and 4 took 7-peer launches 12 % below 3.
+__global__ __launch_bounds__(kAccThreads) __attribute__((amdgpu_waves_per_eu(kPeers <= 8 ? 8 : 4)))
 void accumulate_kernel(const AArgs a)
 {
     __shared__ uint32_t s_cnt[kPeers][kAccWaves];
     __shared__ PeerBlock s_peer[kPeers];
     __shared__ uint8_t s_blk[kPeers][kAccBlkHead + kEscPad];   // each peer's first escapes of the block
     __shared__ uint8_t s_esc[kAccWaves][kTile + kEscPad];      // a tile's escapes when they lie further on
+    __shared__ uint2 s_A[kAccWaves][kPeers][64];                 // the tile's A bytes per peer, parked until decode
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // the workgroup's chunk, and its block within the chunk
@@ -1233,6 +1237,10 @@ void accumulate_kernel(const AArgs a)
         }
     }
     wave_ranks<kPairs>(cnt, rank, total, P);
+    // the A bytes (requested right after the plane dwords, so in by now) wait in LDS until
+    // their peer is decoded: 2 x kPeers fewer live registers
+#pragma unroll
+    for (int p = 0; p < kPeers; p++) s_A[wave][p][lane] = Ap[p];
     if (lane == 0) {
 #pragma unroll
         for (int p = 0; p < kPeers; p++) s_cnt[p][wave] = total[p];
@@ -1298,7 +1306,8 @@ void accumulate_kernel(const AArgs a)
                 wave_lds_sync();
                 tile_esc = esc_lds;
             }
-            const LaneBytes o = decode_lane(rows[p], zf[p], Ap[p], s_peer[p].tlo, s_peer[p].thi, rank[p], tile_esc);
+            const LaneBytes o = decode_lane(rows[p], zf[p], s_A[wave][p][lane], s_peer[p].tlo, s_peer[p].thi, rank[p],
+                                            tile_esc);
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
