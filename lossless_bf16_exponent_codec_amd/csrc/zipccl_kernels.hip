@@ -218,7 +218,11 @@ __device__ inline uint32_t transpose_stage(uint32_t x, const Transpose32& c)
     constexpr int sft = 16 >> k;
     const uint32_t y = partner<sft>(x);
     const uint32_t t = __builtin_amdgcn_alignbit(y, y, c.rot[k]);
-    return (x & c.keep[k]) | (t & ~c.keep[k]);
+    // (x & keep) | (t & ~keep) as one v_bfi_b32: the compiler emits v_and + v_and_or here,
+    // one VALU instruction more per stage (decode-accumulate 1.6 % faster, A/B)
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(c.keep[k]), "v"(x), "v"(t));
+    return r;
 }
 
 // Transposes the 32x32 bit matrix held by each half-wave (row = lane, column = bit):
