@@ -1087,6 +1087,16 @@ struct LaneBytes {
     uint32_t lo0, hi0, lo1, hi1;
 };
 
+// A group of 4 columns whose escape flags z (bit 8c for column c) hold two or more set
+// bits: the byte of the second flagged column becomes x (the group's second escape).
+// With fewer than two flags, E is returned unchanged.
+__device__ inline uint32_t patch_second_escape(uint32_t E, uint32_t z, uint32_t x)
+{
+    const uint32_t rest = z & (z - 1);          // flags after the first
+    const uint32_t second = rest & (0u - rest); // the lowest of them (0 if none)
+    return (E & ~(second * 0xFFu)) | ((x * 0x01010101u) & (second * 0xFFu));
+}
+
 __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint32_t tlo, uint32_t thi, uint32_t r,
                                         const uint8_t* esc_lds)
 {
@@ -1098,14 +1108,22 @@ __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint3
     uint32_t E0 = perm(thi, tlo | x0, row & 0x07070707u);
     uint32_t E1 = perm(thi, tlo | x1, (row >> 4) & 0x07070707u);
     if (n0 > 1 || n1 > 1) {   // rare: several escapes among 4 columns of the lane
-        uint32_t rr = r;
-        for (uint32_t m = z0; m; m &= m - 1) {
-            const uint32_t sh = __builtin_ctz(m);   // 8 * column
-            E0 = (E0 & ~(0xFFu << sh)) | (uint32_t(esc_lds[rr++]) << sh);
-        }
-        for (uint32_t m = z1; m; m &= m - 1) {
-            const uint32_t sh = __builtin_ctz(m);
-            E1 = (E1 & ~(0xFFu << sh)) | (uint32_t(esc_lds[rr++]) << sh);
+        // the second escape of each group goes to the column of its second flag, by masks
+        E0 = patch_second_escape(E0, z0, esc_lds[r + 1]);
+        E1 = patch_second_escape(E1, z1, esc_lds[r + n0 + 1]);
+        if (n0 > 2 || n1 > 2) {   // rarer still: a third or fourth escape, byte by byte
+            uint32_t rr = r + 2;
+            uint32_t m = z0 & (z0 - 1);
+            for (m &= m - 1; m; m &= m - 1) {
+                const uint32_t sh = __builtin_ctz(m);   // 8 * column
+                E0 = (E0 & ~(0xFFu << sh)) | (uint32_t(esc_lds[rr++]) << sh);
+            }
+            rr = r + n0 + 2;
+            m = z1 & (z1 - 1);
+            for (m &= m - 1; m; m &= m - 1) {
+                const uint32_t sh = __builtin_ctz(m);
+                E1 = (E1 & ~(0xFFu << sh)) | (uint32_t(esc_lds[rr++]) << sh);
+            }
         }
     }
     // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
