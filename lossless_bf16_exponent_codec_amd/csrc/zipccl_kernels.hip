@@ -1094,7 +1094,8 @@ __device__ inline uint32_t patch_second_escape(uint32_t E, uint32_t z, uint32_t 
 {
     const uint32_t rest = z & (z - 1);          // flags after the first
     const uint32_t second = rest & (0u - rest); // the lowest of them (0 if none)
-    return (E & ~(second * 0xFFu)) | ((x * 0x01010101u) & (second * 0xFFu));
+    const uint32_t mask = (second << 8) - second;   // its byte (full-rate ops, no 32-bit multiply)
+    return (E & ~mask) | (perm(x, x, 0u) & mask);   // x in every byte
 }
 
 __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint32_t tlo, uint32_t thi, uint32_t r,
