@@ -426,7 +426,7 @@ zipccl_status zipccl_decompress(const void* static_in, uint64_t static_bytes, co
         d.dst = static_cast<uint16_t*>(g.dst);
         d.n = uint32_t(g.n);
         d.unit0 = uint32_t(units);
-        units += units_of(g.n);
+        units += blocks_of(g.n);   // one decompress workgroup per block
         st_off += static_bytes_of(g.n);
     }
     if (st_off > static_bytes) return ZIPCCL_ERR_SIZE;
@@ -459,7 +459,7 @@ zipccl_status zipccl_decompress_shards(const void* const* static_in, const void*
         d.n = uint32_t(g.n);
         d.unit0 = uint32_t(units);
         d.esc_at_first = (flags & ZIPCCL_SHARDS_ESC_AT_FIRST) ? 1u : 0u;
-        units += units_of(g.n);
+        units += blocks_of(g.n);   // one decompress workgroup per block
     }
     a.status = status;
     a.nseg = nseg;

@@ -100,7 +100,7 @@ struct DSeg {              // decompress: one segment
     uint64_t esc_bytes;
     uint16_t* dst;
     uint32_t n;
-    uint32_t unit0;        // first workgroup unit of the segment (units of kUnit values)
+    uint32_t unit0;        // first decompress workgroup of the segment (one per block of kBlock values)
     uint32_t esc_at_first; // 1: esc points at the segment's first escape (header esc_offset ignored)
     uint32_t pad;
 };
@@ -109,7 +109,7 @@ struct DArgs {
     DSeg seg[kMaxSegs];
     uint32_t* status;
     int32_t nseg;
-    uint32_t total_units;
+    uint32_t total_units;  // decompress workgroups: blocks of all segments
 };
 static_assert(sizeof(DArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
