@@ -79,6 +79,16 @@ hipError_t compress_launch(CArgs& a, hipStream_t stream)
 {
     const bool single = single_launch(a, stream);
     a.tag = single ? next_tag() : 0;
+    a.wait_tag = a.tag;
+    a.wait_polls = 1u << 16;
+    // Test hook for the bounded wait's error path: the placing workgroups wait for a tag
+    // no call uses, 4 polls per word, so every one gives up and reports
+    // ZIPCCL_STATUS_WAIT_LIMIT (and writes nothing) within microseconds.
+    const char* e = std::getenv("ZIPCCL_TEST_WAIT_LIMIT");
+    if (single && e && e[0] == '1' && e[1] == 0) {
+        a.wait_tag = (a.tag ^ (1ull << 47)) | 1u;   // never this call's tag, never 0
+        a.wait_polls = 4;
+    }
     return launch_compress(a, stream, single);
 }
 

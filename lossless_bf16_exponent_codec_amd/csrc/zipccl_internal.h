@@ -83,6 +83,8 @@ struct CArgs {
     uint8_t* stage;        // workspace: kUnit bytes per unit
     uint64_t* ready;       // workspace: a ready word per unit (single-launch compress)
     uint64_t tag;          // this launch's tag in the ready words (single-launch compress)
+    uint64_t wait_tag;     // the tag the placing workgroups wait for (== tag; tests force a mismatch)
+    uint32_t wait_polls;   // polls of one ready word before a placing workgroup gives up
     uint32_t* status;      // or null
     const uint8_t* dplans; // device plans (8 bytes per segment) replacing the segments' tables, or null
     int32_t nseg;

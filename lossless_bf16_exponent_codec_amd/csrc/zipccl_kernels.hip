@@ -770,16 +770,15 @@ constexpr uint32_t kPlaceThreads = 64 * kPlaceUnits;
 constexpr uint32_t kPrefixLoads = kDirectPrefixMaxUnits / (4 * kPlaceThreads);   // uint4 loads per thread
 
 // Bounded wait of the single-launch compress: polls for the ready word of unit u of this
-// call (tag) and returns its escape count; after kWaitPolls polls (about 0.1 s) sets
-// `late` and returns 0.  A placing workgroup is dispatched only after every encoder
-// workgroup of the launch (they come first in the grid), and encoders wait for nothing,
-// so the wait ends long before the limit.
-constexpr uint32_t kWaitPolls = 1u << 16;
-
-__device__ inline uint32_t wait_ready(const uint64_t* ready, uint32_t u, uint64_t tag, uint64_t w, bool& late)
+// call (tag) and returns its escape count; after `polls` polls (2^16 by default, about
+// 0.1 s) sets `late` and returns 0.  A placing workgroup is dispatched only after every
+// encoder workgroup of the launch (they come first in the grid), and encoders wait for
+// nothing, so the wait ends long before the limit.
+__device__ inline uint32_t wait_ready(const uint64_t* ready, uint32_t u, uint64_t tag, uint32_t polls, uint64_t w,
+                                      bool& late)
 {
     for (uint32_t k = 0; (w >> kReadyCountBits) != tag; k++) {
-        if (late || k >= kWaitPolls) {   // once one wait has run out, the thread waits no more
+        if (late || k >= polls) {   // once one wait has run out, the thread waits no more
             late = true;
             return 0;
         }
@@ -812,7 +811,7 @@ __device__ inline bool wait_unit_counts(const Args& a, uint32_t u_first, uint32_
         for (uint32_t k = 0; k < kPer; k++) {
             const uint32_t u = base + tid + k * kPlaceThreads;
             if (u >= u_end) break;
-            const uint32_t c = wait_ready(a.ready, u, a.tag, w[k], late);
+            const uint32_t c = wait_ready(a.ready, u, a.wait_tag, a.wait_polls, w[k], late);
             if (u < u_first) acc += c;
             else s_ucnt[u - u_first] = c;
             if (u < u0) accs += c;

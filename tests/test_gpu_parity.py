@@ -894,3 +894,20 @@ def test_compress_chunks_overflow_in_one_call(Z):
     caps[2] = 5000
     st = compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks), esc_caps=caps)
     assert st == Z.STATUS_ESC_OVERFLOW
+
+
+def test_single_launch_wait_limit_is_reported(Z, monkeypatch):
+    # the bounded wait's error path, forced from the host: the placing workgroups wait for
+    # a tag no call writes, 4 polls per word; every one gives up, reports
+    # ZIPCCL_STATUS_WAIT_LIMIT and writes no header; the next call on the same workspace
+    # is exact again
+    x = [W.gaussian_bf16(300000, 0.02, 3), W.gaussian_bf16(70001, 1e-3, 4)]
+    p = [Z.plan(sigma=0.02), Z.plan(sigma=1e-3)]
+    ws = torch.zeros(Z.workspace_size(sum(s.size for s in x), len(x)), dtype=torch.uint8, device="cuda")
+    monkeypatch.setenv("ZIPCCL_TEST_WAIT_LIMIT", "1")
+    r = gpu_compress(Z, x, p, workspace=ws)
+    assert r["status"] & Z.STATUS_WAIT_LIMIT
+    assert (r["static_h"][:64] == POISON).all()   # the first segment's header was not written
+    monkeypatch.delenv("ZIPCCL_TEST_WAIT_LIMIT")
+    r = gpu_compress(Z, x, p, workspace=ws)
+    check_against_oracle(Z, x, p, r)
