@@ -647,6 +647,65 @@ def summarize_pmc(fetch_csv, write_csv, out_path, n_units=4096):
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
+RS_PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d rocprof_out/pmc_rs_{counter} -o run -- "
+              "python3 bench.py --only rs_512m")
+
+
+def summarize_pmc_rs(fetch_csv, write_csv, out_path):
+    """profiles/ text from two rocprofv3 --pmc runs of RS_PMC_CMD (FETCH_SIZE, then
+    WRITE_SIZE): HBM bytes per launch of the reduce-scatter share's kernels, per value,
+    against the algorithmic bytes (decode-accumulate: 7 peers x ~1.40 B + 2 B local + 2 B
+    out per output value; compress: 2 B in + ~1.40 B out per value).  Scaled by the
+    counters' reading of the 1 GiB copy in the same runs.  A decode-accumulate launch has a
+    workgroup per 4096 outputs; a compress launch ceil(units / 8) placing workgroups after
+    its units of 16384 values."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = short_kernel_name(r["Kernel_Name"])
+            if k is None:
+                continue
+            acc.setdefault((k, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return {key: (sum(v) / len(v), len(v)) for key, v in acc.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_f = max(v for (k, g), (v, c) in f.items() if k == COPY_KERNEL)
+    copy_w = max(v for (k, g), (v, c) in w.items() if k == COPY_KERNEL)
+    sf, sw = (GIB / 1024) / copy_f, (GIB / 1024) / copy_w
+    lines = ["# Measured HBM traffic, rs_512m (7 peers x 64 Mi BF16 values, 32 chunks of 2 Mi)", "",
+             "Commands (from the repository root on the GPU host), one run per counter:", "",
+             "    " + RS_PMC_CMD.format(counter="FETCH_SIZE"), "    " + RS_PMC_CMD.format(counter="WRITE_SIZE"), "",
+             f"Scale factors from the 1 GiB copy in the same runs: FETCH_SIZE x{sf:.4f}, WRITE_SIZE x{sw:.4f}.",
+             f"Kernel source sha256: `{kernel_source_sha256()}`", "",
+             "| kernel | grid | launches | values | read MB | write MB | B per value | algorithmic B per value |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (k, grid) in sorted(set(f) & set(w)):
+        if k == COPY_KERNEL:
+            continue
+        (fv, nl), (wv, _) = f[(k, grid)], w[(k, grid)]
+        rd, wr = fv * sf * 1024, wv * sw * 1024
+        wgs = grid // 512
+        if k == "accumulate_kernel":
+            vals, alg = wgs * 4096, "13.80 (per output)"
+        elif k == "compress_single_kernel":
+            units = wgs - (wgs + 8) // 9   # wgs = units + ceil(units / 8)
+            while units + (units + 7) // 8 < wgs:
+                units += 1
+            vals, alg = units * 16384, "3.40"
+        else:
+            continue
+        lines.append(f"| {k} | {grid} | {nl} | {vals} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | "
+                     f"{(rd + wr) / vals:.3f} | {alg} |")
+    lines += ["", "Values per launch follow from the grid (the last chunk of a launch may be short, so",
+              "they are upper bounds for the smaller launches)."]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
 SQ_COUNTERS = "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_BUSY_CYCLES"
 SQ_CMD = ("rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv -d rocprof_out/pmc_sq_rs -o run -- "
           "python3 bench.py --only rs_512m")
@@ -710,6 +769,9 @@ def main(argv=None) -> int:
                     help="write a profiles/ summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-rs-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
                     help="write a profiles/ summary of a rocprofv3 --stats run of --only rs_512m and exit")
+    ap.add_argument("--summarize-rs-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "--only rs_512m and exit")
     ap.add_argument("--summarize-sq", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
                     help="write a profiles/ summary of a rocprofv3 SQ-counter run of --only rs_512m and exit")
     ap.add_argument("--only", default=None,
@@ -726,6 +788,9 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_sq:
         summarize_sq(*args.summarize_sq)
+        return 0
+    if args.summarize_rs_pmc:
+        summarize_pmc_rs(*args.summarize_rs_pmc)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and there is no "
@@ -749,7 +814,9 @@ def main(argv=None) -> int:
         if args.only not in runners:
             print(f"--only takes one of {sorted(runners)}", file=sys.stderr)
             return 2
-        print(json.dumps({"workload": args.only, **runners[args.only]()}), flush=True)
+        res = runners[args.only]()
+        # the 1 GiB copy whose counter readings scale a --pmc run of this command
+        print(json.dumps({"workload": args.only, **res, "hbm_copy_GBps": copy_ceiling(torch)}), flush=True)
         return 0
 
     log("generating bucket_64m")
