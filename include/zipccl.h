@@ -209,7 +209,7 @@ typedef struct zipccl_gather_segment_t {
 } zipccl_gather_segment_t;
 
 /* zipccl_compress over gathered segments: the same outputs, layout, workspace and
- * launches (the encode kernel reads each tile's row indices with scalar loads).
+ * launches (the encoder reads each tile's row indices with scalar loads).
  * Errors: as zipccl_compress; INVALID also for row_len not a multiple of 8 or below 512,
  * or NULL src / rows with nrows > 0; ALIGN for rows not 4-byte aligned; SIZE for
  * nrows * row_len >= 2^32 or src_rows >= 2^32. */
@@ -277,13 +277,14 @@ zipccl_status zipccl_decompress_accumulate_chunks(const void* const* static_in, 
 /* Chunked two-stream pipeline over a reduce-scatter receive share (S2.D; the chunked
  * multi-stream overlap of the CCCL page's pipeline section).  Chunks of `chunk` values
  * of every peer shard are compressed on stream_a (one compress call per chunk, one
- * segment per peer) and decoded + accumulated into dst on stream_b (one launch per
- * chunk).  The streams hand chunks over in groups of G (a power of two, at most 16, the
- * smallest with G * npeers * chunk >= 2^26 values, since each event record or wait costs
- * the host microseconds); a ring of two groups of chunk buffers lets group g + 1
- * compress while group g is reduced.  Each group is compressed by one
- * zipccl_compress_chunks call and reduced by one zipccl_decompress_accumulate_chunks call.  The scratch memory is caller-owned device memory
- * of zipccl_pipeline_scratch_size() bytes: the compress workspace plus 2 * G chunk
+ * segment per peer) and decoded + accumulated into dst on stream_b.  The streams hand
+ * chunks over in groups of G (a power of two, at most 16, the smallest with
+ * G * npeers * chunk >= 2^26 values, since each event record or wait costs the host
+ * microseconds); a ring of two groups of chunk buffers lets group g + 1 compress while
+ * group g is reduced.  Each group is compressed by one zipccl_compress_chunks call (its
+ * chunks share launches) and reduced by one zipccl_decompress_accumulate_chunks call.
+ * The scratch memory is caller-owned device memory of zipccl_pipeline_scratch_size()
+ * bytes: a compress workspace for the chunks that share a launch plus 2 * G chunk
  * buffers of npeers * (static_size(chunk) + chunk) bytes.
  * Overlapping transfers of the compressed chunks would sit between the two streams. */
 typedef struct zipccl_pipeline zipccl_pipeline;
