@@ -10,7 +10,7 @@
 //
 // Work decomposition.  A tile is 512 values: lane l of a wave holds values 8l..8l+7,
 // one 16-byte load.  A block is 8 tiles (4096 values, one escape-offset entry); a unit
-// is 4 blocks (one compress or decompress workgroup, one half block per wave).
+// is 4 blocks (one encoding workgroup, one half block per wave).
 //   * Planes.  A lane looks up, per value, a one-byte code entry (3-bit code plus an
 //     escape flag) and ORs the 8 entries, the one of column j shifted by 4j, into one
 //     32-bit row.  A 32x32 bit transpose inside each half-wave (5 stages: a lane
@@ -21,8 +21,8 @@
 //   * Escapes.  A DPP prefix scan over the wave's per-lane escape counts gives each
 //     lane the position of its first escape; a lane's escapes follow in column order.
 //     Decoding replaces the code-0 byte of the v_perm table with the lane's first
-//     escape of each group of 4 columns, so only lanes with two escapes in one group
-//     patch bytes one by one.
+//     escape of each group of 4 columns; a second escape in a group is placed by masks,
+//     and only a third or fourth is patched byte by byte.
 //   * Compress is one launch (compress_single_kernel): encoding workgroups write the A
 //     bytes and planes, stage each unit's escapes contiguously in the workspace and then
 //     publish the unit's escape count in a ready word tagged with the call's tag; the
@@ -40,7 +40,8 @@
 //   * Decompress: one workgroup per block, one half block per wave, one barrier to share
 //     the escape count of the first half; each segment has its own escape buffer.
 //     Decode-accumulate: one workgroup per block, one wave per tile, all peers of a
-//     tile in one wave; one launch may cover several chunks, each with its own peers.
+//     tile in one wave; the A bytes wait in LDS so that 4 workgroups fit per CU; one
+//     launch may cover several chunks, each with its own peers.
 #include "zipccl_internal.h"
 #include "zipccl.h"
 
