@@ -1161,8 +1161,10 @@ struct PeerBlock {
 template <int kPeers>
 // Up to 7 peers the kernel fits 64 VGPRs without spills (the A bytes wait in LDS, not in
 // registers), so 4 workgroups run per CU; the kernel is latency-bound (at 2 workgroups
-// per CU it took 1.77x as long as at 3), and 4 took 7-peer launches 12 % below 3.
-__global__ __launch_bounds__(kAccThreads) __attribute__((amdgpu_waves_per_eu(kPeers <= 8 ? 8 : 4)))
+// per CU it took 1.77x as long as at 3), and 4 took 7-peer launches 12 % below 3.  With
+// 8 peers the LDS allows 3 workgroups per CU (6 waves per SIMD).
+__global__ __launch_bounds__(kAccThreads)
+__attribute__((amdgpu_waves_per_eu(kPeers <= 7 ? 8 : (kPeers <= 8 ? 6 : 4))))
 void accumulate_kernel(const AArgs a)
 {
     __shared__ uint32_t s_cnt[kPeers][kAccWaves];
