@@ -161,13 +161,16 @@ def run_codec(torch, bc, iters, warmup):
     return (time.perf_counter() - t0) / iters * 1e3
 
 
-def op_times(torch, bc, rounds):
+def op_times(torch, bc, rounds, batches=3):
     """Average launch times (ms) of compress and decompress over back-to-back launches on
-    the rotating sets."""
+    the rotating sets: the median over `batches` batches, so that one disturbed batch
+    does not set the figure."""
     plans = bc.plans()
-    c = batched_ms(torch, lambda k: bc.compress(k, plans), len(bc.sets), rounds)
-    d = batched_ms(torch, bc.decompress, len(bc.sets), rounds)
-    return c, d
+    cs, ds = [], []
+    for _ in range(batches):
+        cs.append(batched_ms(torch, lambda k: bc.compress(k, plans), len(bc.sets), rounds))
+        ds.append(batched_ms(torch, bc.decompress, len(bc.sets), rounds))
+    return median(cs), median(ds)
 
 
 def batched_ms(torch, fn, sets, rounds):
