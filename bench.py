@@ -455,6 +455,7 @@ def bench_estimated_plans(torch, Z, W, rounds):
     n = wl.n_total
     k = len(tens)
     plans_dev = torch.empty(8 * k, dtype=torch.uint8, device="cuda")
+    est_ws = torch.empty(Z.estimate_workspace_size(k), dtype=torch.uint8, device="cuda")
     static_bytes = sum(Z.static_size(x.size) for x in wl.segments)
     st = torch.empty(static_bytes, dtype=torch.uint8, device="cuda")
     esc = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -465,7 +466,8 @@ def bench_estimated_plans(torch, Z, W, rounds):
     import ctypes
     segs = Z._segment_array(tens)
     L = Z.lib()
-    est_args = (segs, k, 16, ctypes.c_void_p(plans_dev.data_ptr()), None)
+    est_args = (segs, k, 16, ctypes.c_void_p(plans_dev.data_ptr()), ctypes.c_void_p(est_ws.data_ptr()),
+                est_ws.numel(), None)
     comp_args = (segs, k, ctypes.c_void_p(plans_dev.data_ptr()), ctypes.c_void_p(st.data_ptr()), st.numel(),
                  ctypes.c_void_p(esc.data_ptr()), esc.numel(), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                  ctypes.c_void_p(n_esc.data_ptr()), ctypes.c_void_p(status.data_ptr()), None)

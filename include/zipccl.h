@@ -144,18 +144,24 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
                               void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
                               uint64_t* n_esc_out, uint32_t* status, void* stream);
 
+/* Device scratch bytes zipccl_estimate_plans needs for nseg segments (16 partial sums of
+ * 16 bytes per segment). */
+uint64_t zipccl_estimate_workspace_size(int nseg);
+
 /* Plans estimated on the device, for tensors whose sigma the caller does not know
  * (S2.A's Gaussian model; the pages derive sigma from the layer's weights instead): for
  * each segment, sigma = sqrt(mean of x^2) over the finite values of every stride-th tile
- * of 512 values (tiles k * stride, k = 0, 1, ...; one workgroup per segment reads them),
- * summed in fp64 in a fixed order, then
- * the table of zipccl_plan(sigma, NULL) (no finite value, or sigma 0: sigma = 1) written
- * to plans_dev[s].  segs[s].plan is ignored.  One launch, nothing returns to the host.
+ * of 512 values (tiles k * stride, k = 0, 1, ...), summed in fp64 in a fixed order (16
+ * workgroups per segment each add their share, a second launch adds the 16 partial sums
+ * in order), then the table of zipccl_plan(sigma, NULL) (no finite value, or sigma 0:
+ * sigma = 1) written to plans_dev[s].  segs[s].plan is ignored.  Two launches on
+ * `stream`; nothing returns to the host, and the result is the same on every run.
  *   plans_dev   device, 8-byte aligned, nseg entries
+ *   workspace   device scratch, 16-byte aligned, zipccl_estimate_workspace_size(nseg) bytes
  * Errors: INVALID (NULL pointers with n > 0, nseg outside 1..ZIPCCL_MAX_SEGMENTS,
- * stride 0), ALIGN, SIZE (n >= 2^32), HIP. */
+ * stride 0), ALIGN, SIZE (n >= 2^32, workspace too small), HIP. */
 zipccl_status zipccl_estimate_plans(const zipccl_segment_t* segs, int nseg, uint32_t stride, zipccl_plan_t* plans_dev,
-                                    void* stream);
+                                    void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* zipccl_compress with segment s coded by the plan in device memory at plans_dev[s]
  * (written by zipccl_estimate_plans, or by the caller: 7 distinct ascending exponents in

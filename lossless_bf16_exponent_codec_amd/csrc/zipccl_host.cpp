@@ -321,11 +321,18 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
                              n_esc_out, status, stream);
 }
 
-zipccl_status zipccl_estimate_plans(const zipccl_segment_t* segs, int nseg, uint32_t stride, zipccl_plan_t* plans_dev,
-                                    void* stream)
+uint64_t zipccl_estimate_workspace_size(int nseg)
 {
-    if (!segs || nseg < 1 || nseg > kMaxSegs || stride < 1 || !plans_dev) return ZIPCCL_ERR_INVALID;
-    if (!aligned(plans_dev, 8)) return ZIPCCL_ERR_ALIGN;
+    if (nseg < 1) nseg = 1;
+    return uint64_t(nseg) * kEstParts * 16;
+}
+
+zipccl_status zipccl_estimate_plans(const zipccl_segment_t* segs, int nseg, uint32_t stride, zipccl_plan_t* plans_dev,
+                                    void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    if (!segs || nseg < 1 || nseg > kMaxSegs || stride < 1 || !plans_dev || !workspace) return ZIPCCL_ERR_INVALID;
+    if (!aligned(plans_dev, 8) || !aligned(workspace, 16)) return ZIPCCL_ERR_ALIGN;
+    if (workspace_bytes < zipccl_estimate_workspace_size(nseg)) return ZIPCCL_ERR_SIZE;
     EArgs a;
     std::memset(&a, 0, sizeof(a));
     for (int s = 0; s < nseg; s++) {
@@ -336,6 +343,7 @@ zipccl_status zipccl_estimate_plans(const zipccl_segment_t* segs, int nseg, uint
         a.n[s] = uint32_t(segs[s].n);
     }
     a.plans = reinterpret_cast<uint8_t*>(plans_dev);
+    a.partial = static_cast<double*>(workspace);
     a.stride = stride;
     a.nseg = nseg;
     return hip_status(launch_estimate_plans(a, static_cast<hipStream_t>(stream)));

@@ -149,11 +149,13 @@ __host__ __device__ inline uint64_t static_bytes_of(uint64_t n) { return offsets
 hipError_t launch_compress(const CArgs& a, hipStream_t s, bool single);
 hipError_t launch_decompress(const DArgs& a, hipStream_t s);
 // Plans from a strided sample of each segment (one workgroup per segment).
+constexpr uint32_t kEstParts = 16;   // workgroups per segment in the estimate
 struct EArgs {
     const uint16_t* src[kMaxSegs];
     uint32_t n[kMaxSegs];
     uint8_t* plans;        // device, 8 bytes per segment
-    uint32_t stride;       // every stride-th group of 8 values is sampled
+    double* partial;       // device scratch: kEstParts (sum, count) pairs per segment
+    uint32_t stride;       // every stride-th tile of 512 values is sampled
     int32_t nseg;
 };
 static_assert(sizeof(EArgs) <= 4096, "kernel arguments are limited to 4 KiB");

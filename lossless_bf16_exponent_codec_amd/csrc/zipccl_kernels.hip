@@ -1506,38 +1506,41 @@ hipError_t launch_compress(const CArgs& a, hipStream_t s, bool single)
 // --------------------------------------------------------------------------------
 // plans from the data: sigma estimated on the device
 // --------------------------------------------------------------------------------
-// One workgroup per segment (16 waves).  The sample is every stride-th tile of 512
-// values: wave w reads sampled tiles w, w + 16, ..., 16 at a time, lane l the 16 bytes of
-// values 8l .. 8l + 7 (coalesced 1 KB per wave load).  Each thread sums, in fp64, the
-// squares of its finite values and counts them; the workgroup adds the 1024 partial sums
-// in a fixed order, so the estimate is the same on every run.  sigma = sqrt(sum / count)
-// (the model's mean is 0; no finite sample, or sigma 0, counts as sigma 1), then the
-// plan's closed form: e0 = 123 + floor(log2(sigma) - c), clamped to 1..248, table
-// e0 .. e0 + 6.
-constexpr uint32_t kEstThreads = 1024;
+// The sample is every stride-th tile of 512 values: sample k is tile k * stride.  Each
+// segment is split over kEstParts workgroups of 4 waves; part p takes samples p, p + 16,
+// p + 32, ...; its wave w takes that list's entries w, w + 4, ..., 8 of them at a time,
+// lane l the 16 bytes of values 8l .. 8l + 7 (one coalesced 1 KB load per wave and
+// sample).  Each thread sums, in fp64, the squares of its finite values and counts them;
+// the workgroup adds its 256 partial sums in a fixed order and stores (sum, count) in the
+// caller's scratch.  A second launch adds each segment's 16 pairs in part order, so the
+// estimate is the same on every run.  sigma = sqrt(sum / count) (the model's mean is 0;
+// no finite sample, or sigma 0, counts as sigma 1), then the plan's closed form:
+// e0 = 123 + floor(log2(sigma) - c), clamped to 1..248, table e0 .. e0 + 6.
+constexpr uint32_t kEstThreads = 256;
 constexpr uint32_t kEstWaves = kEstThreads / 64;
+constexpr uint32_t kEstBatch = 8;   // samples in flight per wave
 constexpr double kSwitchPhaseDev = 0.7195805543641254;   // where the 7-binade window moves up
 
 namespace {
 
-__global__ __launch_bounds__(kEstThreads) void estimate_plans_kernel(const EArgs a)
+__global__ __launch_bounds__(kEstThreads) void estimate_partial_kernel(const EArgs a)
 {
     __shared__ double s_sum[kEstThreads];
     __shared__ uint32_t s_cnt[kEstThreads];
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int s = blockIdx.x;
+    const uint32_t s = blockIdx.x / kEstParts, part = blockIdx.x % kEstParts;
     const uint16_t* src = a.src[s];
     const uint32_t n = a.n[s];
     const uint64_t T = tiles_of(n);
     double sum = 0.0;
     uint32_t cnt = 0;
-    constexpr uint32_t kBatch = 16;   // sampled tiles in flight per wave
-    for (uint64_t k0 = wave; k0 * a.stride < T; k0 += uint64_t(kBatch) * kEstWaves) {
-        uint4 v[kBatch];
+    for (uint64_t j0 = wave; (part + uint64_t(kEstParts) * j0) * a.stride < T; j0 += uint64_t(kEstBatch) * kEstWaves) {
+        uint4 v[kEstBatch];
 #pragma unroll
-        for (uint32_t b = 0; b < kBatch; b++) {
-            const uint64_t i = (k0 + uint64_t(b) * kEstWaves) * a.stride * kTile + 8ull * lane;
+        for (uint32_t b = 0; b < kEstBatch; b++) {
+            const uint64_t k = part + uint64_t(kEstParts) * (j0 + uint64_t(b) * kEstWaves);
+            const uint64_t i = k * a.stride * kTile + 8ull * lane;
             if (i + 8 <= n) {
                 v[b] = load_nt(reinterpret_cast<const uint4*>(src + i));
             } else {   // the segment's ragged end, or past it: missing values read as NaN
@@ -1550,7 +1553,7 @@ __global__ __launch_bounds__(kEstThreads) void estimate_plans_kernel(const EArgs
             }
         }
 #pragma unroll
-        for (uint32_t b = 0; b < kBatch; b++) {
+        for (uint32_t b = 0; b < kEstBatch; b++) {
             const uint32_t w[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
 #pragma unroll
             for (int j = 0; j < 8; j++) {
@@ -1574,22 +1577,41 @@ __global__ __launch_bounds__(kEstThreads) void estimate_plans_kernel(const EArgs
         __syncthreads();
     }
     if (tid == 0) {
-        double sigma = s_cnt[0] ? sqrt(s_sum[0] / double(s_cnt[0])) : 1.0;
-        if (!(sigma > 0.0) || !__builtin_isfinite(sigma)) sigma = 1.0;
-        const double e = 123.0 + floor(log2(sigma) - kSwitchPhaseDev);
-        const uint32_t e0 = uint32_t(fmin(248.0, fmax(1.0, e)));
-        const uint32_t lo = e0 | (e0 + 1) << 8 | (e0 + 2) << 16 | (e0 + 3) << 24;
-        const uint32_t hi = (e0 + 4) | (e0 + 5) << 8 | (e0 + 6) << 16;
-        reinterpret_cast<uint2*>(a.plans)[s] = make_uint2(lo, hi);
+        double* out = a.partial + 2 * (uint64_t(s) * kEstParts + part);
+        out[0] = s_sum[0];
+        out[1] = double(s_cnt[0]);
     }
+}
+
+// One thread per segment: the 16 partial pairs in part order, then the plan.
+__global__ __launch_bounds__(64) void estimate_finish_kernel(const EArgs a)
+{
+    const uint32_t s = threadIdx.x;
+    if (s >= uint32_t(a.nseg)) return;
+    const double* in = a.partial + 2 * uint64_t(s) * kEstParts;
+    double sum = 0.0, cnt = 0.0;
+    for (uint32_t p = 0; p < kEstParts; p++) {
+        sum += in[2 * p];
+        cnt += in[2 * p + 1];
+    }
+    double sigma = cnt > 0.0 ? sqrt(sum / cnt) : 1.0;
+    if (!(sigma > 0.0) || !__builtin_isfinite(sigma)) sigma = 1.0;
+    const double e = 123.0 + floor(log2(sigma) - kSwitchPhaseDev);
+    const uint32_t e0 = uint32_t(fmin(248.0, fmax(1.0, e)));
+    const uint32_t lo = e0 | (e0 + 1) << 8 | (e0 + 2) << 16 | (e0 + 3) << 24;
+    const uint32_t hi = (e0 + 4) | (e0 + 5) << 8 | (e0 + 6) << 16;
+    reinterpret_cast<uint2*>(a.plans)[s] = make_uint2(lo, hi);
 }
 
 }  // namespace
 
+static_assert(kMaxSegs <= 64, "the finishing launch takes one thread per segment");
+
 hipError_t launch_estimate_plans(const EArgs& a, hipStream_t s)
 {
     if (a.nseg < 1) return hipSuccess;
-    hipLaunchKernelGGL(estimate_plans_kernel, dim3(a.nseg), dim3(kEstThreads), 0, s, a);
+    hipLaunchKernelGGL(estimate_partial_kernel, dim3(a.nseg * kEstParts), dim3(kEstThreads), 0, s, a);
+    hipLaunchKernelGGL(estimate_finish_kernel, dim3(1), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -85,7 +85,9 @@ def _load() -> ctypes.CDLL:
                                            ctypes.POINTER(u64), ctypes.POINTER(vp), ctypes.POINTER(u64), vp, u64,
                                            vp, vp, vp]
     lib.zipccl_estimate_plans.restype = i32
-    lib.zipccl_estimate_plans.argtypes = [ctypes.POINTER(SegmentT), i32, ctypes.c_uint32, vp, vp]
+    lib.zipccl_estimate_plans.argtypes = [ctypes.POINTER(SegmentT), i32, ctypes.c_uint32, vp, vp, u64, vp]
+    lib.zipccl_estimate_workspace_size.restype = u64
+    lib.zipccl_estimate_workspace_size.argtypes = [i32]
     lib.zipccl_compress_device_plans.restype = i32
     lib.zipccl_compress_device_plans.argtypes = [ctypes.POINTER(SegmentT), i32, vp, vp, u64, vp, u64, vp, u64, vp,
                                                  vp, vp]
@@ -247,11 +249,17 @@ def _segment_array(tensors):
     return arr
 
 
-def estimate_plans(tensors, plans_dev, stride: int = 16, stream=None):
+def estimate_workspace_size(nseg: int) -> int:
+    return int(_lib.zipccl_estimate_workspace_size(nseg))
+
+
+def estimate_plans(tensors, plans_dev, workspace, stride: int = 16, stream=None):
     """zipccl_estimate_plans: plans_dev, a uint8 device tensor of 8 * len(tensors) bytes,
-    receives one plan per bf16 tensor.  PlanT.from_buffer_copy on its bytes reads them."""
+    receives one plan per bf16 tensor (PlanT.from_buffer_copy on its bytes reads them);
+    workspace, a device tensor of at least estimate_workspace_size(len(tensors)) bytes."""
     _check(_lib.zipccl_estimate_plans(_segment_array(tensors), len(tensors), stride, _ptr(plans_dev),
-                                      _stream(stream)), "zipccl_estimate_plans")
+                                      _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "zipccl_estimate_plans")
 
 
 def compress_device_plans(tensors, plans_dev, static_out, esc_out, workspace, n_esc_out=None, status=None,

@@ -36,7 +36,8 @@ def test_header_declares_the_abi():
                  "zipccl_pipeline_scratch_size", "zipccl_strerror", "zipccl_plan_many",
                  "zipccl_decompress_shards", "zipccl_compress_gather", "zipccl_compress_chunks",
                  "zipccl_decompress_accumulate_chunks", "zipccl_profile_codec", "zipccl_profile_scratch_size",
-                 "zipccl_rs_choose", "zipccl_estimate_plans", "zipccl_compress_device_plans"]:
+                 "zipccl_rs_choose", "zipccl_estimate_plans", "zipccl_estimate_workspace_size",
+                 "zipccl_compress_device_plans"]:
         assert want in names
 
 
@@ -158,10 +159,15 @@ def test_argument_errors_before_any_launch(Z):
     so[1] = fake + 64                    # the second chunk's static part misaligned: nothing enqueued
     assert L.zipccl_compress_chunks(segs2, 1, 2, so, sc, eo, ec, fake, cws, None, None, None) == Z.ERR_ALIGN
     est = L.zipccl_estimate_plans
-    assert est(seg, 1, 16, None, None) == Z.ERR_INVALID
-    assert est(seg, 0, 16, fake, None) == Z.ERR_INVALID
-    assert est(seg, 1, 0, fake, None) == Z.ERR_INVALID
-    assert est(seg, 1, 16, fake + 4, None) == Z.ERR_ALIGN
+    ews = Z.estimate_workspace_size(1)
+    assert ews == 256 and Z.estimate_workspace_size(16) == 16 * 256
+    assert est(seg, 1, 16, None, fake, ews, None) == Z.ERR_INVALID
+    assert est(seg, 1, 16, fake, None, ews, None) == Z.ERR_INVALID
+    assert est(seg, 0, 16, fake, fake, ews, None) == Z.ERR_INVALID
+    assert est(seg, 1, 0, fake, fake, ews, None) == Z.ERR_INVALID
+    assert est(seg, 1, 16, fake + 4, fake, ews, None) == Z.ERR_ALIGN
+    assert est(seg, 1, 16, fake, fake + 8, ews, None) == Z.ERR_ALIGN
+    assert est(seg, 1, 16, fake, fake, ews - 1, None) == Z.ERR_SIZE
     cdp = L.zipccl_compress_device_plans
     assert cdp(seg, 1, None, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_INVALID
     assert cdp(seg, 1, fake + 4, fake, 1 << 20, fake, 100, fake, ws, None, None, None) == Z.ERR_ALIGN

@@ -600,7 +600,7 @@ def sample_sigma(x, stride):
     return s if s > 0 and np.isfinite(s) else 1.0
 
 
-@pytest.mark.parametrize("stride", [1, 16])
+@pytest.mark.parametrize("stride", [1, 7, 16])
 def test_estimate_plans_and_compress_with_them(Z, stride):
     import math
     nan = np.full(4096, 0x7FC1, np.uint16)
@@ -611,9 +611,15 @@ def test_estimate_plans_and_compress_with_them(Z, stride):
             W.gaussian_bf16(30000, 1e-30, 95)]
     tens = [dev_bf16(x) for x in segs]
     plans_dev = torch.full((8 * len(segs),), 0xAA, dtype=torch.uint8, device="cuda")
-    Z.estimate_plans(tens, plans_dev, stride=stride)
+    est_ws = torch.full((Z.estimate_workspace_size(len(segs)),), 0xAA, dtype=torch.uint8, device="cuda")
+    Z.estimate_plans(tens, plans_dev, est_ws, stride=stride)
     torch.cuda.synchronize()
     raw = plans_dev.cpu().numpy().tobytes()
+    # the same plans again, with the first call's partial sums left in the scratch
+    again = torch.full_like(plans_dev, 0x55)
+    Z.estimate_plans(tens, again, est_ws, stride=stride)
+    torch.cuda.synchronize()
+    assert again.cpu().numpy().tobytes() == raw
     got = [Z.PlanT.from_buffer_copy(raw[8 * k:8 * k + 8]) for k in range(len(segs))]
     for k, x in enumerate(segs):
         s = sample_sigma(x, stride)
