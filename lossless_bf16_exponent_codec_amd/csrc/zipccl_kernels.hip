@@ -1202,18 +1202,20 @@ void accumulate_kernel(const AArgs a)
     const uint8_t* const safe = peer_st[0];
     const uint32_t tl = has_tile ? t : T - 1;   // T >= 1: a launch has at least one block
     const uint32_t pdl = pdw == ~0u ? 0u : pdw;   // lanes with p = 3: any dword (bits unused)
+    // Up to 8 peers the launch picks the instance of exactly npeers: every slot exists, so
+    // the peers' pointers are read with no clamp and their loads go out together rather
+    // than one after another.
+    const uint8_t* stp[kPeers];
+#pragma unroll
+    for (int p = 0; p < kPeers; p++) stp[p] = peer_st[kPeers <= 8 || uint32_t(p) < P ? p : 0];
     uint32_t pw[kPeers];
     uint2 Ap[kPeers];
 #pragma unroll
-    for (int p = 0; p < kPeers; p++) {
-        const uint8_t* st = peer_st[uint32_t(p) < P ? p : 0];
-        pw[p] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * tl) + pdl);
-    }
+    for (int p = 0; p < kPeers; p++)
+        pw[p] = load_nt(reinterpret_cast<const uint32_t*>(stp[p] + planes_off(n) + 192ull * tl) + pdl);
 #pragma unroll
-    for (int p = 0; p < kPeers; p++) {
-        const uint8_t* st = peer_st[uint32_t(p) < P ? p : 0];
-        Ap[p] = load_nt(reinterpret_cast<const uint2*>(st + 128 + 512ull * tl + 8 * lane));
-    }
+    for (int p = 0; p < kPeers; p++)
+        Ap[p] = load_nt(reinterpret_cast<const uint2*>(stp[p] + 128 + 512ull * tl + 8 * lane));
     uint4 lv = load_nt(reinterpret_cast<const uint4*>(nvalid == 8 ? reinterpret_cast<const uint8_t*>(local + i0)
                                                                     : safe));
 
@@ -1254,7 +1256,7 @@ void accumulate_kernel(const AArgs a)
         cnt[p] = 0;
         if (p < kPeers) {
             rows[p] = zf[p] = 0;
-            if (uint32_t(p) < P) {
+            if (kPeers <= 8 || uint32_t(p) < P) {   // no branch up to 8 peers: transposes interleave
                 rows[p] = transpose32(pw[p], tc);
                 zf[p] = escape_flags(rows[p], vf);
             }
@@ -1295,7 +1297,7 @@ void accumulate_kernel(const AArgs a)
         for (int q = 0; q < 8 && 8 * h + q < kPeers; q++) {
             const int p = 8 * h + q;
             before[p] = mine[p] = 0;
-            if (uint32_t(p) < P) {
+            if (kPeers <= 8 || uint32_t(p) < P) {
                 const uint32_t base = uint32_t(__builtin_amdgcn_readlane(int(excl), 8 * q));
                 const uint32_t next = q < 7 ? uint32_t(__builtin_amdgcn_readlane(int(excl), 8 * q + 8))
                                             : uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
@@ -1320,7 +1322,7 @@ void accumulate_kernel(const AArgs a)
     uint8_t* esc_lds = s_esc[wave];
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
-        if (uint32_t(p) < P && !bad && has_tile) {
+        if ((kPeers <= 8 || uint32_t(p) < P) && !bad && has_tile) {
             const uint8_t* tile_esc = s_blk[p] + before[p];
             if (before[p] + mine[p] > kAccBlkHead) {
                 // rare (escape-heavy tables): the tile's escapes go past the block's
