@@ -1303,8 +1303,9 @@ void accumulate_kernel(const AArgs a)
                                             : uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
                 before[p] = uint32_t(__builtin_amdgcn_readlane(int(excl), int(8 * q + wave))) - base;
                 mine[p] = total[p];
-                // the offset table must agree with the planes
-                bad = bad || !s_peer[p].ok || next - base != s_peer[p].count;
+                // the offset table must agree with the planes (bitwise, no branch per peer:
+                // the peers' LDS records are read together)
+                bad = bad | (s_peer[p].ok == 0u) | (next - base != s_peer[p].count);
             }
         }
     }
