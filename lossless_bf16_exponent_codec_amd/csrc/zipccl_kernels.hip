@@ -123,6 +123,23 @@ __device__ inline int find_segment(const Seg* seg, int nseg, uint32_t u)
     return lo;
 }
 
+// The same lookup by the whole wave at once, for code where every lane of the wave is
+// active and u is the same in all of them: lane s compares segment s (nseg <= 64), and the
+// last segment whose first index is at most u is the highest lane of the ballot.  One
+// load round trip instead of one per binary-search step (with 1 or 2 segments the binary
+// search needs none or one).
+template <auto First, class Seg>
+__device__ inline int find_segment_wave(const Seg* seg, int nseg, uint32_t u)
+{
+    static_assert(kMaxSegs <= 64, "one lane per segment");
+    if (nseg <= 2) return find_segment<First>(seg, nseg, u);   // no load, or one
+    u = __builtin_amdgcn_readfirstlane(u);
+    const int lane = int(lane_id());
+    const bool at_or_before = lane < nseg && seg[lane].*First <= u;   // seg[0] starts at 0
+    const uint64_t m = __builtin_amdgcn_ballot_w64(at_or_before);
+    return 63 - __builtin_clzll(m | 1ull);
+}
+
 // Loads the 8 values of this lane in tile t; values at or past n read as 0.
 __device__ inline uint4 load_lane(const uint16_t* src, uint64_t t, uint32_t lane, uint32_t n)
 {
@@ -444,7 +461,7 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
 
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, unit);
+    const int s = find_segment_wave<&CSeg::unit0>(a.seg, a.nseg, unit);
     const CSeg& sg = a.seg[s];
     const uint32_t n = sg.n;
     const uint32_t hb = (unit - sg.unit0) * kEncWaves + wave;   // half block within the segment
@@ -1386,7 +1403,7 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(const DArgs a)
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t unit = blockIdx.x;
-    const int s = find_segment<&DSeg::unit0>(a.seg, a.nseg, unit);
+    const int s = find_segment_wave<&DSeg::unit0>(a.seg, a.nseg, unit);
     const DSeg& sg = a.seg[s];
     const uint32_t n = sg.n;
     const uint32_t T = uint32_t(tiles_of(n)), K = uint32_t(blocks_of(n));
