@@ -141,6 +141,15 @@ def test_many_segments_one_launch(Z):
     round_trip(Z, segs, plans)
 
 
+@pytest.mark.parametrize("sizes", [[0, 0, 5000], [5000, 0, 0], [4096, 0, 4097], [0] * 63 + [20000],
+                                   [20000] + [0] * 63, [1, 0, 0, 1, 0, 16385, 0, 0], [0, 16384, 0, 0, 700]])
+def test_empty_segments_around_data(Z, sizes):
+    # segments with no units share their first unit with the next one: each workgroup must
+    # still find the segment that holds its unit, with empty runs before, between and after
+    segs = [W.gaussian_bf16(n, 0.05, 700 + k) if n else np.zeros(0, np.uint16) for k, n in enumerate(sizes)]
+    round_trip(Z, segs, [Z.plan(sigma=0.05)] * len(segs))
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_segments_random_tables(Z, seed):
     # random bit patterns (mostly escapes) and random explicit tables, up to 64 segments
