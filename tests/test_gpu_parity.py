@@ -609,6 +609,31 @@ def sample_sigma(x, stride):
     return s if s > 0 and np.isfinite(s) else 1.0
 
 
+def test_estimate_plans_64_segments(Z):
+    # the most segments one call takes: every part of every segment and every lane of the
+    # finishing launch in use, sizes from empty to several parts' worth of sampled tiles
+    import math
+    rng = np.random.default_rng(77)
+    segs, sig = [], []
+    for k in range(64):
+        n = int(rng.choice([0, 3, 512, 4097, 70000, 300001]))
+        s = float(10 ** rng.uniform(-6, 2))
+        segs.append(W.gaussian_bf16(n, s, 900 + k) if n else np.zeros(0, np.uint16))
+        sig.append(s)
+    tens = [dev_bf16(x) for x in segs]
+    plans_dev = torch.full((8 * 64,), 0xAA, dtype=torch.uint8, device="cuda")
+    est_ws = torch.full((Z.estimate_workspace_size(64),), 0xAA, dtype=torch.uint8, device="cuda")
+    Z.estimate_plans(tens, plans_dev, est_ws, stride=3)
+    torch.cuda.synchronize()
+    raw = plans_dev.cpu().numpy().tobytes()
+    for k, x in enumerate(segs):
+        got = Z.PlanT.from_buffer_copy(raw[8 * k:8 * k + 8])
+        s = sample_sigma(x, 3)
+        if abs(math.log2(s) - math.floor(math.log2(s)) - 0.7195805543641254) < 1e-9:
+            continue                                      # at the switch: either window
+        assert list(got.exponents) == [int(v) for v in O.plan_sigma(s)], (k, x.size, s)
+
+
 @pytest.mark.parametrize("stride", [1, 7, 16])
 def test_estimate_plans_and_compress_with_them(Z, stride):
     import math
