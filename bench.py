@@ -439,7 +439,7 @@ def bench_switcher(torch, Z, W):
     links = {"xgmi_7x153GBps": Z.LinkT(153.0, 2.0, 7), "pcie5_x16_64GBps": Z.LinkT(64.0, 5.0, 1),
              "ib_ndr_50GBps": Z.LinkT(50.0, 5.0, 1)}
     out = {"compress_GBps": round(prof.compress_GBps, 1), "accumulate_GBps": round(prof.accumulate_GBps, 1),
-           "ratio": round(prof.ratio, 5), "ranks": 8, "bytes_per_rank": 8 * wl.extra["shard"] * 2}
+           "compressed_fraction": round(prof.compressed_fraction, 5), "ranks": 8, "bytes_per_rank": 8 * wl.extra["shard"] * 2}
     for name, link in links.items():
         use, tn, tz = Z.rs_choose(prof, link, 8, out["bytes_per_rank"])
         out[name] = {"use_codec": use, "native_us": round(tn, 1), "zipped_us": round(tz, 1)}

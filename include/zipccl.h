@@ -60,7 +60,7 @@ typedef enum zipccl_status {
     ZIPCCL_ERR_ALIGN = 2,     /* a pointer is not aligned as required */
     ZIPCCL_ERR_SIZE = 3,      /* a size limit is exceeded or a buffer is too small */
     ZIPCCL_ERR_HIP = 4,       /* the HIP runtime reported an error */
-    ZIPCCL_ERR_CORRUPT = 5    /* a compressed header failed validation (host-side parse) */
+    ZIPCCL_ERR_CORRUPT = 5    /* a host-side check of device results failed (zipccl_profile_codec) */
 } zipccl_status;
 
 /* Bits OR-ed into the optional device status word. */
@@ -128,15 +128,17 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
  *               beyond esc_cap are dropped and ZIPCCL_STATUS_ESC_OVERFLOW is set; the
  *               headers still carry the true counts.
  *   workspace   device scratch, see zipccl_workspace_size.
- * The work is one kernel launch on `stream`: its encoding workgroups write the
- * fixed-size sections, stage each unit's escapes and publish the unit's escape count in
- * the workspace; its last workgroups compute the escape positions from those counts
- * (bounded wait), write the offset tables and headers and compact the escapes.  While
- * `stream` is being captured into a graph, or with ZIPCCL_SINGLE_LAUNCH=0 in the
- * environment, the same work is two launches (encode, then place); above 2^28 values in
- * one call it is encode, a one-workgroup scan launch, then place.
+ * With a status word the work is one kernel launch on `stream`: its encoding
+ * workgroups write the fixed-size sections, stage each unit's escapes and publish the
+ * unit's escape count in the workspace; its last workgroups compute the escape positions
+ * from those counts (bounded wait; a wait that runs out sets ZIPCCL_STATUS_WAIT_LIMIT),
+ * write the offset tables and headers and compact the escapes.  Without a status word,
+ * while `stream` is being captured into a graph, or with ZIPCCL_SINGLE_LAUNCH=0 in the
+ * environment, the same work is two launches (encode, then place) in which nothing
+ * waits, so nothing can time out unreported; above 2^28 values in one call it is encode,
+ * a one-workgroup scan launch, then place.
  *   n_esc_out   optional device u64[nseg + 1]: per-segment escape counts, then the total.
- *   status      optional device u32, bits OR-ed in.
+ *   status      optional device u32, bits OR-ed in (NULL: the two-launch path).
  * Errors: INVALID (NULL pointers, nseg outside 1..ZIPCCL_MAX_SEGMENTS, bad table),
  * ALIGN, SIZE (segment n >= 2^32, sum >= 2^32, static_cap or workspace too small),
  * HIP (launch failure). */
@@ -323,7 +325,7 @@ void zipccl_pipeline_destroy(zipccl_pipeline* pipe);
 typedef struct zipccl_codec_profile_t {
     double compress_GBps;     /* BF16 bytes compressed per second on this GPU */
     double accumulate_GBps;   /* BF16 bytes of peer shards decoded and accumulated per second */
-    double ratio;             /* compressed bytes / BF16 bytes of the sample */
+    double compressed_fraction; /* compressed bytes / BF16 bytes of the sample (below 1 saves) */
 } zipccl_codec_profile_t;
 
 typedef struct zipccl_link_t {
@@ -339,18 +341,20 @@ uint64_t zipccl_profile_scratch_size(uint64_t n, int npeers);
  * compressed with `plan`): a compress of npeers segments (all the sample) and a
  * decode-accumulate of npeers peer shards, each timed with HIP events over 3 launches
  * after one warm-up, and the compressed size.  Synchronises `stream` (an initialisation
- * call).  scratch: device, 256-byte aligned, zipccl_profile_scratch_size() bytes.
+ * call).  scratch: device, 256-byte aligned, zipccl_profile_scratch_size() bytes; it also
+ * holds the status word of the profiled calls.
  * Errors: INVALID (NULL pointers, n == 0, npeers outside 1..ZIPCCL_MAX_PEERS, bad plan),
- * ALIGN, SIZE (n * npeers >= 2^32, scratch too small), HIP. */
+ * ALIGN, SIZE (n * npeers >= 2^32, scratch too small), HIP, CORRUPT (a profiled call set
+ * a device status bit; the profile is not written). */
 zipccl_status zipccl_profile_codec(const void* sample, uint64_t n, zipccl_plan_t plan, int npeers, void* scratch,
                                    uint64_t scratch_bytes, void* stream, zipccl_codec_profile_t* out);
 
 /* Chooses for a reduce-scatter of `bytes` BF16 bytes per rank over `ranks` ranks (each
  * rank keeps bytes / ranks).  With shard = bytes / ranks and m = ranks - 1 peers:
  *   native  = ceil(m / links) * (latency + shard / bw)        (the reduction rides along)
- *   zipped  = m * shard / compress + ceil(m / links) * (latency + ratio * shard / bw)
+ *   zipped  = m * shard / compress + ceil(m / links) * (latency + compressed_fraction * shard / bw)
  *             + m * shard / accumulate
- * use_codec = zipped < native, except that tensors under 1 MiB and ratios of 1 or more
+ * use_codec = zipped < native, except that tensors under 1 MiB and compressed fractions of 1 or more
  * always take the native path.  Host only; any output pointer may be NULL.
  * Errors: INVALID (NULL prof or link, ranks < 2, links < 1, non-positive rates). */
 zipccl_status zipccl_rs_choose(const zipccl_codec_profile_t* prof, const zipccl_link_t* link, int ranks,

@@ -63,11 +63,15 @@ uint64_t next_tag()
 }
 
 // Whether a compress call runs as one launch: yes unless the positions need the scan
-// kernel, the stream is being captured into a graph (a replay would repeat the tag baked
-// into the captured arguments), or ZIPCCL_SINGLE_LAUNCH=0 asks for the two-launch path.
+// kernel, the caller passed no status word, the stream is being captured into a graph (a
+// replay would repeat the tag baked into the captured arguments), or
+// ZIPCCL_SINGLE_LAUNCH=0 asks for the two-launch path.  The single launch's placing
+// workgroups wait (bounded) for the encoders, and a wait that runs out is reported only
+// through the status word; without one the two launches, which wait for nothing, run
+// instead, so no call can end with unwritten headers that nobody is told about.
 bool single_launch(const CArgs& a, hipStream_t stream)
 {
-    if (!a.direct) return false;
+    if (!a.direct || !a.status) return false;
     const char* e = std::getenv("ZIPCCL_SINGLE_LAUNCH");
     if (e && e[0] == '0' && e[1] == 0) return false;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -119,7 +123,7 @@ const char* zipccl_strerror(zipccl_status s)
         case ZIPCCL_ERR_ALIGN: return "misaligned pointer";
         case ZIPCCL_ERR_SIZE: return "size limit exceeded or buffer too small";
         case ZIPCCL_ERR_HIP: return "HIP runtime error";
-        case ZIPCCL_ERR_CORRUPT: return "corrupt compressed data";
+        case ZIPCCL_ERR_CORRUPT: return "corrupt data or a device status bit set";
     }
     return "unknown status";
 }
@@ -560,7 +564,7 @@ zipccl_status zipccl_decompress_accumulate_chunks(const void* const* static_in, 
 namespace {
 
 struct ProfileLayout {
-    uint64_t ws, st, esc, ne, dst, total;
+    uint64_t ws, st, esc, ne, status, dst, total;
 };
 
 ProfileLayout profile_layout(uint64_t n, int npeers)
@@ -571,7 +575,8 @@ ProfileLayout profile_layout(uint64_t n, int npeers)
     l.st = l.ws + r256(zipccl_workspace_size(n * uint64_t(npeers), npeers));
     l.esc = l.st + r256(uint64_t(npeers) * static_bytes_of(n));
     l.ne = l.esc + r256(uint64_t(npeers) * n);
-    l.dst = l.ne + r256(8 * uint64_t(npeers + 1));
+    l.status = l.ne + r256(8 * uint64_t(npeers + 1));
+    l.dst = l.status + 256;
     l.total = l.dst + r256(2 * n);
     return l;
 }
@@ -608,12 +613,16 @@ zipccl_status zipccl_profile_codec(const void* sample, uint64_t n, zipccl_plan_t
         eb[p] = uint64_t(npeers) * n;
     }
     uint64_t* ne_dev = reinterpret_cast<uint64_t*>(base + l.ne);
+    // a status word of its own: the profile is timed on the same launches callers get
+    // (the single-launch compress needs one), and a set bit fails the call
+    uint32_t* st_dev = reinterpret_cast<uint32_t*>(base + l.status);
+    if (hipMemsetAsync(st_dev, 0, sizeof(uint32_t), s) != hipSuccess) return ZIPCCL_ERR_HIP;
     auto compress = [&]() {
         return zipccl_compress(segs, npeers, base + l.st, uint64_t(npeers) * static_bytes_of(n), base + l.esc,
-                               uint64_t(npeers) * n, base + l.ws, l.st - l.ws, ne_dev, nullptr, stream);
+                               uint64_t(npeers) * n, base + l.ws, l.st - l.ws, ne_dev, st_dev, stream);
     };
     auto accumulate = [&]() {
-        return zipccl_decompress_accumulate(sin, ein, eb, npeers, n, sample, base + l.dst, nullptr, stream);
+        return zipccl_decompress_accumulate(sin, ein, eb, npeers, n, sample, base + l.dst, st_dev, stream);
     };
     hipEvent_t e[4] = {};
     for (auto& ev : e)
@@ -634,13 +643,16 @@ zipccl_status zipccl_profile_codec(const void* sample, uint64_t n, zipccl_plan_t
     uint64_t total_esc = 0;
     ok = ok && hipEventElapsedTime(&tc, e[0], e[1]) == hipSuccess && hipEventElapsedTime(&ta, e[2], e[3]) == hipSuccess;
     ok = ok && hipMemcpy(&total_esc, ne_dev + npeers, sizeof(total_esc), hipMemcpyDeviceToHost) == hipSuccess;
+    uint32_t dev_status = 0;
+    ok = ok && hipMemcpy(&dev_status, st_dev, sizeof(dev_status), hipMemcpyDeviceToHost) == hipSuccess;
     for (auto& ev : e) (void)hipEventDestroy(ev);
     if (r != ZIPCCL_OK) return r;
     if (!ok || tc <= 0 || ta <= 0) return ZIPCCL_ERR_HIP;
+    if (dev_status != 0) return ZIPCCL_ERR_CORRUPT;   // the device reported a status bit
     const double bf16 = 2.0 * double(n) * npeers;   // bytes of one launch
     out->compress_GBps = bf16 / (tc * 1e-3 / kReps) / 1e9;
     out->accumulate_GBps = bf16 / (ta * 1e-3 / kReps) / 1e9;
-    out->ratio = (double(npeers) * double(static_bytes_of(n)) + double(total_esc)) / bf16;
+    out->compressed_fraction = (double(npeers) * double(static_bytes_of(n)) + double(total_esc)) / bf16;
     return ZIPCCL_OK;
 }
 
@@ -648,16 +660,16 @@ zipccl_status zipccl_rs_choose(const zipccl_codec_profile_t* prof, const zipccl_
                                uint64_t bytes, int* use_codec, double* native_us, double* zipped_us)
 {
     if (!prof || !link || ranks < 2 || link->links < 1 || !(link->bw_GBps > 0) || !(link->latency_us >= 0) ||
-        !(prof->compress_GBps > 0) || !(prof->accumulate_GBps > 0) || !(prof->ratio > 0))
+        !(prof->compress_GBps > 0) || !(prof->accumulate_GBps > 0) || !(prof->compressed_fraction > 0))
         return ZIPCCL_ERR_INVALID;
     const double m = ranks - 1;
     const double shard = double(bytes) / ranks;
     const double rounds = std::ceil(m / link->links);
     const double native = rounds * (link->latency_us + shard / (link->bw_GBps * 1e3));
     const double zipped = m * shard / (prof->compress_GBps * 1e3) +
-                          rounds * (link->latency_us + prof->ratio * shard / (link->bw_GBps * 1e3)) +
+                          rounds * (link->latency_us + prof->compressed_fraction * shard / (link->bw_GBps * 1e3)) +
                           m * shard / (prof->accumulate_GBps * 1e3);
-    const bool raw = bytes < (1ull << 20) || prof->ratio >= 1.0;
+    const bool raw = bytes < (1ull << 20) || prof->compressed_fraction >= 1.0;
     if (use_codec) *use_codec = (!raw && zipped < native) ? 1 : 0;
     if (native_us) *native_us = native;
     if (zipped_us) *zipped_us = zipped;

@@ -43,7 +43,7 @@ class GatherSegmentT(ctypes.Structure):
 
 class CodecProfileT(ctypes.Structure):
     _fields_ = [("compress_GBps", ctypes.c_double), ("accumulate_GBps", ctypes.c_double),
-                ("ratio", ctypes.c_double)]
+                ("compressed_fraction", ctypes.c_double)]
 
 
 class LinkT(ctypes.Structure):

@@ -9,6 +9,9 @@ Parity status of each function (how it is pinned, in tests/test_oracle_pins.py):
   plan_sigma            pinned: brute-force BF16 histogram of seeded Gaussian samples,
                         analytic coverage above 97 %, scale invariance sigma -> 2 sigma.
   plan_table            pinned: validation rules, ascending order.
+  sample_sigma          pinned: a hand-computed sample (stride, Inf/NaN skipped, short
+                        last tile), numpy fp64 root mean square of the same sample,
+                        empty / all-NaN / all-zero segments give 1.
   compress / batch      pinned: hand-derived worked example (tests/golden), exhaustive
                         65 536-pattern round trip, size = 11 bits/value + escapes +
                         metadata, escape count = brute-force count, planted mistakes.
@@ -53,6 +56,8 @@ def load(path: str = _LIB_PATH, src: str = _SRC) -> ctypes.CDLL:
     lib.zo_binade_mass.argtypes = [ctypes.c_int, ctypes.c_double]
     lib.zo_plan_sigma.restype = ctypes.c_int
     lib.zo_plan_sigma.argtypes = [ctypes.c_double, _c_u8p]
+    lib.zo_sample_sigma.restype = ctypes.c_double
+    lib.zo_sample_sigma.argtypes = [_c_u16p, ctypes.c_uint64, ctypes.c_uint64]
     lib.zo_plan_table.restype = ctypes.c_int
     lib.zo_plan_table.argtypes = [_c_u8p, _c_u8p]
     lib.zo_compress.restype = ctypes.c_int
@@ -127,6 +132,13 @@ def plan_sigma(sigma: float) -> np.ndarray:
     if rc:
         raise OracleError(rc, "plan_sigma")
     return t
+
+
+def sample_sigma(x, stride: int) -> float:
+    """sigma of the finite values among tiles 0, stride, 2*stride, ... of 512 values."""
+    x = _as_u16(x).ravel()
+    buf = x if x.size else np.zeros(1, np.uint16)
+    return float(lib().zo_sample_sigma(_u16(buf), x.size, stride))
 
 
 def plan_table(table) -> np.ndarray:

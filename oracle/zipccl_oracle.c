@@ -132,6 +132,34 @@ int zo_plan_sigma(double sigma, uint8_t table_out[7])
     return ZO_OK;
 }
 
+/* sigma of a tensor whose sigma the caller does not know.  S2.A models the values as
+ * N(0, sigma^2) and takes sigma from the layer's weights; with no weights at hand the
+ * plainest estimate under that model (mean 0) is the root mean square of the values.
+ * It is taken over a sample: the tiles of 512 values with index 0, stride, 2*stride,
+ * ... (the last may be short), skipping Inf and NaN, summed one value after another in
+ * index order in fp64.  With no finite value, or a mean square of 0, sigma is 1. */
+double zo_sample_sigma(const uint16_t* x, uint64_t n, uint64_t stride)
+{
+    double sum = 0.0;
+    uint64_t count = 0;
+    if (stride == 0) stride = 1;
+    for (uint64_t t = 0; t * ZO_TILE < n; t += stride) {
+        for (uint64_t i = t * ZO_TILE; i < n && i < (t + 1) * ZO_TILE; i++) {
+            uint32_t u = (uint32_t)x[i] << 16;
+            float f;
+            memcpy(&f, &u, 4);
+            if (isinf(f) || isnan(f)) continue;
+            double d = (double)f;
+            sum += d * d;
+            count++;
+        }
+    }
+    if (count == 0) return 1.0;
+    double s = sqrt(sum / (double)count);
+    if (!(s > 0.0) || isinf(s)) return 1.0;
+    return s;
+}
+
 /* A caller-given table: exactly 7 distinct values in 1..254. */
 int zo_plan_table(const uint8_t in[7], uint8_t table_out[7])
 {

@@ -230,7 +230,7 @@ def test_argument_errors_before_any_launch(Z):
     assert L.zipccl_pipeline_create(7, 1000, fake, 1 << 30, None, None, ctypes.byref(h)) == Z.ERR_INVALID
     assert L.zipccl_pipeline_create(7, 4096, fake + 16, 1 << 30, None, None, ctypes.byref(h)) == Z.ERR_ALIGN
     assert L.zipccl_pipeline_create(7, 4096, fake, 16, None, None, ctypes.byref(h)) == Z.ERR_SIZE
-    assert L.zipccl_strerror(Z.ERR_CORRUPT) == b"corrupt compressed data"
+    assert L.zipccl_strerror(Z.ERR_CORRUPT) == b"corrupt data or a device status bit set"
 
 
 def test_rs_switcher_cost_model(Z):

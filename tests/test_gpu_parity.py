@@ -31,7 +31,7 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def gpu_compress(Z, segs, plans, esc_cap=None, workspace=None, poison=True):
+def gpu_compress(Z, segs, plans, esc_cap=None, workspace=None, poison=True, with_status=True):
     tens = [dev_bf16(s) for s in segs]
     sizes = [s.size for s in segs]
     total_static = sum(Z.static_size(n) for n in sizes)
@@ -42,7 +42,7 @@ def gpu_compress(Z, segs, plans, esc_cap=None, workspace=None, poison=True):
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     if workspace is None:
         workspace = torch.zeros(Z.workspace_size(sum(sizes), len(segs)), dtype=torch.uint8, device="cuda")
-    Z.compress(list(zip(tens, plans)), static, esc, workspace, n_esc, status, esc_cap=cap)
+    Z.compress(list(zip(tens, plans)), static, esc, workspace, n_esc, status if with_status else None, esc_cap=cap)
     torch.cuda.synchronize()
     ne = n_esc.cpu().numpy()
     return dict(static=static, esc=esc, n_esc=ne, status=int(status.item()), sizes=sizes,
@@ -592,21 +592,9 @@ def test_profile_codec(Z):
     prof = Z.profile_codec(dev_bf16(x), pl, P)
     assert prof.compress_GBps > 50 and prof.accumulate_GBps > 50
     st, esc, k = O.compress(x, np.array(pl.exponents, np.uint8))
-    assert abs(prof.ratio - (st.size + k) / (2 * n)) < 1e-12
+    assert abs(prof.compressed_fraction - (st.size + k) / (2 * n)) < 1e-12
     use, tn, tz = Z.rs_choose(prof, Z.LinkT(25.0, 5.0, 1), 8, 1 << 30)
     assert tn > 0 and tz > 0
-
-
-def sample_sigma(x, stride):
-    """sigma of the finite values among every stride-th tile of 512 (fp64, numpy)."""
-    n = x.size
-    starts = np.arange(0, n, 512 * stride, dtype=np.int64)
-    idx = (starts[:, None] + np.arange(512)).ravel()
-    idx = idx[idx < n]
-    f = (x[idx].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    f = f[np.isfinite(f)]
-    s = float(np.sqrt((f * f).sum() / f.size)) if f.size else 1.0
-    return s if s > 0 and np.isfinite(s) else 1.0
 
 
 def test_estimate_plans_64_segments(Z):
@@ -628,7 +616,7 @@ def test_estimate_plans_64_segments(Z):
     raw = plans_dev.cpu().numpy().tobytes()
     for k, x in enumerate(segs):
         got = Z.PlanT.from_buffer_copy(raw[8 * k:8 * k + 8])
-        s = sample_sigma(x, 3)
+        s = O.sample_sigma(x, 3)
         if abs(math.log2(s) - math.floor(math.log2(s)) - 0.7195805543641254) < 1e-9:
             continue                                      # at the switch: either window
         assert list(got.exponents) == [int(v) for v in O.plan_sigma(s)], (k, x.size, s)
@@ -656,7 +644,7 @@ def test_estimate_plans_and_compress_with_them(Z, stride):
     assert again.cpu().numpy().tobytes() == raw
     got = [Z.PlanT.from_buffer_copy(raw[8 * k:8 * k + 8]) for k in range(len(segs))]
     for k, x in enumerate(segs):
-        s = sample_sigma(x, stride)
+        s = O.sample_sigma(x, stride)
         phase = math.log2(s) - math.floor(math.log2(s))
         if abs(phase - 0.7195805543641254) < 1e-9:
             continue                                      # at the switch: either window
@@ -951,3 +939,23 @@ def test_single_launch_wait_limit_is_reported(Z, monkeypatch):
     monkeypatch.delenv("ZIPCCL_TEST_WAIT_LIMIT")
     r = gpu_compress(Z, x, p, workspace=ws)
     check_against_oracle(Z, x, p, r)
+
+
+def test_wait_limit_hook_without_status_word(Z, monkeypatch):
+    # without a status word a compress takes the two-launch path, in which no workgroup
+    # waits for another: the forced wait limit has nothing to act on, and the output is
+    # exact (a time-out could otherwise leave headers unwritten with nobody told)
+    x = [W.gaussian_bf16(300000, 0.02, 3), W.gaussian_bf16(70001, 1e-3, 4)]
+    p = [Z.plan(sigma=0.02), Z.plan(sigma=1e-3)]
+    ws = torch.zeros(Z.workspace_size(sum(s.size for s in x), len(x)), dtype=torch.uint8, device="cuda")
+    monkeypatch.setenv("ZIPCCL_TEST_WAIT_LIMIT", "1")
+    r = gpu_compress(Z, x, p, workspace=ws, with_status=False)
+    check_against_oracle(Z, x, p, r)
+    outs, status = gpu_decompress(Z, r)
+    assert status == 0
+    for a, b in zip(x, outs):
+        assert np.array_equal(a, b)
+    # with a status word the same hook makes the single launch's placers give up, and
+    # the status word says so
+    r = gpu_compress(Z, x, p, workspace=ws)
+    assert r["status"] & Z.STATUS_WAIT_LIMIT

@@ -265,6 +265,43 @@ def test_binade_masses_sum_to_one():
         assert abs(tot - 1.0) < 1e-12
 
 
+def test_sample_sigma_hand_computed():
+    # 1030 values, every 2nd tile of 512: tile 0 (512 x 0.5), tile 2 (the short last
+    # tile: 2, -2, +Inf, NaN, 0, 1); tile 1 (2^32 each) is not sampled.  Finite samples:
+    # 512 x 0.25 + 4 + 4 + 0 + 1 = 137 over 516 values.
+    x = np.zeros(1030, np.uint16)
+    x[:512] = 0x3F00
+    x[512:1024] = 0x4F80
+    x[1024:] = [0x4000, 0xC000, 0x7F80, 0x7FC0, 0x0000, 0x3F80]
+    assert O.sample_sigma(x, 2) == math.sqrt(137.0 / 516.0)
+    # every tile: the 2^32 values dominate
+    assert O.sample_sigma(x, 1) == math.sqrt((128.0 + 512 * 2.0 ** 64 + 9.0) / 1028.0)
+    # a stride past the end samples tile 0 only
+    assert O.sample_sigma(x, 5) == 0.5
+
+
+def test_sample_sigma_matches_numpy_rms():
+    for n, sigma, stride, seed in [(100001, 0.02, 3, 1), (4096 * 9 + 7, 3.0, 7, 2), (512, 1e-3, 1, 3)]:
+        x = W.gaussian_bf16(n, sigma, seed)
+        x[::101] = 0xFF80                               # -Inf, skipped
+        starts = np.arange(0, n, 512 * stride, dtype=np.int64)
+        idx = (starts[:, None] + np.arange(512)).ravel()
+        idx = idx[idx < n]
+        f = (x[idx].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        f = f[np.isfinite(f)]
+        want = float(np.sqrt(np.dot(f, f) / f.size))
+        assert abs(O.sample_sigma(x, stride) - want) <= 1e-12 * want
+        assert 0.8 * sigma < want < 1.25 * sigma
+
+
+def test_sample_sigma_degenerate_segments():
+    assert O.sample_sigma(np.zeros(0, np.uint16), 1) == 1.0            # empty
+    assert O.sample_sigma(np.full(700, 0x7FC1, np.uint16), 1) == 1.0   # no finite value
+    assert O.sample_sigma(np.zeros(700, np.uint16), 3) == 1.0          # mean square 0
+    tiny = np.array([0x0001], np.uint16)                               # one subnormal
+    assert O.sample_sigma(tiny, 1) == 2.0 ** -133
+
+
 def test_plan_table_validation():
     assert list(O.plan_table([9, 3, 7, 5, 1, 2, 200])) == [1, 2, 3, 5, 7, 9, 200]
     for bad in ([0, 1, 2, 3, 4, 5, 6], [1, 2, 3, 4, 5, 6, 255], [1, 1, 2, 3, 4, 5, 6]):

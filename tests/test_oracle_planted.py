@@ -28,6 +28,9 @@ MUTANTS = {
                             "return (uint16_t)(hi >> 16);"),
     "peer_dropped": ("for (int p = 0; p < npeers; p++) acc = acc + bf16_to_f32(d[p][i]);",
                      "for (int p = 1; p < npeers; p++) acc = acc + bf16_to_f32(d[p][i]);"),
+    "sigma_sample_keeps_inf": ("if (isinf(f) || isnan(f)) continue;", "if (isnan(f)) continue;"),
+    "sigma_sample_ignores_stride": ("for (uint64_t t = 0; t * ZO_TILE < n; t += stride) {",
+                                    "for (uint64_t t = 0; t * ZO_TILE < n; t += 1) {"),
     "escape_not_stored": ("if (esc_offset + count < esc_cap) esc[esc_offset + count] = (uint8_t)e;",
                           "if (esc_offset + count < esc_cap) esc[esc_offset + count] = (uint8_t)(e ^ 1);"),
 }
@@ -41,6 +44,7 @@ PINS = [
     P.test_accumulate_special_values,
     P.test_decompress_accumulate_matches_torch_cpu,
     P.test_round_to_bf16_matches_torch_on_random_floats,
+    P.test_sample_sigma_hand_computed,
 ]
 
 
