@@ -146,6 +146,23 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
                               void* esc_out, uint64_t esc_cap, void* workspace, uint64_t workspace_bytes,
                               uint64_t* n_esc_out, uint32_t* status, void* stream);
 
+/* zipccl_compress for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same outputs,
+ * launches and errors, with the workspace taken from a static device array inside the
+ * library (ZIPCCL_NOALLOC_SCRATCH_BYTES = 68 474 112 bytes, held by each GPU the library
+ * runs on until the process ends) instead of a caller buffer.  The call allocates nothing;
+ * its first call on a device looks the array's address up.  At most
+ * ZIPCCL_NOALLOC_MAX_VALUES values in total per call; more returns ZIPCCL_ERR_SIZE before
+ * anything is enqueued.  Every call on one GPU uses the same array: calls on one GPU that
+ * can overlap (on different streams, or from different host threads) race and must be
+ * ordered by the caller.  The array keeps what the last call left; no call depends on it.
+ * Errors: as zipccl_compress (INVALID, ALIGN, SIZE, HIP). */
+#define ZIPCCL_NOALLOC_MAX_VALUES (1ull << 26)
+#define ZIPCCL_NOALLOC_SCRATCH_BYTES 68474112ull
+zipccl_status zipccl_compress_noalloc(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
+                                      void* esc_out, uint64_t esc_cap, uint64_t* n_esc_out, uint32_t* status,
+                                      void* stream);
+
 /* Device scratch bytes zipccl_estimate_plans needs for nseg segments (16 partial sums of
  * 16 bytes per segment). */
 uint64_t zipccl_estimate_workspace_size(int nseg);

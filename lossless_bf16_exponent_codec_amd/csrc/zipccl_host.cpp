@@ -325,6 +325,30 @@ zipccl_status zipccl_compress(const zipccl_segment_t* segs, int nseg, void* stat
                              n_esc_out, status, stream);
 }
 
+static_assert(kNoAllocMaxValues == ZIPCCL_NOALLOC_MAX_VALUES && kNoAllocScratchBytes == ZIPCCL_NOALLOC_SCRATCH_BYTES,
+              "the header states the static workspace's limits");
+
+zipccl_status zipccl_compress_noalloc(const zipccl_segment_t* segs, int nseg, void* static_out, uint64_t static_cap,
+                                      void* esc_out, uint64_t esc_cap, uint64_t* n_esc_out, uint32_t* status,
+                                      void* stream)
+{
+    if (!segs || nseg < 1 || nseg > kMaxSegs || !static_out) return ZIPCCL_ERR_INVALID;
+    uint64_t total = 0;
+    for (int s = 0; s < nseg; s++) {
+        if (segs[s].n > kNoAllocMaxValues) return ZIPCCL_ERR_SIZE;
+        total += segs[s].n;
+    }
+    if (total > kNoAllocMaxValues) return ZIPCCL_ERR_SIZE;   // beyond the static workspace
+    if (!aligned(static_out, 128) || (n_esc_out && !aligned(n_esc_out, 8)) || (status && !aligned(status, 4)))
+        return ZIPCCL_ERR_ALIGN;
+    CArgs a;
+    if (zipccl_status r = fill_segments(a, segs, nseg)) return r;
+    void* ws = nullptr;   // the library's static device array on the stream's device
+    if (hipError_t e = noalloc_workspace(static_cast<hipStream_t>(stream), &ws)) return hip_status(e);
+    return compress_segments(a, nseg, static_out, static_cap, esc_out, esc_cap, ws, kNoAllocScratchBytes, n_esc_out,
+                             status, stream);
+}
+
 uint64_t zipccl_estimate_workspace_size(int nseg)
 {
     if (nseg < 1) nseg = 1;

@@ -27,15 +27,25 @@ constexpr uint32_t kEncThreads = 64 * kEncWaves;
 // unit, a u64 ready word per unit (the single-launch compress: the call's tag above
 // the unit's escape count), then kUnit staging bytes per unit that hold its escape
 // exponents, contiguous in value order, until their positions are known.
-__host__ __device__ inline uint64_t ws_counts_bytes(uint64_t units) { return (32 * units + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_pos_bytes(uint64_t units) { return (4 * (8 * units + 1) + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_units_bytes(uint64_t units) { return (4 * (units + 1) + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_ready_bytes(uint64_t units) { return (8 * units + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t ws_bytes(uint64_t units)
+__host__ __device__ constexpr uint64_t ws_counts_bytes(uint64_t units) { return (32 * units + 255) & ~uint64_t(255); }
+__host__ __device__ constexpr uint64_t ws_pos_bytes(uint64_t units) { return (4 * (8 * units + 1) + 255) & ~uint64_t(255); }
+__host__ __device__ constexpr uint64_t ws_units_bytes(uint64_t units) { return (4 * (units + 1) + 255) & ~uint64_t(255); }
+__host__ __device__ constexpr uint64_t ws_ready_bytes(uint64_t units) { return (8 * units + 255) & ~uint64_t(255); }
+__host__ __device__ constexpr uint64_t ws_bytes(uint64_t units)
 {
     return ws_counts_bytes(units) + ws_pos_bytes(units) + ws_units_bytes(units) + ws_ready_bytes(units) +
            uint64_t(kHalf) * 8 * units;
 }
+
+// The no-allocation compress: its workspace is a static device array sized for calls of
+// up to kNoAllocMaxValues values in at most kMaxSegs segments (each segment adds at most
+// one partial unit).
+constexpr uint64_t kNoAllocMaxValues = 1ull << 26;
+constexpr uint64_t kNoAllocMaxUnits = kNoAllocMaxValues / kUnit + kMaxSegs;
+constexpr uint64_t kNoAllocScratchBytes = ws_bytes(kNoAllocMaxUnits);
+// Device address of this library's static compress workspace on the device that runs
+// `stream` (looked up once per device, with that device current).
+hipError_t noalloc_workspace(hipStream_t stream, void** out);
 
 // Ready word of a unit in the single-launch compress: the call's tag (48 bits, drawn
 // per call by the host, never 0) above the unit's escape count (at most kUnit).

@@ -45,6 +45,8 @@
 #include "zipccl_internal.h"
 #include "zipccl.h"
 
+#include <mutex>
+
 namespace zc {
 
 namespace {
@@ -1521,6 +1523,46 @@ hipError_t launch_compress(const CArgs& a, hipStream_t s, bool single)
             hipLaunchKernelGGL(place_kernel, dim3((a.total_blocks + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
     }
     return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------------
+// workspace of the no-allocation compress
+// --------------------------------------------------------------------------------
+// For callers that cannot allocate device memory: the compress workspace as a
+// file-scope device array.  Each GPU the library runs on holds its own copy from the time
+// the library's code is loaded on it until the process ends; every call on that GPU
+// shares it.  In host code `scratch` is only a handle for the runtime, not a device
+// address: the address that kernels are given comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_workspace(hipStream_t stream, void** out)
+{
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 // --------------------------------------------------------------------------------

@@ -80,6 +80,8 @@ def _load() -> ctypes.CDLL:
     lib.zipccl_workspace_size.argtypes = [u64, i32]
     lib.zipccl_compress.restype = i32
     lib.zipccl_compress.argtypes = [ctypes.POINTER(SegmentT), i32, vp, u64, vp, u64, vp, u64, vp, vp, vp]
+    lib.zipccl_compress_noalloc.restype = i32
+    lib.zipccl_compress_noalloc.argtypes = [ctypes.POINTER(SegmentT), i32, vp, u64, vp, u64, vp, vp, vp]
     lib.zipccl_compress_chunks.restype = i32
     lib.zipccl_compress_chunks.argtypes = [ctypes.POINTER(SegmentT), i32, i32, ctypes.POINTER(vp),
                                            ctypes.POINTER(u64), ctypes.POINTER(vp), ctypes.POINTER(u64), vp, u64,
@@ -206,6 +208,24 @@ def compress(segments, static_out, esc_out, workspace, n_esc_out=None, status=No
     rc = _lib.zipccl_compress(arr, nseg, _ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap,
                               _ptr(workspace), _nbytes(workspace), _ptr(n_esc_out), _ptr(status), _stream(stream))
     _check(rc, "zipccl_compress")
+
+
+NOALLOC_MAX_VALUES = 1 << 26
+
+
+def compress_noalloc(segments, static_out, esc_out, n_esc_out=None, status=None, stream=None,
+                     esc_cap: int | None = None):
+    """zipccl_compress_noalloc: zipccl_compress with the library's static device workspace."""
+    nseg = len(segments)
+    arr = (SegmentT * max(nseg, 1))()
+    for k, (t, p) in enumerate(segments):
+        arr[k].src = _ptr(t) if t.numel() else None
+        arr[k].n = t.numel()
+        arr[k].plan = p
+    cap = _nbytes(esc_out) if esc_cap is None else esc_cap
+    rc = _lib.zipccl_compress_noalloc(arr, nseg, _ptr(static_out), _nbytes(static_out), _ptr(esc_out), cap,
+                                      _ptr(n_esc_out), _ptr(status), _stream(stream))
+    _check(rc, "zipccl_compress_noalloc")
 
 
 class PreparedCompressChunks:

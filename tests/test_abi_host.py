@@ -262,3 +262,20 @@ def test_rs_switcher_cost_model(Z):
     assert Z.lib().zipccl_rs_choose(ctypes.byref(prof), ctypes.byref(Z.LinkT(0.0, 5.0, 1)), 8, 1 << 30, None, None,
                                     None) == Z.ERR_INVALID
     assert Z.lib().zipccl_profile_codec(None, 10, Z.plan(sigma=1.0), 1, None, 0, None, None) == Z.ERR_INVALID
+
+
+def test_compress_noalloc_rejects_sizes_past_its_static_workspace(Z):
+    # checked before anything touches a device: host addresses stand in for the buffers
+    buf = np.zeros(64, np.uint64)
+    addr = buf.ctypes.data + (-buf.ctypes.data % 256)
+    segs = (Z.SegmentT * 2)()
+    for k in range(2):
+        segs[k].src = addr
+        segs[k].plan = Z.plan(sigma=1.0)
+    segs[0].n, segs[1].n = Z.NOALLOC_MAX_VALUES, 1              # one value too many
+    rc = Z.lib().zipccl_compress_noalloc(segs, 2, addr, 1 << 40, addr, 1 << 40, None, None, None)
+    assert rc == Z.ERR_SIZE
+    segs[0].n = Z.NOALLOC_MAX_VALUES + 1
+    assert Z.lib().zipccl_compress_noalloc(segs, 1, addr, 1 << 40, addr, 1 << 40, None, None, None) == Z.ERR_SIZE
+    assert Z.lib().zipccl_compress_noalloc(segs, 0, addr, 1 << 40, addr, 1 << 40, None, None, None) == Z.ERR_INVALID
+    assert Z.lib().zipccl_compress_noalloc(segs, 65, addr, 1 << 40, addr, 1 << 40, None, None, None) == Z.ERR_INVALID
