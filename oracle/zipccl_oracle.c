@@ -44,6 +44,18 @@
  *   Escapes: the exponent bytes of the values with code 0, in increasing index
  *   order, written to a separate buffer starting at esc_offset.
  *
+ *   Uncoded blocks (the fallback to no compression where coding would not pay: the
+ *   CCCL page's adaptive strategy section and its advice to fall back when the ratio
+ *   reaches 1).  A tile of m values has m - 192 values (if positive) that do not fit its
+ *   192 plane bytes; summed over the tiles of a block this is the block's overflow O.  A
+ *   block with O > 0 whose coded form would put at least O exponents in the escape buffer
+ *   is stored uncoded instead: its A bytes as usual; the 192 plane bytes of each of its
+ *   tiles hold the exponents of the tile's first 192 values in index order (0 past the
+ *   tile's last value); the exponents of the rest of each tile's values go, tile after
+ *   tile in index order, to the escape buffer.  off[] counts the bytes each block puts
+ *   in the escape buffer, so an uncoded block has exactly O of them and a coded block
+ *   fewer: a decoder tells the two apart from off[] alone.
+ *
  *   code(e) = 1 + r when e equals table[r] (table sorted ascending, 7 distinct values
  *   in 1..254), otherwise 0.  Exponents 0 (zero, subnormal) and 255 (Inf, NaN) are
  *   never in a table, so they always escape.
@@ -206,29 +218,45 @@ int zo_compress(const uint16_t* x, uint64_t n, const uint8_t table_in[7], uint64
     uint8_t* C = B + round_up(192 * T, 128);
     memset(st, 0, sz);
 
-    uint64_t count = 0;
+    uint64_t count = 0;   /* bytes in the escape buffer so far */
     int overflow = 0;
-    for (uint64_t i = 0; i < n; i++) {
-        if (i % ZO_BLOCK == 0) put_u32(C + 4 * (i / ZO_BLOCK), (uint32_t)count);
-        uint16_t v = x[i];
-        unsigned s = sign_of(v), e = exponent_of(v), m = mantissa_of(v);
-        A[i] = (uint8_t)((s << 7) | m);
-        unsigned c = code_of(e, table);
-        uint64_t t = i / 512, l = (i % 512) / 8, j = i % 8;
-        for (unsigned p = 0; p < 3; p++) {
-            if ((c >> p) & 1u) {
-                uint64_t w = 24 * t + 8 * p + j;      /* word index */
-                uint64_t bit = w * 64 + l;            /* bit index in B */
-                B[bit / 8] |= (uint8_t)(1u << (bit % 8));
+    for (uint64_t b = 0; b < K; b++) {
+        uint64_t i0 = b * ZO_BLOCK, i1 = i0 + ZO_BLOCK < n ? i0 + ZO_BLOCK : n;
+        put_u32(C + 4 * b, (uint32_t)count);
+        /* the block's coded escapes and its overflow */
+        uint64_t escapes = 0, ovf = 0;
+        for (uint64_t i = i0; i < i1; i++) {
+            if (code_of(exponent_of(x[i]), table) == 0) escapes++;
+            if (i % 512 >= 192) ovf++;
+        }
+        int uncoded = ovf > 0 && escapes >= ovf;
+        for (uint64_t i = i0; i < i1; i++) {
+            uint16_t v = x[i];
+            unsigned s = sign_of(v), e = exponent_of(v), m = mantissa_of(v);
+            A[i] = (uint8_t)((s << 7) | m);
+            uint64_t t = i / 512, l = (i % 512) / 8, j = i % 8;
+            int to_esc;
+            if (uncoded) {
+                if (i % 512 < 192) B[192 * t + i % 512] = (uint8_t)e;   /* the tile's plane bytes */
+                to_esc = i % 512 >= 192;
+            } else {
+                unsigned c = code_of(e, table);
+                for (unsigned p = 0; p < 3; p++) {
+                    if ((c >> p) & 1u) {
+                        uint64_t w = 24 * t + 8 * p + j;      /* word index */
+                        uint64_t bit = w * 64 + l;            /* bit index in B */
+                        B[bit / 8] |= (uint8_t)(1u << (bit % 8));
+                    }
+                }
+                to_esc = c == 0;
+            }
+            if (to_esc) {
+                if (esc_offset + count < esc_cap) esc[esc_offset + count] = (uint8_t)e;
+                else overflow = 1;
+                count++;
             }
         }
-        if (c == 0) {
-            if (esc_offset + count < esc_cap) esc[esc_offset + count] = (uint8_t)e;
-            else overflow = 1;
-            count++;
-        }
     }
-    (void)K;
 
     put_u32(st + 0, ZO_MAGIC);
     put_u16(st + 4, 1);
@@ -291,33 +319,46 @@ int zo_decompress(const uint8_t* st, uint64_t st_bytes, const uint8_t* esc, uint
     const uint8_t* B = A + 512 * T;
     const uint8_t* C = B + round_up(192 * T, 128);
 
-    uint64_t in_block = 0;      /* escapes seen so far in the current 4096-block */
-    uint64_t used = 0;          /* escapes used so far in the whole segment */
-    for (uint64_t i = 0; i < n; i++) {
-        uint64_t b = i / ZO_BLOCK;
-        if (i % ZO_BLOCK == 0) {
-            in_block = 0;
-            if (get_u32(C + 4 * b) != used) return ZO_ERR_CORRUPT;
+    uint64_t K = zo_blocks(n);
+    uint64_t used = 0;          /* escape-buffer bytes used so far in the whole segment */
+    for (uint64_t b = 0; b < K; b++) {
+        uint64_t i0 = b * ZO_BLOCK, i1 = i0 + ZO_BLOCK < n ? i0 + ZO_BLOCK : n;
+        uint64_t first = get_u32(C + 4 * b);
+        uint64_t last = b + 1 < K ? get_u32(C + 4 * (b + 1)) : n_esc;
+        if (first != used || last < first) return ZO_ERR_CORRUPT;
+        uint64_t ovf = 0;
+        for (uint64_t i = i0; i < i1; i++)
+            if (i % 512 >= 192) ovf++;
+        int uncoded = ovf > 0 && last - first == ovf;
+        uint64_t in_block = 0;  /* escape-buffer bytes of this block used so far */
+        for (uint64_t i = i0; i < i1; i++) {
+            uint64_t t = i / 512, l = (i % 512) / 8, j = i % 8;
+            unsigned e;
+            int from_esc;
+            if (uncoded) {
+                from_esc = i % 512 >= 192;
+                e = from_esc ? 0u : B[192 * t + i % 512];
+            } else {
+                unsigned c = 0;
+                for (unsigned p = 0; p < 3; p++) {
+                    uint64_t bit = (24 * t + 8 * p + j) * 64 + l;
+                    c |= (unsigned)((B[bit / 8] >> (bit % 8)) & 1u) << p;
+                }
+                from_esc = c == 0;
+                e = from_esc ? 0u : table[c - 1];
+            }
+            if (from_esc) {
+                uint64_t k = first + in_block;
+                if (k >= last) return ZO_ERR_CORRUPT;
+                e = esc[esc_offset + k];
+                in_block++;
+                used++;
+            }
+            unsigned a = A[i];
+            unsigned s = (a >> 7) & 1u, m = a & 0x7Fu;
+            out[i] = (uint16_t)((s << 15) | (e << 7) | m);
         }
-        uint64_t t = i / 512, l = (i % 512) / 8, j = i % 8;
-        unsigned c = 0;
-        for (unsigned p = 0; p < 3; p++) {
-            uint64_t bit = (24 * t + 8 * p + j) * 64 + l;
-            c |= (unsigned)((B[bit / 8] >> (bit % 8)) & 1u) << p;
-        }
-        unsigned e;
-        if (c != 0) {
-            e = table[c - 1];
-        } else {
-            uint64_t k = get_u32(C + 4 * b) + in_block;
-            if (k >= n_esc) return ZO_ERR_CORRUPT;
-            e = esc[esc_offset + k];
-            in_block++;
-            used++;
-        }
-        unsigned a = A[i];
-        unsigned s = (a >> 7) & 1u, m = a & 0x7Fu;
-        out[i] = (uint16_t)((s << 15) | (e << 7) | m);
+        if (used != last) return ZO_ERR_CORRUPT;
     }
     if (used != n_esc) return ZO_ERR_CORRUPT;
     return ZO_OK;

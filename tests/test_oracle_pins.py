@@ -71,6 +71,27 @@ def test_worked_example_bytes():
 
 
 # ----------------------------------------------------------------------------------
+# what the escape buffer holds, by brute force over each 4096-value block: the
+# exponents of the values outside the table (coded block), or, when at least as many
+# values escape as the block has values past the first 192 of each tile, the exponents
+# of those values (uncoded block: the fallback to no compression of the CCCL page's
+# adaptive strategy section)
+# ----------------------------------------------------------------------------------
+def escape_stream(x, table):
+    e = (np.asarray(x).astype(np.int64) >> 7) & 0xFF
+    parts, uncoded = [], []
+    for b0 in range(0, e.size, 4096):
+        blk = e[b0:b0 + 4096]
+        outside = ~np.isin(blk, np.asarray(table, np.int64))
+        past192 = np.arange(blk.size) % 512 >= 192
+        unc = past192.sum() > 0 and outside.sum() >= past192.sum()
+        parts.append(blk[past192] if unc else blk[outside])
+        uncoded.append(bool(unc))
+    esc = np.concatenate(parts).astype(np.uint8) if parts else np.zeros(0, np.uint8)
+    return esc, uncoded
+
+
+# ----------------------------------------------------------------------------------
 # lossless: the round trip is the identity on every BF16 bit pattern
 # ----------------------------------------------------------------------------------
 ALL = np.arange(65536, dtype=np.uint32).astype(np.uint16)
@@ -85,16 +106,96 @@ def exhaustive_input():
     "sigma1", [1, 2, 3, 4, 5, 6, 7], [248, 249, 250, 251, 252, 253, 254], [3, 77, 120, 128, 129, 200, 254],
 ])
 def test_exhaustive_round_trip(table):
+    # 97 % of all patterns lie outside any table, so almost every block is uncoded here
     t = O.plan_sigma(1.0) if table == "sigma1" else O.plan_table(table)
     x = exhaustive_input()
     st, esc, k = O.compress(x, t)
-    # escape count == brute-force count of exponents outside the table
-    e = (x.astype(np.int64) >> 7) & 0xFF
-    assert k == int((~np.isin(e, t.astype(np.int64))).sum())
-    # escapes are exactly those exponents, in index order
-    assert np.array_equal(esc, e[~np.isin(e, t.astype(np.int64))].astype(np.uint8))
+    want, unc = escape_stream(x, t)
+    assert k == want.size and np.array_equal(esc, want)
+    assert sum(unc) >= len(unc) - 1
     y = O.decompress(st, esc, x.size)
     assert np.array_equal(y, x)
+
+
+def coded_exhaustive_input(t):
+    # every pattern at every column, each followed by two table values: at most a third
+    # of a block escapes, so every block is coded
+    x = exhaustive_input()
+    fill = (np.asarray(t, np.uint16)[np.arange(2 * x.size) % 7] << 7) | (np.arange(2 * x.size) % 256).astype(np.uint16)
+    out = np.empty(3 * x.size, np.uint16)
+    out[0::3], out[1::3], out[2::3] = x, fill[0::2], fill[1::2]
+    return out
+
+
+@pytest.mark.parametrize("table", ["sigma1", [3, 77, 120, 128, 129, 200, 254]])
+def test_exhaustive_round_trip_coded_blocks(table):
+    t = O.plan_sigma(1.0) if table == "sigma1" else O.plan_table(table)
+    x = coded_exhaustive_input(t)
+    st, esc, k = O.compress(x, t)
+    e = (x.astype(np.int64) >> 7) & 0xFF
+    outside = ~np.isin(e, t.astype(np.int64))
+    want, unc = escape_stream(x, t)
+    assert not any(unc)
+    assert k == int(outside.sum()) and np.array_equal(esc, e[outside].astype(np.uint8))
+    assert np.array_equal(want, esc)
+    assert np.array_equal(O.decompress(st, esc, x.size), x)
+
+
+def test_uncoded_block_by_hand():
+    # one block of 1024 values (2 tiles) with exponents 1, 2, ..., 200, 1, 2, ... and
+    # table 122..128: 987 of 1024 escape, at least the overflow 2 x 320 = 640, so the block
+    # is uncoded: each tile's 192 plane bytes hold the exponents of its values 0..191, the
+    # escape buffer those of values 192..511 of tile 0, then of tile 1
+    i = np.arange(1024)
+    ex = (i % 200) + 1
+    x = ((ex << 7) | (i % 128) | ((i % 3 == 0) << 15)).astype(np.uint16)
+    t = O.plan_sigma(1.0)
+    assert list(t) == list(range(122, 129))
+    st, esc, k = O.compress(x, t)
+    assert k == 640
+    assert np.array_equal(esc, np.concatenate([ex[192:512], ex[704:1024]]).astype(np.uint8))
+    B = st[128 + 1024:128 + 1024 + 384]
+    assert np.array_equal(B[:192], ex[:192].astype(np.uint8))
+    assert np.array_equal(B[192:], ex[512:704].astype(np.uint8))
+    A = st[128:128 + 1024]
+    assert np.array_equal(A, ((x >> 8) & 0x80 | (x & 0x7F)).astype(np.uint8))
+    C = st[128 + 1024 + 384:].view(np.uint32)
+    assert int(C[0]) == 0 and not C[1:].any()
+    assert int(st[32:40].view(np.uint64)[0]) == 640
+    assert np.array_equal(O.decompress(st, esc, 1024), x)
+
+
+def test_uncoded_threshold_is_the_overflow():
+    # a full block overflows 8 x 320 = 2560 values: 2560 escapes make it uncoded (2560
+    # escape-buffer bytes: the exponents past each tile's first 192 values), 2559 keep it
+    # coded (the 2559 escapes themselves)
+    t = O.plan_sigma(1.0)
+    rng = np.random.default_rng(5)
+    for n_out, uncoded in [(2560, True), (2559, False), (4096, True), (0, False)]:
+        e = np.full(4096, 125, np.int64)
+        pos = rng.permutation(4096)[:n_out]
+        e[pos] = rng.choice([0, 5, 121, 129, 255], n_out)
+        x = ((e << 7) | rng.integers(0, 128, 4096) | (rng.integers(0, 2, 4096) << 15)).astype(np.uint16)
+        st, esc, k = O.compress(x, t)
+        if uncoded:
+            assert k == 2560
+            assert np.array_equal(esc, e[np.arange(4096) % 512 >= 192].astype(np.uint8))
+            assert np.array_equal(st[128 + 4096:128 + 4096 + 1536],
+                                  e.reshape(8, 512)[:, :192].ravel().astype(np.uint8))
+        else:
+            assert k == n_out and np.array_equal(esc, e[np.sort(pos)].astype(np.uint8))
+        assert np.array_equal(O.decompress(st, esc, 4096), x)
+
+
+def test_random_bits_do_not_expand():
+    # random bits under a Gaussian table escape about 97 % of the time: every full block
+    # is uncoded, so the compressed size is 2n plus the header and the offset table
+    for n in [4096 * 5, 4096 * 64, 4096 * 64 + 1000]:
+        x = np.random.default_rng(n).integers(0, 65536, n, dtype=np.uint32).astype(np.uint16)
+        st, esc, k = O.compress(x, O.plan_sigma(0.02))
+        K = -(-n // 4096)
+        assert st.size + k <= 2 * n + 128 + 128 * (-(-4 * K // 128)) + 512
+        assert np.array_equal(O.decompress(st, esc, n), x)
 
 
 @pytest.mark.parametrize("n", [0, 1, 7, 8, 63, 64, 511, 512, 513, 4095, 4096, 4097, 16383, 16384, 16385, 70001])
@@ -104,8 +205,8 @@ def test_sizes_and_edges(n):
     t = O.plan_sigma(0.02)
     st, esc, k = O.compress(x, t)
     assert st.size == O.static_size(n)
-    e = (x.astype(np.int64) >> 7) & 0xFF
-    assert k == int((~np.isin(e, t.astype(np.int64))).sum())
+    want, _ = escape_stream(x, t)
+    assert k == want.size and np.array_equal(esc, want)
     assert np.array_equal(O.decompress(st, esc, n), x)
 
 
@@ -116,16 +217,15 @@ from hypothesis import given, settings, strategies as st_
 @given(n=st_.integers(0, 20000), seed=st_.integers(0, 2**32 - 1),
        table=st_.sets(st_.integers(1, 254), min_size=7, max_size=7))
 def test_round_trip_random_bits_and_tables(n, seed, table):
-    # any bit patterns and any 7-exponent table: decode(encode(x)) == x, the escape count
-    # is the brute-force count of exponents outside the table, and the size is the
-    # static part plus one byte per escape
+    # any bit patterns and any 7-exponent table: decode(encode(x)) == x, the escape
+    # bytes are the brute-force stream (coded or uncoded block by block), and the size is
+    # the static part plus one byte per escape-buffer byte
     x = np.random.default_rng(seed).integers(0, 65536, n, dtype=np.uint32).astype(np.uint16)
     t = O.plan_table(sorted(table))
     st, esc, k = O.compress(x, t)
-    e = (x.astype(np.int64) >> 7) & 0xFF
-    outside = ~np.isin(e, np.array(sorted(table), np.int64))
-    assert k == int(outside.sum()) and esc.size == k
-    assert np.array_equal(esc, e[outside].astype(np.uint8))
+    want, _ = escape_stream(x, t)
+    assert k == want.size and esc.size == k
+    assert np.array_equal(esc, want)
     assert st.size == O.static_size(n)
     assert np.array_equal(O.decompress(st, esc, n), x)
 
@@ -153,7 +253,9 @@ def test_all_in_table_and_disjoint_table():
     assert np.array_equal(O.decompress(st, esc, x.size), x)
     t2 = O.plan_table([1, 2, 3, 4, 5, 6, 7])
     st, esc, k = O.compress(x, t2)
-    assert k == x.size
+    # 4200 values, all outside: block 0 is uncoded (2560 escape-buffer bytes), block 1
+    # (104 values, no overflow) keeps its 104 escapes
+    assert k == 2560 + 104
     assert np.array_equal(O.decompress(st, esc, x.size), x)
 
 
@@ -182,7 +284,9 @@ def test_batch_layout_is_concatenation_of_segments():
 def test_escape_overflow_is_reported():
     x = W.gaussian_bf16(10000, 1.0, 5)
     _, _, ne, rc = O.compress_batch([x], [O.plan_table([1, 2, 3, 4, 5, 6, 7])], esc_cap=100)
-    assert rc == O.ERR_OVERFLOW and ne[0] == 10000
+    # every value escapes: blocks 0 and 1 are uncoded (2560 each), block 2 (1808 values,
+    # 3 full tiles and one of 272) overflows 3 x 320 + 80 and is uncoded too
+    assert rc == O.ERR_OVERFLOW and ne[0] == 2 * 2560 + 1040
 
 
 # ----------------------------------------------------------------------------------

@@ -19,8 +19,8 @@ MUTANTS = {
     "plane_lane_bit": ("uint64_t bit = w * 64 + l;", "uint64_t bit = w * 64 + (63 - l);"),
     "descending_rank": ("if (table[r] == e) return (unsigned)(r + 1);",
                         "if (table[r] == e) return (unsigned)(7 - r);"),
-    "offset_after_block": ("if (i % ZO_BLOCK == 0) put_u32(C + 4 * (i / ZO_BLOCK), (uint32_t)count);",
-                           "if (i % ZO_BLOCK == 1) put_u32(C + 4 * (i / ZO_BLOCK), (uint32_t)count);"),
+    "offset_off_by_one": ("put_u32(C + 4 * b, (uint32_t)count);",
+                          "put_u32(C + 4 * b, (uint32_t)(count + (b > 0)));"),
     "binade_edge_off_by_one": ("double lo = ldexp(1.0, e - 127), hi = ldexp(1.0, e - 126);",
                                "double lo = ldexp(1.0, e - 126), hi = ldexp(1.0, e - 125);"),
     "sigma_as_variance": ("double s = sigma * sqrt(2.0);", "double s = sqrt(sigma) * sqrt(2.0);"),
@@ -28,6 +28,9 @@ MUTANTS = {
                             "return (uint16_t)(hi >> 16);"),
     "peer_dropped": ("for (int p = 0; p < npeers; p++) acc = acc + bf16_to_f32(d[p][i]);",
                      "for (int p = 1; p < npeers; p++) acc = acc + bf16_to_f32(d[p][i]);"),
+    "uncoded_threshold_strict": ("int uncoded = ovf > 0 && escapes >= ovf;", "int uncoded = ovf > 0 && escapes > ovf;"),
+    "uncoded_plane_bytes_191": ("if (i % 512 < 192) B[192 * t + i % 512] = (uint8_t)e;",
+                                "if (i % 512 < 191) B[192 * t + i % 512] = (uint8_t)e;"),
     "sigma_sample_keeps_inf": ("if (isinf(f) || isnan(f)) continue;", "if (isnan(f)) continue;"),
     "sigma_sample_ignores_stride": ("for (uint64_t t = 0; t * ZO_TILE < n; t += stride) {",
                                     "for (uint64_t t = 0; t * ZO_TILE < n; t += 1) {"),
@@ -45,6 +48,8 @@ PINS = [
     P.test_decompress_accumulate_matches_torch_cpu,
     P.test_round_to_bf16_matches_torch_on_random_floats,
     P.test_sample_sigma_hand_computed,
+    P.test_uncoded_threshold_is_the_overflow,
+    P.test_uncoded_block_by_hand,
 ]
 
 
