@@ -21,11 +21,20 @@
  *   A         512*T bytes: A[i] = sign << 7 | 7-bit mantissa of value i (0 past n)
  *   B         R128(192*T) bytes: u64 plane word 24*t + 8*p + j holds, in bit l,
  *             bit p of the code of value 512*t + 8*l + j (0 past n)
- *   C         R128(4*K) bytes: u32 off[b] = escapes among values [0, 4096*b)
+ *   C         R128(4*K) bytes: u32 off[b] = escape-buffer bytes of blocks 0..b-1
  *   static_bytes = 128 + 512*T + R128(192*T) + R128(4*K)
  * Escapes: one exponent byte per code-0 value, in index order, stored in a separate
  * escape buffer from byte esc_offset on.  code(e) = 1 + rank of e in the ascending
  * table, 0 if e is not in it; exponents 0 and 255 are never in a table.
+ * Uncoded blocks, the fallback to no compression (CCCL page: adaptive compression
+ * strategy; fall back when the ratio reaches 1): a tile of m values overflows
+ * max(0, m - 192) values (those past the 192 its plane bytes can hold), a block the sum
+ * over its tiles (2560 for 4096 values).  A block with overflow O > 0 whose code-0 values
+ * number at least O is stored uncoded: A as usual; the 192 plane bytes of each tile hold
+ * the exponents of its first 192 values (0 past the tile's end); the exponents of its
+ * other values go to the escape buffer, tile after tile.  off[] and n_esc count escape-
+ * buffer bytes, so an uncoded block has exactly O of them and a coded block fewer.
+ * Random bits thus take 2n bytes plus header and offsets instead of about 2.38n.
  *
  * Conventions.
  *   - All data pointers are device pointers unless stated.  The caller owns every
@@ -108,7 +117,9 @@ zipccl_status zipccl_plan_many(const double* sigma, int n, zipccl_plan_t* out);
 uint64_t zipccl_static_size(uint64_t n);
 
 /* static_size(n) + n_esc: the whole compressed size of one segment (S2.B: 11 bits per
- * value plus 8 bits per escape plus metadata).  n_esc = n gives the worst case. */
+ * value plus 8 bits per escape-buffer byte plus metadata).  The escape-buffer bytes of a
+ * segment never exceed its values (n_esc = n is a safe capacity); with uncoded blocks
+ * they are at most 5n/8 + 192. */
 uint64_t zipccl_compressed_size(uint64_t n, uint64_t n_esc);
 
 /* Device workspace bytes needed by zipccl_compress for up to nseg segments holding

@@ -15,6 +15,12 @@ constexpr uint32_t kUnit = kBlock * kWaves;   // values per workgroup: one block
 constexpr int kMaxSegs = 64;
 constexpr int kMaxPeers = 16;
 
+// Uncoded blocks: the plane bytes of a tile (3 planes x 8 columns x 64 bits) hold the
+// exponents of its first 192 values; the rest of the tile's exponents go to the escape
+// buffer.
+constexpr uint32_t kUncodedPlaneBytes = 192;
+constexpr uint32_t kBlockOverflow = (kBlock / kTile) * (kTile - kUncodedPlaneBytes);   // of a full block: 2560
+
 // Encode granule: half a block (4 tiles, 2048 values) per wave, 8 waves per workgroup.
 constexpr uint32_t kHalf = kBlock / 2;
 constexpr uint32_t kEncWaves = 8;

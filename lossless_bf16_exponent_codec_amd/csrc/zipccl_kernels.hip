@@ -379,6 +379,85 @@ __device__ inline void stage_tile_escapes(const TileEsc& te, uint32_t r, uint8_t
     for (uint32_t m = te.m; m; m &= m - 1) s_esc[r++] = uint8_t(perm(te.e1, te.e0, __builtin_ctz(m) >> 2));
 }
 
+// The 16-byte loads of this lane's values in half block hb (all 2048 values exist):
+// addresses first (a gathered segment reads its row indices with scalar loads), then the
+// 4 loads in straight-line code.
+__device__ inline void load_full_half(const CSeg& sg, uint32_t hb, uint32_t lane, uint4 (&v)[4], bool& bad_row)
+{
+    const uint16_t* src[4];
+    if (sg.rows == nullptr) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) src[k] = sg.src + uint64_t(hb) * kHalf + k * kTile + 8 * lane;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; k++) src[k] = gathered_lane_ptr(sg, hb * kHalf + k * kTile, lane, bad_row);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = load_nt(reinterpret_cast<const uint4*>(src[k]));
+}
+
+// The same for the segment's last, partial half block (values past n read as 0).
+__device__ inline void load_partial_half(const CSeg& sg, uint32_t hb, uint32_t lane, uint4 (&v)[4], bool& bad_row)
+{
+    if (sg.rows == nullptr) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, hb * 4 + k, lane, sg.n);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; k++) v[k] = load_lane_rows(sg, hb * 4 + k, lane, bad_row);
+    }
+}
+
+// Values of a segment of n values that lie past the first 192 of their tile, among the
+// m values from the start of a tile on (every tile full but the last): what a stretch
+// of an uncoded block puts in the escape buffer.  32-bit scalar arithmetic, no branch.
+__device__ inline uint32_t overflow_of(uint32_t m)
+{
+    return (m / kTile) * (kTile - kUncodedPlaneBytes) + max(m % kTile, kUncodedPlaneBytes) - kUncodedPlaneBytes;
+}
+
+// The same for half block hb of the segment (0 past the segment).
+__device__ inline uint32_t half_overflow(uint32_t n, uint32_t hb)
+{
+    const uint32_t full = n / kHalf;   // half blocks with all their values
+    const uint32_t m = hb < full ? kHalf : (hb == full ? n % kHalf : 0u);
+    return overflow_of(m);
+}
+
+// Half block hb of an uncoded block (v: this lane's values of its 4 tiles): the
+// exponents of each tile's values 0..191 replace the tile's 192 plane bytes (lanes
+// 0..23, 8 bytes each; 0 past n), and those of values 192.. are staged in s_esc tile
+// after tile, in value order, in place of the coded escapes.  The plane dwords this
+// wave stored before are overwritten, so it first waits for them to complete.
+__device__ inline void store_uncoded_half(const CSeg& sg, uint32_t hb, uint32_t lane, const uint4 (&v)[4],
+                                          uint8_t* s_esc)
+{
+    const uint32_t n = sg.n;
+    const uint32_t T = uint32_t(tiles_of(n));
+    uint8_t* B = sg.dst + planes_off(n);
+    wait_vm();
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t t = hb * 4 + k;
+        if (t >= T) break;
+        const uint64_t i = uint64_t(t) * kTile + 8ull * lane;
+        const uint32_t nvalid = i >= n ? 0u : uint32_t(min<uint64_t>(8, n - i));
+        const uint32_t d[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) e[j] = uint32_t(j) < nvalid ? (d[j >> 1] >> (7 + 16 * (j & 1))) & 0xFFu : 0u;
+        if (8 * lane < kUncodedPlaneBytes) {
+            const uint2 w = make_uint2(e[0] | e[1] << 8 | e[2] << 16 | e[3] << 24, e[4] | e[5] << 8 | e[6] << 16 | e[7] << 24);
+            *reinterpret_cast<uint2*>(B + 192ull * t + 8 * lane) = w;
+        } else {
+            // earlier tiles of the half are full: each put kTile - 192 bytes before this one
+            uint8_t* q = s_esc + k * (kTile - kUncodedPlaneBytes) + (8 * lane - kUncodedPlaneBytes);
+            for (uint32_t j = 0; j < nvalid; j++) q[j] = uint8_t(e[j]);
+        }
+    }
+    wave_lds_sync();
+}
+
 // Encodes half block hb of a segment (tiles 4hb .. 4hb+3, those that exist): A bytes,
 // planes, the escape count (to workspace slot gh) and the escape exponents in value
 // order in s_esc; zero padding after the segment's last half block.
@@ -475,20 +554,7 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
     const bool full = active && uint64_t(hb + 1) * kHalf <= n;
     bool bad_row = false;   // a gathered row index outside the matrix
     uint4 v[4];
-    if (full) {
-        // addresses first (a gathered segment reads its row indices with scalar loads),
-        // then the 4 loads in straight-line code
-        const uint16_t* src[4];
-        if (sg.rows == nullptr) {
-#pragma unroll
-            for (int k = 0; k < 4; k++) src[k] = sg.src + uint64_t(hb) * kHalf + k * kTile + 8 * lane;
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; k++) src[k] = gathered_lane_ptr(sg, hb * kHalf + k * kTile, lane, bad_row);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; k++) v[k] = load_nt(reinterpret_cast<const uint4*>(src[k]));
-    }
+    if (full) load_full_half(sg, hb, lane, v, bad_row);
     __shared__ uint32_t s_hcnt[kEncWaves];
     uint32_t table_lo, table_hi;
     seg_table(a, s, table_lo, table_hi);
@@ -508,17 +574,16 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
     if (full) {
         run = encode_half<true, kPublish>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
     } else if (active) {
-        if (sg.rows == nullptr) {
-#pragma unroll
-            for (int k = 0; k < 4; k++) v[k] = load_lane(sg.src, hb * 4 + k, lane, n);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; k++) v[k] = load_lane_rows(sg, hb * 4 + k, lane, bad_row);
-        }
+        load_partial_half(sg, hb, lane, v, bad_row);
         run = encode_half<false, kPublish>(a, sg, hb, slot, v, lane, s_lut, tc, s_esc[wave]);
     }
     if (lane == 0) s_hcnt[wave] = run;
     __syncthreads();
+    // Blocks stored uncoded: a block (waves 2k, 2k + 1) whose escapes reach its overflow
+    // (its values past the first 192 of each tile) puts exactly those values' exponents
+    // in the escape buffer instead.  Every wave works out the escape-buffer bytes of all
+    // 8 half blocks from the counts, so no second barrier is needed.
+    const uint32_t hb0 = (unit - sg.unit0) * kEncWaves;   // first half block of the unit
     uint32_t before = 0, total = 0;
 #pragma unroll
     for (uint32_t w = 0; w < kEncWaves; w++) {
@@ -526,8 +591,38 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
         if (w < wave) before += c;
         total += c;
     }
+    bool my_uncoded = false;
+    // a block of 4096 values overflows 2560; only a segment's last unit has shorter ones
+    const bool maybe_uncoded = total >= kBlockOverflow || hb0 + kEncWaves > n / kHalf;
+    if (__builtin_amdgcn_readfirstlane(maybe_uncoded)) {
+        before = total = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kEncWaves / 2; k++) {
+            const uint32_t c0 = s_hcnt[2 * k], c1 = s_hcnt[2 * k + 1];
+            const uint32_t o0 = half_overflow(n, hb0 + 2 * k), o1 = half_overflow(n, hb0 + 2 * k + 1);
+            const bool unc = o0 + o1 > 0 && c0 + c1 >= o0 + o1;
+            const uint32_t b0 = unc ? o0 : c0, b1 = unc ? o1 : c1;
+            if (2 * k < wave) before += b0;
+            if (2 * k + 1 < wave) before += b1;
+            total += b0 + b1;
+            if (wave >> 1 == k) {
+                my_uncoded = unc && active;
+                if (unc) run = (wave & 1) ? o1 : o0;
+            }
+        }
+    }
     before = __builtin_amdgcn_readfirstlane(before);
     total = __builtin_amdgcn_readfirstlane(total);
+    if (__builtin_amdgcn_readfirstlane(my_uncoded)) {   // rare: the wave's block is uncoded
+        bool ignore = false;                           // bad rows were reported by the first pass
+        if (full) load_full_half(sg, hb, lane, v, ignore);
+        else load_partial_half(sg, hb, lane, v, ignore);
+        store_uncoded_half(sg, hb, lane, v, s_esc[wave]);
+        if (lane == 0) {
+            if constexpr (kPublish) store_agent(a.counts + slot, run);
+            else a.counts[slot] = run;
+        }
+    }
     if (!kPublish && tid == 0) a.unit_counts[unit] = total;   // for the place kernel's prefix sums
     // the unit's escapes, contiguous in value order: one run per unit for the place kernel
     uint8_t* stage = a.stage + uint64_t(unit) * kUnit + before;
@@ -1117,6 +1212,44 @@ __device__ inline uint32_t patch_second_escape(uint32_t E, uint32_t z, uint32_t 
     return (E & ~mask) | (perm(x, x, 0u) & mask);   // x in every byte
 }
 
+// BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1, from
+// the lane's A bytes and exponent bytes (values 0-3 in .x / E0, 4-7 in .y / E1).
+__device__ inline LaneBytes assemble_lane(uint2 A, uint32_t E0, uint32_t E1)
+{
+    LaneBytes o;
+    o.lo0 = (A.x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
+    o.hi0 = (A.x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
+    o.lo1 = (A.y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
+    o.hi1 = (A.y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
+    return o;
+}
+
+// Exponent bytes of this lane's 8 values in a tile of an uncoded block (values 0-3 in
+// .x, 4-7 in .y): those of the tile's first 192 values from its 192 plane bytes (lanes
+// 0..23), the others from the escape buffer, where the tile's bytes start at esc (byte by
+// byte: the escape buffer has no alignment).  nvalid: values of the lane that exist.
+__device__ inline uint2 uncoded_exponents(const uint8_t* tile_planes, const uint8_t* esc, uint32_t lane,
+                                          uint32_t nvalid)
+{
+    if (8 * lane < kUncodedPlaneBytes) return *reinterpret_cast<const uint2*>(tile_planes + 8 * lane);
+    const uint8_t* q = esc + (8 * lane - kUncodedPlaneBytes);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < 4; j++) {
+        if (j < nvalid) w0 |= uint32_t(q[j]) << (8 * j);
+        if (j + 4 < nvalid) w1 |= uint32_t(q[j + 4]) << (8 * j);
+        __builtin_amdgcn_sched_barrier(0);   // two loads in flight: few live registers (a rare path)
+    }
+    return make_uint2(w0, w1);
+}
+
+// Escape-buffer bytes of block b of a segment of n values when the block is uncoded.
+__device__ inline uint32_t block_overflow(uint32_t n, uint32_t b)
+{
+    const uint32_t full = n / kBlock;   // blocks with all their values
+    return overflow_of(b < full ? kBlock : (b == full ? n % kBlock : 0u));
+}
+
 __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint32_t tlo, uint32_t thi, uint32_t r,
                                         const uint8_t* esc_lds)
 {
@@ -1146,13 +1279,18 @@ __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint3
             }
         }
     }
-    // BF16 low byte = exponent bit 0 << 7 | mantissa, high byte = sign | exponent >> 1
-    LaneBytes o;
-    o.lo0 = (A.x & 0x7F7F7F7Fu) | ((E0 << 7) & 0x80808080u);
-    o.hi0 = (A.x & 0x80808080u) | ((E0 >> 1) & 0x7F7F7F7Fu);
-    o.lo1 = (A.y & 0x7F7F7F7Fu) | ((E1 << 7) & 0x80808080u);
-    o.hi1 = (A.y & 0x80808080u) | ((E1 >> 1) & 0x7F7F7F7Fu);
-    return o;
+    return assemble_lane(A, E0, E1);
+}
+
+// acc[j] += the lane's decoded value j (f32 bits = BF16 bits << 16: bytes [0, 0, low, high])
+__device__ inline void add_lane(float (&acc)[8], const LaneBytes& o)
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t sel = 0x0C0Cu | ((j & 3u) << 16) | ((4u + (j & 3u)) << 24);
+        const uint32_t f = j < 4 ? perm(o.hi0, o.lo0, sel) : perm(o.hi1, o.lo1, sel);
+        acc[j] = acc[j] + __uint_as_float(f);
+    }
 }
 
 constexpr uint32_t kAccWaves = 8;                  // one wave per tile of a block
@@ -1166,9 +1304,10 @@ constexpr uint32_t kEscPad = 16;                   // decode_lane may read esc_l
 struct PeerBlock {
     uint32_t tlo, thi;
     uint32_t esc_lo, esc_hi;   // escape-buffer offset of the block's first escape
-    uint32_t count;
-    uint32_t ok;
+    uint32_t count;            // the block's bytes in the escape buffer
+    uint32_t state;            // kPeerCorrupt, kPeerCoded or kPeerUncoded
 };
+constexpr uint32_t kPeerCorrupt = 0, kPeerCoded = 1, kPeerUncoded = 2;
 
 // Decode-accumulate: one workgroup per block, one wave per tile.  Every peer's bytes
 // for the tile are requested up front; wave p checks peer p's header and offset-table
@@ -1241,6 +1380,9 @@ void accumulate_kernel(const AArgs a)
     // ---- this wave's share of the header checks: peers wave, wave + 8 ----
     constexpr int kMine = (kPeers + kAccWaves - 1) / kAccWaves;   // peers checked per wave
     uint32_t head[kMine][kAccBlkHead / 64];                       // their blocks' first escapes
+    // a block is uncoded when it puts exactly its overflow in the escape buffer (a coded
+    // block puts fewer escapes there)
+    const uint32_t ovf = block_overflow(n, b);
 #pragma unroll
     for (int i = 0; i < kMine; i++) {
         const uint32_t p = wave + i * kAccWaves;
@@ -1253,7 +1395,8 @@ void accumulate_kernel(const AArgs a)
             uint32_t first = 0, last = 0;
             const bool ok = hd.ok && block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
             const uint64_t e = hd.esc_offset + first;
-            if (lane == 0) s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, ok ? 1u : 0u};
+            const uint32_t state = !ok ? kPeerCorrupt : (ovf > 0 && last - first == ovf ? kPeerUncoded : kPeerCoded);
+            if (lane == 0) s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, state};
             m = ok ? min(last - first, kAccBlkHead) : 0u;
             if (m > 0) src = peer_esc[p] + e;
         }
@@ -1306,7 +1449,7 @@ void accumulate_kernel(const AArgs a)
     // gives every peer's count before this wave's tile and its block total by readlane.
     static_assert(kAccWaves == 8, "one lane per (peer, tile) pair in groups of 8");
     uint32_t before[kPeers], mine[kPeers];
-    bool bad = false;
+    uint64_t odd = 0;   // nonzero: a peer that is not a coded block agreeing with its offsets
 #pragma unroll
     for (int h = 0; h < (kPeers * kAccWaves + 63) / 64; h++) {
         const uint32_t idx = 64 * h + lane;
@@ -1322,13 +1465,34 @@ void accumulate_kernel(const AArgs a)
                                             : uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
                 before[p] = uint32_t(__builtin_amdgcn_readlane(int(excl), int(8 * q + wave))) - base;
                 mine[p] = total[p];
-                // the offset table must agree with the planes (bitwise, no branch per peer:
-                // the peers' LDS records are read together)
-                bad = bad | (s_peer[p].ok == 0u) | (next - base != s_peer[p].count);
+                // the offset table must agree with the planes of a coded block (no branch per
+                // peer: the peers' LDS records are read together; the conditions stay lane
+                // masks in scalar registers)
+                odd |= ballot(s_peer[p].state != kPeerCoded) | ballot(next - base != s_peer[p].count);
             }
         }
     }
-    bad = __builtin_amdgcn_readfirstlane(bad);
+    // rare: a corrupt peer, or one whose block is uncoded (its planes hold exponents, so
+    // they are not checked against its offsets)
+    bool bad = false;
+    uint32_t uncoded = 0;
+    if (odd != 0) {
+        for (int p = 0; p < kPeers; p++) {
+            if (kPeers > 8 && uint32_t(p) >= P) break;
+            const uint32_t state = s_peer[p].state;
+            uint32_t planes = 0;   // the block's escapes according to its planes
+            for (uint32_t w = 0; w < kAccWaves; w++) planes += s_cnt[p][w];
+            bad = bad || state == kPeerCorrupt || (state == kPeerCoded && planes != s_peer[p].count);
+            if (state == kPeerUncoded) uncoded |= 1u << p;
+        }
+        bad = __builtin_amdgcn_readfirstlane(bad);
+        uncoded = __builtin_amdgcn_readfirstlane(uncoded);
+        // an uncoded peer takes the decode loop's rare branch, as a tile whose escapes go
+        // past the block's first 512 does
+#pragma unroll
+        for (int p = 0; p < kPeers; p++)
+            if (uncoded & (1u << p)) mine[p] = kAccBlkHead + 1;
+    }
     // a lane holding the last values of the segment (fewer than 8) reads them now
     if (nvalid > 0 && nvalid < 8) lv = load_lane(local, t, lane, n);
 
@@ -1343,24 +1507,35 @@ void accumulate_kernel(const AArgs a)
 #pragma unroll
     for (int p = 0; p < kPeers; p++) {
         if ((kPeers <= 8 || uint32_t(p) < P) && !bad && has_tile) {
-            const uint8_t* tile_esc = s_blk[p] + before[p];
             if (before[p] + mine[p] > kAccBlkHead) {
-                // rare (escape-heavy tables): the tile's escapes go past the block's
-                // first 512; stage them in the wave's own LDS slot
+                // rare: the tile's escapes go past the block's first 512 (escape-heavy
+                // tables), or the peer's block is uncoded; stage what the tile needs in the
+                // wave's own LDS slot
                 const uint64_t e = uint64_t(s_peer[p].esc_hi) << 32 | s_peer[p].esc_lo;
-                const uint8_t* esc = peer_esc[p] + e + before[p];
-                for (uint32_t k = lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
+                const bool unc = (uncoded >> p) & 1u;
+                if (unc) {
+                    // the tile's exponents in value order: the first 192 from its plane
+                    // bytes, the rest from the escape buffer, where earlier tiles of the
+                    // block (all full) put kTile - 192 bytes each
+                    const uint8_t* pl = peer_st[p] + planes_off(n) + 192ull * t;
+                    const uint8_t* ex = peer_esc[p] + e + wave * (kTile - kUncodedPlaneBytes);
+                    const uint32_t m = uint32_t(min<uint64_t>(kTile, n - uint64_t(t) * kTile));
+#pragma unroll 1
+                    for (uint32_t k = lane; k < m; k += 64)
+                        esc_lds[k] = k < kUncodedPlaneBytes ? pl[k] : ex[k - kUncodedPlaneBytes];
+                } else {
+                    const uint8_t* esc = peer_esc[p] + e + before[p];
+#pragma unroll 1
+                    for (uint32_t k = lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
+                }
                 wave_lds_sync();
-                tile_esc = esc_lds;
-            }
-            const LaneBytes o = decode_lane(rows[p], zf[p], s_A[wave][p][lane], s_peer[p].tlo, s_peer[p].thi, rank[p],
-                                            tile_esc);
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                // f32 bits = BF16 bits << 16: bytes [0, 0, low, high]
-                const uint32_t sel = 0x0C0Cu | ((j & 3u) << 16) | ((4u + (j & 3u)) << 24);
-                const uint32_t f = j < 4 ? perm(o.hi0, o.lo0, sel) : perm(o.hi1, o.lo1, sel);
-                acc[j] = acc[j] + __uint_as_float(f);
+                // an uncoded tile decodes as if every value escaped: codes 0, this lane's
+                // exponents at 8 * lane
+                add_lane(acc, decode_lane(unc ? 0u : rows[p], unc ? valid_flags(nvalid) : zf[p], s_A[wave][p][lane],
+                                          s_peer[p].tlo, s_peer[p].thi, unc ? 8 * lane : rank[p], esc_lds));
+            } else {
+                add_lane(acc, decode_lane(rows[p], zf[p], s_A[wave][p][lane], s_peer[p].tlo, s_peer[p].thi, rank[p],
+                                          s_blk[p] + before[p]));
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -1442,6 +1617,29 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(const DArgs a)
         hd = read_header(st, n, sg.esc_bytes, sg.esc_at_first != 0);
         const uint32_t* C = reinterpret_cast<const uint32_t*>(st + offsets_off(n));
         bad = !hd.ok || !block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
+    }
+    if (active && !bad && last > first && last - first == block_overflow(n, b)) {
+        // rare: an uncoded block (a coded one puts fewer bytes in the escape buffer).  Both
+        // waves of the workgroup hold the same block, so both take this path (and neither
+        // reaches the barrier below).
+        const uint8_t* esc = sg.esc + hd.esc_offset + first + (half ? half_overflow(n, 2 * b) : 0u);
+#pragma unroll
+        for (int k = 0; k < int(kDecHalfTiles); k++) {
+            const uint32_t t = hb * kDecHalfTiles + k;
+            const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
+            const uint32_t nvalid = (t >= T || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
+            const uint2 E = t < T ? uncoded_exponents(st + planes_off(n) + 192ull * t, esc + k * (kTile - kUncodedPlaneBytes),
+                                                      lane, nvalid)
+                                  : make_uint2(0, 0);
+            if (nvalid == 0) continue;
+            const LaneBytes y = assemble_lane(Ap[k], E.x, E.y);
+            const uint32_t ov[4] = {perm(y.hi0, y.lo0, 0x05010400u), perm(y.hi0, y.lo0, 0x07030602u),
+                                    perm(y.hi1, y.lo1, 0x05010400u), perm(y.hi1, y.lo1, 0x07030602u)};
+            if (nvalid == 8) store_nt(reinterpret_cast<uint4*>(sg.dst + i0), make_uint4(ov[0], ov[1], ov[2], ov[3]));
+            else
+                for (uint32_t j = 0; j < nvalid; j++) sg.dst[i0 + j] = uint16_t(ov[j >> 1] >> (16 * (j & 1)));
+        }
+        return;
     }
     // rows, escape flags and the ranks of this lane's escapes within the half block
     const Transpose32 tc = transpose_consts(lane);
