@@ -1,31 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the lossless BF16 exponent codec on one MI355X.
 
-One step = the whole hot path over one 64 Mi-value gradient bucket (16 layers of
-4 Mi values, each layer with its own sigma-predicted table): plan the 16 tables on the
-host, compress all layers in one launch, decompress them in one launch.  Inputs are
-resident in HBM before the timed region.  Four input/output buffer sets rotate, and a
-set is decompressed two steps after it was compressed, so that neither kernel finds
-its input in the 256 MB Infinity Cache (steady state of a pipelined round trip).
+One step = the whole hot path over the reduce-scatter receive share, the largest
+workload that fits one GPU: 7 peer shards of 64 Mi BF16 values (N(0, 1e-3)) and the
+local shard.  Plan the 7 tables on the host, compress the peer shards in 32 chunks of
+2 Mi values (one compress call per chunk, one segment per peer; 8 chunks share a
+launch), then decode the 7 compressed shards of every chunk and add them in fp32, in
+peer order, to the local shard, rounding once to BF16.  Inputs are resident in HBM
+before the timed region; the step's working set (~1.7 GB) is far larger than the
+256 MB Infinity Cache.
 
 Printed (one JSON line on stdout):
-  value      BF16 bytes handled per second by the step: (2n compressed + 2n decompressed)
-             / step wall time, in GB/s (the harmonic mean of the two codec directions);
-  roofline   for the step's dominant operation (compress: compress_single_kernel,
-             or decompress: decompress_kernel, whichever takes longer): algorithmic HBM
-             bytes per launch (2n BF16 bytes + static part + escapes) / average launch
-             time, from HIP events on the launch stream around back-to-back launches over
-             the rotating sets, against the 8 TB/s HBM peak; traffic: the HBM bytes per
-             launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
-             (profiles/pmc_traffic_bucket_64m.txt; null when that was taken on other
-             kernel sources); roofline_other_op for the other operation;
-  cpu_baseline  the plain C oracle, single-threaded, on the same bucket;
-  per_config the other workloads (1 Mi chunk, activations with escapes and specials,
-             MoE dispatch buckets, the same dispatch compressed from the unpermuted
-             token matrix by row index (against a permute copy + compress), the
-             all-gather receive side decoding 16 separately
-             compressed shards in one launch, reduce-scatter share with decode-accumulate
-             and the two-stream pipeline), each with GB/s and HBM fraction.
+  value      BF16 bytes handled per second by the step: (2 x 7n compressed + 2 x 7n
+             decoded) / step wall time, in GB/s;
+  roofline   for the step's dominant kernel (compress_single_kernel): algorithmic
+             HBM bytes per launch (2 B per value + static parts + escape bytes) /
+             average launch time, from HIP events on the launch stream around
+             back-to-back passes, against the 8 TB/s HBM peak; traffic: the HBM bytes
+             per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
+             (profiles/pmc_traffic_rs_512m.txt; null when that was taken on other kernel
+             sources); roofline_other_op for decode-accumulate;
+  cpu_baseline  the plain C oracle on the host's cores, on a bounded sample of the
+             same workload (4 of the 32 chunks), 1 thread and all threads;
+  per_config every workload (1 Mi chunk, 64 Mi gradient bucket, activations with
+             escapes and specials, MoE dispatch buckets, the same dispatch compressed
+             from the unpermuted token matrix by row index, the all-gather receive side,
+             the reduce-scatter share with its two-stream pipeline, plans estimated on
+             the device, the switcher's profile), each with GB/s, HBM fraction and the
+             oracle's time on the host beside it.
 """
 from __future__ import annotations
 
@@ -210,118 +212,162 @@ def codec_report(bc, c, d):
     }
 
 
-def bench_rs(torch, Z, W, iters):
-    """Reduce-scatter receive share: 7 peer shards x 64 Mi, 32 chunks of 2 Mi values."""
-    wl = W.rs_512m()
-    P, chunk, n = wl.extra["peers"], wl.extra["chunk"], wl.extra["shard"]
-    plans = [Z.plan(sigma=s) for s in wl.sigmas]
-    peers = [to_dev(torch, s) for s in wl.segments]
-    local = to_dev(torch, wl.extra["local"])
-    dst = torch.empty(n, dtype=torch.bfloat16, device="cuda")
-    nch = n // chunk
-    S = Z.static_size(chunk)
-    # every chunk's compressed output kept (as a receiver would hold what arrived)
-    static = torch.empty(nch * P * S, dtype=torch.uint8, device="cuda")
-    esc = torch.empty(nch * P * chunk, dtype=torch.uint8, device="cuda")
-    ws = torch.zeros(Z.workspace_size(P * chunk, P), dtype=torch.uint8, device="cuda")
-    n_esc = torch.zeros(nch, P + 1, dtype=torch.int64, device="cuda")
-    status = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    comp = [Z.PreparedCompress([p[c * chunk:(c + 1) * chunk] for p in peers], static[c * P * S:(c + 1) * P * S],
-                               esc[c * P * chunk:(c + 1) * P * chunk], ws, n_esc[c], status) for c in range(nch)]
-    # the same 32 calls through zipccl_compress_chunks: 8 chunks (56 segments) share a
-    # launch, with a workspace that holds them (as the pipeline's does)
-    ws2 = torch.zeros(Z.workspace_size(8 * P * chunk, 8 * P), dtype=torch.uint8, device="cuda")
-    comp_seq = Z.PreparedCompressChunks([[p[c * chunk:(c + 1) * chunk] for p in peers] for c in range(nch)],
-                                        [static[c * P * S:(c + 1) * P * S] for c in range(nch)],
-                                        [esc[c * P * chunk:(c + 1) * P * chunk] for c in range(nch)], ws2,
-                                        n_esc.view(-1), status)
-    acc = [Z.PreparedAccumulate([static.data_ptr() + (c * P + p) * S for p in range(P)],
-                                [esc.data_ptr() + c * P * chunk] * P, chunk, local[c * chunk:], dst[c * chunk:],
-                                status, esc_bytes=[P * chunk] * P) for c in range(nch)]
+class RSShare:
+    """The reduce-scatter receive share on the device: 7 peer shards and the local shard,
+    the 32 chunks' compressed outputs (kept, as a receiver holds what arrived), and the
+    compress and decode-accumulate sequences marshalled once."""
 
-    # the 32 decode-accumulates through zipccl_decompress_accumulate_chunks (18 chunks of
-    # 7 peers per launch)
-    acc_seq = Z.PreparedAccumulateChunks([static.data_ptr() + (c * P + p) * S for c in range(nch) for p in range(P)],
-                                         [esc.data_ptr() + c * P * chunk for c in range(nch) for _ in range(P)],
-                                         P, chunk, n, local, dst, status, esc_bytes=[P * chunk] * (P * nch))
+    def __init__(self, torch, Z, W):
+        wl = W.rs_512m()
+        self.torch, self.Z, self.wl = torch, Z, wl
+        self.P, self.chunk, self.n = wl.extra["peers"], wl.extra["chunk"], wl.extra["shard"]
+        P, chunk, n = self.P, self.chunk, self.n
+        self.nch = n // chunk
+        self.sigmas = wl.sigmas
+        self.peers = [to_dev(torch, s) for s in wl.segments]
+        self.local = to_dev(torch, wl.extra["local"])
+        self.dst = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        self.S = S = Z.static_size(chunk)
+        self.static = torch.empty(self.nch * P * S, dtype=torch.uint8, device="cuda")
+        self.esc = torch.empty(self.nch * P * chunk, dtype=torch.uint8, device="cuda")
+        self.n_esc = torch.zeros(self.nch, P + 1, dtype=torch.int64, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        # 8 chunks (56 segments) share a compress launch, with a workspace that holds them
+        self.per_launch = 8
+        self.ws = torch.zeros(Z.workspace_size(self.per_launch * P * chunk, self.per_launch * P), dtype=torch.uint8,
+                              device="cuda")
+        self.comp_seq = Z.PreparedCompressChunks(
+            [[p[c * chunk:(c + 1) * chunk] for p in self.peers] for c in range(self.nch)],
+            [self.static[c * P * S:(c + 1) * P * S] for c in range(self.nch)],
+            [self.esc[c * P * chunk:(c + 1) * P * chunk] for c in range(self.nch)], self.ws, self.n_esc.view(-1),
+            self.status)
+        self.acc_seq = Z.PreparedAccumulateChunks(
+            [self.static.data_ptr() + (c * P + p) * S for c in range(self.nch) for p in range(P)],
+            [self.esc.data_ptr() + c * P * chunk for c in range(self.nch) for _ in range(P)],
+            P, chunk, n, self.local, self.dst, self.status, esc_bytes=[P * chunk] * (P * self.nch))
 
-    def compress_all():
-        comp_seq.run(plans)
+    def plans(self):
+        return [self.Z.plan(sigma=s) for s in self.sigmas]
 
-    def compress_calls():
-        for c in range(nch):
-            comp[c].run(plans)
+    def compress_all(self, plans=None):
+        self.comp_seq.run(self.plans() if plans is None else plans)
 
-    def accumulate_all():
-        acc_seq.run()
+    def accumulate_all(self):
+        self.acc_seq.run()
 
-    def accumulate_calls():
-        for c in range(nch):
-            acc[c].run()
+    def step(self):
+        self.compress_all()            # the 7 tables are planned on the host each step
+        self.accumulate_all()
 
-    compress_all()
-    accumulate_all()
-    # per pass over the 32 chunks: back-to-back passes between two events, as the other
-    # workloads are timed (launch ramp-up and drain amortised), and single passes
-    c_ms = batched_ms(torch, lambda k: compress_all(), 1, iters)
-    a_ms = batched_ms(torch, lambda k: accumulate_all(), 1, iters)
+    def total_esc(self):
+        return int(self.n_esc[:, -1].sum().item())
+
+    def compress_bytes(self):
+        return 2 * self.P * self.n + self.nch * self.P * self.S + self.total_esc()
+
+    def accumulate_bytes(self):
+        return self.nch * self.P * self.S + self.total_esc() + 2 * self.n + 2 * self.n
+
+    def check(self):
+        """The decode-accumulate output against torch on the device: fp32 adds in peer
+        order, one rounding to BF16 (the inputs hold no NaN, so torch's NaN bits do not
+        matter), and the status word."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        ok = int(self.status.item()) == 0
+        for c0 in range(0, self.n, 1 << 24):
+            sl = slice(c0, min(self.n, c0 + (1 << 24)))
+            acc = self.local[sl].float()
+            for p in self.peers:
+                acc = acc + p[sl].float()
+            ok = ok and bool(torch.equal(acc.to(torch.bfloat16).view(torch.int16), self.dst[sl].view(torch.int16)))
+        return ok
+
+    def launches(self):
+        """Kernel launches of one step, for the counter summaries: kernel, grid size in
+        work-items, launches per step, algorithmic bytes per launch."""
+        units = self.per_launch * self.P * ((self.chunk + 16383) // 16384)
+        nl_c = self.nch // self.per_launch
+        per_acc = 128 // self.P
+        nl_a = -(-self.nch // per_acc)
+        return [{"kernel": "compress_single_kernel", "grid": (units + (units + 7) // 8) * 512, "per_step": nl_c,
+                 "bytes": self.compress_bytes() / nl_c, "values": self.per_launch * self.P * self.chunk},
+                {"kernel": "accumulate_kernel", "grid": (self.chunk // 4096) * 512 * per_acc, "per_step": nl_a,
+                 "bytes": self.accumulate_bytes() / self.nch * per_acc, "values": per_acc * self.chunk,
+                 "note": "grid and bytes of a full launch (the last one holds the remaining chunks)"}]
+
+
+def bench_rs_extra(torch, Z, rs, iters):
+    """The reduce-scatter share's per-operation figures: each sequence alone, back to
+    back (launch ramp-up and drain amortised), one pass between its own events, 32
+    separate calls, and the two-stream pipeline's wall time."""
+    P, chunk, n, nch = rs.P, rs.chunk, rs.n, rs.nch
+    plans = rs.plans()
+    comp = [Z.PreparedCompress([p[c * chunk:(c + 1) * chunk] for p in rs.peers],
+                               rs.static[c * P * rs.S:(c + 1) * P * rs.S], rs.esc[c * P * chunk:(c + 1) * P * chunk],
+                               rs.ws, rs.n_esc[c], rs.status) for c in range(nch)]
+    acc = [Z.PreparedAccumulate([rs.static.data_ptr() + (c * P + p) * rs.S for p in range(P)],
+                                [rs.esc.data_ptr() + c * P * chunk] * P, chunk, rs.local[c * chunk:],
+                                rs.dst[c * chunk:], rs.status, esc_bytes=[P * chunk] * P) for c in range(nch)]
+    rs.compress_all(plans)
+    rs.accumulate_all()
+    c_ms = batched_ms(torch, lambda k: rs.compress_all(plans), 1, iters)
+    a_ms = batched_ms(torch, lambda k: rs.accumulate_all(), 1, iters)
     tc, ta = Timer(torch), Timer(torch)
     for _ in range(iters):
         e = tc.start()
-        compress_all()
+        rs.compress_all(plans)
         tc.stop(e)
         e = ta.start()
-        accumulate_all()
+        rs.accumulate_all()
         ta.stop(e)
     c1_ms, a1_ms = median(tc.ms()), median(ta.ms())
     tp, tq = Timer(torch), Timer(torch)
     for _ in range(iters):
         e = tp.start()
-        compress_calls()
+        for c in range(nch):
+            comp[c].run(plans)
         tp.stop(e)
         e = tq.start()
-        accumulate_calls()
+        for c in range(nch):
+            acc[c].run()
         tq.stop(e)
     cp_ms, ap_ms = median(tp.ms()), median(tq.ms())
-    total_esc = int(n_esc[:, -1].sum().item())
-    static_total = nch * P * S
-    comp_moved = 2 * P * n + static_total + total_esc
-    acc_moved = static_total + total_esc + 2 * n + 2 * n
-    # two-stream pipeline, wall time
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     pipe = Z.Pipeline(P, chunk, sa, sb)
-    pipe.reduce(peers, plans, local, dst, status)
+    pipe.reduce(rs.peers, plans, rs.local, rs.dst, rs.status)
     torch.cuda.synchronize()
     walls = []
     for _ in range(iters):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        pipe.reduce(peers, plans, local, dst, status)
+        pipe.reduce(rs.peers, plans, rs.local, rs.dst, rs.status)
         torch.cuda.synchronize()
         walls.append(time.perf_counter() - t0)
     pipe.close()
-    ok = int(status.item()) == 0
+    ok = rs.check()     # the pipeline's output, against torch
     wall = median(walls)
+    static_total = nch * P * rs.S
+    total_esc = rs.total_esc()
     return {
         "elements_per_peer": n, "peers": P, "chunk": chunk, "chunks": nch,
         "compress_us": round(c_ms * 1e3, 1),
         "compress_GBps": round(2 * P * n / (c_ms * 1e-3) / 1e9, 1),
-        "compress_hbm_frac": round(comp_moved / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "compress_hbm_frac": round(rs.compress_bytes() / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "compress_single_pass_us": round(c1_ms * 1e3, 1),
         "compress_separate_calls_us": round(cp_ms * 1e3, 1),
         "accumulate_us": round(a_ms * 1e3, 1),
         "accumulate_GBps_bf16_in": round(2 * P * n / (a_ms * 1e-3) / 1e9, 1),
-        "accumulate_hbm_frac": round(acc_moved / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "accumulate_hbm_frac": round(rs.accumulate_bytes() / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "accumulate_single_pass_us": round(a1_ms * 1e3, 1),
         "accumulate_separate_calls_us": round(ap_ms * 1e3, 1),
         "pipeline_wall_us": round(wall * 1e6, 1),
         "pipeline_GBps_bf16_in": round(2 * P * n / wall / 1e9, 1),
         "ratio": round(2 * P * n / (static_total + total_esc), 5),
         "escape_frac": round(total_esc / (P * n), 5),
-        "status_ok": ok,
+        "parity_vs_torch_fp32": ok,
     }
-
 
 def bench_allgather(torch, Z, W, rounds):
     """All-gather receive side: the bucket's 16 layers as 16 ranks' shards, each
@@ -508,60 +554,126 @@ def copy_ceiling(torch, iters=10):
     return round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
 
 
-def cpu_baseline(W, O, wl, reps):
-    import numpy as np
-    tables = [O.plan_sigma(s) for s in wl.sigmas]
+
+# ------------------------------------------------------------------------------------
+# the oracle on the host's cores, beside every workload (a baseline, not the target)
+# ------------------------------------------------------------------------------------
+def host_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_codec(O, segments, sigmas, reps=1, sample=None):
+    """The oracle's compress (one batch call) and decompress (one call per segment) of a
+    workload's segments on one thread, median of reps; then the same values as at least
+    host_threads() independent segments (each workload segment split in halves until
+    there are enough), compress + decompress of each as one task on every thread."""
+    from concurrent.futures import ThreadPoolExecutor
+    tables = [O.plan_sigma(s if s is not None else 1.0) for s in sigmas]
+    n = int(sum(x.size for x in segments))
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        st, esc, ne, rc = O.compress_batch(wl.segments, tables)
+        st, esc, ne, rc = O.compress_batch(segments, tables)
         t1 = time.perf_counter()
-        off_st, off_esc = 0, 0
-        for x in wl.segments:
+        off_st = 0
+        for x in segments:
             sz = O.static_size(x.size)
             O.decompress(st[off_st:off_st + sz], esc, x.size)
             off_st += sz
-        t2 = time.perf_counter()
-        times.append((t1 - t0, t2 - t1))
-    c = median([t[0] for t in times])
-    d = median([t[1] for t in times])
-    n = wl.n_total
-    out = {"value": round(4 * n / (c + d) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"{wl.name} full bucket ({n} values), compress + decompress, median of {reps}, 1 thread",
-           "compress_GBps": round(2 * n / c / 1e9, 4), "decompress_GBps": round(2 * n / d / 1e9, 4),
-           "host_cpus": os.cpu_count()}
-    # the same oracle on every host thread (at most 16), one layer per task: the C calls
-    # release the interpreter lock, and the layers are independent
-    from concurrent.futures import ThreadPoolExecutor
-    threads = max(1, min(16, os.cpu_count() or 1, len(wl.segments)))
+        times.append((t1 - t0, time.perf_counter() - t1))
+    c, d = median([t[0] for t in times]), median([t[1] for t in times])
+    threads = host_threads()
+    pieces = list(zip(segments, tables))
+    while len(pieces) < threads and max(p[0].size for p in pieces) > 8192:
+        pieces = [q for x, t in pieces for q in ((x[:x.size // 2], t), (x[x.size // 2:], t))]
 
     def one(k):
-        x = wl.segments[k]
-        st, esc, _ = O.compress(x, tables[k])
-        O.decompress(st, esc, x.size)
+        x, t = pieces[k]
+        s, e, _ = O.compress(x, t)
+        O.decompress(s, e, x.size)
 
     with ThreadPoolExecutor(threads) as pool:
         t0 = time.perf_counter()
-        list(pool.map(one, range(len(wl.segments))))
+        list(pool.map(one, range(len(pieces))))
         wall = time.perf_counter() - t0
-    out["all_threads"] = {"threads": threads, "value": round(4 * n / wall / 1e9, 4), "unit": "GB/s",
-                          "sample": "the same bucket, compress + decompress of each layer as one task"}
-    return out
+    return {"value": round(4 * n / (c + d) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "compress_GBps": round(2 * n / c / 1e9, 4), "decompress_GBps": round(2 * n / d / 1e9, 4),
+            "sample": sample or f"all {n} values, compress + decompress, 1 thread" + (f", median of {reps}" if reps > 1 else ""),
+            "all_threads": {"threads": threads, "value": round(4 * n / wall / 1e9, 4), "unit": "GB/s",
+                            "sample": f"the same values as {len(pieces)} segments, compress + decompress of each as one task"}}
 
+
+def oracle_rs(O, W, chunks=4, reps=3):
+    """The oracle on a bounded sample of the reduce-scatter share: the first `chunks`
+    chunks of the 7 peers (compress each peer's chunk, then decode-accumulate the chunk
+    into the local shard), on one thread (median of reps), and 16 chunks as one task
+    each on every thread."""
+    from concurrent.futures import ThreadPoolExecutor
+    wl = W.rs_512m()
+    P, chunk = wl.extra["peers"], wl.extra["chunk"]
+    tables = [O.plan_sigma(s) for s in wl.sigmas]
+    local = wl.extra["local"]
+
+    def do_chunk(c):
+        t0 = time.perf_counter()
+        comp = [O.compress(p[c * chunk:(c + 1) * chunk], t) for p, t in zip(wl.segments, tables)]
+        t1 = time.perf_counter()
+        O.decompress_accumulate([x[0] for x in comp], [x[1] for x in comp], chunk, local[c * chunk:(c + 1) * chunk])
+        return t1 - t0, time.perf_counter() - t1
+
+    times = []
+    for _ in range(reps):
+        ts = [do_chunk(c) for c in range(chunks)]
+        times.append((sum(t[0] for t in ts), sum(t[1] for t in ts)))
+    c, a = median([t[0] for t in times]), median([t[1] for t in times])
+    v = P * chunk * chunks
+    threads = host_threads()
+    par = 16
+    with ThreadPoolExecutor(threads) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(do_chunk, range(par)))
+        wall = time.perf_counter() - t0
+    return {"value": round(4 * v / (c + a) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "compress_GBps": round(2 * v / c / 1e9, 4), "accumulate_GBps_bf16_in": round(2 * v / a / 1e9, 4),
+            "sample": f"rs_512m chunks 0..{chunks - 1} of the 7 peers ({chunks} x 7 x {chunk} values): compress + "
+                      f"decode-accumulate, median of {reps}, 1 thread",
+            "host_cpus": os.cpu_count(),
+            "all_threads": {"threads": threads, "value": round(4 * P * chunk * par / wall / 1e9, 4), "unit": "GB/s",
+                            "sample": f"rs_512m chunks 0..{par - 1}, compress + decode-accumulate of each chunk as one task"}}
+
+
+# ------------------------------------------------------------------------------------
+# one workload alone (for profiling), with the launches of one pass
+# ------------------------------------------------------------------------------------
+def codec_launches(bc, n_esc):
+    """compress_single_kernel and decompress_kernel launches of one BatchCodec pass."""
+    units = sum((m + 16383) // 16384 for m in bc.sizes)
+    blocks = sum((m + 4095) // 4096 for m in bc.sizes)
+    moved = compress_bytes(bc.n, bc.static_bytes, n_esc)
+    return [{"kernel": "compress_single_kernel", "grid": (units + (units + 7) // 8) * 512, "per_step": 1,
+             "bytes": moved, "values": bc.n},
+            {"kernel": "decompress_kernel", "grid": blocks * 128, "per_step": 1, "bytes": moved, "values": bc.n}]
+
+
+def bench_codec_workload(torch, Z, W, name, rounds=5):
+    w2 = W.get(name)
+    sets = 8 if name == "chunk_1m" else 4
+    b2 = BatchCodec(torch, Z, w2.segments, w2.sigmas, sets)
+    run_codec(torch, b2, 3, 3)
+    cm, dm = op_times(torch, b2, rounds)
+    r2 = codec_report(b2, cm, dm)
+    r2["parity_round_trip"] = b2.verify()
+    launches = codec_launches(b2, b2.n_esc_total())
+    del b2
+    torch.cuda.empty_cache()
+    return r2, launches, w2
 
 # ------------------------------------------------------------------------------------
 # rocprofv3 summaries kept under profiles/ (text), and the measured HBM traffic
 # ------------------------------------------------------------------------------------
 KERNEL_SRC = os.path.join(ROOT, "lossless_bf16_exponent_codec_amd", "csrc", "zipccl_kernels.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "pmc_traffic_bucket_64m.txt")
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats -o bench -- "
-             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra")
-PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d rocprof_out/pmc_{counter} -o run -- "
-           "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-extra")
-RS_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats_rs -o rs -- "
-                "python3 bench.py --only rs_512m")
 OUR_KERNELS = ("compress_single_kernel", "encode_kernel", "place_direct_kernel", "scan_kernel", "place_kernel",
-               "decompress_kernel", "accumulate_kernel")
+               "decompress_kernel", "accumulate_kernel", "estimate_partial_kernel", "estimate_finish_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 GIB = 1 << 30
 
@@ -579,137 +691,126 @@ def short_kernel_name(name):
     return COPY_KERNEL if COPY_KERNEL in name else None
 
 
-def summarize_stats(csv_path, out_path, rs=False):
-    """profiles/ text from rocprofv3 --stats (kernel_stats.csv) of TRACE_CMD (or, with rs,
-    of RS_TRACE_CMD)."""
+def summarize_stats_any(csv_path, out_path, title, command):
+    """profiles/ text from rocprofv3 --kernel-trace --stats (kernel_stats.csv): rocprofv3's
+    own per-kernel averages."""
     import csv
     rows = [r for r in csv.DictReader(open(csv_path)) if short_kernel_name(r["Name"]) in OUR_KERNELS]
-    title = ("# Kernel durations, rs_512m (7 peers x 64 Mi BF16 values in 32 chunks of 2 Mi)" if rs else
-             "# Kernel durations, bucket_64m (16 x 4 Mi BF16 values, one table per layer)")
-    lines = [title, "",
+    lines = [f"# Kernel durations, {title}", "",
              "Command (from the repository root on the GPU host; rocprofv3's own averages):", "",
-             "    " + (RS_TRACE_CMD if rs else TRACE_CMD), "",
-             f"Kernel source sha256: `{kernel_source_sha256()}`", "",
+             "    " + command, "", f"Kernel source sha256: `{kernel_source_sha256()}`", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    if rs:
-        lines += ["", "The chunk compresses run as separate calls (compress_single_kernel, 7 segments of",
-                  "2 Mi values each) and through zipccl_compress_chunks and the pipeline",
-                  "(compress_single_kernel over 8 chunks, 56 segments, per launch); decode-accumulate",
-                  "runs one chunk per launch and 18 chunks per launch (accumulate_kernel)."]
-    else:
-        lines += ["", "Calls include the warmup and verification round trips; all launches are of the",
-                  "bucket workload (compress: compress_single_kernel, decompress: decompress_kernel)."]
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
-def summarize_pmc(fetch_csv, write_csv, out_path, n_units=4096):
-    """profiles/ text from two rocprofv3 --pmc runs of PMC_CMD (FETCH_SIZE, then
-    WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads for the
-    bench's 1 GiB device-to-device copy (the copy reads and writes 1 GiB).  Bucket
-    launches are told apart from others by grid size."""
+def pmc_cmd(name, counter):
+    return (f"rocprofv3 --pmc {counter} --output-format csv -d rocprof_out/pmc_{name}_{counter} -o run -- "
+            f"python3 bench.py --only {name} --launches-out rocprof_out/launches_{name}.json")
+
+
+def per_kernel_counter(path, counter):
+    """Mean counter value per (kernel, grid) over the dispatches of a rocprofv3 --pmc CSV."""
     import csv
-
-    def per_kernel(path, counter):
-        acc = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            k = short_kernel_name(r["Kernel_Name"])
-            if k is None:
-                continue
-            grid = int(r["Grid_Size"])
-            acc.setdefault((k, grid), []).append(float(r["Counter_Value"]))
-        return {key: sum(v) / len(v) for key, v in acc.items()}
-
-    f = per_kernel(fetch_csv, "FETCH_SIZE")
-    w = per_kernel(write_csv, "WRITE_SIZE")
-    copy_f = max(v for (k, g), v in f.items() if k == COPY_KERNEL)
-    copy_w = max(v for (k, g), v in w.items() if k == COPY_KERNEL)
-    sf, sw = (GIB / 1024) / copy_f, (GIB / 1024) / copy_w      # true KiB per counted KiB
-    cmp_ = ("compress_single_kernel", (n_units + (n_units + 7) // 8) * 512)
-    dec = ("decompress_kernel", n_units * 512)
-    kib = {k: (f[k] * sf, w[k] * sw) for k in (cmp_, dec)}
-    comp = sum(kib[cmp_])
-    decomp = sum(kib[dec])
-    lines = ["# Measured HBM traffic, bucket_64m (16 x 4 Mi BF16 values)", "",
-             "Commands (from the repository root on the GPU host), one run per counter:", "",
-             "    " + PMC_CMD.format(counter="FETCH_SIZE"), "    " + PMC_CMD.format(counter="WRITE_SIZE"), "",
-             f"Scale factors from the 1 GiB copy in the same runs: FETCH_SIZE x{sf:.4f}, WRITE_SIZE x{sw:.4f}",
-             f"(the copy counted {copy_f:.0f} KiB fetched and {copy_w:.0f} KiB written per dispatch).", "",
-             "| kernel | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
-             "|---|---|---|---|---|---|"]
-    for k in (cmp_, dec):
-        lines.append(f"| {k[0]} | {k[1]} | {f[k]:.1f} | {w[k]:.1f} | {kib[k][0] * 1024 / 1e6:.2f} | "
-                     f"{kib[k][1] * 1024 / 1e6:.2f} |")
-    lines += ["", "Machine-readable (bench.py reports these as roofline.traffic while the kernel",
-              "source hash matches; bytes per launch):", "", "```",
-              f"source_sha256={kernel_source_sha256()}",
-              f"compress_traffic_bytes={int(comp * 1024)}",
-              f"decompress_traffic_bytes={int(decomp * 1024)}", "```"]
-    open(out_path, "w").write("\n".join(lines) + "\n")
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = short_kernel_name(r["Kernel_Name"])
+        if k is None:
+            continue
+        acc.setdefault((k, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+    return {key: (sum(v) / len(v), len(v)) for key, v in acc.items()}
 
 
-RS_PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d rocprof_out/pmc_rs_{counter} -o run -- "
-              "python3 bench.py --only rs_512m")
-
-
-def summarize_pmc_rs(fetch_csv, write_csv, out_path):
-    """profiles/ text from two rocprofv3 --pmc runs of RS_PMC_CMD (FETCH_SIZE, then
-    WRITE_SIZE): HBM bytes per launch of the reduce-scatter share's kernels, per value,
-    against the algorithmic bytes (decode-accumulate: 7 peers x ~1.40 B + 2 B local + 2 B
-    out per output value; compress: 2 B in + ~1.40 B out per value).  Scaled by the
-    counters' reading of the 1 GiB copy in the same runs.  A decode-accumulate launch has a
-    workgroup per 4096 outputs; a compress launch ceil(units / 8) placing workgroups after
-    its units of 16384 values."""
-    import csv
-
-    def per_kernel(path, counter):
-        acc = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            k = short_kernel_name(r["Kernel_Name"])
-            if k is None:
-                continue
-            acc.setdefault((k, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
-        return {key: (sum(v) / len(v), len(v)) for key, v in acc.items()}
-
-    f = per_kernel(fetch_csv, "FETCH_SIZE")
-    w = per_kernel(write_csv, "WRITE_SIZE")
+def summarize_pmc_any(name, launches_json, fetch_csv, write_csv, out_path):
+    """profiles/pmc_traffic_<name>.txt from two rocprofv3 --pmc runs of pmc_cmd(name, ...)
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch): HBM bytes per launch of each of the
+    workload's kernels against its algorithmic bytes (launches_json, written by the same
+    command).  Each counter is scaled by what it reads for the 1 GiB device copy at the end
+    of the run (the copy reads and writes 1 GiB)."""
+    launches = json.load(open(launches_json))
+    f = per_kernel_counter(fetch_csv, "FETCH_SIZE")
+    w = per_kernel_counter(write_csv, "WRITE_SIZE")
     copy_f = max(v for (k, g), (v, c) in f.items() if k == COPY_KERNEL)
     copy_w = max(v for (k, g), (v, c) in w.items() if k == COPY_KERNEL)
-    sf, sw = (GIB / 1024) / copy_f, (GIB / 1024) / copy_w
-    lines = ["# Measured HBM traffic, rs_512m (7 peers x 64 Mi BF16 values, 32 chunks of 2 Mi)", "",
+    sf, sw = (GIB / 1024) / copy_f, (GIB / 1024) / copy_w      # true KiB per counted KiB
+    lines = [f"# Measured HBM traffic, {name}", "",
              "Commands (from the repository root on the GPU host), one run per counter:", "",
-             "    " + RS_PMC_CMD.format(counter="FETCH_SIZE"), "    " + RS_PMC_CMD.format(counter="WRITE_SIZE"), "",
-             f"Scale factors from the 1 GiB copy in the same runs: FETCH_SIZE x{sf:.4f}, WRITE_SIZE x{sw:.4f}.",
+             "    " + pmc_cmd(name, "FETCH_SIZE"), "    " + pmc_cmd(name, "WRITE_SIZE"), "",
+             f"Scale factors from the 1 GiB copy in the same runs: FETCH_SIZE x{sf:.4f}, WRITE_SIZE x{sw:.4f}",
+             f"(the copy counted {copy_f:.0f} KiB fetched and {copy_w:.0f} KiB written per dispatch).",
              f"Kernel source sha256: `{kernel_source_sha256()}`", "",
-             "| kernel | grid | launches | values | read MB | write MB | B per value | algorithmic B per value |",
+             "| kernel | grid | dispatches | read MB | write MB | measured MB | algorithmic MB | measured / algorithmic |",
              "|---|---|---|---|---|---|---|---|"]
-    for (k, grid) in sorted(set(f) & set(w)):
-        if k == COPY_KERNEL:
+    mr = []
+    for L in launches:
+        key = (L["kernel"], L["grid"])
+        if key not in f or key not in w:
             continue
-        (fv, nl), (wv, _) = f[(k, grid)], w[(k, grid)]
+        (fv, nd), (wv, _) = f[key], w[key]
         rd, wr = fv * sf * 1024, wv * sw * 1024
-        wgs = grid // 512
-        if k == "accumulate_kernel":
-            vals, alg = wgs * 4096, "13.80 (per output)"
-        elif k == "compress_single_kernel":
-            units = wgs - (wgs + 8) // 9   # wgs = units + ceil(units / 8)
-            while units + (units + 7) // 8 < wgs:
-                units += 1
-            vals, alg = units * 16384, "3.40"
-        else:
-            continue
-        lines.append(f"| {k} | {grid} | {nl} | {vals} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | "
-                     f"{(rd + wr) / vals:.3f} | {alg} |")
-    lines += ["", "Values per launch follow from the grid (the last chunk of a launch may be short, so",
-              "they are upper bounds for the smaller launches)."]
+        lines.append(f"| {L['kernel']} | {L['grid']} | {nd} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | {(rd + wr) / 1e6:.2f} | "
+                     f"{L['bytes'] / 1e6:.2f} | {(rd + wr) / L['bytes']:.4f} |")
+        mr.append(f"{L['kernel']}_{L['grid']}_traffic_bytes={int(rd + wr)}")
+    lines += ["", "Machine-readable (bench.py reports these as roofline.traffic while the kernel source",
+              "hash matches; bytes per launch):", "", "```", f"source_sha256={kernel_source_sha256()}"] + mr + ["```"]
     open(out_path, "w").write("\n".join(lines) + "\n")
 
+
+TCC_PASSES = ("TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_BUBBLE_sum TCC_EA0_RDREQ_128B_sum",
+              "TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum")
+
+
+def tcc_cmd(k):
+    return (f"rocprofv3 --pmc {TCC_PASSES[k]} --output-format csv -d rocprof_out/tcc{k} -o run -- "
+            "python3 bench.py --only bucket_64m --launches-out rocprof_out/launches_bucket_64m.json")
+
+
+def summarize_tcc(csv0, csv1, out_path):
+    """Appends to out_path the read bytes of each kernel by three routes, from the raw TCC
+    counters of two --pmc passes of tcc_cmd: FETCH_SIZE's own expression (128-byte requests
+    taken from TCC_BUBBLE), the request counts by size (TCC_EA0_RDREQ_128B / 64B / 32B),
+    and the DRAM read requests in 32-byte units (TCC_EA0_RDREQ_DRAM_32B)."""
+    c = {}
+    for path, names in ((csv0, TCC_PASSES[0]), (csv1, TCC_PASSES[1])):
+        for cn in names.split():
+            for key, (v, n) in per_kernel_counter(path, cn).items():
+                c.setdefault(key, {})[cn] = v
+    lines = ["", "## Cross-check of the FETCH_SIZE scale with raw TCC read-request counters", "",
+             "Commands (two passes of four TCC counters each):", "", "    " + tcc_cmd(0), "    " + tcc_cmd(1), "",
+             "Bytes read per dispatch: by FETCH_SIZE's expression (TCC_BUBBLE x 128 + other requests x 64, 32-byte "
+             "ones x 32); by request size (RDREQ_128B x 128 + RDREQ_64B x 64 + RDREQ_32B x 32); and the DRAM "
+             "read requests in 32-byte units (RDREQ_DRAM_32B x 32).  Write bytes: WRREQ_64B x 64 + other x 32.", "",
+             "| kernel | grid | FETCH_SIZE-style MB | by request size MB | DRAM 32B units MB | write MB |",
+             "|---|---|---|---|---|---|"]
+    for (k, g), d in sorted(c.items()):
+        if k not in (COPY_KERNEL, "compress_single_kernel", "decompress_kernel") or len(d) < 8:
+            continue
+        rd = d["TCC_EA0_RDREQ_sum"]
+        fs = d["TCC_BUBBLE_sum"] * 128 + (rd - d["TCC_BUBBLE_sum"] - d["TCC_EA0_RDREQ_32B_sum"]) * 64 + \
+            d["TCC_EA0_RDREQ_32B_sum"] * 32
+        bs = d["TCC_EA0_RDREQ_128B_sum"] * 128 + d["TCC_EA0_RDREQ_64B_sum"] * 64 + d["TCC_EA0_RDREQ_32B_sum"] * 32
+        dr = d["TCC_EA0_RDREQ_DRAM_32B_sum"] * 32
+        wb = d["TCC_EA0_WRREQ_64B_sum"] * 64 + (d["TCC_EA0_WRREQ_sum"] - d["TCC_EA0_WRREQ_64B_sum"]) * 32
+        lines.append(f"| {k} | {g} | {fs / 1e6:.2f} | {bs / 1e6:.2f} | {dr / 1e6:.2f} | {wb / 1e6:.2f} |")
+    open(out_path, "a").write("\n".join(lines) + "\n")
+
+
+def measured_traffic(name, kernel, grid):
+    """Bytes per launch from profiles/pmc_traffic_<name>.txt, or None if it is missing, was
+    taken on another version of the kernels, or has no row for this launch."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", f"pmc_traffic_{name}.txt")).read()
+    except OSError:
+        return None
+    kv = dict(line.split("=", 1) for line in text.splitlines() if "=" in line and " " not in line.strip())
+    if kv.get("source_sha256") != kernel_source_sha256():
+        return None
+    v = kv.get(f"{kernel}_{grid}_traffic_bytes")
+    return int(v) if v is not None else None
 
 SQ_COUNTERS = "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_BUSY_CYCLES"
 SQ_CMD = ("rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv -d rocprof_out/pmc_sq_rs -o run -- "
@@ -746,17 +847,47 @@ def summarize_sq(csv_path, out_path):
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
-def measured_traffic():
-    """Bytes per launch from the committed PMC summary, or {} if it is missing or was
-    taken on another version of the kernels."""
-    try:
-        text = open(TRAFFIC_PROFILE).read()
-    except OSError:
-        return {}
-    kv = dict(line.split("=", 1) for line in text.splitlines() if "=" in line and " " not in line.strip())
-    if kv.get("source_sha256") != kernel_source_sha256():
-        return {}
-    return {"compress": int(kv["compress_traffic_bytes"]), "decompress": int(kv["decompress_traffic_bytes"])}
+
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats -o bench -- "
+             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extra")
+
+
+def only_cmd_stats(name):
+    return (f"rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/stats_{name} -o run -- "
+            f"python3 bench.py --only {name}")
+
+
+_WL = {}
+
+
+def workload(W, name):
+    if name not in _WL:
+        _WL[name] = W.get(name)
+    return _WL[name]
+
+
+def run_only(torch, Z, W, name):
+    """One workload alone: its figures and the launches of one pass."""
+    if name in ("chunk_1m", "bucket_64m", "act_8192x7168", "moe_16384x7168"):
+        res, launches, _ = bench_codec_workload(torch, Z, W, name)
+        return res, launches
+    if name == "rs_512m":
+        rs = RSShare(torch, Z, W)
+        res = bench_rs_extra(torch, Z, rs, 5)
+        return res, rs.launches()
+    if name == "moe_routed_16384x7168":
+        return bench_moe_gather(torch, Z, W, 5), []
+    if name == "allgather_16x4m":
+        return bench_allgather(torch, Z, W, 5), []
+    if name == "bucket_64m_estimated_plans":
+        return bench_estimated_plans(torch, Z, W, 5), []
+    if name == "rs_switcher":
+        return bench_switcher(torch, Z, W), []
+    raise KeyError(name)
+
+
+ONLY_NAMES = ("chunk_1m", "bucket_64m", "act_8192x7168", "moe_16384x7168", "moe_routed_16384x7168",
+              "allgather_16x4m", "rs_512m", "bucket_64m_estimated_plans", "rs_switcher")
 
 
 def main(argv=None) -> int:
@@ -764,38 +895,38 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (> 2)")
+    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets of the bucket (> 2)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
-    ap.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
-                    help="write a profiles/ summary of a rocprofv3 --stats run and exit")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
-                    help="write a profiles/ summary of two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--summarize-rs-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
-                    help="write a profiles/ summary of a rocprofv3 --stats run of --only rs_512m and exit")
-    ap.add_argument("--summarize-rs-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
-                    help="write a profiles/ summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "--only rs_512m and exit")
+    ap.add_argument("--only", default=None, choices=ONLY_NAMES,
+                    help="run one workload alone (for profiling) and print its figures")
+    ap.add_argument("--launches-out", default=None, help="with --only: write the pass's launches (JSON) here")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("NAME", "KERNEL_STATS_CSV", "OUT_MD"),
+                    help="profiles/ summary of a rocprofv3 --stats run (NAME: headline, or the --only workload)")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("NAME", "LAUNCHES_JSON", "FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="profiles/ summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --only NAME")
+    ap.add_argument("--summarize-tcc", nargs=3, metavar=("CSV0", "CSV1", "OUT_MD"),
+                    help="append the raw TCC read-request cross-check to a traffic summary")
     ap.add_argument("--summarize-sq", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
-                    help="write a profiles/ summary of a rocprofv3 SQ-counter run of --only rs_512m and exit")
-    ap.add_argument("--only", default=None,
-                    help="run one of the other workloads alone (for profiling) and print its figures")
+                    help="profiles/ summary of a rocprofv3 SQ-counter run of --only rs_512m")
     args = ap.parse_args(argv)
     if args.summarize_stats:
-        summarize_stats(*args.summarize_stats)
+        name, csv_path, out = args.summarize_stats
+        if name == "headline":
+            summarize_stats_any(csv_path, out, "headline step (rs_512m: 7 peers x 64 Mi values in 32 chunks of 2 Mi, "
+                                "compress + decode-accumulate)", TRACE_CMD)
+        else:
+            summarize_stats_any(csv_path, out, name, only_cmd_stats(name))
         return 0
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc_any(*args.summarize_pmc)
         return 0
-    if args.summarize_rs_stats:
-        summarize_stats(*args.summarize_rs_stats, rs=True)
+    if args.summarize_tcc:
+        summarize_tcc(*args.summarize_tcc)
         return 0
     if args.summarize_sq:
         summarize_sq(*args.summarize_sq)
-        return 0
-    if args.summarize_rs_pmc:
-        summarize_pmc_rs(*args.summarize_rs_pmc)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the codec's hot path is single-GPU and there is no "
@@ -811,51 +942,51 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
 
     if args.only:
-        runners = {"rs_512m": lambda: bench_rs(torch, Z, W, 5),
-                   "rs_switcher": lambda: bench_switcher(torch, Z, W),
-                   "bucket_64m_estimated_plans": lambda: bench_estimated_plans(torch, Z, W, 5),
-                   "allgather_16x4m": lambda: bench_allgather(torch, Z, W, 5),
-                   "moe_routed_16384x7168": lambda: bench_moe_gather(torch, Z, W, 5)}
-        if args.only not in runners:
-            print(f"--only takes one of {sorted(runners)}", file=sys.stderr)
-            return 2
-        res = runners[args.only]()
+        res, launches = run_only(torch, Z, W, args.only)
+        if args.launches_out:
+            os.makedirs(os.path.dirname(os.path.abspath(args.launches_out)), exist_ok=True)
+            json.dump(launches, open(args.launches_out, "w"))
         # the 1 GiB copy whose counter readings scale a --pmc run of this command
         print(json.dumps({"workload": args.only, **res, "hbm_copy_GBps": copy_ceiling(torch)}), flush=True)
         return 0
 
-    log("generating bucket_64m")
-    wl = W.bucket_64m()
-    bc = BatchCodec(torch, Z, wl.segments, wl.sigmas, args.sets)
-    n = bc.n
-
+    # ---- the headline step: the reduce-scatter receive share ----
+    log("generating rs_512m")
+    rs = RSShare(torch, Z, W)
+    P, n = rs.P, rs.n
     log(f"warmup {args.warmup}, timing {args.steps} steps")
-    ms_per_step = run_codec(torch, bc, args.steps, args.warmup)
-    value = 4 * n / (ms_per_step * 1e-3) / 1e9
-    # per-launch averages (roofline, per-operation figures): back-to-back launches over
-    # the rotating sets
-    c_avg, d_avg = op_times(torch, bc, max(2, args.steps // len(bc.sets)))
-    ok = bc.verify()
-    rep = codec_report(bc, c_avg, d_avg)
-    n_esc = bc.n_esc_total()
-    moved = compress_bytes(n, bc.static_bytes, n_esc)
-
-    traffic = measured_traffic()
-
-    def roof(name, op, avg_ms, launches):
-        ach = moved / (avg_ms * 1e-3) / 1e9
-        return {"bound": "hbm", "kernel": name, "launches": launches, "achieved": round(ach, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                "bytes_per_launch": moved, "avg_launch_us": round(avg_ms * 1e3, 2), "traffic": traffic.get(op)}
-
-    # the step's dominant operation: decompress is one launch; so is compress
-    # (compress_single_kernel; encode_kernel, scan_kernel, place_kernel above 2^28 values)
-    units = sum((m + 16383) // 16384 for m in bc.sizes)
-    c_launches = (["compress_single_kernel"] if units <= 16384
-                  else ["encode_kernel", "scan_kernel", "place_kernel"])
-    roof_d = roof("decompress_kernel", "decompress", d_avg, ["decompress_kernel"])
-    roof_c = roof("compress", "compress", c_avg, c_launches)
-    primary, secondary = (roof_d, roof_c) if d_avg >= c_avg else (roof_c, roof_d)
+    for _ in range(args.warmup):
+        rs.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rs.step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    value = 4 * P * n / (ms_per_step * 1e-3) / 1e9
+    ok = rs.check()
+    # per-launch averages for the roofline: each sequence alone, back-to-back passes
+    # between two HIP events on the launch stream (median of three batches)
+    plans = rs.plans()
+    rounds = max(2, args.steps // 3)
+    c_ms = median([batched_ms(torch, lambda k: rs.compress_all(plans), 1, rounds) for _ in range(3)])
+    a_ms = median([batched_ms(torch, lambda k: rs.accumulate_all(), 1, rounds) for _ in range(3)])
+    lc, la = rs.launches()
+    c_launch_ms = c_ms / lc["per_step"]
+    a_launch_ms = a_ms / la["per_step"]
+    c_bytes = rs.compress_bytes() / lc["per_step"]
+    a_bytes = rs.accumulate_bytes() / la["per_step"]
+    roof_c = {"bound": "hbm", "kernel": "compress_single_kernel", "achieved": round(c_bytes / (c_launch_ms * 1e-3) / 1e9, 1),
+              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(c_bytes / (c_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+              "traffic": measured_traffic("rs_512m", lc["kernel"], lc["grid"]),
+              "bytes_per_launch": int(c_bytes), "avg_launch_us": round(c_launch_ms * 1e3, 2),
+              "launches_per_step": lc["per_step"], "values_per_launch": lc["values"]}
+    roof_a = {"bound": "hbm", "kernel": "accumulate_kernel", "achieved": round(a_bytes / (a_launch_ms * 1e-3) / 1e9, 1),
+              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(a_bytes / (a_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+              "traffic": None, "bytes_per_launch": int(a_bytes), "avg_launch_us": round(a_launch_ms * 1e3, 2),
+              "launches_per_step": la["per_step"],
+              "note": "launches hold 18 and 14 chunks of 7 peers; bytes and time are per launch on average"}
+    total_esc = rs.total_esc()
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -867,39 +998,52 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "bucket_64m: gradient bucket of 16 layers x 4194304 BF16 values, "
-                               "N(0, sigma_l), sigma_l log-uniform in [1e-4, 1e-1], one table per layer",
-                   "elements": n, "segments": len(bc.sizes), "rotating_sets": args.sets},
-        "compress_GBps": rep["compress_GBps"],
-        "decompress_GBps": rep["decompress_GBps"],
-        "compress_hbm_frac": rep["compress_hbm_frac"],
-        "decompress_hbm_frac": rep["decompress_hbm_frac"],
-        "ratio": rep["ratio"],
-        "bits_per_value": rep["bits_per_value"],
-        "escape_frac": rep["escape_frac"],
-        "parity_round_trip": ok,
-        "roofline": primary,
-        "roofline_other_op": secondary,
+        "config": {"workload": "rs_512m: reduce-scatter receive share, 7 peer shards x 67108864 BF16 values "
+                               "N(0, 1e-3) compressed in 32 chunks of 2097152 values (8 chunks per launch), then "
+                               "decoded and added in fp32, peers in order, into the local shard N(0, 1e-3), one "
+                               "BF16 rounding",
+                   "elements_per_peer": n, "peers": P, "chunk": rs.chunk, "chunks": rs.nch},
+        "compress_GBps": round(2 * P * n / (c_ms * 1e-3) / 1e9, 1),
+        "accumulate_GBps_bf16_in": round(2 * P * n / (a_ms * 1e-3) / 1e9, 1),
+        "compress_hbm_frac": roof_c["frac"],
+        "accumulate_hbm_frac": roof_a["frac"],
+        "ratio": round(2 * P * n / (rs.nch * P * rs.S + total_esc), 5),
+        "bits_per_value": round(8 * (rs.nch * P * rs.S + total_esc) / (P * n), 4),
+        "escape_frac": round(total_esc / (P * n), 5),
+        "parity_vs_torch_fp32": ok,
+        "roofline": roof_c,
+        "roofline_other_op": roof_a,
     }
     log("copy ceiling")
     out["hbm_copy_GBps"] = copy_ceiling(torch)
     out["roofline"]["frac_of_copy"] = round(out["roofline"]["achieved"] / out["hbm_copy_GBps"], 4)
+    from oracle import oracle as O
     if not args.no_extra:
-        per = {"bucket_64m": rep}
+        per = {}
+        log("workload bucket_64m")
+        wl = workload(W, "bucket_64m")
+        bc = BatchCodec(torch, Z, wl.segments, wl.sigmas, args.sets)
+        step_ms = run_codec(torch, bc, 10, 3)
+        cm, dm = op_times(torch, bc, max(2, args.steps // len(bc.sets)))
+        r = codec_report(bc, cm, dm)
+        r["step_GBps"] = round(4 * bc.n / (step_ms * 1e-3) / 1e9, 1)
+        r["parity_round_trip"] = bc.verify()
+        r["compress_traffic_bytes"] = measured_traffic("bucket_64m", *[(L["kernel"], L["grid"]) for L in
+                                                                        codec_launches(bc, bc.n_esc_total())][0])
+        r["decompress_traffic_bytes"] = measured_traffic("bucket_64m", *[(L["kernel"], L["grid"]) for L in
+                                                                          codec_launches(bc, bc.n_esc_total())][1])
+        per["bucket_64m"] = r
+        del bc
+        torch.cuda.empty_cache()
         for name in ("chunk_1m", "act_8192x7168", "moe_16384x7168"):
             log(f"workload {name}")
-            w2 = W.get(name)
-            sets = 8 if name == "chunk_1m" else 4
-            b2 = BatchCodec(torch, Z, w2.segments, w2.sigmas, sets)
-            run_codec(torch, b2, 3, 3)
-            cm, dm = op_times(torch, b2, 5)
-            r2 = codec_report(b2, cm, dm)
-            r2["parity_round_trip"] = b2.verify()
+            r2, launches, w2 = bench_codec_workload(torch, Z, W, name)
+            r2["compress_traffic_bytes"] = measured_traffic(name, launches[0]["kernel"], launches[0]["grid"])
+            r2["decompress_traffic_bytes"] = measured_traffic(name, launches[1]["kernel"], launches[1]["grid"])
+            _WL[name] = w2
             per[name] = r2
-            del b2
-            torch.cuda.empty_cache()
         log("workload moe_routed_16384x7168")
         per["moe_routed_16384x7168"] = bench_moe_gather(torch, Z, W, 5)
         torch.cuda.empty_cache()
@@ -909,15 +1053,20 @@ def main(argv=None) -> int:
         log("workload allgather_16x4m")
         per["allgather_16x4m"] = bench_allgather(torch, Z, W, 5)
         torch.cuda.empty_cache()
-        log("workload rs_512m")
-        per["rs_512m"] = bench_rs(torch, Z, W, 5)
+        log("workload rs_512m (per operation, pipeline)")
+        per["rs_512m"] = bench_rs_extra(torch, Z, rs, 5)
         log("reduce-scatter switcher")
         per["rs_switcher"] = bench_switcher(torch, Z, W)
         out["per_config"] = per
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle, 1 thread)")
-        from oracle import oracle as O
-        out["cpu_baseline"] = cpu_baseline(W, O, wl, args.cpu_reps)
+        log("cpu baseline (oracle): reduce-scatter share sample")
+        out["cpu_baseline"] = oracle_rs(O, W, chunks=4, reps=args.cpu_reps)
+        if "per_config" in out:
+            out["per_config"]["rs_512m"]["oracle"] = out["cpu_baseline"]
+            for name in ("chunk_1m", "bucket_64m", "act_8192x7168", "moe_16384x7168"):
+                log(f"oracle on {name}")
+                wl = workload(W, name)
+                out["per_config"][name]["oracle"] = oracle_codec(O, wl.segments, wl.sigmas)
     print(json.dumps(out), flush=True)
     return 0 if ok else 1
 

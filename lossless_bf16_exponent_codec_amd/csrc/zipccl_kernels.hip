@@ -1208,7 +1208,11 @@ __device__ inline uint32_t patch_second_escape(uint32_t E, uint32_t z, uint32_t 
 {
     const uint32_t rest = z & (z - 1);          // flags after the first
     const uint32_t second = rest & (0u - rest); // the lowest of them (0 if none)
-    const uint32_t mask = (second << 8) - second;   // its byte (full-rate ops, no 32-bit multiply)
+    // its byte as (second << 8) - second: the empty asm keeps the compiler from folding
+    // it into a multiply by 255, a quarter-rate instruction
+    uint32_t up = second << 8;
+    asm("" : "+v"(up));
+    const uint32_t mask = up - second;
     return (E & ~mask) | (perm(x, x, 0u) & mask);   // x in every byte
 }
 
@@ -1334,11 +1338,10 @@ void accumulate_kernel(const AArgs a)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // the workgroup's chunk, and its block within the chunk
     const uint32_t P = uint32_t(a.npeers);
-    const uint32_t bpc = uint32_t(blocks_of(a.chunk));
-    const uint32_t c = blockIdx.x / bpc;
-    const uint32_t b = blockIdx.x - c * bpc;
+    const uint32_t c = blockIdx.y, b = blockIdx.x;   // one grid row per chunk
     const uint64_t first = uint64_t(c) * a.chunk;
     const uint32_t n = uint32_t(min<uint64_t>(a.chunk, a.n - first));
+    if (b >= uint32_t(blocks_of(n))) return;         // the last chunk's row is longer than it
     const uint8_t* const* peer_st = a.st + c * P;
     const uint8_t* const* peer_esc = a.esc + c * P;
     const uint64_t* peer_eb = a.esc_bytes + c * P;
@@ -1348,7 +1351,8 @@ void accumulate_kernel(const AArgs a)
     const uint32_t t = b * 8 + wave;
     const bool has_tile = t < T;
     const uint64_t i0 = uint64_t(t) * kTile + 8ull * lane;
-    const uint32_t nvalid = (!has_tile || i0 >= n) ? 0u : uint32_t(min<uint64_t>(8, n - i0));
+    const uint32_t rem = has_tile ? n - t * kTile : 0u;   // values from the tile's start on (32-bit, no overflow)
+    const uint32_t nvalid = rem > 8 * lane ? min(8u, rem - 8 * lane) : 0u;
     const uint32_t pdw = decoder_plane_dword(lane);
 
     // ---- requests ----
@@ -1359,7 +1363,7 @@ void accumulate_kernel(const AArgs a)
     // escape heads are still on their way.  Plane dwords first, then A bytes, then local.
     const uint8_t* const safe = peer_st[0];
     const uint32_t tl = has_tile ? t : T - 1;   // T >= 1: a launch has at least one block
-    const uint32_t pdl = pdw == ~0u ? 0u : pdw;   // lanes with p = 3: any dword (bits unused)
+    const uint32_t pdl = pdw == ~0u ? 0u : 4 * pdw;   // byte offset; lanes with p = 3: any dword (bits unused)
     // Up to 8 peers the launch picks the instance of exactly npeers: every slot exists, so
     // the peers' pointers are read with no clamp and their loads go out together rather
     // than one after another.
@@ -1370,7 +1374,7 @@ void accumulate_kernel(const AArgs a)
     uint2 Ap[kPeers];
 #pragma unroll
     for (int p = 0; p < kPeers; p++)
-        pw[p] = load_nt(reinterpret_cast<const uint32_t*>(stp[p] + planes_off(n) + 192ull * tl) + pdl);
+        pw[p] = load_nt(reinterpret_cast<const uint32_t*>(stp[p] + planes_off(n) + 192ull * tl + pdl));
 #pragma unroll
     for (int p = 0; p < kPeers; p++)
         Ap[p] = load_nt(reinterpret_cast<const uint2*>(stp[p] + 128 + 512ull * tl + 8 * lane));
@@ -1597,13 +1601,13 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(const DArgs a)
     // first, in straight-line code (tiles past the segment's last re-read it, lanes with
     // no plane dword read dword 0), so each transpose waits only for its own dword.
     const uint32_t T1 = T - 1;   // n >= 1: a segment with no values has no units
-    const uint32_t pdl = pdw == ~0u ? 0u : pdw;
+    const uint32_t pdl = pdw == ~0u ? 0u : 4 * pdw;   // byte offset
     uint2 Ap[kDecHalfTiles];
     uint32_t pw[kDecHalfTiles];
 #pragma unroll
     for (int k = 0; k < int(kDecHalfTiles); k++) {
         const uint32_t t = min(hb * kDecHalfTiles + k, T1);
-        pw[k] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t) + pdl);
+        pw[k] = load_nt(reinterpret_cast<const uint32_t*>(st + planes_off(n) + 192ull * t + pdl));
     }
 #pragma unroll
     for (int k = 0; k < int(kDecHalfTiles); k++) {
@@ -1885,21 +1889,21 @@ hipError_t launch_decompress(const DArgs& a, hipStream_t s)
 hipError_t launch_accumulate(const AArgs& a, hipStream_t s)
 {
     if (a.n == 0 || a.nchunks < 1) return hipSuccess;
-    const uint64_t last = a.n - uint64_t(a.nchunks - 1) * a.chunk;   // values of the last chunk
-    const uint32_t grid = uint32_t(uint64_t(a.nchunks - 1) * blocks_of(a.chunk) + blocks_of(last));
-    if (grid == 0) return hipSuccess;
+    // one grid row per chunk; a row holds a full chunk's blocks (the last chunk's surplus
+    // workgroups return at once)
+    const dim3 grid(uint32_t(blocks_of(a.nchunks > 1 ? a.chunk : a.n)), uint32_t(a.nchunks));
     // every peer slot of the instance issues its loads, so up to 8 peers the instance
     // holds exactly npeers
     switch (a.npeers) {
-        case 1: hipLaunchKernelGGL(accumulate_kernel<1>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(accumulate_kernel<2>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        case 3: hipLaunchKernelGGL(accumulate_kernel<3>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(accumulate_kernel<4>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        case 5: hipLaunchKernelGGL(accumulate_kernel<5>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        case 6: hipLaunchKernelGGL(accumulate_kernel<6>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        case 7: hipLaunchKernelGGL(accumulate_kernel<7>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        case 8: hipLaunchKernelGGL(accumulate_kernel<8>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL(accumulate_kernel<kMaxPeers>, dim3(grid), dim3(kAccThreads), 0, s, a); break;
+        case 1: hipLaunchKernelGGL(accumulate_kernel<1>, grid, dim3(kAccThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(accumulate_kernel<2>, grid, dim3(kAccThreads), 0, s, a); break;
+        case 3: hipLaunchKernelGGL(accumulate_kernel<3>, grid, dim3(kAccThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(accumulate_kernel<4>, grid, dim3(kAccThreads), 0, s, a); break;
+        case 5: hipLaunchKernelGGL(accumulate_kernel<5>, grid, dim3(kAccThreads), 0, s, a); break;
+        case 6: hipLaunchKernelGGL(accumulate_kernel<6>, grid, dim3(kAccThreads), 0, s, a); break;
+        case 7: hipLaunchKernelGGL(accumulate_kernel<7>, grid, dim3(kAccThreads), 0, s, a); break;
+        case 8: hipLaunchKernelGGL(accumulate_kernel<8>, grid, dim3(kAccThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL(accumulate_kernel<kMaxPeers>, grid, dim3(kAccThreads), 0, s, a); break;
     }
     return hipGetLastError();
 }
