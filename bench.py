@@ -8,7 +8,9 @@ local shard.  Plan the 7 tables on the host, compress the peer shards in 32 chun
 launch), then decode the 7 compressed shards of every chunk and add them in fp32, in
 peer order, to the local shard, rounding once to BF16.  Inputs are resident in HBM
 before the timed region; the step's working set (~1.7 GB) is far larger than the
-256 MB Infinity Cache.
+256 MB Infinity Cache.  Every timed measurement comes after the same work has run
+untimed for a few tenths of a second: an idle GPU sits at a low clock and the first
+milliseconds of load run at ramping clocks.
 
 Printed (one JSON line on stdout):
   value      BF16 bytes handled per second by the step: (2 x 7n compressed + 2 x 7n
@@ -150,6 +152,7 @@ def run_codec(torch, bc, iters, warmup):
     plans = bc.plans()
     for i in range(-LAG, 0):
         bc.compress(i % R, plans)
+    settle(torch, lambda k: (bc.compress(k % R, plans), bc.decompress((k - LAG) % R)))
     for i in range(warmup):
         bc.compress(i % R, plans)
         bc.decompress((i - LAG) % R)
@@ -175,14 +178,33 @@ def op_times(torch, bc, rounds, batches=3):
     return median(cs), median(ds)
 
 
+SETTLE_S = 0.3   # untimed work before each timed measurement, in seconds
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Run fn(k) back to back, untimed, for `seconds` of wall time.  An idle MI355X sits
+    at a low shader clock (about 160 MHz read by amd-smi) and raises it only under
+    sustained load; a batch timed right after host work (generating a workload) ran
+    partly at ramping clocks, up to 38 % slower than the same kernels under continuous
+    load, which held their time for 45 s.  The first launch of a kernel also loads it."""
+    t_end = time.perf_counter() + seconds
+    k = 0
+    while True:
+        fn(k)
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() >= t_end:
+                break
+    torch.cuda.synchronize()
+
+
 def batched_ms(torch, fn, sets, rounds):
     """Average time of one launch of fn(k) over rounds x sets back-to-back launches on
     the rotating sets, from two HIP events on the launch stream around the whole batch
-    (the events' own latency is then not counted per launch).  One untimed round comes
-    first: the first launch of a kernel also loads it."""
-    for k in range(sets):
-        fn(k)
-    torch.cuda.synchronize()
+    (the events' own latency is then not counted per launch), after the same launches
+    have run untimed until the clock has settled."""
+    settle(torch, lambda k: fn(k % sets))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(rounds):
@@ -284,18 +306,34 @@ class RSShare:
             ok = ok and bool(torch.equal(acc.to(torch.bfloat16).view(torch.int16), self.dst[sl].view(torch.int16)))
         return ok
 
+    def accumulate_traffic_per_launch(self):
+        """Measured HBM bytes of the decode-accumulate launches of one pass, per launch on
+        average (the launches hold different numbers of chunks), or None."""
+        per_acc = 128 // self.P
+        grids = [(self.chunk // 4096) * 512 * min(per_acc, self.nch - c0) for c0 in range(0, self.nch, per_acc)]
+        t = [measured_traffic("rs_512m", "accumulate_kernel", g) for g in grids]
+        return None if None in t else int(sum(t) / len(t))
+
     def launches(self):
         """Kernel launches of one step, for the counter summaries: kernel, grid size in
-        work-items, launches per step, algorithmic bytes per launch."""
+        work-items, launches per step, algorithmic bytes per launch.  Decode-accumulate
+        launches hold 128 / 7 = 18 chunks each, the last one the rest (14)."""
         units = self.per_launch * self.P * ((self.chunk + 16383) // 16384)
         nl_c = self.nch // self.per_launch
+        out = [{"kernel": "compress_single_kernel", "grid": (units + (units + 7) // 8) * 512, "per_step": nl_c,
+                "bytes": self.compress_bytes() / nl_c, "values": self.per_launch * self.P * self.chunk}]
         per_acc = 128 // self.P
-        nl_a = -(-self.nch // per_acc)
-        return [{"kernel": "compress_single_kernel", "grid": (units + (units + 7) // 8) * 512, "per_step": nl_c,
-                 "bytes": self.compress_bytes() / nl_c, "values": self.per_launch * self.P * self.chunk},
-                {"kernel": "accumulate_kernel", "grid": (self.chunk // 4096) * 512 * per_acc, "per_step": nl_a,
-                 "bytes": self.accumulate_bytes() / self.nch * per_acc, "values": per_acc * self.chunk,
-                 "note": "grid and bytes of a full launch (the last one holds the remaining chunks)"}]
+        shapes = {}
+        for c0 in range(0, self.nch, per_acc):
+            k = min(per_acc, self.nch - c0)
+            shapes[k] = shapes.get(k, 0) + 1
+        for k, count in shapes.items():
+            out.append({"kernel": "accumulate_kernel", "grid": (self.chunk // 4096) * 512 * k, "per_step": count,
+                        "bytes": self.accumulate_bytes() / self.nch * k, "values": k * self.chunk})
+        return out
+
+    def accumulate_launches_per_step(self):
+        return -(-self.nch // (128 // self.P))
 
 
 def bench_rs_extra(torch, Z, rs, iters):
@@ -395,13 +433,15 @@ def bench_allgather(torch, Z, W, rounds):
     ok = int(status.item()) == 0
     ok = ok and all(bool(torch.equal(s["out"].view(torch.int16), want.view(torch.int16))) for s in sets)
     moved = sum(Z.static_size(m) for m in sizes) + n_esc + 2 * n
+    blocks = sum((m + 4095) // 4096 for m in sizes)
+    launches = [{"kernel": "decompress_kernel", "grid": blocks * 128, "per_step": 1, "bytes": moved, "values": n}]
     return {
         "elements": n, "shards": len(sizes),
         "decompress_us": round(d * 1e3, 2),
         "decompress_GBps": round(2 * n / (d * 1e-3) / 1e9, 1),
         "decompress_hbm_frac": round(moved / (d * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "parity_round_trip": ok,
-    }
+    }, launches
 
 
 def bench_moe_gather(torch, Z, W, rounds):
@@ -463,6 +503,11 @@ def bench_moe_gather(torch, Z, W, rounds):
     ok = (int(status.item()) == 0 and bool(torch.equal(st_g, s0["st"]))
           and bool(torch.equal(esc_g, s0["esc"][:total_esc])))
     moved = compress_bytes(n, static_bytes, total_esc)
+    units = sum((m + 16383) // 16384 for m in sizes)
+    launches = [{"kernel": "compress_single_kernel", "grid": (units + (units + 7) // 8) * 512, "per_step": 1,
+                 "bytes": moved, "values": n,
+                 "note": "the gathered compress and the compress of the permuted copy launch this kernel with "
+                         "the same grid and move the same algorithmic bytes; the counters average both"}]
     return {
         "elements": n, "segments": len(sizes),
         "gather_compress_us": round(g * 1e3, 2),
@@ -472,7 +517,7 @@ def bench_moe_gather(torch, Z, W, rounds):
         "compress_permuted_us": round(cp * 1e3, 2),
         "permute_plus_compress_us": round((pm + cp) * 1e3, 2),
         "parity_vs_permuted": ok,
-    }
+    }, launches
 
 
 def bench_switcher(torch, Z, W):
@@ -541,8 +586,7 @@ def copy_ceiling(torch, iters=10):
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
+    settle(torch, lambda k: b.copy_(a))
     t = Timer(torch)
     for _ in range(iters):
         e = t.start()
@@ -876,9 +920,9 @@ def run_only(torch, Z, W, name):
         res = bench_rs_extra(torch, Z, rs, 5)
         return res, rs.launches()
     if name == "moe_routed_16384x7168":
-        return bench_moe_gather(torch, Z, W, 5), []
+        return bench_moe_gather(torch, Z, W, 5)
     if name == "allgather_16x4m":
-        return bench_allgather(torch, Z, W, 5), []
+        return bench_allgather(torch, Z, W, 5)
     if name == "bucket_64m_estimated_plans":
         return bench_estimated_plans(torch, Z, W, 5), []
     if name == "rs_switcher":
@@ -955,6 +999,7 @@ def main(argv=None) -> int:
     rs = RSShare(torch, Z, W)
     P, n = rs.P, rs.n
     log(f"warmup {args.warmup}, timing {args.steps} steps")
+    settle(torch, lambda k: rs.step(), 2 * SETTLE_S)   # untimed: the clock comes up first
     for _ in range(args.warmup):
         rs.step()
     torch.cuda.synchronize()
@@ -971,11 +1016,12 @@ def main(argv=None) -> int:
     rounds = max(2, args.steps // 3)
     c_ms = median([batched_ms(torch, lambda k: rs.compress_all(plans), 1, rounds) for _ in range(3)])
     a_ms = median([batched_ms(torch, lambda k: rs.accumulate_all(), 1, rounds) for _ in range(3)])
-    lc, la = rs.launches()
+    lc = rs.launches()[0]
+    nl_a = rs.accumulate_launches_per_step()
     c_launch_ms = c_ms / lc["per_step"]
-    a_launch_ms = a_ms / la["per_step"]
+    a_launch_ms = a_ms / nl_a
     c_bytes = rs.compress_bytes() / lc["per_step"]
-    a_bytes = rs.accumulate_bytes() / la["per_step"]
+    a_bytes = rs.accumulate_bytes() / nl_a
     roof_c = {"bound": "hbm", "kernel": "compress_single_kernel", "achieved": round(c_bytes / (c_launch_ms * 1e-3) / 1e9, 1),
               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(c_bytes / (c_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
               "traffic": measured_traffic("rs_512m", lc["kernel"], lc["grid"]),
@@ -983,9 +1029,10 @@ def main(argv=None) -> int:
               "launches_per_step": lc["per_step"], "values_per_launch": lc["values"]}
     roof_a = {"bound": "hbm", "kernel": "accumulate_kernel", "achieved": round(a_bytes / (a_launch_ms * 1e-3) / 1e9, 1),
               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(a_bytes / (a_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-              "traffic": None, "bytes_per_launch": int(a_bytes), "avg_launch_us": round(a_launch_ms * 1e3, 2),
-              "launches_per_step": la["per_step"],
-              "note": "launches hold 18 and 14 chunks of 7 peers; bytes and time are per launch on average"}
+              "traffic": rs.accumulate_traffic_per_launch(), "bytes_per_launch": int(a_bytes),
+              "avg_launch_us": round(a_launch_ms * 1e3, 2),
+              "launches_per_step": nl_a,
+              "note": "launches hold 18 and 14 chunks of 7 peers; bytes, time and traffic are per launch on average"}
     total_esc = rs.total_esc()
     out = {
         "metric": METRIC,
@@ -1045,13 +1092,17 @@ def main(argv=None) -> int:
             _WL[name] = w2
             per[name] = r2
         log("workload moe_routed_16384x7168")
-        per["moe_routed_16384x7168"] = bench_moe_gather(torch, Z, W, 5)
+        r3, l3 = bench_moe_gather(torch, Z, W, 5)
+        r3["gather_compress_traffic_bytes"] = measured_traffic("moe_routed_16384x7168", l3[0]["kernel"], l3[0]["grid"])
+        per["moe_routed_16384x7168"] = r3
         torch.cuda.empty_cache()
         log("bucket with plans estimated on the device")
         per["bucket_64m_estimated_plans"] = bench_estimated_plans(torch, Z, W, 5)
         torch.cuda.empty_cache()
         log("workload allgather_16x4m")
-        per["allgather_16x4m"] = bench_allgather(torch, Z, W, 5)
+        r4, l4 = bench_allgather(torch, Z, W, 5)
+        r4["decompress_traffic_bytes"] = measured_traffic("allgather_16x4m", l4[0]["kernel"], l4[0]["grid"])
+        per["allgather_16x4m"] = r4
         torch.cuda.empty_cache()
         log("workload rs_512m (per operation, pipeline)")
         per["rs_512m"] = bench_rs_extra(torch, Z, rs, 5)
