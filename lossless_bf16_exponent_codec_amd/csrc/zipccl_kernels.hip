@@ -1078,12 +1078,18 @@ __global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs
 // Compress in one launch: workgroups 0 .. total_units - 1 encode (as encode_kernel) and
 // publish each unit's escape count in its ready word; the last ceil(total_units / 8)
 // place (as place_direct_kernel) once the ready words they need carry this call's tag.
+// Placers are dispatched last group first: the group with the most ready words to read
+// (all units before it) starts while the last encoders still run, so only the last few
+// words are left to wait for when they finish; the early groups, dispatched last, read
+// few words.  (In group order the last placer started when the last encoders ended and
+// then read all 7168 words of a 117 Mi-value launch in rounds: 5.4 us of the launch's
+// 7.7 us after its last encoder.)
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void compress_single_kernel(const CArgs a)
 {
     static_assert(kEncThreads == kPlaceThreads, "both roles use the same workgroup size");
     if (blockIdx.x < a.total_units) encode_unit<true>(a, blockIdx.x);
-    else place_group<true>(a, blockIdx.x - a.total_units);
+    else place_group<true>(a, gridDim.x - 1 - blockIdx.x);
 }
 
 
