@@ -1234,6 +1234,24 @@ __device__ inline LaneBytes assemble_lane(uint2 A, uint32_t E0, uint32_t E1)
     return o;
 }
 
+// Every byte rotated right by one bit: exponent bit 0 to bit 7, bits 1-7 down by one,
+// i.e. the bits of the BF16 low byte's top bit and of the high byte's low 7 bits.
+__device__ inline uint32_t rotr1_bytes(uint32_t x) { return ((x >> 1) & 0x7F7F7F7Fu) | ((x << 7) & 0x80808080u); }
+// the low byte of x twice (v_perm), shifted right by one
+__device__ inline uint8_t rotr1_byte(uint32_t x) { return uint8_t(perm(x, x, 0x0C0C0000u) >> 1); }
+
+// The same from exponent bytes already rotated by rotr1 (R0 / R1): each output byte is a
+// bit select of an A byte and a rotated exponent byte, with no shift.
+__device__ inline LaneBytes assemble_lane_rot(uint2 A, uint32_t R0, uint32_t R1)
+{
+    LaneBytes o;
+    o.lo0 = (A.x & 0x7F7F7F7Fu) | (R0 & 0x80808080u);
+    o.hi0 = (A.x & 0x80808080u) | (R0 & 0x7F7F7F7Fu);
+    o.lo1 = (A.y & 0x7F7F7F7Fu) | (R1 & 0x80808080u);
+    o.hi1 = (A.y & 0x80808080u) | (R1 & 0x7F7F7F7Fu);
+    return o;
+}
+
 // Exponent bytes of this lane's 8 values in a tile of an uncoded block (values 0-3 in
 // .x, 4-7 in .y): those of the tile's first 192 values from its 192 plane bytes (lanes
 // 0..23), the others from the escape buffer, where the tile's bytes start at esc (byte by
@@ -1260,17 +1278,23 @@ __device__ inline uint32_t block_overflow(uint32_t n, uint32_t b)
     return overflow_of(b < full ? kBlock : (b == full ? n % kBlock : 0u));
 }
 
+template <bool kRot = false>
 __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint32_t tlo, uint32_t thi, uint32_t r,
                                         const uint8_t* esc_lds)
 {
-    const uint32_t z0 = z & 0x01010101u, z1 = (z >> 4) & 0x01010101u;
-    const uint32_t n0 = __builtin_popcount(z0), n1 = __builtin_popcount(z1);
+    // byte b of z holds column b's flag in bit 0 and column b + 4's in bit 4, so the sum
+    // of z's bytes (one v_sad_u8 against 0) is n0 + 16 n1: the escapes of each group of
+    // 4 columns, at most 4 each
+    const uint32_t s = __builtin_amdgcn_sad_u8(z, 0u, 0u);
+    const uint32_t n0 = s & 0xFu;
     // a code 0 selects table byte 0: the first escape of each group of 4 columns goes
     // there, so a group with at most one escape decodes with one v_perm
     const uint32_t x0 = esc_lds[r], x1 = esc_lds[r + n0];
     uint32_t E0 = perm(thi, tlo | x0, row & 0x07070707u);
     uint32_t E1 = perm(thi, tlo | x1, (row >> 4) & 0x07070707u);
-    if (n0 > 1 || n1 > 1) {   // rare: several escapes among 4 columns of the lane
+    if (s & 0x66u) {   // rare: n0 or n1 is 2, 3 or 4 (several escapes among 4 columns of the lane)
+        const uint32_t z0 = z & 0x01010101u, z1 = (z >> 4) & 0x01010101u;
+        const uint32_t n1 = s >> 4;
         // the second escape of each group goes to the column of its second flag, by masks
         E0 = patch_second_escape(E0, z0, esc_lds[r + 1]);
         E1 = patch_second_escape(E1, z1, esc_lds[r + n0 + 1]);
@@ -1289,7 +1313,7 @@ __device__ inline LaneBytes decode_lane(uint32_t row, uint32_t z, uint2 A, uint3
             }
         }
     }
-    return assemble_lane(A, E0, E1);
+    return kRot ? assemble_lane_rot(A, E0, E1) : assemble_lane(A, E0, E1);
 }
 
 // acc[j] += the lane's decoded value j (f32 bits = BF16 bits << 16: bytes [0, 0, low, high])
@@ -1312,7 +1336,7 @@ constexpr uint32_t kEscPad = 16;                   // decode_lane may read esc_l
 // one wave and shared through LDS: the v_perm decode table, where the block's escapes
 // start in the peer's escape buffer and how many there are.
 struct PeerBlock {
-    uint32_t tlo, thi;
+    uint32_t tlo, thi;         // the v_perm decode table, each byte rotated right by one bit
     uint32_t esc_lo, esc_hi;   // escape-buffer offset of the block's first escape
     uint32_t count;            // the block's bytes in the escape buffer
     uint32_t state;            // kPeerCorrupt, kPeerCoded or kPeerUncoded
@@ -1337,7 +1361,7 @@ void accumulate_kernel(const AArgs a)
 {
     __shared__ uint32_t s_cnt[kPeers][kAccWaves];
     __shared__ PeerBlock s_peer[kPeers];
-    __shared__ uint8_t s_blk[kPeers][kAccBlkHead + kEscPad];   // each peer's first escapes of the block
+    __shared__ __attribute__((aligned(16))) uint8_t s_blk[kPeers][kAccBlkHead + kEscPad];   // each peer's first escapes of the block
     __shared__ uint8_t s_esc[kAccWaves][kTile + kEscPad];      // a tile's escapes when they lie further on
     __shared__ uint2 s_A[kAccWaves][kPeers][64];                 // the tile's A bytes per peer, parked until decode
     const uint32_t lane = lane_id();
@@ -1406,7 +1430,11 @@ void accumulate_kernel(const AArgs a)
             const bool ok = hd.ok && block_escapes(C, b, K, hd.n_esc, min(kBlock, n - b * kBlock), first, last);
             const uint64_t e = hd.esc_offset + first;
             const uint32_t state = !ok ? kPeerCorrupt : (ovf > 0 && last - first == ovf ? kPeerUncoded : kPeerCoded);
-            if (lane == 0) s_peer[p] = PeerBlock{hd.tlo, hd.thi, uint32_t(e), uint32_t(e >> 32), last - first, state};
+            // the decode table with every exponent rotated (rotr1): decoding then assembles
+            // each lane's bytes without shifts (escape bytes are rotated where they are staged)
+            if (lane == 0)
+                s_peer[p] = PeerBlock{rotr1_bytes(hd.tlo), rotr1_bytes(hd.thi), uint32_t(e), uint32_t(e >> 32),
+                                      last - first, state};
             m = ok ? min(last - first, kAccBlkHead) : 0u;
             if (m > 0) src = peer_esc[p] + e;
         }
@@ -1450,6 +1478,11 @@ void accumulate_kernel(const AArgs a)
         if (p < P) {
 #pragma unroll
             for (uint32_t k = 0; k < kAccBlkHead / 64; k++) s_blk[p][64 * k + lane] = uint8_t(head[i][k]);
+            // rotated (rotr1) in place, 4 bytes per dword: the decode table's form
+            wave_lds_sync();
+            uint32_t* w = reinterpret_cast<uint32_t*>(s_blk[p]);
+#pragma unroll
+            for (uint32_t k = 0; k < kAccBlkHead / 256; k++) w[64 * k + lane] = rotr1_bytes(w[64 * k + lane]);
         }
     }
     __syncthreads();
@@ -1532,19 +1565,19 @@ void accumulate_kernel(const AArgs a)
                     const uint32_t m = uint32_t(min<uint64_t>(kTile, n - uint64_t(t) * kTile));
 #pragma unroll 1
                     for (uint32_t k = lane; k < m; k += 64)
-                        esc_lds[k] = k < kUncodedPlaneBytes ? pl[k] : ex[k - kUncodedPlaneBytes];
+                        esc_lds[k] = rotr1_byte(k < kUncodedPlaneBytes ? pl[k] : ex[k - kUncodedPlaneBytes]);
                 } else {
                     const uint8_t* esc = peer_esc[p] + e + before[p];
 #pragma unroll 1
-                    for (uint32_t k = lane; k < mine[p]; k += 64) esc_lds[k] = esc[k];
+                    for (uint32_t k = lane; k < mine[p]; k += 64) esc_lds[k] = rotr1_byte(esc[k]);
                 }
                 wave_lds_sync();
                 // an uncoded tile decodes as if every value escaped: codes 0, this lane's
                 // exponents at 8 * lane
-                add_lane(acc, decode_lane(unc ? 0u : rows[p], unc ? valid_flags(nvalid) : zf[p], s_A[wave][p][lane],
+                add_lane(acc, decode_lane<true>(unc ? 0u : rows[p], unc ? valid_flags(nvalid) : zf[p], s_A[wave][p][lane],
                                           s_peer[p].tlo, s_peer[p].thi, unc ? 8 * lane : rank[p], esc_lds));
             } else {
-                add_lane(acc, decode_lane(rows[p], zf[p], s_A[wave][p][lane], s_peer[p].tlo, s_peer[p].thi, rank[p],
+                add_lane(acc, decode_lane<true>(rows[p], zf[p], s_A[wave][p][lane], s_peer[p].tlo, s_peer[p].thi, rank[p],
                                           s_blk[p] + before[p]));
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
