@@ -169,13 +169,13 @@ def run_codec(torch, bc, iters, warmup):
 def op_times(torch, bc, rounds, batches=3):
     """Average launch times (ms) of compress and decompress over back-to-back launches on
     the rotating sets: the median over `batches` batches, so that one disturbed batch
-    does not set the figure."""
+    does not set the figure, and the fastest batch."""
     plans = bc.plans()
     cs, ds = [], []
     for _ in range(batches):
         cs.append(batched_ms(torch, lambda k: bc.compress(k, plans), len(bc.sets), rounds))
         ds.append(batched_ms(torch, bc.decompress, len(bc.sets), rounds))
-    return median(cs), median(ds)
+    return median(cs), median(ds), min(cs), min(ds)
 
 
 SETTLE_S = 0.3   # untimed work before each timed measurement, in seconds
@@ -215,8 +215,9 @@ def batched_ms(torch, fn, sets, rounds):
     return e0.elapsed_time(e1) / (rounds * sets)
 
 
-def codec_report(bc, c, d):
-    """Per-operation figures from average launch times c, d (ms)."""
+def codec_report(bc, c, d, c_min=None, d_min=None):
+    """Per-operation figures from average launch times c, d (ms; medians over batches,
+    with the fastest batch's c_min, d_min beside them)."""
     n_esc = bc.n_esc_total()
     moved = compress_bytes(bc.n, bc.static_bytes, n_esc)
     return {
@@ -224,6 +225,8 @@ def codec_report(bc, c, d):
         "segments": len(bc.sizes),
         "compress_us": round(c * 1e3, 2),
         "decompress_us": round(d * 1e3, 2),
+        "compress_us_min": None if c_min is None else round(c_min * 1e3, 2),
+        "decompress_us_min": None if d_min is None else round(d_min * 1e3, 2),
         "compress_GBps": round(2 * bc.n / (c * 1e-3) / 1e9, 1),
         "decompress_GBps": round(2 * bc.n / (d * 1e-3) / 1e9, 1),
         "compress_hbm_frac": round(moved / (c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -606,6 +609,23 @@ def host_threads():
     return max(1, min(16, os.cpu_count() or 1))
 
 
+def host_info():
+    """The host the oracle runs on: logical CPUs, the CPU model and the NUMA nodes (Linux)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        numa = len([d for d in os.listdir("/sys/devices/system/node") if d.startswith("node") and d[4:].isdigit()])
+    except OSError:
+        numa = None
+    return {"host_cpus": os.cpu_count(), "cpu_model": model, "numa_nodes": numa}
+
+
 def oracle_codec(O, segments, sigmas, reps=1, sample=None):
     """The oracle's compress (one batch call) and decompress (one call per segment) of a
     workload's segments on one thread, median of reps; then the same values as at least
@@ -681,7 +701,7 @@ def oracle_rs(O, W, chunks=4, reps=3):
             "compress_GBps": round(2 * v / c / 1e9, 4), "accumulate_GBps_bf16_in": round(2 * v / a / 1e9, 4),
             "sample": f"rs_512m chunks 0..{chunks - 1} of the 7 peers ({chunks} x 7 x {chunk} values): compress + "
                       f"decode-accumulate, median of {reps}, 1 thread",
-            "host_cpus": os.cpu_count(),
+            **host_info(),
             "all_threads": {"threads": threads, "value": round(4 * P * chunk * par / wall / 1e9, 4), "unit": "GB/s",
                             "sample": f"rs_512m chunks 0..{par - 1}, compress + decode-accumulate of each chunk as one task"}}
 
@@ -704,8 +724,8 @@ def bench_codec_workload(torch, Z, W, name, rounds=5):
     sets = 8 if name == "chunk_1m" else 4
     b2 = BatchCodec(torch, Z, w2.segments, w2.sigmas, sets)
     run_codec(torch, b2, 3, 3)
-    cm, dm = op_times(torch, b2, rounds)
-    r2 = codec_report(b2, cm, dm)
+    cm, dm, cmin, dmin = op_times(torch, b2, rounds)
+    r2 = codec_report(b2, cm, dm, cmin, dmin)
     r2["parity_round_trip"] = b2.verify()
     launches = codec_launches(b2, b2.n_esc_total())
     del b2
@@ -1014,8 +1034,9 @@ def main(argv=None) -> int:
     # between two HIP events on the launch stream (median of three batches)
     plans = rs.plans()
     rounds = max(2, args.steps // 3)
-    c_ms = median([batched_ms(torch, lambda k: rs.compress_all(plans), 1, rounds) for _ in range(3)])
-    a_ms = median([batched_ms(torch, lambda k: rs.accumulate_all(), 1, rounds) for _ in range(3)])
+    c_all = [batched_ms(torch, lambda k: rs.compress_all(plans), 1, rounds) for _ in range(3)]
+    a_all = [batched_ms(torch, lambda k: rs.accumulate_all(), 1, rounds) for _ in range(3)]
+    c_ms, a_ms = median(c_all), median(a_all)
     lc = rs.launches()[0]
     nl_a = rs.accumulate_launches_per_step()
     c_launch_ms = c_ms / lc["per_step"]
@@ -1026,11 +1047,12 @@ def main(argv=None) -> int:
               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(c_bytes / (c_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
               "traffic": measured_traffic("rs_512m", lc["kernel"], lc["grid"]),
               "bytes_per_launch": int(c_bytes), "avg_launch_us": round(c_launch_ms * 1e3, 2),
+              "avg_launch_us_min": round(min(c_all) / lc["per_step"] * 1e3, 2),
               "launches_per_step": lc["per_step"], "values_per_launch": lc["values"]}
     roof_a = {"bound": "hbm", "kernel": "accumulate_kernel", "achieved": round(a_bytes / (a_launch_ms * 1e-3) / 1e9, 1),
               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(a_bytes / (a_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
               "traffic": rs.accumulate_traffic_per_launch(), "bytes_per_launch": int(a_bytes),
-              "avg_launch_us": round(a_launch_ms * 1e3, 2),
+              "avg_launch_us": round(a_launch_ms * 1e3, 2), "avg_launch_us_min": round(min(a_all) / nl_a * 1e3, 2),
               "launches_per_step": nl_a,
               "note": "launches hold 18 and 14 chunks of 7 peers; bytes, time and traffic are per launch on average"}
     total_esc = rs.total_esc()
@@ -1073,8 +1095,8 @@ def main(argv=None) -> int:
         wl = workload(W, "bucket_64m")
         bc = BatchCodec(torch, Z, wl.segments, wl.sigmas, args.sets)
         step_ms = run_codec(torch, bc, 10, 3)
-        cm, dm = op_times(torch, bc, max(2, args.steps // len(bc.sets)))
-        r = codec_report(bc, cm, dm)
+        cm, dm, cmin, dmin = op_times(torch, bc, max(2, args.steps // len(bc.sets)))
+        r = codec_report(bc, cm, dm, cmin, dmin)
         r["step_GBps"] = round(4 * bc.n / (step_ms * 1e-3) / 1e9, 1)
         r["parity_round_trip"] = bc.verify()
         r["compress_traffic_bytes"] = measured_traffic("bucket_64m", *[(L["kernel"], L["grid"]) for L in
