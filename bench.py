@@ -742,10 +742,23 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 GIB = 1 << 30
 
 
+def kernel_code_text(text):
+    """The kernel source without its comments, trailing blanks and empty lines: what a
+    profile was taken on, so that a change to comments alone keeps it valid (the source
+    has no string literal holding "//")."""
+    lines = []
+    for line in text.splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            lines.append(line)
+    return "\n".join(lines) + "\n"
+
+
 def kernel_source_sha256():
+    """sha256 of the kernel code (kernel_code_text of zipccl_kernels.hip)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        return hashlib.sha256(kernel_code_text(f.read()).encode()).hexdigest()
 
 
 def short_kernel_name(name):
@@ -762,7 +775,8 @@ def summarize_stats_any(csv_path, out_path, title, command):
     rows = [r for r in csv.DictReader(open(csv_path)) if short_kernel_name(r["Name"]) in OUR_KERNELS]
     lines = [f"# Kernel durations, {title}", "",
              "Command (from the repository root on the GPU host; rocprofv3's own averages):", "",
-             "    " + command, "", f"Kernel source sha256: `{kernel_source_sha256()}`", "",
+             "    " + command, "",
+             f"Kernel code sha256 (zipccl_kernels.hip without comments): `{kernel_source_sha256()}`", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -806,7 +820,7 @@ def summarize_pmc_any(name, launches_json, fetch_csv, write_csv, out_path):
              "    " + pmc_cmd(name, "FETCH_SIZE"), "    " + pmc_cmd(name, "WRITE_SIZE"), "",
              f"Scale factors from the 1 GiB copy in the same runs: FETCH_SIZE x{sf:.4f}, WRITE_SIZE x{sw:.4f}",
              f"(the copy counted {copy_f:.0f} KiB fetched and {copy_w:.0f} KiB written per dispatch).",
-             f"Kernel source sha256: `{kernel_source_sha256()}`", "",
+             f"Kernel code sha256 (zipccl_kernels.hip without comments): `{kernel_source_sha256()}`", "",
              "| kernel | grid | dispatches | read MB | write MB | measured MB | algorithmic MB | measured / algorithmic |",
              "|---|---|---|---|---|---|---|---|"]
     mr = []
@@ -895,7 +909,7 @@ def summarize_sq(csv_path, out_path):
         acc.setdefault((k, grid), {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     lines = ["# Instruction counts, rs_512m kernels (rocprofv3 SQ counters, mean per launch)", "",
              "Command (from the repository root on the GPU host):", "", "    " + SQ_CMD, "",
-             f"Kernel source sha256: `{kernel_source_sha256()}`", "",
+             f"Kernel code sha256 (zipccl_kernels.hip without comments): `{kernel_source_sha256()}`", "",
              "| kernel | grid | launches | waves | VALU | SALU | LDS | VMEM rd | VMEM wr | VALU issue us |",
              "|---|---|---|---|---|---|---|---|---|---|"]
     for (k, grid), d in sorted(acc.items()):

@@ -23,25 +23,32 @@
 //     Decoding replaces the code-0 byte of the v_perm table with the lane's first
 //     escape of each group of 4 columns; a second escape in a group is placed by masks,
 //     and only a third or fourth is patched byte by byte.
-//   * Compress is one launch (compress_single_kernel): encoding workgroups write the A
-//     bytes and planes, stage each unit's escapes contiguously in the workspace and then
-//     publish the unit's escape count in a ready word tagged with the call's tag; the
-//     grid's last workgroups (dispatched after every encoder) wait, bounded, for the
-//     ready words before their units, then compute escape positions, compact the
-//     escapes and write offset tables and headers.  What one workgroup hands to another
-//     goes through agent-scope (write-through) stores and loads, so no cache-wide
-//     write-back or invalidate is needed.  Under graph capture the same work is two
-//     launches that wait for nothing (encode_kernel, place_direct_kernel); above 2^28
-//     values a one-workgroup scan kernel computes the positions and a per-block place
-//     kernel follows.
+//   * Uncoded blocks.  A block whose escapes would reach its overflow (the values past
+//     the first 192 of each tile) is rewritten by its encoding waves: plane bytes hold
+//     the first 192 exponents of each tile, the rest go where the escapes would have
+//     gone.  Decoders recognise such a block from its offset-table entries alone.
+//   * Compress is one launch (compress_single_kernel) when the caller passes a status
+//     word: encoding workgroups write the A bytes and planes, stage each unit's escapes
+//     contiguously in the workspace and then publish the unit's escape count in a ready
+//     word tagged with the call's tag; the grid's last workgroups (dispatched after every
+//     encoder, last group first) wait, bounded, for the ready words before their units,
+//     then compute escape positions, compact the escapes and write offset tables and
+//     headers.  What one workgroup hands to another goes through agent-scope
+//     (write-through) stores and loads, so no cache-wide write-back or invalidate is
+//     needed.  Without a status word (a wait that ran out could not be reported) and
+//     under graph capture the same work is two launches that wait for nothing
+//     (encode_kernel, place_direct_kernel); above 2^28 values a one-workgroup scan kernel
+//     computes the positions and a per-block place kernel follows.
 //     One launch may compress several independent calls (the chunks of a sequence):
 //     each segment names its call, and positions, offsets and headers count from the
 //     first escape of the call.
 //   * Decompress: one workgroup per block, one half block per wave, one barrier to share
 //     the escape count of the first half; each segment has its own escape buffer.
 //     Decode-accumulate: one workgroup per block, one wave per tile, all peers of a
-//     tile in one wave; the A bytes wait in LDS so that 4 workgroups fit per CU; one
-//     launch may cover several chunks, each with its own peers.
+//     tile in one wave; the A bytes wait in LDS so that 4 workgroups fit per CU; its
+//     decode table and staged escapes hold exponents rotated by one bit, so a lane's
+//     bytes assemble without shifts; one launch may cover several chunks, each with its
+//     own peers.
 #include "zipccl_internal.h"
 #include "zipccl.h"
 
@@ -1352,9 +1359,10 @@ constexpr uint32_t kPeerCorrupt = 0, kPeerCoded = 1, kPeerUncoded = 2;
 // order.
 template <int kPeers>
 // Up to 7 peers the kernel fits 64 VGPRs without spills (the A bytes wait in LDS, not in
-// registers), so 4 workgroups run per CU; the kernel is latency-bound (at 2 workgroups
-// per CU it took 1.77x as long as at 3), and 4 took 7-peer launches 12 % below 3.  With
-// 8 peers the LDS allows 3 workgroups per CU (6 waves per SIMD).
+// registers), so 4 workgroups run per CU.  At low occupancy it was latency-bound (at 2
+// workgroups per CU it took 1.77x as long as at 3, and 4 took 7-peer launches 12 % below
+// 3); at 4 it is bound by VALU issue (~124 instructions per wave plus ~80 per peer).
+// With 8 peers the LDS allows 3 workgroups per CU (6 waves per SIMD).
 __global__ __launch_bounds__(kAccThreads)
 __attribute__((amdgpu_waves_per_eu(kPeers <= 7 ? 8 : (kPeers <= 8 ? 6 : 4))))
 void accumulate_kernel(const AArgs a)

@@ -78,3 +78,12 @@ def test_summaries_from_rocprof_csv(tmp_path):
     bench.summarize_tcc(str(c0), str(c1), str(out2))
     assert f"| __amd_rocclr_copyBuffer | 1 | {GIB / 1e6:.2f} | {GIB / 1e6:.2f} | {GIB / 1e6:.2f} | {GIB / 1e6:.2f} |" \
         in out2.read_text()
+
+
+def test_profiles_follow_the_kernel_code_not_its_comments():
+    sys.path.insert(0, ROOT)
+    import bench
+    code = "// header\nint f(int x)  \n{\n\n    return x + 1;   // one more\n}\n"
+    assert bench.kernel_code_text(code) == "int f(int x)\n{\n    return x + 1;\n}\n"
+    assert bench.kernel_code_text(code.replace("one more", "plus one")) == bench.kernel_code_text(code)
+    assert bench.kernel_code_text(code.replace("x + 1", "x + 2")) != bench.kernel_code_text(code)
