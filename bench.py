@@ -44,6 +44,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COMPRESS_CALLS_PER_LAUNCH = 8    # chunk calls that share one compress launch (the library takes up
+                                 # to 16, but each placer then sums 4x as many ready words: 16 took
+                                 # 150.1 us per launch against 2 x 74 us for two launches of 8)
+ACC_SLOTS = 256                  # peer segments one decode-accumulate launch takes
 METRIC = "codec GB/s (bf16 in) compress/decompress, % of HBM peak, compression ratio"
 
 
@@ -259,7 +263,7 @@ class RSShare:
         self.n_esc = torch.zeros(self.nch, P + 1, dtype=torch.int64, device="cuda")
         self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
         # 8 chunks (56 segments) share a compress launch, with a workspace that holds them
-        self.per_launch = 8
+        self.per_launch = COMPRESS_CALLS_PER_LAUNCH
         self.ws = torch.zeros(Z.workspace_size(self.per_launch * P * chunk, self.per_launch * P), dtype=torch.uint8,
                               device="cuda")
         self.comp_seq = Z.PreparedCompressChunks(
@@ -312,7 +316,7 @@ class RSShare:
     def accumulate_traffic_per_launch(self):
         """Measured HBM bytes of the decode-accumulate launches of one pass, per launch on
         average (the launches hold different numbers of chunks), or None."""
-        per_acc = 128 // self.P
+        per_acc = ACC_SLOTS // self.P
         grids = [(self.chunk // 4096) * 512 * min(per_acc, self.nch - c0) for c0 in range(0, self.nch, per_acc)]
         t = [measured_traffic("rs_512m", "accumulate_kernel", g) for g in grids]
         return None if None in t else int(sum(t) / len(t))
@@ -320,12 +324,12 @@ class RSShare:
     def launches(self):
         """Kernel launches of one step, for the counter summaries: kernel, grid size in
         work-items, launches per step, algorithmic bytes per launch.  Decode-accumulate
-        launches hold 128 / 7 = 18 chunks each, the last one the rest (14)."""
+        launches hold up to 256 / 7 = 36 chunks each (one launch for the 32 chunks)."""
         units = self.per_launch * self.P * ((self.chunk + 16383) // 16384)
         nl_c = self.nch // self.per_launch
         out = [{"kernel": "compress_single_kernel", "grid": (units + (units + 7) // 8) * 512, "per_step": nl_c,
                 "bytes": self.compress_bytes() / nl_c, "values": self.per_launch * self.P * self.chunk}]
-        per_acc = 128 // self.P
+        per_acc = ACC_SLOTS // self.P
         shapes = {}
         for c0 in range(0, self.nch, per_acc):
             k = min(per_acc, self.nch - c0)
@@ -336,7 +340,7 @@ class RSShare:
         return out
 
     def accumulate_launches_per_step(self):
-        return -(-self.nch // (128 // self.P))
+        return -(-self.nch // (ACC_SLOTS // self.P))
 
 
 def bench_rs_extra(torch, Z, rs, iters):
@@ -1068,7 +1072,7 @@ def main(argv=None) -> int:
               "traffic": rs.accumulate_traffic_per_launch(), "bytes_per_launch": int(a_bytes),
               "avg_launch_us": round(a_launch_ms * 1e3, 2), "avg_launch_us_min": round(min(a_all) / nl_a * 1e3, 2),
               "launches_per_step": nl_a,
-              "note": "launches hold 18 and 14 chunks of 7 peers; bytes, time and traffic are per launch on average"}
+              "note": "one launch holds all 32 chunks of 7 peers (up to 36 fit); bytes, time and traffic per launch"}
     total_esc = rs.total_esc()
     out = {
         "metric": METRIC,

@@ -208,7 +208,7 @@ zipccl_status zipccl_compress_device_plans(const zipccl_segment_t* segs, int nse
  *   zipccl_compress(segs + k * nseg, nseg, static_out[k], static_cap[k], esc_out[k],
  *                   esc_cap[k], ..., n_esc_out + k * (nseg + 1), status, stream)
  * writes, byte for byte (each chunk's escapes and esc_offsets are its own), but
- * consecutive chunks share a kernel launch (up to 8 chunks and 64 segments per launch)
+ * consecutive chunks share a kernel launch (up to 16 chunks and 128 segments per launch)
  * while the workspace holds them all, so that a launch has enough work to fill the GPU.
  *   segs        host array of nchunks * nseg segments, chunk after chunk; 1 <= nseg <=
  *               ZIPCCL_MAX_PEERS
@@ -298,7 +298,7 @@ zipccl_status zipccl_decompress_accumulate(const void* const* static_in, const v
                                            const void* local, void* dst, uint32_t* status, void* stream);
 
 /* zipccl_decompress_accumulate over consecutive chunks, in as few launches as the kernel
- * arguments allow (128 / npeers chunks each): chunk c covers values [c * chunk,
+ * arguments allow (256 / npeers chunks each): chunk c covers values [c * chunk,
  * min(n, (c + 1) * chunk)) of local and dst, and peer p's compressed segment of it is at
  * static_in[c * npeers + p] with escapes in esc_in[c * npeers + p] (esc_bytes[...] long).
  * The result is that of one zipccl_decompress_accumulate call per chunk.  static_in,

@@ -1,5 +1,7 @@
 // Internal definitions shared by the HIP kernels and the host layer of libzipccl.
-// Kernel arguments travel by value in the kernel-argument segment (< 4 KiB each).
+// Kernel arguments travel by value in the kernel-argument segment: up to 4 KiB for
+// the per-call tables; the compress and decode-accumulate launches that several calls
+// share carry larger tables (about 8 and 6 KiB; this runtime passes 16 KiB intact).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,8 +14,10 @@ constexpr uint32_t kBlock = 4096;             // values per escape-offset entry 
 constexpr uint32_t kWaves = 4;                // waves per workgroup
 constexpr uint32_t kThreads = 64 * kWaves;    // 256
 constexpr uint32_t kUnit = kBlock * kWaves;   // values per workgroup: one block per wave
-constexpr int kMaxSegs = 64;
+constexpr int kMaxSegs = 64;       // segments of one call
+constexpr int kLaunchSegs = 128;   // segments of one compress launch (several calls)
 constexpr int kMaxPeers = 16;
+constexpr uint64_t kMaxKernelArgs = 12288;   // bytes; 16 KiB measured to arrive intact
 
 // Uncoded blocks: the plane bytes of a tile (3 planes x 8 columns x 64 bits) hold the
 // exponents of its first 192 values; the rest of the tile's exponents go to the escape
@@ -88,10 +92,10 @@ struct CCall {
     uint32_t unit0;        // first unit of the call
     uint32_t block_end;    // one past the call's last block (launch-wide numbering)
 };
-constexpr int kMaxCalls = 8;
+constexpr int kMaxCalls = 16;
 
 struct CArgs {
-    CSeg seg[kMaxSegs];
+    CSeg seg[kLaunchSegs];
     CCall call[kMaxCalls];
     uint32_t* counts;      // workspace: escapes per half-block slot
     uint32_t* pos;         // workspace: launch-wide position of each slot's first escape
@@ -110,7 +114,7 @@ struct CArgs {
     uint32_t direct;       // 1: the place kernel computes positions from unit_counts
 };
 
-static_assert(sizeof(CArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+static_assert(sizeof(CArgs) <= kMaxKernelArgs, "kernel arguments of a compress launch");
 
 struct DSeg {              // decompress: one segment
     const uint8_t* src;    // static part
@@ -135,7 +139,7 @@ static_assert(sizeof(DArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 // may be shorter; chunk is a multiple of kBlock unless nchunks == 1): chunk c covers
 // values [c * chunk, min(n, (c + 1) * chunk)) of local / dst and has one compressed
 // segment per peer, at st[c * npeers + p] with escapes in esc[c * npeers + p].
-constexpr int kMaxAccSlots = 128;
+constexpr int kMaxAccSlots = 256;
 
 struct AArgs {
     const uint8_t* st[kMaxAccSlots];
@@ -149,7 +153,7 @@ struct AArgs {
     int32_t npeers;
     int32_t nchunks;
 };
-static_assert(sizeof(AArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+static_assert(sizeof(AArgs) <= kMaxKernelArgs, "kernel arguments of a decode-accumulate launch");
 
 __host__ __device__ inline uint64_t round128(uint64_t v) { return (v + 127) & ~uint64_t(127); }
 __host__ __device__ inline uint64_t tiles_of(uint64_t n) { return (n + kTile - 1) / kTile; }

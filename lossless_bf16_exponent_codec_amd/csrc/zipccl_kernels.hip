@@ -133,19 +133,24 @@ __device__ inline int find_segment(const Seg* seg, int nseg, uint32_t u)
 }
 
 // The same lookup by the whole wave at once, for code where every lane of the wave is
-// active and u is the same in all of them: lane s compares segment s (nseg <= 64), and the
-// last segment whose first index is at most u is the highest lane of the ballot.  One
-// load round trip instead of one per binary-search step (with 1 or 2 segments the binary
-// search needs none or one).
+// active and u is the same in all of them: lane s compares segments s and s + 64 (nseg <=
+// 128), and the last segment whose first index is at most u is the highest lane of the
+// ballots.  One load round trip instead of one per binary-search step (with 1 or 2
+// segments the binary search needs none or one).
 template <auto First, class Seg>
 __device__ inline int find_segment_wave(const Seg* seg, int nseg, uint32_t u)
 {
-    static_assert(kMaxSegs <= 64, "one lane per segment");
+    static_assert(kLaunchSegs <= 128 && kMaxSegs <= 128, "two segments per lane at most");
     if (nseg <= 2) return find_segment<First>(seg, nseg, u);   // no load, or one
     u = __builtin_amdgcn_readfirstlane(u);
     const int lane = int(lane_id());
-    const bool at_or_before = lane < nseg && seg[lane].*First <= u;   // seg[0] starts at 0
-    const uint64_t m = __builtin_amdgcn_ballot_w64(at_or_before);
+    const bool lo = lane < nseg && seg[lane].*First <= u;   // seg[0] starts at 0
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lo);
+    if (nseg > 64) {   // only in tables of more than 64 entries
+        const bool hi = lane + 64 < nseg && seg[lane + 64].*First <= u;
+        const uint64_t mh = __builtin_amdgcn_ballot_w64(hi);
+        if (mh != 0) return 127 - __builtin_clzll(mh);
+    }
     return 63 - __builtin_clzll(m | 1ull);
 }
 

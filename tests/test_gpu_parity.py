@@ -383,7 +383,7 @@ def accumulate_chunks_setup(Z, npeers, chunk, n, seed):
 
 
 @pytest.mark.parametrize("npeers,chunk,n", [(3, 8192, 5 * 8192 + 1000),   # ragged last chunk
-                                             (16, 4096, 9 * 4096),          # 8 chunks per launch: two launches
+                                             (16, 4096, 17 * 4096 + 1000),  # 16 chunks per launch: two launches
                                              (7, 1 << 20, (1 << 20) + 4096)])
 def test_accumulate_chunks_matches_oracle(Z, npeers, chunk, n):
     print(f"accumulate chunks P={npeers} chunk={chunk} n={n}", flush=True)
@@ -895,17 +895,17 @@ def batch_workspace(Z, chunks):
 
 
 def test_compress_chunks_shared_launches(Z):
-    chunks, plans = long_chunk_sequence()
+    # 20 calls: a launch holds at most 16
+    chunks, plans = long_chunk_sequence(nchunks=20)
     print("chunks sharing launches", [[b.size for b in ch] for ch in chunks], flush=True)
     assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
 
 
 def test_compress_chunks_shared_launches_many_peers(Z):
-    # 7 segments per chunk: at most 9 chunks fit the 64-segment launch, 8 calls at most
-    chunks, _ = long_chunk_sequence(nchunks=10, S=3, seed=1)
+    # 7 segments per chunk: at most 18 chunks fit the 128-segment launch, 16 calls at most
     rng = np.random.default_rng(5)
     chunks = [[W.gaussian_bf16(int(rng.choice([4096, 20000, 65536])), 1e-3, 4000 + 7 * k + i) for i in range(7)]
-              for k in range(10)]
+              for k in range(20)]
     plans = [Z.plan(sigma=1e-3)] * 7
     assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
 

@@ -89,7 +89,7 @@ def test_reduce_scatter_share_pipeline(Z):
         assert list(n_esc[c].cpu().numpy()[:P]) == ne and int(n_esc[c, P].item()) == sum(ne)
         assert np.array_equal(esc[c * P * chunk:c * P * chunk + sum(ne)].cpu().numpy(), e), f"chunk {c}"
     # decode-accumulate as the benchmark times it: zipccl_decompress_accumulate_chunks over the
-    # 32 chunks' outputs (launches of 18 and 14 chunks), against the oracle's full result
+    # 32 chunks' outputs (one launch), against the oracle's full result
     # (the in-place pipeline run above overwrote `local`, so the local shard is loaded again)
     local2 = dev_bf16(wl.extra["local"])
     out = torch.full((n,), -21846, dtype=torch.int16, device="cuda").view(torch.bfloat16)   # 0xAAAA
