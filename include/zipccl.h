@@ -38,7 +38,9 @@
  *
  * Conventions.
  *   - All data pointers are device pointers unless stated.  The caller owns every
- *     buffer; the library allocates no device memory and keeps no global state.
+ *     buffer; the library allocates no device memory.  Its only global state is the
+ *     static workspace of zipccl_compress_noalloc (one per device, with its address
+ *     looked up once per device).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues
  *     work on it and returns; nothing synchronises the host.
  *   - Argument errors are returned before anything is enqueued.  Data-dependent
