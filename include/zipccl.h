@@ -317,7 +317,7 @@ zipccl_status zipccl_decompress_accumulate_chunks(const void* const* static_in, 
  * of every peer shard are compressed on stream_a (one compress call per chunk, one
  * segment per peer) and decoded + accumulated into dst on stream_b.  The streams hand
  * chunks over in groups of G (a power of two, at most 16, the smallest with
- * G * npeers * chunk >= 2^26 values, since each event record or wait costs the host
+ * G * npeers * chunk >= 2^27 values, since each event record or wait costs the host
  * microseconds); a ring of two groups of chunk buffers lets group g + 1 compress while
  * group g is reduced.  Each group is compressed by one zipccl_compress_chunks call (its
  * chunks share launches) and reduced by one zipccl_decompress_accumulate_chunks call.

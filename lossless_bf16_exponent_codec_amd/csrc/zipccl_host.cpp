@@ -716,16 +716,17 @@ struct zipccl_pipeline {
 
 namespace {
 
-// Chunks per hand-off: an event record or wait costs the host a few microseconds, and
-// each hand-off ends a compress launch sequence with a place-only launch and splits the
-// decode-accumulate launches, so the streams hand over groups of chunks holding at
-// least 2^26 values (each chunk is still its own compress call and its own segments).
-// Measured on 7 x 2 Mi-value chunks: hand-offs of 2, 4, 8, 16 chunks took 889, 793,
-// 732, 705 us for 32 chunks; 8 keeps the ring at 2 x 8 chunk buffers.
+// Chunks per hand-off: an event record or wait costs the host a few microseconds and
+// leaves the waiting stream idle for ~11 us of GPU time (kernel trace), and each
+// hand-off splits the launches the chunks could share, so the streams hand over groups
+// of chunks holding at least 2^27 values (each chunk is still its own compress call and
+// its own segments).  Measured on 7 x 2 Mi-value chunks, 32 chunks: groups of 8 took
+// 509.7 us, groups of 16 489.0 us, with a ring of 2 x 16 chunk buffers (1.35 GB of
+// scratch; 0.68 GB for 8).
 uint32_t pipeline_group(int npeers, uint64_t chunk)
 {
     uint32_t g = 1;
-    while (g < 16 && uint64_t(g) * uint64_t(npeers) * chunk < (1ull << 26)) g *= 2;
+    while (g < 16 && uint64_t(g) * uint64_t(npeers) * chunk < (1ull << 27)) g *= 2;
     return g;
 }
 
