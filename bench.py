@@ -44,9 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-COMPRESS_CALLS_PER_LAUNCH = 8    # chunk calls that share one compress launch (the library takes up
-                                 # to 16, but each placer then sums 4x as many ready words: 16 took
-                                 # 150.1 us per launch against 2 x 74 us for two launches of 8)
+COMPRESS_CALLS_PER_LAUNCH = 16   # chunk calls that share one compress launch (the most the library
+                                 # takes; launches of 8 took 4 % longer per pass)
 ACC_SLOTS = 256                  # peer segments one decode-accumulate launch takes
 METRIC = "codec GB/s (bf16 in) compress/decompress, % of HBM peak, compression ratio"
 

@@ -269,13 +269,13 @@ zipccl_status fill_segments(CArgs& a, const zipccl_segment_t* segs, int nseg, bo
 }
 
 // Launches prepared chunk calls in order on one stream.  Consecutive calls whose
-// positions the place workgroups compute themselves (direct) share a launch while the
-// launch has room (kMaxCalls calls, kLaunchSegs segments, kDirectPrefixMaxUnits units) and
-// the workspace holds all their units; each keeps its own outputs and escape numbering.
+// positions the place workgroups compute themselves (direct: at most
+// kDirectPrefixMaxUnits units each) share a launch while the launch has room (kMaxCalls
+// calls, kLaunchSegs segments) and the workspace holds all their units; each keeps its
+// own outputs and escape numbering.
 zipccl_status launch_chunks(const std::vector<CArgs>& calls, void* workspace, uint64_t workspace_bytes,
                             hipStream_t stream)
 {
-    const uint64_t max_units = direct_prefix_max_units();
     size_t k = 0;
     while (k < calls.size()) {
         CArgs b = calls[k];
@@ -284,7 +284,7 @@ zipccl_status launch_chunks(const std::vector<CArgs>& calls, void* workspace, ui
             for (; j < calls.size() && b.ncalls < kMaxCalls; j++) {
                 const CArgs& c = calls[j];
                 const uint64_t units = uint64_t(b.total_units) + c.total_units;
-                if (!c.direct || c.dplans || b.nseg + c.nseg > kLaunchSegs || units > max_units ||
+                if (!c.direct || c.dplans || b.nseg + c.nseg > kLaunchSegs || units >= (1ull << 32) ||
                     ws_bytes(units) > workspace_bytes)
                     break;
                 for (int s = 0; s < c.nseg; s++) {
@@ -731,16 +731,15 @@ uint32_t pipeline_group(int npeers, uint64_t chunk)
 }
 
 // Scratch layout: one compress workspace that holds as many chunks as share a compress
-// launch (at most kMaxCalls, kLaunchSegs segments, kDirectPrefixMaxUnits units), then
+// launch (at most kMaxCalls, kLaunchSegs segments), then
 // 2 * group chunk slots (a ring of two groups), each holding the chunk's npeers static
 // parts and room for all its escapes.
 void pipeline_layout(int npeers, uint64_t chunk, uint64_t& slot_static, uint64_t& slot_esc, uint64_t& ws)
 {
     slot_static = uint64_t(npeers) * static_bytes_of(chunk);
     slot_esc = (uint64_t(npeers) * chunk + 255) & ~uint64_t(255);
-    uint64_t b = std::min<uint64_t>({uint64_t(pipeline_group(npeers, chunk)), uint64_t(kMaxCalls),
-                                     uint64_t(kLaunchSegs / npeers)});
-    while (b > 1 && b * units_of(chunk) * uint64_t(npeers) > kDirectPrefixMaxUnits) b--;
+    const uint64_t b = std::min<uint64_t>({uint64_t(pipeline_group(npeers, chunk)), uint64_t(kMaxCalls),
+                                           uint64_t(kLaunchSegs / npeers)});
     ws = (zipccl_workspace_size(b * uint64_t(npeers) * chunk, int(b) * npeers) + 255) & ~uint64_t(255);
 }
 

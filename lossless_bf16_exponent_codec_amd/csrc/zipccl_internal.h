@@ -1,7 +1,7 @@
 // Internal definitions shared by the HIP kernels and the host layer of libzipccl.
 // Kernel arguments travel by value in the kernel-argument segment: up to 4 KiB for
 // the per-call tables; the compress and decode-accumulate launches that several calls
-// share carry larger tables (about 8 and 6 KiB; this runtime passes 16 KiB intact).
+// share carry larger tables (about 8 and 6 KiB; this runtime passes 16000 bytes intact).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,7 +17,7 @@ constexpr uint32_t kUnit = kBlock * kWaves;   // values per workgroup: one block
 constexpr int kMaxSegs = 64;       // segments of one call
 constexpr int kLaunchSegs = 128;   // segments of one compress launch (several calls)
 constexpr int kMaxPeers = 16;
-constexpr uint64_t kMaxKernelArgs = 12288;   // bytes; 16 KiB measured to arrive intact
+constexpr uint64_t kMaxKernelArgs = 12288;   // bytes; 16000 measured to arrive intact
 
 // Uncoded blocks: the plane bytes of a tile (3 planes x 8 columns x 64 bits) hold the
 // exponents of its first 192 values; the rest of the tile's exponents go to the escape
@@ -61,8 +61,9 @@ hipError_t noalloc_workspace(hipStream_t stream, void** out);
 // per call by the host, never 0) above the unit's escape count (at most kUnit).
 constexpr uint32_t kReadyCountBits = 16;
 
-// Up to this many workgroup units (2^28 values) the place kernel sums the unit counts
-// before its unit itself; above, a one-workgroup scan kernel computes the positions.
+// Up to this many workgroup units (2^28 values) in a call the place kernel sums the unit
+// counts of the call before its unit itself; above, a one-workgroup scan kernel computes
+// the positions (and the call has a launch of its own).
 constexpr uint32_t kDirectPrefixMaxUnits = 16384;
 
 struct CSeg {              // compress: one segment

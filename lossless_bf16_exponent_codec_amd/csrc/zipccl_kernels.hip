@@ -30,10 +30,10 @@
 //   * Compress is one launch (compress_single_kernel) when the caller passes a status
 //     word: encoding workgroups write the A bytes and planes, stage each unit's escapes
 //     contiguously in the workspace and then publish the unit's escape count in a ready
-//     word tagged with the call's tag; the grid's last workgroups (dispatched after every
-//     encoder, last group first) wait, bounded, for the ready words before their units,
-//     then compute escape positions, compact the escapes and write offset tables and
-//     headers.  What one workgroup hands to another goes through agent-scope
+//     word tagged with the call's tag; placing workgroups, interleaved in the grid about
+//     one generation of encoders behind the units they place, wait (bounded) for the
+//     ready words of their call's units up to theirs, then compute escape positions,
+//     compact the escapes and write offset tables and headers.  What one workgroup hands to another goes through agent-scope
 //     (write-through) stores and loads, so no cache-wide write-back or invalidate is
 //     needed.  Without a status word (a wait that ran out could not be reported) and
 //     under graph capture the same work is two launches that wait for nothing
@@ -886,21 +886,23 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const CArgs a)
 }
 
 // Place without the scan kernel: one workgroup per 8 encode units, one unit (4 blocks)
-// per wave.  The workgroup sums the escape counts of all units before its first one
-// (and before the first unit of that unit's segment) from unit_counts[], a few
-// kilobytes read from L2; each wave then copies its unit's escapes (staged contiguous,
-// the first 512 bytes requested up front) in one run and derives its blocks' offsets
-// from the unit's 8 half-block counts.  Every load that needs no segment information
-// is issued before the segment lookups in the kernel arguments.
+// per wave.  Escape positions count from the first escape of a unit's call, so the
+// workgroup sums the escape counts of the units of its first unit's call before its
+// first unit (and before the first unit of that unit's segment) from unit_counts[], a
+// few kilobytes read from L2; each wave then copies its unit's escapes (staged
+// contiguous, the first 512 bytes requested up front) in one run and derives its
+// blocks' offsets from the unit's 8 half-block counts.  A call has at most
+// kDirectPrefixMaxUnits units; a launch of several calls may have more.
 constexpr uint32_t kPlaceUnits = 8;
 constexpr uint32_t kPlaceThreads = 64 * kPlaceUnits;
-constexpr uint32_t kPrefixLoads = kDirectPrefixMaxUnits / (4 * kPlaceThreads);   // uint4 loads per thread
+// uint4 loads per thread: the call's units before the group, from a multiple of 4 on
+constexpr uint32_t kPrefixLoads = (kDirectPrefixMaxUnits + 3 + 4 * kPlaceThreads - 1) / (4 * kPlaceThreads);
 
 // Bounded wait of the single-launch compress: polls for the ready word of unit u of this
 // call (tag) and returns its escape count; after `polls` polls (2^16 by default, about
-// 0.1 s) sets `late` and returns 0.  A placing workgroup is dispatched only after every
-// encoder workgroup of the launch (they come first in the grid), and encoders wait for
-// nothing, so the wait ends long before the limit.
+// 0.1 s) sets `late` and returns 0.  A placing workgroup comes after every encoder whose
+// word it waits for in the grid (workgroups are dispatched in grid order), and encoders
+// wait for nothing, so the wait ends long before the limit.
 __device__ inline uint32_t wait_ready(const uint64_t* ready, uint32_t u, uint64_t tag, uint32_t polls, uint64_t w,
                                       bool& late)
 {
@@ -915,19 +917,18 @@ __device__ inline uint32_t wait_ready(const uint64_t* ready, uint32_t u, uint64_
     return uint32_t(w & ((1u << kReadyCountBits) - 1u));
 }
 
-// Unit counts of the single-launch compress, from the ready words of units [0, u_end)
-// (each thread takes every kPlaceThreads-th, 4 loads in flight): the escapes before
-// u_first (acc), before u0 (accs) and before c0 (accc); the counts of the group's own
-// units go to s_ucnt.
+// Unit counts of the single-launch compress, from the ready words of units [c0, u_end)
+// (c0: the first unit of the call of the group's first unit; each thread takes every
+// kPlaceThreads-th, 4 loads in flight): the escapes from c0 to u_first (acc) and to u0
+// (accs); the counts of the group's own units go to s_ucnt.
 template <class Args>
-__device__ inline bool wait_unit_counts(const Args& a, uint32_t u_first, uint32_t u_end, uint32_t u0, uint32_t c0,
-                                        uint32_t tid, uint32_t* s_ucnt, uint32_t& acc, uint32_t& accs,
-                                        uint32_t& accc)
+__device__ inline bool wait_unit_counts(const Args& a, uint32_t c0, uint32_t u_first, uint32_t u_end, uint32_t u0,
+                                        uint32_t tid, uint32_t* s_ucnt, uint32_t& acc, uint32_t& accs)
 {
     constexpr uint32_t kPer = 4;
     bool late = false;
-    acc = accs = accc = 0;
-    for (uint32_t base = 0; base < u_end; base += kPer * kPlaceThreads) {
+    acc = accs = 0;
+    for (uint32_t base = c0; base < u_end; base += kPer * kPlaceThreads) {
         uint64_t w[kPer];
 #pragma unroll
         for (uint32_t k = 0; k < kPer; k++) {
@@ -942,22 +943,22 @@ __device__ inline bool wait_unit_counts(const Args& a, uint32_t u_first, uint32_
             if (u < u_first) acc += c;
             else s_ucnt[u - u_first] = c;
             if (u < u0) accs += c;
-            if (u < c0) accc += c;
         }
     }
     return late;
 }
 
 // Positions count from the first escape of the unit's call: each workgroup sums the
-// unit counts before its first unit, before the first unit of that unit's segment and
-// before the first unit of that unit's call.
+// unit counts of its first unit's call before its first unit and before the first unit
+// of that unit's segment (a call or segment that starts inside the group starts at the
+// counts of the group's units before it).
 // kWait (single-launch compress): the counts come from the encoders' ready words, waited
 // for; the encoder output read after that (half-block counts, staged escapes) is read
 // with agent-scope loads.
 template <bool kWait, class Args>
-__device__ inline void place_group(const Args& a, uint32_t group)
+__device__ inline void place_group(const Args& a, uint32_t group, bool one_call)
 {
-    __shared__ uint32_t s_red[3][kPlaceUnits];
+    __shared__ uint32_t s_red[2][kPlaceUnits];
     __shared__ uint32_t s_ucnt[kPlaceUnits];
     __shared__ uint32_t s_late;
     __shared__ __attribute__((aligned(16))) uint8_t s_head[kPlaceUnits][1024];   // staged escapes, per wave
@@ -970,47 +971,44 @@ __device__ inline void place_group(const Args& a, uint32_t group)
     const uint8_t* stage = a.stage + uint64_t(unit) * kUnit;   // the unit's escapes, contiguous
     uint2 head = make_uint2(0, 0);
     uint32_t hc[2 * kWaves];   // the unit's half-block escape counts
-    uint32_t acc = 0, accs = 0, accc = 0;
-    int s, s_first;
-    uint32_t u0, c0;
+    uint32_t acc = 0, accs = 0;
+    const int s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
+    const int s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
+    const uint32_t u0 = a.seg[s_first].unit0;             // first unit of the first unit's segment
+    // ... and of its call (0 in a launch of one call, which the caller read with the
+    // launch's first arguments: no dependent argument loads before the first ready words
+    // are requested)
+    const uint32_t c0 = one_call ? 0u : a.call[a.seg[s_first].call].unit0;
     if constexpr (!kWait) {
         head = active ? reinterpret_cast<const uint2*>(stage)[lane] : make_uint2(0, 0);
 #pragma unroll
         for (uint32_t k = 0; k < 2 * kWaves; k++) hc[k] = active ? a.counts[slot0 + k] : 0u;
         if (lane == 0) s_ucnt[wave] = active ? a.unit_counts[unit] : 0u;
-        uint4 q[kPrefixLoads];     // unit_counts[0 .. u_first), 4 per load (u_first is a multiple of 8)
+        // unit_counts[c0 .. u_first), 4 per load from the multiple of 4 at or below c0
+        // (u_first is a multiple of 8)
+        const uint32_t q0 = c0 & ~3u;
+        uint4 q[kPrefixLoads];
 #pragma unroll
         for (uint32_t r = 0; r < kPrefixLoads; r++) {
-            const uint32_t i = 4 * (tid + r * kPlaceThreads);
+            const uint32_t i = q0 + 4 * (tid + r * kPlaceThreads);
             q[r] = i < u_first ? *reinterpret_cast<const uint4*>(a.unit_counts + i) : make_uint4(0, 0, 0, 0);
         }
-        // segment lookups meanwhile
-        s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
-        s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
-        u0 = a.seg[s_first].unit0;
-        c0 = a.call[a.seg[s_first].call].unit0;
-        // escapes before the group's first unit, the first unit of its segment and of its call
 #pragma unroll
         for (uint32_t r = 0; r < kPrefixLoads; r++) {
-            const uint32_t i = 4 * (tid + r * kPlaceThreads);
+            const uint32_t i = q0 + 4 * (tid + r * kPlaceThreads);
             const uint32_t v[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
 #pragma unroll
             for (uint32_t k = 0; k < 4; k++) {
-                acc += v[k];
-                if (i + k < u0) accs += v[k];
-                if (i + k < c0) accc += v[k];
+                if (i + k >= c0) acc += v[k];
+                if (i + k >= c0 && i + k < u0) accs += v[k];
             }
         }
     } else {
-        s = find_segment<&CSeg::unit0>(a.seg, a.nseg, active ? unit : a.total_units - 1);
-        s_first = find_segment<&CSeg::unit0>(a.seg, a.nseg, u_first);
-        u0 = a.seg[s_first].unit0;
-        c0 = a.call[a.seg[s_first].call].unit0;
         const uint32_t u_end = min(u_first + kPlaceUnits, a.total_units);
         if (tid == 0) s_late = 0;
         if (tid < kPlaceUnits && u_first + tid >= u_end) s_ucnt[tid] = 0;
         __syncthreads();
-        const bool late = wait_unit_counts(a, u_first, u_end, u0, c0, tid, s_ucnt, acc, accs, accc);
+        const bool late = wait_unit_counts(a, c0, u_first, u_end, u0, tid, s_ucnt, acc, accs);
         if (late) s_late = 1;   // any thread; read after the barrier below
     }
     const CSeg sg = a.seg[s];
@@ -1021,12 +1019,10 @@ __device__ inline void place_group(const Args& a, uint32_t group)
     for (int o = 32; o > 0; o >>= 1) {
         acc += __shfl_xor(acc, o, 64);
         accs += __shfl_xor(accs, o, 64);
-        accc += __shfl_xor(accc, o, 64);
     }
     if (lane == 0) {
         s_red[0][wave] = acc;
         s_red[1][wave] = accs;
-        s_red[2][wave] = accc;
     }
     if constexpr (!kWait) reinterpret_cast<uint2*>(s_head[wave])[lane] = head;
     __syncthreads();
@@ -1046,17 +1042,17 @@ __device__ inline void place_group(const Args& a, uint32_t group)
         wave_lds_sync();
     }
     if (!active) return;
-    uint32_t pre = 0, first_base = 0, call_base = 0;
+    uint32_t pre = 0, first_base = 0;
 #pragma unroll
     for (uint32_t w = 0; w < kPlaceUnits; w++) {
         pre += s_red[0][w];
         first_base += s_red[1][w];
-        call_base += s_red[2][w];
     }
     // escapes before this unit, before its segment's first unit and before its call's
-    // first unit (launch-wide): a segment or call that starts inside the group starts at
-    // `pre` plus the units of the group before it; otherwise it holds the group's first
-    // unit, and its start was summed above
+    // first unit, counted from the first escape of the group's first call: a segment or
+    // call that starts inside the group starts at `pre` plus the units of the group
+    // before it; otherwise it holds the group's first unit, and its start was summed
+    // above (0 for the call)
     const CCall& c = a.call[sg.call];
     uint32_t upos = pre;
     for (uint32_t w = 0; w < wave; w++) upos += s_ucnt[w];
@@ -1065,7 +1061,7 @@ __device__ inline void place_group(const Args& a, uint32_t group)
         base = pre;
         for (uint32_t w = 0; w < sg.unit0 - u_first; w++) base += s_ucnt[w];
     }
-    uint32_t cbase = call_base;
+    uint32_t cbase = 0;
     if (c.unit0 >= u_first) {
         cbase = pre;
         for (uint32_t w = 0; w < c.unit0 - u_first; w++) cbase += s_ucnt[w];
@@ -1085,23 +1081,58 @@ __device__ inline void place_group(const Args& a, uint32_t group)
     }
 }
 
-__global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a) { place_group<false>(a, blockIdx.x); }
+__global__ __launch_bounds__(kPlaceThreads) void place_direct_kernel(const CArgs a)
+{
+    place_group<false>(a, blockIdx.x, a.ncalls <= 1);
+}
 
-// Compress in one launch: workgroups 0 .. total_units - 1 encode (as encode_kernel) and
-// publish each unit's escape count in its ready word; the last ceil(total_units / 8)
-// place (as place_direct_kernel) once the ready words they need carry this call's tag.
-// Placers are dispatched last group first: the group with the most ready words to read
-// (all units before it) starts while the last encoders still run, so only the last few
-// words are left to wait for when they finish; the early groups, dispatched last, read
-// few words.  (In group order the last placer started when the last encoders ended and
-// then read all 7168 words of a 117 Mi-value launch in rounds: 5.4 us of the launch's
-// 7.7 us after its last encoder.)
+// Compress in one launch: total_units workgroups encode (as encode_kernel) and publish
+// each unit's escape count in its ready word; ceil(total_units / 8) place (as
+// place_direct_kernel) once the ready words they need carry this call's tag.
+// The grid interleaves the two roles, in unit order: the workgroup that places group c
+// (units 8c .. 8c + 7) comes right after the encoder of unit 8c + 8 + kPlaceLag, so its
+// units were encoded about one generation of workgroups earlier and it finds their
+// counts ready while later units are still being encoded.  The last kTailGroups groups
+// (all of them in a launch of up to 4096 units) are placed after the last encoder, last
+// group first: they fill the slots the last generation of encoders frees, and the last
+// group, which has the most ready words of its call to read, starts while the last
+// encoders still run.  Every placer comes after every encoder it waits for, and encoders
+// wait for nothing, so every wait ends.
+// Measured on 32 chunk calls of 7 x 2 Mi values: launches of 8 calls with every placer
+// at the end took 317.9 us, interleaved launches of 16 calls 306.2 us (32 calls per
+// launch were no faster than 16).  A lag of 512 units left placers waiting in slots the
+// encoders needed (336 us); 1024 to 2048 measured alike.  No tail groups: 310.1 us.
+constexpr uint32_t kPlaceLag = 1024;   // units: about one generation of encoders
+constexpr uint32_t kTailGroups = 512;  // groups placed after the last encoder (all, if fewer)
+
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void compress_single_kernel(const CArgs a)
 {
     static_assert(kEncThreads == kPlaceThreads, "both roles use the same workgroup size");
-    if (blockIdx.x < a.total_units) encode_unit<true>(a, blockIdx.x);
-    else place_group<true>(a, gridDim.x - 1 - blockIdx.x);
+    constexpr uint32_t L = kPlaceLag, Q = kPlaceUnits;
+    const uint32_t E = a.total_units, b = blockIdx.x;
+    const bool one_call = a.ncalls <= 1;   // next to total_units in the arguments: one load
+    const uint32_t groups = (E + Q - 1) / Q;
+    // groups placed before the last encoder: 0 .. interleaved - 1
+    const uint32_t interleaved = min(E >= L + Q ? (E - L) / Q : 0u, groups > kTailGroups ? groups - kTailGroups : 0u);
+    bool place = false;
+    uint32_t idx = b;                              // the unit or group of this workgroup
+    if (b >= E + interleaved) {                    // after the last encoder, last group first
+        place = true;
+        idx = groups - 1 - (b - E - interleaved);
+    } else if (b >= L + Q) {
+        const uint32_t r = b - L - Q;
+        if (r >= (Q + 1) * interleaved) {          // encoders after the interleaved placers
+            idx = b - interleaved;
+        } else {                                   // cycles of one placer then Q encoders
+            const uint32_t cycle = r / (Q + 1), pos = r % (Q + 1);
+            place = pos == 0;
+            idx = place ? cycle : L + Q + Q * cycle + pos - 1;
+        }
+    }
+    // one call site per role: the kernel's code stays the size of the two roles
+    if (place) place_group<true>(a, idx, one_call);
+    else encode_unit<true>(a, idx);
 }
 
 

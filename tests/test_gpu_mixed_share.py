@@ -1,5 +1,5 @@
-"""The reduce-scatter share in the benchmark's launch shapes (8 chunk calls per compress
-launch, every chunk in one decode-accumulate launch) with peers of every kind a receiver
+"""The reduce-scatter share in the benchmark's launch shapes (up to 16 chunk calls per
+compress launch, every chunk in one decode-accumulate launch) with peers of every kind a receiver
 can meet: Gaussian shards under their own plan, random bits (uncoded blocks), an
 activation-like shard with zeros, outliers and special values, an all-zero shard, a
 shard coded under a plan for another scale, and a shard whose blocks alternate between
@@ -50,7 +50,7 @@ def test_mixed_peers_in_benchmark_launch_shapes(Z):
     S = Z.static_size(chunk)
     static = torch.full((nch * P * S,), 0xAA, dtype=torch.uint8, device="cuda")
     esc = torch.full((nch * P * chunk,), 0xAA, dtype=torch.uint8, device="cuda")
-    ws = torch.zeros(Z.workspace_size(8 * P * chunk, 8 * P), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(Z.workspace_size(16 * P * chunk, 16 * P), dtype=torch.uint8, device="cuda")
     n_esc = torch.full((nch, P + 1), -1, dtype=torch.int64, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     Z.PreparedCompressChunks([[p[c * chunk:(c + 1) * chunk] for p in peers] for c in range(nch)],
@@ -60,8 +60,8 @@ def test_mixed_peers_in_benchmark_launch_shapes(Z):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     tables = [np.array(p.exponents, np.uint8) for p in plans]
-    # chunks in the first launch, at its end, and in the second launch, byte for byte
-    for c in (0, 7, 9):
+    # chunks at the launch's start, in its middle and at its end, byte for byte
+    for c in (0, 7, 11):
         segs = [x[c * chunk:(c + 1) * chunk] for x in peers_h]
         st, e, ne, rc = O.compress_batch(segs, tables)
         got_st = static[c * P * S:(c + 1) * P * S].cpu().numpy()

@@ -871,7 +871,7 @@ def test_compress_in_captured_graph(Z):
 
 
 # ------------------------------------------------------------------------------------
-# chunk sequences whose calls share launches (up to 8 calls per launch)
+# chunk sequences whose calls share launches (up to 16 calls and 128 segments per launch)
 # ------------------------------------------------------------------------------------
 def long_chunk_sequence(nchunks=11, S=3, seed=0):
     # ragged, tiny and empty segments; chunk 4 is all empty (a launch of its own) and
@@ -895,23 +895,57 @@ def batch_workspace(Z, chunks):
 
 
 def test_compress_chunks_shared_launches(Z):
-    # 20 calls: a launch holds at most 16
-    chunks, plans = long_chunk_sequence(nchunks=20)
+    # 40 calls: a launch holds at most 16
+    chunks, plans = long_chunk_sequence(nchunks=40)
     print("chunks sharing launches", [[b.size for b in ch] for ch in chunks], flush=True)
     assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
 
 
 def test_compress_chunks_shared_launches_many_peers(Z):
-    # 7 segments per chunk: at most 18 chunks fit the 128-segment launch, 16 calls at most
+    # 7 segments per chunk: 16 chunks (112 segments) per launch, then the last 4
     rng = np.random.default_rng(5)
     chunks = [[W.gaussian_bf16(int(rng.choice([4096, 20000, 65536])), 1e-3, 4000 + 7 * k + i) for i in range(7)]
-              for k in range(20)]
+              for k in range(36)]
     plans = [Z.plan(sigma=1e-3)] * 7
     assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
 
 
 def test_compress_chunks_shared_launches_two_launch_path(Z, two_launches):
     chunks, plans = long_chunk_sequence(seed=2)
+    assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
+
+
+@pytest.mark.parametrize("units", [1031, 1032, 1033, 1040, 1041, 1057])
+def test_single_call_around_the_placer_lag(Z, units):
+    # a call of `units` encoding workgroups (16384 values each, the last one ragged): the
+    # placing workgroups of its first groups are interleaved with its encoders once the
+    # call has more than 1032 units, those of the last ones follow the last encoder
+    n = units * 16384 - 777
+    print(f"single call of {units} units", flush=True)
+    x = W.gaussian_bf16(n, 0.02, 7000 + units)
+    p = Z.plan(sigma=0.02)
+    r = gpu_compress(Z, [x], [p])
+    check_against_oracle(Z, [x], [p], r)
+
+
+def test_compress_chunks_interleaved_across_calls(Z):
+    # 12 calls of 3 ragged segments (about 9300 units) in one launch: placing groups that
+    # span two calls, interleaved with the encoders of later calls
+    rng = np.random.default_rng(11)
+    chunks = [[W.gaussian_bf16(int((1 << 22) + rng.integers(-50000, 50000)), (0.02, 1.0, 1e-3)[i], 8000 + 3 * k + i)
+               for i in range(3)] for k in range(12)]
+    plans = [Z.plan(sigma=s) for s in (0.02, 1.0, 1e-3)]
+    print("interleaved calls", [[b.size for b in ch] for ch in chunks], flush=True)
+    assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
+
+
+def test_compress_chunks_interleaved_two_launch_path(Z, two_launches):
+    # the same launch shape through encode_kernel + place_direct_kernel: each placing
+    # group sums only the units of its call (more than 16384 units in the launch)
+    rng = np.random.default_rng(12)
+    chunks = [[W.gaussian_bf16(int((1 << 24) + rng.integers(-50000, 50000)), 1e-3, 8100 + 3 * k + i)
+               for i in range(3)] for k in range(6)]
+    plans = [Z.plan(sigma=1e-3)] * 3
     assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
 
 
