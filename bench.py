@@ -4,7 +4,7 @@
 One step = the whole hot path over the reduce-scatter receive share, the largest
 workload that fits one GPU: 7 peer shards of 64 Mi BF16 values (N(0, 1e-3)) and the
 local shard.  Plan the 7 tables on the host, compress the peer shards in 32 chunks of
-2 Mi values (one compress call per chunk, one segment per peer; 8 chunks share a
+2 Mi values (one compress call per chunk, one segment per peer; 16 chunks share a
 launch), then decode the 7 compressed shards of every chunk and add them in fp32, in
 peer order, to the local shard, rounding once to BF16.  Inputs are resident in HBM
 before the timed region; the step's working set (~1.7 GB) is far larger than the
@@ -21,7 +21,9 @@ Printed (one JSON line on stdout):
              back-to-back passes, against the 8 TB/s HBM peak; traffic: the HBM bytes
              per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
              (profiles/pmc_traffic_rs_512m.txt; null when that was taken on other kernel
-             sources); roofline_other_op for decode-accumulate;
+             sources); roofline_other_op for decode-accumulate; each also beside the
+             rate a plain streaming kernel of the same read/write mix reaches on this
+             GPU (stream_ceiling_GBps; all the probes' rates in stream_ceilings_GBps);
   cpu_baseline  the plain C oracle on the host's cores, on a bounded sample of the
              same workload (4 of the 32 chunks), 1 thread and all threads;
   per_config every workload (1 Mi chunk, 64 Mi gradient bucket, activations with
@@ -261,7 +263,7 @@ class RSShare:
         self.esc = torch.empty(self.nch * P * chunk, dtype=torch.uint8, device="cuda")
         self.n_esc = torch.zeros(self.nch, P + 1, dtype=torch.int64, device="cuda")
         self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
-        # 8 chunks (56 segments) share a compress launch, with a workspace that holds them
+        # 16 chunks (112 segments) share a compress launch, with a workspace that holds them
         self.per_launch = COMPRESS_CALLS_PER_LAUNCH
         self.ws = torch.zeros(Z.workspace_size(self.per_launch * P * chunk, self.per_launch * P), dtype=torch.uint8,
                               device="cuda")
@@ -603,6 +605,44 @@ def copy_ceiling(torch, iters=10):
     torch.cuda.empty_cache()
     return round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
 
+
+# Streaming probes (libzcprobe.so, built beside the codec): plain kernels that move memory
+# in the codec's shapes with nothing to compute.  Each rate is bytes read plus written per
+# second over 1 GiB buffers: the rate the same GPU reaches for that mix.
+PROBE_KINDS = {"copy": 0, "read": 1, "write": 2, "mix_16_12": 3, "streams_8_1": 4}
+
+
+def stream_ceilings(torch, iters=10):
+    import ctypes
+    path = os.path.join(ROOT, "lossless_bf16_exponent_codec_amd", "libzcprobe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run python -m lossless_bf16_exponent_codec_amd.build")
+    lib = ctypes.CDLL(path)
+    lib.zcprobe_launch.restype = ctypes.c_int
+    lib.zcprobe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.zcprobe_moved_bytes.restype = ctypes.c_uint64
+    lib.zcprobe_moved_bytes.argtypes = [ctypes.c_int, ctypes.c_uint64]
+    nbytes = 1 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, kind in PROBE_KINDS.items():
+        def launch(_k=None, kind=kind):
+            r = lib.zcprobe_launch(kind, a.data_ptr(), b.data_ptr(), nbytes, stream)
+            if r != 0:
+                raise RuntimeError(f"zcprobe_launch({name}) returned {r}")
+        settle(torch, launch)
+        t = Timer(torch)
+        for _ in range(iters):
+            e = t.start()
+            launch()
+            t.stop(e)
+        out[name] = round(lib.zcprobe_moved_bytes(kind, nbytes) / (median(t.ms()) * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------------------------
@@ -1087,7 +1127,7 @@ def main(argv=None) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "rs_512m: reduce-scatter receive share, 7 peer shards x 67108864 BF16 values "
-                               "N(0, 1e-3) compressed in 32 chunks of 2097152 values (8 chunks per launch), then "
+                               "N(0, 1e-3) compressed in 32 chunks of 2097152 values (16 chunks per launch), then "
                                "decoded and added in fp32, peers in order, into the local shard N(0, 1e-3), one "
                                "BF16 rounding",
                    "elements_per_peer": n, "peers": P, "chunk": rs.chunk, "chunks": rs.nch},
@@ -1105,6 +1145,16 @@ def main(argv=None) -> int:
     log("copy ceiling")
     out["hbm_copy_GBps"] = copy_ceiling(torch)
     out["roofline"]["frac_of_copy"] = round(out["roofline"]["achieved"] / out["hbm_copy_GBps"], 4)
+    log("streaming probes")
+    ceil = stream_ceilings(torch)
+    out["stream_ceilings_GBps"] = ceil
+    # each kernel beside the probe of its own mix: compress reads 2 B and writes ~1.4 B per
+    # value (probe: 16 B read, 12 B written); decode-accumulate reads 8 streams (7 peers and
+    # the local shard) and writes one (probe: 8 x 16 B read, 16 B written)
+    for key, probe in (("roofline", "mix_16_12"), ("roofline_other_op", "streams_8_1")):
+        out[key]["stream_ceiling_GBps"] = ceil[probe]
+        out[key]["stream_ceiling_probe"] = probe
+        out[key]["frac_of_stream_ceiling"] = round(out[key]["achieved"] / ceil[probe], 4)
     from oracle import oracle as O
     if not args.no_extra:
         per = {}

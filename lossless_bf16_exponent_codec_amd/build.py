@@ -1,4 +1,5 @@
-"""Builds libzipccl.so in-tree with hipcc for gfx950.
+"""Builds libzipccl.so in-tree with hipcc for gfx950, and libzcprobe.so, the benchmark's
+streaming probes (plain memory-moving kernels, no part of the codec).
 
     python -m lossless_bf16_exponent_codec_amd.build [--save-temps DIR]
 """
@@ -16,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzipccl.so")
 SOURCES = [os.path.join(CSRC, "zipccl_kernels.hip"), os.path.join(CSRC, "zipccl_host.cpp")]
+PROBE_LIB = os.path.join(PKG, "libzcprobe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
 ARCH = "gfx950"
 
 
@@ -26,7 +29,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str = LIB, save_temps: str | None = None) -> list:
+def command(out: str = LIB, save_temps: str | None = None, sources=None) -> list:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed FP32 instructions stay off: the codec needs none and some of their
            # forms are not trusted on this hardware
@@ -36,7 +39,7 @@ def command(out: str = LIB, save_temps: str | None = None) -> list:
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
         cmd += ["-save-temps=obj"]
-    cmd += ["-x", "hip"] + SOURCES
+    cmd += ["-x", "hip"] + (SOURCES if sources is None else sources)
     return cmd
 
 
@@ -50,12 +53,24 @@ def build(out: str = LIB, save_temps: str | None = None, verbose: bool = False) 
     return out
 
 
+def build_probe(out: str = PROBE_LIB, verbose: bool = False) -> str:
+    """The benchmark's streaming probes (libzcprobe.so)."""
+    cmd = command(out, sources=PROBE_SOURCES)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--save-temps", default=None)
     ap.add_argument("--out", default=LIB)
+    ap.add_argument("--no-probe", action="store_true", help="build libzipccl.so only")
     args = ap.parse_args(argv)
     build(args.out, args.save_temps, verbose=True)
+    if not args.no_probe:
+        build_probe(verbose=True)
     return 0
 
 

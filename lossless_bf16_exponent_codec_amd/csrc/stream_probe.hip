@@ -1,0 +1,133 @@
+// Streaming probes for the benchmark (not part of the codec): plain kernels that move
+// memory in the shapes the codec's kernels do, so that a launch's HBM rate can be set
+// beside what a kernel with nothing to compute reaches on the same GPU.
+//
+// Every probe uses 16-byte non-temporal lane accesses over buffers of `bytes` bytes
+// (src read, dst written; both at least `bytes` long, 256-byte aligned, bytes a multiple
+// of 2^20):
+//   ZCPROBE_COPY        read src, write dst (1 : 1)
+//   ZCPROBE_READ        read src (a word is written only if an impossible xor comes out)
+//   ZCPROBE_WRITE       write dst
+//   ZCPROBE_MIX_16_12   compress-like: per 16 bytes read from the first half of src, 8 + 4
+//                       bytes written to two sections of dst
+//   ZCPROBE_STREAMS_8_1 decode-accumulate-like: 8 input streams (src in 8 equal parts,
+//                       16 bytes from each) xor-ed into one output stream
+// zcprobe_moved_bytes(kind, bytes) gives the bytes one launch reads plus writes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+constexpr int ZCPROBE_COPY = 0, ZCPROBE_READ = 1, ZCPROBE_WRITE = 2, ZCPROBE_MIX_16_12 = 3, ZCPROBE_STREAMS_8_1 = 4;
+
+__global__ __launch_bounds__(256) void copy_k(const v4u* __restrict__ a, v4u* __restrict__ b, uint64_t n4)
+{
+    const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
+}
+
+__global__ __launch_bounds__(256) void read_k(const v4u* __restrict__ a, uint32_t* __restrict__ out, uint64_t n4)
+{
+    const uint64_t i = uint64_t(blockIdx.x) * 1024 + threadIdx.x;
+    v4u v[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = i + 256 * k < n4 ? __builtin_nontemporal_load(a + i + 256 * k) : v4u{0, 0, 0, 0};
+    uint32_t acc = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    if (acc == 0x9E3779B9u && v[0].x == 0x7F4A7C15u) out[0] = acc;   // keeps the loads; never true for the filled input
+}
+
+__global__ __launch_bounds__(256) void write_k(v4u* __restrict__ b, uint64_t n4)
+{
+    const uint64_t i = uint64_t(blockIdx.x) * 1024 + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+        if (i + 256 * k < n4) __builtin_nontemporal_store(v4u{unsigned(k), 1u, 2u, 3u}, b + i + 256 * k);
+}
+
+__global__ __launch_bounds__(256) void mix_k(const v4u* __restrict__ a, uint8_t* __restrict__ b, uint64_t m4)
+{
+    const uint64_t i = uint64_t(blockIdx.x) * 1024 + threadIdx.x;
+    v4u v[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = i + 256 * k < m4 ? __builtin_nontemporal_load(a + i + 256 * k) : v4u{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint64_t j = i + 256 * k;
+        if (j < m4) {
+            __builtin_nontemporal_store(v2u{v[k].x, v[k].y}, reinterpret_cast<v2u*>(b) + j);           // 8 B: A-like
+            __builtin_nontemporal_store(v[k].z ^ v[k].w, reinterpret_cast<uint32_t*>(b + 8 * m4) + j);   // 4 B: plane-like
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void streams_k(const v4u* __restrict__ a, v4u* __restrict__ b, uint64_t q4)
+{
+    const uint64_t j = uint64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (j >= q4) return;
+    v4u s = __builtin_nontemporal_load(a + j);
+#pragma unroll
+    for (int q = 1; q < 8; q++) s ^= __builtin_nontemporal_load(a + j + q * q4);
+    __builtin_nontemporal_store(s, b + j);
+}
+
+bool valid(int kind, const void* src, void* dst, uint64_t bytes)
+{
+    if (kind < ZCPROBE_COPY || kind > ZCPROBE_STREAMS_8_1) return false;
+    if (bytes == 0 || bytes % (1u << 20) != 0) return false;
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 256 != 0) return false;
+    return dst != nullptr && (kind == ZCPROBE_WRITE || src != nullptr);   // every probe writes dst
+}
+
+}  // namespace
+
+// Bytes one launch of `kind` over buffers of `bytes` bytes reads plus writes (0: invalid kind).
+extern "C" uint64_t zcprobe_moved_bytes(int kind, uint64_t bytes)
+{
+    const uint64_t n4 = bytes / 16;
+    switch (kind) {
+        case ZCPROBE_COPY: return 2 * bytes;
+        case ZCPROBE_READ: return bytes;
+        case ZCPROBE_WRITE: return bytes;
+        case ZCPROBE_MIX_16_12: return (n4 / 2) * 28;
+        case ZCPROBE_STREAMS_8_1: return (n4 / 8) * 16 * 9;
+        default: return 0;
+    }
+}
+
+// Launches one probe on `stream` (a hipStream_t; null: the default stream).  READ writes
+// at most one word, at dst (at least 4 bytes).  Returns a hipError_t value (0: launched);
+// an invalid kind, size or alignment returns hipErrorInvalidValue and launches nothing.
+extern "C" int zcprobe_launch(int kind, const void* src, void* dst, uint64_t bytes, void* stream)
+{
+    if (!valid(kind, src, dst, bytes)) return int(hipErrorInvalidValue);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint64_t n4 = bytes / 16;
+    const v4u* a = static_cast<const v4u*>(src);
+    switch (kind) {
+        case ZCPROBE_COPY:
+            hipLaunchKernelGGL(copy_k, dim3(uint32_t((n4 + 255) / 256)), dim3(256), 0, s, a, static_cast<v4u*>(dst), n4);
+            break;
+        case ZCPROBE_READ:
+            hipLaunchKernelGGL(read_k, dim3(uint32_t((n4 + 1023) / 1024)), dim3(256), 0, s, a, static_cast<uint32_t*>(dst), n4);
+            break;
+        case ZCPROBE_WRITE:
+            hipLaunchKernelGGL(write_k, dim3(uint32_t((n4 + 1023) / 1024)), dim3(256), 0, s, static_cast<v4u*>(dst), n4);
+            break;
+        case ZCPROBE_MIX_16_12: {   // reads the first half of src; writes 12 / 16 of that to dst
+            const uint64_t m4 = n4 / 2;
+            hipLaunchKernelGGL(mix_k, dim3(uint32_t((m4 + 1023) / 1024)), dim3(256), 0, s, a, static_cast<uint8_t*>(dst), m4);
+            break;
+        }
+        case ZCPROBE_STREAMS_8_1: {   // src in 8 parts of q4 lanes; dst gets q4 lanes
+            const uint64_t q4 = n4 / 8;
+            hipLaunchKernelGGL(streams_k, dim3(uint32_t((q4 + 255) / 256)), dim3(256), 0, s, a, static_cast<v4u*>(dst), q4);
+            break;
+        }
+    }
+    return int(hipGetLastError());
+}

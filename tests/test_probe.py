@@ -1,0 +1,64 @@
+"""The benchmark's streaming probes (libzcprobe.so): the library loads and exports its two
+calls, the byte counts the benchmark divides by, argument checks on the host (no GPU
+needed), and on the GPU that the copy and the 8-stream probe move the bytes they claim."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PATH = os.path.join(ROOT, "lossless_bf16_exponent_codec_amd", "libzcprobe.so")
+COPY, READ, WRITE, MIX, STREAMS = 0, 1, 2, 3, 4
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(PATH), "libzcprobe.so is built by python -m lossless_bf16_exponent_codec_amd.build"
+    L = ctypes.CDLL(PATH)
+    L.zcprobe_launch.restype = ctypes.c_int
+    L.zcprobe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    L.zcprobe_moved_bytes.restype = ctypes.c_uint64
+    L.zcprobe_moved_bytes.argtypes = [ctypes.c_int, ctypes.c_uint64]
+    return L
+
+
+def test_moved_bytes(lib):
+    G = 1 << 30
+    assert lib.zcprobe_moved_bytes(COPY, G) == 2 * G
+    assert lib.zcprobe_moved_bytes(READ, G) == G
+    assert lib.zcprobe_moved_bytes(WRITE, G) == G
+    assert lib.zcprobe_moved_bytes(MIX, G) == G // 2 + (G // 2) * 12 // 16   # half read, 12/16 of it written
+    assert lib.zcprobe_moved_bytes(STREAMS, G) == G + G // 8                  # 8 parts read, one part written
+    assert lib.zcprobe_moved_bytes(5, G) == 0
+
+
+def test_bad_arguments_launch_nothing(lib):
+    bad = 1   # hipErrorInvalidValue
+    p = 1 << 20   # an aligned host-side stand-in: every call below is refused before any launch
+    assert lib.zcprobe_launch(7, p, p, MiB, None) == bad          # no such probe
+    assert lib.zcprobe_launch(COPY, p, p, MiB + 16, None) == bad  # not a multiple of 2^20
+    assert lib.zcprobe_launch(COPY, p, p, 0, None) == bad
+    assert lib.zcprobe_launch(COPY, p + 16, p, MiB, None) == bad  # not 256-byte aligned
+    assert lib.zcprobe_launch(COPY, None, p, MiB, None) == bad    # nothing to read
+    assert lib.zcprobe_launch(WRITE, p, None, MiB, None) == bad   # nothing to write
+
+
+@pytest.mark.gpu
+def test_copy_and_streams_move_their_bytes(lib):
+    import torch
+    n = 4 * MiB
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert lib.zcprobe_launch(COPY, src.data_ptr(), dst.data_ptr(), n, s) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    dst.zero_()
+    assert lib.zcprobe_launch(STREAMS, src.data_ptr(), dst.data_ptr(), n, s) == 0
+    torch.cuda.synchronize()
+    parts = src.cpu().numpy().reshape(8, n // 8)
+    want = np.bitwise_xor.reduce(parts, axis=0)
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:n // 8], want) and not got[n // 8:].any()
