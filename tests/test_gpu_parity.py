@@ -915,11 +915,12 @@ def test_compress_chunks_shared_launches_two_launch_path(Z, two_launches):
     assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
 
 
-@pytest.mark.parametrize("units", [1031, 1032, 1033, 1040, 1041, 1057])
+@pytest.mark.parametrize("units", [4096, 4097, 4104, 4105, 4111, 4200])
 def test_single_call_around_the_placer_lag(Z, units):
     # a call of `units` encoding workgroups (16384 values each, the last one ragged): the
-    # placing workgroups of its first groups are interleaved with its encoders once the
-    # call has more than 1032 units, those of the last ones follow the last encoder
+    # last 512 placing groups follow the last encoder, so the first groups' placers are
+    # interleaved with the encoders once the call has more than 4096 units (one group at
+    # 4097 to 4104 units, two at 4105)
     n = units * 16384 - 777
     print(f"single call of {units} units", flush=True)
     x = W.gaussian_bf16(n, 0.02, 7000 + units)
@@ -936,6 +937,23 @@ def test_compress_chunks_interleaved_across_calls(Z):
                for i in range(3)] for k in range(12)]
     plans = [Z.plan(sigma=s) for s in (0.02, 1.0, 1e-3)]
     print("interleaved calls", [[b.size for b in ch] for ch in chunks], flush=True)
+    assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
+
+
+def test_compress_chunks_interleaved_with_empty_and_tiny_segments(Z):
+    # 16 calls in one launch, about 5700 units, whose segments mix multi-million-value
+    # stretches with empty, 1-value, 513-value and 16385-value ones, so that interleaved
+    # placing groups start, end and span calls at segments that hold a single unit or none
+    big = [1 << 22, (1 << 22) + 4097, 3 * (1 << 20) + 1]
+    small = [0, 1, 513, 16385, 0]
+    chunks = []
+    for k in range(16):
+        ns = [big[k % 3], small[k % 5], big[(k + 1) % 3] if k % 4 else small[(k + 2) % 5]]
+        if k == 9:
+            ns = [0, 0, 0]
+        chunks.append([W.gaussian_bf16(n, (0.02, 1.0, 1e-3)[i], 8200 + 3 * k + i) for i, n in enumerate(ns)])
+    plans = [Z.plan(sigma=s) for s in (0.02, 1.0, 1e-3)]
+    print("interleaved calls with small segments", [[b.size for b in ch] for ch in chunks], flush=True)
     assert compress_chunks_vs_oracle(Z, chunks, plans, ws_bytes=batch_workspace(Z, chunks)) == 0
 
 

@@ -1,14 +1,15 @@
-"""Full-size parity on the five workloads, in the launch configuration the benchmark
-times: every compressed byte, every escape and every decoded value equals the
-oracle's; the reduce-scatter share goes through the two-stream pipeline."""
+"""Full-size parity on the workloads, in the launch configuration the benchmark times:
+every compressed byte, every escape and every decoded value equals the oracle's; the
+routed MoE dispatch is compressed by row index; the reduce-scatter share goes through
+the two-stream pipeline."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import oracle as O
 from lossless_bf16_exponent_codec_amd import workloads as W
-from tests.test_gpu_parity import (check_against_oracle, dev_bf16, first_diff, gpu_compress, gpu_decompress,
-                                   host_u16)
+from tests.test_gpu_parity import (check_against_oracle, dev_bf16, first_diff, gpu_compress, gpu_compress_gather,
+                                   gpu_decompress, host_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +35,25 @@ def test_workload_round_trip(Z, name):
     ratio = 2 * wl.n_total / (r["static_h"].size + int(r["n_esc"][-1]))
     assert ratio == 2 * wl.n_total / (st.size + esc.size)
     assert ratio > 1.35
+
+
+def test_routed_dispatch_gathered_full_size(Z):
+    # the 16384 x 7168 token matrix compressed by row index into its 8 Zipf buckets (one
+    # call, 7168 units: the placers of its first groups run among the encoders), byte for
+    # byte against the oracle's compress of the gathered rows, then decoded back
+    print("workload moe_routed_16384x7168", flush=True)
+    wl = W.moe_routed_16384x7168()
+    H = wl.extra["hidden"]
+    mat = wl.segments[0].reshape(-1, H)
+    rows = wl.extra["rows"]
+    plans = [Z.plan(sigma=s) for s in wl.sigmas]
+    res = gpu_compress_gather(Z, mat, rows, plans)
+    segs = [mat[idx].reshape(-1) for idx in rows]
+    check_against_oracle(Z, segs, plans, res)
+    outs, status = gpu_decompress(Z, res)
+    assert status == 0
+    for x, y in zip(segs, outs):
+        assert np.array_equal(x, y), first_diff(x, y)
 
 
 def test_reduce_scatter_share_pipeline(Z):
