@@ -62,3 +62,14 @@ def test_copy_and_streams_move_their_bytes(lib):
     want = np.bitwise_xor.reduce(parts, axis=0)
     got = dst.cpu().numpy()
     assert np.array_equal(got[:n // 8], want) and not got[n // 8:].any()
+    # the compress-like mix: per 16-byte lane of src's first half, its first 8 bytes to
+    # dst's first section and the xor of its last two words to the second
+    dst.zero_()
+    assert lib.zcprobe_launch(MIX, src.data_ptr(), dst.data_ptr(), n, s) == 0
+    torch.cuda.synchronize()
+    lanes = src.cpu().numpy()[:n // 2].view(np.uint32).reshape(-1, 4)
+    m = lanes.shape[0]
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:8 * m].view(np.uint32).reshape(-1, 2), lanes[:, :2])
+    assert np.array_equal(got[8 * m:12 * m].view(np.uint32), lanes[:, 2] ^ lanes[:, 3])
+    assert not got[12 * m:].any()
