@@ -609,7 +609,7 @@ def copy_ceiling(torch, iters=10):
 # Streaming probes (libzcprobe.so, built beside the codec): plain kernels that move memory
 # in the codec's shapes with nothing to compute.  Each rate is bytes read plus written per
 # second over 1 GiB buffers: the rate the same GPU reaches for that mix.
-PROBE_KINDS = {"copy": 0, "read": 1, "write": 2, "mix_16_12": 3, "streams_8_1": 4}
+PROBE_KINDS = {"copy": 0, "read": 1, "write": 2, "mix_16_12": 3, "acc_7": 4}
 
 
 def stream_ceilings(torch, iters=10):
@@ -1149,9 +1149,10 @@ def main(argv=None) -> int:
     ceil = stream_ceilings(torch)
     out["stream_ceilings_GBps"] = ceil
     # each kernel beside the probe of its own mix: compress reads 2 B and writes ~1.4 B per
-    # value (probe: 16 B read, 12 B written); decode-accumulate reads 8 streams (7 peers and
-    # the local shard) and writes one (probe: 8 x 16 B read, 16 B written)
-    for key, probe in (("roofline", "mix_16_12"), ("roofline_other_op", "streams_8_1")):
+    # value (probe: 16 B read, 12 B written); decode-accumulate reads each of 7 peers' A and
+    # plane bytes of a tile plus the local values and writes the sum (probe: the same reads
+    # and write in its workgroup and wave shape, escapes and arithmetic left out)
+    for key, probe in (("roofline", "mix_16_12"), ("roofline_other_op", "acc_7")):
         out[key]["stream_ceiling_GBps"] = ceil[probe]
         out[key]["stream_ceiling_probe"] = probe
         out[key]["frac_of_stream_ceiling"] = round(out[key]["achieved"] / ceil[probe], 4)

@@ -12,8 +12,11 @@
 //   ZCPROBE_WRITE       write dst
 //   ZCPROBE_MIX_16_12   compress-like: per 16 bytes read from the first half of src, 8 + 4
 //                       bytes written to two sections of dst
-//   ZCPROBE_STREAMS_8_1 decode-accumulate-like: 8 input streams (src in 8 equal parts,
-//                       16 bytes from each) xor-ed into one output stream
+//   ZCPROBE_ACC_7       decode-accumulate-like: one 512-thread workgroup per block of 8
+//                       tiles, one tile per wave; per tile it reads, from each of 7 peer
+//                       regions of src, 512 A bytes (8 per lane) and 192 plane bytes (a
+//                       dword in 48 of 64 lanes) from a separate plane section, plus 16
+//                       bytes per lane of a local region, and writes 16 bytes per lane
 // zcprobe_moved_bytes(kind, bytes) gives the bytes one launch reads plus writes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,7 +26,13 @@ namespace {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-constexpr int ZCPROBE_COPY = 0, ZCPROBE_READ = 1, ZCPROBE_WRITE = 2, ZCPROBE_MIX_16_12 = 3, ZCPROBE_STREAMS_8_1 = 4;
+constexpr int ZCPROBE_COPY = 0, ZCPROBE_READ = 1, ZCPROBE_WRITE = 2, ZCPROBE_MIX_16_12 = 3, ZCPROBE_ACC_7 = 4;
+constexpr int kAccPeers = 7;
+constexpr uint64_t kAccPeerTileBytes = 512 + 192;   // a tile's A and plane bytes in one peer region
+constexpr uint64_t kAccTileBytes = kAccPeers * kAccPeerTileBytes + 1024;   // of src per tile, local included
+
+// Tiles of the ACC_7 probe over buffers of `bytes` bytes (a multiple of 8).
+uint64_t acc_tiles(uint64_t bytes) { return (bytes / kAccTileBytes) & ~uint64_t(7); }
 
 __global__ __launch_bounds__(256) void copy_k(const v4u* __restrict__ a, v4u* __restrict__ b, uint64_t n4)
 {
@@ -58,19 +67,31 @@ __global__ __launch_bounds__(256) void mix_k(const v4u* __restrict__ a, uint8_t*
     __builtin_nontemporal_store(v.z ^ v.w, reinterpret_cast<uint32_t*>(b + 8 * m4) + j);   // 4 B: plane-like
 }
 
-__global__ __launch_bounds__(256) void streams_k(const v4u* __restrict__ a, v4u* __restrict__ b, uint64_t q4)
+// src: 7 peer regions of T * 704 bytes (A section of 512 T, then plane section of 192 T),
+// then the local region (1024 T); dst: T * 1024 bytes.  Grid: T / 8 workgroups.
+__global__ __launch_bounds__(512) void acc_k(const uint8_t* __restrict__ src, v4u* __restrict__ dst, uint64_t T)
 {
-    const uint64_t j = uint64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (j >= q4) return;
-    v4u s = __builtin_nontemporal_load(a + j);
+    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint64_t t = uint64_t(blockIdx.x) * 8 + wave;
+    const uint32_t c = lane & 31, q = c & 3;
+    const uint32_t pdw = q < 3 ? 2 * (8 * q + (c >> 2)) + (lane >> 5) : 0u;   // 48 lanes, 192 bytes
+    uint32_t acc = 0;
 #pragma unroll
-    for (int q = 1; q < 8; q++) s ^= __builtin_nontemporal_load(a + j + q * q4);
-    __builtin_nontemporal_store(s, b + j);
+    for (int p = 0; p < kAccPeers; p++) {
+        const uint8_t* base = src + p * kAccPeerTileBytes * T;
+        const v2u A = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(base + 512 * t) + lane);
+        const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + 512 * T + 192 * t) + pdw);
+        acc ^= A.x ^ A.y ^ w;
+    }
+    const v4u* local = reinterpret_cast<const v4u*>(src + kAccPeers * kAccPeerTileBytes * T);
+    v4u v = __builtin_nontemporal_load(local + 64 * t + lane);
+    v.x ^= acc;
+    __builtin_nontemporal_store(v, dst + 64 * t + lane);
 }
 
 bool valid(int kind, const void* src, void* dst, uint64_t bytes)
 {
-    if (kind < ZCPROBE_COPY || kind > ZCPROBE_STREAMS_8_1) return false;
+    if (kind < ZCPROBE_COPY || kind > ZCPROBE_ACC_7) return false;
     if (bytes == 0 || bytes % (1u << 20) != 0) return false;
     if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 256 != 0) return false;
     return dst != nullptr && (kind == ZCPROBE_WRITE || src != nullptr);   // every probe writes dst
@@ -87,7 +108,7 @@ extern "C" uint64_t zcprobe_moved_bytes(int kind, uint64_t bytes)
         case ZCPROBE_READ: return bytes;
         case ZCPROBE_WRITE: return bytes;
         case ZCPROBE_MIX_16_12: return (n4 / 2) * 28;
-        case ZCPROBE_STREAMS_8_1: return (n4 / 8) * 16 * 9;
+        case ZCPROBE_ACC_7: return acc_tiles(bytes) * (kAccPeers * kAccPeerTileBytes + 2 * 1024);
         default: return 0;
     }
 }
@@ -116,9 +137,10 @@ extern "C" int zcprobe_launch(int kind, const void* src, void* dst, uint64_t byt
             hipLaunchKernelGGL(mix_k, dim3(uint32_t((m4 + 255) / 256)), dim3(256), 0, s, a, static_cast<uint8_t*>(dst), m4);
             break;
         }
-        case ZCPROBE_STREAMS_8_1: {   // src in 8 parts of q4 lanes; dst gets q4 lanes
-            const uint64_t q4 = n4 / 8;
-            hipLaunchKernelGGL(streams_k, dim3(uint32_t((q4 + 255) / 256)), dim3(256), 0, s, a, static_cast<v4u*>(dst), q4);
+        case ZCPROBE_ACC_7: {
+            const uint64_t T = acc_tiles(bytes);
+            hipLaunchKernelGGL(acc_k, dim3(uint32_t(T / 8)), dim3(512), 0, s, static_cast<const uint8_t*>(src),
+                               static_cast<v4u*>(dst), T);
             break;
         }
     }

@@ -1,6 +1,7 @@
 """The benchmark's streaming probes (libzcprobe.so): the library loads and exports its two
 calls, the byte counts the benchmark divides by, argument checks on the host (no GPU
-needed), and on the GPU that the copy and the 8-stream probe move the bytes they claim."""
+needed), and on the GPU that the copy, decode-accumulate-like and mix probes move the bytes
+they claim."""
 import ctypes
 import os
 
@@ -9,7 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PATH = os.path.join(ROOT, "lossless_bf16_exponent_codec_amd", "libzcprobe.so")
-COPY, READ, WRITE, MIX, STREAMS = 0, 1, 2, 3, 4
+COPY, READ, WRITE, MIX, ACC = 0, 1, 2, 3, 4
 MiB = 1 << 20
 
 
@@ -30,7 +31,8 @@ def test_moved_bytes(lib):
     assert lib.zcprobe_moved_bytes(READ, G) == G
     assert lib.zcprobe_moved_bytes(WRITE, G) == G
     assert lib.zcprobe_moved_bytes(MIX, G) == G // 2 + (G // 2) * 12 // 16   # half read, 12/16 of it written
-    assert lib.zcprobe_moved_bytes(STREAMS, G) == G + G // 8                  # 8 parts read, one part written
+    T = (G // (7 * 704 + 1024)) // 8 * 8                                      # tiles of 512 values
+    assert lib.zcprobe_moved_bytes(ACC, G) == T * (7 * 704 + 2 * 1024)        # 7 peers' A + planes, local, out
     assert lib.zcprobe_moved_bytes(5, G) == 0
 
 
@@ -46,7 +48,7 @@ def test_bad_arguments_launch_nothing(lib):
 
 
 @pytest.mark.gpu
-def test_copy_and_streams_move_their_bytes(lib):
+def test_copy_accumulate_and_mix_probes_move_their_bytes(lib):
     import torch
     n = 4 * MiB
     src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
@@ -55,13 +57,27 @@ def test_copy_and_streams_move_their_bytes(lib):
     assert lib.zcprobe_launch(COPY, src.data_ptr(), dst.data_ptr(), n, s) == 0
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+    # the decode-accumulate-like probe: per tile, the xor of 7 peers' A words and plane
+    # dwords goes into the first word of each lane's 16 local bytes
     dst.zero_()
-    assert lib.zcprobe_launch(STREAMS, src.data_ptr(), dst.data_ptr(), n, s) == 0
+    assert lib.zcprobe_launch(ACC, src.data_ptr(), dst.data_ptr(), n, s) == 0
     torch.cuda.synchronize()
-    parts = src.cpu().numpy().reshape(8, n // 8)
-    want = np.bitwise_xor.reduce(parts, axis=0)
+    T = (n // (7 * 704 + 1024)) // 8 * 8
+    h = src.cpu().numpy()
+    lane = np.arange(64)
+    c, q = lane & 31, lane & 3
+    pdw = np.where(q < 3, 2 * (8 * q + (c >> 2)) + (lane >> 5), 0)
+    acc = np.zeros((T, 64), np.uint32)
+    for p in range(7):
+        base = h[p * 704 * T:(p + 1) * 704 * T]
+        A = base[:512 * T].view(np.uint32).reshape(T, 64, 2)
+        planes = base[512 * T:].view(np.uint32).reshape(T, 48)
+        acc ^= A[:, :, 0] ^ A[:, :, 1] ^ planes[:, pdw]
+    local = h[7 * 704 * T:7 * 704 * T + 1024 * T].view(np.uint32).reshape(T, 64, 4).copy()
+    local[:, :, 0] ^= acc
     got = dst.cpu().numpy()
-    assert np.array_equal(got[:n // 8], want) and not got[n // 8:].any()
+    assert np.array_equal(got[:1024 * T].view(np.uint32).reshape(T, 64, 4), local)
+    assert not got[1024 * T:].any()
     # the compress-like mix: per 16-byte lane of src's first half, its first 8 bytes to
     # dst's first section and the xor of its last two words to the second
     dst.zero_()
