@@ -143,9 +143,10 @@ uint64_t zipccl_workspace_size(uint64_t total_n, int nseg);
  *   workspace   device scratch, see zipccl_workspace_size.
  * With a status word the work is one kernel launch on `stream`: its encoding
  * workgroups write the fixed-size sections, stage each unit's escapes and publish the
- * unit's escape count in the workspace; its last workgroups compute the escape positions
- * from those counts (bounded wait; a wait that runs out sets ZIPCCL_STATUS_WAIT_LIMIT),
- * write the offset tables and headers and compact the escapes.  Without a status word,
+ * unit's escape count in the workspace; its placing workgroups, each behind the encoders
+ * of the units it places in the launch's grid, compute the escape positions from those
+ * counts (bounded wait; a wait that runs out sets ZIPCCL_STATUS_WAIT_LIMIT), write the
+ * offset tables and headers and compact the escapes.  Without a status word,
  * while `stream` is being captured into a graph, or with ZIPCCL_SINGLE_LAUNCH=0 in the
  * environment, the same work is two launches (encode, then place) in which nothing
  * waits, so nothing can time out unreported; above 2^28 values in one call it is encode,
@@ -212,6 +213,7 @@ zipccl_status zipccl_compress_device_plans(const zipccl_segment_t* segs, int nse
  * writes, byte for byte (each chunk's escapes and esc_offsets are its own), but
  * consecutive chunks share a kernel launch (up to 16 chunks and 128 segments per launch)
  * while the workspace holds them all, so that a launch has enough work to fill the GPU.
+ * A chunk of more than 2^28 values has a launch of its own.
  *   segs        host array of nchunks * nseg segments, chunk after chunk; 1 <= nseg <=
  *               ZIPCCL_MAX_PEERS
  *   static_out, static_cap, esc_out, esc_cap   host arrays of nchunks entries
