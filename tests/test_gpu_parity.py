@@ -995,6 +995,23 @@ def test_single_launch_wait_limit_is_reported(Z, monkeypatch):
     check_against_oracle(Z, x, p, r)
 
 
+def test_wait_limit_with_interleaved_placers(Z, monkeypatch):
+    # the same forced time-out in a launch large enough (4200 units) that the placers of its
+    # first groups run among the encoders: every placer gives up within its 4 polls per word,
+    # the launch ends, nothing is placed, and the next call is exact again
+    x = [W.gaussian_bf16(4200 * 16384 - 5, 0.02, 31)]
+    p = [Z.plan(sigma=0.02)]
+    print("wait limit, one call of 4200 units", flush=True)
+    ws = torch.zeros(Z.workspace_size(x[0].size, 1), dtype=torch.uint8, device="cuda")
+    monkeypatch.setenv("ZIPCCL_TEST_WAIT_LIMIT", "1")
+    r = gpu_compress(Z, x, p, workspace=ws)
+    assert r["status"] & Z.STATUS_WAIT_LIMIT
+    assert (r["static_h"][:64] == POISON).all()
+    monkeypatch.delenv("ZIPCCL_TEST_WAIT_LIMIT")
+    r = gpu_compress(Z, x, p, workspace=ws)
+    check_against_oracle(Z, x, p, r)
+
+
 def test_wait_limit_hook_without_status_word(Z, monkeypatch):
     # without a status word a compress takes the two-launch path, in which no workgroup
     # waits for another: the forced wait limit has nothing to act on, and the output is
