@@ -24,6 +24,8 @@ Printed (one JSON line on stdout):
              sources); roofline_other_op for decode-accumulate; each also beside the
              rate a plain streaming kernel of the same read/write mix reaches on this
              GPU (stream_ceiling_GBps; all the probes' rates in stream_ceilings_GBps);
+  pipelined_step  the same step through the two-stream pipeline (zipccl_pipeline_reduce,
+             calls back to back), beside the one-stream step;
   cpu_baseline  the plain C oracle on the host's cores, on a bounded sample of the
              same workload (4 of the 32 chunks), 1 thread and all threads;
   per_config every workload (1 Mi chunk, 64 Mi gradient bucket, activations with
@@ -391,6 +393,14 @@ def bench_rs_extra(torch, Z, rs, iters):
         pipe.reduce(rs.peers, plans, rs.local, rs.dst, rs.status)
         torch.cuda.synchronize()
         walls.append(time.perf_counter() - t0)
+    # calls back to back, as a training loop would issue them: host enqueue of one call
+    # overlaps the GPU work of the one before
+    settle(torch, lambda k: pipe.reduce(rs.peers, plans, rs.local, rs.dst, rs.status))
+    t0 = time.perf_counter()
+    for _ in range(4 * iters):
+        pipe.reduce(rs.peers, plans, rs.local, rs.dst, rs.status)
+    torch.cuda.synchronize()
+    b2b = (time.perf_counter() - t0) / (4 * iters)
     pipe.close()
     ok = rs.check()     # the pipeline's output, against torch
     wall = median(walls)
@@ -410,6 +420,7 @@ def bench_rs_extra(torch, Z, rs, iters):
         "accumulate_separate_calls_us": round(ap_ms * 1e3, 1),
         "pipeline_wall_us": round(wall * 1e6, 1),
         "pipeline_GBps_bf16_in": round(2 * P * n / wall / 1e9, 1),
+        "pipeline_back_to_back_us": round(b2b * 1e6, 1),
         "ratio": round(2 * P * n / (static_total + total_esc), 5),
         "escape_frac": round(total_esc / (P * n), 5),
         "parity_vs_torch_fp32": ok,
@@ -1196,6 +1207,14 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         log("workload rs_512m (per operation, pipeline)")
         per["rs_512m"] = bench_rs_extra(torch, Z, rs, 5)
+        # the same step through the two-stream pipeline (zipccl_pipeline_reduce: compress on one
+        # stream, decode-accumulate on the other, handed over in groups of chunks); on one GPU
+        # there is no transfer for it to overlap, so the step above runs the chunk calls on one
+        # stream and this figure stands beside it
+        pb = per["rs_512m"]["pipeline_back_to_back_us"]
+        out["pipelined_step"] = {"value": round(4 * P * n / (pb * 1e-6) / 1e9, 1), "unit": "GB/s",
+                                 "ms_per_step": round(pb * 1e-3, 4), "streams": 2,
+                                 "api": "zipccl_pipeline_reduce, calls back to back"}
         log("reduce-scatter switcher")
         per["rs_switcher"] = bench_switcher(torch, Z, W)
         out["per_config"] = per
