@@ -33,12 +33,13 @@
 //     word tagged with the call's tag; placing workgroups, interleaved in the grid about
 //     one generation of encoders behind the units they place, wait (bounded) for the
 //     ready words of their call's units up to theirs, then compute escape positions,
-//     compact the escapes and write offset tables and headers.  What one workgroup hands to another goes through agent-scope
-//     (write-through) stores and loads, so no cache-wide write-back or invalidate is
-//     needed.  Without a status word (a wait that ran out could not be reported) and
-//     under graph capture the same work is two launches that wait for nothing
-//     (encode_kernel, place_direct_kernel); above 2^28 values a one-workgroup scan kernel
-//     computes the positions and a per-block place kernel follows.
+//     compact the escapes and write offset tables and headers.  What one workgroup
+//     hands to another goes through agent-scope (write-through) stores and loads, so no
+//     cache-wide write-back or invalidate is needed.  Without a status word (a wait that
+//     ran out could not be reported) and under graph capture the same work is two launches
+//     that wait for nothing (encode_kernel, place_direct_kernel); above 2^28 values in a
+//     call a one-workgroup scan kernel computes the positions and a per-block place
+//     kernel follows.
 //     One launch may compress several independent calls (the chunks of a sequence):
 //     each segment names its call, and positions, offsets and headers count from the
 //     first escape of the call.
