@@ -29,6 +29,7 @@ constexpr uint32_t kBlockOverflow = (kBlock / kTile) * (kTile - kUncodedPlaneByt
 constexpr uint32_t kHalf = kBlock / 2;
 constexpr uint32_t kEncWaves = 8;
 constexpr uint32_t kEncThreads = 64 * kEncWaves;
+constexpr uint32_t kStageHead = 2 * kEncWaves;   // bytes: a unit's slot counts in its staged record
 
 // Compress workspace, by half-block slot: slot 8u + w belongs to wave w of workgroup
 // unit u (slots past a segment's end hold 0 escapes).  A u32 escape count per slot,
@@ -36,7 +37,9 @@ constexpr uint32_t kEncThreads = 64 * kEncWaves;
 // used only when the positions come from the scan kernel), a u32 escape count per
 // unit, a u64 ready word per unit (the single-launch compress: the call's tag above
 // the unit's escape count), then kUnit staging bytes per unit that hold its escape
-// exponents, contiguous in value order, until their positions are known.
+// exponents, contiguous in value order, until their positions are known.  The
+// single-launch compress leaves the per-slot counts alone: a unit's staging bytes open
+// with its 8 slot counts (u16 each, kStageHead bytes) and its escapes follow them.
 __host__ __device__ constexpr uint64_t ws_counts_bytes(uint64_t units) { return (32 * units + 255) & ~uint64_t(255); }
 __host__ __device__ constexpr uint64_t ws_pos_bytes(uint64_t units) { return (4 * (8 * units + 1) + 255) & ~uint64_t(255); }
 __host__ __device__ constexpr uint64_t ws_units_bytes(uint64_t units) { return (4 * (units + 1) + 255) & ~uint64_t(255); }

@@ -527,9 +527,8 @@ __device__ inline uint32_t encode_half(const Args& a, const CSeg& sg, uint32_t h
     const uint32_t run = min(half_ranks(cnt, start), kHalf);
 #pragma unroll
     for (int k = 0; k < 4; k++) stage_tile_escapes(te[k], start[k], s_esc);
-    if (lane == 0) {
-        if constexpr (kPublish) store_agent(a.counts + gh, run);
-        else a.counts[gh] = run;
+    if constexpr (!kPublish) {   // the single launch puts the count in the unit's staged record
+        if (lane == 0) a.counts[gh] = run;
     }
     if (hb == 2 * K - 1) {   // zero padding of the plane and offset sections
         const uint32_t bpad = uint32_t(round128(192ull * T) - 192ull * T);
@@ -631,28 +630,38 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
         if (full) load_full_half(sg, hb, lane, v, ignore);
         else load_partial_half(sg, hb, lane, v, ignore);
         store_uncoded_half(sg, hb, lane, v, s_esc[wave]);
-        if (lane == 0) {
-            if constexpr (kPublish) store_agent(a.counts + slot, run);
-            else a.counts[slot] = run;
+        if constexpr (!kPublish) {
+            if (lane == 0) a.counts[slot] = run;
         }
     }
     if (!kPublish && tid == 0) a.unit_counts[unit] = total;   // for the place kernel's prefix sums
     // the unit's escapes, contiguous in value order: one run per unit for the place kernel
-    uint8_t* stage = a.stage + uint64_t(unit) * kUnit + before;
     const uint8_t* esc_lds = s_esc[wave];
     if constexpr (kPublish) {
-        for (uint32_t k = lane; k < run; k += 64) store_agent(stage + k, esc_lds[k]);
-        if (!active && lane == 0) store_agent(a.counts + slot, 0u);
+        // The unit's staged record, assembled in LDS: its 8 half-block counts (u16), then
+        // its escapes.  It is written through to memory (agent scope) as whole 8-byte words,
+        // consecutive across the workgroup's lanes: per-wave byte runs written through cost
+        // each unit several partial-line writes (3.5 % of a 64 Mi-value launch with 1 %
+        // escapes, 7 % with 7.5 %).  A block holds at most kBlockOverflow escape bytes.
+        __shared__ __attribute__((aligned(16))) uint8_t s_rec[kStageHead + 4 * kBlockOverflow];
+        if (lane == 0) reinterpret_cast<uint16_t*>(s_rec)[wave] = uint16_t(run);
+        for (uint32_t k = lane; k < run; k += 64) s_rec[kStageHead + before + k] = esc_lds[k];
+        __syncthreads();
+        const uint32_t words = (kStageHead + min(total, 4 * kBlockOverflow) + 7) / 8;
+        uint64_t* rec = reinterpret_cast<uint64_t*>(a.stage + uint64_t(unit) * kUnit);
+        for (uint32_t k = tid; k < words; k += kEncThreads)
+            store_agent(rec + k, reinterpret_cast<const uint64_t*>(s_rec)[k]);
     } else {
+        uint8_t* stage = a.stage + uint64_t(unit) * kUnit + before;
         for (uint32_t k = lane; k < run; k += 64) stage[k] = esc_lds[k];
         if (!active && lane == 0) a.counts[slot] = 0;   // the scan kernel reads every slot
     }
     if (ballot(bad_row) && lane == 0) or_status(a.status, ZIPCCL_STATUS_BAD_INDEX);
     if constexpr (kPublish) {
-        // What the placing workgroup reads (the half-block counts and the staged escapes)
-        // was stored at agent scope, i.e. written through to memory; each wave waits for
-        // its stores to complete, and after the barrier the ready word is written.  (A
-        // release fence would write back the XCD's whole L2 per wave: ~20x slower.)
+        // What the placing workgroup reads (the staged record) was stored at agent scope,
+        // i.e. written through to memory; each wave waits for its stores to complete, and
+        // after the barrier the ready word is written.  (A release fence would write back
+        // the XCD's whole L2 per wave: ~20x slower.)
         wait_vm();
         __syncthreads();
         if (tid == 0)
@@ -793,16 +802,17 @@ __device__ inline bool copy_run(const CCall& c, const uint8_t* src, uint32_t p, 
 }
 
 // Copies the m staged escapes of one unit to its call's esc[p ...] (every lane of one wave).  lds:
-// the wave's 1 KB LDS buffer, holding the first 512 staged bytes; more (rare) are
-// brought from the unit's staging area (stage) 1 KB at a time, 16 bytes per lane.
-// Returns true if a byte fell at or past esc_cap.
+// the wave's 1 KB LDS buffer, holding the first 512 bytes of the unit's staging area
+// (stage), where the escapes start `skip` bytes in; more are brought from the staging
+// area 1 KB at a time, 16 bytes per lane.  Returns true if a byte fell at or past esc_cap.
 template <bool kAgent>
-__device__ inline bool place_unit_escapes(const CCall& c, uint8_t* lds, const uint8_t* stage, uint32_t p,
-                                          uint32_t m, uint32_t lane)
+__device__ inline bool place_unit_escapes(const CCall& c, uint8_t* lds, const uint8_t* stage, uint32_t skip,
+                                          uint32_t p, uint32_t m, uint32_t lane)
 {
-    bool over = copy_run(c, lds, p, 0, min(m, 512u), lane);
-    for (uint32_t c0 = 512; c0 < m; c0 += 1024) {   // rare: more than 512 escapes in the unit
-        const uint32_t o = c0 + 16 * lane;
+    const uint32_t head = 512 - skip;   // escapes in the first 512 bytes
+    bool over = copy_run(c, lds + skip, p, 0, min(m, head), lane);
+    for (uint32_t c0 = head; c0 < m; c0 += 1024) {   // more than `head` escapes in the unit
+        const uint32_t o = skip + c0 + 16 * lane;      // byte of the staging area, a multiple of 16
         uint4 x = make_uint4(0, 0, 0, 0);
         if (o + 16 <= kUnit) {
             const uint4* q = reinterpret_cast<const uint4*>(stage + o);
@@ -1037,8 +1047,13 @@ __device__ inline void place_group(const Args& a, uint32_t group, bool one_call)
         // agent-scope loads see them (an acquire fence would invalidate the L2 per wave)
         const uint64_t h = load_agent(reinterpret_cast<const uint64_t*>(stage) + lane);
         head = make_uint2(uint32_t(h), uint32_t(h >> 32));
+        // the unit's 8 half-block counts, u16 each, open its staged record (lanes 0 and 1)
 #pragma unroll
-        for (uint32_t k = 0; k < 2 * kWaves; k++) hc[k] = load_agent(a.counts + slot0 + k);
+        for (uint32_t k = 0; k < 2 * kWaves; k += 2) {
+            const uint32_t q = __builtin_amdgcn_readlane(k & 2 ? head.y : head.x, k >> 2);
+            hc[k] = q & 0xFFFFu;
+            hc[k + 1] = q >> 16;
+        }
         reinterpret_cast<uint2*>(s_head[wave])[lane] = head;
         wave_lds_sync();
     }
@@ -1070,7 +1085,8 @@ __device__ inline void place_group(const Args& a, uint32_t group, bool one_call)
     upos -= cbase;   // positions within the call's escapes
     base -= cbase;
     // the unit's escapes in one run; its blocks' positions from its 8 half-block counts
-    if (ballot(place_unit_escapes<kWait>(c, s_head[wave], stage, upos, s_ucnt[wave], lane)) && lane == 0)
+    if (ballot(place_unit_escapes<kWait>(c, s_head[wave], stage, kWait ? kStageHead : 0u, upos, s_ucnt[wave], lane)) &&
+        lane == 0)
         or_status(a.status, ZIPCCL_STATUS_ESC_OVERFLOW);
     uint32_t p = upos;
 #pragma unroll
