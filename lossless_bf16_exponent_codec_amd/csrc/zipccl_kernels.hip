@@ -782,15 +782,28 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const CArgs a)
     }
 }
 
-// Copies len bytes from LDS (src) to esc[p + off ...], lane l writing bytes l, l + 64, ...
-// so that each store instruction covers 64 consecutive bytes.  Bytes at or past esc_cap
-// are dropped (returns true if there were any).
+// Copies len bytes from LDS (src, 4-byte aligned, with at least len rounded up to 4 bytes
+// readable) to esc[p + off ...].  The dwords of the destination that the run covers
+// whole are written as dwords (lane l: dwords l, l + 64, ...; each a v_alignbyte of two
+// LDS dwords), the at most 3 bytes before and after them byte by byte: the units on
+// either side own the rest of those dwords.  Bytes at or past esc_cap are dropped
+// (returns true if there were any), byte by byte.
 __device__ inline bool copy_run(const CCall& c, const uint8_t* src, uint32_t p, uint32_t off, uint32_t len,
                                 uint32_t lane)
 {
     uint8_t* dst = c.esc + p + off;
     if (uint64_t(p) + off + len <= c.esc_cap) {   // the common case: no per-byte check
-        for (uint32_t k = lane; k < len; k += 64) dst[k] = src[k];
+        const uint32_t h = min(len, uint32_t(0u - uint32_t(reinterpret_cast<uintptr_t>(dst))) & 3u);
+        const uint32_t nd = (len - h) / 4, t0 = h + 4 * nd;   // whole dwords, then the tail
+        if (lane < h) dst[lane] = src[lane];
+        if (lane < len - t0) dst[t0 + lane] = src[t0 + lane];
+        uint32_t* dw = reinterpret_cast<uint32_t*>(dst + h);
+        const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+        if (h == 0) {
+            for (uint32_t i = lane; i < nd; i += 64) dw[i] = s32[i];
+        } else {   // dword i holds source bytes h + 4i .. h + 4i + 3 (all before t0 <= len)
+            for (uint32_t i = lane; i < nd; i += 64) dw[i] = __builtin_amdgcn_alignbyte(s32[i + 1], s32[i], h);
+        }
         return false;
     }
     bool over = false;

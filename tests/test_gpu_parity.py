@@ -793,6 +793,57 @@ def test_two_launch_path_edges_and_overflow(Z, two_launches):
     assert np.array_equal(r["static_h"], st) and np.array_equal(r["esc_h"][:1000], esc[:1000])
 
 
+def unaligned_escape_batch(Z):
+    # units whose escape runs start and end at every offset within a dword: few escapes,
+    # nearly all (more than a unit's first 496 staged bytes), random bits, ragged sizes
+    rng = np.random.default_rng(77)
+    segs, plans = [], []
+    for k, n in enumerate([5, 16384, 70001, 4097, 300000, 1, 33333]):
+        kind = k % 3
+        if kind == 0:
+            segs.append(W.gaussian_bf16(n, 0.02, 900 + k))
+            plans.append(Z.plan(sigma=0.02))
+        elif kind == 1:
+            segs.append(W.gaussian_bf16(n, 1.0, 900 + k))
+            plans.append(Z.plan(table=[1, 2, 3, 4, 5, 6, 7]))   # nearly every value escapes
+        else:
+            segs.append(rng.integers(0, 1 << 16, n, dtype=np.int64).astype(np.uint16))
+            plans.append(Z.plan(sigma=float(10 ** rng.uniform(-3, 0))))
+    return segs, plans
+
+
+@pytest.mark.parametrize("single", [True, False])
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_escape_buffer_at_unaligned_addresses(Z, monkeypatch, single, shift):
+    # the escape buffer starts `shift` bytes past a 256-byte boundary: every escape is the
+    # oracle's and no byte outside [0, cap) of the buffer is written, with room for all
+    # escapes and with a cap that cuts them off mid-dword
+    if not single:
+        monkeypatch.setenv("ZIPCCL_SINGLE_LAUNCH", "0")
+    segs, plans = unaligned_escape_batch(Z)
+    st_o, esc_o, ne_o, _ = O.compress_batch(segs, oracle_tables(plans))
+    total = sum(ne_o)
+    sizes = [s.size for s in segs]
+    tens = [dev_bf16(s) for s in segs]
+    for cap in (total + 5, total - 4097):
+        static = torch.full((sum(Z.static_size(n) for n in sizes),), POISON, dtype=torch.uint8, device="cuda")
+        buf = torch.full((shift + cap + 67,), POISON, dtype=torch.uint8, device="cuda")
+        esc = buf[shift:shift + cap]
+        assert esc.data_ptr() % 4 == shift
+        n_esc = torch.full((len(segs) + 1,), -1, dtype=torch.int64, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(Z.workspace_size(sum(sizes), len(segs)), dtype=torch.uint8, device="cuda")
+        Z.compress(list(zip(tens, plans)), static, esc, ws, n_esc, status, esc_cap=cap)
+        torch.cuda.synchronize()
+        h = buf.cpu().numpy()
+        kept = min(cap, total)
+        assert int(status.item()) == (0 if cap >= total else Z.STATUS_ESC_OVERFLOW)
+        assert list(n_esc.cpu().numpy()[:-1]) == ne_o
+        assert np.array_equal(static.cpu().numpy(), st_o)
+        assert np.array_equal(h[shift:shift + kept], esc_o[:kept]), first_diff(h[shift:shift + kept], esc_o[:kept])
+        assert (h[:shift] == POISON).all() and (h[shift + kept:] == POISON).all()
+
+
 def test_single_launch_overflow_status_only(Z):
     # the escape overflow is the only status bit: the placing workgroups never ran out of
     # their bounded wait
