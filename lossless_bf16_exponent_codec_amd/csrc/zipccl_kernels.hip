@@ -561,8 +561,14 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
     const bool active = hb < 2 * blocks_of(n);
 
     // Every load of the half block first.  A half block with all 2048 values loads in
-    // straight-line code, so each tile waits only for its own load; the segment's last,
-    // partial half block loads after the barrier (values past n read as 0).
+    // straight-line code before the code table is built; the segment's last, partial half
+    // block loads after the barrier (values past n read as 0).  The compiler emits these
+    // loads as flat loads (their addresses come from the segment table), and a flat load
+    // also counts on the LDS/scalar counter, so the wave's first wait for a scalar result
+    // waits for all four.  Loads through global-space pointers, which let each tile wait
+    // for its own, measured 0.9-1.6 % slower, and issuing the fourth only after the first
+    // tile's stores slower still; the decoders, whose loads are global, lose 19-30 % when
+    // they wait for all of theirs at once.
     const bool full = active && uint64_t(hb + 1) * kHalf <= n;
     bool bad_row = false;   // a gathered row index outside the matrix
     uint4 v[4];
