@@ -647,7 +647,7 @@ __device__ inline void encode_unit(const Args& a, uint32_t unit)
         // The unit's staged record, assembled in LDS: its 8 half-block counts (u16), then
         // its escapes.  It is written through to memory (agent scope) as whole 8-byte words,
         // consecutive across the workgroup's lanes: per-wave byte runs written through cost
-        // each unit several partial-line writes (3.5 % of a 64 Mi-value launch with 1 %
+        // each unit several partial-line writes (3.5 % of a 64 Mi-value launch with 2.4 %
         // escapes, 7 % with 7.5 %).  A block holds at most kBlockOverflow escape bytes.
         __shared__ __attribute__((aligned(16))) uint8_t s_rec[kStageHead + 4 * kBlockOverflow];
         if (lane == 0) reinterpret_cast<uint16_t*>(s_rec)[wave] = uint16_t(run);
