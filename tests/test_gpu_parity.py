@@ -680,17 +680,20 @@ def scan_path(monkeypatch):
     yield
 
 
-def compress_chunks_vs_oracle(Z, chunks_bits, plans, ws_bytes=None, esc_caps=None):
+def compress_chunks_vs_oracle(Z, chunks_bits, plans, ws_bytes=None, esc_caps=None, esc_shifts=None):
     # ws_bytes: workspace size (default: twice what the largest chunk needs, so that
     # about two chunks share a launch); esc_caps: per-chunk escape capacities (default:
-    # room for every value)
+    # room for every value); esc_shifts: per chunk, how many bytes past a 256-byte boundary
+    # its escape buffer starts (the bytes around it must stay unwritten)
     C, S = len(chunks_bits), len(chunks_bits[0])
     tens = [[dev_bf16(b) for b in ch] for ch in chunks_bits]
     sizes = [[b.size for b in ch] for ch in chunks_bits]
     st_sizes = [sum(Z.static_size(n) for n in sz) for sz in sizes]
     statics = [torch.full((max(t, 1),), POISON, dtype=torch.uint8, device="cuda") for t in st_sizes]
     caps = [sum(sz) for sz in sizes] if esc_caps is None else esc_caps
-    escs = [torch.full((max(c, 1),), POISON, dtype=torch.uint8, device="cuda") for c in caps]
+    shifts = [0] * C if esc_shifts is None else esc_shifts
+    bufs = [torch.full((shifts[k] + max(caps[k], 1) + 64,), POISON, dtype=torch.uint8, device="cuda") for k in range(C)]
+    escs = [bufs[k][shifts[k]:shifts[k] + max(caps[k], 1)] for k in range(C)]
     if ws_bytes is None:
         ws_bytes = 2 * Z.workspace_size(max(sum(sz) for sz in sizes), S)
     ws = torch.full((ws_bytes,), POISON, dtype=torch.uint8, device="cuda")
@@ -708,6 +711,8 @@ def compress_chunks_vs_oracle(Z, chunks_bits, plans, ws_bytes=None, esc_caps=Non
         assert np.array_equal(sh, st), f"chunk {k}: " + first_diff(sh, st)
         m = min(sum(ne_o), caps[k])
         assert np.array_equal(escs[k].cpu().numpy()[:m], esc[:m]), f"chunk {k}"
+        bh = bufs[k].cpu().numpy()
+        assert (bh[:shifts[k]] == POISON).all() and (bh[shifts[k] + m:] == POISON).all(), f"chunk {k}"
     return st_all
 
 
@@ -721,6 +726,24 @@ def chunk_sequence():
 
 def test_compress_chunks_matches_per_call_oracle(Z):
     compress_chunks_vs_oracle(Z, chunk_sequence(), [Z.plan(sigma=s) for s in (0.02, 1.0, 1e-3)])
+
+
+def test_compress_chunks_unaligned_escape_buffers(Z):
+    # several calls in one launch, each writing its escapes into a buffer that starts 1, 2
+    # or 3 bytes past a dword: few escapes, nearly all (units with more than a record's
+    # first 496 bytes), random bits; ragged sizes; one chunk's cap cuts its escapes off
+    rng = np.random.default_rng(78)
+    shapes = [[70001, 16384, 5000], [1 << 18, 33333, 4097], [1, 100000, 16385], [20000, 0, 65536], [8, 3, 300001]]
+    chunks = []
+    for k, ch in enumerate(shapes):
+        chunks.append([W.gaussian_bf16(ch[0], 0.02, 3000 + 10 * k), W.gaussian_bf16(ch[1], 1.0, 3001 + 10 * k),
+                       rng.integers(0, 1 << 16, ch[2], dtype=np.int64).astype(np.uint16)])
+    plans = [Z.plan(sigma=0.02), Z.plan(table=[1, 2, 3, 4, 5, 6, 7]), Z.plan(sigma=0.1)]
+    totals = [sum(O.compress_batch(ch, oracle_tables(plans))[2]) for ch in chunks]
+    caps = [t + 7 for t in totals]
+    caps[2] = totals[2] - 1001   # this chunk overflows: only its status bit and its first cap bytes are checked
+    status = compress_chunks_vs_oracle(Z, chunks, plans, esc_caps=caps, esc_shifts=[1, 2, 3, 1, 2])
+    assert status == Z.STATUS_ESC_OVERFLOW
 
 
 def test_compress_chunks_scan_path(Z, scan_path):
