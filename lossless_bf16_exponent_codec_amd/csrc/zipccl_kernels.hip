@@ -28,9 +28,10 @@
 //     the first 192 exponents of each tile, the rest go where the escapes would have
 //     gone.  Decoders recognise such a block from its offset-table entries alone.
 //   * Compress is one launch (compress_single_kernel) when the caller passes a status
-//     word: encoding workgroups write the A bytes and planes, stage each unit's escapes
-//     contiguously in the workspace and then publish the unit's escape count in a ready
-//     word tagged with the call's tag; placing workgroups, interleaved in the grid about
+//     word: encoding workgroups write the A bytes and planes, stage each unit's half-block
+//     counts and escapes in the workspace as one record (whole 8-byte words) and then
+//     publish the unit's escape count in a ready word tagged with the call's tag; placing
+//     workgroups, interleaved in the grid about
 //     one generation of encoders behind the units they place, wait (bounded) for the
 //     ready words of their call's units up to theirs, then compute escape positions,
 //     compact the escapes and write offset tables and headers.  What one workgroup
